@@ -1,0 +1,357 @@
+"""CPU oracle for W12: the plain, slow, obviously-correct definition of every result
+the HIP library computes.  TEST INFRASTRUCTURE ONLY: nothing in the product path
+(the ``lossless_bit_weight_w12_amd`` package, its C-ABI library or kernels) may import,
+call or link this file; only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` use it.  It shares no code, tables or constants
+generators with the HIP path.
+
+What the pages fix, and where (pages are cited by title and section):
+
+* "StargazerX0/SpecPilot" (hotrepo.ai repo digest), section "What it is": W12 is a
+  12-bit weight format whose decode inside the GEMM is bit-exact, and decoding is
+  greedy with the target model choosing every token.
+* "SpecPilot" (fasttoolhub glossary), section "Differentiation": the 12-bit format is
+  general and lossless.
+* "SpecPilot: an agent doubled speculative decoding speed, and the 10.87x needs
+  context" (ai.jakubjirak.com review), section "The mechanisms it found": about
+  12.01-12.02 bits per weight on dense models, decoded in GEMM registers; 12 instead
+  of 16 bits cuts weight traffic by a quarter; the LM head's argmax is certified
+  exact.  Section "The caveats the README states": batched kernels reduce in another
+  order, so near-ties can flip -- which is why argmax here is defined on exact logits.
+* "StargazerX0/SpecPilot", section "Results and verification": each committed token
+  must be the target's own choice (the accepted-prefix rule below).
+
+The pages give no bit layout.  W12 v1 (defined here and implemented independently on
+the GPU) is the plainest layout with 12 = 1 sign + 7 mantissa + 4 code bits per weight
+and a per-tensor codebook (a per-group codebook would cost about one extra bit per
+weight, contradicting the 12.01-12.02 figure):
+
+  fields     BF16 b: s = b>>15, e = (b>>7)&0xFF, m = b&0x7F, sm = (s<<7)|m
+  histogram  H[e] over all N*K elements (e = 0..255)
+  codebook   the 16 exponents with the largest H[e], ties to the smaller e (H = 0 is
+             eligible), then sorted ascending -> C[0..15]
+  codes      code = j with C[j] = e; e not in C -> escape: code 0 is stored and the
+             true exponent goes to the escape list
+  tiles      W [N out, K in] row-major, N % 16 == 0, K % 128 == 0.  Tile (b, g)
+             covers rows 16b..16b+15 and columns 128g..128g+127, 3072 bytes at offset
+             (b*(K/128) + g)*3072.  Lane slot l = 0..63: r = l % 16, q = l // 16.
+             Element t = 0..31 of slot l: j = t // 8, i = t % 8,
+             kappa = 32j + 8q + i  (row 16b + r, column 128g + kappa).
+             sm byte at 1024*(t // 16) + 16*l + (t % 16);
+             code nibble in the little-endian u32 at 2048 + 16*l + 4*j, at bit
+             4*(i // 2) + 16*(i % 2)  (even i in the low half-word, odd i in the high).
+  escapes    u32 record (r<<28) | (k<<8) | e per escape; the records of row-block b
+             are esc[esc_off[b] : esc_off[b+1]], sorted ascending by (k, r);
+             esc_off[0] = 0, esc_off[N/16] = n_esc.
+  header     64 bytes LE: "W12\\0", version 1 (u32), N, K, n_esc (u64), C[16],
+             e_max (u8: largest exponent field < 255 present, 0 if none), 15 zero bytes.
+  size       bytes = 3072*(N/16)*(K/128) + 4*n_esc + 4*(N/16 + 1) + 64
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+import numpy as np
+
+TILE_ROWS = 16
+TILE_K = 128
+TILE_BYTES = 3072
+HEADER_BYTES = 64
+# GEMM acceptance rule: |y - z| <= REL_TOL * sum_k |x_k||w_k| + ABS_TOL per element
+REL_TOL = 2e-3
+ABS_TOL = 1e-6
+
+
+# ----------------------------------------------------------------------------- fields
+def split_fields(w: np.ndarray):
+    """Sign, exponent field, mantissa and the sign/mantissa byte of BF16 bit patterns."""
+    b = np.asarray(w, dtype=np.uint16).astype(np.uint32)
+    s = b >> 15
+    e = (b >> 7) & 0xFF
+    m = b & 0x7F
+    sm = (s << 7) | m
+    return s, e, m, sm
+
+
+def join_fields(sm: np.ndarray, e: np.ndarray) -> np.ndarray:
+    """BF16 bits from the sm byte and the exponent field: (s<<15) | (e<<7) | m."""
+    sm = np.asarray(sm, dtype=np.uint32)
+    e = np.asarray(e, dtype=np.uint32)
+    return (((sm >> 7) << 15) | (e << 7) | (sm & 0x7F)).astype(np.uint16)
+
+
+def exponent_histogram(w: np.ndarray) -> np.ndarray:
+    _, e, _, _ = split_fields(w.reshape(-1))
+    return np.bincount(e.astype(np.int64), minlength=256).astype(np.int64)
+
+
+def choose_codebook(hist: np.ndarray) -> np.ndarray:
+    """Top-16 exponents by count, ties to the smaller exponent, returned ascending."""
+    order = sorted(range(256), key=lambda ex: (-int(hist[ex]), ex))
+    return np.array(sorted(order[:16]), dtype=np.uint8)
+
+
+def finite_e_max(hist: np.ndarray) -> int:
+    present = [ex for ex in range(255) if hist[ex] > 0]
+    return max(present) if present else 0
+
+
+# ----------------------------------------------------------------------------- layout
+def slot_layout():
+    """Per (lane slot l, element t): row r, column offset kappa, sm byte offset, code
+    word offset and code bit position inside that word.  Arrays of shape [64, 32]."""
+    l = np.arange(64)[:, None] * np.ones((1, 32), dtype=np.int64)
+    t = np.ones((64, 1), dtype=np.int64) * np.arange(32)[None, :]
+    r = l % 16
+    q = l // 16
+    j = t // 8
+    i = t % 8
+    kappa = 32 * j + 8 * q + i
+    sm_pos = 1024 * (t // 16) + 16 * l + (t % 16)
+    word_pos = 2048 + 16 * l + 4 * j
+    bit = 4 * (i // 2) + 16 * (i % 2)
+    return r, kappa, sm_pos, word_pos, bit
+
+
+@dataclass
+class W12Blob:
+    n: int
+    k: int
+    codebook: np.ndarray      # uint8[16], ascending
+    e_max: int
+    tiles: np.ndarray         # uint8[(n/16)*(k/128)*3072]
+    esc_off: np.ndarray       # uint32[n/16 + 1]
+    esc: np.ndarray           # uint32[n_esc]
+
+    @property
+    def n_esc(self) -> int:
+        return int(self.esc.size)
+
+
+def check_shape(n: int, k: int):
+    if n <= 0 or k <= 0 or n % TILE_ROWS or k % TILE_K or k >= (1 << 20):
+        raise ValueError(f"W12 v1 needs N % 16 == 0, K % 128 == 0, 0 < K < 2^20 (got {n}x{k})")
+
+
+# ----------------------------------------------------------------------------- encode
+def encode(w: np.ndarray, rows_per_chunk: int = 4096) -> W12Blob:
+    """W12 v1 encode of BF16 bits w [N, K] (uint16)."""
+    w = np.ascontiguousarray(w, dtype=np.uint16)
+    n, k = w.shape
+    check_shape(n, k)
+    hist = exponent_histogram(w)
+    cb = choose_codebook(hist)
+    code_of = np.full(256, -1, dtype=np.int64)
+    code_of[cb.astype(np.int64)] = np.arange(16)
+    nb, gk = n // TILE_ROWS, k // TILE_K
+    r_ix, kap, sm_pos, word_pos, bit = slot_layout()
+    tiles = np.zeros((nb, gk, TILE_BYTES), dtype=np.uint8)
+    esc_parts = []
+    rows_per_chunk = max(16, rows_per_chunk - rows_per_chunk % 16)
+    for n0 in range(0, n, rows_per_chunk):
+        n1 = min(n, n0 + rows_per_chunk)
+        _, e, _, sm = split_fields(w[n0:n1])
+        code = code_of[e]
+        is_esc = code < 0
+        code = np.where(is_esc, 0, code)
+        b0, b1 = n0 // 16, n1 // 16
+        # [blocks, 16 rows, gk, 128] -> [blocks, gk, 16, 128]
+        sm4 = sm.reshape(b1 - b0, 16, gk, 128).transpose(0, 2, 1, 3)
+        cd4 = code.reshape(b1 - b0, 16, gk, 128).transpose(0, 2, 1, 3)
+        sm_slots = sm4[:, :, r_ix, kap]            # [blocks, gk, 64, 32]
+        cd_slots = cd4[:, :, r_ix, kap]
+        tb = tiles[b0:b1]
+        tb[:, :, sm_pos.reshape(-1)] = sm_slots.reshape(b1 - b0, gk, -1).astype(np.uint8)
+        # code words: 4 words of 8 nibbles per slot
+        words = np.zeros((b1 - b0, gk, 64, 4), dtype=np.uint32)
+        for t in range(32):
+            words[:, :, :, t // 8] |= (cd_slots[:, :, :, t].astype(np.uint32)
+                                       << np.uint32(bit[0, t]))
+        wb = words.reshape(b1 - b0, gk, 64 * 4).astype("<u4").view(np.uint8)
+        wb = wb.reshape(b1 - b0, gk, 64, 4, 4)     # [.., l, j, byte]
+        for jj in range(4):
+            for by in range(4):
+                tb[:, :, 2048 + 16 * np.arange(64) + 4 * jj + by] = wb[:, :, :, jj, by]
+        # escapes of this chunk, as (row, col, exponent)
+        rr, cc = np.nonzero(is_esc)
+        if rr.size:
+            esc_parts.append((rr + n0, cc, e[rr, cc]))
+    if esc_parts:
+        rows = np.concatenate([p[0] for p in esc_parts]).astype(np.int64)
+        cols = np.concatenate([p[1] for p in esc_parts]).astype(np.int64)
+        exps = np.concatenate([p[2] for p in esc_parts]).astype(np.int64)
+    else:
+        rows = cols = exps = np.zeros(0, dtype=np.int64)
+    blk = rows // 16
+    rr = rows % 16
+    order = np.lexsort((rr, cols, blk))            # by block, then k, then r
+    blk, rr, cols, exps = blk[order], rr[order], cols[order], exps[order]
+    esc = ((rr << 28) | (cols << 8) | exps).astype(np.uint32)
+    counts = np.bincount(blk, minlength=nb) if blk.size else np.zeros(nb, dtype=np.int64)
+    esc_off = np.zeros(nb + 1, dtype=np.uint32)
+    esc_off[1:] = np.cumsum(counts)
+    return W12Blob(n=n, k=k, codebook=cb, e_max=finite_e_max(hist),
+                   tiles=tiles.reshape(-1), esc_off=esc_off, esc=esc)
+
+
+# ----------------------------------------------------------------------------- decode
+def decode(blob: W12Blob, blocks_per_chunk: int = 256) -> np.ndarray:
+    """Inverse of encode: BF16 bits [N, K]."""
+    n, k = blob.n, blob.k
+    nb, gk = n // 16, k // 128
+    r_ix, kap, sm_pos, word_pos, bit = slot_layout()
+    tiles_all = blob.tiles.reshape(nb, gk, TILE_BYTES)
+    out = np.empty((n, k), dtype=np.uint16)
+    for b0 in range(0, nb, blocks_per_chunk):
+        b1 = min(nb, b0 + blocks_per_chunk)
+        cb = b1 - b0
+        tiles = tiles_all[b0:b1]
+        sm_slots = tiles[:, :, sm_pos.reshape(-1)].reshape(cb, gk, 64, 32).astype(np.uint32)
+        wbytes = tiles[:, :, 2048:3072].reshape(cb, gk, 64, 4, 4).astype(np.uint32)
+        words = (wbytes[..., 0] | (wbytes[..., 1] << 8) | (wbytes[..., 2] << 16)
+                 | (wbytes[..., 3] << 24))                           # [cb, gk, 64, 4]
+        codes = np.empty((cb, gk, 64, 32), dtype=np.uint32)
+        for t in range(32):
+            codes[:, :, :, t] = (words[:, :, :, t // 8] >> np.uint32(bit[0, t])) & 0xF
+        e_slots = blob.codebook.astype(np.uint32)[codes]
+        sm = np.empty((cb, gk, 16, 128), dtype=np.uint32)
+        ex = np.empty((cb, gk, 16, 128), dtype=np.uint32)
+        sm[:, :, r_ix, kap] = sm_slots
+        ex[:, :, r_ix, kap] = e_slots
+        sm = sm.transpose(0, 2, 1, 3).reshape(cb * 16, k)
+        ex = ex.transpose(0, 2, 1, 3).reshape(cb * 16, k)
+        for b in range(b0, b1):
+            for rec in blob.esc[blob.esc_off[b]:blob.esc_off[b + 1]]:
+                rec = int(rec)
+                r, kk, e = rec >> 28, (rec >> 8) & 0xFFFFF, rec & 0xFF
+                ex[16 * (b - b0) + r, kk] = e
+        out[16 * b0:16 * b1] = join_fields(sm, ex)
+    return out
+
+
+# ----------------------------------------------------------------------------- sizes
+def header(blob: W12Blob) -> bytes:
+    h = bytearray(HEADER_BYTES)
+    h[0:4] = b"W12\x00"
+    h[4:8] = (1).to_bytes(4, "little")
+    h[8:16] = blob.n.to_bytes(8, "little")
+    h[16:24] = blob.k.to_bytes(8, "little")
+    h[24:32] = blob.n_esc.to_bytes(8, "little")
+    h[32:48] = bytes(blob.codebook.tolist())
+    h[48] = blob.e_max
+    return bytes(h)
+
+
+def serialize(blob: W12Blob) -> bytes:
+    return (header(blob) + blob.tiles.tobytes() + blob.esc_off.astype("<u4").tobytes()
+            + blob.esc.astype("<u4").tobytes())
+
+
+def blob_bytes(blob: W12Blob) -> int:
+    return len(serialize(blob))
+
+
+def bits_per_weight(blob: W12Blob) -> float:
+    return 8.0 * blob_bytes(blob) / (blob.n * blob.k)
+
+
+# ----------------------------------------------------------------------------- GEMM
+def bf16_to_f64(b: np.ndarray) -> np.ndarray:
+    return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def gemm_reference(x: np.ndarray, w: np.ndarray, rows_per_chunk: int = 8192):
+    """z = x . W^T and S = |x| . |W|^T in float64 for BF16 bits x [M, K], w [N, K].
+    Each BF16 product is exact in float64; the float64 sum is within K*2^-53*S of the
+    exact value, negligible against the acceptance rule."""
+    xf = bf16_to_f64(x)
+    n = w.shape[0]
+    z = np.empty((x.shape[0], n))
+    s = np.empty((x.shape[0], n))
+    for n0 in range(0, n, rows_per_chunk):
+        wf = bf16_to_f64(w[n0:n0 + rows_per_chunk])
+        z[:, n0:n0 + wf.shape[0]] = xf @ wf.T
+        s[:, n0:n0 + wf.shape[0]] = np.abs(xf) @ np.abs(wf).T
+    return z, s
+
+
+def gemm_w12(x: np.ndarray, blob: W12Blob):
+    """The W12 GEMM as the pages describe it: decode the weights bit-exactly, then the
+    plain BF16 product (FP64 here)."""
+    return gemm_reference(x, decode(blob))
+
+
+def gemm_rows(x: np.ndarray, w_rows: np.ndarray):
+    """z and S for selected weight rows (sampled checks at full size)."""
+    return gemm_reference(x, w_rows)
+
+
+def within_tolerance(y_bits: np.ndarray, z: np.ndarray, s: np.ndarray):
+    """Per-element acceptance |y - z| <= 2e-3*S + 1e-6 for BF16 outputs y."""
+    y = bf16_to_f64(y_bits)
+    return np.abs(y - z) <= REL_TOL * s + ABS_TOL
+
+
+# ----------------------------------------------------------------------------- exact
+def exact_parts(b: np.ndarray):
+    """Integer form of finite BF16 values: value = sign * M * 2^E with
+    normal (e >= 1): M = 128 + m, E = e - 134; zero/subnormal (e = 0): M = m, E = -133."""
+    s, e, m, _ = split_fields(b)
+    s = s.astype(np.int64)
+    e = e.astype(np.int64)
+    m = m.astype(np.int64)
+    if np.any(e == 255):
+        raise ValueError("exact logits are defined for finite BF16 only")
+    mant = np.where(e > 0, m + 128, m)
+    ex = np.where(e > 0, e - 134, -133)
+    sign = 1 - 2 * s
+    return sign, mant, ex
+
+
+EXACT_SHIFT = 266   # -(smallest product exponent): every product is an integer at 2^-266
+
+
+def exact_logit(x_row: np.ndarray, w_row: np.ndarray) -> int:
+    """Z = sum_k x_k * w_k * 2^266 as an exact Python integer."""
+    sx, mx, ex = exact_parts(x_row)
+    sw, mw, ew = exact_parts(w_row)
+    prod = sx * sw * mx * mw                 # |prod| < 2^16
+    sh = ex + ew + EXACT_SHIFT               # 0 .. 506
+    total = 0
+    for shv in np.unique(sh):
+        part = int(prod[sh == shv].sum())    # |part| < K * 2^16, exact in int64
+        total += part << int(shv)
+    return total
+
+
+def argmax_exact(x: np.ndarray, w: np.ndarray, rows_per_chunk: int = 8192):
+    """Per row m: the index v maximising the exact logit sum_k x[m,k]*W[v,k], lowest
+    index on an exact tie.  Steps: float64 logits z64 and S64 for every v; a rigorous
+    filter keeps v with z64_v >= max z64 - 2*gamma*max S64, gamma = (K+2)*2^-52 (the
+    float64 error of any summation order is below gamma*S); exact integer logits of
+    the survivors decide.  Returns (argmax int64[M], candidate counts)."""
+    k = x.shape[1]
+    z64, s64 = gemm_reference(x, w, rows_per_chunk)
+    gamma = (k + 2) * 2.0 ** -52
+    out = np.empty(x.shape[0], dtype=np.int64)
+    ncand = np.empty(x.shape[0], dtype=np.int64)
+    for mi in range(x.shape[0]):
+        zmax = z64[mi].max()
+        thr = zmax - 2.0 * gamma * s64[mi].max()
+        cand = np.nonzero(z64[mi] >= thr)[0]
+        ncand[mi] = cand.size
+        best_v, best_z = -1, None
+        for v in cand:                        # ascending: lowest index kept on ties
+            zv = exact_logit(x[mi], w[v])
+            if best_z is None or zv > best_z:
+                best_v, best_z = int(v), zv
+        out[mi] = best_v
+    return out, ncand
+
+
+def accepted_length(argmax: np.ndarray, draft: np.ndarray) -> int:
+    """Greedy verification: the number of leading draft tokens equal to the target's
+    own choice (first mismatch position, or n_draft if none)."""
+    for i in range(len(draft)):
+        if int(argmax[i]) != int(draft[i]):
+            return i
+    return len(draft)

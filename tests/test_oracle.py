@@ -1,0 +1,337 @@
+"""Pins for the CPU oracle: every check here compares the oracle with something other
+than itself -- a hand-derived worked example, closed forms, invariants of the layout,
+exact rational brute force, or constructions whose answer is known in advance.
+The mutation tests at the end plant plausible mistakes in the oracle (on the CPU) and
+show that at least one pin fails for each."""
+import json
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+from hypothesis import given, settings, strategies as st, HealthCheck
+
+from oracle import w12_oracle as o
+import w12_inputs as wi
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def bf16_fraction(b) -> Fraction:
+    """Exact value of a BF16 pattern via Python's float (independent of the oracle)."""
+    f = np.array([int(b) << 16], dtype=np.uint32).view(np.float32)[0]
+    return Fraction(float(f))
+
+
+# ----------------------------------------------------------------------------- format
+def worked_example_matrix():
+    w = np.zeros((16, 128), dtype=np.uint16)
+    for r in range(16):
+        for c in range(128):
+            s = 1 if c >= 64 else 0
+            w[r, c] = (s << 15) | ((100 + r) << 7) | (c & 0x7F)
+    w[5, 77] = (1 << 15) | (30 << 7) | 77
+    return w
+
+
+def test_worked_example_golden():
+    g = json.load(open(os.path.join(GOLDEN, "w12_v1_worked_example.json")))
+    w = worked_example_matrix()
+    b = o.encode(w)
+    assert b.codebook.tolist() == g["codebook"]
+    assert b.e_max == g["e_max"]
+    assert b.esc_off.tolist() == g["esc_off"]
+    assert b.esc.tolist() == g["esc"]
+    for pos, val in g["tile_bytes"].items():
+        assert int(b.tiles[int(pos)]) == val, pos
+    for pos, val in g["code_words"].items():
+        p = int(pos)
+        word = int.from_bytes(bytes(b.tiles[p:p + 4].tolist()), "little")
+        assert word == val, pos
+    assert o.blob_bytes(b) == g["total_bytes"]
+    assert o.bits_per_weight(b) == g["bits_per_weight"]
+    assert o.header(b).hex() == g["header_hex"]
+    assert np.array_equal(o.decode(b), w)
+
+
+def test_all_bf16_patterns_roundtrip():
+    w = wi.all_bf16_patterns()
+    b = o.encode(w)
+    # every exponent field occurs 256 times: the tie rule picks 0..15
+    assert b.codebook.tolist() == list(range(16))
+    assert b.n_esc == 65536 * 240 // 256
+    assert b.e_max == 254
+    assert np.array_equal(o.decode(b), w)
+
+
+def test_slot_layout_is_a_bijection():
+    r, kap, sm_pos, word_pos, bit = o.slot_layout()
+    pairs = set(zip(r.reshape(-1).tolist(), kap.reshape(-1).tolist()))
+    assert len(pairs) == 2048 and pairs == {(a, c) for a in range(16) for c in range(128)}
+    assert sorted(sm_pos.reshape(-1).tolist()) == list(range(2048))
+    nib = set()
+    for wp, bt in zip(word_pos.reshape(-1).tolist(), bit.reshape(-1).tolist()):
+        nib.add(2 * wp + bt // 4)          # nibble index inside the tile
+    assert nib == set(range(2 * 2048, 2 * 3072))
+
+
+def test_codebook_definition_pairwise():
+    """Pairwise form of the rule: each chosen exponent beats each unchosen one by
+    (count, then smaller exponent)."""
+    g = np.random.default_rng(7)
+    for trial in range(200):
+        h = g.integers(0, 4, size=256) * g.integers(0, 2, size=256)
+        if trial % 3 == 0:
+            h[:] = 0
+            h[g.choice(256, size=5, replace=False)] = g.integers(1, 9, size=5)
+        cb = o.choose_codebook(h).tolist()
+        assert cb == sorted(set(cb)) and len(cb) == 16
+        chosen = set(cb)
+        for c in chosen:
+            for d in range(256):
+                if d not in chosen:
+                    assert (h[c] > h[d]) or (h[c] == h[d] and c < d)
+
+
+@settings(max_examples=25, deadline=None, suppress_health_check=[HealthCheck.too_slow])
+@given(a=st.integers(1, 4), bb=st.integers(1, 3), seed=st.integers(0, 2**31 - 1),
+       kind=st.sampled_from(["bits", "gauss", "narrow"]))
+def test_roundtrip_and_escape_invariants(a, bb, seed, kind):
+    n, k = 16 * a, 128 * bb
+    g = np.random.default_rng(seed)
+    if kind == "bits":
+        w = wi.random_bits((n, k), g)
+    elif kind == "gauss":
+        w = wi.gaussian_bf16((n, k), 0.02, g)
+    else:   # few distinct exponents: codebook padded with unused ones
+        w = ((g.integers(0, 2, (n, k)) << 15) | (g.integers(120, 123, (n, k)) << 7)
+             | g.integers(0, 128, (n, k))).astype(np.uint16)
+    b = o.encode(w)
+    assert np.array_equal(o.decode(b), w)
+    # closed form: n_esc = sum of counts of exponents outside the codebook
+    e = (w.astype(np.int64) >> 7) & 0xFF
+    assert b.n_esc == int((~np.isin(e, b.codebook.astype(np.int64))).sum())
+    assert b.esc_off[0] == 0 and b.esc_off[-1] == b.n_esc
+    assert np.all(np.diff(b.esc_off.astype(np.int64)) >= 0)
+    for blk in range(n // 16):
+        recs = b.esc[b.esc_off[blk]:b.esc_off[blk + 1]].astype(np.int64)
+        keys = [((rc >> 8) & 0xFFFFF, rc >> 28) for rc in recs]
+        assert keys == sorted(keys)
+        for rc in recs:
+            r, kk, ee = rc >> 28, (rc >> 8) & 0xFFFFF, rc & 0xFF
+            assert e[16 * blk + r, kk] == ee and ee not in b.codebook
+
+
+@pytest.mark.parametrize("n,k", [(16, 128), (64, 1024), (1024, 1024)])
+def test_bits_per_weight_closed_form(n, k):
+    w = wi.gaussian_bf16((n, k), 0.02, np.random.default_rng(n + k))
+    b = o.encode(w)
+    nb, gk = n // 16, k // 128
+    expect = 3072 * nb * gk + 4 * b.n_esc + 4 * (nb + 1) + 64
+    assert o.blob_bytes(b) == expect
+    assert b.tiles.size * 4 == 3 * (2 * n * k)       # tiles are exactly 3/4 of BF16 bytes
+    assert o.bits_per_weight(b) == 12 + 8 * (4 * b.n_esc + 4 * (nb + 1) + 64) / (n * k)
+
+
+def test_gaussian_codebook_and_escape_rate():
+    """For N(0, 0.02^2) the 16 most populated binades are e = 108..123 (masses of the
+    neighbours: e=107 ~ 3.8e-5, e=124 ~ 4e-10), so escapes are the |w| < 2^-19 tail
+    (rate ~ 2*pdf(0)*2^-19 = 7.6e-5)."""
+    w = wi.config_weights(1)["w"]
+    b = o.encode(w)
+    assert b.codebook.tolist() == list(range(108, 124))
+    rate = b.n_esc / w.size
+    assert 2e-5 < rate < 2e-4
+
+
+def test_outlier_workload_escapes():
+    w = wi.config_weights(2)["w"]
+    b = o.encode(w)
+    assert b.n_esc >= 0.0005 * w.size
+    assert np.array_equal(o.decode(b), w)
+
+
+# ----------------------------------------------------------------------------- GEMM
+@pytest.mark.parametrize("m", [1, 2, 7, 15, 16, 17, 31, 32])
+def test_gemm_reference_vs_exact_rationals(m):
+    g = np.random.default_rng(100 + m)
+    n, k = 16, 128
+    x = wi.gaussian_bf16((m, k), 1.0, g)
+    w = wi.gaussian_bf16((n, k), 0.02, g)
+    z, s = o.gemm_reference(x, w)
+    xf = [[bf16_fraction(v) for v in row] for row in x]
+    wf = [[bf16_fraction(v) for v in row] for row in w]
+    for mi in range(m):
+        for ni in range(n):
+            exact = sum(a * c for a, c in zip(xf[mi], wf[ni]))
+            sabs = sum(abs(a * c) for a, c in zip(xf[mi], wf[ni]))
+            assert abs(Fraction(z[mi, ni]) - exact) <= Fraction(k, 2**52) * sabs
+            assert abs(Fraction(s[mi, ni]) - sabs) <= Fraction(k, 2**52) * sabs
+
+
+def test_gemm_reference_special_case_library():
+    """With W in BF16 the reference is the float64 matrix product: torch on the CPU."""
+    import torch
+    g = np.random.default_rng(5)
+    x = wi.gaussian_bf16((4, 256), 1.0, g)
+    w = wi.gaussian_bf16((32, 256), 0.02, g)
+    z, _ = o.gemm_reference(x, w)
+    xt = torch.from_numpy(wi.bf16_bits_to_f32(x).astype(np.float64))
+    wt = torch.from_numpy(wi.bf16_bits_to_f32(w).astype(np.float64))
+    assert np.allclose(z, (xt @ wt.T).numpy(), rtol=0, atol=1e-12)
+
+
+def test_tolerance_rule():
+    g = np.random.default_rng(3)
+    x = wi.gaussian_bf16((2, 512), 1.0, g)
+    w = wi.gaussian_bf16((16, 512), 0.02, g)
+    z, s = o.gemm_reference(x, w)
+    y = wi.f32_to_bf16_bits(z.astype(np.float32))
+    assert o.within_tolerance(y, z, s).all()
+    bad = y.copy()
+    bad[0, 3] ^= 0x0100          # move the exponent: far outside the rule
+    assert not o.within_tolerance(bad, z, s)[0, 3]
+
+
+# ----------------------------------------------------------------------------- exact argmax
+def test_exact_logit_matches_rationals():
+    g = np.random.default_rng(11)
+    for k in (128, 640):
+        x = wi.gaussian_bf16((1, k), 1.0, g)[0]
+        w = wi.gaussian_bf16((1, k), 0.02, g)[0]
+        w[:5] = [0x0001, 0x8003, 0x0000, 0x7F7F, 0x0080]   # subnormals, zero, max, min normal
+        x[:5] = [0x0005, 0x3F80, 0x8000, 0x0001, 0x8081]
+        z = o.exact_logit(x, w)
+        exact = sum(bf16_fraction(a) * bf16_fraction(c) for a, c in zip(x, w))
+        assert Fraction(z, 2**266) == exact
+
+
+def brute_argmax(x, w):
+    out = []
+    wf = [[bf16_fraction(v) for v in row] for row in w]
+    for row in x:
+        xf = [bf16_fraction(v) for v in row]
+        vals = [sum(a * c for a, c in zip(xf, wr)) for wr in wf]
+        best = max(vals)
+        out.append(vals.index(best))     # first (lowest) index attaining the max
+    return out
+
+
+def test_argmax_matches_brute_force():
+    g = np.random.default_rng(12)
+    x = wi.gaussian_bf16((3, 128), 1.0, g)
+    w = wi.gaussian_bf16((48, 128), 0.02, g)
+    am, _ = o.argmax_exact(x, w)
+    assert am.tolist() == brute_argmax(x, w)
+
+
+def test_argmax_planted_exact_tie_picks_lowest_index():
+    g = np.random.default_rng(13)
+    x = wi.gaussian_bf16((1, 256), 1.0, g)
+    w = wi.gaussian_bf16((64, 256), 0.02, g)
+    v1 = int(o.argmax_exact(x, w)[0][0])
+    v2 = 3 if v1 != 3 else 60
+    w[v2] = w[v1]
+    am, _ = o.argmax_exact(x, w)
+    assert am[0] == min(v1, v2)
+
+
+def test_argmax_planted_one_ulp_pair():
+    """Copy the winner's row, then move one weight by one BF16 ulp in the direction that
+    raises (or lowers) the logit: the answer is known by construction."""
+    g = np.random.default_rng(14)
+    x = wi.gaussian_bf16((1, 256), 1.0, g)
+    w = wi.gaussian_bf16((64, 256), 0.02, g)
+    v1 = int(o.argmax_exact(x, w)[0][0])
+    v2 = 10 if v1 > 10 else 63
+    for raise_it in (True, False):
+        w2 = w.copy()
+        w2[v2] = w2[v1]
+        kk = next(i for i in range(256) if (w2[v2, i] & 0x7F) not in (0, 0x7F)
+                  and (x[0, i] & 0x7FFF) != 0)
+        same_sign = ((x[0, kk] >> 15) == (w2[v2, kk] >> 15))
+        bump = 1 if same_sign == raise_it else -1       # +1 ulp in magnitude raises x*w if signs agree
+        w2[v2, kk] = int(w2[v2, kk]) + bump
+        am, _ = o.argmax_exact(x, w2)
+        assert am[0] == (v2 if raise_it else v1)
+
+
+def test_accepted_length_cases():
+    am = np.array([5, 6, 7, 8])
+    assert o.accepted_length(am, np.array([9, 6, 7, 8])) == 0
+    assert o.accepted_length(am, np.array([5, 6, 7, 8])) == 4
+    assert o.accepted_length(am, np.array([5, 6, 0, 8])) == 2     # later matches not counted
+    assert o.accepted_length(am, np.array([5, 6])) == 2
+    assert o.accepted_length(am, np.array([], dtype=np.int64)) == 0
+
+
+# ----------------------------------------------------------------------------- mutations
+def _pins_fail(fn):
+    try:
+        fn()
+    except (AssertionError, ValueError):
+        return True
+    return False
+
+
+def test_mutation_tie_rule_is_caught(monkeypatch):
+    def bad(hist):
+        order = sorted(range(256), key=lambda ex: (-int(hist[ex]), -ex))
+        return np.array(sorted(order[:16]), dtype=np.uint8)
+    monkeypatch.setattr(o, "choose_codebook", bad)
+    assert _pins_fail(test_all_bf16_patterns_roundtrip)
+
+
+def test_mutation_nibble_order_is_caught(monkeypatch):
+    orig = o.slot_layout
+
+    def bad():
+        r, kap, sm_pos, word_pos, bit = orig()
+        i = np.arange(32)[None, :] % 8
+        return r, kap, sm_pos, word_pos, 4 * i * np.ones((64, 1), dtype=np.int64)
+    monkeypatch.setattr(o, "slot_layout", bad)
+    assert _pins_fail(test_worked_example_golden)
+
+
+def test_mutation_escape_order_is_caught(monkeypatch):
+    orig = o.encode
+
+    def bad(w, rows_per_chunk=4096):
+        b = orig(w, rows_per_chunk)
+        for blk in range(b.n // 16):
+            seg = b.esc[b.esc_off[blk]:b.esc_off[blk + 1]]
+            seg[:] = np.array(sorted(seg.tolist()), dtype=np.uint32)   # sorted by r first
+        return b
+    monkeypatch.setattr(o, "encode", bad)
+    assert _pins_fail(lambda: test_roundtrip_and_escape_invariants.hypothesis.inner_test(
+        a=2, bb=2, seed=1, kind="bits"))
+
+
+def test_mutation_sign_in_exact_logit_is_caught(monkeypatch):
+    orig = o.exact_parts
+
+    def bad(b):
+        s, mant, ex = orig(b)
+        return np.ones_like(s), mant, ex
+    monkeypatch.setattr(o, "exact_parts", bad)
+    assert _pins_fail(test_exact_logit_matches_rationals)
+
+
+def test_mutation_transposed_gemm_is_caught(monkeypatch):
+    orig = o.gemm_reference
+
+    def bad(x, w, rows_per_chunk=8192):
+        z, s = orig(x, w, rows_per_chunk)
+        return z[:, ::-1].copy(), s
+    monkeypatch.setattr(o, "gemm_reference", bad)
+    assert _pins_fail(lambda: test_gemm_reference_vs_exact_rationals(1))
+
+
+def test_mutation_subnormal_exponent_is_caught(monkeypatch):
+    orig = o.exact_parts
+
+    def bad(b):
+        s, mant, ex = orig(b)
+        return s, mant, np.where(mant < 128, ex - 1, ex)
+    monkeypatch.setattr(o, "exact_parts", bad)
+    assert _pins_fail(test_exact_logit_matches_rationals)
