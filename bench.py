@@ -1,0 +1,243 @@
+"""Benchmark of the W12 decode/verification GEMM on one MI355X.
+
+Workload (default): the MLP block of a dense ~22B decoder -- fused gate+up
+W [34816, 5120] and down W [5120, 17408], BF16 ~N(0, 0.02^2) packed to W12, x rows
+BF16 ~N(0, 1) -- at M = 1, 4, 8, 16 and 32 rows.  One step = the ten W12 GEMMs
+(gate+up and down at every M).  `value` is the step's algorithmic bytes (W12 format
+bytes + x + y of every GEMM) divided by the step time, in GB/s, with all inputs
+resident in HBM.  The same step on plain BF16 weights with the same kernel family
+gives the speedup.  Weight copies are rotated so that no GEMM finds its weights in the
+256 MB Infinity Cache.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "W12 GEMM achieved HBM GB/s (% of peak) and speedup vs BF16, M=1..32"
+PEAK_GBPS = 8000.0          # MI355X HBM3E peak
+MS = (1, 4, 8, 16, 32)
+N_GU, K_GU = 34816, 5120
+N_DN, K_DN = 5120, 17408
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def w12_bytes(t) -> int:
+    return t.nbytes()
+
+
+def gemm_bytes(t, m: int) -> int:
+    return w12_bytes(t) + 2 * m * t.k + 2 * m * t.n
+
+
+def bf16_bytes(n: int, k: int, m: int) -> int:
+    return 2 * n * k + 2 * m * k + 2 * m * n
+
+
+def cpu_baseline(seconds_target: float = 12.0):
+    """The CPU oracle's W12 GEMM (bit-exact decode, then the FP64 product) on a bounded
+    sample of the gate+up matrix: the first R rows, at every M of the workload."""
+    import numpy as np
+    from oracle import w12_oracle as o
+    import w12_inputs as wi
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+    except Exception:
+        blas_threads = 1
+    rows = 512
+    w = wi.weight(3, wi.T_W, (rows, K_GU))     # same stream: the first rows of gate+up
+    blob = o.encode(w)
+    xs = {m: wi.activations(3, wi.T_X, m, K_GU) for m in MS}
+    done_bytes, t_total, reps = 0, 0.0, 0
+    while t_total < seconds_target and reps < 50:
+        for m in MS:
+            t0 = time.perf_counter()
+            o.gemm_w12(xs[m], blob)
+            t_total += time.perf_counter() - t0
+            done_bytes += o.blob_bytes(blob) + 2 * m * K_GU + 2 * m * rows
+        reps += 1
+    return {"value": done_bytes / t_total / 1e9, "unit": "GB/s", "cores": int(blas_threads),
+            "kind": "oracle",
+            "sample": f"oracle W12 GEMM (decode + FP64 product) on the first {rows} rows of the "
+                      f"gate+up matrix [{rows}x{K_GU}], M in {list(MS)}, {reps} passes, "
+                      f"{t_total:.1f} s; BLAS threads {blas_threads}"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--rotate-bytes", type=float, default=float(1 << 30),
+                    help="bytes of weight copies each timed loop rotates over (defeats the "
+                         "256 MB Infinity Cache)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--profile-only", action="store_true",
+                    help="run a few W12 steps and exit (for rocprofv3)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported (this path has no "
+              f"multi-GPU sharding; every box here has one MI355X)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import w12_inputs as wi
+    import lossless_bit_weight_w12_amd as w12
+
+    dev = torch.device("cuda:0")
+    log("bench: generating the MLP-block weights (seeded, host) ...")
+    t0 = time.time()
+    w_gu = torch.from_numpy(wi.weight(3, wi.T_W, (N_GU, K_GU)).view(np.int16)).to(dev)
+    w_dn = torch.from_numpy(wi.weight(3, wi.T_W2, (N_DN, K_DN)).view(np.int16)).to(dev)
+    log(f"bench: weights on device in {time.time() - t0:.1f} s; encoding to W12 ...")
+    t_gu = [w12.encode(w_gu)]
+    t_dn = [w12.encode(w_dn)]
+    b_gu, b_dn = [w_gu], [w_dn]
+
+    def n_copies(nbytes):
+        return max(2, -(-int(args.rotate_bytes) // int(nbytes)))
+
+    def clone(t):
+        return w12.W12Tensor(**{**t.__dict__, "tiles": t.tiles.clone(),
+                                "esc_off": t.esc_off.clone(), "esc": t.esc.clone()})
+    while len(t_gu) < n_copies(t_gu[0].nbytes()):
+        t_gu.append(clone(t_gu[0]))
+    while len(t_dn) < n_copies(t_dn[0].nbytes()):
+        t_dn.append(clone(t_dn[0]))
+    while len(b_gu) < n_copies(2 * N_GU * K_GU):
+        b_gu.append(w_gu.clone())
+    while len(b_dn) < n_copies(2 * N_DN * K_DN):
+        b_dn.append(w_dn.clone())
+    xs = {m: (torch.from_numpy(wi.activations(3, wi.T_X, m, K_GU).view(np.int16)).to(dev),
+              torch.from_numpy(wi.activations(3, wi.T_X2, m, K_DN).view(np.int16)).to(dev)) for m in MS}
+    ys = {m: (torch.empty((m, N_GU), dtype=torch.bfloat16, device=dev),
+              torch.empty((m, N_DN), dtype=torch.bfloat16, device=dev)) for m in MS}
+    yb = {m: (torch.empty((m, N_GU), dtype=torch.bfloat16, device=dev),
+              torch.empty((m, N_DN), dtype=torch.bfloat16, device=dev)) for m in MS}
+    torch.cuda.synchronize()
+    log(f"bench: bits/weight gate+up {t_gu[0].bits_per_weight():.5f}, down {t_dn[0].bits_per_weight():.5f}")
+
+    def w12_step(c):
+        for m in MS:
+            w12.gemm(xs[m][0], t_gu[c % len(t_gu)], out=ys[m][0])
+            w12.gemm(xs[m][1], t_dn[c % len(t_dn)], out=ys[m][1])
+
+    def bf16_step(c):
+        for m in MS:
+            w12.gemm_bf16(xs[m][0], b_gu[c % len(b_gu)], out=yb[m][0])
+            w12.gemm_bf16(xs[m][1], b_dn[c % len(b_dn)], out=yb[m][1])
+
+    if args.profile_only:
+        for i in range(args.steps):
+            w12_step(i)
+            bf16_step(i)
+        torch.cuda.synchronize()
+        log("bench: profile-only run done")
+        return
+
+    step_bytes = sum(gemm_bytes(t_gu[0], m) + gemm_bytes(t_dn[0], m) for m in MS)
+    step_bytes_bf16 = sum(bf16_bytes(N_GU, K_GU, m) + bf16_bytes(N_DN, K_DN, m) for m in MS)
+
+    def timed(step_fn, steps, warmup):
+        for i in range(warmup):
+            step_fn(i)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(steps):
+            step_fn(i)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps     # ms per step
+
+    log("bench: timing W12 steps ...")
+    ms_w12 = timed(w12_step, args.steps, args.warmup)
+    log("bench: timing BF16 steps ...")
+    ms_bf16 = timed(bf16_step, args.steps, args.warmup)
+    # W12 and BF16 kernels share the MAC order: their outputs must agree bit for bit
+    same = all(torch.equal(ys[m][i].view(torch.int16), yb[m][i].view(torch.int16))
+               for m in MS for i in (0, 1))
+
+    # per-(M, matrix) launch durations, each over R launches on rotating copies
+    per = {}
+    reps = 40
+    for m in MS:
+        for name, tl, bl, xi in (("gate_up", t_gu, b_gu, 0), ("down", t_dn, b_dn, 1)):
+            res = {}
+            for kind in ("w12", "bf16"):
+                for i in range(5):
+                    if kind == "w12":
+                        w12.gemm(xs[m][xi], tl[i % len(tl)], out=ys[m][xi])
+                    else:
+                        w12.gemm_bf16(xs[m][xi], bl[i % len(bl)], out=yb[m][xi])
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for i in range(reps):
+                    if kind == "w12":
+                        w12.gemm(xs[m][xi], tl[i % len(tl)], out=ys[m][xi])
+                    else:
+                        w12.gemm_bf16(xs[m][xi], bl[i % len(bl)], out=yb[m][xi])
+                e1.record()
+                torch.cuda.synchronize()
+                res[kind] = e0.elapsed_time(e1) / reps * 1e3     # us per launch
+            nbytes = gemm_bytes(tl[0], m)
+            per[f"M{m}_{name}"] = {
+                "us_w12": round(res["w12"], 2), "us_bf16": round(res["bf16"], 2),
+                "gbps_w12": round(nbytes / res["w12"] / 1e3, 1),
+                "pct_peak_w12": round(100 * nbytes / res["w12"] / 1e3 / PEAK_GBPS, 1),
+                "gbps_bf16": round(bf16_bytes(tl[0].n, tl[0].k, m) / res["bf16"] / 1e3, 1),
+                "speedup_vs_bf16": round(res["bf16"] / res["w12"], 3)}
+    # dominant kernel = the (M, matrix) GEMM with the largest share of the step
+    dom_key = max(per, key=lambda kk: per[kk]["us_w12"])
+    dom = per[dom_key]
+    m_dom = int(dom_key.split("_")[0][1:])
+    t_dom = t_gu[0] if dom_key.endswith("gate_up") else t_dn[0]
+    alg = gemm_bytes(t_dom, m_dom)
+    roofline = {"bound": "hbm", "achieved": round(alg / dom["us_w12"] / 1e3, 1), "peak": PEAK_GBPS,
+                "unit": "GB/s", "frac": round(alg / dom["us_w12"] / 1e3 / PEAK_GBPS, 4),
+                "traffic": None, "kernel": f"w12_gemm {dom_key}", "alg_bytes_per_launch": alg,
+                "avg_launch_us": dom["us_w12"]}
+
+    value = step_bytes / (ms_w12 * 1e-3) / 1e9
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_w12, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded BF16 ~N(0,0.02^2) weights, x ~N(0,1))",
+        "config": {"workload": "mlp_block gate+up[34816x5120] + down[5120x17408], M in 1,4,8,16,32",
+                   "m": list(MS), "rotated_copies": {"w12_gate_up": len(t_gu), "w12_down": len(t_dn),
+                                                     "bf16_gate_up": len(b_gu), "bf16_down": len(b_dn)},
+                   "bits_per_weight": round(t_gu[0].bits_per_weight(), 5)},
+        "pct_of_peak": round(100 * value / PEAK_GBPS, 2),
+        "speedup_vs_bf16": round(ms_bf16 / ms_w12, 4),
+        "bf16_ms_per_step": round(ms_bf16, 4),
+        "bf16_gbps": round(step_bytes_bf16 / (ms_bf16 * 1e-3) / 1e9, 1),
+        "w12_equals_bf16_bitwise": bool(same),
+        "per_gemm": per,
+        "roofline": roofline,
+        "cpu_baseline": None,
+        "host": {"cpu": platform.processor() or platform.machine(),
+                 "affinity_cores": len(os.sched_getaffinity(0))},
+    }
+    if not args.no_cpu_baseline:
+        log("bench: timing the CPU oracle on a bounded sample ...")
+        out["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

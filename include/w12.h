@@ -1,0 +1,167 @@
+/*
+ * w12.h -- C ABI of libw12.so: the W12 lossless 12-bit weight format on MI355X
+ * (gfx950): encode, bit-exact decode, the memory-bound decode/verification GEMM
+ * (M = 1..32 rows of BF16 x against W12 weights, FP32 accumulate, BF16 out) and the
+ * greedy verification epilogue (exact-logit argmax per row, accepted-prefix length).
+ *
+ * Sources (pages cited by title and section):
+ *  - "StargazerX0/SpecPilot" (hotrepo.ai), "What it is": W12 is a 12-bit weight
+ *    format decoded bit-exactly inside the GEMM; decoding is greedy and the target
+ *    model decides each token.  "Results and verification": every committed token
+ *    must be the target's own choice.
+ *  - "SpecPilot" (fasttoolhub glossary), "Differentiation": the format is a general,
+ *    lossless 12-bit weight format.
+ *  - "SpecPilot: an agent doubled speculative decoding speed, and the 10.87x needs
+ *    context", "The mechanisms it found": about 12.01-12.02 bits per weight, decoded
+ *    in GEMM registers, a quarter less weight traffic than BF16 in memory-bound
+ *    decode, and a certified exact-argmax LM head; "The caveats the README states":
+ *    reduction order can flip near-ties (hence argmax on exact logits).
+ *
+ * W12 v1 layout (the pages fix only its properties; this is the layout defined here):
+ *  - W is [n out][k in] BF16, row-major; n % 16 == 0, k % 128 == 0, 0 < k < 2^20.
+ *  - Per-tensor codebook C[16]: the 16 exponent fields with the largest counts (ties
+ *    to the smaller field), strictly ascending.  Element code = index of its exponent
+ *    in C; an exponent outside C is an escape (code 0 stored, true exponent listed).
+ *  - Tile (b, g) = rows 16b..16b+15 x columns 128g..128g+127, 3072 bytes at byte
+ *    offset (b*(k/128) + g)*3072.  Lane slot l = 0..63 (r = l%16, q = l/16) holds
+ *    32 elements t = 0..31 (j = t/8, i = t%8) at column 128g + 32j + 8q + i of row
+ *    16b + r.  Byte 1024*(t/16) + 16l + t%16 holds sm = (sign<<7) | mantissa; the
+ *    little-endian u32 at 2048 + 16l + 4j holds the 8 codes of j, code of i at bit
+ *    4*(i/2) + 16*(i%2).  (Slot l's 8 elements of j are exactly lane l's 8 BF16 A-
+ *    operand values of one v_mfma_f32_16x16x32_bf16 step.)
+ *  - Escapes: u32 (r<<28) | (k<<8) | e per escape; row-block b owns
+ *    esc[esc_off[b] .. esc_off[b+1]), sorted ascending by (k, r); esc_off has
+ *    n/16 + 1 entries, esc_off[0] = 0, esc_off[n/16] = n_esc.
+ *  - Bits per weight = 12 + 8*(4*n_esc + 4*(n/16 + 1) + 64)/(n*k) counting a 64-byte
+ *    header; tile bytes are exactly 3/4 of the BF16 bytes.
+ *
+ * Conventions for every call:
+ *  - Pointers marked "device" are HIP device memory owned by the caller; the library
+ *    never allocates or frees device memory and never synchronises, except
+ *    w12_encode_count (documented below).  Inputs must not alias outputs.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Calls are asynchronous;
+ *    buffers must stay alive until the stream has passed the call.
+ *  - Arguments are validated on the host before any HIP call; on error nothing is
+ *    launched and outputs are untouched.  Launch failures return W12_ERR_HIP; device
+ *    faults surface at the caller's next synchronisation.
+ *  - The workspace `ws` (device, w12_workspace_bytes(op, ...) bytes, 256-byte aligned)
+ *    must be zero-filled once before its first use (w12_workspace_init does that on
+ *    the stream); every call leaves its counters zero again.  Two calls that run
+ *    concurrently must not share a workspace.
+ */
+#ifndef W12_H
+#define W12_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t w12_status;
+
+#define W12_OK             0
+#define W12_ERR_NULL      -1  /* a required pointer is NULL */
+#define W12_ERR_SHAPE     -2  /* n % 16, k % 128, k >= 2^20, n == 0, size overflow */
+#define W12_ERR_RANGE     -3  /* m outside 1..32, n_draft > m, unknown op */
+#define W12_ERR_FORMAT    -4  /* codebook not strictly ascending, e_max >= 255 */
+#define W12_ERR_WORKSPACE -5  /* workspace smaller than w12_workspace_bytes() */
+#define W12_ERR_HIP       -6  /* a HIP runtime call or kernel launch failed */
+#define W12_ERR_ALIGN     -7  /* tiles/x/w/y/ws not aligned as documented */
+
+#define W12_MAX_M 32
+
+/* Host-side descriptor of one W12 tensor (device buffers + host metadata). */
+typedef struct w12_desc {
+  uint64_t n;             /* output rows, multiple of 16 */
+  uint64_t k;             /* input columns, multiple of 128, < 2^20 */
+  uint64_t n_esc;         /* number of escape records */
+  uint8_t codebook[16];   /* strictly ascending exponent fields */
+  uint8_t e_max;          /* largest exponent field < 255 present in W (0 if none) */
+  uint8_t reserved[7];
+  void* tiles;            /* device, w12_tiles_bytes(n, k) bytes, 16-byte aligned */
+  uint32_t* esc_off;      /* device, n/16 + 1 entries */
+  uint32_t* esc;          /* device, n_esc entries (may be NULL when n_esc == 0) */
+} w12_desc;
+
+/* Operation ids for w12_workspace_bytes. */
+#define W12_OP_ENCODE    0
+#define W12_OP_DECODE    1
+#define W12_OP_GEMM      2
+#define W12_OP_GEMM_BF16 3
+#define W12_OP_VERIFY    4
+
+/* Bytes of the tile array: (n/16)*(k/128)*3072; 0 if the shape is invalid. */
+size_t w12_tiles_bytes(uint64_t n, uint64_t k);
+
+/* Workspace bytes needed by `op` for m rows (ignored by ENCODE/DECODE) and an
+ * n x k weight; 0 for an invalid op or shape.  Never more than a few MB except
+ * VERIFY, which holds FP32 logits [m][n] plus per-row-block maxima. */
+size_t w12_workspace_bytes(int op, uint32_t m, uint64_t n, uint64_t k);
+
+/* Zero-fills `ws` on `stream` with a kernel (no hipMemset). */
+w12_status w12_workspace_init(void* ws, size_t ws_bytes, void* stream);
+
+/* Encode, first half (exponent histogram -> codebook, e_max, n_esc).
+ * w: device BF16 bits [n][k] row-major, 16-byte aligned.  Results land in host memory
+ * (codebook_out[16], *e_max_out, *n_esc_out); this call SYNCHRONISES `stream` to
+ * return them.  Defines the codebook rule of the W12 v1 layout above (lossless format
+ * per "SpecPilot" glossary, "Differentiation"). */
+w12_status w12_encode_count(const uint16_t* w, uint64_t n, uint64_t k,
+                            uint8_t codebook_out[16], uint8_t* e_max_out,
+                            uint64_t* n_esc_out, void* ws, size_t ws_bytes, void* stream);
+
+/* Encode, second half: writes d->tiles, d->esc_off and d->esc for w [n][k] using
+ * d->codebook; d->n_esc must be the count w12_encode_count returned for that
+ * codebook (escape writes are bounded by it, so a wrong value cannot overflow `esc`).
+ * Output bytes are identical to the CPU oracle's. */
+w12_status w12_encode(const uint16_t* w, const w12_desc* d, void* ws, size_t ws_bytes,
+                      void* stream);
+
+/* Bit-exact inverse: w_out device BF16 [n][k] row-major (16-byte aligned). */
+w12_status w12_decode(const w12_desc* d, uint16_t* w_out, void* stream);
+
+/* y = x . W^T with W decoded in registers ("StargazerX0/SpecPilot", "What it is"):
+ * x device BF16 [m][k], y device BF16 [m][n] (row-major, 16-byte aligned), m in 1..32,
+ * FP32 accumulation, round-to-nearest-even to BF16.  IEEE propagation for non-finite
+ * inputs. */
+w12_status w12_gemm(const uint16_t* x, uint32_t m, const w12_desc* d, uint16_t* y,
+                    void* ws, size_t ws_bytes, void* stream);
+
+/* The same kernel family reading plain BF16 weights w [n][k] row-major (the baseline
+ * W12 is measured against: plain BF16 decoding in "What it is"). */
+w12_status w12_gemm_bf16(const uint16_t* x, uint32_t m, const uint16_t* w, uint64_t n,
+                         uint64_t k, uint16_t* y, void* ws, size_t ws_bytes, void* stream);
+
+/* Greedy verification over the LM head (review page, "The mechanisms it found":
+ * certified exact-argmax LM head; "StargazerX0/SpecPilot", "Results and
+ * verification": committed tokens are the target's own choice).
+ * x device BF16 [m][k] (m in 1..32, finite), W12 head d (finite weights), draft
+ * device int32 [n_draft] (n_draft <= m).  Writes argmax_out device int32 [m]: the index
+ * v maximising the EXACT logit sum_k x[row,k]*W[v,k], lowest index on exact ties; and
+ * accepted_out device int32 [1]: the first i < n_draft with argmax[i] != draft[i], or
+ * n_draft.  FP32 logits are computed once, then every v within a certified error
+ * bound of the maximum is recomputed exactly, so the result does not depend on the
+ * reduction order.  A row whose logits are not finite gets argmax -1. */
+w12_status w12_lmhead_verify(const uint16_t* x, uint32_t m, const w12_desc* d,
+                             const int32_t* draft, uint32_t n_draft, int32_t* argmax_out,
+                             int32_t* accepted_out, void* ws, size_t ws_bytes,
+                             void* stream);
+
+/* Harness op for the layer chain: y[row] = bf16(x[row] / sqrt(mean(x[row]^2))) in FP32,
+ * x, y device BF16 [m][k].  Not part of the W12 method itself. */
+w12_status w12_rms_rescale(const uint16_t* x, uint32_t m, uint64_t k, uint16_t* y,
+                           void* stream);
+
+/* Static description of a status code. */
+const char* w12_status_str(w12_status s);
+
+/* Library version: 0x000100 for W12 v1, library 0.1. */
+uint32_t w12_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* W12_H */

@@ -1,0 +1,347 @@
+// C-ABI host layer of libw12.so: argument validation (before any HIP call), workspace
+// layout, kernel-family dispatch and launch.  No HIP call happens at load time.
+#include "../../include/w12.h"
+#include "w12_internal.h"
+
+#include <string.h>
+
+using namespace w12;
+
+namespace {
+
+constexpr uint64_t kMaxK = 1ull << 20;
+constexpr uint64_t kMaxN = 1ull << 31;
+constexpr int kTargetWorkgroups = 1024;   // 4 per CU on 256 CUs
+
+inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+inline bool shape_ok(uint64_t n, uint64_t k) {
+  return n > 0 && k > 0 && n % 16 == 0 && k % 128 == 0 && k < kMaxK && n < kMaxN &&
+         (n / 16) * (k / 128) < (1ull << 31);
+}
+
+inline bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+w12_status check_desc(const w12_desc* d, bool need_data) {
+  if (!d) return W12_ERR_NULL;
+  if (!shape_ok(d->n, d->k)) return W12_ERR_SHAPE;
+  for (int i = 1; i < 16; ++i)
+    if (d->codebook[i] <= d->codebook[i - 1]) return W12_ERR_FORMAT;
+  if (d->e_max >= 255) return W12_ERR_FORMAT;
+  if (d->n_esc > (uint64_t)d->n * d->k || d->n_esc >= (1ull << 32)) return W12_ERR_FORMAT;
+  if (need_data) {
+    if (!d->tiles || !d->esc_off) return W12_ERR_NULL;
+    if (d->n_esc > 0 && !d->esc) return W12_ERR_NULL;
+    if (!aligned(d->tiles, 16)) return W12_ERR_ALIGN;
+  }
+  return W12_OK;
+}
+
+inline bool codebook_is_run(const uint8_t* c) {
+  for (int i = 1; i < 16; ++i)
+    if (c[i] != (uint8_t)(c[0] + i)) return false;
+  return true;
+}
+
+// Work split: row-blocks per workgroup and K splits so that the grid holds enough
+// workgroups to keep 256 CUs streaming; splits keep at least one 4-column chunk.
+GemmPlan make_plan(uint64_t n, uint64_t k, int epi) {
+  GemmPlan p;
+  const uint64_t nb = n / 16, g = k / 128;
+  p.rbw = nb >= 1024 ? 2 : 1;
+  p.n_rbg = (uint32_t)((nb + p.rbw - 1) / p.rbw);
+  uint64_t ns = 1;
+  if (epi == EPI_BF16)
+    while ((uint64_t)p.n_rbg * ns < (uint64_t)kTargetWorkgroups && g >= ns * 2 * 4) ns *= 2;
+  uint64_t cols = (g + ns - 1) / ns;
+  cols = (cols + 3) & ~3ull;
+  p.cols_per_split = (uint32_t)cols;
+  p.nsplit = (uint32_t)((g + cols - 1) / cols);
+  return p;
+}
+
+size_t gemm_ws_bytes(uint32_t m, uint64_t n, uint64_t k) {
+  const GemmPlan p = make_plan(n, k, EPI_BF16);
+  size_t b = align256((size_t)p.n_rbg * 4);
+  if (p.nsplit > 1) b += align256((size_t)p.nsplit * m * n * 4);
+  return b;
+}
+
+struct VerifyLayout {
+  size_t logits, rbmax_v, rbmax_i, cand, ncand, total;
+};
+
+VerifyLayout verify_layout(uint32_t m, uint64_t n) {
+  VerifyLayout L;
+  const uint64_t nb = n / 16;
+  L.logits = 0;
+  L.rbmax_v = L.logits + align256((size_t)m * n * 4);
+  L.rbmax_i = L.rbmax_v + align256((size_t)m * nb * 4);
+  L.cand = L.rbmax_i + align256((size_t)m * nb * 4);
+  L.ncand = L.cand + align256((size_t)m * n * 4);
+  L.total = L.ncand + align256((size_t)m * 4);
+  return L;
+}
+
+struct EncodeLayout {
+  size_t hist, result, total, tile_cnt, tile_off, bytes;
+};
+
+EncodeLayout encode_layout(uint64_t n, uint64_t k) {
+  EncodeLayout L;
+  const uint64_t tiles = (n / 16) * (k / 128);
+  L.hist = 0;                 // 256 x u64
+  L.result = 2048;            // 64 bytes
+  L.total = 2048 + 64;        // u32
+  L.tile_cnt = 4096;
+  L.tile_off = L.tile_cnt + align256((size_t)tiles * 4);
+  L.bytes = L.tile_off + align256((size_t)tiles * 4);
+  return L;
+}
+
+inline w12_status hip_status(hipError_t e) { return e == hipSuccess ? W12_OK : W12_ERR_HIP; }
+
+void fill_args_codebook(GemmArgs& a, const w12_desc* d) {
+  for (int i = 0; i < 4; ++i)
+    a.lut[i] = (uint32_t)d->codebook[4 * i] | ((uint32_t)d->codebook[4 * i + 1] << 8) |
+               ((uint32_t)d->codebook[4 * i + 2] << 16) | ((uint32_t)d->codebook[4 * i + 3] << 24);
+  a.basepair = (uint32_t)d->codebook[0] | ((uint32_t)d->codebook[0] << 16);
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t w12_tiles_bytes(uint64_t n, uint64_t k) {
+  if (!shape_ok(n, k)) return 0;
+  return (size_t)(n / 16) * (k / 128) * 3072u;
+}
+
+size_t w12_workspace_bytes(int op, uint32_t m, uint64_t n, uint64_t k) {
+  if (!shape_ok(n, k)) return 0;
+  switch (op) {
+    case W12_OP_ENCODE: return encode_layout(n, k).bytes;
+    case W12_OP_DECODE: return 0;
+    case W12_OP_GEMM:
+    case W12_OP_GEMM_BF16:
+      if (m < 1 || m > W12_MAX_M) return 0;
+      return gemm_ws_bytes(m, n, k);
+    case W12_OP_VERIFY:
+      if (m < 1 || m > W12_MAX_M) return 0;
+      return verify_layout(m, n).total;
+    default: return 0;
+  }
+}
+
+w12_status w12_workspace_init(void* ws, size_t ws_bytes, void* stream) {
+  if (ws_bytes == 0) return W12_OK;
+  if (!ws) return W12_ERR_NULL;
+  if (!aligned(ws, 16)) return W12_ERR_ALIGN;
+  return hip_status(launch_fill_zero(ws, ws_bytes, (hipStream_t)stream));
+}
+
+w12_status w12_encode_count(const uint16_t* w, uint64_t n, uint64_t k, uint8_t codebook_out[16],
+                            uint8_t* e_max_out, uint64_t* n_esc_out, void* ws, size_t ws_bytes,
+                            void* stream) {
+  if (!w || !codebook_out || !e_max_out || !n_esc_out || !ws) return W12_ERR_NULL;
+  if (!shape_ok(n, k)) return W12_ERR_SHAPE;
+  if (ws_bytes < encode_layout(n, k).bytes) return W12_ERR_WORKSPACE;
+  if (!aligned(w, 16) || !aligned(ws, 256)) return W12_ERR_ALIGN;
+  hipStream_t s = (hipStream_t)stream;
+  const EncodeLayout L = encode_layout(n, k);
+  uint8_t* base = (uint8_t*)ws;
+  hipError_t e = launch_fill_zero(base, 4096, s);
+  if (e == hipSuccess) e = launch_encode_hist(w, n * k, (unsigned long long*)(base + L.hist), s);
+  if (e == hipSuccess) e = launch_encode_codebook((const unsigned long long*)(base + L.hist), base + L.result, s);
+  uint8_t res[64];
+  if (e == hipSuccess) e = hipMemcpyAsync(res, base + L.result, 64, hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return W12_ERR_HIP;
+  memcpy(codebook_out, res, 16);
+  *e_max_out = res[16];
+  uint64_t ne;
+  memcpy(&ne, res + 24, 8);
+  *n_esc_out = ne;
+  return W12_OK;
+}
+
+w12_status w12_encode(const uint16_t* w, const w12_desc* d, void* ws, size_t ws_bytes,
+                      void* stream) {
+  if (!w || !ws) return W12_ERR_NULL;
+  w12_status st = check_desc(d, true);
+  if (st != W12_OK) return st;
+  const EncodeLayout L = encode_layout(d->n, d->k);
+  if (ws_bytes < L.bytes) return W12_ERR_WORKSPACE;
+  if (!aligned(w, 16) || !aligned(ws, 256)) return W12_ERR_ALIGN;
+  hipStream_t s = (hipStream_t)stream;
+  uint8_t* base = (uint8_t*)ws;
+  const uint32_t nb = (uint32_t)(d->n / 16), g = (uint32_t)(d->k / 128);
+  Mask256 mask;
+  memset(&mask, 0, sizeof(mask));
+  Codebook16 cb;
+  for (int i = 0; i < 16; ++i) {
+    cb.c[i] = d->codebook[i];
+    mask.m[d->codebook[i] >> 5] |= 1u << (d->codebook[i] & 31);
+  }
+  uint32_t* tile_cnt = (uint32_t*)(base + L.tile_cnt);
+  uint32_t* tile_off = (uint32_t*)(base + L.tile_off);
+  hipError_t e = launch_encode_count_tiles(w, nb, g, mask, tile_cnt, s);
+  if (e == hipSuccess)
+    e = launch_encode_scan(tile_cnt, nb * g, g, tile_off, d->esc_off, (uint32_t*)(base + L.total), s);
+  if (e == hipSuccess)
+    e = launch_encode_pack(w, nb, g, cb, tile_off, (uint8_t*)d->tiles, d->esc, d->n_esc, s);
+  return hip_status(e);
+}
+
+w12_status w12_decode(const w12_desc* d, uint16_t* w_out, void* stream) {
+  if (!w_out) return W12_ERR_NULL;
+  w12_status st = check_desc(d, true);
+  if (st != W12_OK) return st;
+  if (!aligned(w_out, 16)) return W12_ERR_ALIGN;
+  Codebook16 cb;
+  for (int i = 0; i < 16; ++i) cb.c[i] = d->codebook[i];
+  return hip_status(launch_decode((const uint8_t*)d->tiles, d->esc_off, d->esc,
+                                  (uint32_t)(d->n / 16), (uint32_t)(d->k / 128), cb, w_out,
+                                  (hipStream_t)stream));
+}
+
+w12_status w12_gemm(const uint16_t* x, uint32_t m, const w12_desc* d, uint16_t* y, void* ws,
+                    size_t ws_bytes, void* stream) {
+  if (!x || !y || !ws) return W12_ERR_NULL;
+  w12_status st = check_desc(d, true);
+  if (st != W12_OK) return st;
+  if (m < 1 || m > W12_MAX_M) return W12_ERR_RANGE;
+  if (ws_bytes < gemm_ws_bytes(m, d->n, d->k)) return W12_ERR_WORKSPACE;
+  if (!aligned(x, 16) || !aligned(y, 4) || !aligned(ws, 256)) return W12_ERR_ALIGN;
+  const GemmPlan p = make_plan(d->n, d->k, EPI_BF16);
+  GemmArgs a;
+  memset(&a, 0, sizeof(a));
+  a.x = x;
+  a.w = (const uint8_t*)d->tiles;
+  a.esc_off = d->esc_off;
+  a.esc = d->esc;
+  a.y = y;
+  a.counters = (uint32_t*)ws;
+  a.partial = (float*)((uint8_t*)ws + align256((size_t)p.n_rbg * 4));
+  a.m = m;
+  a.n = (uint32_t)d->n;
+  a.k = (uint32_t)d->k;
+  a.g_cols = (uint32_t)(d->k / 128);
+  a.nb = (uint32_t)(d->n / 16);
+  a.nsplit = p.nsplit;
+  a.cols_per_split = p.cols_per_split;
+  fill_args_codebook(a, d);
+  const int src = codebook_is_run(d->codebook) ? SRC_RUN : SRC_LUT;
+  return hip_status(launch_gemm(a, src, EPI_BF16, p, (hipStream_t)stream));
+}
+
+w12_status w12_gemm_bf16(const uint16_t* x, uint32_t m, const uint16_t* w, uint64_t n,
+                         uint64_t k, uint16_t* y, void* ws, size_t ws_bytes, void* stream) {
+  if (!x || !w || !y || !ws) return W12_ERR_NULL;
+  if (!shape_ok(n, k)) return W12_ERR_SHAPE;
+  if (m < 1 || m > W12_MAX_M) return W12_ERR_RANGE;
+  if (ws_bytes < gemm_ws_bytes(m, n, k)) return W12_ERR_WORKSPACE;
+  if (!aligned(x, 16) || !aligned(w, 16) || !aligned(y, 4) || !aligned(ws, 256)) return W12_ERR_ALIGN;
+  const GemmPlan p = make_plan(n, k, EPI_BF16);
+  GemmArgs a;
+  memset(&a, 0, sizeof(a));
+  a.x = x;
+  a.w = (const uint8_t*)w;
+  a.y = y;
+  a.counters = (uint32_t*)ws;
+  a.partial = (float*)((uint8_t*)ws + align256((size_t)p.n_rbg * 4));
+  a.m = m;
+  a.n = (uint32_t)n;
+  a.k = (uint32_t)k;
+  a.g_cols = (uint32_t)(k / 128);
+  a.nb = (uint32_t)(n / 16);
+  a.nsplit = p.nsplit;
+  a.cols_per_split = p.cols_per_split;
+  return hip_status(launch_gemm(a, SRC_BF16, EPI_BF16, p, (hipStream_t)stream));
+}
+
+w12_status w12_lmhead_verify(const uint16_t* x, uint32_t m, const w12_desc* d, const int32_t* draft,
+                             uint32_t n_draft, int32_t* argmax_out, int32_t* accepted_out,
+                             void* ws, size_t ws_bytes, void* stream) {
+  if (!x || !argmax_out || !accepted_out || !ws) return W12_ERR_NULL;
+  if (n_draft > 0 && !draft) return W12_ERR_NULL;
+  w12_status st = check_desc(d, true);
+  if (st != W12_OK) return st;
+  if (m < 1 || m > W12_MAX_M || n_draft > m) return W12_ERR_RANGE;
+  const VerifyLayout L = verify_layout(m, d->n);
+  if (ws_bytes < L.total) return W12_ERR_WORKSPACE;
+  if (!aligned(x, 16) || !aligned(ws, 256) || !aligned(argmax_out, 4) || !aligned(accepted_out, 4))
+    return W12_ERR_ALIGN;
+  hipStream_t s = (hipStream_t)stream;
+  uint8_t* base = (uint8_t*)ws;
+  GemmPlan p = make_plan(d->n, d->k, EPI_LOGITS);
+  GemmArgs a;
+  memset(&a, 0, sizeof(a));
+  a.x = x;
+  a.w = (const uint8_t*)d->tiles;
+  a.esc_off = d->esc_off;
+  a.esc = d->esc;
+  a.logits = (float*)(base + L.logits);
+  a.rbmax_v = (float*)(base + L.rbmax_v);
+  a.rbmax_i = (int32_t*)(base + L.rbmax_i);
+  a.m = m;
+  a.n = (uint32_t)d->n;
+  a.k = (uint32_t)d->k;
+  a.g_cols = (uint32_t)(d->k / 128);
+  a.nb = (uint32_t)(d->n / 16);
+  a.nsplit = 1;
+  a.cols_per_split = p.cols_per_split;
+  fill_args_codebook(a, d);
+  const int src = codebook_is_run(d->codebook) ? SRC_RUN : SRC_LUT;
+  hipError_t e = launch_gemm(a, src, EPI_LOGITS, p, s);
+  VerifyArgs v;
+  memset(&v, 0, sizeof(v));
+  v.x = x;
+  v.tiles = (const uint8_t*)d->tiles;
+  v.esc_off = d->esc_off;
+  v.esc = d->esc;
+  v.logits = a.logits;
+  v.rbmax_v = a.rbmax_v;
+  v.rbmax_i = a.rbmax_i;
+  v.cand = (int32_t*)(base + L.cand);
+  v.ncand = (int32_t*)(base + L.ncand);
+  v.argmax = argmax_out;
+  v.draft = draft;
+  v.accepted = accepted_out;
+  v.m = m;
+  v.n = a.n;
+  v.k = a.k;
+  v.g_cols = a.g_cols;
+  v.nb = a.nb;
+  v.n_draft = n_draft;
+  v.e_max = d->e_max;
+  for (int i = 0; i < 4; ++i) v.lut[i] = a.lut[i];
+  if (e == hipSuccess) e = launch_verify_pass2(v, s);
+  if (e == hipSuccess) e = launch_accept(v, s);
+  return hip_status(e);
+}
+
+w12_status w12_rms_rescale(const uint16_t* x, uint32_t m, uint64_t k, uint16_t* y, void* stream) {
+  if (!x || !y) return W12_ERR_NULL;
+  if (m < 1 || m > (1u << 20)) return W12_ERR_RANGE;
+  if (k == 0 || k >= kMaxK) return W12_ERR_SHAPE;
+  return hip_status(launch_rms_rescale(x, m, (uint32_t)k, y, (hipStream_t)stream));
+}
+
+const char* w12_status_str(w12_status s) {
+  switch (s) {
+    case W12_OK: return "ok";
+    case W12_ERR_NULL: return "null pointer";
+    case W12_ERR_SHAPE: return "bad shape (n % 16, k % 128, 0 < k < 2^20)";
+    case W12_ERR_RANGE: return "value out of range (m in 1..32, n_draft <= m)";
+    case W12_ERR_FORMAT: return "bad W12 descriptor (codebook not ascending, e_max, n_esc)";
+    case W12_ERR_WORKSPACE: return "workspace too small";
+    case W12_ERR_HIP: return "HIP runtime error";
+    case W12_ERR_ALIGN: return "misaligned pointer";
+    default: return "unknown status";
+  }
+}
+
+uint32_t w12_version(void) { return 0x000100u; }
+
+}  // extern "C"

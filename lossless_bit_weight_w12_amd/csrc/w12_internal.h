@@ -1,0 +1,107 @@
+// Internal definitions shared by the host layer and the kernels of libw12.so.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace w12 {
+
+// Weight source of the GEMM kernel family.
+enum Src : int {
+  SRC_RUN = 0,   // W12 tiles, codebook is a run C[j] = C[0] + j (exponent = base + code)
+  SRC_LUT = 1,   // W12 tiles, arbitrary ascending codebook (16-entry byte LUT)
+  SRC_BF16 = 2,  // plain BF16 rows [n][k]
+};
+
+// Epilogue of the GEMM kernel family.
+enum Epi : int {
+  EPI_BF16 = 0,    // y = bf16(x . W^T)
+  EPI_LOGITS = 1,  // fp32 logits [m][n] + per-row-block maxima (verification pass 1)
+};
+
+struct GemmArgs {
+  const uint16_t* x;        // [m][k] BF16
+  const uint8_t* w;         // W12 tiles, or BF16 rows
+  const uint32_t* esc_off;  // [nb + 1]
+  const uint32_t* esc;      // [n_esc]
+  uint16_t* y;              // [m][n] BF16 (EPI_BF16)
+  float* logits;            // [m][n] (EPI_LOGITS)
+  float* rbmax_v;           // [m][nb] (EPI_LOGITS)
+  int32_t* rbmax_i;         // [m][nb] (EPI_LOGITS)
+  float* partial;           // [nsplit][m][n] split-K partial sums
+  uint32_t* counters;       // [n_rbg] split-K arrival tickets (zero between calls)
+  uint32_t m, n, k, g_cols, nb;
+  uint32_t nsplit, cols_per_split;
+  uint32_t lut[4];          // codebook bytes C[0..15] (SRC_LUT)
+  uint32_t basepair;        // C[0] | C[0] << 16 (SRC_RUN)
+};
+
+struct GemmPlan {
+  int rbw;                  // row-blocks per workgroup (1 or 2)
+  uint32_t nsplit;          // K splits across workgroups
+  uint32_t cols_per_split;  // tile columns per split
+  uint32_t n_rbg;           // row-block groups = ceil(nb / rbw)
+};
+
+// Launch one GEMM (kernel family chosen by m, src, epi and plan.rbw).
+hipError_t launch_gemm_run(const GemmArgs& a, int epi, const GemmPlan& p, hipStream_t s);
+hipError_t launch_gemm_lut(const GemmArgs& a, int epi, const GemmPlan& p, hipStream_t s);
+hipError_t launch_gemm_bf16_src(const GemmArgs& a, int epi, const GemmPlan& p, hipStream_t s);
+inline hipError_t launch_gemm(const GemmArgs& a, int src, int epi, const GemmPlan& p,
+                              hipStream_t s) {
+  if (src == SRC_RUN) return launch_gemm_run(a, epi, p, s);
+  if (src == SRC_LUT) return launch_gemm_lut(a, epi, p, s);
+  return launch_gemm_bf16_src(a, epi, p, s);
+}
+
+// Codec kernels.
+hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
+hipError_t launch_encode_hist(const uint16_t* w, uint64_t count, unsigned long long* hist,
+                              hipStream_t s);
+hipError_t launch_encode_codebook(const unsigned long long* hist, uint8_t* result,
+                                  hipStream_t s);
+struct Mask256 {
+  uint32_t m[8];
+};
+struct Codebook16 {
+  uint8_t c[16];
+};
+hipError_t launch_encode_count_tiles(const uint16_t* w, uint32_t nb, uint32_t g_cols,
+                                     const Mask256& member, uint32_t* tile_cnt, hipStream_t s);
+hipError_t launch_encode_scan(const uint32_t* tile_cnt, uint32_t n_tiles, uint32_t g_cols,
+                              uint32_t* tile_off, uint32_t* esc_off, uint32_t* total,
+                              hipStream_t s);
+hipError_t launch_encode_pack(const uint16_t* w, uint32_t nb, uint32_t g_cols,
+                              const Codebook16& cb, const uint32_t* tile_off,
+                              uint8_t* tiles, uint32_t* esc, uint64_t esc_cap,
+                              hipStream_t s);
+hipError_t launch_decode(const uint8_t* tiles, const uint32_t* esc_off, const uint32_t* esc,
+                         uint32_t nb, uint32_t g_cols, const Codebook16& cb,
+                         uint16_t* w_out, hipStream_t s);
+
+// Verification pass 2 (certified exact argmax) and accept.
+struct VerifyArgs {
+  const uint16_t* x;
+  const uint8_t* tiles;
+  const uint32_t* esc_off;
+  const uint32_t* esc;
+  const float* logits;      // [m][n]
+  const float* rbmax_v;     // [m][nb]
+  const int32_t* rbmax_i;   // [m][nb]
+  int32_t* cand;            // [m][n] candidate lists
+  int32_t* argmax;          // [m]
+  int32_t* ncand;           // [m] candidates recomputed exactly (diagnostic; may be NULL)
+  const int32_t* draft;
+  int32_t* accepted;
+  uint32_t m, n, k, g_cols, nb, n_draft;
+  uint32_t e_max;
+  uint32_t lut[4];
+};
+hipError_t launch_verify_pass2(const VerifyArgs& a, hipStream_t s);
+hipError_t launch_accept(const VerifyArgs& a, hipStream_t s);
+
+hipError_t launch_rms_rescale(const uint16_t* x, uint32_t m, uint32_t k, uint16_t* y,
+                              hipStream_t s);
+
+}  // namespace w12

@@ -1,0 +1,276 @@
+"""Thin Python binding of libw12.so (ctypes).
+
+Argument marshalling only: torch supplies device memory and the current HIP stream;
+every step of encode, decode, GEMM and verification runs in the library's HIP kernels.
+There is no CPU fallback: without the built library (or without a GPU) the calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from ctypes import c_int, c_int32, c_size_t, c_uint8, c_uint32, c_uint64, c_void_p
+from dataclasses import dataclass
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libw12.so")
+_LIB = None
+
+OP_ENCODE, OP_DECODE, OP_GEMM, OP_GEMM_BF16, OP_VERIFY = 0, 1, 2, 3, 4
+MAX_M = 32
+STATUS = {0: "W12_OK", -1: "W12_ERR_NULL", -2: "W12_ERR_SHAPE", -3: "W12_ERR_RANGE",
+          -4: "W12_ERR_FORMAT", -5: "W12_ERR_WORKSPACE", -6: "W12_ERR_HIP", -7: "W12_ERR_ALIGN"}
+EXPORTS = ("w12_tiles_bytes", "w12_workspace_bytes", "w12_workspace_init", "w12_encode_count",
+           "w12_encode", "w12_decode", "w12_gemm", "w12_gemm_bf16", "w12_lmhead_verify",
+           "w12_rms_rescale", "w12_status_str", "w12_version")
+
+
+class W12Error(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn} failed: {STATUS.get(status, status)} ({status_str(status)})")
+
+
+class W12Desc(ctypes.Structure):
+    _fields_ = [("n", c_uint64), ("k", c_uint64), ("n_esc", c_uint64),
+                ("codebook", c_uint8 * 16), ("e_max", c_uint8), ("reserved", c_uint8 * 7),
+                ("tiles", c_void_p), ("esc_off", c_void_p), ("esc", c_void_p)]
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def lib():
+    """Load libw12.so; raises if it has not been built (no silent fallback)."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(f"{_LIB_PATH} is not built; run "
+                               "`python -m lossless_bit_weight_w12_amd.build` first")
+        L = ctypes.CDLL(_LIB_PATH)
+        L.w12_tiles_bytes.restype = c_size_t
+        L.w12_tiles_bytes.argtypes = [c_uint64, c_uint64]
+        L.w12_workspace_bytes.restype = c_size_t
+        L.w12_workspace_bytes.argtypes = [c_int, c_uint32, c_uint64, c_uint64]
+        L.w12_workspace_init.restype = c_int32
+        L.w12_workspace_init.argtypes = [c_void_p, c_size_t, c_void_p]
+        L.w12_encode_count.restype = c_int32
+        L.w12_encode_count.argtypes = [c_void_p, c_uint64, c_uint64, c_void_p, c_void_p, c_void_p,
+                                       c_void_p, c_size_t, c_void_p]
+        L.w12_encode.restype = c_int32
+        L.w12_encode.argtypes = [c_void_p, ctypes.POINTER(W12Desc), c_void_p, c_size_t, c_void_p]
+        L.w12_decode.restype = c_int32
+        L.w12_decode.argtypes = [ctypes.POINTER(W12Desc), c_void_p, c_void_p]
+        L.w12_gemm.restype = c_int32
+        L.w12_gemm.argtypes = [c_void_p, c_uint32, ctypes.POINTER(W12Desc), c_void_p, c_void_p,
+                               c_size_t, c_void_p]
+        L.w12_gemm_bf16.restype = c_int32
+        L.w12_gemm_bf16.argtypes = [c_void_p, c_uint32, c_void_p, c_uint64, c_uint64, c_void_p,
+                                    c_void_p, c_size_t, c_void_p]
+        L.w12_lmhead_verify.restype = c_int32
+        L.w12_lmhead_verify.argtypes = [c_void_p, c_uint32, ctypes.POINTER(W12Desc), c_void_p,
+                                        c_uint32, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]
+        L.w12_rms_rescale.restype = c_int32
+        L.w12_rms_rescale.argtypes = [c_void_p, c_uint32, c_uint64, c_void_p, c_void_p]
+        L.w12_status_str.restype = ctypes.c_char_p
+        L.w12_status_str.argtypes = [c_int32]
+        L.w12_version.restype = c_uint32
+        L.w12_version.argtypes = []
+        _LIB = L
+    return _LIB
+
+
+def status_str(s: int) -> str:
+    return lib().w12_status_str(int(s)).decode()
+
+
+def _check(fn: str, st: int):
+    if st != 0:
+        raise W12Error(fn, st)
+
+
+def tiles_bytes(n: int, k: int) -> int:
+    return int(lib().w12_tiles_bytes(n, k))
+
+
+def workspace_bytes(op: int, m: int, n: int, k: int) -> int:
+    return int(lib().w12_workspace_bytes(op, m, n, k))
+
+
+# ----------------------------------------------------------------------------- torch glue
+def _torch():
+    import torch
+    return torch
+
+
+def _stream(dev):
+    return c_void_p(_torch().cuda.current_stream(dev).cuda_stream)
+
+
+def _ptr(t) -> c_void_p:
+    return c_void_p(t.data_ptr())
+
+
+def _as_bits(t):
+    """View a BF16 / int16 / uint16 CUDA tensor as 16-bit storage (no copy)."""
+    torch = _torch()
+    if not t.is_cuda:
+        raise ValueError("W12 calls need CUDA (HIP) tensors")
+    if t.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
+        raise ValueError(f"expected BF16 bits, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    return t
+
+
+_WS = {}
+
+
+def workspace(nbytes: int, device, purpose: str = "gemm"):
+    """A zero-initialised workspace of at least nbytes on `device`, cached per purpose
+    ("gemm" for both GEMM entry points, whose split-K counters the library leaves at
+    zero; "verify"; "encode"), grown on demand."""
+    torch = _torch()
+    dev = torch.device(device)
+    key = (dev.index if dev.index is not None else torch.cuda.current_device(), purpose)
+    buf = _WS.get(key)
+    if buf is None or buf.numel() < nbytes:
+        buf = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=dev)
+        _WS[key] = buf
+    return buf
+
+
+@dataclass
+class W12Tensor:
+    """A W12-encoded weight [n, k] resident on the GPU."""
+    n: int
+    k: int
+    n_esc: int
+    codebook: tuple
+    e_max: int
+    tiles: object      # torch.uint8 [tiles_bytes]
+    esc_off: object    # torch.int32 [n/16 + 1]
+    esc: object        # torch.int32 [max(n_esc, 1)]
+
+    def desc(self) -> W12Desc:
+        d = W12Desc()
+        d.n, d.k, d.n_esc = self.n, self.k, self.n_esc
+        for i, c in enumerate(self.codebook):
+            d.codebook[i] = c
+        d.e_max = self.e_max
+        d.tiles = self.tiles.data_ptr()
+        d.esc_off = self.esc_off.data_ptr()
+        d.esc = self.esc.data_ptr()
+        return d
+
+    @property
+    def device(self):
+        return self.tiles.device
+
+    def nbytes(self) -> int:
+        """Bytes of the format: tiles + escapes + offsets + the 64-byte header."""
+        return self.tiles.numel() + 4 * self.n_esc + 4 * (self.n // 16 + 1) + 64
+
+    def bits_per_weight(self) -> float:
+        return 8.0 * self.nbytes() / (self.n * self.k)
+
+
+def encode(w) -> W12Tensor:
+    """Encode BF16 weights w [n, k] (CUDA) to W12 on the same device."""
+    torch = _torch()
+    w = _as_bits(w)
+    n, k = w.shape
+    L = lib()
+    dev = w.device
+    ws = workspace(workspace_bytes(OP_ENCODE, 1, n, k), dev, "encode")
+    cb = (c_uint8 * 16)()
+    emax = c_uint8()
+    nesc = c_uint64()
+    s = _stream(dev)
+    _check("w12_encode_count", L.w12_encode_count(_ptr(w), n, k, ctypes.byref(cb), ctypes.byref(emax),
+                                                  ctypes.byref(nesc), _ptr(ws), ws.numel(), s))
+    t = W12Tensor(n=n, k=k, n_esc=int(nesc.value), codebook=tuple(cb), e_max=int(emax.value),
+                  tiles=torch.empty(tiles_bytes(n, k), dtype=torch.uint8, device=dev),
+                  esc_off=torch.empty(n // 16 + 1, dtype=torch.int32, device=dev),
+                  esc=torch.empty(max(int(nesc.value), 1), dtype=torch.int32, device=dev))
+    d = t.desc()
+    _check("w12_encode", L.w12_encode(_ptr(w), ctypes.byref(d), _ptr(ws), ws.numel(), s))
+    return t
+
+
+def decode(t: W12Tensor, out=None):
+    torch = _torch()
+    if out is None:
+        out = torch.empty((t.n, t.k), dtype=torch.bfloat16, device=t.device)
+    d = t.desc()
+    _check("w12_decode", lib().w12_decode(ctypes.byref(d), _ptr(_as_bits(out)), _stream(t.device)))
+    return out
+
+
+def gemm(x, t: W12Tensor, out=None):
+    """y = x . W^T, x BF16 [m, k] (m <= 32), y BF16 [m, n]."""
+    torch = _torch()
+    x = _as_bits(x)
+    m = x.shape[0]
+    if x.shape[1] != t.k:
+        raise ValueError(f"x has {x.shape[1]} columns, W has k = {t.k}")
+    if out is None:
+        out = torch.empty((m, t.n), dtype=torch.bfloat16, device=x.device)
+    ws = workspace(max(workspace_bytes(OP_GEMM, m, t.n, t.k), 256), x.device)
+    d = t.desc()
+    _check("w12_gemm", lib().w12_gemm(_ptr(x), m, ctypes.byref(d), _ptr(_as_bits(out)), _ptr(ws),
+                                      ws.numel(), _stream(x.device)))
+    return out
+
+
+def gemm_bf16(x, w, out=None):
+    """The same kernel family on plain BF16 weights w [n, k]."""
+    torch = _torch()
+    x = _as_bits(x)
+    w = _as_bits(w)
+    m = x.shape[0]
+    n, k = w.shape
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.bfloat16, device=x.device)
+    ws = workspace(max(workspace_bytes(OP_GEMM_BF16, m, n, k), 256), x.device)
+    _check("w12_gemm_bf16", lib().w12_gemm_bf16(_ptr(x), m, _ptr(w), n, k, _ptr(_as_bits(out)),
+                                                _ptr(ws), ws.numel(), _stream(x.device)))
+    return out
+
+
+def lmhead_verify(x, t: W12Tensor, draft, argmax_out=None, accepted_out=None):
+    """Exact-logit argmax per row (lowest index on ties) and accepted-prefix length."""
+    torch = _torch()
+    x = _as_bits(x)
+    m = x.shape[0]
+    if argmax_out is None:
+        argmax_out = torch.empty(m, dtype=torch.int32, device=x.device)
+    if accepted_out is None:
+        accepted_out = torch.empty(1, dtype=torch.int32, device=x.device)
+    n_draft = int(draft.numel())
+    ws = workspace(workspace_bytes(OP_VERIFY, m, t.n, t.k), x.device, "verify")
+    d = t.desc()
+    _check("w12_lmhead_verify", lib().w12_lmhead_verify(
+        _ptr(x), m, ctypes.byref(d), _ptr(draft) if n_draft else None, n_draft, _ptr(argmax_out),
+        _ptr(accepted_out), _ptr(ws), ws.numel(), _stream(x.device)))
+    return argmax_out, accepted_out
+
+
+def verify_candidates(t: W12Tensor, m: int):
+    """Per-row count of logits recomputed exactly by the last verification on this
+    device's workspace (diagnostic)."""
+    torch = _torch()
+    ws = workspace(workspace_bytes(OP_VERIFY, m, t.n, t.k), t.device, "verify")
+    nb = t.n // 16
+    a = lambda v: (v + 255) // 256 * 256
+    off = a(m * t.n * 4) + 2 * a(m * nb * 4) + a(m * t.n * 4)
+    return ws[off:off + 4 * m].view(torch.int32).clone()
+
+
+def rms_rescale(x, out=None):
+    torch = _torch()
+    x = _as_bits(x)
+    m, k = x.shape
+    if out is None:
+        out = torch.empty_like(x)
+    _check("w12_rms_rescale", lib().w12_rms_rescale(_ptr(x), m, k, _ptr(_as_bits(out)), _stream(x.device)))
+    return out

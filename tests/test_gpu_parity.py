@@ -1,0 +1,236 @@
+"""GPU parity of libw12.so against the CPU oracle, element by element, through the
+C ABI (via the thin binding).  Sizes span several tiles with ragged tails (odd
+row-block counts, tile columns not a multiple of the 4-column chunk), split-K shapes,
+both codebook paths (run and lookup table), escape-heavy matrices, every M in 1..32,
+and greedy verification with planted exact ties and 1-ulp pairs.
+
+Bars: encode bytes, decode bits, argmax and accepted length are bit-exact; GEMM
+outputs satisfy |y - z| <= 2e-3 * sum|x||w| + 1e-6 per element, or -- where one
+product dominates a row so that no BF16 value can -- are the BF16 rounding of a value
+within that tolerance (oracle.gemm_accept)."""
+import numpy as np
+import pytest
+
+from oracle import w12_oracle as o
+import w12_inputs as wi
+from gpu_util import narrow_exponents, say, to_dev, to_host, wide_exponents
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def env():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a visible MI355X"
+    import lossless_bit_weight_w12_amd as w12
+    w12.lib()
+    return torch, w12
+
+
+def matrices():
+    g = np.random.default_rng(2026)
+    yield "worked_example", __import__("test_oracle").worked_example_matrix()
+    yield "all_patterns", wi.all_bf16_patterns()
+    yield "gauss_48x384", wi.gaussian_bf16((48, 384), 0.02, g)
+    yield "gauss_272x1280", wi.gaussian_bf16((272, 1280), 0.02, g)
+    yield "bits_64x256", wi.random_bits((64, 256), g)
+    yield "narrow_32x128", narrow_exponents((32, 128), g)
+    yield "wide_48x640", wide_exponents((48, 640), g)
+    yield "outliers_320x640", wi.add_exponent_outliers(wi.gaussian_bf16((320, 640), 0.02, g), 0.01, 9)
+
+
+MATS = list(matrices())
+
+
+@pytest.mark.parametrize("name,w", MATS, ids=[m[0] for m in MATS])
+def test_encode_bytes_and_decode(env, name, w):
+    torch, w12 = env
+    say("encode/decode", name, w.shape)
+    ref = o.encode(w)
+    t = w12.encode(to_dev(w, torch))
+    torch.cuda.synchronize()
+    assert t.codebook == tuple(ref.codebook.tolist())
+    assert t.e_max == ref.e_max and t.n_esc == ref.n_esc
+    assert np.array_equal(t.tiles.cpu().numpy(), ref.tiles)
+    assert np.array_equal(t.esc_off.cpu().numpy().view(np.uint32), ref.esc_off)
+    assert np.array_equal(t.esc.cpu().numpy().view(np.uint32)[:ref.n_esc], ref.esc)
+    dec = w12.decode(t)
+    assert np.array_equal(to_host(dec), w)
+
+
+def _gemm_case(env, w, x, which):
+    torch, w12 = env
+    xt = to_dev(x, torch)
+    if which == "bf16":
+        y = w12.gemm_bf16(xt, to_dev(w, torch))
+    else:
+        t = w12.encode(to_dev(w, torch))
+        y = torch.full((x.shape[0], w.shape[0]), -1, dtype=torch.int16, device="cuda:0").view(torch.bfloat16)
+        w12.gemm(xt, t, out=y)
+    torch.cuda.synchronize()
+    z, s = o.gemm_reference(x, w)
+    yb = to_host(y)
+    ok = o.gemm_accept(yb, z, s)
+    bad = np.argwhere(~ok)
+    assert ok.all(), f"{bad.shape[0]} outside tolerance, first {bad[:4].tolist()} y={wi.bf16_bits_to_f32(yb[tuple(bad[0])])} z={z[tuple(bad[0])]}"
+    return yb
+
+
+# (n, k): ragged row-block counts, partial 4-column chunks, split-K, long K
+SHAPES = [(16, 128), (272, 1280), (48, 640), (64, 4096), (2080, 512)]
+
+
+@pytest.mark.parametrize("m", list(range(1, 33)))
+def test_gemm_all_m_run_codebook(env, m):
+    g = np.random.default_rng(1000 + m)
+    for n, k in SHAPES:
+        say("gemm run", m, n, k)
+        w = wi.gaussian_bf16((n, k), 0.02, g)
+        x = wi.gaussian_bf16((m, k), 1.0, g)
+        _gemm_case(env, w, x, "w12")
+
+
+@pytest.mark.parametrize("m", [1, 2, 3, 4, 7, 8, 9, 15, 16, 17, 24, 31, 32])
+def test_gemm_lut_codebook_and_escapes(env, m):
+    g = np.random.default_rng(2000 + m)
+    for n, k in [(48, 640), (320, 1280), (64, 4096)]:
+        say("gemm lut", m, n, k)
+        w = wide_exponents((n, k), g, 108, 132)
+        x = wi.gaussian_bf16((m, k), 1.0, g)
+        _gemm_case(env, w, x, "w12")
+        w2 = wi.add_exponent_outliers(wi.gaussian_bf16((n, k), 0.02, g), 0.01, 7)
+        _gemm_case(env, w2, x, "w12")
+
+
+@pytest.mark.parametrize("m", [1, 2, 4, 5, 8, 12, 15, 16, 20, 32])
+def test_gemm_bf16_baseline(env, m):
+    g = np.random.default_rng(3000 + m)
+    for n, k in SHAPES:
+        say("gemm bf16", m, n, k)
+        w = wi.gaussian_bf16((n, k), 0.02, g)
+        x = wi.gaussian_bf16((m, k), 1.0, g)
+        _gemm_case(env, w, x, "bf16")
+
+
+def test_gemm_deterministic_and_overwrites(env):
+    torch, w12 = env
+    g = np.random.default_rng(4)
+    for m, (n, k) in [(1, (64, 4096)), (8, (272, 1280)), (32, (2080, 512))]:
+        say("determinism", m, n, k)
+        w = wi.gaussian_bf16((n, k), 0.02, g)
+        x = wi.gaussian_bf16((m, k), 1.0, g)
+        t = w12.encode(to_dev(w, torch))
+        xt = to_dev(x, torch)
+        y1 = w12.gemm(xt, t)
+        y2 = torch.full_like(y1.view(torch.int16), -1).view(torch.bfloat16)
+        w12.gemm(xt, t, out=y2)
+        torch.cuda.synchronize()
+        assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+
+
+def test_gemm_nonfinite_propagates(env):
+    torch, w12 = env
+    g = np.random.default_rng(5)
+    w = wi.gaussian_bf16((32, 256), 0.02, g)
+    w[3, 7] = 0x7FC0          # NaN
+    w[9, 100] = 0x7F80        # +Inf
+    x = wi.gaussian_bf16((2, 256), 1.0, g)
+    y = to_host(w12.gemm(to_dev(x, torch), w12.encode(to_dev(w, torch))))
+    yf = wi.bf16_bits_to_f32(y)
+    assert np.isnan(yf[:, 3]).all() and np.isinf(yf[:, 9]).all()
+    finite_cols = [c for c in range(32) if c not in (3, 9)]
+    z, s = o.gemm_reference(x, w[finite_cols])
+    assert o.gemm_accept(y[:, finite_cols], z, s).all()
+
+
+# ----------------------------------------------------------------------------- verify
+def plant_pairs(x, w, rows, g):
+    """Plant near-ties for the given x rows: W[v2] := W[v1] (v1 = float64 argmax of the
+    row); for odd plants one weight of both rows is set to a tiny value and W[v2]'s copy
+    is moved by one BF16 ulp, so the two logits differ by |x_k| * 2^-27-ish, far below
+    one FP32 ulp of the logit.  The expected answers are recomputed by the oracle."""
+    w = w.copy()
+    n = w.shape[0]
+    for idx, m in enumerate(rows):
+        z, _ = o.gemm_reference(x[m:m + 1], w)
+        v1 = int(np.argmax(z[0]))
+        v2 = int(g.integers(0, n - 1))
+        v2 = v2 + 1 if v2 >= v1 else v2
+        w[v2] = w[v1]
+        if idx % 2 == 1:
+            kk = int(g.integers(0, w.shape[1]))
+            tiny = (int(g.integers(0, 2)) << 15) | (107 << 7) | int(g.integers(1, 127))
+            w[v1, kk] = tiny
+            w[v2, kk] = tiny + (1 if g.integers(0, 2) else -1)
+    return w
+
+
+@pytest.mark.parametrize("m", [1, 2, 7, 15, 16, 24, 32])
+def test_verify_matches_oracle(env, m):
+    torch, w12 = env
+    g = np.random.default_rng(5000 + m)
+    n, k = 4096, 512
+    x = wi.gaussian_bf16((m, k), 1.0, g)
+    w = wi.gaussian_bf16((n, k), 0.02, g)
+    w = plant_pairs(x, w, list(range(m)), g)
+    say("verify", m, n, k)
+    am_ref, ncand = o.argmax_exact(x, w)
+    t = w12.encode(to_dev(w, torch))
+    xt = to_dev(x, torch)
+    for p in sorted({0, m // 2, m}):
+        draft = am_ref.copy().astype(np.int32)
+        if p < m:
+            draft[p] = (draft[p] + 1 + int(g.integers(0, n - 1))) % n
+        am, acc = w12.lmhead_verify(xt, t, torch.from_numpy(draft).to("cuda:0"))
+        torch.cuda.synchronize()
+        assert am.cpu().numpy().tolist() == am_ref.tolist()
+        assert int(acc.item()) == o.accepted_length(am_ref, draft) == p
+    nc = w12.verify_candidates(t, m).cpu().numpy()
+    assert (nc >= 1).all()
+
+
+def test_verify_exact_tie_lowest_index_and_escapes(env):
+    """Rows tie exactly (copies), the head is escape-heavy (lookup-table codebook)."""
+    torch, w12 = env
+    g = np.random.default_rng(6)
+    n, k, m = 1024, 640, 5
+    w = wide_exponents((n, k), g, 100, 126)
+    x = wi.gaussian_bf16((m, k), 1.0, g)
+    z, _ = o.gemm_reference(x, w)
+    for mi in range(m):
+        v1 = int(np.argmax(z[mi]))
+        w[(v1 * 7 + 3) % n] = w[v1]
+    am_ref, _ = o.argmax_exact(x, w)
+    t = w12.encode(to_dev(w, torch))
+    say("verify ties", n, k, m, "codebook", t.codebook)
+    draft = am_ref.astype(np.int32)
+    am, acc = w12.lmhead_verify(to_dev(x, torch), t, torch.from_numpy(draft).to("cuda:0"))
+    torch.cuda.synchronize()
+    assert am.cpu().numpy().tolist() == am_ref.tolist()
+    assert int(acc.item()) == m
+
+
+def test_verify_nonfinite_row_reports_minus_one(env):
+    torch, w12 = env
+    g = np.random.default_rng(7)
+    w = wi.gaussian_bf16((256, 256), 0.02, g)
+    x = wi.gaussian_bf16((3, 256), 1.0, g)
+    x[1, 5] = 0x7F80
+    am, acc = w12.lmhead_verify(to_dev(x, torch), w12.encode(to_dev(w, torch)),
+                                torch.zeros(0, dtype=torch.int32, device="cuda:0"))
+    torch.cuda.synchronize()
+    ref, _ = o.argmax_exact(x[[0, 2]], w)
+    got = am.cpu().numpy()
+    assert got[1] == -1 and got[0] == ref[0] and got[2] == ref[1]
+    assert int(acc.item()) == 0
+
+
+def test_rms_rescale(env):
+    torch, w12 = env
+    g = np.random.default_rng(8)
+    x = wi.gaussian_bf16((24, 5120), 3.0, g)
+    y = to_host(w12.rms_rescale(to_dev(x, torch)))
+    yf = wi.bf16_bits_to_f32(y).astype(np.float64)
+    xf = wi.bf16_bits_to_f32(x).astype(np.float64)
+    ref = xf / np.sqrt(np.mean(xf * xf, axis=1, keepdims=True))
+    assert np.all(np.abs(yf - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-30)

@@ -1,0 +1,141 @@
+"""Host-side checks of libw12.so that need no GPU: it builds for gfx950, loads, exports
+every symbol include/w12.h declares, and rejects bad arguments before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import lossless_bit_weight_w12_amd as w12
+from lossless_bit_weight_w12_amd import w12 as B
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "w12.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(w12.lib_path()):
+        from lossless_bit_weight_w12_amd import build
+        build.build(verbose=False)
+    return w12.lib()
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(w12_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol(L):
+    names = declared_functions()
+    assert set(names) == set(B.EXPORTS)
+    for nm in names:
+        assert hasattr(L, nm), nm
+
+
+def test_status_strings(L):
+    for code in range(-7, 1):
+        assert w12.status_str(code) and w12.status_str(code) != "unknown status"
+    assert w12.status_str(-99) == "unknown status"
+    assert L.w12_version() == 0x000100
+
+
+@pytest.mark.parametrize("n,k", [(16, 128), (1024, 1024), (151936, 5120), (5120, 17408)])
+def test_tiles_bytes_closed_form(L, n, k):
+    assert w12.tiles_bytes(n, k) == (n // 16) * (k // 128) * 3072 == 3 * 2 * n * k // 4
+
+
+@pytest.mark.parametrize("n,k", [(0, 128), (15, 128), (16, 100), (16, 1 << 20), (17, 128)])
+def test_bad_shapes_report_zero(L, n, k):
+    assert w12.tiles_bytes(n, k) == 0
+    assert w12.workspace_bytes(w12.OP_GEMM, 1, n, k) == 0
+
+
+def test_workspace_sizes(L):
+    assert w12.workspace_bytes(w12.OP_GEMM, 0, 1024, 1024) == 0
+    assert w12.workspace_bytes(w12.OP_GEMM, 33, 1024, 1024) == 0
+    assert w12.workspace_bytes(99, 1, 1024, 1024) == 0
+    n, k, m = 151936, 5120, 16
+    v = w12.workspace_bytes(w12.OP_VERIFY, m, n, k)
+    assert v >= 4 * m * n * 2 + 8 * m * (n // 16)
+    assert w12.workspace_bytes(w12.OP_ENCODE, 1, n, k) >= 8 * (n // 16) * (k // 128)
+
+
+FAKE = 0x10000          # non-null, 256-byte aligned, never dereferenced (validation fails first)
+
+
+def desc(n=1024, k=1024, cb=tuple(range(100, 116)), e_max=120, n_esc=0):
+    d = B.W12Desc()
+    d.n, d.k, d.n_esc = n, k, n_esc
+    for i, c in enumerate(cb):
+        d.codebook[i] = c
+    d.e_max = e_max
+    d.tiles = FAKE
+    d.esc_off = FAKE
+    d.esc = FAKE if n_esc else None
+    return d
+
+
+def gemm(L, x=FAKE, m=1, d=None, y=FAKE, ws=FAKE, wsb=1 << 30):
+    d = d or desc()
+    return L.w12_gemm(x, m, ctypes.byref(d), y, ws, wsb, None)
+
+
+def test_gemm_validation(L):
+    assert gemm(L, x=None) == -1
+    assert gemm(L, y=None) == -1
+    assert L.w12_gemm(FAKE, 1, None, FAKE, FAKE, 1 << 30, None) == -1
+    assert gemm(L, d=desc(n=1000)) == -2
+    assert gemm(L, d=desc(k=1000)) == -2
+    assert gemm(L, d=desc(k=1 << 20)) == -2
+    assert gemm(L, m=0) == -3
+    assert gemm(L, m=33) == -3
+    assert gemm(L, d=desc(cb=(5,) * 16)) == -4
+    assert gemm(L, d=desc(cb=tuple(range(115, 99, -1)))) == -4
+    assert gemm(L, d=desc(e_max=255)) == -4
+    bad = desc(n_esc=4)
+    bad.esc = None
+    assert gemm(L, d=bad) == -1
+    assert gemm(L, m=16, wsb=0, d=desc(n=64, k=4096)) == -5     # split-K needs partials
+    assert gemm(L, x=FAKE + 2) == -7
+    assert gemm(L, ws=FAKE + 16) == -7
+    mis = desc()
+    mis.tiles = FAKE + 4
+    assert gemm(L, d=mis) == -7
+
+
+def test_gemm_bf16_validation(L):
+    f = L.w12_gemm_bf16
+    assert f(None, 1, FAKE, 1024, 1024, FAKE, FAKE, 1 << 30, None) == -1
+    assert f(FAKE, 1, FAKE, 1000, 1024, FAKE, FAKE, 1 << 30, None) == -2
+    assert f(FAKE, 40, FAKE, 1024, 1024, FAKE, FAKE, 1 << 30, None) == -3
+    assert f(FAKE, 1, FAKE + 8, 1024, 1024, FAKE, FAKE, 1 << 30, None) == -7
+
+
+def test_verify_validation(L):
+    f = L.w12_lmhead_verify
+    d = desc(n=2048, k=512)
+    big = 1 << 34
+    assert f(FAKE, 4, ctypes.byref(d), FAKE, 4, None, FAKE, FAKE, big, None) == -1
+    assert f(FAKE, 4, ctypes.byref(d), None, 2, FAKE, FAKE, FAKE, big, None) == -1
+    assert f(FAKE, 4, ctypes.byref(d), FAKE, 5, FAKE, FAKE, FAKE, big, None) == -3   # n_draft > m
+    assert f(FAKE, 0, ctypes.byref(d), FAKE, 0, FAKE, FAKE, FAKE, big, None) == -3
+    assert f(FAKE, 4, ctypes.byref(d), FAKE, 4, FAKE, FAKE, FAKE, 100, None) == -5
+
+
+def test_encode_decode_validation(L):
+    cb = (ctypes.c_uint8 * 16)()
+    em = ctypes.c_uint8()
+    ne = ctypes.c_uint64()
+    f = L.w12_encode_count
+    assert f(None, 16, 128, cb, ctypes.byref(em), ctypes.byref(ne), FAKE, 1 << 20, None) == -1
+    assert f(FAKE, 16, 100, cb, ctypes.byref(em), ctypes.byref(ne), FAKE, 1 << 20, None) == -2
+    assert f(FAKE, 16, 128, cb, ctypes.byref(em), ctypes.byref(ne), FAKE, 16, None) == -5
+    assert f(FAKE + 2, 16, 128, cb, ctypes.byref(em), ctypes.byref(ne), FAKE, 1 << 20, None) == -7
+    d = desc()
+    assert L.w12_encode(FAKE, ctypes.byref(d), FAKE, 16, None) == -5
+    assert L.w12_encode(None, ctypes.byref(d), FAKE, 1 << 30, None) == -1
+    assert L.w12_decode(ctypes.byref(desc(k=100)), FAKE, None) == -2
+    assert L.w12_decode(ctypes.byref(desc()), None, None) == -1
+    assert L.w12_rms_rescale(FAKE, 0, 128, FAKE, None) == -3
+    assert L.w12_workspace_init(None, 64, None) == -1
