@@ -44,9 +44,9 @@
  *  - Arguments are validated on the host before any HIP call; on error nothing is
  *    launched and outputs are untouched.  Launch failures return W12_ERR_HIP; device
  *    faults surface at the caller's next synchronisation.
- *  - The workspace `ws` (device, w12_workspace_bytes(op, ...) bytes, 256-byte aligned)
- *    must be zero-filled once before its first use (w12_workspace_init does that on
- *    the stream); every call leaves its counters zero again.  Two calls that run
+ *  - The workspace `ws` (device, w12_workspace_bytes(op, ...) bytes, 256-byte aligned;
+ *    may be NULL when that size is 0) holds intermediate results only: its contents
+ *    need no initialisation and are not meaningful after the call.  Two calls that run
  *    concurrently must not share a workspace.
  */
 #ifndef W12_H
@@ -96,11 +96,14 @@ typedef struct w12_desc {
 size_t w12_tiles_bytes(uint64_t n, uint64_t k);
 
 /* Workspace bytes needed by `op` for m rows (ignored by ENCODE/DECODE) and an
- * n x k weight; 0 for an invalid op or shape.  Never more than a few MB except
- * VERIFY, which holds FP32 logits [m][n] plus per-row-block maxima. */
+ * n x k weight; 0 for an invalid op or shape, and 0 when the op needs none (DECODE,
+ * and GEMM shapes that are not split along K).  GEMM split along K needs FP32
+ * partials [splits][m][n]; VERIFY holds FP32 logits [m][n] plus per-row-block maxima
+ * and candidate lists; ENCODE holds the histogram and per-tile escape counts. */
 size_t w12_workspace_bytes(int op, uint32_t m, uint64_t n, uint64_t k);
 
-/* Zero-fills `ws` on `stream` with a kernel (no hipMemset). */
+/* Zero-fills `ws` on `stream` with a kernel (no hipMemset); a convenience, no call
+ * requires a zeroed workspace. */
 w12_status w12_workspace_init(void* ws, size_t ws_bytes, void* stream);
 
 /* Encode, first half (exponent histogram -> codebook, e_max, n_esc).

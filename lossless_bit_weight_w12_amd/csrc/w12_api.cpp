@@ -62,9 +62,7 @@ GemmPlan make_plan(uint64_t n, uint64_t k, int epi) {
 
 size_t gemm_ws_bytes(uint32_t m, uint64_t n, uint64_t k) {
   const GemmPlan p = make_plan(n, k, EPI_BF16);
-  size_t b = align256((size_t)p.n_rbg * 4);
-  if (p.nsplit > 1) b += align256((size_t)p.nsplit * m * n * 4);
-  return b;
+  return p.nsplit > 1 ? align256((size_t)p.nsplit * m * n * 4) : 0;
 }
 
 struct VerifyLayout {
@@ -207,11 +205,13 @@ w12_status w12_decode(const w12_desc* d, uint16_t* w_out, void* stream) {
 
 w12_status w12_gemm(const uint16_t* x, uint32_t m, const w12_desc* d, uint16_t* y, void* ws,
                     size_t ws_bytes, void* stream) {
-  if (!x || !y || !ws) return W12_ERR_NULL;
+  if (!x || !y) return W12_ERR_NULL;
   w12_status st = check_desc(d, true);
   if (st != W12_OK) return st;
   if (m < 1 || m > W12_MAX_M) return W12_ERR_RANGE;
-  if (ws_bytes < gemm_ws_bytes(m, d->n, d->k)) return W12_ERR_WORKSPACE;
+  const size_t need = gemm_ws_bytes(m, d->n, d->k);
+  if (ws_bytes < need) return W12_ERR_WORKSPACE;
+  if (need > 0 && !ws) return W12_ERR_NULL;
   if (!aligned(x, 16) || !aligned(y, 4) || !aligned(ws, 256)) return W12_ERR_ALIGN;
   const GemmPlan p = make_plan(d->n, d->k, EPI_BF16);
   GemmArgs a;
@@ -221,15 +221,12 @@ w12_status w12_gemm(const uint16_t* x, uint32_t m, const w12_desc* d, uint16_t* 
   a.esc_off = d->esc_off;
   a.esc = d->esc;
   a.y = y;
-  a.counters = (uint32_t*)ws;
-  a.partial = (float*)((uint8_t*)ws + align256((size_t)p.n_rbg * 4));
+  a.partial = (float*)ws;
   a.m = m;
   a.n = (uint32_t)d->n;
   a.k = (uint32_t)d->k;
   a.g_cols = (uint32_t)(d->k / 128);
   a.nb = (uint32_t)(d->n / 16);
-  a.nsplit = p.nsplit;
-  a.cols_per_split = p.cols_per_split;
   fill_args_codebook(a, d);
   const int src = codebook_is_run(d->codebook) ? SRC_RUN : SRC_LUT;
   return hip_status(launch_gemm(a, src, EPI_BF16, p, (hipStream_t)stream));
@@ -237,10 +234,12 @@ w12_status w12_gemm(const uint16_t* x, uint32_t m, const w12_desc* d, uint16_t* 
 
 w12_status w12_gemm_bf16(const uint16_t* x, uint32_t m, const uint16_t* w, uint64_t n,
                          uint64_t k, uint16_t* y, void* ws, size_t ws_bytes, void* stream) {
-  if (!x || !w || !y || !ws) return W12_ERR_NULL;
+  if (!x || !w || !y) return W12_ERR_NULL;
   if (!shape_ok(n, k)) return W12_ERR_SHAPE;
   if (m < 1 || m > W12_MAX_M) return W12_ERR_RANGE;
-  if (ws_bytes < gemm_ws_bytes(m, n, k)) return W12_ERR_WORKSPACE;
+  const size_t need = gemm_ws_bytes(m, n, k);
+  if (ws_bytes < need) return W12_ERR_WORKSPACE;
+  if (need > 0 && !ws) return W12_ERR_NULL;
   if (!aligned(x, 16) || !aligned(w, 16) || !aligned(y, 4) || !aligned(ws, 256)) return W12_ERR_ALIGN;
   const GemmPlan p = make_plan(n, k, EPI_BF16);
   GemmArgs a;
@@ -248,15 +247,12 @@ w12_status w12_gemm_bf16(const uint16_t* x, uint32_t m, const uint16_t* w, uint6
   a.x = x;
   a.w = (const uint8_t*)w;
   a.y = y;
-  a.counters = (uint32_t*)ws;
-  a.partial = (float*)((uint8_t*)ws + align256((size_t)p.n_rbg * 4));
+  a.partial = (float*)ws;
   a.m = m;
   a.n = (uint32_t)n;
   a.k = (uint32_t)k;
   a.g_cols = (uint32_t)(k / 128);
   a.nb = (uint32_t)(n / 16);
-  a.nsplit = p.nsplit;
-  a.cols_per_split = p.cols_per_split;
   return hip_status(launch_gemm(a, SRC_BF16, EPI_BF16, p, (hipStream_t)stream));
 }
 
@@ -289,8 +285,6 @@ w12_status w12_lmhead_verify(const uint16_t* x, uint32_t m, const w12_desc* d, c
   a.k = (uint32_t)d->k;
   a.g_cols = (uint32_t)(d->k / 128);
   a.nb = (uint32_t)(d->n / 16);
-  a.nsplit = 1;
-  a.cols_per_split = p.cols_per_split;
   fill_args_codebook(a, d);
   const int src = codebook_is_run(d->codebook) ? SRC_RUN : SRC_LUT;
   hipError_t e = launch_gemm(a, src, EPI_LOGITS, p, s);

@@ -46,6 +46,14 @@ constexpr int kChunk = 4;                        // tile columns per LDS x chunk
 constexpr int kXsStride = kChunk * 128 + 8;      // BF16 per LDS row (+16 B pad: no bank
                                                  // conflicts for the MFMA B reads)
 
+// Scalar parameters of one GEMM launch.
+struct GemmParams {
+  uint32_t m, n, k, g_cols, nb;
+  uint32_t cols_per_split;
+  uint32_t lut[4];
+  uint32_t basepair;
+};
+
 // BF16 pair view of a 32-bit word.  Taken by value on purpose: this compiler
 // miscompiles __builtin_bit_cast applied directly to an ext-vector element (it reads
 // element 0 whatever the index), so vector elements must pass through a scalar first.
@@ -81,15 +89,15 @@ struct TileRegs {
 };
 
 template <int SRC>
-__device__ __forceinline__ void load_tile(TileRegs<SRC>& t, const GemmArgs& a, uint32_t b,
-                                          uint32_t g, int lane) {
+__device__ __forceinline__ void load_tile(TileRegs<SRC>& t, const uint8_t* __restrict__ w,
+                                          const GemmParams& p, uint32_t b, uint32_t g, int lane) {
   if constexpr (SRC == SRC_BF16) {
     const int r = lane & 15, q = lane >> 4;
-    const uint8_t* base = a.w + ((size_t)(16u * b + r) * a.k + 128u * g + 8u * q) * 2u;
+    const uint8_t* base = w + ((size_t)(16u * b + r) * p.k + 128u * g + 8u * q) * 2u;
 #pragma unroll
     for (int j = 0; j < 4; ++j) t.v[j] = *reinterpret_cast<const u32x4*>(base + 64 * j);
   } else {
-    const uint8_t* base = a.w + ((size_t)b * a.g_cols + g) * 3072u + (uint32_t)lane * 16u;
+    const uint8_t* base = w + ((size_t)b * p.g_cols + g) * 3072u + (uint32_t)lane * 16u;
 #pragma unroll
     for (int s = 0; s < 3; ++s) t.v[s] = *reinterpret_cast<const u32x4*>(base + 1024 * s);
   }
@@ -97,7 +105,7 @@ __device__ __forceinline__ void load_tile(TileRegs<SRC>& t, const GemmArgs& a, u
 
 // Registers -> 16 BF16 pairs (P[4j+p] = element 2p in the low half, 2p+1 in the high).
 template <int SRC>
-__device__ __forceinline__ void unpack_tile(const TileRegs<SRC>& t, const GemmArgs& a,
+__device__ __forceinline__ void unpack_tile(const TileRegs<SRC>& t, const GemmParams& a,
                                             uint32_t P[16]) {
   if constexpr (SRC == SRC_BF16) {
 #pragma unroll
@@ -134,30 +142,47 @@ __device__ __forceinline__ void unpack_tile(const TileRegs<SRC>& t, const GemmAr
   }
 }
 
-// Escape cursor of one row-block: records [pos, end) not yet consumed; lane i of `win`
-// holds record wb + i.
+// Escape cursor of one row-block, wave-uniform (scalar registers): records [pos, end)
+// not yet consumed; `next` is record pos (or a sentinel whose column is past any K).
 struct EscCursor {
-  uint32_t pos, end, wb, win;
+  uint32_t pos, end, next;
 };
 
-__device__ __forceinline__ void esc_load_window(EscCursor& c, const uint32_t* esc, int lane) {
-  c.wb = c.pos;
-  const uint32_t idx = c.pos + (uint32_t)lane;
-  c.win = (idx < c.end) ? esc[idx] : 0xFFFFFFFFu;
+constexpr uint32_t kEscSentinel = 0xFFFFFFFFu;
+
+__device__ __forceinline__ uint32_t esc_col(uint32_t rec) { return (rec >> 8) & 0xFFFFFu; }
+
+// Escape records are read-only for the whole launch and addressed uniformly: reading
+// them through the constant address space makes them scalar (SMEM) loads, which do not
+// share the vector-memory counter with the tile prefetch.
+typedef const __attribute__((address_space(4))) uint32_t* const_u32_ptr;
+
+__device__ __forceinline__ uint32_t sload(const uint32_t* p, uint32_t i) {
+  return ((const_u32_ptr)p)[i];
 }
 
-// Position the cursor at the first record with column >= kmin.
-__device__ __forceinline__ void esc_seek(EscCursor& c, const uint32_t* esc, uint32_t kmin,
-                                         int lane) {
-  for (;;) {
-    esc_load_window(c, esc, lane);
-    if (kmin == 0u || c.pos >= c.end) return;
-    const uint32_t kk = (c.win >> 8) & 0xFFFFFu;
-    const bool below = (c.wb + (uint32_t)lane < c.end) && kk < kmin;
-    const uint32_t nbelow = (uint32_t)__builtin_popcountll(__builtin_amdgcn_ballot_w64(below));
-    c.pos += nbelow;
-    if (nbelow < 64u) return;
+__device__ __forceinline__ uint32_t esc_fetch(const uint32_t* __restrict__ esc, uint32_t pos,
+                                              uint32_t end) {
+  return pos < end ? sload(esc, pos) : kEscSentinel;
+}
+
+// Start the cursor at the first record of row-block b with column >= kmin (binary
+// search over the row-block's records, which are sorted by column).
+__device__ __forceinline__ void esc_begin(EscCursor& c, const uint32_t* __restrict__ esc_off,
+                                          const uint32_t* __restrict__ esc, uint32_t b,
+                                          uint32_t kmin) {
+  uint32_t lo = sload(esc_off, b);
+  const uint32_t end = sload(esc_off, b + 1);
+  if (kmin > 0u) {
+    uint32_t hi = end;
+    while (lo < hi) {
+      const uint32_t mid = lo + ((hi - lo) >> 1);
+      if (esc_col(sload(esc, mid)) < kmin) lo = mid + 1; else hi = mid;
+    }
   }
+  c.pos = lo;
+  c.end = end;
+  c.next = esc_fetch(esc, lo, end);
 }
 
 __device__ __forceinline__ void patch_pair(uint32_t P[16], uint32_t pi, uint32_t sh, uint32_t e,
@@ -172,30 +197,22 @@ __device__ __forceinline__ void patch_pair(uint32_t P[16], uint32_t pi, uint32_t
   }
 }
 
-// Patch the escapes of tile column g into P (records sorted by column, then row).
-__device__ __forceinline__ void esc_apply(EscCursor& c, const uint32_t* esc, uint32_t g,
-                                          int lane, uint32_t P[16]) {
-  if (c.pos >= c.end) return;
+// Patch the escapes of tile column g into P.  Records of columns below g (other
+// waves' columns) are skipped; the cursor stops at the first record past the tile.
+__device__ __forceinline__ void esc_apply(EscCursor& c, const uint32_t* __restrict__ esc,
+                                          uint32_t g, int lane, uint32_t P[16]) {
   const uint32_t klo = g * 128u, khi = klo + 128u;
-  for (;;) {
-    const uint32_t li = c.pos - c.wb;
-    const uint32_t kk = (c.win >> 8) & 0xFFFFFu;
-    const bool valid = ((uint32_t)lane >= li) && (c.wb + (uint32_t)lane < c.end);
-    const uint64_t below = __builtin_amdgcn_ballot_w64(valid && kk < khi);
-    uint64_t hit = __builtin_amdgcn_ballot_w64(valid && kk >= klo && kk < khi);
-    while (hit) {
-      const int bit = __builtin_ctzll(hit);
-      hit &= hit - 1;
-      const uint32_t rec = __builtin_amdgcn_readlane(c.win, bit);
+  while (esc_col(c.next) < khi) {
+    const uint32_t rec = c.next;
+    if (esc_col(rec) >= klo) {
       const uint32_t rr = rec >> 28;
-      const uint32_t kap = ((rec >> 8) & 0xFFFFFu) - klo;
+      const uint32_t kap = esc_col(rec) - klo;
       const uint32_t j = kap >> 5, qq = (kap >> 3) & 3u, i = kap & 7u;
-      const uint32_t owner = 16u * qq + rr;
-      patch_pair(P, 4u * j + (i >> 1), 7u + 16u * (i & 1u), rec & 0xFFu, (uint32_t)lane == owner);
+      patch_pair(P, 4u * j + (i >> 1), 7u + 16u * (i & 1u), rec & 0xFFu,
+                 (uint32_t)lane == 16u * qq + rr);
     }
-    c.pos += (uint32_t)__builtin_popcountll(below);
-    if (c.pos >= c.end || c.pos - c.wb < 64u) return;
-    esc_load_window(c, esc, lane);   // window used up: the next records may still be < khi
+    ++c.pos;
+    c.next = esc_fetch(esc, c.pos, c.end);
   }
 }
 
@@ -205,17 +222,22 @@ struct XStage {
   u32x4 v[kUnits];
 };
 
+// Every thread issues the same loads on every path (addresses clamped into range,
+// out-of-range units zeroed after the load), so the compiler's wait counts stay exact.
 template <int MT>
-__device__ __forceinline__ void x_load(XStage<MT>& st, const GemmArgs& a, uint32_t m_rows,
-                                       uint32_t c0, uint32_t gb, int tid) {
+__device__ __forceinline__ void x_load(XStage<MT>& st, const uint16_t* __restrict__ x,
+                                       uint32_t k, uint32_t m_rows, uint32_t c0, uint32_t gb,
+                                       int tid) {
 #pragma unroll
   for (int i = 0; i < XStage<MT>::kUnits; ++i) {
     const uint32_t u = (uint32_t)tid + kThreads * i;
-    const uint32_t m = u >> 6, cu = u & 63u;
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (u < MT * 64u && m < m_rows && c0 + (cu >> 4) < gb)
-      v = *reinterpret_cast<const u32x4*>(a.x + (size_t)m * a.k + 128u * c0 + 8u * cu);
-    st.v[i] = v;
+    const uint32_t uu = u < MT * 64u ? u : u % (MT * 64u);
+    const uint32_t m = uu >> 6, cu = uu & 63u;
+    const uint32_t col = c0 + (cu >> 4);
+    const bool ok = m < m_rows && col < gb;
+    const uint32_t ml = min(m, m_rows - 1u), cl = min(col, gb - 1u);
+    const u32x4 v = *reinterpret_cast<const u32x4*>(x + (size_t)ml * k + 128u * cl + 8u * (cu & 15u));
+    st.v[i] = ok ? v : u32x4{0u, 0u, 0u, 0u};
   }
 }
 
@@ -232,20 +254,27 @@ __device__ __forceinline__ void x_store(const XStage<MT>& st, uint16_t* xs, int 
 }
 
 // M: rows for the VALU path (compile-time); MT: LDS rows (= M, or 16/32 for MFMA).
+// EPI_BF16 with gridDim.y > 1 writes FP32 partials [split][m][n] (reduced by
+// k_splitk_reduce); with one split it writes y directly.
 template <int M, int MT, bool MF, int RBW, int SRC, int EPI>
-__global__ __launch_bounds__(kThreads) void k_gemm(GemmArgs a) {
+__global__ __launch_bounds__(kThreads) void k_gemm(
+    const uint16_t* __restrict__ x, const uint8_t* __restrict__ w,
+    const uint32_t* __restrict__ esc_off, const uint32_t* __restrict__ esc,
+    uint16_t* __restrict__ y, float* __restrict__ out_f32, float* __restrict__ rbmax_v,
+    int32_t* __restrict__ rbmax_i, GemmParams p) {
   constexpr int NH = MF ? MT / 16 : 1;
   __shared__ __align__(16) uint16_t xs[MT * kXsStride];
-  __shared__ float fin[RBW * MT * 16];
-  __shared__ uint32_t s_last;
+  __shared__ float fin[EPI == EPI_LOGITS ? RBW * MT * 16 : 1];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform, in an SGPR
   const int r = lane & 15, q = lane >> 4;
   const uint32_t rbg = blockIdx.x, split = blockIdx.y;
   const uint32_t b0 = rbg * RBW;
-  const uint32_t ga = split * a.cols_per_split;
-  const uint32_t gb = min(a.g_cols, ga + a.cols_per_split);
-  const uint32_t m_rows = MF ? a.m : (uint32_t)M;
+  const uint32_t ga = split * p.cols_per_split;
+  const uint32_t gb = min(p.g_cols, ga + p.cols_per_split);
+  const uint32_t m_rows = MF ? p.m : (uint32_t)M;
+  const uint32_t nchunks = (gb - ga + kChunk - 1) / kChunk;
 
   float vacc[RBW][MF ? 1 : M];
   f32x4 macc[RBW][NH];
@@ -260,37 +289,28 @@ __global__ __launch_bounds__(kThreads) void k_gemm(GemmArgs a) {
   EscCursor ec[RBW];
   if constexpr (SRC != SRC_BF16) {
 #pragma unroll
-    for (int rb = 0; rb < RBW; ++rb) {
-      const uint32_t b = b0 + rb;
-      if (b < a.nb) {
-        ec[rb].pos = __builtin_amdgcn_readfirstlane(a.esc_off[b]);
-        ec[rb].end = __builtin_amdgcn_readfirstlane(a.esc_off[b + 1]);
-        esc_seek(ec[rb], a.esc, ga * 128u, lane);
-      } else {
-        ec[rb].pos = ec[rb].end = ec[rb].wb = 0u;
-        ec[rb].win = 0xFFFFFFFFu;
-      }
-    }
+    for (int rb = 0; rb < RBW; ++rb) esc_begin(ec[rb], esc_off, esc, min(b0 + rb, p.nb - 1u), ga * 128u);
   }
 
   TileRegs<SRC> tA[RBW], tB[RBW];
   XStage<MT> xr;
 
-  auto load_tiles = [&](TileRegs<SRC>* t, uint32_t g) {
-    if (g < gb) {
+  auto load_tiles = [&](TileRegs<SRC>* t, uint32_t c) {
+    const uint32_t g = min(c + (uint32_t)wave, gb - 1u);
 #pragma unroll
-      for (int rb = 0; rb < RBW; ++rb)
-        if (b0 + rb < a.nb) load_tile<SRC>(t[rb], a, b0 + rb, g, lane);
-    }
+    for (int rb = 0; rb < RBW; ++rb) load_tile<SRC>(t[rb], w, p, min(b0 + rb, p.nb - 1u), g, lane);
   };
 
-  auto compute = [&](const TileRegs<SRC>* t, uint32_t g) {
+  auto compute = [&](const TileRegs<SRC>* t, uint32_t c) {
+    const uint32_t g = c + (uint32_t)wave;
     if (g >= gb) return;
     uint32_t P[RBW][16];
 #pragma unroll
     for (int rb = 0; rb < RBW; ++rb) {
-      unpack_tile<SRC>(t[rb], a, P[rb]);
-      if constexpr (SRC != SRC_BF16) esc_apply(ec[rb], a.esc, g, lane, P[rb]);
+      unpack_tile<SRC>(t[rb], p, P[rb]);
+      if constexpr (SRC != SRC_BF16) {
+        if (b0 + rb < p.nb) esc_apply(ec[rb], esc, g, lane, P[rb]);
+      }
     }
     const uint16_t* xrow = xs + 128 * wave + 8 * q;
 #pragma unroll
@@ -314,43 +334,40 @@ __global__ __launch_bounds__(kThreads) void k_gemm(GemmArgs a) {
 #pragma unroll
           for (int rb = 0; rb < RBW; ++rb)
 #pragma unroll
-            for (int p = 0; p < 4; ++p)
+            for (int pp = 0; pp < 4; ++pp)
               vacc[rb][m] = __builtin_amdgcn_fdot2_f32_bf16(
-                  as_bf16x2(P[rb][4 * j + p]), as_bf16x2(xv[p]), vacc[rb][m], false);
+                  as_bf16x2(P[rb][4 * j + pp]), as_bf16x2(xv[pp]), vacc[rb][m], false);
         }
       }
     }
   };
 
-  // ---- main loop: chunk c0 computes from LDS while chunk c0+4 is in flight
+  // ---- main loop.  Chunk i computes from LDS while chunk i+1's x and tiles are in
+  // flight.  Every iteration issues the same loads (past the last chunk the addresses
+  // are clamped to the last tile column, which is still in L2, and x is zeroed), so
+  // the wait before each compute is a fixed count and never drains the prefetch.
   uint32_t c0 = ga;
-  x_load<MT>(xr, a, m_rows, c0, gb, tid);
-  load_tiles(tA, c0 + wave);
+  x_load<MT>(xr, x, p.k, m_rows, c0, gb, tid);
+  load_tiles(tA, c0);
   x_store<MT>(xr, xs, tid);
   __syncthreads();
-  for (;;) {
-    uint32_t c1 = c0 + kChunk;
-    if (c1 < gb) {
-      x_load<MT>(xr, a, m_rows, c1, gb, tid);
-      load_tiles(tB, c1 + wave);
-    }
-    compute(tA, c0 + wave);
-    if (c1 >= gb) break;
+  for (uint32_t i = 0;;) {
+    x_load<MT>(xr, x, p.k, m_rows, c0 + kChunk, gb, tid);
+    load_tiles(tB, c0 + kChunk);
+    compute(tA, c0);
     __syncthreads();
     x_store<MT>(xr, xs, tid);
     __syncthreads();
-    c0 = c1;
-    c1 = c0 + kChunk;
-    if (c1 < gb) {
-      x_load<MT>(xr, a, m_rows, c1, gb, tid);
-      load_tiles(tA, c1 + wave);
-    }
-    compute(tB, c0 + wave);
-    if (c1 >= gb) break;
+    c0 += kChunk;
+    if (++i >= nchunks) break;
+    x_load<MT>(xr, x, p.k, m_rows, c0 + kChunk, gb, tid);
+    load_tiles(tA, c0 + kChunk);
+    compute(tB, c0);
     __syncthreads();
     x_store<MT>(xr, xs, tid);
     __syncthreads();
-    c0 = c1;
+    c0 += kChunk;
+    if (++i >= nchunks) break;
   }
   __syncthreads();   // LDS x no longer read: reuse it for the cross-wave reduction
 
@@ -382,12 +399,12 @@ __global__ __launch_bounds__(kThreads) void k_gemm(GemmArgs a) {
     const int rb = o / (MT * 16), rem = o % (MT * 16), m = rem >> 4, rr = rem & 15;
     float s = 0.f;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
+    for (int wv = 0; wv < kWaves; ++wv) {
       if constexpr (MF) {
         const int h = m >> 4, ln = 16 * (rr >> 2) + (m & 15), i = rr & 3;
-        s += red[(((w * RBW + rb) * NH + h) * 4 + i) * 64 + ln];
+        s += red[(((wv * RBW + rb) * NH + h) * 4 + i) * 64 + ln];
       } else {
-        s += red[((w * RBW + rb) * M + m) * 16 + rr];
+        s += red[((wv * RBW + rb) * M + m) * 16 + rr];
       }
     }
     return s;
@@ -399,13 +416,13 @@ __global__ __launch_bounds__(kThreads) void k_gemm(GemmArgs a) {
       const uint32_t b = b0 + rb;
       const float v = final_value(o);
       fin[o] = v;
-      if (b < a.nb && (uint32_t)m < m_rows) a.logits[(size_t)m * a.n + 16u * b + rr] = v;
+      if (b < p.nb && (uint32_t)m < m_rows) out_f32[(size_t)m * p.n + 16u * b + rr] = v;
     }
     __syncthreads();
     for (int o = tid; o < RBW * MT; o += kThreads) {
       const int rb = o / MT, m = o % MT;
       const uint32_t b = b0 + rb;
-      if (b >= a.nb || (uint32_t)m >= m_rows) continue;
+      if (b >= p.nb || (uint32_t)m >= m_rows) continue;
       float best = fin[o * 16];
       int bi = 0;
       bool finite = __builtin_isfinite(best);
@@ -414,63 +431,55 @@ __global__ __launch_bounds__(kThreads) void k_gemm(GemmArgs a) {
         finite = finite && __builtin_isfinite(v);
         if (v > best) { best = v; bi = rr; }
       }
-      a.rbmax_v[(size_t)m * a.nb + b] = finite ? best : __builtin_nanf("");
-      a.rbmax_i[(size_t)m * a.nb + b] = (int32_t)(16u * b + bi);
+      rbmax_v[(size_t)m * p.nb + b] = finite ? best : __builtin_nanf("");
+      rbmax_i[(size_t)m * p.nb + b] = (int32_t)(16u * b + bi);
     }
-    return;
   } else {
-    if (a.nsplit == 1) {
-      for (int o = tid; o < kOut; o += kThreads) {
-        const int rb = o / (MT * 16), rem = o % (MT * 16), m = rem >> 4, rr = rem & 15;
-        const uint32_t b = b0 + rb;
-        const float v = final_value(o);
-        if (b < a.nb && (uint32_t)m < m_rows) a.y[(size_t)m * a.n + 16u * b + rr] = f32_to_bf16_rne(v);
-      }
-      return;
-    }
+    const bool direct = gridDim.y == 1;
     for (int o = tid; o < kOut; o += kThreads) {
       const int rb = o / (MT * 16), rem = o % (MT * 16), m = rem >> 4, rr = rem & 15;
       const uint32_t b = b0 + rb;
       const float v = final_value(o);
-      if (b < a.nb && (uint32_t)m < m_rows)
-        __hip_atomic_store(a.partial + ((size_t)split * m_rows + m) * a.n + 16u * b + rr, v,
-                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (b >= p.nb || (uint32_t)m >= m_rows) continue;
+      if (direct) y[(size_t)m * p.n + 16u * b + rr] = f32_to_bf16_rne(v);
+      else out_f32[((size_t)split * m_rows + m) * p.n + 16u * b + rr] = v;
     }
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) {
-      const uint32_t t = __hip_atomic_fetch_add(a.counters + rbg, 1u, __ATOMIC_ACQ_REL,
-                                                __HIP_MEMORY_SCOPE_AGENT);
-      s_last = (t == a.nsplit - 1u) ? 1u : 0u;
-    }
-    __syncthreads();
-    if (!s_last) return;
-    __threadfence();
-    for (int o = tid; o < kOut; o += kThreads) {
-      const int rb = o / (MT * 16), rem = o % (MT * 16), m = rem >> 4, rr = rem & 15;
-      const uint32_t b = b0 + rb;
-      if (b >= a.nb || (uint32_t)m >= m_rows) continue;
-      float s = 0.f;
-      for (uint32_t sp = 0; sp < a.nsplit; ++sp)
-        s += __hip_atomic_load(a.partial + ((size_t)sp * m_rows + m) * a.n + 16u * b + rr,
-                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      a.y[(size_t)m * a.n + 16u * b + rr] = f32_to_bf16_rne(s);
-    }
-    if (tid == 0)
-      __hip_atomic_store(a.counters + rbg, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+// Sum of the split-K partials in split order (deterministic), rounded to BF16.
+static __global__ __launch_bounds__(256) void k_splitk_reduce(const float* __restrict__ partial,
+                                                       uint16_t* __restrict__ y, uint32_t nsplit,
+                                                       uint32_t mn) {
+  const uint32_t stride = gridDim.x * 256u;
+  for (uint32_t i = blockIdx.x * 256u + threadIdx.x; i < mn; i += stride) {
+    float s = 0.f;
+    for (uint32_t sp = 0; sp < nsplit; ++sp) s += partial[(size_t)sp * mn + i];
+    y[i] = f32_to_bf16_rne(s);
   }
 }
 
 // Host-side launcher for one weight source: dispatch on m (exact for the VALU path,
-// 16 or 32 columns for MFMA), rbw and epilogue.
+// 16 or 32 columns for MFMA), rbw and epilogue; split-K adds the reduce kernel.
 template <int SRC>
-hipError_t launch_gemm_src(const GemmArgs& a, int epi, const GemmPlan& p, hipStream_t s) {
-  dim3 grid(p.n_rbg, p.nsplit), block(kThreads);
-#define W12_L(M_, MT_, MF_, RBW_, EPI_) \
-  hipLaunchKernelGGL((k_gemm<M_, MT_, MF_, RBW_, SRC, EPI_>), grid, block, 0, s, a)
+hipError_t launch_gemm_src(const GemmArgs& a, int epi, const GemmPlan& pl, hipStream_t s) {
+  dim3 grid(pl.n_rbg, pl.nsplit), block(kThreads);
+  GemmParams p;
+  p.m = a.m;
+  p.n = a.n;
+  p.k = a.k;
+  p.g_cols = a.g_cols;
+  p.nb = a.nb;
+  p.cols_per_split = pl.cols_per_split;
+  for (int i = 0; i < 4; ++i) p.lut[i] = a.lut[i];
+  p.basepair = a.basepair;
+  float* f32 = epi == EPI_LOGITS ? a.logits : a.partial;
+#define W12_L(M_, MT_, MF_, RBW_, EPI_)                                                          \
+  hipLaunchKernelGGL((k_gemm<M_, MT_, MF_, RBW_, SRC, EPI_>), grid, block, 0, s, a.x, a.w,     \
+                     a.esc_off, a.esc, a.y, f32, a.rbmax_v, a.rbmax_i, p)
 #define W12_RBW(M_, MT_, MF_, EPI_)            \
   do {                                         \
-    if (p.rbw == 1) W12_L(M_, MT_, MF_, 1, EPI_); \
+    if (pl.rbw == 1) W12_L(M_, MT_, MF_, 1, EPI_); \
     else W12_L(M_, MT_, MF_, 2, EPI_);          \
   } while (0)
 #define W12_EPI(M_, MT_, MF_)                                       \
@@ -500,7 +509,15 @@ hipError_t launch_gemm_src(const GemmArgs& a, int epi, const GemmPlan& p, hipStr
 #undef W12_EPI
 #undef W12_RBW
 #undef W12_L
-  return hipGetLastError();
+  hipError_t e = hipGetLastError();
+  if (e == hipSuccess && epi == EPI_BF16 && pl.nsplit > 1) {
+    const uint32_t mn = a.m * a.n;
+    uint32_t blocks = (mn + 255u) / 256u;
+    if (blocks > 1024u) blocks = 1024u;
+    hipLaunchKernelGGL(k_splitk_reduce, dim3(blocks), dim3(256), 0, s, a.partial, a.y, pl.nsplit, mn);
+    e = hipGetLastError();
+  }
+  return e;
 }
 
 }  // namespace w12

@@ -30,9 +30,7 @@ struct GemmArgs {
   float* rbmax_v;           // [m][nb] (EPI_LOGITS)
   int32_t* rbmax_i;         // [m][nb] (EPI_LOGITS)
   float* partial;           // [nsplit][m][n] split-K partial sums
-  uint32_t* counters;       // [n_rbg] split-K arrival tickets (zero between calls)
   uint32_t m, n, k, g_cols, nb;
-  uint32_t nsplit, cols_per_split;
   uint32_t lut[4];          // codebook bytes C[0..15] (SRC_LUT)
   uint32_t basepair;        // C[0] | C[0] << 16 (SRC_RUN)
 };
