@@ -1,6 +1,6 @@
 // C-ABI host layer of libw12.so: argument validation (before any HIP call), workspace
 // layout, kernel-family dispatch and launch.  No HIP call happens at load time.
-#include "../../include/w12.h"
+#include "w12.h"
 #include "w12_internal.h"
 
 #include <string.h>
@@ -43,12 +43,17 @@ inline bool codebook_is_run(const uint8_t* c) {
   return true;
 }
 
+#ifndef W12_RBW2_MIN_NB
+#define W12_RBW2_MIN_NB 1024   // row-blocks from which workgroups take two row-blocks
+#endif
+
 // Work split: row-blocks per workgroup and K splits so that the grid holds enough
-// workgroups to keep 256 CUs streaming; splits keep at least one 4-column chunk.
-GemmPlan make_plan(uint64_t n, uint64_t k, int epi) {
+// workgroups to keep 256 CUs streaming; splits keep at least one column per wave.
+GemmPlan make_plan(uint32_t m, uint64_t n, uint64_t k, int epi) {
+  (void)m;
   GemmPlan p;
   const uint64_t nb = n / 16, g = k / 128;
-  p.rbw = nb >= 1024 ? 2 : 1;
+  p.rbw = nb >= W12_RBW2_MIN_NB ? 2 : 1;
   p.n_rbg = (uint32_t)((nb + p.rbw - 1) / p.rbw);
   uint64_t ns = 1;
   if (epi == EPI_BF16)
@@ -61,7 +66,7 @@ GemmPlan make_plan(uint64_t n, uint64_t k, int epi) {
 }
 
 size_t gemm_ws_bytes(uint32_t m, uint64_t n, uint64_t k) {
-  const GemmPlan p = make_plan(n, k, EPI_BF16);
+  const GemmPlan p = make_plan(m, n, k, EPI_BF16);
   return p.nsplit > 1 ? align256((size_t)p.nsplit * m * n * 4) : 0;
 }
 
@@ -213,7 +218,7 @@ w12_status w12_gemm(const uint16_t* x, uint32_t m, const w12_desc* d, uint16_t* 
   if (ws_bytes < need) return W12_ERR_WORKSPACE;
   if (need > 0 && !ws) return W12_ERR_NULL;
   if (!aligned(x, 16) || !aligned(y, 4) || !aligned(ws, 256)) return W12_ERR_ALIGN;
-  const GemmPlan p = make_plan(d->n, d->k, EPI_BF16);
+  const GemmPlan p = make_plan(m, d->n, d->k, EPI_BF16);
   GemmArgs a;
   memset(&a, 0, sizeof(a));
   a.x = x;
@@ -241,7 +246,7 @@ w12_status w12_gemm_bf16(const uint16_t* x, uint32_t m, const uint16_t* w, uint6
   if (ws_bytes < need) return W12_ERR_WORKSPACE;
   if (need > 0 && !ws) return W12_ERR_NULL;
   if (!aligned(x, 16) || !aligned(w, 16) || !aligned(y, 4) || !aligned(ws, 256)) return W12_ERR_ALIGN;
-  const GemmPlan p = make_plan(n, k, EPI_BF16);
+  const GemmPlan p = make_plan(m, n, k, EPI_BF16);
   GemmArgs a;
   memset(&a, 0, sizeof(a));
   a.x = x;
@@ -270,7 +275,7 @@ w12_status w12_lmhead_verify(const uint16_t* x, uint32_t m, const w12_desc* d, c
     return W12_ERR_ALIGN;
   hipStream_t s = (hipStream_t)stream;
   uint8_t* base = (uint8_t*)ws;
-  GemmPlan p = make_plan(d->n, d->k, EPI_LOGITS);
+  GemmPlan p = make_plan(m, d->n, d->k, EPI_LOGITS);
   GemmArgs a;
   memset(&a, 0, sizeof(a));
   a.x = x;

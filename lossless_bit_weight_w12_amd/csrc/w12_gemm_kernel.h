@@ -40,11 +40,15 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 
+#ifndef W12_MFMA_MIN_M
+#define W12_MFMA_MIN_M 4    // m from which the MFMA path runs (below: VALU v_dot2)
+#endif
+
 constexpr int kWaves = 4;
 constexpr int kThreads = 256;
-constexpr int kChunk = 4;                        // tile columns per LDS x chunk
-constexpr int kXsStride = kChunk * 128 + 8;      // BF16 per LDS row (+16 B pad: no bank
-                                                 // conflicts for the MFMA B reads)
+constexpr int kXsStride = 128 + 8;   // BF16 per LDS row of one wave's x column (+16 B pad:
+                                     // no bank conflicts for the MFMA B reads)
+
 
 // Scalar parameters of one GEMM launch.
 struct GemmParams {
@@ -95,11 +99,15 @@ __device__ __forceinline__ void load_tile(TileRegs<SRC>& t, const uint8_t* __res
     const int r = lane & 15, q = lane >> 4;
     const uint8_t* base = w + ((size_t)(16u * b + r) * p.k + 128u * g + 8u * q) * 2u;
 #pragma unroll
+    // plain loads: each instruction covers half of every 128-byte line it touches, and
+    // the other half is read by the next instruction from L2
     for (int j = 0; j < 4; ++j) t.v[j] = *reinterpret_cast<const u32x4*>(base + 64 * j);
   } else {
     const uint8_t* base = w + ((size_t)b * p.g_cols + g) * 3072u + (uint32_t)lane * 16u;
 #pragma unroll
-    for (int s = 0; s < 3; ++s) t.v[s] = *reinterpret_cast<const u32x4*>(base + 1024 * s);
+    // streaming (nontemporal) loads: every instruction reads 1 KB of whole lines
+    for (int s = 0; s < 3; ++s)
+      t.v[s] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + 1024 * s));
   }
 }
 
@@ -143,9 +151,16 @@ __device__ __forceinline__ void unpack_tile(const TileRegs<SRC>& t, const GemmPa
 }
 
 // Escape cursor of one row-block, wave-uniform (scalar registers): records [pos, end)
-// not yet consumed; `next` is record pos (or a sentinel whose column is past any K).
+// not yet consumed, and a window w[] holding records pos..pos+3 (a sentinel, whose
+// column is past any K, beyond end).  Scalar loads share a wait counter with LDS, so
+// the window is refilled only after the tile's last LDS read (esc_refill), never in
+// front of one; a tile with more than four escapes in one row-block refills inline.
+constexpr int kEscWin = 4;
 struct EscCursor {
-  uint32_t pos, end, next;
+  uint32_t pos, end;
+  uint32_t w[kEscWin];   // records pos .. pos + nwin - 1, then sentinels
+  uint32_t nwin;
+  bool stale;            // records consumed since the last refill
 };
 
 constexpr uint32_t kEscSentinel = 0xFFFFFFFFu;
@@ -161,9 +176,11 @@ __device__ __forceinline__ uint32_t sload(const uint32_t* p, uint32_t i) {
   return ((const_u32_ptr)p)[i];
 }
 
-__device__ __forceinline__ uint32_t esc_fetch(const uint32_t* __restrict__ esc, uint32_t pos,
-                                              uint32_t end) {
-  return pos < end ? sload(esc, pos) : kEscSentinel;
+__device__ __forceinline__ void esc_refill(EscCursor& c, const uint32_t* __restrict__ esc) {
+#pragma unroll
+  for (int i = 0; i < kEscWin; ++i) c.w[i] = c.pos + i < c.end ? sload(esc, c.pos + i) : kEscSentinel;
+  c.nwin = min(c.end - c.pos, (uint32_t)kEscWin);
+  c.stale = false;
 }
 
 // Start the cursor at the first record of row-block b with column >= kmin (binary
@@ -182,7 +199,7 @@ __device__ __forceinline__ void esc_begin(EscCursor& c, const uint32_t* __restri
   }
   c.pos = lo;
   c.end = end;
-  c.next = esc_fetch(esc, lo, end);
+  esc_refill(c, esc);
 }
 
 __device__ __forceinline__ void patch_pair(uint32_t P[16], uint32_t pi, uint32_t sh, uint32_t e,
@@ -198,57 +215,64 @@ __device__ __forceinline__ void patch_pair(uint32_t P[16], uint32_t pi, uint32_t
 }
 
 // Patch the escapes of tile column g into P.  Records of columns below g (other
-// waves' columns) are skipped; the cursor stops at the first record past the tile.
+// waves' columns) are skipped; consumption stops at the first record past the tile.
+// The window is shifted as records are consumed and refilled inline only when it runs
+// dry inside a tile (more than four escapes of one row-block in one tile).
 __device__ __forceinline__ void esc_apply(EscCursor& c, const uint32_t* __restrict__ esc,
                                           uint32_t g, int lane, uint32_t P[16]) {
   const uint32_t klo = g * 128u, khi = klo + 128u;
-  while (esc_col(c.next) < khi) {
-    const uint32_t rec = c.next;
+  while (esc_col(c.w[0]) < khi) {
+    const uint32_t rec = c.w[0];
     if (esc_col(rec) >= klo) {
       const uint32_t rr = rec >> 28;
       const uint32_t kap = esc_col(rec) - klo;
-      const uint32_t j = kap >> 5, qq = (kap >> 3) & 3u, i = kap & 7u;
-      patch_pair(P, 4u * j + (i >> 1), 7u + 16u * (i & 1u), rec & 0xFFu,
+      const uint32_t j = kap >> 5, qq = (kap >> 3) & 3u, ii = kap & 7u;
+      patch_pair(P, 4u * j + (ii >> 1), 7u + 16u * (ii & 1u), rec & 0xFFu,
                  (uint32_t)lane == 16u * qq + rr);
     }
+#pragma unroll
+    for (int i = 0; i + 1 < kEscWin; ++i) c.w[i] = c.w[i + 1];
+    c.w[kEscWin - 1] = kEscSentinel;
     ++c.pos;
-    c.next = esc_fetch(esc, c.pos, c.end);
+    --c.nwin;
+    c.stale = true;
+    if (c.nwin == 0u && c.pos < c.end) esc_refill(c, esc);
   }
 }
 
+// One wave's x column: MT rows x 128 BF16 = 16*MT units of 16 bytes over 64 lanes.
 template <int MT>
 struct XStage {
-  static constexpr int kUnits = (MT * 64 + kThreads - 1) / kThreads;   // 16-byte units
+  static constexpr int kUnits = (16 * MT + 63) / 64;
   u32x4 v[kUnits];
 };
 
-// Every thread issues the same loads on every path (addresses clamped into range,
+// Every lane issues the same loads on every path (addresses clamped into range,
 // out-of-range units zeroed after the load), so the compiler's wait counts stay exact.
 template <int MT>
 __device__ __forceinline__ void x_load(XStage<MT>& st, const uint16_t* __restrict__ x,
-                                       uint32_t k, uint32_t m_rows, uint32_t c0, uint32_t gb,
-                                       int tid) {
+                                       uint32_t k, uint32_t m_rows, uint32_t g, uint32_t gb,
+                                       int lane) {
 #pragma unroll
   for (int i = 0; i < XStage<MT>::kUnits; ++i) {
-    const uint32_t u = (uint32_t)tid + kThreads * i;
-    const uint32_t uu = u < MT * 64u ? u : u % (MT * 64u);
-    const uint32_t m = uu >> 6, cu = uu & 63u;
-    const uint32_t col = c0 + (cu >> 4);
-    const bool ok = m < m_rows && col < gb;
-    const uint32_t ml = min(m, m_rows - 1u), cl = min(col, gb - 1u);
-    const u32x4 v = *reinterpret_cast<const u32x4*>(x + (size_t)ml * k + 128u * cl + 8u * (cu & 15u));
+    const uint32_t u = (uint32_t)lane + 64u * i;
+    const uint32_t uu = u < 16u * MT ? u : u % (16u * MT);
+    const uint32_t m = uu >> 4, cu = uu & 15u;
+    const bool ok = m < m_rows && g < gb;
+    const uint32_t ml = min(m, m_rows - 1u), gl = min(g, gb - 1u);
+    const u32x4 v = *reinterpret_cast<const u32x4*>(x + (size_t)ml * k + 128u * gl + 8u * cu);
     st.v[i] = ok ? v : u32x4{0u, 0u, 0u, 0u};
   }
 }
 
 template <int MT>
-__device__ __forceinline__ void x_store(const XStage<MT>& st, uint16_t* xs, int tid) {
+__device__ __forceinline__ void x_store(const XStage<MT>& st, uint16_t* xw, int lane) {
 #pragma unroll
   for (int i = 0; i < XStage<MT>::kUnits; ++i) {
-    const uint32_t u = (uint32_t)tid + kThreads * i;
-    if (u < MT * 64u) {
-      const uint32_t m = u >> 6, cu = u & 63u;
-      *reinterpret_cast<u32x4*>(xs + m * kXsStride + 8u * cu) = st.v[i];
+    const uint32_t u = (uint32_t)lane + 64u * i;
+    if (u < 16u * MT) {
+      const uint32_t m = u >> 4, cu = u & 15u;
+      *reinterpret_cast<u32x4*>(xw + m * kXsStride + 8u * cu) = st.v[i];
     }
   }
 }
@@ -263,7 +287,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm(
     uint16_t* __restrict__ y, float* __restrict__ out_f32, float* __restrict__ rbmax_v,
     int32_t* __restrict__ rbmax_i, GemmParams p) {
   constexpr int NH = MF ? MT / 16 : 1;
-  __shared__ __align__(16) uint16_t xs[MT * kXsStride];
+  __shared__ __align__(16) uint16_t xs[kWaves * MT * kXsStride];   // one x column per wave
   __shared__ float fin[EPI == EPI_LOGITS ? RBW * MT * 16 : 1];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -274,7 +298,6 @@ __global__ __launch_bounds__(kThreads) void k_gemm(
   const uint32_t ga = split * p.cols_per_split;
   const uint32_t gb = min(p.g_cols, ga + p.cols_per_split);
   const uint32_t m_rows = MF ? p.m : (uint32_t)M;
-  const uint32_t nchunks = (gb - ga + kChunk - 1) / kChunk;
 
   float vacc[RBW][MF ? 1 : M];
   f32x4 macc[RBW][NH];
@@ -287,23 +310,19 @@ __global__ __launch_bounds__(kThreads) void k_gemm(
   }
 
   EscCursor ec[RBW];
-  if constexpr (SRC != SRC_BF16) {
-#pragma unroll
-    for (int rb = 0; rb < RBW; ++rb) esc_begin(ec[rb], esc_off, esc, min(b0 + rb, p.nb - 1u), ga * 128u);
-  }
 
   TileRegs<SRC> tA[RBW], tB[RBW];
   XStage<MT> xr;
 
-  auto load_tiles = [&](TileRegs<SRC>* t, uint32_t c) {
-    const uint32_t g = min(c + (uint32_t)wave, gb - 1u);
+  uint16_t* xw = xs + wave * MT * kXsStride;   // this wave's x column in LDS
+
+  auto load_tiles = [&](TileRegs<SRC>* t, uint32_t g) {
+    const uint32_t gl = min(g, gb - 1u);
 #pragma unroll
-    for (int rb = 0; rb < RBW; ++rb) load_tile<SRC>(t[rb], w, p, min(b0 + rb, p.nb - 1u), g, lane);
+    for (int rb = 0; rb < RBW; ++rb) load_tile<SRC>(t[rb], w, p, min(b0 + rb, p.nb - 1u), gl, lane);
   };
 
-  auto compute = [&](const TileRegs<SRC>* t, uint32_t c) {
-    const uint32_t g = c + (uint32_t)wave;
-    if (g >= gb) return;
+  auto compute = [&](const TileRegs<SRC>* t, uint32_t g) {
     uint32_t P[RBW][16];
 #pragma unroll
     for (int rb = 0; rb < RBW; ++rb) {
@@ -312,7 +331,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm(
         if (b0 + rb < p.nb) esc_apply(ec[rb], esc, g, lane, P[rb]);
       }
     }
-    const uint16_t* xrow = xs + 128 * wave + 8 * q;
+    const uint16_t* xrow = xw + 8 * q;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       if constexpr (MF) {
@@ -340,34 +359,52 @@ __global__ __launch_bounds__(kThreads) void k_gemm(
         }
       }
     }
+    if constexpr (SRC != SRC_BF16) {
+      // refill after the tile's last LDS read: a pending scalar load would otherwise
+      // hold up the LDS waits (they share one counter)
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int rb = 0; rb < RBW; ++rb)
+        if (ec[rb].stale) esc_refill(ec[rb], esc);
+    }
   };
 
-  // ---- main loop.  Chunk i computes from LDS while chunk i+1's x and tiles are in
-  // flight.  Every iteration issues the same loads (past the last chunk the addresses
-  // are clamped to the last tile column, which is still in L2, and x is zeroed), so
-  // the wait before each compute is a fixed count and never drains the prefetch.
-  uint32_t c0 = ga;
-  x_load<MT>(xr, x, p.k, m_rows, c0, gb, tid);
-  load_tiles(tA, c0);
-  x_store<MT>(xr, xs, tid);
-  __syncthreads();
-  for (uint32_t i = 0;;) {
-    x_load<MT>(xr, x, p.k, m_rows, c0 + kChunk, gb, tid);
-    load_tiles(tB, c0 + kChunk);
-    compute(tA, c0);
-    __syncthreads();
-    x_store<MT>(xr, xs, tid);
-    __syncthreads();
-    c0 += kChunk;
-    if (++i >= nchunks) break;
-    x_load<MT>(xr, x, p.k, m_rows, c0 + kChunk, gb, tid);
-    load_tiles(tA, c0 + kChunk);
-    compute(tB, c0);
-    __syncthreads();
-    x_store<MT>(xr, xs, tid);
-    __syncthreads();
-    c0 += kChunk;
-    if (++i >= nchunks) break;
+  // ---- main loop.  Wave w streams tile columns ga+w, ga+w+4, ... of its row-blocks
+  // independently of the other waves (x goes through the wave's own LDS slot, so no
+  // workgroup barrier): column g computes while column g+4's x and tiles are in flight.
+  // Every iteration issues the same loads (past the last column the addresses are
+  // clamped to the last tile column, still in L2, and x is zeroed), so the wait before
+  // each compute is a fixed count and never drains the prefetch.
+  uint32_t g = ga + (uint32_t)wave;
+  if (g < gb) {
+    x_load<MT>(xr, x, p.k, m_rows, g, gb, lane);
+    load_tiles(tA, g);
+    // escape cursors start after the first tiles are requested: their scalar loads
+    // (one or two dependent round trips) overlap the first tile fetch
+    if constexpr (SRC != SRC_BF16) {
+#pragma unroll
+      for (int rb = 0; rb < RBW; ++rb) esc_begin(ec[rb], esc_off, esc, min(b0 + rb, p.nb - 1u), ga * 128u);
+    }
+    x_store<MT>(xr, xw, lane);
+    __builtin_amdgcn_wave_barrier();
+    for (;;) {
+      x_load<MT>(xr, x, p.k, m_rows, g + kWaves, gb, lane);
+      load_tiles(tB, g + kWaves);
+      compute(tA, g);
+      __builtin_amdgcn_wave_barrier();
+      x_store<MT>(xr, xw, lane);
+      __builtin_amdgcn_wave_barrier();
+      g += kWaves;
+      if (g >= gb) break;
+      x_load<MT>(xr, x, p.k, m_rows, g + kWaves, gb, lane);
+      load_tiles(tA, g + kWaves);
+      compute(tB, g);
+      __builtin_amdgcn_wave_barrier();
+      x_store<MT>(xr, xw, lane);
+      __builtin_amdgcn_wave_barrier();
+      g += kWaves;
+      if (g >= gb) break;
+    }
   }
   __syncthreads();   // LDS x no longer read: reuse it for the cross-wave reduction
 
@@ -487,24 +524,27 @@ hipError_t launch_gemm_src(const GemmArgs& a, int epi, const GemmPlan& pl, hipSt
     if (epi == EPI_BF16) W12_RBW(M_, MT_, MF_, EPI_BF16);          \
     else if constexpr (SRC != SRC_BF16) W12_RBW(M_, MT_, MF_, EPI_LOGITS); \
   } while (0)
-  switch (a.m) {
-    case 1: W12_EPI(1, 1, false); break;
-    case 2: W12_EPI(2, 2, false); break;
-    case 3: W12_EPI(3, 3, false); break;
-    case 4: W12_EPI(4, 4, false); break;
-    case 5: W12_EPI(5, 5, false); break;
-    case 6: W12_EPI(6, 6, false); break;
-    case 7: W12_EPI(7, 7, false); break;
-    case 8: W12_EPI(8, 8, false); break;
-    case 9: W12_EPI(9, 9, false); break;
-    case 10: W12_EPI(10, 10, false); break;
-    case 11: W12_EPI(11, 11, false); break;
-    case 12: W12_EPI(12, 12, false); break;
-    case 13: W12_EPI(13, 13, false); break;
-    case 14: W12_EPI(14, 14, false); break;
-    case 15: W12_EPI(15, 15, false); break;
-    case 16: W12_EPI(16, 16, true); break;
-    default: W12_EPI(32, 32, true); break;
+  if (a.m >= W12_MFMA_MIN_M) {
+    if (a.m <= 16) W12_EPI(16, 16, true);
+    else W12_EPI(32, 32, true);
+  } else {
+    switch (a.m) {
+      case 1: W12_EPI(1, 1, false); break;
+      case 2: W12_EPI(2, 2, false); break;
+      case 3: W12_EPI(3, 3, false); break;
+      case 4: W12_EPI(4, 4, false); break;
+      case 5: W12_EPI(5, 5, false); break;
+      case 6: W12_EPI(6, 6, false); break;
+      case 7: W12_EPI(7, 7, false); break;
+      case 8: W12_EPI(8, 8, false); break;
+      case 9: W12_EPI(9, 9, false); break;
+      case 10: W12_EPI(10, 10, false); break;
+      case 11: W12_EPI(11, 11, false); break;
+      case 12: W12_EPI(12, 12, false); break;
+      case 13: W12_EPI(13, 13, false); break;
+      case 14: W12_EPI(14, 14, false); break;
+      default: W12_EPI(15, 15, false); break;
+    }
   }
 #undef W12_EPI
 #undef W12_RBW
