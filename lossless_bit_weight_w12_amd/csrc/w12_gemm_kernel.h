@@ -40,10 +40,6 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 
-#ifndef W12_MFMA_MIN_M
-#define W12_MFMA_MIN_M 4    // m from which the MFMA path runs (below: VALU v_dot2)
-#endif
-
 constexpr int kWaves = 4;
 constexpr int kThreads = 256;
 constexpr int kXsStride = 128 + 8;   // BF16 per LDS row of one wave's x column (+16 B pad:
@@ -484,6 +480,161 @@ __global__ __launch_bounds__(kThreads) void k_gemm(
   }
 }
 
+// ---------------------------------------------------------------------------------
+// Column-synchronous MFMA kernel (m >= W12_MFMA_MIN_M).  A workgroup of NW waves covers
+// NW consecutive row-blocks, one per wave, and all waves walk the same tile columns of
+// the K-range together.  The x column (MT rows x 128 BF16) is loaded once per
+// workgroup -- each thread a slice -- into one of two LDS slots, so one barrier per
+// column suffices (the slot written for column g+1 was last read for column g-1, which
+// every wave finished before the previous barrier).  Compared with a wave per column
+// this divides the x traffic per tile by NW.  Each wave owns its row-block's outputs:
+// lane l holds D[4q+i][l%16 + 16h], i.e. rows 16b+4q..16b+4q+3 of output column m.
+template <int MT, int NW, int SRC, int EPI>
+__global__ __launch_bounds__(NW * 64) void k_gemm_cs(
+    const uint16_t* __restrict__ x, const uint8_t* __restrict__ w,
+    const uint32_t* __restrict__ esc_off, const uint32_t* __restrict__ esc,
+    uint16_t* __restrict__ y, float* __restrict__ out_f32, float* __restrict__ rbmax_v,
+    int32_t* __restrict__ rbmax_i, GemmParams p) {
+  constexpr int NH = MT / 16;
+  constexpr int NT = NW * 64;
+  constexpr int kUnits = (16 * MT + NT - 1) / NT;     // 16-byte x units per thread
+  __shared__ __align__(16) uint16_t xs[2][MT * kXsStride];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r = lane & 15, q = lane >> 4;
+  const uint32_t b = blockIdx.x * NW + (uint32_t)wave;
+  const bool bvalid = b < p.nb;
+  const uint32_t bl = min(b, p.nb - 1u);
+  const uint32_t split = blockIdx.y;
+  const uint32_t ga = split * p.cols_per_split;
+  const uint32_t gb = min(p.g_cols, ga + p.cols_per_split);
+  const uint32_t m_rows = p.m;
+
+  f32x4 acc[NH];
+#pragma unroll
+  for (int h = 0; h < NH; ++h) acc[h] = f32x4{0.f, 0.f, 0.f, 0.f};
+  TileRegs<SRC> tA, tB;
+  u32x4 xr[kUnits];
+  EscCursor ec;
+
+  auto xload = [&](uint32_t g) {
+    const uint32_t gl = min(g, gb - 1u);
+#pragma unroll
+    for (int i = 0; i < kUnits; ++i) {
+      const uint32_t u = (uint32_t)tid + NT * i;
+      const uint32_t uu = u < 16u * MT ? u : u % (16u * MT);
+      const uint32_t m = uu >> 4, cu = uu & 15u;
+      const bool ok = m < m_rows && g < gb;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(x + (size_t)min(m, m_rows - 1u) * p.k + 128u * gl + 8u * cu);
+      xr[i] = ok ? v : u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+  auto xstore = [&](uint32_t slot) {
+#pragma unroll
+    for (int i = 0; i < kUnits; ++i) {
+      const uint32_t u = (uint32_t)tid + NT * i;
+      if (u < 16u * MT) {
+        const uint32_t m = u >> 4, cu = u & 15u;
+        *reinterpret_cast<u32x4*>(&xs[slot][m * kXsStride + 8u * cu]) = xr[i];
+      }
+    }
+  };
+  auto compute = [&](const TileRegs<SRC>& t, uint32_t g) {
+    uint32_t P[16];
+    unpack_tile<SRC>(t, p, P);
+    if constexpr (SRC != SRC_BF16) {
+      if (bvalid) esc_apply(ec, esc, g, lane, P);
+    }
+    const uint16_t* xrow = &xs[g & 1u][8 * q];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const u32x4 av = {P[4 * j], P[4 * j + 1], P[4 * j + 2], P[4 * j + 3]};
+#pragma unroll
+      for (int h = 0; h < NH; ++h) {
+        const u32x4 xv = *reinterpret_cast<const u32x4*>(xrow + (16 * h + r) * kXsStride + 32 * j);
+        acc[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av),
+                                                         __builtin_bit_cast(bf16x8_t, xv), acc[h], 0, 0, 0);
+      }
+    }
+    if constexpr (SRC != SRC_BF16) {
+      __builtin_amdgcn_sched_barrier(0);
+      if (ec.stale) esc_refill(ec, esc);
+    }
+  };
+
+  // ---- main loop: every iteration issues the same loads (column g+1 clamped past the
+  // end, x zeroed), so each wait is a fixed count; one barrier per column.
+  uint32_t g = ga;
+  xload(g);
+  load_tile<SRC>(tA, w, p, bl, g, lane);
+  if constexpr (SRC != SRC_BF16) esc_begin(ec, esc_off, esc, bl, ga * 128u);
+  xstore(g & 1u);
+  __syncthreads();
+  for (;;) {
+    xload(g + 1);
+    load_tile<SRC>(tB, w, p, bl, min(g + 1, gb - 1u), lane);
+    compute(tA, g);
+    xstore((g + 1) & 1u);
+    __syncthreads();
+    if (++g >= gb) break;
+    xload(g + 1);
+    load_tile<SRC>(tA, w, p, bl, min(g + 1, gb - 1u), lane);
+    compute(tB, g);
+    xstore((g + 1) & 1u);
+    __syncthreads();
+    if (++g >= gb) break;
+  }
+
+  if (!bvalid) return;
+  const uint32_t n0 = 16u * b + 4u * (uint32_t)q;
+  if constexpr (EPI == EPI_LOGITS) {
+#pragma unroll
+    for (int h = 0; h < NH; ++h) {
+      const uint32_t m = 16u * h + (uint32_t)r;
+      // best of this lane's 4 rows, lowest row on ties; non-finite poisons the block
+      float best = acc[h][0];
+      int bi = 0;
+      bool finite = __builtin_isfinite(acc[h][0]);
+#pragma unroll
+      for (int i = 1; i < 4; ++i) {
+        finite = finite && __builtin_isfinite(acc[h][i]);
+        if (acc[h][i] > best) { best = acc[h][i]; bi = i; }
+      }
+      int row = 4 * q + bi;
+#pragma unroll
+      for (int off = 16; off <= 32; off <<= 1) {
+        const float ob = __shfl_xor(best, off);
+        const int orow = __shfl_xor(row, off);
+        const int ofin = __shfl_xor((int)finite, off);
+        finite = finite && ofin;
+        if (ob > best || (ob == best && orow < row)) { best = ob; row = orow; }
+      }
+      if (m < m_rows) {
+        *reinterpret_cast<f32x4*>(out_f32 + (size_t)m * p.n + n0) = acc[h];
+        if (q == 0) {
+          rbmax_v[(size_t)m * p.nb + b] = finite ? best : __builtin_nanf("");
+          rbmax_i[(size_t)m * p.nb + b] = (int32_t)(16u * b + row);
+        }
+      }
+    }
+  } else {
+    const bool direct = gridDim.y == 1;
+#pragma unroll
+    for (int h = 0; h < NH; ++h) {
+      const uint32_t m = 16u * h + (uint32_t)r;
+      if (m >= m_rows) continue;
+      if (direct) {
+        const uint32_t lo = (uint32_t)f32_to_bf16_rne(acc[h][0]) | ((uint32_t)f32_to_bf16_rne(acc[h][1]) << 16);
+        const uint32_t hi = (uint32_t)f32_to_bf16_rne(acc[h][2]) | ((uint32_t)f32_to_bf16_rne(acc[h][3]) << 16);
+        *reinterpret_cast<uint2*>(y + (size_t)m * p.n + n0) = make_uint2(lo, hi);
+      } else {
+        *reinterpret_cast<f32x4*>(out_f32 + ((size_t)split * m_rows + m) * p.n + n0) = acc[h];
+      }
+    }
+  }
+}
+
 // Sum of the split-K partials in split order (deterministic), rounded to BF16.
 static __global__ __launch_bounds__(256) void k_splitk_reduce(const float* __restrict__ partial,
                                                        uint16_t* __restrict__ y, uint32_t nsplit,
@@ -524,28 +675,40 @@ hipError_t launch_gemm_src(const GemmArgs& a, int epi, const GemmPlan& pl, hipSt
     if (epi == EPI_BF16) W12_RBW(M_, MT_, MF_, EPI_BF16);          \
     else if constexpr (SRC != SRC_BF16) W12_RBW(M_, MT_, MF_, EPI_LOGITS); \
   } while (0)
-  if (a.m >= W12_MFMA_MIN_M) {
-    if (a.m <= 16) W12_EPI(16, 16, true);
-    else W12_EPI(32, 32, true);
+#define W12_CS(MT_, EPI_)                                                                     \
+  do {                                                                                        \
+    if (pl.nw == 8)                                                                           \
+      hipLaunchKernelGGL((k_gemm_cs<MT_, 8, SRC, EPI_>), grid, dim3(512), 0, s, a.x, a.w,     \
+                         a.esc_off, a.esc, a.y, f32, a.rbmax_v, a.rbmax_i, p);                \
+    else                                                                                      \
+      hipLaunchKernelGGL((k_gemm_cs<MT_, 4, SRC, EPI_>), grid, dim3(256), 0, s, a.x, a.w,     \
+                         a.esc_off, a.esc, a.y, f32, a.rbmax_v, a.rbmax_i, p);                \
+  } while (0)
+#define W12_CS_EPI(MT_)                                                     \
+  do {                                                                      \
+    if (epi == EPI_BF16) W12_CS(MT_, EPI_BF16);                            \
+    else if constexpr (SRC != SRC_BF16) W12_CS(MT_, EPI_LOGITS);           \
+  } while (0)
+  if (pl.kind == KIND_COLUMN_SYNC) {
+    if (a.m <= 16) W12_CS_EPI(16);
+    else W12_CS_EPI(32);
+  } else if (pl.mfma) {
+    W12_EPI(16, 16, true);
   } else {
+#define W12_VCASE(M_)                                          \
+  case M_:                                                     \
+    if constexpr (M_ < W12_MFMA_MIN_M) W12_EPI(M_, M_, false); \
+    break;
     switch (a.m) {
-      case 1: W12_EPI(1, 1, false); break;
-      case 2: W12_EPI(2, 2, false); break;
-      case 3: W12_EPI(3, 3, false); break;
-      case 4: W12_EPI(4, 4, false); break;
-      case 5: W12_EPI(5, 5, false); break;
-      case 6: W12_EPI(6, 6, false); break;
-      case 7: W12_EPI(7, 7, false); break;
-      case 8: W12_EPI(8, 8, false); break;
-      case 9: W12_EPI(9, 9, false); break;
-      case 10: W12_EPI(10, 10, false); break;
-      case 11: W12_EPI(11, 11, false); break;
-      case 12: W12_EPI(12, 12, false); break;
-      case 13: W12_EPI(13, 13, false); break;
-      case 14: W12_EPI(14, 14, false); break;
-      default: W12_EPI(15, 15, false); break;
+      W12_VCASE(1) W12_VCASE(2) W12_VCASE(3) W12_VCASE(4) W12_VCASE(5)
+      W12_VCASE(6) W12_VCASE(7) W12_VCASE(8) W12_VCASE(9) W12_VCASE(10)
+      W12_VCASE(11) W12_VCASE(12) W12_VCASE(13) W12_VCASE(14) W12_VCASE(15)
+      default: break;
     }
+#undef W12_VCASE
   }
+#undef W12_CS_EPI
+#undef W12_CS
 #undef W12_EPI
 #undef W12_RBW
 #undef W12_L

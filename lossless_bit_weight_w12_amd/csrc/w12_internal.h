@@ -5,6 +5,13 @@
 #include <stddef.h>
 #include <stdint.h>
 
+// m from which the MFMA path runs; below it the VALU v_dot2 path.  Measured on the MLP
+// shapes: from m = 4 the VALU path is VALU-issue-bound and the MFMA path (x zero-padded
+// to 16 rows) is faster.
+#ifndef W12_MFMA_MIN_M
+#define W12_MFMA_MIN_M 4
+#endif
+
 namespace w12 {
 
 // Weight source of the GEMM kernel family.
@@ -35,8 +42,17 @@ struct GemmArgs {
   uint32_t basepair;        // C[0] | C[0] << 16 (SRC_RUN)
 };
 
+// Kernel shapes of the GEMM family.
+enum Kind : int {
+  KIND_WAVE_COLUMNS = 0,    // k_gemm: each wave streams its own tile columns (VALU or MFMA)
+  KIND_COLUMN_SYNC = 1,     // k_gemm_cs: a workgroup's waves share each x column (MFMA)
+};
+
 struct GemmPlan {
-  int rbw;                  // row-blocks per workgroup (1 or 2)
+  int kind;                 // Kind
+  bool mfma;                // KIND_WAVE_COLUMNS: MFMA (m >= W12_MFMA_MIN_M) or VALU
+  int rbw;                  // KIND_WAVE_COLUMNS: row-blocks per wave (1 or 2)
+  int nw;                   // KIND_COLUMN_SYNC: waves (= row-blocks) per workgroup (4 or 8)
   uint32_t nsplit;          // K splits across workgroups
   uint32_t cols_per_split;  // tile columns per split
   uint32_t n_rbg;           // row-block groups = ceil(nb / rbw)
