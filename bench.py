@@ -9,11 +9,23 @@ resident in HBM.  The same step on plain BF16 weights with the same kernel famil
 gives the speedup.  Weight copies are rotated so that no GEMM finds its weights in the
 256 MB Infinity Cache.
 
-    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+Two more workloads are timed in the same run and reported beside the main line:
+the LM-head greedy verification ([151936, 5120], M = 16) and a whole weight-streaming
+decode step (64 layers of q, k, v, o, gate, up, down + LM head, M = 24, RMS-chained).
+
+`roofline.traffic` is the HBM traffic of the dominant launch measured by rocprofv3
+counters (FETCH_SIZE and WRITE_SIZE passes over `--profile-only --calibrate-copy`,
+scaled by what the counters read for a 1 GiB device copy); it is read from
+profiles/w12_gemm_traffic.json and reported only while the kernel sources still hash to
+the value recorded there (null otherwise).
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline] [--no-extras]
 """
 from __future__ import annotations
 
 import argparse
+import glob
+import hashlib
 import json
 import os
 import platform
@@ -76,6 +88,134 @@ def cpu_baseline(seconds_target: float = 12.0):
                       f"{t_total:.1f} s; BLAS threads {blas_threads}"}
 
 
+COPY_BYTES = 1 << 30
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "w12_gemm_traffic.json")
+
+
+def kernel_source_hash() -> str:
+    """sha256 over the library's sources and header: counters taken on other sources
+    do not describe the kernels that run now."""
+    h = hashlib.sha256()
+    files = sorted(glob.glob(os.path.join(ROOT, "lossless_bit_weight_w12_amd", "csrc", "*")))
+    files.append(os.path.join(ROOT, "include", "w12.h"))
+    for f in files:
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(dom_key: str):
+    """HBM bytes per launch of the dominant GEMM from the recorded counter passes, or
+    None when no record matches the current sources."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None, "no counter record"
+    if rec.get("source_sha256") != kernel_source_hash():
+        return None, "kernel sources changed since the counters were taken"
+    k = rec.get("launches", {}).get(dom_key)
+    if k is None:
+        return None, f"no counter record for {dom_key}"
+    return int(k["hbm_bytes"]), (f"FETCH_SIZE x {rec['fetch_scale']:.4f} + WRITE_SIZE x "
+                                 f"{rec['write_scale']:.4f} per launch ({rec['profile']})")
+
+
+def time_calls(torch, fn, reps: int, warmup: int = 3) -> float:
+    """Mean milliseconds per call of fn() over reps calls between one event pair."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def extra_workloads(torch, w12, wi, np, dev, args):
+    """LM-head verification (M = 16) and the 64-layer decode step (M = 24).  Weights
+    are drawn on the device (randn * 0.02 -> BF16, seeded) and encoded by the library."""
+    from lossless_bit_weight_w12_amd.decode_step import DecodeStack, MATS
+    c5 = wi.CONFIG_SHAPES[5]
+    vocab, hid, m5 = c5["vocab"], c5["hidden"], c5["m"][0]
+    t0 = time.time()
+    head = w12.encode(wi.device_lm_head(torch, vocab, hid))
+    torch.cuda.synchronize()
+    log(f"bench: LM head encoded in {time.time() - t0:.1f} s; timing verification ...")
+
+    # ---- LM-head greedy verification, M = 16
+    x16 = torch.from_numpy(wi.verify_batch_x(0).view(np.int16)).to(dev)
+    am, _ = w12.lmhead_verify(x16, head, torch.zeros(0, dtype=torch.int32, device=dev))
+    p, r = wi.verify_mismatch(0, vocab)
+    draft = am.clone()
+    if p < 16:
+        draft[p] = (draft[p] + 1 + r) % vocab
+    am_out = torch.empty(16, dtype=torch.int32, device=dev)
+    acc_out = torch.empty(1, dtype=torch.int32, device=dev)
+    vcall = w12.prepare_verify(x16, head, draft, am_out, acc_out)
+    ms_verify = time_calls(torch, vcall, 50)
+    accepted = int(acc_out.item())
+    y16 = torch.empty((16, vocab), dtype=torch.bfloat16, device=dev)
+    gcall = w12.prepare_gemm(x16, head, y16)
+    ms_gemm16 = time_calls(torch, gcall, 50)
+    v_bytes = head.nbytes() + 2 * 16 * hid + 8 * 16 * vocab + 4 * 16
+    g_bytes = head.nbytes() + 2 * 16 * hid + 2 * 16 * vocab
+    verify = {
+        "workload": f"LM head [{vocab}x{hid}] W12, M=16, greedy verify of a 16-token draft",
+        "us_per_verify": round(ms_verify * 1e3, 1),
+        "gbps_verify": round(v_bytes / (ms_verify * 1e-3) / 1e9, 1),
+        "pct_peak_verify": round(100 * v_bytes / (ms_verify * 1e-3) / 1e9 / PEAK_GBPS, 1),
+        "us_gemm_bf16_out_same_shape": round(ms_gemm16 * 1e3, 1),
+        "gbps_gemm_same_shape": round(g_bytes / (ms_gemm16 * 1e-3) / 1e9, 1),
+        "verify_overhead_us": round((ms_verify - ms_gemm16) * 1e3, 1),
+        "accepted": accepted, "planted_mismatch_at": p,
+        "accepted_matches_plant": accepted == p}
+    log(f"bench: verify {verify['us_per_verify']} us ({verify['gbps_verify']} GB/s); "
+        f"building the 64-layer stack ...")
+
+    # ---- decode step, 64 layers + head, M = 24
+    t0 = time.time()
+    shapes = {name: (n, k) for name, n, k in wi.LAYER_MATS}
+    layers = []
+    for li in range(c5["layers"]):
+        L = {}
+        for mi, name in enumerate(MATS):
+            n, k = shapes[name]
+            L[name] = w12.encode(wi.device_layer_weight(torch, li, mi, n, k))
+        layers.append(L)
+        if li % 16 == 15:
+            log(f"bench: {li + 1} layers encoded ({time.time() - t0:.1f} s)")
+    torch.cuda.synchronize()
+    stack = DecodeStack(layers, head, m5)
+    h0 = torch.from_numpy(wi.decode_step_x(m5, hid).view(np.int16)).to(dev)
+    d5 = torch.from_numpy(wi.decode_step_draft(vocab, m5)).to(dev)
+    stack.prepare(d5)
+
+    def one_step():
+        stack.h.copy_(h0)
+        stack.run()
+    ms_step = time_calls(torch, one_step, args.decode_steps, warmup=2)
+    wb, io = stack.weight_bytes(), stack.io_bytes()
+    n_params = sum(t.n * t.k for L in layers for t in L.values()) + head.n * head.k
+    step = {
+        "workload": f"decode step: {c5['layers']} layers x (q,k,v,o,gate,up,down) + LM head "
+                    f"verify, M={m5}, RMS-chained, {n_params} params",
+        "ms_per_step": round(ms_step, 3),
+        "tokens_per_s_equiv": round(1e3 / ms_step, 1),
+        "rows_per_s": round(m5 * 1e3 / ms_step, 1),
+        "w12_weight_gb": round(wb / 1e9, 3), "io_gb": round(io / 1e9, 4),
+        "gbps": round((wb + io) / (ms_step * 1e-3) / 1e9, 1),
+        "pct_peak": round(100 * (wb + io) / (ms_step * 1e-3) / 1e9 / PEAK_GBPS, 1),
+        "bits_per_weight": round(8 * wb / n_params, 5),
+        "timed_steps": args.decode_steps, "setup_s": round(time.time() - t0, 1)}
+    log(f"bench: decode step {step['ms_per_step']} ms ({step['gbps']} GB/s)")
+    return verify, step
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -87,6 +227,12 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-only", action="store_true",
                     help="run a few W12 steps and exit (for rocprofv3)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="with --profile-only: also run a 1 GiB device-to-device copy, the "
+                         "known-size kernel that scales the traffic counters")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the LM-head verification and decode-step workloads")
+    ap.add_argument("--decode-steps", type=int, default=20)
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported (this path has no "
@@ -130,6 +276,7 @@ def main():
               torch.empty((m, N_DN), dtype=torch.bfloat16, device=dev)) for m in MS}
     torch.cuda.synchronize()
     log(f"bench: bits/weight gate+up {t_gu[0].bits_per_weight():.5f}, down {t_dn[0].bits_per_weight():.5f}")
+    log(f"bench: W12 bytes gate_up {t_gu[0].nbytes()} down {t_dn[0].nbytes()}")
 
     def w12_step(c):
         for m in MS:
@@ -145,6 +292,12 @@ def main():
         for i in range(args.steps):
             w12_step(i)
             bf16_step(i)
+        if args.calibrate_copy:
+            src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev)
+            dst = torch.empty_like(src)
+            src.fill_(1)
+            torch.cuda.synchronize()
+            dst.copy_(src)
         torch.cuda.synchronize()
         log("bench: profile-only run done")
         return
@@ -207,9 +360,11 @@ def main():
     m_dom = int(dom_key.split("_")[0][1:])
     t_dom = t_gu[0] if dom_key.endswith("gate_up") else t_dn[0]
     alg = gemm_bytes(t_dom, m_dom)
+    traffic, traffic_note = measured_traffic(dom_key)
     roofline = {"bound": "hbm", "achieved": round(alg / dom["us_w12"] / 1e3, 1), "peak": PEAK_GBPS,
                 "unit": "GB/s", "frac": round(alg / dom["us_w12"] / 1e3 / PEAK_GBPS, 4),
-                "traffic": None, "kernel": f"w12_gemm {dom_key}", "alg_bytes_per_launch": alg,
+                "traffic": traffic, "traffic_note": traffic_note,
+                "kernel": f"w12_gemm {dom_key}", "alg_bytes_per_launch": alg,
                 "avg_launch_us": dom["us_w12"]}
 
     value = step_bytes / (ms_w12 * 1e-3) / 1e9
@@ -233,6 +388,10 @@ def main():
         "host": {"cpu": platform.processor() or platform.machine(),
                  "affinity_cores": len(os.sched_getaffinity(0))},
     }
+    if not args.no_extras:
+        del t_gu, t_dn, b_gu, b_dn, w_gu, w_dn
+        torch.cuda.empty_cache()
+        out["lm_head_verify"], out["decode_step"] = extra_workloads(torch, w12, wi, np, dev, args)
     if not args.no_cpu_baseline:
         log("bench: timing the CPU oracle on a bounded sample ...")
         out["cpu_baseline"] = cpu_baseline()

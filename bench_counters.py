@@ -1,0 +1,121 @@
+"""Turn two rocprofv3 counter passes over `bench.py --profile-only --calibrate-copy` into
+the per-launch HBM traffic record that bench.py reports as `roofline.traffic`.
+
+    python bench_counters.py FETCH_DIR WRITE_DIR "<profile command>" PROFILE_LOG
+
+FETCH_DIR / WRITE_DIR hold run_counter_collection.csv from
+    rocprofv3 --pmc FETCH_SIZE -d FETCH_DIR -o run --output-format csv -- python3 bench.py --profile-only --steps 2 --calibrate-copy
+and the same with WRITE_SIZE.  Both counters are per dispatch, in KiB.  The scales come
+from the known-size kernels at the end of the run: the 1 GiB device-to-device copy
+(reads 1 GiB) and the 1 GiB fill before it (writes 1 GiB).  A `w12_gemm` launch is its
+GEMM kernel plus, when K is split, the reduction kernel that follows it.  Writes
+profiles/w12_gemm_traffic.json and profiles/w12_gemm_mlp_block_traffic.md.
+"""
+from __future__ import annotations
+
+import csv
+import json
+import os
+import sys
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+
+ENCODE_KERNELS = ("k_fill_zero", "k_hist", "k_codebook", "k_count_tiles", "k_scan", "k_pack")
+
+
+def read(d: str, counter: str):
+    rows = []
+    with open(os.path.join(d, "run_counter_collection.csv")) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] != counter:
+                continue
+            rows.append((int(r["Dispatch_Id"]), r["Kernel_Name"], int(r["Grid_Size"]),
+                         float(r["Counter_Value"])))
+    rows.sort()
+    return rows
+
+
+def launches(rows):
+    """Group the GEMM-family dispatches into w12_gemm / w12_gemm_bf16 launches."""
+    out = []
+    for _, name, grid, val in rows:
+        if "w12::" not in name or any(k in name for k in ENCODE_KERNELS):
+            continue
+        short = name.split("(")[0].replace("void ", "")
+        if "k_splitk_reduce" in short:
+            out[-1]["kernels"].append(short)
+            out[-1]["value"] += val
+        else:
+            out.append({"kernels": [short], "grid": grid, "value": val})
+    return out
+
+
+def main():
+    fetch_dir, write_dir, command, log_path = sys.argv[1:5]
+    w12_bytes = {}
+    with open(log_path) as f:
+        for line in f:
+            if line.startswith("bench: W12 bytes"):
+                t = line.split()
+                w12_bytes = {t[3]: int(t[4]), t[5]: int(t[6])}
+    shapes = {"gate_up": (bench.N_GU, bench.K_GU), "down": (bench.N_DN, bench.K_DN)}
+    fr, wr = read(fetch_dir, "FETCH_SIZE"), read(write_dir, "WRITE_SIZE")
+    # calibration: the last copy kernel reads 1 GiB; the fill before it writes 1 GiB
+    tail_f = [r for r in fr if r[0] > max(x[0] for x in fr if "w12::" in x[1])]
+    tail_w = [r for r in wr if r[0] > max(x[0] for x in wr if "w12::" in x[1])]
+    copy_f = max(tail_f, key=lambda r: r[3])
+    fill_w = max(tail_w, key=lambda r: r[3])
+    fetch_scale = bench.COPY_BYTES / (copy_f[3] * 1024.0)
+    write_scale = bench.COPY_BYTES / (fill_w[3] * 1024.0)
+    lf, lw = launches(fr), launches(wr)
+    assert len(lf) == len(lw) and len(lf) % 20 == 0, (len(lf), len(lw))
+    keys = [f"M{m}_{name}" for m in bench.MS for name in ("gate_up", "down")]
+    rec = {"source_sha256": bench.kernel_source_hash(), "profile": command,
+           "fetch_scale": fetch_scale, "write_scale": write_scale,
+           "calibration": {"copy_kernel": copy_f[1][:80], "copy_fetch_kib": copy_f[3],
+                           "fill_kernel": fill_w[1][:80], "fill_write_kib": fill_w[3],
+                           "bytes": bench.COPY_BYTES},
+           "launches": {}, "bf16_launches": {}}
+    steps = len(lf) // 20
+    for i, key in enumerate(keys):
+        for kind, off in (("launches", 0), ("bf16_launches", 10)):
+            idx = [20 * s + off + i for s in range(steps)]
+            f_kib = sum(lf[j]["value"] for j in idx) / steps
+            w_kib = sum(lw[j]["value"] for j in idx) / steps
+            m = int(key.split("_")[0][1:])
+            n, k = shapes[key.split("_", 1)[1]]
+            wb = w12_bytes[key.split("_", 1)[1]] if kind == "launches" else 2 * n * k
+            rec[kind][key] = {"kernels": lf[idx[0]]["kernels"], "grid": lf[idx[0]]["grid"],
+                              "fetch_kib": round(f_kib, 3), "write_kib": round(w_kib, 3),
+                              "hbm_bytes": int(round(f_kib * 1024 * fetch_scale
+                                                     + w_kib * 1024 * write_scale)),
+                              "alg_bytes": wb + 2 * m * k + 2 * m * n}
+    with open(os.path.join(ROOT, "profiles", "w12_gemm_traffic.json"), "w") as f:
+        json.dump(rec, f, indent=1)
+    lines = ["# HBM traffic per launch: MLP block GEMMs (rocprofv3 counters)", "",
+             "Commands (from the repository root, on one MI355X):", "",
+             f"    {command.replace('PMC', 'FETCH_SIZE').replace('DIR', 'gpurun_out/pmc_fetch')}",
+             f"    {command.replace('PMC', 'WRITE_SIZE').replace('DIR', 'gpurun_out/pmc_write')}",
+             f"    python bench_counters.py gpurun_out/pmc_fetch gpurun_out/pmc_write \"<command>\"",
+             "",
+             f"Scales: FETCH_SIZE x {fetch_scale:.4f} (a 1 GiB device copy, `{copy_f[1][:40]}`, "
+             f"reads {copy_f[3]:.0f} KiB), WRITE_SIZE x {write_scale:.4f} (a 1 GiB fill, "
+             f"`{fill_w[1][:40]}`, writes {fill_w[3]:.0f} KiB).  Source sha256 "
+             f"`{rec['source_sha256'][:16]}...`.", "",
+             "| launch | kernels | W12: HBM bytes | algorithmic | ratio | BF16 kernel: HBM bytes | algorithmic | ratio |",
+             "|---|---|---|---|---|---|---|---|"]
+    for key in keys:
+        a, b = rec["launches"][key], rec["bf16_launches"][key]
+        lines.append(f"| {key} | `{' + '.join(a['kernels'])}` | {a['hbm_bytes']:,} | {a['alg_bytes']:,} | "
+                     f"{a['hbm_bytes'] / a['alg_bytes']:.3f} | {b['hbm_bytes']:,} | {b['alg_bytes']:,} | "
+                     f"{b['hbm_bytes'] / b['alg_bytes']:.3f} |")
+    with open(os.path.join(ROOT, "profiles", "w12_gemm_mlp_block_traffic.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(json.dumps({k: v["hbm_bytes"] for k, v in rec["launches"].items()}))
+
+
+if __name__ == "__main__":
+    main()

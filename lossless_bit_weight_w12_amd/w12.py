@@ -126,9 +126,9 @@ _WS = {}
 
 
 def workspace(nbytes: int, device, purpose: str = "gemm"):
-    """A zero-initialised workspace of at least nbytes on `device`, cached per purpose
-    ("gemm" for both GEMM entry points, whose split-K counters the library leaves at
-    zero; "verify"; "encode"), grown on demand."""
+    """A workspace of at least nbytes on `device`, cached per purpose ("gemm" for both
+    GEMM entry points, "verify", "encode") so that calls of different kinds queued on
+    one stream never share scratch memory; grown on demand."""
     torch = _torch()
     dev = torch.device(device)
     key = (dev.index if dev.index is not None else torch.cuda.current_device(), purpose)
@@ -274,3 +274,49 @@ def rms_rescale(x, out=None):
         out = torch.empty_like(x)
     _check("w12_rms_rescale", lib().w12_rms_rescale(_ptr(x), m, k, _ptr(_as_bits(out)), _stream(x.device)))
     return out
+
+
+# ----------------------------------------------------------------------------- prepared calls
+class Prepared:
+    """One library call with its arguments marshalled once (device pointers, descriptor,
+    workspace, stream); calling it re-issues the call with no other Python work.  The
+    tensors it refers to must stay alive, and the stream is the one current when it was
+    prepared."""
+
+    def __init__(self, name: str, fn, args, keep):
+        self.name, self._fn, self._args, self._keep = name, fn, args, keep
+
+    def __call__(self):
+        st = self._fn(*self._args)
+        if st != 0:
+            raise W12Error(self.name, st)
+
+
+def prepare_gemm(x, t: W12Tensor, out) -> Prepared:
+    x, out = _as_bits(x), _as_bits(out)
+    m = x.shape[0]
+    if x.shape[1] != t.k or tuple(out.shape) != (m, t.n):
+        raise ValueError("prepare_gemm: x must be [m, k] and out [m, n]")
+    ws = workspace(max(workspace_bytes(OP_GEMM, m, t.n, t.k), 256), x.device)
+    d = t.desc()
+    args = (_ptr(x), m, ctypes.byref(d), _ptr(out), _ptr(ws), ws.numel(), _stream(x.device))
+    return Prepared("w12_gemm", lib().w12_gemm, args, (x, t, out, ws, d))
+
+
+def prepare_rms(x, out) -> Prepared:
+    x, out = _as_bits(x), _as_bits(out)
+    m, k = x.shape
+    args = (_ptr(x), m, k, _ptr(out), _stream(x.device))
+    return Prepared("w12_rms_rescale", lib().w12_rms_rescale, args, (x, out))
+
+
+def prepare_verify(x, t: W12Tensor, draft, argmax_out, accepted_out) -> Prepared:
+    x = _as_bits(x)
+    m = x.shape[0]
+    n_draft = int(draft.numel())
+    ws = workspace(workspace_bytes(OP_VERIFY, m, t.n, t.k), x.device, "verify")
+    d = t.desc()
+    args = (_ptr(x), m, ctypes.byref(d), _ptr(draft) if n_draft else None, n_draft,
+            _ptr(argmax_out), _ptr(accepted_out), _ptr(ws), ws.numel(), _stream(x.device))
+    return Prepared("w12_lmhead_verify", lib().w12_lmhead_verify, args,
+                    (x, t, draft, argmax_out, accepted_out, ws, d))

@@ -133,13 +133,20 @@ def check_shape(n: int, k: int):
 
 
 # ----------------------------------------------------------------------------- encode
-def encode(w: np.ndarray, rows_per_chunk: int = 4096) -> W12Blob:
-    """W12 v1 encode of BF16 bits w [N, K] (uint16)."""
+def encode(w: np.ndarray, rows_per_chunk: int = 4096, codebook=None) -> W12Blob:
+    """W12 v1 encode of BF16 bits w [N, K] (uint16).
+
+    The bytes of a row-block depend only on its 16 rows and the tensor's codebook, so
+    passing the codebook of a larger tensor encodes a band of its row-blocks exactly as
+    the whole-tensor encode would (escape offsets then count from the band's start;
+    e_max stays that of the rows given)."""
     w = np.ascontiguousarray(w, dtype=np.uint16)
     n, k = w.shape
     check_shape(n, k)
     hist = exponent_histogram(w)
-    cb = choose_codebook(hist)
+    cb = choose_codebook(hist) if codebook is None else np.asarray(codebook, dtype=np.uint8)
+    if cb.shape != (16,) or np.any(np.diff(cb.astype(np.int64)) <= 0):
+        raise ValueError("codebook must be 16 strictly ascending exponents")
     code_of = np.full(256, -1, dtype=np.int64)
     code_of[cb.astype(np.int64)] = np.arange(16)
     nb, gk = n // TILE_ROWS, k // TILE_K

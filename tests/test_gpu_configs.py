@@ -1,0 +1,215 @@
+"""The five workloads at full size on the GPU, through the C ABI, against the oracle.
+
+1  W [1024, 1024], x [1, 1024]: encode bytes, decode, GEMV, every output.
+2  W [5120, 5120] with 0.1 % exponent outliers, x [1, 5120]: encode bytes (escape path),
+   decode, GEMV, every output.
+3  MLP block: gate+up [34816, 5120] and down [5120, 17408], M in {1, 4, 8, 16, 32}:
+   encode bytes, decode, every output of every GEMM (W12 and the BF16 kernel).
+4  LM head [151936, 5120], three M = 16 batches (batch 0 plain, batches 1-2 the 32 rows
+   with planted near-ties): codebook, escape count and decode of the whole head, bytes of
+   sampled row-block bands, argmax and accepted length of every row against the oracle.
+5  Decode step: 64 layers of q, k, v, o, gate, up, down + LM head drawn on the device,
+   M = 24, RMS-chained; at layers 0, 21, 42, 63 every GEMM output is checked against the
+   oracle on the captured inputs and every weight's decode against its regenerated
+   source; the final verification against the oracle's exact argmax.
+
+Bars as in the other GPU tests: bytes, bits, argmax and accepted length exact; GEMM
+outputs by oracle.gemm_accept."""
+import numpy as np
+import pytest
+
+from oracle import w12_oracle as o
+import w12_inputs as wi
+import plant
+from gpu_util import say, to_dev, to_host
+
+pytestmark = [pytest.mark.gpu, pytest.mark.slow]
+
+
+@pytest.fixture(scope="module")
+def env():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a visible MI355X"
+    import lossless_bit_weight_w12_amd as w12
+    w12.lib()
+    return torch, w12
+
+
+def _check_encode(t, w):
+    ref = o.encode(w)
+    assert t.codebook == tuple(ref.codebook.tolist())
+    assert t.e_max == ref.e_max and t.n_esc == ref.n_esc
+    assert np.array_equal(t.tiles.cpu().numpy(), ref.tiles)
+    assert np.array_equal(t.esc_off.cpu().numpy().view(np.uint32), ref.esc_off)
+    assert np.array_equal(t.esc.cpu().numpy().view(np.uint32)[:ref.n_esc], ref.esc)
+    assert t.nbytes() == o.blob_bytes(ref)
+    return ref
+
+
+def _check_gemm(y_dev, x, w):
+    z, s = o.gemm_reference(x, w)
+    y = to_host(y_dev)
+    ok = o.gemm_accept(y, z, s)
+    bad = np.argwhere(~ok)
+    assert ok.all(), f"{bad.shape[0]} outputs outside tolerance, first {bad[:4].tolist()}"
+
+
+def _check_summary(torch, w12, t, w_host, w_dev, bands):
+    """Codebook, e_max and escape count from the oracle's histogram of the whole
+    tensor, the whole tensor's decode, and the bytes and escape records of sampled
+    row-block bands encoded by the oracle with that codebook."""
+    hist = o.exponent_histogram(w_host)
+    cb = o.choose_codebook(hist)
+    assert t.codebook == tuple(cb.tolist())
+    assert t.e_max == o.finite_e_max(hist)
+    assert t.n_esc == int(hist.sum() - hist[cb.astype(np.int64)].sum())
+    assert torch.equal(w12.decode(t).view(torch.int16), w_dev.view(torch.int16))
+    gk = t.k // 128
+    esc_off = t.esc_off.cpu().numpy().view(np.uint32)
+    for b0, b1 in bands:
+        ref = o.encode(w_host[16 * b0:16 * b1], codebook=cb)
+        got = t.tiles[b0 * gk * 3072:b1 * gk * 3072].cpu().numpy()
+        assert np.array_equal(got, ref.tiles), (b0, b1)
+        lo, hi = int(esc_off[b0]), int(esc_off[b1])
+        assert np.array_equal(esc_off[b0:b1 + 1] - lo, ref.esc_off)
+        assert np.array_equal(t.esc[lo:hi].cpu().numpy().view(np.uint32), ref.esc)
+
+
+def test_config1_layer_1024(env):
+    torch, w12 = env
+    w = wi.config_weights(1)["w"]
+    x = wi.activations(1, wi.T_X, 1, 1024)
+    say("config 1", w.shape)
+    t = w12.encode(to_dev(w, torch))
+    ref = _check_encode(t, w)
+    assert np.array_equal(to_host(w12.decode(t)), w)
+    _check_gemm(w12.gemm(to_dev(x, torch), t), x, w)
+    say("config 1 bits/weight", o.bits_per_weight(ref), "escapes", ref.n_esc)
+
+
+def test_config2_outliers_escape_path(env):
+    torch, w12 = env
+    w = wi.config_weights(2)["w"]
+    x = wi.activations(2, wi.T_X, 1, 5120)
+    say("config 2", w.shape)
+    t = w12.encode(to_dev(w, torch))
+    ref = _check_encode(t, w)
+    assert ref.n_esc >= 0.0005 * w.size
+    assert np.array_equal(to_host(w12.decode(t)), w)
+    xt = to_dev(x, torch)
+    _check_gemm(w12.gemm(xt, t), x, w)
+    _check_gemm(w12.gemm_bf16(xt, to_dev(w, torch)), x, w)
+    say("config 2 bits/weight", o.bits_per_weight(ref), "escapes", ref.n_esc)
+
+
+@pytest.mark.parametrize("name", ["gate_up", "down"])
+def test_config3_mlp_block(env, name):
+    torch, w12 = env
+    w = wi.weight(3, wi.T_W if name == "gate_up" else wi.T_W2, wi.CONFIG_SHAPES[3][name])
+    n, k = w.shape
+    say("config 3", name, w.shape)
+    wd = to_dev(w, torch)
+    t = w12.encode(wd)
+    _check_encode(t, w)
+    assert torch.equal(w12.decode(t).view(torch.int16), wd.view(torch.int16))
+    for m in wi.CONFIG_SHAPES[3]["m"]:
+        say("config 3", name, "m", m)
+        x = wi.activations(3, wi.T_X if name == "gate_up" else wi.T_X2, m, k)
+        xt = to_dev(x, torch)
+        y = w12.gemm(xt, t)
+        yb = w12.gemm_bf16(xt, wd)
+        _check_gemm(y, x, w)
+        _check_gemm(yb, x, w)
+        # same decoded weights, same MAC order: the two kernels agree bit for bit
+        assert torch.equal(y.view(torch.int16), yb.view(torch.int16))
+
+
+@pytest.fixture(scope="module")
+def lm_head():
+    """Workload 4's head with the 32 near-tie rows of batches 1-2 planted, and the three
+    hidden batches."""
+    w = wi.config_weights(4)["w"]
+    xs = [wi.verify_batch_x(b) for b in range(wi.VERIFY_BATCHES)]
+    tie_x = np.concatenate(xs[1:])
+    say("config 4 planting", tie_x.shape[0], "near-tie rows")
+    w, pairs = plant.plant_near_ties(tie_x, w, lambda i: wi.tie_rng(1 + i // 16, i % 16))
+    plant.check_plants(tie_x, w, pairs)
+    return w, xs
+
+
+def test_config4_lm_head_verify(env, lm_head):
+    torch, w12 = env
+    w, xs = lm_head
+    vocab = w.shape[0]
+    wd = to_dev(w, torch)
+    t = w12.encode(wd)
+    nb = vocab // 16
+    _check_summary(torch, w12, t, w, wd, [(0, 3), (nb // 2, nb // 2 + 2), (nb - 3, nb)])
+    del wd
+    x_all = np.concatenate(xs)
+    am_ref, ncand_ref = o.argmax_exact(x_all, w)
+    say("config 4 oracle candidates per row", ncand_ref.tolist())
+    for b, x in enumerate(xs):
+        ref = am_ref[16 * b:16 * b + 16]
+        p, r = wi.verify_mismatch(b, vocab)
+        draft = ref.astype(np.int32).copy()
+        if p < 16:
+            draft[p] = (draft[p] + 1 + r) % vocab
+        say("config 4 batch", b, "p", p)
+        am, acc = w12.lmhead_verify(to_dev(x, torch), t, torch.from_numpy(draft).to("cuda:0"))
+        torch.cuda.synchronize()
+        assert am.cpu().numpy().tolist() == ref.tolist()
+        assert int(acc.item()) == o.accepted_length(ref, draft) == p
+        nc = w12.verify_candidates(t, 16).cpu().numpy()
+        say("config 4 batch", b, "GPU candidates per row", nc.tolist())
+        assert (nc >= 1).all()
+
+
+SAMPLED_LAYERS = (0, 21, 42, 63)
+
+
+def test_config5_decode_step(env):
+    torch, w12 = env
+    from lossless_bit_weight_w12_amd.decode_step import DecodeStack, MATS
+    c5 = wi.CONFIG_SHAPES[5]
+    m, hid, vocab = c5["m"][0], c5["hidden"], c5["vocab"]
+    shapes = {name: (n, k) for name, n, k in wi.LAYER_MATS}
+    layers = []
+    for li in range(c5["layers"]):
+        if li % 8 == 0:
+            say("config 5 encoding layer", li)
+        L = {}
+        for mi, name in enumerate(MATS):
+            n, k = shapes[name]
+            L[name] = w12.encode(wi.device_layer_weight(torch, li, mi, n, k))
+        layers.append(L)
+    head = w12.encode(wi.device_lm_head(torch, vocab, hid))
+    stack = DecodeStack(layers, head, m)
+    x0 = wi.decode_step_x(m, hid)
+    draft = wi.decode_step_draft(vocab, m)
+    say("config 5 running the step")
+    h, am, acc, caps = stack.step(to_dev(x0, torch), torch.from_numpy(draft).to("cuda:0"),
+                                  capture=SAMPLED_LAYERS)
+    torch.cuda.synchronize()
+    inputs = {"q": "h", "k": "h", "v": "h", "o": "a", "gate": "b", "up": "b", "down": "c"}
+    for li in SAMPLED_LAYERS:
+        cap = caps[li]
+        for mi, name in enumerate(MATS):
+            n, k = shapes[name]
+            say("config 5 layer", li, name)
+            src = wi.device_layer_weight(torch, li, mi, n, k)
+            assert torch.equal(w12.decode(layers[li][name]).view(torch.int16), src.view(torch.int16))
+            w_host = to_host(src)
+            _check_gemm(cap[name], to_host(cap[inputs[name]]), w_host)
+        # the chain's rescaled rows have unit mean square (BF16 rounding aside)
+        for key in ("a", "b", "c"):
+            v = cap[key].float()
+            ms = (v * v).mean(dim=1)
+            assert torch.all((ms - 1).abs() < 1e-2), (li, key, ms)
+    # final verification against the oracle on the captured final h
+    say("config 5 LM head verify")
+    w_head = to_host(wi.device_lm_head(torch, vocab, hid))
+    h_host = to_host(h)
+    am_ref, _ = o.argmax_exact(h_host, w_head)
+    assert am.cpu().numpy().tolist() == am_ref.tolist()
+    assert int(acc.item()) == o.accepted_length(am_ref, draft)

@@ -144,6 +144,28 @@ def test_gaussian_codebook_and_escape_rate():
     assert 2e-5 < rate < 2e-4
 
 
+def test_band_encode_with_tensor_codebook_is_a_slice():
+    """A band of row-blocks encoded with the whole tensor's codebook gives exactly the
+    whole encode's bytes and escape records for those blocks (row-blocks are encoded
+    independently once the codebook is fixed); the sampled checks at full size rely
+    on this."""
+    g = np.random.default_rng(77)
+    w = wi.add_exponent_outliers(wi.gaussian_bf16((160, 384), 0.02, g), 0.01, 5)
+    w[37, 5] = 0x7F80
+    full = o.encode(w)
+    for b0, b1 in [(0, 1), (3, 7), (9, 10)]:
+        band = o.encode(w[16 * b0:16 * b1], codebook=full.codebook)
+        gk = 384 // 128
+        assert np.array_equal(band.tiles, full.tiles[b0 * gk * 3072:b1 * gk * 3072])
+        lo, hi = full.esc_off[b0], full.esc_off[b1]
+        assert np.array_equal(band.esc, full.esc[lo:hi])
+        assert np.array_equal(band.esc_off, full.esc_off[b0:b1 + 1] - lo)
+    with pytest.raises(ValueError):
+        o.encode(w, codebook=np.arange(15, dtype=np.uint8))
+    with pytest.raises(ValueError):
+        o.encode(w, codebook=np.array([5] * 16, dtype=np.uint8))
+
+
 def test_outlier_workload_escapes():
     w = wi.config_weights(2)["w"]
     b = o.encode(w)

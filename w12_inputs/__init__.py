@@ -142,3 +142,47 @@ def device_layer_weight(torch, layer: int, mat: int, n: int, k: int, device="cud
     w = torch.randn((n, k), generator=g, device=device, dtype=torch.float32)
     w.mul_(SIGMA_W)
     return w.to(torch.bfloat16)
+
+
+# ----------------------------------------------------------------------------- workload 4
+VERIFY_BATCHES = 3        # batch 0 plain, batches 1-2 carry the 32 near-tie rows
+
+
+def verify_batch_x(b: int, m: int = 16, k: int = 5120) -> np.ndarray:
+    """Hidden rows of LM-head batch b (~N(0,1) BF16)."""
+    if b == 0:
+        return activations(4, T_X, m, k)
+    return gaussian_bf16((m, k), 1.0, rng(4, T_X, 100 + b))
+
+
+def verify_mismatch(b: int, vocab: int, m: int = 16):
+    """(p, r) of batch b: the draft's first mismatch position p in 0..m (m = none) and
+    the offset r in [0, vocab - 2] that makes the wrong token."""
+    p = int(rng(4, T_P, b).integers(0, m + 1))
+    r = int(rng(4, T_R, b).integers(0, vocab - 1))
+    return p, r
+
+
+def tie_rng(b: int, row: int) -> np.random.Generator:
+    """Random choices of the near-tie plant for row `row` of batch b."""
+    return rng(4, T_TIE, 1000 * b + row)
+
+
+# ----------------------------------------------------------------------------- workload 5
+def device_lm_head_seed() -> int:
+    return device_layer_seed(64, 7)
+
+
+def device_lm_head(torch, vocab: int, k: int, device="cuda"):
+    """The decode step's LM head, drawn on the device like the layer matrices."""
+    return device_layer_weight(torch, 64, 7, vocab, k, device)
+
+
+def decode_step_x(m: int = 24, k: int = 5120) -> np.ndarray:
+    """h0 of the decode-step chain, ~N(0,1) BF16 [m, k]."""
+    return activations(5, T_X, m, k)
+
+
+def decode_step_draft(vocab: int, m: int = 24) -> np.ndarray:
+    """Seeded draft tokens for the chain's LM-head verify."""
+    return rng(5, T_P).integers(0, vocab, size=m).astype(np.int32)
