@@ -98,8 +98,9 @@ size_t w12_tiles_bytes(uint64_t n, uint64_t k);
 /* Workspace bytes needed by `op` for m rows (ignored by ENCODE/DECODE) and an
  * n x k weight; 0 for an invalid op or shape, and 0 when the op needs none (DECODE,
  * and GEMM shapes that are not split along K).  GEMM split along K needs FP32
- * partials [splits][m][n]; VERIFY holds FP32 logits [m][n] plus per-row-block maxima
- * and candidate lists; ENCODE holds the histogram and per-tile escape counts. */
+ * partials [splits][m][n]; VERIFY holds per-row candidate counts (int32 [m], at offset
+ * 0), FP32 logits [m][n], their error scales sum_k |x_k||w_k| [m][n], per-row-block
+ * maxima and candidate lists; ENCODE holds the histogram and per-tile escape counts. */
 size_t w12_workspace_bytes(int op, uint32_t m, uint64_t n, uint64_t k);
 
 /* Zero-fills `ws` on `stream` with a kernel (no hipMemset); a convenience, no call
@@ -144,9 +145,11 @@ w12_status w12_gemm_bf16(const uint16_t* x, uint32_t m, const uint16_t* w, uint6
  * device int32 [n_draft] (n_draft <= m).  Writes argmax_out device int32 [m]: the index
  * v maximising the EXACT logit sum_k x[row,k]*W[v,k], lowest index on exact ties; and
  * accepted_out device int32 [1]: the first i < n_draft with argmax[i] != draft[i], or
- * n_draft.  FP32 logits are computed once, then every v within a certified error
- * bound of the maximum is recomputed exactly, so the result does not depend on the
- * reduction order.  A row whose logits are not finite gets argmax -1. */
+ * n_draft.  FP32 logits z^_v and S_v = sum_k |x_k||w_vk| are computed once; with
+ * B(S) a bound on |z^ - z| for any summation order, every v whose upper bound
+ * z^_v + B(S_v) reaches the lower bound z^* - B(S_*) of the computed maximum is
+ * recomputed exactly, so the result does not depend on the reduction order.  A row
+ * whose logits are not finite gets argmax -1. */
 w12_status w12_lmhead_verify(const uint16_t* x, uint32_t m, const w12_desc* d,
                              const int32_t* draft, uint32_t n_draft, int32_t* argmax_out,
                              int32_t* accepted_out, void* ws, size_t ws_bytes,

@@ -92,19 +92,23 @@ size_t gemm_ws_bytes(uint32_t m, uint64_t n, uint64_t k) {
   return p.nsplit > 1 ? align256((size_t)p.nsplit * m * n * 4) : 0;
 }
 
+// Verify workspace: per-row candidate counts first (a fixed place for diagnostics),
+// then FP32 logits and S = sum |x||w| per logit, per-row-block maxima, candidate lists.
 struct VerifyLayout {
-  size_t logits, rbmax_v, rbmax_i, cand, ncand, total;
+  size_t ncand, logits, sabs, rbmax_v, rbmax_s, rbmax_i, cand, total;
 };
 
 VerifyLayout verify_layout(uint32_t m, uint64_t n) {
   VerifyLayout L;
   const uint64_t nb = n / 16;
-  L.logits = 0;
-  L.rbmax_v = L.logits + align256((size_t)m * n * 4);
-  L.rbmax_i = L.rbmax_v + align256((size_t)m * nb * 4);
+  L.ncand = 0;
+  L.logits = L.ncand + align256((size_t)m * 4);
+  L.sabs = L.logits + align256((size_t)m * n * 4);
+  L.rbmax_v = L.sabs + align256((size_t)m * n * 4);
+  L.rbmax_s = L.rbmax_v + align256((size_t)m * nb * 4);
+  L.rbmax_i = L.rbmax_s + align256((size_t)m * nb * 4);
   L.cand = L.rbmax_i + align256((size_t)m * nb * 4);
-  L.ncand = L.cand + align256((size_t)m * n * 4);
-  L.total = L.ncand + align256((size_t)m * 4);
+  L.total = L.cand + align256((size_t)m * n * 4);
   return L;
 }
 
@@ -305,7 +309,9 @@ w12_status w12_lmhead_verify(const uint16_t* x, uint32_t m, const w12_desc* d, c
   a.esc_off = d->esc_off;
   a.esc = d->esc;
   a.logits = (float*)(base + L.logits);
+  a.sabs = (float*)(base + L.sabs);
   a.rbmax_v = (float*)(base + L.rbmax_v);
+  a.rbmax_s = (float*)(base + L.rbmax_s);
   a.rbmax_i = (int32_t*)(base + L.rbmax_i);
   a.m = m;
   a.n = (uint32_t)d->n;
@@ -322,7 +328,9 @@ w12_status w12_lmhead_verify(const uint16_t* x, uint32_t m, const w12_desc* d, c
   v.esc_off = d->esc_off;
   v.esc = d->esc;
   v.logits = a.logits;
+  v.sabs = a.sabs;
   v.rbmax_v = a.rbmax_v;
+  v.rbmax_s = a.rbmax_s;
   v.rbmax_i = a.rbmax_i;
   v.cand = (int32_t*)(base + L.cand);
   v.ncand = (int32_t*)(base + L.ncand);

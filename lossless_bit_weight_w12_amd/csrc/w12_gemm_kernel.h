@@ -39,6 +39,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+constexpr uint32_t kAbs2 = 0x7FFF7FFFu;   // clears the sign bits of two packed BF16
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 256;
@@ -280,11 +281,16 @@ template <int M, int MT, bool MF, int RBW, int SRC, int EPI>
 __global__ __launch_bounds__(kThreads) void k_gemm(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ w,
     const uint32_t* __restrict__ esc_off, const uint32_t* __restrict__ esc,
-    uint16_t* __restrict__ y, float* __restrict__ out_f32, float* __restrict__ rbmax_v,
-    int32_t* __restrict__ rbmax_i, GemmParams p) {
+    uint16_t* __restrict__ y, float* __restrict__ out_f32, float* __restrict__ out_s,
+    float* __restrict__ rbmax_v, float* __restrict__ rbmax_s, int32_t* __restrict__ rbmax_i,
+    GemmParams p) {
   constexpr int NH = MF ? MT / 16 : 1;
+  // the logits epilogue also accumulates S = sum_k |x_k||w_k| per output (the scale of
+  // its rounding-error bound)
+  constexpr bool kS = EPI == EPI_LOGITS;
   __shared__ __align__(16) uint16_t xs[kWaves * MT * kXsStride];   // one x column per wave
-  __shared__ float fin[EPI == EPI_LOGITS ? RBW * MT * 16 : 1];
+  __shared__ float fin[kS ? RBW * MT * 16 : 1];
+  __shared__ float fin_s[kS ? RBW * MT * 16 : 1];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform, in an SGPR
@@ -295,14 +301,14 @@ __global__ __launch_bounds__(kThreads) void k_gemm(
   const uint32_t gb = min(p.g_cols, ga + p.cols_per_split);
   const uint32_t m_rows = MF ? p.m : (uint32_t)M;
 
-  float vacc[RBW][MF ? 1 : M];
-  f32x4 macc[RBW][NH];
+  float vacc[RBW][MF ? 1 : M], vsacc[RBW][MF ? 1 : M];
+  f32x4 macc[RBW][NH], msacc[RBW][NH];
 #pragma unroll
   for (int rb = 0; rb < RBW; ++rb) {
 #pragma unroll
-    for (int m = 0; m < (MF ? 1 : M); ++m) vacc[rb][m] = 0.f;
+    for (int m = 0; m < (MF ? 1 : M); ++m) vacc[rb][m] = vsacc[rb][m] = 0.f;
 #pragma unroll
-    for (int h = 0; h < NH; ++h) macc[rb][h] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int h = 0; h < NH; ++h) macc[rb][h] = msacc[rb][h] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
   EscCursor ec[RBW];
@@ -340,6 +346,10 @@ __global__ __launch_bounds__(kThreads) void k_gemm(
             const u32x4 av = {P[rb][4 * j], P[rb][4 * j + 1], P[rb][4 * j + 2], P[rb][4 * j + 3]};
             macc[rb][h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
                 __builtin_bit_cast(bf16x8_t, av), bv, macc[rb][h], 0, 0, 0);
+            if constexpr (kS)
+              msacc[rb][h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                  __builtin_bit_cast(bf16x8_t, av & kAbs2), __builtin_bit_cast(bf16x8_t, xv & kAbs2),
+                  msacc[rb][h], 0, 0, 0);
           }
         }
       } else {
@@ -349,9 +359,14 @@ __global__ __launch_bounds__(kThreads) void k_gemm(
 #pragma unroll
           for (int rb = 0; rb < RBW; ++rb)
 #pragma unroll
-            for (int pp = 0; pp < 4; ++pp)
+            for (int pp = 0; pp < 4; ++pp) {
               vacc[rb][m] = __builtin_amdgcn_fdot2_f32_bf16(
                   as_bf16x2(P[rb][4 * j + pp]), as_bf16x2(xv[pp]), vacc[rb][m], false);
+              if constexpr (kS)
+                vsacc[rb][m] = __builtin_amdgcn_fdot2_f32_bf16(
+                    as_bf16x2(P[rb][4 * j + pp] & 0x7FFF7FFFu), as_bf16x2(xv[pp] & 0x7FFF7FFFu),
+                    vsacc[rb][m], false);
+            }
         }
       }
     }
@@ -404,40 +419,47 @@ __global__ __launch_bounds__(kThreads) void k_gemm(
   }
   __syncthreads();   // LDS x no longer read: reuse it for the cross-wave reduction
 
-  // ---- cross-lane / cross-wave reduction into red[] (aliases xs)
+  // ---- cross-lane / cross-wave reduction into red[] (aliases xs); the S sums, when
+  // kept, go to a second region of the same size
   float* red = reinterpret_cast<float*>(xs);
-  if constexpr (MF) {
+  constexpr int kRed = MF ? kWaves * RBW * NH * 4 * 64 : kWaves * RBW * M * 16;
+  static_assert((kS ? 2 : 1) * kRed * sizeof(float) <= sizeof(xs), "reduction fits in xs");
+  auto to_red = [&](float* dst, float (*va)[MF ? 1 : M], f32x4 (*ma)[NH]) {
+    if constexpr (MF) {
 #pragma unroll
-    for (int rb = 0; rb < RBW; ++rb)
+      for (int rb = 0; rb < RBW; ++rb)
 #pragma unroll
-      for (int h = 0; h < NH; ++h)
+        for (int h = 0; h < NH; ++h)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          red[(((wave * RBW + rb) * NH + h) * 4 + i) * 64 + lane] = macc[rb][h][i];
-  } else {
+          for (int i = 0; i < 4; ++i)
+            dst[(((wave * RBW + rb) * NH + h) * 4 + i) * 64 + lane] = ma[rb][h][i];
+    } else {
 #pragma unroll
-    for (int rb = 0; rb < RBW; ++rb)
+      for (int rb = 0; rb < RBW; ++rb)
 #pragma unroll
-      for (int m = 0; m < M; ++m) {
-        float v = vacc[rb][m];
-        v += __shfl_xor(v, 16);
-        v += __shfl_xor(v, 32);
-        if (q == 0) red[((wave * RBW + rb) * M + m) * 16 + r] = v;
-      }
-  }
+        for (int m = 0; m < M; ++m) {
+          float v = va[rb][m];
+          v += __shfl_xor(v, 16);
+          v += __shfl_xor(v, 32);
+          if (q == 0) dst[((wave * RBW + rb) * M + m) * 16 + r] = v;
+        }
+    }
+  };
+  to_red(red, vacc, macc);
+  if constexpr (kS) to_red(red + kRed, vsacc, msacc);
   __syncthreads();
 
   constexpr int kOut = RBW * MT * 16;   // (rb, m, row) outputs of this workgroup
-  auto final_value = [&](int o) -> float {
+  auto final_value = [&](const float* src, int o) -> float {
     const int rb = o / (MT * 16), rem = o % (MT * 16), m = rem >> 4, rr = rem & 15;
     float s = 0.f;
 #pragma unroll
     for (int wv = 0; wv < kWaves; ++wv) {
       if constexpr (MF) {
         const int h = m >> 4, ln = 16 * (rr >> 2) + (m & 15), i = rr & 3;
-        s += red[(((wv * RBW + rb) * NH + h) * 4 + i) * 64 + ln];
+        s += src[(((wv * RBW + rb) * NH + h) * 4 + i) * 64 + ln];
       } else {
-        s += red[((wv * RBW + rb) * M + m) * 16 + rr];
+        s += src[((wv * RBW + rb) * M + m) * 16 + rr];
       }
     }
     return s;
@@ -447,24 +469,30 @@ __global__ __launch_bounds__(kThreads) void k_gemm(
     for (int o = tid; o < kOut; o += kThreads) {
       const int rb = o / (MT * 16), rem = o % (MT * 16), m = rem >> 4, rr = rem & 15;
       const uint32_t b = b0 + rb;
-      const float v = final_value(o);
+      const float v = final_value(red, o), sv = final_value(red + kRed, o);
       fin[o] = v;
-      if (b < p.nb && (uint32_t)m < m_rows) out_f32[(size_t)m * p.n + 16u * b + rr] = v;
+      fin_s[o] = sv;
+      if (b < p.nb && (uint32_t)m < m_rows) {
+        out_f32[(size_t)m * p.n + 16u * b + rr] = v;
+        out_s[(size_t)m * p.n + 16u * b + rr] = sv;
+      }
     }
     __syncthreads();
     for (int o = tid; o < RBW * MT; o += kThreads) {
       const int rb = o / MT, m = o % MT;
       const uint32_t b = b0 + rb;
       if (b >= p.nb || (uint32_t)m >= m_rows) continue;
-      float best = fin[o * 16];
+      float best = fin[o * 16], smax = fin_s[o * 16];
       int bi = 0;
       bool finite = __builtin_isfinite(best);
       for (int rr = 1; rr < 16; ++rr) {
         const float v = fin[o * 16 + rr];
         finite = finite && __builtin_isfinite(v);
         if (v > best) { best = v; bi = rr; }
+        smax = fmaxf(smax, fin_s[o * 16 + rr]);
       }
       rbmax_v[(size_t)m * p.nb + b] = finite ? best : __builtin_nanf("");
+      rbmax_s[(size_t)m * p.nb + b] = smax;
       rbmax_i[(size_t)m * p.nb + b] = (int32_t)(16u * b + bi);
     }
   } else {
@@ -472,7 +500,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm(
     for (int o = tid; o < kOut; o += kThreads) {
       const int rb = o / (MT * 16), rem = o % (MT * 16), m = rem >> 4, rr = rem & 15;
       const uint32_t b = b0 + rb;
-      const float v = final_value(o);
+      const float v = final_value(red, o);
       if (b >= p.nb || (uint32_t)m >= m_rows) continue;
       if (direct) y[(size_t)m * p.n + 16u * b + rr] = f32_to_bf16_rne(v);
       else out_f32[((size_t)split * m_rows + m) * p.n + 16u * b + rr] = v;
@@ -493,9 +521,11 @@ template <int MT, int NW, int SRC, int EPI>
 __global__ __launch_bounds__(NW * 64) void k_gemm_cs(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ w,
     const uint32_t* __restrict__ esc_off, const uint32_t* __restrict__ esc,
-    uint16_t* __restrict__ y, float* __restrict__ out_f32, float* __restrict__ rbmax_v,
-    int32_t* __restrict__ rbmax_i, GemmParams p) {
+    uint16_t* __restrict__ y, float* __restrict__ out_f32, float* __restrict__ out_s,
+    float* __restrict__ rbmax_v, float* __restrict__ rbmax_s, int32_t* __restrict__ rbmax_i,
+    GemmParams p) {
   constexpr int NH = MT / 16;
+  constexpr bool kS = EPI == EPI_LOGITS;   // also accumulate S = sum |x||w| per output
   constexpr int NT = NW * 64;
   constexpr int kUnits = (16 * MT + NT - 1) / NT;     // 16-byte x units per thread
   __shared__ __align__(16) uint16_t xs[2][MT * kXsStride];
@@ -511,9 +541,9 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_cs(
   const uint32_t gb = min(p.g_cols, ga + p.cols_per_split);
   const uint32_t m_rows = p.m;
 
-  f32x4 acc[NH];
+  f32x4 acc[NH], sacc[NH];
 #pragma unroll
-  for (int h = 0; h < NH; ++h) acc[h] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int h = 0; h < NH; ++h) acc[h] = sacc[h] = f32x4{0.f, 0.f, 0.f, 0.f};
   TileRegs<SRC> tA, tB;
   u32x4 xr[kUnits];
   EscCursor ec;
@@ -555,6 +585,10 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_cs(
         const u32x4 xv = *reinterpret_cast<const u32x4*>(xrow + (16 * h + r) * kXsStride + 32 * j);
         acc[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av),
                                                          __builtin_bit_cast(bf16x8_t, xv), acc[h], 0, 0, 0);
+        if constexpr (kS)
+          sacc[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av & kAbs2),
+                                                            __builtin_bit_cast(bf16x8_t, xv & kAbs2),
+                                                            sacc[h], 0, 0, 0);
       }
     }
     if constexpr (SRC != SRC_BF16) {
@@ -593,13 +627,14 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_cs(
     for (int h = 0; h < NH; ++h) {
       const uint32_t m = 16u * h + (uint32_t)r;
       // best of this lane's 4 rows, lowest row on ties; non-finite poisons the block
-      float best = acc[h][0];
+      float best = acc[h][0], smax = sacc[h][0];
       int bi = 0;
       bool finite = __builtin_isfinite(acc[h][0]);
 #pragma unroll
       for (int i = 1; i < 4; ++i) {
         finite = finite && __builtin_isfinite(acc[h][i]);
         if (acc[h][i] > best) { best = acc[h][i]; bi = i; }
+        smax = fmaxf(smax, sacc[h][i]);
       }
       int row = 4 * q + bi;
 #pragma unroll
@@ -607,13 +642,16 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_cs(
         const float ob = __shfl_xor(best, off);
         const int orow = __shfl_xor(row, off);
         const int ofin = __shfl_xor((int)finite, off);
+        smax = fmaxf(smax, __shfl_xor(smax, off));
         finite = finite && ofin;
         if (ob > best || (ob == best && orow < row)) { best = ob; row = orow; }
       }
       if (m < m_rows) {
         *reinterpret_cast<f32x4*>(out_f32 + (size_t)m * p.n + n0) = acc[h];
+        *reinterpret_cast<f32x4*>(out_s + (size_t)m * p.n + n0) = sacc[h];
         if (q == 0) {
           rbmax_v[(size_t)m * p.nb + b] = finite ? best : __builtin_nanf("");
+          rbmax_s[(size_t)m * p.nb + b] = smax;
           rbmax_i[(size_t)m * p.nb + b] = (int32_t)(16u * b + row);
         }
       }
@@ -664,7 +702,7 @@ hipError_t launch_gemm_src(const GemmArgs& a, int epi, const GemmPlan& pl, hipSt
   float* f32 = epi == EPI_LOGITS ? a.logits : a.partial;
 #define W12_L(M_, MT_, MF_, RBW_, EPI_)                                                          \
   hipLaunchKernelGGL((k_gemm<M_, MT_, MF_, RBW_, SRC, EPI_>), grid, block, 0, s, a.x, a.w,     \
-                     a.esc_off, a.esc, a.y, f32, a.rbmax_v, a.rbmax_i, p)
+                     a.esc_off, a.esc, a.y, f32, a.sabs, a.rbmax_v, a.rbmax_s, a.rbmax_i, p)
 #define W12_RBW(M_, MT_, MF_, EPI_)            \
   do {                                         \
     if (pl.rbw == 1) W12_L(M_, MT_, MF_, 1, EPI_); \
@@ -679,10 +717,10 @@ hipError_t launch_gemm_src(const GemmArgs& a, int epi, const GemmPlan& pl, hipSt
   do {                                                                                        \
     if (pl.nw == 8)                                                                           \
       hipLaunchKernelGGL((k_gemm_cs<MT_, 8, SRC, EPI_>), grid, dim3(512), 0, s, a.x, a.w,     \
-                         a.esc_off, a.esc, a.y, f32, a.rbmax_v, a.rbmax_i, p);                \
+                         a.esc_off, a.esc, a.y, f32, a.sabs, a.rbmax_v, a.rbmax_s, a.rbmax_i, p); \
     else                                                                                      \
       hipLaunchKernelGGL((k_gemm_cs<MT_, 4, SRC, EPI_>), grid, dim3(256), 0, s, a.x, a.w,     \
-                         a.esc_off, a.esc, a.y, f32, a.rbmax_v, a.rbmax_i, p);                \
+                         a.esc_off, a.esc, a.y, f32, a.sabs, a.rbmax_v, a.rbmax_s, a.rbmax_i, p); \
   } while (0)
 #define W12_CS_EPI(MT_)                                                     \
   do {                                                                      \

@@ -34,8 +34,10 @@ struct GemmArgs {
   const uint32_t* esc;      // [n_esc]
   uint16_t* y;              // [m][n] BF16 (EPI_BF16)
   float* logits;            // [m][n] (EPI_LOGITS)
-  float* rbmax_v;           // [m][nb] (EPI_LOGITS)
-  int32_t* rbmax_i;         // [m][nb] (EPI_LOGITS)
+  float* sabs;              // [m][n] sum_k |x_k||w_k| per logit (EPI_LOGITS)
+  float* rbmax_v;           // [m][nb] largest logit of each row-block (EPI_LOGITS)
+  float* rbmax_s;           // [m][nb] largest sabs of each row-block (EPI_LOGITS)
+  int32_t* rbmax_i;         // [m][nb] index of rbmax_v, lowest on ties (EPI_LOGITS)
   float* partial;           // [nsplit][m][n] split-K partial sums
   uint32_t m, n, k, g_cols, nb;
   uint32_t lut[4];          // codebook bytes C[0..15] (SRC_LUT)
@@ -101,7 +103,9 @@ struct VerifyArgs {
   const uint32_t* esc_off;
   const uint32_t* esc;
   const float* logits;      // [m][n]
+  const float* sabs;        // [m][n]
   const float* rbmax_v;     // [m][nb]
+  const float* rbmax_s;     // [m][nb]
   const int32_t* rbmax_i;   // [m][nb]
   int32_t* cand;            // [m][n] candidate lists
   int32_t* argmax;          // [m]

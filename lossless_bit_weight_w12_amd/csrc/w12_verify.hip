@@ -1,15 +1,23 @@
 // Greedy verification epilogue: certified exact argmax over the LM-head logits and
 // the accepted-prefix length.
 //
-// Pass 1 (the GEMM kernel family with the logits epilogue) leaves FP32 logits z^[m][v]
-// and, per 16-row block, the largest z^ and its index.  Pass 2 (one workgroup per row):
-//   1. z* = max z^ over the block maxima;
-//   2. a bound B on |z^ - z| valid for any reduction order the GEMM kernels use:
-//        B = K 2^-22 Sx (1 + (K+1) 2^-23) 2^(e_max-126) + K 2^-126 (1 + Xmax + 2^(e_max-126))
-//      (Sx = sum |x_k| in FP64, Xmax = max |x_k|; 2^(e_max-126) bounds |w| strictly;
-//      the first term allows a relative error of 2^-23 per product and per addition,
-//      the second covers denormal inputs and products flushed to zero);
-//   3. every v with z^_v >= z* - 2B is a candidate (the exact argmax always is);
+// Pass 1 (the GEMM kernel family with the logits epilogue) leaves FP32 logits z^[m][v],
+// S^[m][v] = the same kernel's FP32 sum of |x_k||w_vk|, and per 16-row block the
+// largest z^ (with its index) and the largest S^.  Pass 2 (one workgroup per row):
+//   1. z* = max z^ over the block maxima (lowest index on ties), S* its S^;
+//   2. the error bound.  A product of two BF16 values is exact in FP32 unless it
+//      underflows.  Whatever the summation order, each of the K products of a logit
+//      passes through at most D = K + 64 additions (the slack covers the accumulators'
+//      zero starts and the cross-wave sums), each with relative error below
+//      eps = 2^-23 (round-to-nearest or toward zero), so with g = D eps / (1 - D eps)
+//        |z^ - z| <= g S + A,   S = sum_k |x_k w_k|,
+//      A = D 2^-126 (1 + Xmax + Wmax) covering flushed denormal inputs, products and
+//      partial sums (Xmax = max |x_k|, Wmax = 2^(e_max-126) > |w|).  S^ sums the same
+//      nonnegative terms, so S <= S^/(1-g) + A, and B(S^) = g (S^/(1-g) + A) + A,
+//      inflated by 2^-20 for its FP64 evaluation, bounds |z^ - z|;
+//   3. L = z* - B(S*) is below the true maximum, so every v with z^_v + B(S^_v) >= L is
+//      a candidate (the exact argmax always is); whole blocks are skipped when their
+//      largest z^ plus B(largest S^) falls below L;
 //   4. each candidate's logit is recomputed exactly: sum_k x_k w_vk as an integer in
 //      units of 2^-266 (a BF16 product is +-Mx*Mw*2^(Ex+Ew) with 8-bit significands),
 //      accumulated in 64-bit LDS limbs; the largest exact value wins, lowest index on
@@ -62,7 +70,6 @@ __device__ __forceinline__ void limb_add(unsigned long long* limbs, int sgn, uin
 __global__ __launch_bounds__(256) void k_verify_pass2(VerifyArgs a) {
   __shared__ float s_bv[256];
   __shared__ int32_t s_bi[256];
-  __shared__ double s_sx[256];
   __shared__ double s_xm[256];
   __shared__ unsigned long long limbs[kLimbs];
   __shared__ uint32_t best[kLimbs];
@@ -81,18 +88,15 @@ __global__ __launch_bounds__(256) void k_verify_pass2(VerifyArgs a) {
     if (v != v) bad = true;
     else if (v > bv || (v == bv && i < bi)) { bv = v; bi = i; }
   }
-  // 2. Sx and Xmax
-  double sx = 0.0, xm = 0.0;
+  // 2. Xmax (and finiteness of x)
+  double xm = 0.0;
   for (uint32_t i = tid; i < a.k; i += 256) {
     const uint32_t bits = xr[i];
     if (((bits >> 7) & 0xFFu) == 0xFFu) bad = true;
-    const double v = fabs((double)__uint_as_float(bits << 16));
-    sx += v;
-    xm = fmax(xm, v);
+    xm = fmax(xm, fabs((double)__uint_as_float(bits << 16)));
   }
   s_bv[tid] = bv;
   s_bi[tid] = bi;
-  s_sx[tid] = sx;
   s_xm[tid] = xm;
   if (tid == 0) { s_cnt = 0; s_bad = 0; }
   __syncthreads();
@@ -102,29 +106,34 @@ __global__ __launch_bounds__(256) void k_verify_pass2(VerifyArgs a) {
       const float v2 = s_bv[tid + off];
       const int32_t i2 = s_bi[tid + off];
       if (v2 > s_bv[tid] || (v2 == s_bv[tid] && i2 < s_bi[tid])) { s_bv[tid] = v2; s_bi[tid] = i2; }
-      s_sx[tid] += s_sx[tid + off];
       s_xm[tid] = fmax(s_xm[tid], s_xm[tid + off]);
     }
     __syncthreads();
   }
   const float zmax = s_bv[0];
-  const double kd = (double)a.k;
+  const double dd = (double)a.k + 64.0;
+  const double gam = dd * ldexp(1.0, -23) / (1.0 - dd * ldexp(1.0, -23));
   const double wmax = ldexp(1.0, (int)a.e_max - 126);
-  double bound = kd * ldexp(1.0, -22) * s_sx[0] * (1.0 + (kd + 1.0) * ldexp(1.0, -23)) * wmax +
-                 kd * ldexp(1.0, -126) * (1.0 + s_xm[0] + wmax);
-  bound *= 1.0 + ldexp(1.0, -20);
-  const double thr = (double)zmax - 2.0 * bound;
-  if (s_bad || !__builtin_isfinite(zmax) || !__builtin_isfinite(thr)) {
+  const double absb = dd * ldexp(1.0, -126) * (1.0 + s_xm[0] + wmax);
+  const double infl = 1.0 + ldexp(1.0, -20);
+  auto bound = [&](float s_hat) -> double {
+    return (gam * ((double)s_hat / (1.0 - gam) + absb) + absb) * infl;
+  };
+  const uint64_t vstar = s_bi[0] >= 0 && (uint32_t)s_bi[0] < a.n ? (uint32_t)s_bi[0] : 0u;
+  const double lo = (double)zmax - bound(a.sabs[(uint64_t)row * a.n + vstar]);
+  if (s_bad || !__builtin_isfinite(zmax) || lo != lo) {
     if (tid == 0) { a.argmax[row] = -1; if (a.ncand) a.ncand[row] = 0; }
     return;
   }
   // 3. candidates
   int32_t* cand = a.cand + (uint64_t)row * a.n;
   for (uint32_t b = tid; b < a.nb; b += 256) {
-    if ((double)a.rbmax_v[(uint64_t)row * a.nb + b] < thr) continue;
+    const uint64_t bo = (uint64_t)row * a.nb + b;
+    if ((double)a.rbmax_v[bo] + bound(a.rbmax_s[bo]) < lo) continue;
     for (uint32_t rr = 0; rr < 16; ++rr) {
-      const uint32_t v = 16u * b + rr;
-      if ((double)a.logits[(uint64_t)row * a.n + v] >= thr) cand[atomicAdd(&s_cnt, 1u)] = (int32_t)v;
+      const uint64_t vo = (uint64_t)row * a.n + 16u * b + rr;
+      if ((double)a.logits[vo] + bound(a.sabs[vo]) >= lo)
+        cand[atomicAdd(&s_cnt, 1u)] = (int32_t)(16u * b + rr);
     }
   }
   __syncthreads();
