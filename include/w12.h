@@ -98,9 +98,11 @@ size_t w12_tiles_bytes(uint64_t n, uint64_t k);
 /* Workspace bytes needed by `op` for m rows (ignored by ENCODE/DECODE) and an
  * n x k weight; 0 for an invalid op or shape, and 0 when the op needs none (DECODE,
  * and GEMM shapes that are not split along K).  GEMM split along K needs FP32
- * partials [splits][m][n]; VERIFY holds per-row candidate counts (int32 [m], at offset
- * 0), FP32 logits [m][n], their error scales sum_k |x_k||w_k| [m][n], per-row-block
- * maxima and candidate lists; ENCODE holds the histogram and per-tile escape counts. */
+ * partials [splits][m][n]; VERIFY holds, each region starting on a 256-byte boundary
+ * in this order: per-row candidate counts (int32 [m]), FP32 logits [m][n], their
+ * error scales sum_k |x_k||w_k| (FP32 [m][n]), per-row-block maxima and candidate
+ * lists (readable after a call for diagnostics); ENCODE holds the histogram and
+ * per-tile escape counts. */
 size_t w12_workspace_bytes(int op, uint32_t m, uint64_t n, uint64_t k);
 
 /* Zero-fills `ws` on `stream` with a kernel (no hipMemset); a convenience, no call
@@ -129,12 +131,16 @@ w12_status w12_decode(const w12_desc* d, uint16_t* w_out, void* stream);
 /* y = x . W^T with W decoded in registers ("StargazerX0/SpecPilot", "What it is"):
  * x device BF16 [m][k], y device BF16 [m][n] (row-major, 16-byte aligned), m in 1..32,
  * FP32 accumulation, round-to-nearest-even to BF16.  IEEE propagation for non-finite
- * inputs. */
+ * inputs.  ws: w12_workspace_bytes(W12_OP_GEMM, ...) bytes (may be NULL when that is
+ * 0; no initialization needed); calls that share a workspace must be ordered on one
+ * stream.  The result is deterministic: when K is split, a second kernel sums the FP32
+ * partials in split order. */
 w12_status w12_gemm(const uint16_t* x, uint32_t m, const w12_desc* d, uint16_t* y,
                     void* ws, size_t ws_bytes, void* stream);
 
 /* The same kernel family reading plain BF16 weights w [n][k] row-major (the baseline
- * W12 is measured against: plain BF16 decoding in "What it is"). */
+ * W12 is measured against: plain BF16 decoding in "What it is").  Workspace as for
+ * w12_gemm (W12_OP_GEMM_BF16). */
 w12_status w12_gemm_bf16(const uint16_t* x, uint32_t m, const uint16_t* w, uint64_t n,
                          uint64_t k, uint16_t* y, void* ws, size_t ws_bytes, void* stream);
 

@@ -43,6 +43,9 @@ inline bool codebook_is_run(const uint8_t* c) {
   return true;
 }
 
+#ifndef W12_CS_NOSPLIT_MIN_NB
+#define W12_CS_NOSPLIT_MIN_NB 1024   // row-blocks from which column-synchronous launches keep K whole
+#endif
 #ifndef W12_RBW2_MIN_NB
 #define W12_RBW2_MIN_NB 1024   // row-blocks from which workgroups take two row-blocks
 #endif
@@ -78,7 +81,10 @@ GemmPlan make_plan(uint32_t m, uint64_t n, uint64_t k, int epi) {
     min_cols = 4;
   }
   uint64_t ns = 1;
-  if (epi == EPI_BF16)
+  // column-synchronous launches over many row-blocks keep K whole: the reduce kernel
+  // and the partials cost more than the extra parallelism gains
+  const bool keep_k = p.kind == KIND_COLUMN_SYNC && nb >= W12_CS_NOSPLIT_MIN_NB;
+  if (epi == EPI_BF16 && !keep_k)
     while (units * ns < (uint64_t)kTargetWorkgroups && g >= ns * 2 * min_cols) ns *= 2;
   uint64_t cols = (g + ns - 1) / ns;
   cols = (cols + 3) & ~3ull;
@@ -87,6 +93,8 @@ GemmPlan make_plan(uint32_t m, uint64_t n, uint64_t k, int epi) {
   return p;
 }
 
+// GEMM workspace when K is split: FP32 partials [nsplit][m][n], summed by the reduce
+// kernel; no state survives a call.
 size_t gemm_ws_bytes(uint32_t m, uint64_t n, uint64_t k) {
   const GemmPlan p = make_plan(m, n, k, EPI_BF16);
   return p.nsplit > 1 ? align256((size_t)p.nsplit * m * n * 4) : 0;

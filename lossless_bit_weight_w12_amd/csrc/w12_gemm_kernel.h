@@ -41,8 +41,6 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 constexpr uint32_t kAbs2 = 0x7FFF7FFFu;   // clears the sign bits of two packed BF16
 
-constexpr int kWaves = 4;
-constexpr int kThreads = 256;
 constexpr int kXsStride = 128 + 8;   // BF16 per LDS row of one wave's x column (+16 B pad:
                                      // no bank conflicts for the MFMA B reads)
 
@@ -277,8 +275,8 @@ __device__ __forceinline__ void x_store(const XStage<MT>& st, uint16_t* xw, int 
 // M: rows for the VALU path (compile-time); MT: LDS rows (= M, or 16/32 for MFMA).
 // EPI_BF16 with gridDim.y > 1 writes FP32 partials [split][m][n] (reduced by
 // k_splitk_reduce); with one split it writes y directly.
-template <int M, int MT, bool MF, int RBW, int SRC, int EPI>
-__global__ __launch_bounds__(kThreads) void k_gemm(
+template <int M, int MT, bool MF, int RBW, int NWV, int SRC, int EPI>
+__global__ __launch_bounds__(NWV * 64) void k_gemm(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ w,
     const uint32_t* __restrict__ esc_off, const uint32_t* __restrict__ esc,
     uint16_t* __restrict__ y, float* __restrict__ out_f32, float* __restrict__ out_s,
@@ -288,7 +286,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm(
   // the logits epilogue also accumulates S = sum_k |x_k||w_k| per output (the scale of
   // its rounding-error bound)
   constexpr bool kS = EPI == EPI_LOGITS;
-  __shared__ __align__(16) uint16_t xs[kWaves * MT * kXsStride];   // one x column per wave
+  __shared__ __align__(16) uint16_t xs[NWV * MT * kXsStride];   // one x column per wave
   __shared__ float fin[kS ? RBW * MT * 16 : 1];
   __shared__ float fin_s[kS ? RBW * MT * 16 : 1];
 
@@ -399,21 +397,21 @@ __global__ __launch_bounds__(kThreads) void k_gemm(
     x_store<MT>(xr, xw, lane);
     __builtin_amdgcn_wave_barrier();
     for (;;) {
-      x_load<MT>(xr, x, p.k, m_rows, g + kWaves, gb, lane);
-      load_tiles(tB, g + kWaves);
+      x_load<MT>(xr, x, p.k, m_rows, g + NWV, gb, lane);
+      load_tiles(tB, g + NWV);
       compute(tA, g);
       __builtin_amdgcn_wave_barrier();
       x_store<MT>(xr, xw, lane);
       __builtin_amdgcn_wave_barrier();
-      g += kWaves;
+      g += NWV;
       if (g >= gb) break;
-      x_load<MT>(xr, x, p.k, m_rows, g + kWaves, gb, lane);
-      load_tiles(tA, g + kWaves);
+      x_load<MT>(xr, x, p.k, m_rows, g + NWV, gb, lane);
+      load_tiles(tA, g + NWV);
       compute(tB, g);
       __builtin_amdgcn_wave_barrier();
       x_store<MT>(xr, xw, lane);
       __builtin_amdgcn_wave_barrier();
-      g += kWaves;
+      g += NWV;
       if (g >= gb) break;
     }
   }
@@ -422,7 +420,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm(
   // ---- cross-lane / cross-wave reduction into red[] (aliases xs); the S sums, when
   // kept, go to a second region of the same size
   float* red = reinterpret_cast<float*>(xs);
-  constexpr int kRed = MF ? kWaves * RBW * NH * 4 * 64 : kWaves * RBW * M * 16;
+  constexpr int kRed = MF ? NWV * RBW * NH * 4 * 64 : NWV * RBW * M * 16;
   static_assert((kS ? 2 : 1) * kRed * sizeof(float) <= sizeof(xs), "reduction fits in xs");
   auto to_red = [&](float* dst, float (*va)[MF ? 1 : M], f32x4 (*ma)[NH]) {
     if constexpr (MF) {
@@ -454,7 +452,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm(
     const int rb = o / (MT * 16), rem = o % (MT * 16), m = rem >> 4, rr = rem & 15;
     float s = 0.f;
 #pragma unroll
-    for (int wv = 0; wv < kWaves; ++wv) {
+    for (int wv = 0; wv < NWV; ++wv) {
       if constexpr (MF) {
         const int h = m >> 4, ln = 16 * (rr >> 2) + (m & 15), i = rr & 3;
         s += src[(((wv * RBW + rb) * NH + h) * 4 + i) * 64 + ln];
@@ -466,7 +464,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm(
   };
 
   if constexpr (EPI == EPI_LOGITS) {
-    for (int o = tid; o < kOut; o += kThreads) {
+    for (int o = tid; o < kOut; o += (NWV * 64)) {
       const int rb = o / (MT * 16), rem = o % (MT * 16), m = rem >> 4, rr = rem & 15;
       const uint32_t b = b0 + rb;
       const float v = final_value(red, o), sv = final_value(red + kRed, o);
@@ -478,7 +476,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm(
       }
     }
     __syncthreads();
-    for (int o = tid; o < RBW * MT; o += kThreads) {
+    for (int o = tid; o < RBW * MT; o += (NWV * 64)) {
       const int rb = o / MT, m = o % MT;
       const uint32_t b = b0 + rb;
       if (b >= p.nb || (uint32_t)m >= m_rows) continue;
@@ -497,7 +495,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm(
     }
   } else {
     const bool direct = gridDim.y == 1;
-    for (int o = tid; o < kOut; o += kThreads) {
+    for (int o = tid; o < kOut; o += (NWV * 64)) {
       const int rb = o / (MT * 16), rem = o % (MT * 16), m = rem >> 4, rr = rem & 15;
       const uint32_t b = b0 + rb;
       const float v = final_value(red, o);
@@ -620,9 +618,9 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_cs(
     if (++g >= gb) break;
   }
 
-  if (!bvalid) return;
   const uint32_t n0 = 16u * b + 4u * (uint32_t)q;
   if constexpr (EPI == EPI_LOGITS) {
+    if (!bvalid) return;
 #pragma unroll
     for (int h = 0; h < NH; ++h) {
       const uint32_t m = 16u * h + (uint32_t)r;
@@ -658,17 +656,17 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_cs(
     }
   } else {
     const bool direct = gridDim.y == 1;
+    auto store_y = [&](uint32_t m, const f32x4& v) {
+      const uint32_t lo = (uint32_t)f32_to_bf16_rne(v[0]) | ((uint32_t)f32_to_bf16_rne(v[1]) << 16);
+      const uint32_t hi = (uint32_t)f32_to_bf16_rne(v[2]) | ((uint32_t)f32_to_bf16_rne(v[3]) << 16);
+      *reinterpret_cast<uint2*>(y + (size_t)m * p.n + n0) = make_uint2(lo, hi);
+    };
 #pragma unroll
     for (int h = 0; h < NH; ++h) {
       const uint32_t m = 16u * h + (uint32_t)r;
-      if (m >= m_rows) continue;
-      if (direct) {
-        const uint32_t lo = (uint32_t)f32_to_bf16_rne(acc[h][0]) | ((uint32_t)f32_to_bf16_rne(acc[h][1]) << 16);
-        const uint32_t hi = (uint32_t)f32_to_bf16_rne(acc[h][2]) | ((uint32_t)f32_to_bf16_rne(acc[h][3]) << 16);
-        *reinterpret_cast<uint2*>(y + (size_t)m * p.n + n0) = make_uint2(lo, hi);
-      } else {
-        *reinterpret_cast<f32x4*>(out_f32 + ((size_t)split * m_rows + m) * p.n + n0) = acc[h];
-      }
+      if (m >= m_rows || !bvalid) continue;
+      if (direct) store_y(m, acc[h]);
+      else *reinterpret_cast<f32x4*>(out_f32 + ((size_t)split * m_rows + m) * p.n + n0) = acc[h];
     }
   }
 }
@@ -689,7 +687,7 @@ static __global__ __launch_bounds__(256) void k_splitk_reduce(const float* __res
 // 16 or 32 columns for MFMA), rbw and epilogue; split-K adds the reduce kernel.
 template <int SRC>
 hipError_t launch_gemm_src(const GemmArgs& a, int epi, const GemmPlan& pl, hipStream_t s) {
-  dim3 grid(pl.n_rbg, pl.nsplit), block(kThreads);
+  dim3 grid(pl.n_rbg, pl.nsplit);
   GemmParams p;
   p.m = a.m;
   p.n = a.n;
@@ -700,13 +698,14 @@ hipError_t launch_gemm_src(const GemmArgs& a, int epi, const GemmPlan& pl, hipSt
   for (int i = 0; i < 4; ++i) p.lut[i] = a.lut[i];
   p.basepair = a.basepair;
   float* f32 = epi == EPI_LOGITS ? a.logits : a.partial;
-#define W12_L(M_, MT_, MF_, RBW_, EPI_)                                                          \
-  hipLaunchKernelGGL((k_gemm<M_, MT_, MF_, RBW_, SRC, EPI_>), grid, block, 0, s, a.x, a.w,     \
-                     a.esc_off, a.esc, a.y, f32, a.sabs, a.rbmax_v, a.rbmax_s, a.rbmax_i, p)
-#define W12_RBW(M_, MT_, MF_, EPI_)            \
-  do {                                         \
-    if (pl.rbw == 1) W12_L(M_, MT_, MF_, 1, EPI_); \
-    else W12_L(M_, MT_, MF_, 2, EPI_);          \
+#define W12_L(M_, MT_, MF_, RBW_, NWV_, EPI_)                                                     \
+  hipLaunchKernelGGL((k_gemm<M_, MT_, MF_, RBW_, NWV_, SRC, EPI_>), grid, dim3(NWV_ * 64), 0, s, \
+                     a.x, a.w, a.esc_off, a.esc, a.y, f32, a.sabs, a.rbmax_v, a.rbmax_s,        \
+                     a.rbmax_i, p)
+#define W12_RBW(M_, MT_, MF_, EPI_)                   \
+  do {                                                \
+    if (pl.rbw == 2) W12_L(M_, MT_, MF_, 2, 4, EPI_); \
+    else W12_L(M_, MT_, MF_, 1, 4, EPI_);             \
   } while (0)
 #define W12_EPI(M_, MT_, MF_)                                       \
   do {                                                              \

@@ -263,6 +263,21 @@ def verify_candidates(t: W12Tensor, m: int):
     return ws[:4 * m].view(torch.int32).clone()     # the counts open the verify workspace
 
 
+def verify_pass1(t: W12Tensor, m: int):
+    """FP32 logits z^ [m, n] and their error scales S^ = sum_k |x_k||w_vk| [m, n] left by
+    the last verification on this device's workspace (diagnostic; layout as documented
+    for the VERIFY workspace: int32 counts [m], then logits, then S, each from a
+    256-byte boundary)."""
+    torch = _torch()
+    ws = workspace(workspace_bytes(OP_VERIFY, m, t.n, t.k), t.device, "verify")
+    a = lambda v: (v + 255) // 256 * 256
+    o_logits = a(4 * m)
+    o_s = o_logits + a(4 * m * t.n)
+    z = ws[o_logits:o_logits + 4 * m * t.n].view(torch.float32).view(m, t.n).clone()
+    s = ws[o_s:o_s + 4 * m * t.n].view(torch.float32).view(m, t.n).clone()
+    return z, s
+
+
 def rms_rescale(x, out=None):
     torch = _torch()
     x = _as_bits(x)

@@ -128,6 +128,33 @@ def test_gemm_deterministic_and_overwrites(env):
         assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
 
 
+def test_gemm_workspace_reuse_across_shapes(env):
+    """One workspace serves split-K launches of different shapes in any order: the
+    arrival counters sit at a fixed place and every call leaves them at zero."""
+    torch, w12 = env
+    g = np.random.default_rng(12)
+    cases = []
+    for m, (n, k) in [(1, (272, 1280)), (1, (64, 4096)), (8, (64, 4096)), (32, (320, 2048)),
+                      (4, (2080, 512))]:
+        w = wi.gaussian_bf16((n, k), 0.02, g)
+        x = wi.gaussian_bf16((m, k), 1.0, g)
+        cases.append((to_dev(x, torch), w12.encode(to_dev(w, torch)), x, w))
+    first = []
+    for xt, t, x, w in cases:
+        say("workspace reuse", x.shape, w.shape)
+        y = w12.gemm(xt, t)
+        torch.cuda.synchronize()
+        z, s = o.gemm_reference(x, w)
+        assert o.gemm_accept(to_host(y), z, s).all()
+        first.append(y)
+    for rep in range(3):
+        for i in (4, 0, 3, 1, 2):
+            xt, t, _, _ = cases[i]
+            y = w12.gemm(xt, t)
+            torch.cuda.synchronize()
+            assert torch.equal(y.view(torch.int16), first[i].view(torch.int16)), (rep, i)
+
+
 def test_gemm_nonfinite_propagates(env):
     torch, w12 = env
     g = np.random.default_rng(5)
@@ -187,6 +214,45 @@ def test_verify_matches_oracle(env, m):
         assert int(acc.item()) == o.accepted_length(am_ref, draft) == p
     nc = w12.verify_candidates(t, m).cpu().numpy()
     assert (nc >= 1).all()
+
+
+def _certified_bound(s_hat, k, e_max, xmax):
+    """The bound the verification relies on, as its header states it: any summation
+    order of K exact products, each addition with relative error below 2^-23, at most
+    D = K + 64 additions on a path, plus flushed denormals."""
+    d = k + 64.0
+    gam = d * 2.0 ** -23 / (1 - d * 2.0 ** -23)
+    a = d * 2.0 ** -126 * (1 + xmax + 2.0 ** (e_max - 126))
+    return gam * (s_hat / (1 - gam) + a) + a, gam, a
+
+
+@pytest.mark.parametrize("m,kind", [(1, "gauss"), (3, "wide"), (7, "gauss"), (16, "outliers"),
+                                    (24, "gauss"), (32, "wide")])
+def test_verify_pass1_error_within_certified_bound(env, m, kind):
+    """The FP32 logits of verification pass 1 stay within the certified bound of the
+    exact values on every output (the assumption the exact-argmax filter rests on), and
+    the kernel's sum |x||w| is a valid scale for it."""
+    torch, w12 = env
+    g = np.random.default_rng(9000 + m)
+    n, k = 2048, 5120
+    if kind == "gauss":
+        w = wi.gaussian_bf16((n, k), 0.02, g)
+    elif kind == "wide":
+        w = wide_exponents((n, k), g, 104, 126)
+    else:
+        w = wi.add_exponent_outliers(wi.gaussian_bf16((n, k), 0.02, g), 0.01, 3)
+    x = wi.gaussian_bf16((m, k), 1.0, g)
+    t = w12.encode(to_dev(w, torch))
+    say("pass-1 bound", m, kind, "codebook", t.codebook)
+    w12.lmhead_verify(to_dev(x, torch), t, torch.zeros(0, dtype=torch.int32, device="cuda:0"))
+    z_hat, s_hat = (v.cpu().numpy().astype(np.float64) for v in w12.verify_pass1(t, m))
+    z, s = o.gemm_reference(x, w)
+    xmax = np.abs(wi.bf16_bits_to_f32(x).astype(np.float64)).max()
+    bound, gam, a = _certified_bound(s_hat, k, t.e_max, xmax)
+    err = np.abs(z_hat - z)
+    assert (err <= bound).all(), float((err / bound).max())
+    assert (s <= s_hat / (1 - gam) + a).all()
+    say("pass-1 bound", m, kind, "max |z^-z| / (g S) =", float((err / (gam * s + 1e-300)).max()))
 
 
 def test_verify_exact_tie_lowest_index_and_escapes(env):
