@@ -136,10 +136,36 @@ def time_calls(torch, fn, reps: int, warmup: int = 3) -> float:
     return e0.elapsed_time(e1) / reps
 
 
+def build_decode_stack(torch, w12, wi, np, dev, head=None):
+    """The 64-layer stack (+ LM head) of the decode step, drawn on the device and
+    encoded by the library, prepared for M = 24 with the seeded draft."""
+    from lossless_bit_weight_w12_amd.decode_step import DecodeStack, MATS
+    c5 = wi.CONFIG_SHAPES[5]
+    vocab, hid, m5 = c5["vocab"], c5["hidden"], c5["m"][0]
+    if head is None:
+        head = w12.encode(wi.device_lm_head(torch, vocab, hid))
+    t0 = time.time()
+    shapes = {name: (n, k) for name, n, k in wi.LAYER_MATS}
+    layers = []
+    for li in range(c5["layers"]):
+        L = {}
+        for mi, name in enumerate(MATS):
+            n, k = shapes[name]
+            L[name] = w12.encode(wi.device_layer_weight(torch, li, mi, n, k))
+        layers.append(L)
+        if li % 16 == 15:
+            log(f"bench: {li + 1} layers encoded ({time.time() - t0:.1f} s)")
+    torch.cuda.synchronize()
+    stack = DecodeStack(layers, head, m5)
+    h0 = torch.from_numpy(wi.decode_step_x(m5, hid).view(np.int16)).to(dev)
+    d5 = torch.from_numpy(wi.decode_step_draft(vocab, m5)).to(dev)
+    stack.prepare(d5)
+    return stack, h0
+
+
 def extra_workloads(torch, w12, wi, np, dev, args):
     """LM-head verification (M = 16) and the 64-layer decode step (M = 24).  Weights
     are drawn on the device (randn * 0.02 -> BF16, seeded) and encoded by the library."""
-    from lossless_bit_weight_w12_amd.decode_step import DecodeStack, MATS
     c5 = wi.CONFIG_SHAPES[5]
     vocab, hid, m5 = c5["vocab"], c5["hidden"], c5["m"][0]
     t0 = time.time()
@@ -179,21 +205,8 @@ def extra_workloads(torch, w12, wi, np, dev, args):
 
     # ---- decode step, 64 layers + head, M = 24
     t0 = time.time()
-    shapes = {name: (n, k) for name, n, k in wi.LAYER_MATS}
-    layers = []
-    for li in range(c5["layers"]):
-        L = {}
-        for mi, name in enumerate(MATS):
-            n, k = shapes[name]
-            L[name] = w12.encode(wi.device_layer_weight(torch, li, mi, n, k))
-        layers.append(L)
-        if li % 16 == 15:
-            log(f"bench: {li + 1} layers encoded ({time.time() - t0:.1f} s)")
-    torch.cuda.synchronize()
-    stack = DecodeStack(layers, head, m5)
-    h0 = torch.from_numpy(wi.decode_step_x(m5, hid).view(np.int16)).to(dev)
-    d5 = torch.from_numpy(wi.decode_step_draft(vocab, m5)).to(dev)
-    stack.prepare(d5)
+    stack, h0 = build_decode_stack(torch, w12, wi, np, dev, head)
+    layers = stack.layers
 
     def one_step():
         stack.h.copy_(h0)
@@ -233,6 +246,8 @@ def main():
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the LM-head verification and decode-step workloads")
     ap.add_argument("--decode-steps", type=int, default=20)
+    ap.add_argument("--profile-decode", action="store_true",
+                    help="build the 64-layer decode stack, run --steps steps and exit (for rocprofv3)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported (this path has no "
@@ -245,6 +260,14 @@ def main():
     import lossless_bit_weight_w12_amd as w12
 
     dev = torch.device("cuda:0")
+    if args.profile_decode:
+        stack, h0 = build_decode_stack(torch, w12, wi, np, dev)
+        for _ in range(args.steps):
+            stack.h.copy_(h0)
+            stack.run()
+        torch.cuda.synchronize()
+        log("bench: profile-decode run done")
+        return
     log("bench: generating the MLP-block weights (seeded, host) ...")
     t0 = time.time()
     w_gu = torch.from_numpy(wi.weight(3, wi.T_W, (N_GU, K_GU)).view(np.int16)).to(dev)

@@ -162,7 +162,9 @@ w12_status w12_lmhead_verify(const uint16_t* x, uint32_t m, const w12_desc* d,
                              void* stream);
 
 /* Harness op for the layer chain: y[row] = bf16(x[row] / sqrt(mean(x[row]^2))) in FP32,
- * x, y device BF16 [m][k].  Not part of the W12 method itself. */
+ * x, y device BF16 [m][k] (16-byte aligned, k % 8 == 0, 0 < k < 2^20, m <= 2^20;
+ * otherwise W12_ERR_ALIGN / W12_ERR_SHAPE / W12_ERR_RANGE).  Not part of the W12
+ * method itself. */
 w12_status w12_rms_rescale(const uint16_t* x, uint32_t m, uint64_t k, uint16_t* y,
                            void* stream);
 

@@ -5,13 +5,27 @@
 
 #include <string.h>
 
+#include <algorithm>
+
 using namespace w12;
 
 namespace {
 
 constexpr uint64_t kMaxK = 1ull << 20;
 constexpr uint64_t kMaxN = 1ull << 31;
-constexpr int kTargetWorkgroups = 1024;   // 4 per CU on 256 CUs
+#ifndef W12_TARGET_WG
+#define W12_TARGET_WG 1024
+#endif
+#ifndef W12_CS_FEW_NW
+#define W12_CS_FEW_NW 4
+#endif
+#ifndef W12_NS_CAP
+#define W12_NS_CAP 8
+#endif
+#ifndef W12_CS_MIN_COLS
+#define W12_CS_MIN_COLS 4
+#endif
+constexpr int kTargetWorkgroups = W12_TARGET_WG;   // 4-wave workgroups: 4 per CU on 256 CUs
 
 inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
@@ -43,9 +57,6 @@ inline bool codebook_is_run(const uint8_t* c) {
   return true;
 }
 
-#ifndef W12_CS_NOSPLIT_MIN_NB
-#define W12_CS_NOSPLIT_MIN_NB 1024   // row-blocks from which column-synchronous launches keep K whole
-#endif
 #ifndef W12_RBW2_MIN_NB
 #define W12_RBW2_MIN_NB 1024   // row-blocks from which workgroups take two row-blocks
 #endif
@@ -62,7 +73,7 @@ inline bool codebook_is_run(const uint8_t* c) {
 GemmPlan make_plan(uint32_t m, uint64_t n, uint64_t k, int epi) {
   GemmPlan p;
   const uint64_t nb = n / 16, g = k / 128;
-  uint64_t units, min_cols;
+  uint64_t units, min_cols;   // min_cols: tile columns a split keeps at least
   p.kind = KIND_WAVE_COLUMNS;
   p.mfma = m >= W12_MFMA_MIN_M;
   p.rbw = 1;
@@ -70,10 +81,10 @@ GemmPlan make_plan(uint32_t m, uint64_t n, uint64_t k, int epi) {
   const bool few_rows = nb < W12_RBW2_MIN_NB;
   if (p.mfma && (few_rows || m >= 16)) {
     p.kind = KIND_COLUMN_SYNC;
-    p.nw = few_rows ? 8 : 4;
+    p.nw = few_rows ? W12_CS_FEW_NW : 4;
     p.n_rbg = (uint32_t)((nb + p.nw - 1) / p.nw);
     units = (uint64_t)p.n_rbg * p.nw / 4;     // in 4-wave workgroup equivalents
-    min_cols = 8;
+    min_cols = W12_CS_MIN_COLS;
   } else {
     p.rbw = few_rows ? 1 : 2;
     p.n_rbg = (uint32_t)((nb + p.rbw - 1) / p.rbw);
@@ -81,15 +92,17 @@ GemmPlan make_plan(uint32_t m, uint64_t n, uint64_t k, int epi) {
     min_cols = 4;
   }
   uint64_t ns = 1;
-  // column-synchronous launches over many row-blocks keep K whole: the reduce kernel
-  // and the partials cost more than the extra parallelism gains
-  const bool keep_k = p.kind == KIND_COLUMN_SYNC && nb >= W12_CS_NOSPLIT_MIN_NB;
-  if (epi == EPI_BF16 && !keep_k)
-    while (units * ns < (uint64_t)kTargetWorkgroups && g >= ns * 2 * min_cols) ns *= 2;
-  uint64_t cols = (g + ns - 1) / ns;
-  cols = (cols + 3) & ~3ull;
-  p.cols_per_split = (uint32_t)cols;
-  p.nsplit = (uint32_t)((g + cols - 1) / cols);
+  // column-synchronous launches that already fill the chip (>= 512 four-wave
+  // workgroups) keep K whole: the reduce kernel and the partials cost more than the
+  // extra parallelism gains
+  const bool keep_k = p.kind == KIND_COLUMN_SYNC && units >= (uint64_t)kTargetWorkgroups / 2;
+  if (epi == EPI_BF16 && !keep_k) {
+    // enough splits to reach the workgroup target, each keeping >= min_cols columns
+    ns = ((uint64_t)kTargetWorkgroups + units - 1) / units;
+    ns = std::min<uint64_t>(ns, std::min<uint64_t>(W12_NS_CAP, g / min_cols));
+    ns = std::max<uint64_t>(ns, 1);
+  }
+  p.nsplit = (uint32_t)ns;     // the kernels deal the K range evenly over the splits
   return p;
 }
 
@@ -361,7 +374,8 @@ w12_status w12_lmhead_verify(const uint16_t* x, uint32_t m, const w12_desc* d, c
 w12_status w12_rms_rescale(const uint16_t* x, uint32_t m, uint64_t k, uint16_t* y, void* stream) {
   if (!x || !y) return W12_ERR_NULL;
   if (m < 1 || m > (1u << 20)) return W12_ERR_RANGE;
-  if (k == 0 || k >= kMaxK) return W12_ERR_SHAPE;
+  if (k == 0 || k >= kMaxK || k % 8) return W12_ERR_SHAPE;
+  if (!aligned(x, 16) || !aligned(y, 16)) return W12_ERR_ALIGN;
   return hip_status(launch_rms_rescale(x, m, (uint32_t)k, y, (hipStream_t)stream));
 }
 

@@ -330,28 +330,45 @@ hipError_t launch_decode(const uint8_t* tiles, const uint32_t* esc_off, const ui
 }
 
 // ---------------------------------------------------------------- RMS rescale (chain)
-__global__ __launch_bounds__(256) void k_rms(const uint16_t* x, uint32_t k, uint16_t* y) {
-  __shared__ float part[256];
-  const uint32_t row = blockIdx.x, tid = threadIdx.x;
-  const uint16_t* xr = x + (uint64_t)row * k;
+// One workgroup per row; k % 8 == 0 and 16-byte aligned rows, so every thread moves
+// 8 BF16 per load and store.  The sum of squares is reduced in a fixed order (per
+// thread, then a fixed tree), so the result is deterministic.
+__global__ __launch_bounds__(256) void k_rms(const uint16_t* __restrict__ x, uint32_t k,
+                                             uint16_t* __restrict__ y) {
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  __shared__ float part[4];
+  const uint32_t row = blockIdx.x, tid = threadIdx.x, units = k >> 3;
+  const u32x4* xr = reinterpret_cast<const u32x4*>(x + (uint64_t)row * k);
+  u32x4* yr = reinterpret_cast<u32x4*>(y + (uint64_t)row * k);
   float s = 0.f;
-  for (uint32_t i = tid; i < k; i += 256) {
-    const float v = __uint_as_float((uint32_t)xr[i] << 16);
-    s += v * v;
+  for (uint32_t u = tid; u < units; u += 256) {
+    const u32x4 v = xr[u];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float lo = __uint_as_float(v[i] << 16), hi = __uint_as_float(v[i] & 0xFFFF0000u);
+      s += lo * lo + hi * hi;
+    }
   }
-  part[tid] = s;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off);
+  if ((tid & 63) == 0) part[tid >> 6] = s;
   __syncthreads();
-  for (uint32_t off = 128; off > 0; off >>= 1) {
-    if (tid < off) part[tid] += part[tid + off];
-    __syncthreads();
-  }
-  const float rms = sqrtf(part[0] / (float)k);
-  for (uint32_t i = tid; i < k; i += 256) {
-    const float v = __uint_as_float((uint32_t)xr[i] << 16) / rms;
-    uint32_t u = __float_as_uint(v);
+  const float rms = sqrtf(((part[0] + part[1]) + (part[2] + part[3])) / (float)k);
+  auto rne = [](float f) -> uint32_t {
+    uint32_t u = __float_as_uint(f);
     if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu)) u |= 0x00400000u;
     else u += 0x7FFFu + ((u >> 16) & 1u);
-    y[(uint64_t)row * k + i] = (uint16_t)(u >> 16);
+    return u >> 16;
+  };
+  for (uint32_t u = tid; u < units; u += 256) {
+    const u32x4 v = xr[u];
+    u32x4 o;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float lo = __uint_as_float(v[i] << 16) / rms, hi = __uint_as_float(v[i] & 0xFFFF0000u) / rms;
+      o[i] = rne(lo) | (rne(hi) << 16);
+    }
+    yr[u] = o;
   }
 }
 

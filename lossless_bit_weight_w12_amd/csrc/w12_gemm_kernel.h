@@ -48,7 +48,6 @@ constexpr int kXsStride = 128 + 8;   // BF16 per LDS row of one wave's x column 
 // Scalar parameters of one GEMM launch.
 struct GemmParams {
   uint32_t m, n, k, g_cols, nb;
-  uint32_t cols_per_split;
   uint32_t lut[4];
   uint32_t basepair;
 };
@@ -295,8 +294,9 @@ __global__ __launch_bounds__(NWV * 64) void k_gemm(
   const int r = lane & 15, q = lane >> 4;
   const uint32_t rbg = blockIdx.x, split = blockIdx.y;
   const uint32_t b0 = rbg * RBW;
-  const uint32_t ga = split * p.cols_per_split;
-  const uint32_t gb = min(p.g_cols, ga + p.cols_per_split);
+  // split s of S covers tile columns [s*G/S, (s+1)*G/S): the K range dealt evenly
+  const uint32_t ga = (uint32_t)(((uint64_t)split * p.g_cols) / gridDim.y);
+  const uint32_t gb = (uint32_t)(((uint64_t)(split + 1u) * p.g_cols) / gridDim.y);
   const uint32_t m_rows = MF ? p.m : (uint32_t)M;
 
   float vacc[RBW][MF ? 1 : M], vsacc[RBW][MF ? 1 : M];
@@ -535,8 +535,9 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_cs(
   const bool bvalid = b < p.nb;
   const uint32_t bl = min(b, p.nb - 1u);
   const uint32_t split = blockIdx.y;
-  const uint32_t ga = split * p.cols_per_split;
-  const uint32_t gb = min(p.g_cols, ga + p.cols_per_split);
+  // split s of S covers tile columns [s*G/S, (s+1)*G/S): the K range dealt evenly
+  const uint32_t ga = (uint32_t)(((uint64_t)split * p.g_cols) / gridDim.y);
+  const uint32_t gb = (uint32_t)(((uint64_t)(split + 1u) * p.g_cols) / gridDim.y);
   const uint32_t m_rows = p.m;
 
   f32x4 acc[NH], sacc[NH];
@@ -694,7 +695,6 @@ hipError_t launch_gemm_src(const GemmArgs& a, int epi, const GemmPlan& pl, hipSt
   p.k = a.k;
   p.g_cols = a.g_cols;
   p.nb = a.nb;
-  p.cols_per_split = pl.cols_per_split;
   for (int i = 0; i < 4; ++i) p.lut[i] = a.lut[i];
   p.basepair = a.basepair;
   float* f32 = epi == EPI_LOGITS ? a.logits : a.partial;

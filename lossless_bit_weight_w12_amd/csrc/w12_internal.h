@@ -56,7 +56,6 @@ struct GemmPlan {
   int rbw;                  // KIND_WAVE_COLUMNS: row-blocks per wave (1 or 2)
   int nw;                   // KIND_COLUMN_SYNC: waves (= row-blocks) per workgroup (4 or 8)
   uint32_t nsplit;          // K splits across workgroups
-  uint32_t cols_per_split;  // tile columns per split
   uint32_t n_rbg;           // row-block groups = ceil(nb / rbw)
 };
 

@@ -291,10 +291,11 @@ def test_verify_nonfinite_row_reports_minus_one(env):
     assert int(acc.item()) == 0
 
 
-def test_rms_rescale(env):
+@pytest.mark.parametrize("k", [8, 1024, 5120, 17408])
+def test_rms_rescale(env, k):
     torch, w12 = env
-    g = np.random.default_rng(8)
-    x = wi.gaussian_bf16((24, 5120), 3.0, g)
+    g = np.random.default_rng(8 + k)
+    x = wi.gaussian_bf16((24, k), 3.0, g)
     y = to_host(w12.rms_rescale(to_dev(x, torch)))
     yf = wi.bf16_bits_to_f32(y).astype(np.float64)
     xf = wi.bf16_bits_to_f32(x).astype(np.float64)

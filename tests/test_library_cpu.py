@@ -138,4 +138,6 @@ def test_encode_decode_validation(L):
     assert L.w12_decode(ctypes.byref(desc(k=100)), FAKE, None) == -2
     assert L.w12_decode(ctypes.byref(desc()), None, None) == -1
     assert L.w12_rms_rescale(FAKE, 0, 128, FAKE, None) == -3
+    assert L.w12_rms_rescale(FAKE, 4, 100, FAKE, None) == -2        # k % 8 != 0
+    assert L.w12_rms_rescale(FAKE + 8, 4, 128, FAKE, None) == -7    # x not 16-byte aligned
     assert L.w12_workspace_init(None, 64, None) == -1
