@@ -71,6 +71,7 @@ typedef int32_t w12_status;
 #define W12_ERR_ALIGN     -7  /* tiles/x/w/y/ws not aligned as documented */
 
 #define W12_MAX_M 32
+#define W12_MAX_GROUP 4   /* weights of one w12_gemm_group call, at most */
 
 /* Host-side descriptor of one W12 tensor (device buffers + host metadata). */
 typedef struct w12_desc {
@@ -91,6 +92,7 @@ typedef struct w12_desc {
 #define W12_OP_GEMM      2
 #define W12_OP_GEMM_BF16 3
 #define W12_OP_VERIFY    4
+#define W12_OP_GEMM_GROUP 5   /* n = the group's rows added up */
 
 /* Bytes of the tile array: (n/16)*(k/128)*3072; 0 if the shape is invalid. */
 size_t w12_tiles_bytes(uint64_t n, uint64_t k);
@@ -137,6 +139,19 @@ w12_status w12_decode(const w12_desc* d, uint16_t* w_out, void* stream);
  * partials in split order. */
 w12_status w12_gemm(const uint16_t* x, uint32_t m, const w12_desc* d, uint16_t* y,
                     void* ws, size_t ws_bytes, void* stream);
+
+/* Several W12 weights that read the same x (q, k and v of a layer; gate and up):
+ * ys[i] = x . W_i^T for i < n_w (1..W12_MAX_GROUP), all with the same k, in one launch
+ * per codebook kind (row-blocks of the weights numbered consecutively), plus the
+ * split-K reduce kernel when K is split.  descs: host array of n_w descriptors; ys:
+ * host array of n_w device BF16 outputs [m][n_i].  Same arithmetic, rounding and
+ * determinism as w12_gemm (the K split can differ, so the last bit can too).
+ * ws: w12_workspace_bytes(W12_OP_GEMM_GROUP, m, sum of n_i, k) bytes.  Errors: as
+ * w12_gemm; W12_ERR_RANGE for n_w outside 1..W12_MAX_GROUP, W12_ERR_SHAPE for weights
+ * of different k. */
+w12_status w12_gemm_group(const uint16_t* x, uint32_t m, const w12_desc* const* descs,
+                          uint32_t n_w, uint16_t* const* ys, void* ws, size_t ws_bytes,
+                          void* stream);
 
 /* The same kernel family reading plain BF16 weights w [n][k] row-major (the baseline
  * W12 is measured against: plain BF16 decoding in "What it is").  Workspace as for

@@ -70,7 +70,7 @@ inline bool codebook_is_run(const uint8_t* c) {
 //    shared by 8 row-blocks; at m = 32 the down projection goes 3.1 -> 4.3 TB/s);
 //  - many row-blocks: wave-column MFMA below m = 16 (no per-column barrier), column-
 //    synchronous with 4 waves from m = 16 (x traffic dominates).
-GemmPlan make_plan(uint32_t m, uint64_t n, uint64_t k, int epi) {
+GemmPlan make_plan(uint32_t m, uint64_t n, uint64_t k, int epi, bool bf16_src = false) {
   GemmPlan p;
   const uint64_t nb = n / 16, g = k / 128;
   uint64_t units, min_cols;   // min_cols: tile columns a split keeps at least
@@ -92,10 +92,12 @@ GemmPlan make_plan(uint32_t m, uint64_t n, uint64_t k, int epi) {
     min_cols = 4;
   }
   uint64_t ns = 1;
-  // column-synchronous launches that already fill the chip (>= 512 four-wave
+  // W12 column-synchronous launches that already fill the chip (>= 512 four-wave
   // workgroups) keep K whole: the reduce kernel and the partials cost more than the
-  // extra parallelism gains
-  const bool keep_k = p.kind == KIND_COLUMN_SYNC && units >= (uint64_t)kTargetWorkgroups / 2;
+  // extra parallelism gains.  The BF16 kernel (4 KB tiles) is faster split: measured
+  // on the MLP gate+up at M16 / M32, 81 / 92 us split in two against 87 / 100 us whole.
+  const bool keep_k = !bf16_src && p.kind == KIND_COLUMN_SYNC &&
+                      units >= (uint64_t)kTargetWorkgroups / 2;
   if (epi == EPI_BF16 && !keep_k) {
     // enough splits to reach the workgroup target, each keeping >= min_cols columns
     ns = ((uint64_t)kTargetWorkgroups + units - 1) / units;
@@ -108,9 +110,17 @@ GemmPlan make_plan(uint32_t m, uint64_t n, uint64_t k, int epi) {
 
 // GEMM workspace when K is split: FP32 partials [nsplit][m][n], summed by the reduce
 // kernel; no state survives a call.
-size_t gemm_ws_bytes(uint32_t m, uint64_t n, uint64_t k) {
-  const GemmPlan p = make_plan(m, n, k, EPI_BF16);
+size_t gemm_ws_bytes(uint32_t m, uint64_t n, uint64_t k, bool bf16_src = false) {
+  const GemmPlan p = make_plan(m, n, k, EPI_BF16, bf16_src);
   return p.nsplit > 1 ? align256((size_t)p.nsplit * m * n * 4) : 0;
+}
+
+// A group may run as two launches (one per codebook kind), each over part of the rows:
+// enough for the most splits any part can take.
+size_t group_ws_bytes(uint32_t m, uint64_t n_total, uint64_t k) {
+  const uint64_t g = k / 128;
+  const uint64_t cap = std::min<uint64_t>(W12_NS_CAP, std::max<uint64_t>(g / 4, 1));
+  return cap > 1 ? align256((size_t)cap * m * n_total * 4) : 0;
 }
 
 // Verify workspace: per-row candidate counts first (a fixed place for diagnostics),
@@ -151,11 +161,49 @@ EncodeLayout encode_layout(uint64_t n, uint64_t k) {
 
 inline w12_status hip_status(hipError_t e) { return e == hipSuccess ? W12_OK : W12_ERR_HIP; }
 
-void fill_args_codebook(GemmArgs& a, const w12_desc* d) {
+// Segment of a launch for a W12 weight (codebook as kernel arguments).
+Seg w12_seg(const w12_desc* d, uint16_t* y, uint32_t rb0) {
+  Seg g;
+  memset(&g, 0, sizeof(g));
+  g.w = (const uint8_t*)d->tiles;
+  g.esc_off = d->esc_off;
+  g.esc = d->esc;
+  g.y = y;
+  g.rb0 = rb0;
+  g.n = (uint32_t)d->n;
   for (int i = 0; i < 4; ++i)
-    a.lut[i] = (uint32_t)d->codebook[4 * i] | ((uint32_t)d->codebook[4 * i + 1] << 8) |
+    g.lut[i] = (uint32_t)d->codebook[4 * i] | ((uint32_t)d->codebook[4 * i + 1] << 8) |
                ((uint32_t)d->codebook[4 * i + 2] << 16) | ((uint32_t)d->codebook[4 * i + 3] << 24);
-  a.basepair = (uint32_t)d->codebook[0] | ((uint32_t)d->codebook[0] << 16);
+  g.basepair = (uint32_t)d->codebook[0] | ((uint32_t)d->codebook[0] << 16);
+  return g;
+}
+
+// Launch parameters common to every segment.
+void fill_params(GemmParams& p, uint32_t m, uint64_t k, uint64_t n_total, uint32_t nseg) {
+  p.m = m;
+  p.k = (uint32_t)k;
+  p.g_cols = (uint32_t)(k / 128);
+  p.n = (uint32_t)n_total;
+  p.nb = (uint32_t)(n_total / 16);
+  p.nseg = nseg;
+}
+
+// One launch over segments ds[0..nseg) (same k, same codebook kind): y_i = x . W_i^T.
+hipError_t launch_w12_group(const uint16_t* x, uint32_t m, const w12_desc* const* ds,
+                            uint16_t* const* ys, uint32_t nseg, void* ws, hipStream_t s) {
+  GemmArgs a;
+  memset(&a, 0, sizeof(a));
+  a.x = x;
+  a.partial = (float*)ws;
+  uint64_t n_total = 0;
+  for (uint32_t i = 0; i < nseg; ++i) {
+    a.p.seg[i] = w12_seg(ds[i], ys[i], (uint32_t)(n_total / 16));
+    n_total += ds[i]->n;
+  }
+  fill_params(a.p, m, ds[0]->k, n_total, nseg);
+  const GemmPlan p = make_plan(m, n_total, ds[0]->k, EPI_BF16);
+  const int src = codebook_is_run(ds[0]->codebook) ? SRC_RUN : SRC_LUT;
+  return launch_gemm(a, src, EPI_BF16, p, s);
 }
 
 }  // namespace
@@ -175,10 +223,13 @@ size_t w12_workspace_bytes(int op, uint32_t m, uint64_t n, uint64_t k) {
     case W12_OP_GEMM:
     case W12_OP_GEMM_BF16:
       if (m < 1 || m > W12_MAX_M) return 0;
-      return gemm_ws_bytes(m, n, k);
+      return gemm_ws_bytes(m, n, k, op == W12_OP_GEMM_BF16);
     case W12_OP_VERIFY:
       if (m < 1 || m > W12_MAX_M) return 0;
       return verify_layout(m, n).total;
+    case W12_OP_GEMM_GROUP:
+      if (m < 1 || m > W12_MAX_M) return 0;
+      return group_ws_bytes(m, n, k);
     default: return 0;
   }
 }
@@ -265,23 +316,41 @@ w12_status w12_gemm(const uint16_t* x, uint32_t m, const w12_desc* d, uint16_t* 
   if (ws_bytes < need) return W12_ERR_WORKSPACE;
   if (need > 0 && !ws) return W12_ERR_NULL;
   if (!aligned(x, 16) || !aligned(y, 4) || !aligned(ws, 256)) return W12_ERR_ALIGN;
-  const GemmPlan p = make_plan(m, d->n, d->k, EPI_BF16);
-  GemmArgs a;
-  memset(&a, 0, sizeof(a));
-  a.x = x;
-  a.w = (const uint8_t*)d->tiles;
-  a.esc_off = d->esc_off;
-  a.esc = d->esc;
-  a.y = y;
-  a.partial = (float*)ws;
-  a.m = m;
-  a.n = (uint32_t)d->n;
-  a.k = (uint32_t)d->k;
-  a.g_cols = (uint32_t)(d->k / 128);
-  a.nb = (uint32_t)(d->n / 16);
-  fill_args_codebook(a, d);
-  const int src = codebook_is_run(d->codebook) ? SRC_RUN : SRC_LUT;
-  return hip_status(launch_gemm(a, src, EPI_BF16, p, (hipStream_t)stream));
+  return hip_status(launch_w12_group(x, m, &d, &y, 1, ws, (hipStream_t)stream));
+}
+
+w12_status w12_gemm_group(const uint16_t* x, uint32_t m, const w12_desc* const* descs,
+                          uint32_t n_w, uint16_t* const* ys, void* ws, size_t ws_bytes,
+                          void* stream) {
+  if (!x || !descs || !ys) return W12_ERR_NULL;
+  if (n_w < 1 || n_w > W12_MAX_GROUP || m < 1 || m > W12_MAX_M) return W12_ERR_RANGE;
+  uint64_t n_total = 0;
+  for (uint32_t i = 0; i < n_w; ++i) {
+    w12_status st = check_desc(descs[i], true);
+    if (st != W12_OK) return st;
+    if (!ys[i]) return W12_ERR_NULL;
+    if (descs[i]->k != descs[0]->k) return W12_ERR_SHAPE;
+    if (!aligned(ys[i], 4)) return W12_ERR_ALIGN;
+    n_total += descs[i]->n;
+  }
+  if (n_total >= kMaxN) return W12_ERR_SHAPE;
+  const size_t need = group_ws_bytes(m, n_total, descs[0]->k);
+  if (ws_bytes < need) return W12_ERR_WORKSPACE;
+  if (need > 0 && !ws) return W12_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(ws, 256)) return W12_ERR_ALIGN;
+  // one launch per codebook kind (run / lookup table), in the callers' order within each
+  const w12_desc* dd[2][W12_MAX_GROUP];
+  uint16_t* yy[2][W12_MAX_GROUP];
+  uint32_t cnt[2] = {0, 0};
+  for (uint32_t i = 0; i < n_w; ++i) {
+    const int kind = codebook_is_run(descs[i]->codebook) ? 0 : 1;
+    dd[kind][cnt[kind]] = descs[i];
+    yy[kind][cnt[kind]++] = ys[i];
+  }
+  hipError_t e = hipSuccess;
+  for (int kind = 0; kind < 2 && e == hipSuccess; ++kind)
+    if (cnt[kind]) e = launch_w12_group(x, m, dd[kind], yy[kind], cnt[kind], ws, (hipStream_t)stream);
+  return hip_status(e);
 }
 
 w12_status w12_gemm_bf16(const uint16_t* x, uint32_t m, const uint16_t* w, uint64_t n,
@@ -289,22 +358,19 @@ w12_status w12_gemm_bf16(const uint16_t* x, uint32_t m, const uint16_t* w, uint6
   if (!x || !w || !y) return W12_ERR_NULL;
   if (!shape_ok(n, k)) return W12_ERR_SHAPE;
   if (m < 1 || m > W12_MAX_M) return W12_ERR_RANGE;
-  const size_t need = gemm_ws_bytes(m, n, k);
+  const size_t need = gemm_ws_bytes(m, n, k, true);
   if (ws_bytes < need) return W12_ERR_WORKSPACE;
   if (need > 0 && !ws) return W12_ERR_NULL;
   if (!aligned(x, 16) || !aligned(w, 16) || !aligned(y, 4) || !aligned(ws, 256)) return W12_ERR_ALIGN;
-  const GemmPlan p = make_plan(m, n, k, EPI_BF16);
+  const GemmPlan p = make_plan(m, n, k, EPI_BF16, true);
   GemmArgs a;
   memset(&a, 0, sizeof(a));
   a.x = x;
-  a.w = (const uint8_t*)w;
-  a.y = y;
   a.partial = (float*)ws;
-  a.m = m;
-  a.n = (uint32_t)n;
-  a.k = (uint32_t)k;
-  a.g_cols = (uint32_t)(k / 128);
-  a.nb = (uint32_t)(n / 16);
+  a.p.seg[0].w = (const uint8_t*)w;
+  a.p.seg[0].y = y;
+  a.p.seg[0].n = (uint32_t)n;
+  fill_params(a.p, m, k, n, 1);
   return hip_status(launch_gemm(a, SRC_BF16, EPI_BF16, p, (hipStream_t)stream));
 }
 
@@ -326,20 +392,13 @@ w12_status w12_lmhead_verify(const uint16_t* x, uint32_t m, const w12_desc* d, c
   GemmArgs a;
   memset(&a, 0, sizeof(a));
   a.x = x;
-  a.w = (const uint8_t*)d->tiles;
-  a.esc_off = d->esc_off;
-  a.esc = d->esc;
+  a.p.seg[0] = w12_seg(d, nullptr, 0);
+  fill_params(a.p, m, d->k, d->n, 1);
   a.logits = (float*)(base + L.logits);
   a.sabs = (float*)(base + L.sabs);
   a.rbmax_v = (float*)(base + L.rbmax_v);
   a.rbmax_s = (float*)(base + L.rbmax_s);
   a.rbmax_i = (int32_t*)(base + L.rbmax_i);
-  a.m = m;
-  a.n = (uint32_t)d->n;
-  a.k = (uint32_t)d->k;
-  a.g_cols = (uint32_t)(d->k / 128);
-  a.nb = (uint32_t)(d->n / 16);
-  fill_args_codebook(a, d);
   const int src = codebook_is_run(d->codebook) ? SRC_RUN : SRC_LUT;
   hipError_t e = launch_gemm(a, src, EPI_LOGITS, p, s);
   VerifyArgs v;
@@ -359,13 +418,13 @@ w12_status w12_lmhead_verify(const uint16_t* x, uint32_t m, const w12_desc* d, c
   v.draft = draft;
   v.accepted = accepted_out;
   v.m = m;
-  v.n = a.n;
-  v.k = a.k;
-  v.g_cols = a.g_cols;
-  v.nb = a.nb;
+  v.n = a.p.n;
+  v.k = a.p.k;
+  v.g_cols = a.p.g_cols;
+  v.nb = a.p.nb;
   v.n_draft = n_draft;
   v.e_max = d->e_max;
-  for (int i = 0; i < 4; ++i) v.lut[i] = a.lut[i];
+  for (int i = 0; i < 4; ++i) v.lut[i] = a.p.seg[0].lut[i];
   if (e == hipSuccess) e = launch_verify_pass2(v, s);
   if (e == hipSuccess) e = launch_accept(v, s);
   return hip_status(e);

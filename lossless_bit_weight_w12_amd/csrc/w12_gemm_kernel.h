@@ -5,30 +5,34 @@
 // it is": decoding happens bit-exactly inside the GEMM; review page, "The mechanisms
 // it found": 12 instead of 16 bits per weight cuts the weight traffic by a quarter).
 //
-// Work decomposition
-//   workgroup = 4 waves = RBW consecutive row-blocks (16 rows each) x a K-range of
-//   tile columns [ga, gb) (blockIdx.y selects the split).  The K-range is processed in
-//   chunks of 4 tile columns; wave w takes column c0 + w of each chunk, so the four
-//   waves stream four adjacent 3 KB tiles per row-block.  x for the chunk is staged
-//   through LDS (register prefetch one chunk ahead, so the global x loads are issued
-//   before the tile prefetch and never make a wait on the tiles necessary).
-//   Tile loads are issued one chunk ahead (double-buffered registers).
+// A launch multiplies one x by up to kMaxSeg weights that share K (a group: q, k and
+// v of a layer, or gate and up); their row-blocks are numbered consecutively and each
+// wave looks up the weight its row-block belongs to (tiles, escapes, codebook, y).  A
+// single GEMM is a group of one.
+//
+// Kernel shapes
+//   k_gemm (wave columns): a workgroup of NWV waves owns RBW consecutive row-blocks and
+//   a K-range [ga, gb) (blockIdx.y selects the split); wave w streams tile columns
+//   ga+w, ga+w+NWV, ... with its own x column in LDS, so no workgroup barrier is needed;
+//   the waves' partial sums meet in LDS at the end.
+//   k_gemm_cs (column synchronous, MFMA): a workgroup of NW waves owns NW row-blocks,
+//   one per wave; all waves walk the same columns and share each x column through LDS
+//   (one barrier per column).
 // Per tile, lane l (row r = l%16, k-group q = l/16) holds the 32 weights of its slot:
 //   three coalesced 16-byte loads per lane (1 KB per wave instruction), unpacked into
 //   16 BF16 pairs P[4j+p] = {w(k0+2p), w(k0+2p+1)} with k0 = 32j + 8q.  Those 8 BF16 of
 //   group j are exactly the lane's A operand of v_mfma_f32_16x16x32_bf16 (row r,
 //   k = 8q..8q+7 of the 32-wide step), and adjacent-k pairs for v_dot2_f32_bf16.
-// M <= 15: VALU path, v_dot2 (2 MACs per instruction) with x pairs read from LDS as
-//   broadcast ds_read_b128 (16 lanes share each address); partial sums are reduced
-//   across the 4 lanes that share a row with cross-lane shuffles, then across waves.
-// M >= 16: MFMA path, W tile as the 16-row A operand, x as the B operand (16 or 32
-//   columns, rows >= M zero-filled in LDS).
+// m < W12_MFMA_MIN_M: VALU path, v_dot2 (2 MACs per instruction) with x pairs read from
+//   LDS as broadcast ds_read_b128; partial sums are reduced across the 4 lanes that
+//   share a row with cross-lane shuffles, then across waves.
+// Otherwise MFMA: W tile as the 16-row A operand, x as the B operand (16 or 32 columns,
+//   rows >= m zero-filled in LDS).
 // Escapes (exponents outside the codebook) are patched into the unpacked registers by
-//   the owning lane, walking the row-block's sorted escape list with a 64-record
-//   window held one record per lane (ballot selects the records of the current tile).
-// Split-K (blockIdx.y > 0 exists): FP32 partials go to the workspace and the last
-//   workgroup to arrive (ticket counter) sums them in split order -- deterministic --
-//   and resets the counter to zero for the next call.
+//   the owning lane, walking the row-block's sorted escape list through a 4-record
+//   window in scalar registers.
+// Split-K (gridDim.y > 1): FP32 partials go to the workspace and k_splitk_reduce sums
+//   them in split order (deterministic).
 #pragma once
 
 #include "w12_internal.h"
@@ -45,12 +49,44 @@ constexpr int kXsStride = 128 + 8;   // BF16 per LDS row of one wave's x column 
                                      // no bank conflicts for the MFMA B reads)
 
 
-// Scalar parameters of one GEMM launch.
-struct GemmParams {
-  uint32_t m, n, k, g_cols, nb;
+// The weight a row-block belongs to, selected from the launch's table with constant
+// indices only (the table stays in the kernel-argument segment; for a wave-uniform b
+// every field is a scalar).
+struct SegView {
+  const uint8_t* w;
+  const uint32_t* esc_off;
+  const uint32_t* esc;
+  uint16_t* y;
+  uint32_t rb0, n, basepair;
   uint32_t lut[4];
-  uint32_t basepair;
 };
+
+__device__ __forceinline__ SegView seg_view(const GemmParams& p, uint32_t b) {
+  SegView v;
+  v.w = p.seg[0].w;
+  v.esc_off = p.seg[0].esc_off;
+  v.esc = p.seg[0].esc;
+  v.y = p.seg[0].y;
+  v.rb0 = p.seg[0].rb0;
+  v.n = p.seg[0].n;
+  v.basepair = p.seg[0].basepair;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) v.lut[i] = p.seg[0].lut[i];
+#pragma unroll
+  for (int s = 1; s < kMaxSeg; ++s) {
+    const bool here = (uint32_t)s < p.nseg && b >= p.seg[s].rb0;
+    v.w = here ? p.seg[s].w : v.w;
+    v.esc_off = here ? p.seg[s].esc_off : v.esc_off;
+    v.esc = here ? p.seg[s].esc : v.esc;
+    v.y = here ? p.seg[s].y : v.y;
+    v.rb0 = here ? p.seg[s].rb0 : v.rb0;
+    v.n = here ? p.seg[s].n : v.n;
+    v.basepair = here ? p.seg[s].basepair : v.basepair;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v.lut[i] = here ? p.seg[s].lut[i] : v.lut[i];
+  }
+  return v;
+}
 
 // BF16 pair view of a 32-bit word.  Taken by value on purpose: this compiler
 // miscompiles __builtin_bit_cast applied directly to an ext-vector element (it reads
@@ -107,7 +143,7 @@ __device__ __forceinline__ void load_tile(TileRegs<SRC>& t, const uint8_t* __res
 
 // Registers -> 16 BF16 pairs (P[4j+p] = element 2p in the low half, 2p+1 in the high).
 template <int SRC>
-__device__ __forceinline__ void unpack_tile(const TileRegs<SRC>& t, const GemmParams& a,
+__device__ __forceinline__ void unpack_tile(const TileRegs<SRC>& t, const SegView& a,
                                             uint32_t P[16]) {
   if constexpr (SRC == SRC_BF16) {
 #pragma unroll
@@ -276,9 +312,7 @@ __device__ __forceinline__ void x_store(const XStage<MT>& st, uint16_t* xw, int 
 // k_splitk_reduce); with one split it writes y directly.
 template <int M, int MT, bool MF, int RBW, int NWV, int SRC, int EPI>
 __global__ __launch_bounds__(NWV * 64) void k_gemm(
-    const uint16_t* __restrict__ x, const uint8_t* __restrict__ w,
-    const uint32_t* __restrict__ esc_off, const uint32_t* __restrict__ esc,
-    uint16_t* __restrict__ y, float* __restrict__ out_f32, float* __restrict__ out_s,
+    const uint16_t* __restrict__ x, float* __restrict__ out_f32, float* __restrict__ out_s,
     float* __restrict__ rbmax_v, float* __restrict__ rbmax_s, int32_t* __restrict__ rbmax_i,
     GemmParams p) {
   constexpr int NH = MF ? MT / 16 : 1;
@@ -310,6 +344,14 @@ __global__ __launch_bounds__(NWV * 64) void k_gemm(
   }
 
   EscCursor ec[RBW];
+  SegView sv[RBW];          // the weight of each row-block (launch numbering b0 + rb)
+  uint32_t bl[RBW];         // the row-block inside that weight (clamped into range)
+#pragma unroll
+  for (int rb = 0; rb < RBW; ++rb) {
+    const uint32_t bg = min(b0 + rb, p.nb - 1u);
+    sv[rb] = seg_view(p, bg);
+    bl[rb] = bg - sv[rb].rb0;
+  }
 
   TileRegs<SRC> tA[RBW], tB[RBW];
   XStage<MT> xr;
@@ -319,16 +361,16 @@ __global__ __launch_bounds__(NWV * 64) void k_gemm(
   auto load_tiles = [&](TileRegs<SRC>* t, uint32_t g) {
     const uint32_t gl = min(g, gb - 1u);
 #pragma unroll
-    for (int rb = 0; rb < RBW; ++rb) load_tile<SRC>(t[rb], w, p, min(b0 + rb, p.nb - 1u), gl, lane);
+    for (int rb = 0; rb < RBW; ++rb) load_tile<SRC>(t[rb], sv[rb].w, p, bl[rb], gl, lane);
   };
 
   auto compute = [&](const TileRegs<SRC>* t, uint32_t g) {
     uint32_t P[RBW][16];
 #pragma unroll
     for (int rb = 0; rb < RBW; ++rb) {
-      unpack_tile<SRC>(t[rb], p, P[rb]);
+      unpack_tile<SRC>(t[rb], sv[rb], P[rb]);
       if constexpr (SRC != SRC_BF16) {
-        if (b0 + rb < p.nb) esc_apply(ec[rb], esc, g, lane, P[rb]);
+        if (b0 + rb < p.nb) esc_apply(ec[rb], sv[rb].esc, g, lane, P[rb]);
       }
     }
     const uint16_t* xrow = xw + 8 * q;
@@ -374,7 +416,7 @@ __global__ __launch_bounds__(NWV * 64) void k_gemm(
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int rb = 0; rb < RBW; ++rb)
-        if (ec[rb].stale) esc_refill(ec[rb], esc);
+        if (ec[rb].stale) esc_refill(ec[rb], sv[rb].esc);
     }
   };
 
@@ -392,7 +434,7 @@ __global__ __launch_bounds__(NWV * 64) void k_gemm(
     // (one or two dependent round trips) overlap the first tile fetch
     if constexpr (SRC != SRC_BF16) {
 #pragma unroll
-      for (int rb = 0; rb < RBW; ++rb) esc_begin(ec[rb], esc_off, esc, min(b0 + rb, p.nb - 1u), ga * 128u);
+      for (int rb = 0; rb < RBW; ++rb) esc_begin(ec[rb], sv[rb].esc_off, sv[rb].esc, bl[rb], ga * 128u);
     }
     x_store<MT>(xr, xw, lane);
     __builtin_amdgcn_wave_barrier();
@@ -500,8 +542,15 @@ __global__ __launch_bounds__(NWV * 64) void k_gemm(
       const uint32_t b = b0 + rb;
       const float v = final_value(red, o);
       if (b >= p.nb || (uint32_t)m >= m_rows) continue;
-      if (direct) y[(size_t)m * p.n + 16u * b + rr] = f32_to_bf16_rne(v);
-      else out_f32[((size_t)split * m_rows + m) * p.n + 16u * b + rr] = v;
+      if (direct) {
+        const bool second = RBW == 2 && rb == 1;     // per-thread: pick the row-block's weight
+        uint16_t* yy = second ? sv[RBW - 1].y : sv[0].y;
+        const uint32_t nn = second ? sv[RBW - 1].n : sv[0].n;
+        const uint32_t bb = second ? bl[RBW - 1] : bl[0];
+        yy[(size_t)m * nn + 16u * bb + rr] = f32_to_bf16_rne(v);
+      } else {
+        out_f32[((size_t)split * m_rows + m) * p.n + 16u * b + rr] = v;
+      }
     }
   }
 }
@@ -517,9 +566,7 @@ __global__ __launch_bounds__(NWV * 64) void k_gemm(
 // lane l holds D[4q+i][l%16 + 16h], i.e. rows 16b+4q..16b+4q+3 of output column m.
 template <int MT, int NW, int SRC, int EPI>
 __global__ __launch_bounds__(NW * 64) void k_gemm_cs(
-    const uint16_t* __restrict__ x, const uint8_t* __restrict__ w,
-    const uint32_t* __restrict__ esc_off, const uint32_t* __restrict__ esc,
-    uint16_t* __restrict__ y, float* __restrict__ out_f32, float* __restrict__ out_s,
+    const uint16_t* __restrict__ x, float* __restrict__ out_f32, float* __restrict__ out_s,
     float* __restrict__ rbmax_v, float* __restrict__ rbmax_s, int32_t* __restrict__ rbmax_i,
     GemmParams p) {
   constexpr int NH = MT / 16;
@@ -533,7 +580,8 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_cs(
   const int r = lane & 15, q = lane >> 4;
   const uint32_t b = blockIdx.x * NW + (uint32_t)wave;
   const bool bvalid = b < p.nb;
-  const uint32_t bl = min(b, p.nb - 1u);
+  const SegView sv = seg_view(p, min(b, p.nb - 1u));
+  const uint32_t bl = min(b, p.nb - 1u) - sv.rb0;   // row-block inside its weight
   const uint32_t split = blockIdx.y;
   // split s of S covers tile columns [s*G/S, (s+1)*G/S): the K range dealt evenly
   const uint32_t ga = (uint32_t)(((uint64_t)split * p.g_cols) / gridDim.y);
@@ -571,9 +619,9 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_cs(
   };
   auto compute = [&](const TileRegs<SRC>& t, uint32_t g) {
     uint32_t P[16];
-    unpack_tile<SRC>(t, p, P);
+    unpack_tile<SRC>(t, sv, P);
     if constexpr (SRC != SRC_BF16) {
-      if (bvalid) esc_apply(ec, esc, g, lane, P);
+      if (bvalid) esc_apply(ec, sv.esc, g, lane, P);
     }
     const uint16_t* xrow = &xs[g & 1u][8 * q];
 #pragma unroll
@@ -592,7 +640,7 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_cs(
     }
     if constexpr (SRC != SRC_BF16) {
       __builtin_amdgcn_sched_barrier(0);
-      if (ec.stale) esc_refill(ec, esc);
+      if (ec.stale) esc_refill(ec, sv.esc);
     }
   };
 
@@ -600,26 +648,27 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_cs(
   // end, x zeroed), so each wait is a fixed count; one barrier per column.
   uint32_t g = ga;
   xload(g);
-  load_tile<SRC>(tA, w, p, bl, g, lane);
-  if constexpr (SRC != SRC_BF16) esc_begin(ec, esc_off, esc, bl, ga * 128u);
+  load_tile<SRC>(tA, sv.w, p, bl, g, lane);
+  if constexpr (SRC != SRC_BF16) esc_begin(ec, sv.esc_off, sv.esc, bl, ga * 128u);
   xstore(g & 1u);
   __syncthreads();
   for (;;) {
     xload(g + 1);
-    load_tile<SRC>(tB, w, p, bl, min(g + 1, gb - 1u), lane);
+    load_tile<SRC>(tB, sv.w, p, bl, min(g + 1, gb - 1u), lane);
     compute(tA, g);
     xstore((g + 1) & 1u);
     __syncthreads();
     if (++g >= gb) break;
     xload(g + 1);
-    load_tile<SRC>(tA, w, p, bl, min(g + 1, gb - 1u), lane);
+    load_tile<SRC>(tA, sv.w, p, bl, min(g + 1, gb - 1u), lane);
     compute(tB, g);
     xstore((g + 1) & 1u);
     __syncthreads();
     if (++g >= gb) break;
   }
 
-  const uint32_t n0 = 16u * b + 4u * (uint32_t)q;
+  const uint32_t n0 = 16u * b + 4u * (uint32_t)q;       // launch numbering (logits, partials)
+  const uint32_t n0l = 16u * bl + 4u * (uint32_t)q;     // inside the weight (y)
   if constexpr (EPI == EPI_LOGITS) {
     if (!bvalid) return;
 #pragma unroll
@@ -660,7 +709,7 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_cs(
     auto store_y = [&](uint32_t m, const f32x4& v) {
       const uint32_t lo = (uint32_t)f32_to_bf16_rne(v[0]) | ((uint32_t)f32_to_bf16_rne(v[1]) << 16);
       const uint32_t hi = (uint32_t)f32_to_bf16_rne(v[2]) | ((uint32_t)f32_to_bf16_rne(v[3]) << 16);
-      *reinterpret_cast<uint2*>(y + (size_t)m * p.n + n0) = make_uint2(lo, hi);
+      *reinterpret_cast<uint2*>(sv.y + (size_t)m * sv.n + n0l) = make_uint2(lo, hi);
     };
 #pragma unroll
     for (int h = 0; h < NH; ++h) {
@@ -674,13 +723,15 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_cs(
 
 // Sum of the split-K partials in split order (deterministic), rounded to BF16.
 static __global__ __launch_bounds__(256) void k_splitk_reduce(const float* __restrict__ partial,
-                                                       uint16_t* __restrict__ y, uint32_t nsplit,
-                                                       uint32_t mn) {
+                                                       GemmParams p, uint32_t nsplit) {
+  const uint32_t mn = p.m * p.n;
   const uint32_t stride = gridDim.x * 256u;
   for (uint32_t i = blockIdx.x * 256u + threadIdx.x; i < mn; i += stride) {
     float s = 0.f;
     for (uint32_t sp = 0; sp < nsplit; ++sp) s += partial[(size_t)sp * mn + i];
-    y[i] = f32_to_bf16_rne(s);
+    const uint32_t m = i / p.n, row = i - m * p.n;
+    const SegView sv = seg_view(p, row >> 4);
+    sv.y[(size_t)m * sv.n + row - 16u * sv.rb0] = f32_to_bf16_rne(s);
   }
 }
 
@@ -689,19 +740,11 @@ static __global__ __launch_bounds__(256) void k_splitk_reduce(const float* __res
 template <int SRC>
 hipError_t launch_gemm_src(const GemmArgs& a, int epi, const GemmPlan& pl, hipStream_t s) {
   dim3 grid(pl.n_rbg, pl.nsplit);
-  GemmParams p;
-  p.m = a.m;
-  p.n = a.n;
-  p.k = a.k;
-  p.g_cols = a.g_cols;
-  p.nb = a.nb;
-  for (int i = 0; i < 4; ++i) p.lut[i] = a.lut[i];
-  p.basepair = a.basepair;
+  const GemmParams& p = a.p;
   float* f32 = epi == EPI_LOGITS ? a.logits : a.partial;
 #define W12_L(M_, MT_, MF_, RBW_, NWV_, EPI_)                                                     \
   hipLaunchKernelGGL((k_gemm<M_, MT_, MF_, RBW_, NWV_, SRC, EPI_>), grid, dim3(NWV_ * 64), 0, s, \
-                     a.x, a.w, a.esc_off, a.esc, a.y, f32, a.sabs, a.rbmax_v, a.rbmax_s,        \
-                     a.rbmax_i, p)
+                     a.x, f32, a.sabs, a.rbmax_v, a.rbmax_s, a.rbmax_i, p)
 #define W12_RBW(M_, MT_, MF_, EPI_)                   \
   do {                                                \
     if (pl.rbw == 2) W12_L(M_, MT_, MF_, 2, 4, EPI_); \
@@ -715,11 +758,11 @@ hipError_t launch_gemm_src(const GemmArgs& a, int epi, const GemmPlan& pl, hipSt
 #define W12_CS(MT_, EPI_)                                                                     \
   do {                                                                                        \
     if (pl.nw == 8)                                                                           \
-      hipLaunchKernelGGL((k_gemm_cs<MT_, 8, SRC, EPI_>), grid, dim3(512), 0, s, a.x, a.w,     \
-                         a.esc_off, a.esc, a.y, f32, a.sabs, a.rbmax_v, a.rbmax_s, a.rbmax_i, p); \
+      hipLaunchKernelGGL((k_gemm_cs<MT_, 8, SRC, EPI_>), grid, dim3(512), 0, s, a.x, f32,     \
+                         a.sabs, a.rbmax_v, a.rbmax_s, a.rbmax_i, p);                         \
     else                                                                                      \
-      hipLaunchKernelGGL((k_gemm_cs<MT_, 4, SRC, EPI_>), grid, dim3(256), 0, s, a.x, a.w,     \
-                         a.esc_off, a.esc, a.y, f32, a.sabs, a.rbmax_v, a.rbmax_s, a.rbmax_i, p); \
+      hipLaunchKernelGGL((k_gemm_cs<MT_, 4, SRC, EPI_>), grid, dim3(256), 0, s, a.x, f32,     \
+                         a.sabs, a.rbmax_v, a.rbmax_s, a.rbmax_i, p);                         \
   } while (0)
 #define W12_CS_EPI(MT_)                                                     \
   do {                                                                      \
@@ -727,7 +770,7 @@ hipError_t launch_gemm_src(const GemmArgs& a, int epi, const GemmPlan& pl, hipSt
     else if constexpr (SRC != SRC_BF16) W12_CS(MT_, EPI_LOGITS);           \
   } while (0)
   if (pl.kind == KIND_COLUMN_SYNC) {
-    if (a.m <= 16) W12_CS_EPI(16);
+    if (p.m <= 16) W12_CS_EPI(16);
     else W12_CS_EPI(32);
   } else if (pl.mfma) {
     W12_EPI(16, 16, true);
@@ -736,7 +779,7 @@ hipError_t launch_gemm_src(const GemmArgs& a, int epi, const GemmPlan& pl, hipSt
   case M_:                                                     \
     if constexpr (M_ < W12_MFMA_MIN_M) W12_EPI(M_, M_, false); \
     break;
-    switch (a.m) {
+    switch (p.m) {
       W12_VCASE(1) W12_VCASE(2) W12_VCASE(3) W12_VCASE(4) W12_VCASE(5)
       W12_VCASE(6) W12_VCASE(7) W12_VCASE(8) W12_VCASE(9) W12_VCASE(10)
       W12_VCASE(11) W12_VCASE(12) W12_VCASE(13) W12_VCASE(14) W12_VCASE(15)
@@ -751,10 +794,10 @@ hipError_t launch_gemm_src(const GemmArgs& a, int epi, const GemmPlan& pl, hipSt
 #undef W12_L
   hipError_t e = hipGetLastError();
   if (e == hipSuccess && epi == EPI_BF16 && pl.nsplit > 1) {
-    const uint32_t mn = a.m * a.n;
+    const uint32_t mn = p.m * p.n;
     uint32_t blocks = (mn + 255u) / 256u;
     if (blocks > 1024u) blocks = 1024u;
-    hipLaunchKernelGGL(k_splitk_reduce, dim3(blocks), dim3(256), 0, s, a.partial, a.y, pl.nsplit, mn);
+    hipLaunchKernelGGL(k_splitk_reduce, dim3(blocks), dim3(256), 0, s, a.partial, p, pl.nsplit);
     e = hipGetLastError();
   }
   return e;

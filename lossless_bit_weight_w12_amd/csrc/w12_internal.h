@@ -27,21 +27,38 @@ enum Epi : int {
   EPI_LOGITS = 1,  // fp32 logits [m][n] + per-row-block maxima (verification pass 1)
 };
 
+// One weight of a launch.  A launch multiplies one x by up to kMaxSeg weights that
+// share K (a group), their row-blocks numbered consecutively; a single GEMM is a group
+// of one.
+constexpr int kMaxSeg = 4;
+struct Seg {
+  const uint8_t* w;         // W12 tiles, or BF16 rows [n][k]
+  const uint32_t* esc_off;  // [n/16 + 1] (W12)
+  const uint32_t* esc;      // [n_esc] (W12)
+  uint16_t* y;              // [m][n] BF16 (EPI_BF16)
+  uint32_t rb0;             // first row-block of this weight in the launch
+  uint32_t n;               // rows of this weight
+  uint32_t basepair;        // SRC_RUN: C[0] | C[0] << 16
+  uint32_t lut[4];          // SRC_LUT: codebook bytes C[0..15]
+};
+
+// Scalar parameters of one launch (a kernel argument).
+struct GemmParams {
+  uint32_t m, k, g_cols;
+  uint32_t nb, n;           // row-blocks and rows of all the launch's weights together
+  uint32_t nseg;
+  Seg seg[kMaxSeg];
+};
+
 struct GemmArgs {
   const uint16_t* x;        // [m][k] BF16
-  const uint8_t* w;         // W12 tiles, or BF16 rows
-  const uint32_t* esc_off;  // [nb + 1]
-  const uint32_t* esc;      // [n_esc]
-  uint16_t* y;              // [m][n] BF16 (EPI_BF16)
   float* logits;            // [m][n] (EPI_LOGITS)
   float* sabs;              // [m][n] sum_k |x_k||w_k| per logit (EPI_LOGITS)
   float* rbmax_v;           // [m][nb] largest logit of each row-block (EPI_LOGITS)
   float* rbmax_s;           // [m][nb] largest sabs of each row-block (EPI_LOGITS)
   int32_t* rbmax_i;         // [m][nb] index of rbmax_v, lowest on ties (EPI_LOGITS)
-  float* partial;           // [nsplit][m][n] split-K partial sums
-  uint32_t m, n, k, g_cols, nb;
-  uint32_t lut[4];          // codebook bytes C[0..15] (SRC_LUT)
-  uint32_t basepair;        // C[0] | C[0] << 16 (SRC_RUN)
+  float* partial;           // [nsplit][m][n] split-K partial sums (launch numbering)
+  GemmParams p;
 };
 
 // Kernel shapes of the GEMM family.

@@ -41,14 +41,12 @@ class DecodeStack:
 
     def _layer_calls(self, L):
         o = self.out
-        return [w12.prepare_gemm(self.h, L["q"], o["q"]),
-                w12.prepare_gemm(self.h, L["k"], o["k"]),
-                w12.prepare_gemm(self.h, L["v"], o["v"]),
+        # q, k, v read h and gate, up read rms(o): one grouped launch each
+        return [w12.prepare_gemm_group(self.h, [L["q"], L["k"], L["v"]], [o["q"], o["k"], o["v"]]),
                 w12.prepare_rms(o["q"], self.a),
                 w12.prepare_gemm(self.a, L["o"], o["o"]),
                 w12.prepare_rms(o["o"], self.b),
-                w12.prepare_gemm(self.b, L["gate"], o["gate"]),
-                w12.prepare_gemm(self.b, L["up"], o["up"]),
+                w12.prepare_gemm_group(self.b, [L["gate"], L["up"]], [o["gate"], o["up"]]),
                 w12.prepare_rms(o["up"], self.c),
                 w12.prepare_gemm(self.c, L["down"], o["down"]),
                 w12.prepare_rms(o["down"], self.h)]

@@ -14,12 +14,13 @@ from dataclasses import dataclass
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libw12.so")
 _LIB = None
 
-OP_ENCODE, OP_DECODE, OP_GEMM, OP_GEMM_BF16, OP_VERIFY = 0, 1, 2, 3, 4
+OP_ENCODE, OP_DECODE, OP_GEMM, OP_GEMM_BF16, OP_VERIFY, OP_GEMM_GROUP = 0, 1, 2, 3, 4, 5
 MAX_M = 32
+MAX_GROUP = 4
 STATUS = {0: "W12_OK", -1: "W12_ERR_NULL", -2: "W12_ERR_SHAPE", -3: "W12_ERR_RANGE",
           -4: "W12_ERR_FORMAT", -5: "W12_ERR_WORKSPACE", -6: "W12_ERR_HIP", -7: "W12_ERR_ALIGN"}
 EXPORTS = ("w12_tiles_bytes", "w12_workspace_bytes", "w12_workspace_init", "w12_encode_count",
-           "w12_encode", "w12_decode", "w12_gemm", "w12_gemm_bf16", "w12_lmhead_verify",
+           "w12_encode", "w12_decode", "w12_gemm", "w12_gemm_group", "w12_gemm_bf16", "w12_lmhead_verify",
            "w12_rms_rescale", "w12_status_str", "w12_version")
 
 
@@ -63,6 +64,9 @@ def lib():
         L.w12_gemm.restype = c_int32
         L.w12_gemm.argtypes = [c_void_p, c_uint32, ctypes.POINTER(W12Desc), c_void_p, c_void_p,
                                c_size_t, c_void_p]
+        L.w12_gemm_group.restype = c_int32
+        L.w12_gemm_group.argtypes = [c_void_p, c_uint32, c_void_p, c_uint32, c_void_p, c_void_p,
+                                     c_size_t, c_void_p]
         L.w12_gemm_bf16.restype = c_int32
         L.w12_gemm_bf16.argtypes = [c_void_p, c_uint32, c_void_p, c_uint64, c_uint64, c_void_p,
                                     c_void_p, c_size_t, c_void_p]
@@ -222,6 +226,33 @@ def gemm(x, t: W12Tensor, out=None):
     return out
 
 
+def _group_args(x, ts, outs):
+    torch = _torch()
+    x = _as_bits(x)
+    m = x.shape[0]
+    if not 1 <= len(ts) <= MAX_GROUP:
+        raise ValueError(f"a group holds 1..{MAX_GROUP} weights")
+    if any(t.k != x.shape[1] for t in ts):
+        raise ValueError("every weight of a group must have k = x.shape[1]")
+    if outs is None:
+        outs = [torch.empty((m, t.n), dtype=torch.bfloat16, device=x.device) for t in ts]
+    descs = [t.desc() for t in ts]
+    darr = (ctypes.POINTER(W12Desc) * len(ts))(*[ctypes.pointer(d) for d in descs])
+    yarr = (c_void_p * len(ts))(*[_as_bits(o).data_ptr() for o in outs])
+    ws = workspace(max(workspace_bytes(OP_GEMM_GROUP, m, sum(t.n for t in ts), ts[0].k), 256),
+                   x.device)
+    args = (_ptr(x), m, ctypes.cast(darr, c_void_p), len(ts), ctypes.cast(yarr, c_void_p), _ptr(ws),
+            ws.numel(), _stream(x.device))
+    return args, outs, (x, ts, outs, ws, descs, darr, yarr)
+
+
+def gemm_group(x, ts, outs=None):
+    """y_i = x . W_i^T for the weights ts (1..4, same k) in one launch per codebook kind."""
+    args, outs, keep = _group_args(x, ts, outs)
+    _check("w12_gemm_group", lib().w12_gemm_group(*args))
+    return outs
+
+
 def gemm_bf16(x, w, out=None):
     """The same kernel family on plain BF16 weights w [n, k]."""
     torch = _torch()
@@ -313,6 +344,11 @@ def prepare_gemm(x, t: W12Tensor, out) -> Prepared:
     d = t.desc()
     args = (_ptr(x), m, ctypes.byref(d), _ptr(out), _ptr(ws), ws.numel(), _stream(x.device))
     return Prepared("w12_gemm", lib().w12_gemm, args, (x, t, out, ws, d))
+
+
+def prepare_gemm_group(x, ts, outs) -> Prepared:
+    args, outs, keep = _group_args(x, ts, outs)
+    return Prepared("w12_gemm_group", lib().w12_gemm_group, args, keep)
 
 
 def prepare_rms(x, out) -> Prepared:

@@ -102,6 +102,53 @@ def test_gemm_lut_codebook_and_escapes(env, m):
         _gemm_case(env, w2, x, "w12")
 
 
+# weight groups sharing x: few row-blocks with split K (q/k/v-like), many row-blocks
+# (gate/up-like), and ragged groups whose row-block boundaries fall inside workgroups
+GROUPS = [[(320, 512), (64, 512), (64, 512)],
+          [(1088, 1280), (1088, 1280)],
+          [(48, 640), (16, 640), (32, 640), (272, 640)],
+          [(16, 4096)]]
+
+
+@pytest.mark.parametrize("m", [1, 2, 3, 4, 8, 15, 16, 24, 32])
+def test_gemm_group(env, m):
+    torch, w12 = env
+    g = np.random.default_rng(7000 + m)
+    for shapes in GROUPS:
+        k = shapes[0][1]
+        say("gemm group", m, shapes)
+        ws = [wi.gaussian_bf16(sh, 0.02, g) for sh in shapes]
+        x = wi.gaussian_bf16((m, k), 1.0, g)
+        ts = [w12.encode(to_dev(w, torch)) for w in ws]
+        outs = [torch.full((m, sh[0]), -1, dtype=torch.int16, device="cuda:0").view(torch.bfloat16)
+                for sh in shapes]
+        w12.gemm_group(to_dev(x, torch), ts, outs)
+        torch.cuda.synchronize()
+        for w, y in zip(ws, outs):
+            z, s = o.gemm_reference(x, w)
+            assert o.gemm_accept(to_host(y), z, s).all()
+
+
+def test_gemm_group_mixed_codebooks(env):
+    """Run and lookup-table codebooks in one call (two launches), escapes in both."""
+    torch, w12 = env
+    g = np.random.default_rng(7100)
+    k = 1280
+    ws = [wi.add_exponent_outliers(wi.gaussian_bf16((320, k), 0.02, g), 0.01, 11),
+          wide_exponents((64, k), g, 104, 130),
+          wi.gaussian_bf16((96, k), 0.02, g),
+          wide_exponents((32, k), g, 110, 140)]
+    for m in (1, 7, 24):
+        say("gemm group mixed", m)
+        x = wi.gaussian_bf16((m, k), 1.0, g)
+        ts = [w12.encode(to_dev(w, torch)) for w in ws]
+        outs = w12.gemm_group(to_dev(x, torch), ts)
+        torch.cuda.synchronize()
+        for w, y in zip(ws, outs):
+            z, s = o.gemm_reference(x, w)
+            assert o.gemm_accept(to_host(y), z, s).all()
+
+
 @pytest.mark.parametrize("m", [1, 2, 4, 5, 8, 12, 15, 16, 20, 32])
 def test_gemm_bf16_baseline(env, m):
     g = np.random.default_rng(3000 + m)

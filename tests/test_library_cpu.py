@@ -104,6 +104,31 @@ def test_gemm_validation(L):
     assert gemm(L, d=mis) == -7
 
 
+def test_gemm_group_validation(L):
+    f = L.w12_gemm_group
+    ds = [desc(n=1024, k=1024), desc(n=256, k=1024), desc(n=256, k=1024)]
+    darr = (ctypes.POINTER(B.W12Desc) * 3)(*[ctypes.pointer(d) for d in ds])
+    yarr = (ctypes.c_void_p * 3)(FAKE, FAKE, FAKE)
+    big = 1 << 30
+    assert f(None, 1, darr, 3, yarr, FAKE, big, None) == -1
+    assert f(FAKE, 1, None, 3, yarr, FAKE, big, None) == -1
+    assert f(FAKE, 1, darr, 3, None, FAKE, big, None) == -1
+    assert f(FAKE, 1, darr, 0, yarr, FAKE, big, None) == -3
+    assert f(FAKE, 1, darr, 5, yarr, FAKE, big, None) == -3
+    assert f(FAKE, 33, darr, 3, yarr, FAKE, big, None) == -3
+    assert f(FAKE, 1, darr, 3, yarr, FAKE, 0, None) == -5           # split-K needs partials
+    assert f(FAKE + 2, 1, darr, 3, yarr, FAKE, big, None) == -7
+    yarr[1] = None
+    assert f(FAKE, 1, darr, 3, yarr, FAKE, big, None) == -1
+    yarr[1] = FAKE
+    odd = (ctypes.POINTER(B.W12Desc) * 2)(ctypes.pointer(desc(k=1024)), ctypes.pointer(desc(k=2048)))
+    assert f(FAKE, 1, odd, 2, yarr, FAKE, big, None) == -2           # different k
+    badcb = (ctypes.POINTER(B.W12Desc) * 2)(ctypes.pointer(desc()), ctypes.pointer(desc(cb=(5,) * 16)))
+    assert f(FAKE, 1, badcb, 2, yarr, FAKE, big, None) == -4
+    assert w12.workspace_bytes(w12.OP_GEMM_GROUP, 24, 7168, 5120) >= \
+        w12.workspace_bytes(w12.OP_GEMM, 24, 7168, 5120)
+
+
 def test_gemm_bf16_validation(L):
     f = L.w12_gemm_bf16
     assert f(None, 1, FAKE, 1024, 1024, FAKE, FAKE, 1 << 30, None) == -1
