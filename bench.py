@@ -248,6 +248,8 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=20)
     ap.add_argument("--profile-decode", action="store_true",
                     help="build the 64-layer decode stack, run --steps steps and exit (for rocprofv3)")
+    ap.add_argument("--profile-verify", action="store_true",
+                    help="run --steps LM-head verifications (M = 16) and exit (for rocprofv3)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported (this path has no "
@@ -260,6 +262,16 @@ def main():
     import lossless_bit_weight_w12_amd as w12
 
     dev = torch.device("cuda:0")
+    if args.profile_verify:
+        c5 = wi.CONFIG_SHAPES[5]
+        head = w12.encode(wi.device_lm_head(torch, c5["vocab"], c5["hidden"]))
+        x16 = torch.from_numpy(wi.verify_batch_x(0).view(np.int16)).to(dev)
+        draft = torch.zeros(16, dtype=torch.int32, device=dev)
+        for _ in range(args.steps):
+            w12.lmhead_verify(x16, head, draft)
+        torch.cuda.synchronize()
+        log("bench: profile-verify run done")
+        return
     if args.profile_decode:
         stack, h0 = build_decode_stack(torch, w12, wi, np, dev)
         for _ in range(args.steps):

@@ -32,6 +32,7 @@
 namespace w12 {
 
 constexpr int kLimbs = 18;   // 18 x 32 bits > 542 bits (largest |sum| for K < 2^20)
+constexpr uint32_t kScreenMax = 512;   // candidates screened in FP64 (more: all go exact)
 
 __device__ __forceinline__ bool exact_parts(uint32_t bits, int& sgn, uint32_t& mant, int& ex) {
   const uint32_t e = (bits >> 7) & 0xFFu, m = bits & 0x7Fu;
@@ -67,46 +68,55 @@ __device__ __forceinline__ void limb_add(unsigned long long* limbs, int sgn, uin
   if (hi) atomicAdd(limbs + idx + 1, (unsigned long long)hi);
 }
 
-__global__ __launch_bounds__(256) void k_verify_pass2(VerifyArgs a) {
-  __shared__ float s_bv[256];
-  __shared__ int32_t s_bi[256];
-  __shared__ double s_xm[256];
+constexpr uint32_t kT = 512;   // threads of the pass-2 workgroup (one workgroup per row)
+
+__global__ __launch_bounds__(kT) void k_verify_pass2(VerifyArgs a) {
+  __shared__ float s_bv[kT];
+  __shared__ int32_t s_bi[kT];
+  __shared__ double s_d0[kT], s_d1[kT];
+  __shared__ uint32_t s_u0[kT];
   __shared__ unsigned long long limbs[kLimbs];
   __shared__ uint32_t best[kLimbs];
   __shared__ int32_t s_best_v, s_best_sign;
-  __shared__ uint32_t s_cnt, s_bad;
+  __shared__ uint32_t s_cnt, s_bad, s_nsurv;
+  __shared__ double s_z64[kScreenMax], s_b64[kScreenMax];
   const uint32_t row = blockIdx.x, tid = threadIdx.x;
   const uint16_t* xr = a.x + (uint64_t)row * a.k;
+  const float* rv = a.rbmax_v + (uint64_t)row * a.nb;
+  const float* rs = a.rbmax_s + (uint64_t)row * a.nb;
+  const int32_t* ri = a.rbmax_i + (uint64_t)row * a.nb;
 
   // 1. z* and its index over the block maxima (NaN marks a non-finite block)
   float bv = -__builtin_inff();
   int32_t bi = 0x7FFFFFFF;
   bool bad = false;
-  for (uint32_t b = tid; b < a.nb; b += 256) {
-    const float v = a.rbmax_v[(uint64_t)row * a.nb + b];
-    const int32_t i = a.rbmax_i[(uint64_t)row * a.nb + b];
+#pragma unroll 4
+  for (uint32_t b = tid; b < a.nb; b += kT) {
+    const float v = rv[b];
+    const int32_t i = ri[b];
     if (v != v) bad = true;
     else if (v > bv || (v == bv && i < bi)) { bv = v; bi = i; }
   }
   // 2. Xmax (and finiteness of x)
   double xm = 0.0;
-  for (uint32_t i = tid; i < a.k; i += 256) {
+#pragma unroll 4
+  for (uint32_t i = tid; i < a.k; i += kT) {
     const uint32_t bits = xr[i];
     if (((bits >> 7) & 0xFFu) == 0xFFu) bad = true;
     xm = fmax(xm, fabs((double)__uint_as_float(bits << 16)));
   }
   s_bv[tid] = bv;
   s_bi[tid] = bi;
-  s_xm[tid] = xm;
+  s_d0[tid] = xm;
   if (tid == 0) { s_cnt = 0; s_bad = 0; }
   __syncthreads();
   if (bad) atomicOr(&s_bad, 1u);
-  for (uint32_t off = 128; off > 0; off >>= 1) {
+  for (uint32_t off = kT / 2; off > 0; off >>= 1) {
     if (tid < off) {
       const float v2 = s_bv[tid + off];
       const int32_t i2 = s_bi[tid + off];
       if (v2 > s_bv[tid] || (v2 == s_bv[tid] && i2 < s_bi[tid])) { s_bv[tid] = v2; s_bi[tid] = i2; }
-      s_xm[tid] = fmax(s_xm[tid], s_xm[tid + off]);
+      s_d0[tid] = fmax(s_d0[tid], s_d0[tid + off]);
     }
     __syncthreads();
   }
@@ -114,38 +124,112 @@ __global__ __launch_bounds__(256) void k_verify_pass2(VerifyArgs a) {
   const double dd = (double)a.k + 64.0;
   const double gam = dd * ldexp(1.0, -23) / (1.0 - dd * ldexp(1.0, -23));
   const double wmax = ldexp(1.0, (int)a.e_max - 126);
-  const double absb = dd * ldexp(1.0, -126) * (1.0 + s_xm[0] + wmax);
+  const double absb = dd * ldexp(1.0, -126) * (1.0 + s_d0[0] + wmax);
   const double infl = 1.0 + ldexp(1.0, -20);
-  auto bound = [&](float s_hat) -> double {
-    return (gam * ((double)s_hat / (1.0 - gam) + absb) + absb) * infl;
-  };
+  // B(S^) = (g (S^/(1-g) + A) + A) * infl = c1 S^ + c0
+  const double c1 = gam / (1.0 - gam) * infl, c0 = (gam * absb + absb) * infl;
   const uint64_t vstar = s_bi[0] >= 0 && (uint32_t)s_bi[0] < a.n ? (uint32_t)s_bi[0] : 0u;
-  const double lo = (double)zmax - bound(a.sabs[(uint64_t)row * a.n + vstar]);
+  const double lo = (double)zmax - (c1 * (double)a.sabs[(uint64_t)row * a.n + vstar] + c0);
   if (s_bad || !__builtin_isfinite(zmax) || lo != lo) {
     if (tid == 0) { a.argmax[row] = -1; if (a.ncand) a.ncand[row] = 0; }
     return;
   }
   // 3. candidates
   int32_t* cand = a.cand + (uint64_t)row * a.n;
-  for (uint32_t b = tid; b < a.nb; b += 256) {
-    const uint64_t bo = (uint64_t)row * a.nb + b;
-    if ((double)a.rbmax_v[bo] + bound(a.rbmax_s[bo]) < lo) continue;
+#pragma unroll 4
+  for (uint32_t b = tid; b < a.nb; b += kT) {
+    if ((double)rv[b] + (c1 * (double)rs[b] + c0) < lo) continue;
     for (uint32_t rr = 0; rr < 16; ++rr) {
       const uint64_t vo = (uint64_t)row * a.n + 16u * b + rr;
-      if ((double)a.logits[vo] + bound(a.sabs[vo]) >= lo)
+      if ((double)a.logits[vo] + (c1 * (double)a.sabs[vo] + c0) >= lo)
         cand[atomicAdd(&s_cnt, 1u)] = (int32_t)(16u * b + rr);
     }
   }
   __syncthreads();
   const uint32_t ncand = s_cnt;
   if (tid == 0) { s_best_v = -1; if (a.ncand) a.ncand[row] = (int32_t)ncand; }
-  // 4. exact recompute of every candidate
-  for (uint32_t c = 0; c < ncand; ++c) {
+
+  // 4. FP64 screen.  A BF16 product is exact in FP64; summed in any order with the
+  // escape corrections as extra terms (K' = K + 2 * escapes of the row terms), the FP64
+  // logit is within g64 * S64 of the exact one, g64 = (K'+8) 2^-53 / (1 - (K'+8) 2^-53).
+  // Only the candidates whose FP64 intervals reach the best lower bound go on to the
+  // exact integer sum; usually that is one, and it is the answer.
+  const bool screen = ncand <= kScreenMax;
+  if (screen) {
+    for (uint32_t c = 0; c < ncand; ++c) {
+      const uint32_t v = (uint32_t)cand[c];
+      const uint32_t b = v >> 4, r = v & 15u;
+      double z = 0.0, sa = 0.0;
+      uint32_t code;
+#pragma unroll 4
+      for (uint32_t kk = tid; kk < a.k; kk += kT) {
+        const uint32_t wb = decode_w(a.tiles, a.g_cols, v, kk, a.lut, &code);
+        const double p = (double)__uint_as_float((uint32_t)xr[kk] << 16) *
+                         (double)__uint_as_float(wb << 16);
+        z += p;
+        sa += fabs(p);
+      }
+      uint32_t nesc = 0;
+      const uint32_t e0 = a.esc_off[b], e1 = a.esc_off[b + 1];
+      for (uint32_t i = e0 + tid; i < e1; i += kT) {
+        const uint32_t rec = a.esc[i];
+        if ((rec >> 28) != r) continue;
+        const uint32_t kk = (rec >> 8) & 0xFFFFFu;
+        const uint32_t wb = decode_w(a.tiles, a.g_cols, v, kk, a.lut, &code);
+        const uint32_t wt = (wb & 0x807Fu) | ((rec & 0xFFu) << 7);
+        const double xv = (double)__uint_as_float((uint32_t)xr[kk] << 16);
+        const double pw = xv * (double)__uint_as_float(wb << 16);
+        const double pt = xv * (double)__uint_as_float(wt << 16);
+        z += pt - pw;          // two more rounded additions: counted in K'
+        sa += fabs(pt) + fabs(pw);
+        ++nesc;
+      }
+      s_d0[tid] = z;
+      s_d1[tid] = sa;
+      s_u0[tid] = nesc;
+      __syncthreads();
+      for (uint32_t off = kT / 2; off > 0; off >>= 1) {
+        if (tid < off) {
+          s_d0[tid] += s_d0[tid + off];
+          s_d1[tid] += s_d1[tid + off];
+          s_u0[tid] += s_u0[tid + off];
+        }
+        __syncthreads();
+      }
+      if (tid == 0) {
+        const double kk2 = (double)a.k + 2.0 * (double)s_u0[0] + 8.0;
+        const double g64 = kk2 * ldexp(1.0, -53) / (1.0 - kk2 * ldexp(1.0, -53));
+        s_z64[c] = s_d0[0];
+        s_b64[c] = g64 * s_d1[0] / (1.0 - g64) * (1.0 + ldexp(1.0, -20));
+      }
+      __syncthreads();
+    }
+    // survivors: every candidate whose upper bound reaches the largest lower bound
+    if (tid == 0) {
+      double lo64 = -__builtin_inf();
+      for (uint32_t c = 0; c < ncand; ++c) lo64 = fmax(lo64, s_z64[c] - s_b64[c]);
+      uint32_t ns = 0;
+      for (uint32_t c = 0; c < ncand; ++c)
+        if (s_z64[c] + s_b64[c] >= lo64) cand[ns++] = cand[c];
+      s_nsurv = ns;
+    }
+    __syncthreads();
+  } else if (tid == 0) {
+    s_nsurv = ncand;
+  }
+  __syncthreads();
+  const uint32_t nsurv = s_nsurv;
+  if (nsurv == 1u) {
+    if (tid == 0) a.argmax[row] = s_bad ? -1 : cand[0];
+    return;
+  }
+  // 5. exact recompute of the survivors
+  for (uint32_t c = 0; c < nsurv; ++c) {
     const uint32_t v = (uint32_t)cand[c];
     if (tid < kLimbs) limbs[tid] = 0ull;
     __syncthreads();
     uint32_t code;
-    for (uint32_t kk = tid; kk < a.k; kk += 256) {
+    for (uint32_t kk = tid; kk < a.k; kk += kT) {
       const uint32_t wb = decode_w(a.tiles, a.g_cols, v, kk, a.lut, &code);
       int sx_, sw_, ex_, ew_;
       uint32_t mx_, mw_;
@@ -157,7 +241,7 @@ __global__ __launch_bounds__(256) void k_verify_pass2(VerifyArgs a) {
     // escapes of this row: replace the product decoded with the stored code
     const uint32_t b = v >> 4, r = v & 15u;
     const uint32_t e0 = a.esc_off[b], e1 = a.esc_off[b + 1];
-    for (uint32_t i = e0 + tid; i < e1; i += 256) {
+    for (uint32_t i = e0 + tid; i < e1; i += kT) {
       const uint32_t rec = a.esc[i];
       if ((rec >> 28) != r) continue;
       const uint32_t kk = (rec >> 8) & 0xFFFFFu;
@@ -211,7 +295,7 @@ __global__ void k_accept(const int32_t* argmax, const int32_t* draft, uint32_t n
 }
 
 hipError_t launch_verify_pass2(const VerifyArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(k_verify_pass2, dim3(a.m), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(k_verify_pass2, dim3(a.m), dim3(kT), 0, s, a);
   return hipGetLastError();
 }
 
