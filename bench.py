@@ -356,9 +356,11 @@ def main():
     ms_w12 = timed(w12_step, args.steps, args.warmup)
     log("bench: timing BF16 steps ...")
     ms_bf16 = timed(bf16_step, args.steps, args.warmup)
-    # W12 and BF16 kernels share the MAC order: their outputs must agree bit for bit
-    same = all(torch.equal(ys[m][i].view(torch.int16), yb[m][i].view(torch.int16))
-               for m in MS for i in (0, 1))
+    # W12 and BF16 launches that split K the same way add the same products in the same
+    # order, so their outputs agree bit for bit; where the BF16 kernel splits K
+    # differently the last bit can differ
+    same = {f"M{m}_{name}": bool(torch.equal(ys[m][i].view(torch.int16), yb[m][i].view(torch.int16)))
+            for m in MS for i, name in ((0, "gate_up"), (1, "down"))}
 
     # per-(M, matrix) launch durations, each over R launches on rotating copies
     per = {}
@@ -416,7 +418,7 @@ def main():
         "speedup_vs_bf16": round(ms_bf16 / ms_w12, 4),
         "bf16_ms_per_step": round(ms_bf16, 4),
         "bf16_gbps": round(step_bytes_bf16 / (ms_bf16 * 1e-3) / 1e9, 1),
-        "w12_equals_bf16_bitwise": bool(same),
+        "w12_equals_bf16_bitwise": same,
         "per_gemm": per,
         "roofline": roofline,
         "cpu_baseline": None,
