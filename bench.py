@@ -212,6 +212,29 @@ def extra_workloads(torch, w12, wi, np, dev, args):
         stack.h.copy_(h0)
         stack.run()
     ms_step = time_calls(torch, one_step, args.decode_steps, warmup=2)
+    am_eager, h_eager = stack.argmax.clone(), stack.h.clone()
+    # the same step captured once as a HIP graph and replayed (no memset nodes: the
+    # library's calls are kernels only); every replay must give the eager answer
+    ms_graph, graph_ok = None, None
+    if not args.no_graph:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            stack.prepare(stack.draft)            # marshal the calls on the capture stream
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph, stream=side):
+                stack.h.copy_(h0)
+                stack.run()
+        torch.cuda.current_stream().wait_stream(side)
+        graph_ok = True
+        for _ in range(3):
+            graph.replay()
+            torch.cuda.synchronize()
+            graph_ok = graph_ok and bool(torch.equal(stack.argmax, am_eager)) and \
+                bool(torch.equal(stack.h.view(torch.int16), h_eager.view(torch.int16)))
+            torch.zeros(1, device=dev).add_(1)    # eager work between the replays
+        ms_graph = time_calls(torch, graph.replay, args.decode_steps, warmup=2)
+        stack.prepare(stack.draft)                # back to the current stream
     wb, io = stack.weight_bytes(), stack.io_bytes()
     n_params = sum(t.n * t.k for L in layers for t in L.values()) + head.n * head.k
     step = {
@@ -224,7 +247,9 @@ def extra_workloads(torch, w12, wi, np, dev, args):
         "gbps": round((wb + io) / (ms_step * 1e-3) / 1e9, 1),
         "pct_peak": round(100 * (wb + io) / (ms_step * 1e-3) / 1e9 / PEAK_GBPS, 1),
         "bits_per_weight": round(8 * wb / n_params, 5),
-        "timed_steps": args.decode_steps, "setup_s": round(time.time() - t0, 1)}
+        "timed_steps": args.decode_steps, "setup_s": round(time.time() - t0, 1),
+        "ms_per_step_hip_graph": None if ms_graph is None else round(ms_graph, 3),
+        "hip_graph_replays_match_eager": graph_ok}
     log(f"bench: decode step {step['ms_per_step']} ms ({step['gbps']} GB/s)")
     return verify, step
 
@@ -246,6 +271,8 @@ def main():
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the LM-head verification and decode-step workloads")
     ap.add_argument("--decode-steps", type=int, default=20)
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip the HIP-graph replay of the decode step")
     ap.add_argument("--profile-decode", action="store_true",
                     help="build the 64-layer decode stack, run --steps steps and exit (for rocprofv3)")
     ap.add_argument("--profile-verify", action="store_true",
@@ -303,6 +330,9 @@ def main():
         b_gu.append(w_gu.clone())
     while len(b_dn) < n_copies(2 * N_DN * K_DN):
         b_dn.append(w_dn.clone())
+    # second baseline: the same BF16 weights in 4 KB tiles (full-line streaming loads)
+    bt_gu = [w12.bf16_tile(b) for b in b_gu]
+    bt_dn = [w12.bf16_tile(b) for b in b_dn]
     xs = {m: (torch.from_numpy(wi.activations(3, wi.T_X, m, K_GU).view(np.int16)).to(dev),
               torch.from_numpy(wi.activations(3, wi.T_X2, m, K_DN).view(np.int16)).to(dev)) for m in MS}
     ys = {m: (torch.empty((m, N_GU), dtype=torch.bfloat16, device=dev),
@@ -322,6 +352,11 @@ def main():
         for m in MS:
             w12.gemm_bf16(xs[m][0], b_gu[c % len(b_gu)], out=yb[m][0])
             w12.gemm_bf16(xs[m][1], b_dn[c % len(b_dn)], out=yb[m][1])
+
+    def bf16t_step(c):
+        for m in MS:
+            w12.gemm_bf16_tiled(xs[m][0], bt_gu[c % len(bt_gu)], N_GU, K_GU, out=yb[m][0])
+            w12.gemm_bf16_tiled(xs[m][1], bt_dn[c % len(bt_dn)], N_DN, K_DN, out=yb[m][1])
 
     if args.profile_only:
         for i in range(args.steps):
@@ -356,9 +391,13 @@ def main():
     ms_w12 = timed(w12_step, args.steps, args.warmup)
     log("bench: timing BF16 steps ...")
     ms_bf16 = timed(bf16_step, args.steps, args.warmup)
+    log("bench: timing tiled-BF16 steps ...")
+    ms_bf16t = timed(bf16t_step, args.steps, args.warmup)
     # W12 and BF16 launches that split K the same way add the same products in the same
     # order, so their outputs agree bit for bit; where the BF16 kernel splits K
     # differently the last bit can differ
+    bf16_step(0)
+    torch.cuda.synchronize()
     same = {f"M{m}_{name}": bool(torch.equal(ys[m][i].view(torch.int16), yb[m][i].view(torch.int16)))
             for m in MS for i, name in ((0, "gate_up"), (1, "down"))}
 
@@ -366,21 +405,22 @@ def main():
     per = {}
     reps = 40
     for m in MS:
-        for name, tl, bl, xi in (("gate_up", t_gu, b_gu, 0), ("down", t_dn, b_dn, 1)):
+        for name, tl, bl, btl, xi in (("gate_up", t_gu, b_gu, bt_gu, 0),
+                                      ("down", t_dn, b_dn, bt_dn, 1)):
             res = {}
-            for kind in ("w12", "bf16"):
+            nn, kk = tl[0].n, tl[0].k
+            launch = {
+                "w12": lambda i: w12.gemm(xs[m][xi], tl[i % len(tl)], out=ys[m][xi]),
+                "bf16": lambda i: w12.gemm_bf16(xs[m][xi], bl[i % len(bl)], out=yb[m][xi]),
+                "bf16t": lambda i: w12.gemm_bf16_tiled(xs[m][xi], btl[i % len(btl)], nn, kk,
+                                                       out=yb[m][xi])}
+            for kind, fn in launch.items():
                 for i in range(5):
-                    if kind == "w12":
-                        w12.gemm(xs[m][xi], tl[i % len(tl)], out=ys[m][xi])
-                    else:
-                        w12.gemm_bf16(xs[m][xi], bl[i % len(bl)], out=yb[m][xi])
+                    fn(i)
                 e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 e0.record()
                 for i in range(reps):
-                    if kind == "w12":
-                        w12.gemm(xs[m][xi], tl[i % len(tl)], out=ys[m][xi])
-                    else:
-                        w12.gemm_bf16(xs[m][xi], bl[i % len(bl)], out=yb[m][xi])
+                    fn(i)
                 e1.record()
                 torch.cuda.synchronize()
                 res[kind] = e0.elapsed_time(e1) / reps * 1e3     # us per launch
@@ -390,7 +430,10 @@ def main():
                 "gbps_w12": round(nbytes / res["w12"] / 1e3, 1),
                 "pct_peak_w12": round(100 * nbytes / res["w12"] / 1e3 / PEAK_GBPS, 1),
                 "gbps_bf16": round(bf16_bytes(tl[0].n, tl[0].k, m) / res["bf16"] / 1e3, 1),
-                "speedup_vs_bf16": round(res["bf16"] / res["w12"], 3)}
+                "speedup_vs_bf16": round(res["bf16"] / res["w12"], 3),
+                "us_bf16_tiled": round(res["bf16t"], 2),
+                "gbps_bf16_tiled": round(bf16_bytes(tl[0].n, tl[0].k, m) / res["bf16t"] / 1e3, 1),
+                "speedup_vs_bf16_tiled": round(res["bf16t"] / res["w12"], 3)}
     # dominant kernel = the (M, matrix) GEMM with the largest share of the step
     dom_key = max(per, key=lambda kk: per[kk]["us_w12"])
     dom = per[dom_key]
@@ -418,6 +461,9 @@ def main():
         "speedup_vs_bf16": round(ms_bf16 / ms_w12, 4),
         "bf16_ms_per_step": round(ms_bf16, 4),
         "bf16_gbps": round(step_bytes_bf16 / (ms_bf16 * 1e-3) / 1e9, 1),
+        "speedup_vs_bf16_tiled": round(ms_bf16t / ms_w12, 4),
+        "bf16_tiled_ms_per_step": round(ms_bf16t, 4),
+        "bf16_tiled_gbps": round(step_bytes_bf16 / (ms_bf16t * 1e-3) / 1e9, 1),
         "w12_equals_bf16_bitwise": same,
         "per_gemm": per,
         "roofline": roofline,
@@ -426,7 +472,7 @@ def main():
                  "affinity_cores": len(os.sched_getaffinity(0))},
     }
     if not args.no_extras:
-        del t_gu, t_dn, b_gu, b_dn, w_gu, w_dn
+        del t_gu, t_dn, b_gu, b_dn, bt_gu, bt_dn, w_gu, w_dn
         torch.cuda.empty_cache()
         out["lm_head_verify"], out["decode_step"] = extra_workloads(torch, w12, wi, np, dev, args)
     if not args.no_cpu_baseline:

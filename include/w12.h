@@ -159,6 +159,19 @@ w12_status w12_gemm_group(const uint16_t* x, uint32_t m, const w12_desc* const* 
 w12_status w12_gemm_bf16(const uint16_t* x, uint32_t m, const uint16_t* w, uint64_t n,
                          uint64_t k, uint16_t* y, void* ws, size_t ws_bytes, void* stream);
 
+/* The second baseline: BF16 weights in 4 KB tiles, read by the same kernel family with
+ * the same streaming loads as W12 tiles (every wave instruction reads 1 KB of whole
+ * lines).  w12_bf16_tile writes the tiled copy of row-major w [n][k] (device, 16-byte
+ * aligned) into w_tiled (device, n*k*2 bytes, 16-byte aligned): tile (b, g) at
+ * (b*(k/128) + g)*4096, lane slot l (r = l%16, q = l/16) of group j at 1024j + 16l
+ * holding row 16b + r, columns 128g + 32j + 8q .. +7.  w12_gemm_bf16_tiled takes that
+ * copy; workspace as for w12_gemm_bf16 (W12_OP_GEMM_BF16).  Shapes and errors as
+ * w12_gemm_bf16. */
+w12_status w12_bf16_tile(const uint16_t* w, uint64_t n, uint64_t k, void* w_tiled, void* stream);
+w12_status w12_gemm_bf16_tiled(const uint16_t* x, uint32_t m, const void* w_tiled, uint64_t n,
+                               uint64_t k, uint16_t* y, void* ws, size_t ws_bytes,
+                               void* stream);
+
 /* Greedy verification over the LM head (review page, "The mechanisms it found":
  * certified exact-argmax LM head; "StargazerX0/SpecPilot", "Results and
  * verification": committed tokens are the target's own choice).

@@ -374,6 +374,35 @@ w12_status w12_gemm_bf16(const uint16_t* x, uint32_t m, const uint16_t* w, uint6
   return hip_status(launch_gemm(a, SRC_BF16, EPI_BF16, p, (hipStream_t)stream));
 }
 
+w12_status w12_bf16_tile(const uint16_t* w, uint64_t n, uint64_t k, void* w_tiled, void* stream) {
+  if (!w || !w_tiled) return W12_ERR_NULL;
+  if (!shape_ok(n, k)) return W12_ERR_SHAPE;
+  if (!aligned(w, 16) || !aligned(w_tiled, 16)) return W12_ERR_ALIGN;
+  return hip_status(launch_bf16_tile(w, (uint32_t)(n / 16), (uint32_t)(k / 128),
+                                     (uint8_t*)w_tiled, (hipStream_t)stream));
+}
+
+w12_status w12_gemm_bf16_tiled(const uint16_t* x, uint32_t m, const void* w_tiled, uint64_t n,
+                               uint64_t k, uint16_t* y, void* ws, size_t ws_bytes, void* stream) {
+  if (!x || !w_tiled || !y) return W12_ERR_NULL;
+  if (!shape_ok(n, k)) return W12_ERR_SHAPE;
+  if (m < 1 || m > W12_MAX_M) return W12_ERR_RANGE;
+  const size_t need = gemm_ws_bytes(m, n, k, true);
+  if (ws_bytes < need) return W12_ERR_WORKSPACE;
+  if (need > 0 && !ws) return W12_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(w_tiled, 16) || !aligned(y, 4) || !aligned(ws, 256)) return W12_ERR_ALIGN;
+  const GemmPlan p = make_plan(m, n, k, EPI_BF16, true);
+  GemmArgs a;
+  memset(&a, 0, sizeof(a));
+  a.x = x;
+  a.partial = (float*)ws;
+  a.p.seg[0].w = (const uint8_t*)w_tiled;
+  a.p.seg[0].y = y;
+  a.p.seg[0].n = (uint32_t)n;
+  fill_params(a.p, m, k, n, 1);
+  return hip_status(launch_gemm(a, SRC_BF16T, EPI_BF16, p, (hipStream_t)stream));
+}
+
 w12_status w12_lmhead_verify(const uint16_t* x, uint32_t m, const w12_desc* d, const int32_t* draft,
                              uint32_t n_draft, int32_t* argmax_out, int32_t* accepted_out,
                              void* ws, size_t ws_bytes, void* stream) {

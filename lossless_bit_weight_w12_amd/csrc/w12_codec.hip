@@ -372,6 +372,34 @@ __global__ __launch_bounds__(256) void k_rms(const uint16_t* __restrict__ x, uin
   }
 }
 
+// Row-major BF16 -> 4 KB tiles: tile (b, g) at (b * g_cols + g) * 4096, lane slot l
+// (r = l % 16, q = l / 16) of group j at 1024 j + 16 l holding row 16b + r, columns
+// 128g + 32j + 8q .. +7.  One thread per 16-byte unit.
+__global__ __launch_bounds__(256) void k_bf16_tile(const uint16_t* __restrict__ w, uint32_t nb,
+                                                   uint32_t g_cols, uint8_t* __restrict__ out) {
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  const uint64_t units = (uint64_t)nb * g_cols * 256u;
+  const uint64_t k = (uint64_t)g_cols * 128u;
+  for (uint64_t u = (uint64_t)blockIdx.x * 256u + threadIdx.x; u < units;
+       u += (uint64_t)gridDim.x * 256u) {
+    const uint64_t tile = u >> 8;
+    const uint32_t within = (uint32_t)(u & 255u), j = within >> 6, l = within & 63u;
+    const uint64_t b = tile / g_cols, g = tile % g_cols;
+    const uint32_t r = l & 15u, q = l >> 4;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(w + (16u * b + r) * k + 128u * g + 32u * j + 8u * q);
+    *reinterpret_cast<u32x4*>(out + tile * 4096u + 1024u * j + 16u * l) = v;
+  }
+}
+
+hipError_t launch_bf16_tile(const uint16_t* w, uint32_t nb, uint32_t g_cols, uint8_t* out,
+                            hipStream_t s) {
+  const uint64_t units = (uint64_t)nb * g_cols * 256u;
+  uint64_t blocks = (units + 255u) / 256u;
+  if (blocks > 65536u) blocks = 65536u;
+  hipLaunchKernelGGL(k_bf16_tile, dim3((uint32_t)blocks), dim3(256), 0, s, w, nb, g_cols, out);
+  return hipGetLastError();
+}
+
 hipError_t launch_rms_rescale(const uint16_t* x, uint32_t m, uint32_t k, uint16_t* y,
                               hipStream_t s) {
   hipLaunchKernelGGL(k_rms, dim3(m), dim3(256), 0, s, x, k, y);

@@ -45,6 +45,9 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 constexpr uint32_t kAbs2 = 0x7FFF7FFFu;   // clears the sign bits of two packed BF16
 
+// Plain BF16 sources (row-major or tiled): no decode, no escapes.
+constexpr bool plain_bf16(int src) { return src == SRC_BF16 || src == SRC_BF16T; }
+
 constexpr int kXsStride = 128 + 8;   // BF16 per LDS row of one wave's x column (+16 B pad:
                                      // no bank conflicts for the MFMA B reads)
 
@@ -119,7 +122,7 @@ __device__ __forceinline__ uint32_t lut16(uint32_t c, uint32_t t0, uint32_t t1, 
 
 template <int SRC>
 struct TileRegs {
-  u32x4 v[SRC == SRC_BF16 ? 4 : 3];
+  u32x4 v[plain_bf16(SRC) ? 4 : 3];
 };
 
 template <int SRC>
@@ -132,6 +135,13 @@ __device__ __forceinline__ void load_tile(TileRegs<SRC>& t, const uint8_t* __res
     // plain loads: each instruction covers half of every 128-byte line it touches, and
     // the other half is read by the next instruction from L2
     for (int j = 0; j < 4; ++j) t.v[j] = *reinterpret_cast<const u32x4*>(base + 64 * j);
+  } else if constexpr (SRC == SRC_BF16T) {
+    // 4 KB tiles: the lane's 16 bytes of group j at 1024 j + 16 lane, so every wave
+    // instruction reads 1 KB of whole lines (streaming loads, as for W12 tiles)
+    const uint8_t* base = w + ((size_t)b * p.g_cols + g) * 4096u + (uint32_t)lane * 16u;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      t.v[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + 1024 * j));
   } else {
     const uint8_t* base = w + ((size_t)b * p.g_cols + g) * 3072u + (uint32_t)lane * 16u;
 #pragma unroll
@@ -145,7 +155,7 @@ __device__ __forceinline__ void load_tile(TileRegs<SRC>& t, const uint8_t* __res
 template <int SRC>
 __device__ __forceinline__ void unpack_tile(const TileRegs<SRC>& t, const SegView& a,
                                             uint32_t P[16]) {
-  if constexpr (SRC == SRC_BF16) {
+  if constexpr (plain_bf16(SRC)) {
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -369,7 +379,7 @@ __global__ __launch_bounds__(NWV * 64) void k_gemm(
 #pragma unroll
     for (int rb = 0; rb < RBW; ++rb) {
       unpack_tile<SRC>(t[rb], sv[rb], P[rb]);
-      if constexpr (SRC != SRC_BF16) {
+      if constexpr (!plain_bf16(SRC)) {
         if (b0 + rb < p.nb) esc_apply(ec[rb], sv[rb].esc, g, lane, P[rb]);
       }
     }
@@ -410,7 +420,7 @@ __global__ __launch_bounds__(NWV * 64) void k_gemm(
         }
       }
     }
-    if constexpr (SRC != SRC_BF16) {
+    if constexpr (!plain_bf16(SRC)) {
       // refill after the tile's last LDS read: a pending scalar load would otherwise
       // hold up the LDS waits (they share one counter)
       __builtin_amdgcn_sched_barrier(0);
@@ -432,7 +442,7 @@ __global__ __launch_bounds__(NWV * 64) void k_gemm(
     load_tiles(tA, g);
     // escape cursors start after the first tiles are requested: their scalar loads
     // (one or two dependent round trips) overlap the first tile fetch
-    if constexpr (SRC != SRC_BF16) {
+    if constexpr (!plain_bf16(SRC)) {
 #pragma unroll
       for (int rb = 0; rb < RBW; ++rb) esc_begin(ec[rb], sv[rb].esc_off, sv[rb].esc, bl[rb], ga * 128u);
     }
@@ -620,7 +630,7 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_cs(
   auto compute = [&](const TileRegs<SRC>& t, uint32_t g) {
     uint32_t P[16];
     unpack_tile<SRC>(t, sv, P);
-    if constexpr (SRC != SRC_BF16) {
+    if constexpr (!plain_bf16(SRC)) {
       if (bvalid) esc_apply(ec, sv.esc, g, lane, P);
     }
     const uint16_t* xrow = &xs[g & 1u][8 * q];
@@ -638,7 +648,7 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_cs(
                                                             sacc[h], 0, 0, 0);
       }
     }
-    if constexpr (SRC != SRC_BF16) {
+    if constexpr (!plain_bf16(SRC)) {
       __builtin_amdgcn_sched_barrier(0);
       if (ec.stale) esc_refill(ec, sv.esc);
     }
@@ -649,7 +659,7 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_cs(
   uint32_t g = ga;
   xload(g);
   load_tile<SRC>(tA, sv.w, p, bl, g, lane);
-  if constexpr (SRC != SRC_BF16) esc_begin(ec, sv.esc_off, sv.esc, bl, ga * 128u);
+  if constexpr (!plain_bf16(SRC)) esc_begin(ec, sv.esc_off, sv.esc, bl, ga * 128u);
   xstore(g & 1u);
   __syncthreads();
   for (;;) {
@@ -753,7 +763,7 @@ hipError_t launch_gemm_src(const GemmArgs& a, int epi, const GemmPlan& pl, hipSt
 #define W12_EPI(M_, MT_, MF_)                                       \
   do {                                                              \
     if (epi == EPI_BF16) W12_RBW(M_, MT_, MF_, EPI_BF16);          \
-    else if constexpr (SRC != SRC_BF16) W12_RBW(M_, MT_, MF_, EPI_LOGITS); \
+    else if constexpr (!plain_bf16(SRC)) W12_RBW(M_, MT_, MF_, EPI_LOGITS); \
   } while (0)
 #define W12_CS(MT_, EPI_)                                                                     \
   do {                                                                                        \
@@ -767,7 +777,7 @@ hipError_t launch_gemm_src(const GemmArgs& a, int epi, const GemmPlan& pl, hipSt
 #define W12_CS_EPI(MT_)                                                     \
   do {                                                                      \
     if (epi == EPI_BF16) W12_CS(MT_, EPI_BF16);                            \
-    else if constexpr (SRC != SRC_BF16) W12_CS(MT_, EPI_LOGITS);           \
+    else if constexpr (!plain_bf16(SRC)) W12_CS(MT_, EPI_LOGITS);           \
   } while (0)
   if (pl.kind == KIND_COLUMN_SYNC) {
     if (p.m <= 16) W12_CS_EPI(16);

@@ -19,6 +19,7 @@ enum Src : int {
   SRC_RUN = 0,   // W12 tiles, codebook is a run C[j] = C[0] + j (exponent = base + code)
   SRC_LUT = 1,   // W12 tiles, arbitrary ascending codebook (16-entry byte LUT)
   SRC_BF16 = 2,  // plain BF16 rows [n][k]
+  SRC_BF16T = 3, // plain BF16 in 4 KB tiles (the layout of w12_bf16_tile)
 };
 
 // Epilogue of the GEMM kernel family.
@@ -80,10 +81,12 @@ struct GemmPlan {
 hipError_t launch_gemm_run(const GemmArgs& a, int epi, const GemmPlan& p, hipStream_t s);
 hipError_t launch_gemm_lut(const GemmArgs& a, int epi, const GemmPlan& p, hipStream_t s);
 hipError_t launch_gemm_bf16_src(const GemmArgs& a, int epi, const GemmPlan& p, hipStream_t s);
+hipError_t launch_gemm_bf16t_src(const GemmArgs& a, int epi, const GemmPlan& p, hipStream_t s);
 inline hipError_t launch_gemm(const GemmArgs& a, int src, int epi, const GemmPlan& p,
                               hipStream_t s) {
   if (src == SRC_RUN) return launch_gemm_run(a, epi, p, s);
   if (src == SRC_LUT) return launch_gemm_lut(a, epi, p, s);
+  if (src == SRC_BF16T) return launch_gemm_bf16t_src(a, epi, p, s);
   return launch_gemm_bf16_src(a, epi, p, s);
 }
 
@@ -108,6 +111,8 @@ hipError_t launch_encode_pack(const uint16_t* w, uint32_t nb, uint32_t g_cols,
                               const Codebook16& cb, const uint32_t* tile_off,
                               uint8_t* tiles, uint32_t* esc, uint64_t esc_cap,
                               hipStream_t s);
+hipError_t launch_bf16_tile(const uint16_t* w, uint32_t nb, uint32_t g_cols, uint8_t* out,
+                            hipStream_t s);
 hipError_t launch_decode(const uint8_t* tiles, const uint32_t* esc_off, const uint32_t* esc,
                          uint32_t nb, uint32_t g_cols, const Codebook16& cb,
                          uint16_t* w_out, hipStream_t s);

@@ -20,7 +20,8 @@ MAX_GROUP = 4
 STATUS = {0: "W12_OK", -1: "W12_ERR_NULL", -2: "W12_ERR_SHAPE", -3: "W12_ERR_RANGE",
           -4: "W12_ERR_FORMAT", -5: "W12_ERR_WORKSPACE", -6: "W12_ERR_HIP", -7: "W12_ERR_ALIGN"}
 EXPORTS = ("w12_tiles_bytes", "w12_workspace_bytes", "w12_workspace_init", "w12_encode_count",
-           "w12_encode", "w12_decode", "w12_gemm", "w12_gemm_group", "w12_gemm_bf16", "w12_lmhead_verify",
+           "w12_encode", "w12_decode", "w12_gemm", "w12_gemm_group", "w12_gemm_bf16", "w12_bf16_tile",
+           "w12_gemm_bf16_tiled", "w12_lmhead_verify",
            "w12_rms_rescale", "w12_status_str", "w12_version")
 
 
@@ -70,6 +71,11 @@ def lib():
         L.w12_gemm_bf16.restype = c_int32
         L.w12_gemm_bf16.argtypes = [c_void_p, c_uint32, c_void_p, c_uint64, c_uint64, c_void_p,
                                     c_void_p, c_size_t, c_void_p]
+        L.w12_bf16_tile.restype = c_int32
+        L.w12_bf16_tile.argtypes = [c_void_p, c_uint64, c_uint64, c_void_p, c_void_p]
+        L.w12_gemm_bf16_tiled.restype = c_int32
+        L.w12_gemm_bf16_tiled.argtypes = [c_void_p, c_uint32, c_void_p, c_uint64, c_uint64,
+                                          c_void_p, c_void_p, c_size_t, c_void_p]
         L.w12_lmhead_verify.restype = c_int32
         L.w12_lmhead_verify.argtypes = [c_void_p, c_uint32, ctypes.POINTER(W12Desc), c_void_p,
                                         c_uint32, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]
@@ -265,6 +271,31 @@ def gemm_bf16(x, w, out=None):
     ws = workspace(max(workspace_bytes(OP_GEMM_BF16, m, n, k), 256), x.device)
     _check("w12_gemm_bf16", lib().w12_gemm_bf16(_ptr(x), m, _ptr(w), n, k, _ptr(_as_bits(out)),
                                                 _ptr(ws), ws.numel(), _stream(x.device)))
+    return out
+
+
+def bf16_tile(w):
+    """4 KB-tiled copy of BF16 weights w [n, k] (the second baseline's layout)."""
+    torch = _torch()
+    w = _as_bits(w)
+    n, k = w.shape
+    out = torch.empty(n * k * 2, dtype=torch.uint8, device=w.device)
+    _check("w12_bf16_tile", lib().w12_bf16_tile(_ptr(w), n, k, _ptr(out), _stream(w.device)))
+    return out
+
+
+def gemm_bf16_tiled(x, w_tiled, n: int, k: int, out=None):
+    """The same kernel family on 4 KB-tiled BF16 weights (from bf16_tile)."""
+    torch = _torch()
+    x = _as_bits(x)
+    m = x.shape[0]
+    if x.shape[1] != k or w_tiled.numel() * w_tiled.element_size() != 2 * n * k:
+        raise ValueError("gemm_bf16_tiled: x must be [m, k] and w_tiled n*k*2 bytes")
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.bfloat16, device=x.device)
+    ws = workspace(max(workspace_bytes(OP_GEMM_BF16, m, n, k), 256), x.device)
+    _check("w12_gemm_bf16_tiled", lib().w12_gemm_bf16_tiled(
+        _ptr(x), m, _ptr(w_tiled), n, k, _ptr(_as_bits(out)), _ptr(ws), ws.numel(), _stream(x.device)))
     return out
 
 

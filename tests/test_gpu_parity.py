@@ -159,6 +159,32 @@ def test_gemm_bf16_baseline(env, m):
         _gemm_case(env, w, x, "bf16")
 
 
+def tiled_reference(w):
+    """The documented 4 KB tile layout built with numpy: tile (b, g), group j, lane
+    l = 16q + r holds row 16b + r, columns 128g + 32j + 8q .. +7."""
+    n, k = w.shape
+    t = w.reshape(n // 16, 16, k // 128, 4, 4, 8)          # b, r, g, j, q, e
+    t = t.transpose(0, 2, 3, 4, 1, 5)                      # b, g, j, q, r, e
+    return np.ascontiguousarray(t).reshape(-1).view(np.uint8)
+
+
+@pytest.mark.parametrize("m", [1, 2, 4, 8, 16, 24, 32])
+def test_gemm_bf16_tiled_baseline(env, m):
+    torch, w12 = env
+    g = np.random.default_rng(3500 + m)
+    for n, k in SHAPES:
+        say("gemm bf16 tiled", m, n, k)
+        w = wi.gaussian_bf16((n, k), 0.02, g)
+        x = wi.gaussian_bf16((m, k), 1.0, g)
+        wt = w12.bf16_tile(to_dev(w, torch))
+        torch.cuda.synchronize()
+        assert np.array_equal(wt.cpu().numpy(), tiled_reference(w))
+        y = w12.gemm_bf16_tiled(to_dev(x, torch), wt, n, k)
+        torch.cuda.synchronize()
+        z, s = o.gemm_reference(x, w)
+        assert o.gemm_accept(to_host(y), z, s).all()
+
+
 def test_gemm_deterministic_and_overwrites(env):
     torch, w12 = env
     g = np.random.default_rng(4)

@@ -137,6 +137,17 @@ def test_gemm_bf16_validation(L):
     assert f(FAKE, 1, FAKE + 8, 1024, 1024, FAKE, FAKE, 1 << 30, None) == -7
 
 
+def test_bf16_tiled_validation(L):
+    assert L.w12_bf16_tile(None, 1024, 1024, FAKE, None) == -1
+    assert L.w12_bf16_tile(FAKE, 1000, 1024, FAKE, None) == -2
+    assert L.w12_bf16_tile(FAKE, 1024, 1024, FAKE + 8, None) == -7
+    f = L.w12_gemm_bf16_tiled
+    assert f(FAKE, 1, None, 1024, 1024, FAKE, FAKE, 1 << 30, None) == -1
+    assert f(FAKE, 1, FAKE, 1024, 100, FAKE, FAKE, 1 << 30, None) == -2
+    assert f(FAKE, 0, FAKE, 1024, 1024, FAKE, FAKE, 1 << 30, None) == -3
+    assert f(FAKE, 1, FAKE + 4, 1024, 1024, FAKE, FAKE, 1 << 30, None) == -7
+
+
 def test_verify_validation(L):
     f = L.w12_lmhead_verify
     d = desc(n=2048, k=512)
