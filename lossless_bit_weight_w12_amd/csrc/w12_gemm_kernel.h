@@ -317,7 +317,8 @@ __device__ __forceinline__ void x_store(const XStage<MT>& st, uint16_t* xw, int 
   }
 }
 
-// M: rows for the VALU path (compile-time); MT: LDS rows (= M, or 16/32 for MFMA).
+// M: x rows staged (compile-time; the VALU path's rows, or for MFMA 4, 8 or 16 of the
+// MT = 16 columns of the B operand); MT: LDS rows.
 // EPI_BF16 with gridDim.y > 1 writes FP32 partials [split][m][n] (reduced by
 // k_splitk_reduce); with one split it writes y directly.
 template <int M, int MT, bool MF, int RBW, int NWV, int SRC, int EPI>
@@ -364,7 +365,7 @@ __global__ __launch_bounds__(NWV * 64) void k_gemm(
   }
 
   TileRegs<SRC> tA[RBW], tB[RBW];
-  XStage<MT> xr;
+  XStage<M> xr;      // only the M staged rows (MFMA: 4, 8 or 16 of the 16 padded)
 
   uint16_t* xw = xs + wave * MT * kXsStride;   // this wave's x column in LDS
 
@@ -389,7 +390,11 @@ __global__ __launch_bounds__(NWV * 64) void k_gemm(
       if constexpr (MF) {
 #pragma unroll
         for (int h = 0; h < NH; ++h) {
-          const u32x4 xv = *reinterpret_cast<const u32x4*>(xrow + (16 * h + r) * kXsStride + 32 * j);
+          // rows past the M staged ones are padding: their LDS rows are never written
+          // or read, and the B operand gets zeros there
+          const u32x4 xv = (16 * h + r) < M
+              ? *reinterpret_cast<const u32x4*>(xrow + (16 * h + r) * kXsStride + 32 * j)
+              : u32x4{0u, 0u, 0u, 0u};
           const bf16x8_t bv = __builtin_bit_cast(bf16x8_t, xv);
 #pragma unroll
           for (int rb = 0; rb < RBW; ++rb) {
@@ -438,7 +443,7 @@ __global__ __launch_bounds__(NWV * 64) void k_gemm(
   // each compute is a fixed count and never drains the prefetch.
   uint32_t g = ga + (uint32_t)wave;
   if (g < gb) {
-    x_load<MT>(xr, x, p.k, m_rows, g, gb, lane);
+    x_load<M>(xr, x, p.k, m_rows, g, gb, lane);
     load_tiles(tA, g);
     // escape cursors start after the first tiles are requested: their scalar loads
     // (one or two dependent round trips) overlap the first tile fetch
@@ -446,22 +451,22 @@ __global__ __launch_bounds__(NWV * 64) void k_gemm(
 #pragma unroll
       for (int rb = 0; rb < RBW; ++rb) esc_begin(ec[rb], sv[rb].esc_off, sv[rb].esc, bl[rb], ga * 128u);
     }
-    x_store<MT>(xr, xw, lane);
+    x_store<M>(xr, xw, lane);
     __builtin_amdgcn_wave_barrier();
     for (;;) {
-      x_load<MT>(xr, x, p.k, m_rows, g + NWV, gb, lane);
+      x_load<M>(xr, x, p.k, m_rows, g + NWV, gb, lane);
       load_tiles(tB, g + NWV);
       compute(tA, g);
       __builtin_amdgcn_wave_barrier();
-      x_store<MT>(xr, xw, lane);
+      x_store<M>(xr, xw, lane);
       __builtin_amdgcn_wave_barrier();
       g += NWV;
       if (g >= gb) break;
-      x_load<MT>(xr, x, p.k, m_rows, g + NWV, gb, lane);
+      x_load<M>(xr, x, p.k, m_rows, g + NWV, gb, lane);
       load_tiles(tA, g + NWV);
       compute(tB, g);
       __builtin_amdgcn_wave_barrier();
-      x_store<MT>(xr, xw, lane);
+      x_store<M>(xr, xw, lane);
       __builtin_amdgcn_wave_barrier();
       g += NWV;
       if (g >= gb) break;
@@ -783,7 +788,9 @@ hipError_t launch_gemm_src(const GemmArgs& a, int epi, const GemmPlan& pl, hipSt
     if (p.m <= 16) W12_CS_EPI(16);
     else W12_CS_EPI(32);
   } else if (pl.mfma) {
-    W12_EPI(16, 16, true);
+    if (p.m <= 4) W12_EPI(4, 16, true);
+    else if (p.m <= 8) W12_EPI(8, 16, true);
+    else W12_EPI(16, 16, true);
   } else {
 #define W12_VCASE(M_)                                          \
   case M_:                                                     \
