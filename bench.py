@@ -340,6 +340,19 @@ def main():
     yb = {m: (torch.empty((m, N_GU), dtype=torch.bfloat16, device=dev),
               torch.empty((m, N_DN), dtype=torch.bfloat16, device=dev)) for m in MS}
     torch.cuda.synchronize()
+    # encode throughput (one-off work, reported beside the step): the whole of
+    # w12_encode_count (which synchronises to return the codebook) + w12_encode
+    enc_reps = 5
+    torch.cuda.synchronize()
+    t_enc = time.perf_counter()
+    for _ in range(enc_reps):
+        w12.encode(w_gu)
+    torch.cuda.synchronize()
+    enc_s = (time.perf_counter() - t_enc) / enc_reps
+    encode_info = {"matrix": f"gate+up [{N_GU}x{K_GU}] BF16 -> W12", "ms": round(enc_s * 1e3, 3),
+                   "gbps_bf16_read": round(2 * N_GU * K_GU / enc_s / 1e9, 1),
+                   "gweights_per_s": round(N_GU * K_GU / enc_s / 1e9, 2)}
+    log(f"bench: encode {encode_info}")
     log(f"bench: bits/weight gate+up {t_gu[0].bits_per_weight():.5f}, down {t_dn[0].bits_per_weight():.5f}")
     log(f"bench: W12 bytes gate_up {t_gu[0].nbytes()} down {t_dn[0].nbytes()}")
 
@@ -466,6 +479,7 @@ def main():
         "bf16_tiled_gbps": round(step_bytes_bf16 / (ms_bf16t * 1e-3) / 1e9, 1),
         "w12_equals_bf16_bitwise": same,
         "per_gemm": per,
+        "encode": encode_info,
         "roofline": roofline,
         "cpu_baseline": None,
         "host": {"cpu": platform.processor() or platform.machine(),

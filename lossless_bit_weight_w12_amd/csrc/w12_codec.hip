@@ -151,33 +151,58 @@ hipError_t launch_encode_count_tiles(const uint16_t* w, uint32_t nb, uint32_t g_
 }
 
 // ---------------------------------------------------------------- 4. scan over tiles
+// One workgroup walks the counts in chunks of 8192: each chunk is read coalesced into
+// LDS, every thread scans 8 consecutive counts in registers, the 1024 thread sums are
+// scanned with wave shuffles and a 16-entry LDS step, and the running total carries
+// into the next chunk.
+constexpr uint32_t kScanChunk = 8192;
 __global__ __launch_bounds__(1024) void k_scan(const uint32_t* tile_cnt, uint32_t n_tiles,
                                                uint32_t g_cols, uint32_t* tile_off,
                                                uint32_t* esc_off, uint32_t* total) {
-  __shared__ uint32_t part[1024];
-  const uint32_t tid = threadIdx.x;
-  const uint32_t per = (n_tiles + 1023u) / 1024u;
-  const uint32_t lo = min(n_tiles, tid * per), hi = min(n_tiles, lo + per);
-  uint32_t s = 0;
-  for (uint32_t i = lo; i < hi; ++i) s += tile_cnt[i];
-  part[tid] = s;
-  __syncthreads();
-  // Hillis-Steele inclusive scan over 1024 partial sums
-  for (uint32_t off = 1; off < 1024u; off <<= 1) {
-    const uint32_t v = tid >= off ? part[tid - off] : 0u;
+  __shared__ uint32_t buf[kScanChunk];
+  __shared__ uint32_t wsum[16];
+  const uint32_t tid = threadIdx.x, lane = tid & 63u, wave = tid >> 6;
+  uint32_t carry = 0;
+  for (uint32_t base = 0; base < n_tiles; base += kScanChunk) {
+#pragma unroll
+    for (uint32_t j = 0; j < 8; ++j) {
+      const uint32_t i = base + j * 1024u + tid;
+      buf[j * 1024u + tid] = i < n_tiles ? tile_cnt[i] : 0u;
+    }
     __syncthreads();
-    part[tid] += v;
+    uint32_t v[8], run = 0;
+#pragma unroll
+    for (uint32_t e = 0; e < 8; ++e) { v[e] = run; run += buf[8u * tid + e]; }   // exclusive
+    // inclusive scan of the thread sums across the wave
+    uint32_t inc = run;
+#pragma unroll
+    for (uint32_t off = 1; off < 64; off <<= 1) {
+      const uint32_t o = __shfl_up(inc, off);
+      if (lane >= off) inc += o;
+    }
+    if (lane == 63) wsum[wave] = inc;
     __syncthreads();
+    uint32_t before = 0, chunk_total = 0;
+    for (uint32_t w = 0; w < 16; ++w) {
+      const uint32_t t = wsum[w];
+      before += w < wave ? t : 0u;
+      chunk_total += t;
+    }
+    const uint32_t excl = carry + before + inc - run;
+#pragma unroll
+    for (uint32_t e = 0; e < 8; ++e) {
+      const uint32_t i = base + 8u * tid + e;
+      if (i < n_tiles) {
+        tile_off[i] = excl + v[e];
+        if (i % g_cols == 0) esc_off[i / g_cols] = excl + v[e];
+      }
+    }
+    carry += chunk_total;
+    __syncthreads();   // buf and wsum are rewritten by the next chunk
   }
-  uint32_t run = part[tid] - s;   // exclusive prefix of this thread's range
-  for (uint32_t i = lo; i < hi; ++i) {
-    tile_off[i] = run;
-    if (i % g_cols == 0) esc_off[i / g_cols] = run;
-    run += tile_cnt[i];
-  }
-  if (tid == 1023) {
-    esc_off[n_tiles / g_cols] = part[1023];
-    *total = part[1023];
+  if (tid == 0) {
+    esc_off[n_tiles / g_cols] = carry;
+    *total = carry;
   }
 }
 

@@ -120,8 +120,6 @@ def test_config3_mlp_block(env, name):
         yb = w12.gemm_bf16(xt, wd)
         _check_gemm(y, x, w)
         _check_gemm(yb, x, w)
-        # same decoded weights, same MAC order: the two kernels agree bit for bit
-        assert torch.equal(y.view(torch.int16), yb.view(torch.int16))
 
 
 @pytest.fixture(scope="module")
