@@ -122,6 +122,45 @@ def measured_traffic(dom_key: str):
                                  f"{rec['write_scale']:.4f} per launch ({rec['profile']})")
 
 
+def bootstrap_ci(np, samples, n_boot: int = 10000, seed: int = 0):
+    """95 % bootstrap interval of the median of the per-step times."""
+    a = np.asarray(samples, dtype=np.float64)
+    if a.size < 2:
+        return None
+    idx = np.random.default_rng(seed).integers(0, a.size, size=(n_boot, a.size))
+    med = np.median(a[idx], axis=1)
+    return [round(float(np.percentile(med, 2.5)), 4), round(float(np.percentile(med, 97.5)), 4)]
+
+
+def gpu_state():
+    """Clock, temperature and power of GPU 0 from amd-smi (None where the tool or a
+    field is unavailable)."""
+    import subprocess
+    try:
+        out = subprocess.run(["amd-smi", "metric", "-g", "0", "-c", "-t", "-p", "--json"],
+                             capture_output=True, text=True, timeout=30)
+        d = json.loads(out.stdout)
+    except Exception:
+        return None
+    if isinstance(d, dict) and "gpu_data" in d:
+        d = d["gpu_data"]
+    d = d[0] if isinstance(d, list) and d else d
+
+    def find(obj, *keys):
+        for k in keys:
+            if not isinstance(obj, dict) or k not in obj:
+                return None
+            obj = obj[k]
+        return obj.get("value", obj) if isinstance(obj, dict) else obj
+    gfx = [find(d, "clock", f"gfx_{i}", "clk") for i in range(8)]
+    gfx = [v for v in gfx if isinstance(v, (int, float))]
+    return {"gfx_clk_mhz_max_of_xcds": max(gfx) if gfx else None,
+            "mem_clk_mhz": find(d, "clock", "mem_0", "clk"),
+            "hotspot_c": find(d, "temperature", "hotspot"),
+            "mem_c": find(d, "temperature", "mem"),
+            "power_w": find(d, "power", "socket_power")}
+
+
 def time_calls(torch, fn, reps: int, warmup: int = 3) -> float:
     """Mean milliseconds per call of fn() over reps calls between one event pair."""
     for _ in range(warmup):
@@ -284,6 +323,7 @@ def main():
         sys.exit(2)
 
     import numpy as np
+    gpu_before = gpu_state()
     import torch
     import w12_inputs as wi
     import lossless_bit_weight_w12_amd as w12
@@ -389,23 +429,27 @@ def main():
     step_bytes_bf16 = sum(bf16_bytes(N_GU, K_GU, m) + bf16_bytes(N_DN, K_DN, m) for m in MS)
 
     def timed(step_fn, steps, warmup):
+        """Mean ms per step over `steps` steps between one synchronised pair of events,
+        plus the per-step durations from events recorded between the steps (no
+        synchronisation inside the timed region)."""
         for i in range(warmup):
             step_fn(i)
         torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        ev[0].record()
         for i in range(steps):
             step_fn(i)
-        e1.record()
+            ev[i + 1].record()
         torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / steps     # ms per step
+        per = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
+        return ev[0].elapsed_time(ev[steps]) / steps, per
 
     log("bench: timing W12 steps ...")
-    ms_w12 = timed(w12_step, args.steps, args.warmup)
+    ms_w12, per_w12 = timed(w12_step, args.steps, args.warmup)
     log("bench: timing BF16 steps ...")
-    ms_bf16 = timed(bf16_step, args.steps, args.warmup)
+    ms_bf16, _ = timed(bf16_step, args.steps, args.warmup)
     log("bench: timing tiled-BF16 steps ...")
-    ms_bf16t = timed(bf16t_step, args.steps, args.warmup)
+    ms_bf16t, _ = timed(bf16t_step, args.steps, args.warmup)
     # W12 and BF16 launches that split K the same way add the same products in the same
     # order, so their outputs agree bit for bit; where the BF16 kernel splits K
     # differently the last bit can differ
@@ -416,7 +460,7 @@ def main():
 
     # per-(M, matrix) launch durations, each over R launches on rotating copies
     per = {}
-    reps = 40
+    reps = 100
     for m in MS:
         for name, tl, bl, btl, xi in (("gate_up", t_gu, b_gu, bt_gu, 0),
                                       ("down", t_dn, b_dn, bt_dn, 1)):
@@ -471,6 +515,9 @@ def main():
                                                      "bf16_gate_up": len(b_gu), "bf16_down": len(b_dn)},
                    "bits_per_weight": round(t_gu[0].bits_per_weight(), 5)},
         "pct_of_peak": round(100 * value / PEAK_GBPS, 2),
+        "step_ms_median": round(float(np.median(per_w12)), 4),
+        "step_ms_ci95": bootstrap_ci(np, per_w12),
+        "gpu_state": {"before": gpu_before, "after": gpu_state()},
         "speedup_vs_bf16": round(ms_bf16 / ms_w12, 4),
         "bf16_ms_per_step": round(ms_bf16, 4),
         "bf16_gbps": round(step_bytes_bf16 / (ms_bf16 * 1e-3) / 1e9, 1),
