@@ -23,7 +23,8 @@ sys.path.insert(0, ROOT)
 
 import bench  # noqa: E402
 
-ENCODE_KERNELS = ("k_fill_zero", "k_hist", "k_codebook", "k_count_tiles", "k_scan", "k_pack")
+ENCODE_KERNELS = ("k_fill_zero", "k_hist", "k_codebook", "k_count_tiles", "k_scan", "k_pack",
+                  "k_bf16_tile")
 
 
 def read(d: str, counter: str):
