@@ -144,7 +144,7 @@ w12_status w12_gemm(const uint16_t* x, uint32_t m, const w12_desc* d, uint16_t* 
  * ys[i] = x . W_i^T for i < n_w (1..W12_MAX_GROUP), all with the same k, in one launch
  * per codebook kind (row-blocks of the weights numbered consecutively), plus the
  * split-K reduce kernel when K is split.  descs: host array of n_w descriptors; ys:
- * host array of n_w device BF16 outputs [m][n_i].  Same arithmetic, rounding and
+ * host array of n_w device BF16 outputs [m][n_i], each 16-byte aligned.  Same arithmetic, rounding and
  * determinism as w12_gemm (the K split can differ, so the last bit can too).
  * ws: w12_workspace_bytes(W12_OP_GEMM_GROUP, m, sum of n_i, k) bytes.  Errors: as
  * w12_gemm; W12_ERR_RANGE for n_w outside 1..W12_MAX_GROUP, W12_ERR_SHAPE for weights

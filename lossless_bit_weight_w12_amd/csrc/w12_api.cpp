@@ -22,6 +22,7 @@ constexpr uint64_t kMaxN = 1ull << 31;
 #ifndef W12_NS_CAP
 #define W12_NS_CAP 8
 #endif
+static_assert(W12_NS_CAP >= 1 && W12_NS_CAP <= w12::kMaxSplit, "split cap within the reduce kernel's limit");
 #ifndef W12_CS_MIN_COLS
 #define W12_CS_MIN_COLS 4
 #endif
@@ -315,7 +316,7 @@ w12_status w12_gemm(const uint16_t* x, uint32_t m, const w12_desc* d, uint16_t* 
   const size_t need = gemm_ws_bytes(m, d->n, d->k);
   if (ws_bytes < need) return W12_ERR_WORKSPACE;
   if (need > 0 && !ws) return W12_ERR_NULL;
-  if (!aligned(x, 16) || !aligned(y, 4) || !aligned(ws, 256)) return W12_ERR_ALIGN;
+  if (!aligned(x, 16) || !aligned(y, 16) || !aligned(ws, 256)) return W12_ERR_ALIGN;
   return hip_status(launch_w12_group(x, m, &d, &y, 1, ws, (hipStream_t)stream));
 }
 
@@ -330,7 +331,7 @@ w12_status w12_gemm_group(const uint16_t* x, uint32_t m, const w12_desc* const* 
     if (st != W12_OK) return st;
     if (!ys[i]) return W12_ERR_NULL;
     if (descs[i]->k != descs[0]->k) return W12_ERR_SHAPE;
-    if (!aligned(ys[i], 4)) return W12_ERR_ALIGN;
+    if (!aligned(ys[i], 16)) return W12_ERR_ALIGN;
     n_total += descs[i]->n;
   }
   if (n_total >= kMaxN) return W12_ERR_SHAPE;
@@ -361,7 +362,7 @@ w12_status w12_gemm_bf16(const uint16_t* x, uint32_t m, const uint16_t* w, uint6
   const size_t need = gemm_ws_bytes(m, n, k, true);
   if (ws_bytes < need) return W12_ERR_WORKSPACE;
   if (need > 0 && !ws) return W12_ERR_NULL;
-  if (!aligned(x, 16) || !aligned(w, 16) || !aligned(y, 4) || !aligned(ws, 256)) return W12_ERR_ALIGN;
+  if (!aligned(x, 16) || !aligned(w, 16) || !aligned(y, 16) || !aligned(ws, 256)) return W12_ERR_ALIGN;
   const GemmPlan p = make_plan(m, n, k, EPI_BF16, true);
   GemmArgs a;
   memset(&a, 0, sizeof(a));
@@ -390,7 +391,7 @@ w12_status w12_gemm_bf16_tiled(const uint16_t* x, uint32_t m, const void* w_tile
   const size_t need = gemm_ws_bytes(m, n, k, true);
   if (ws_bytes < need) return W12_ERR_WORKSPACE;
   if (need > 0 && !ws) return W12_ERR_NULL;
-  if (!aligned(x, 16) || !aligned(w_tiled, 16) || !aligned(y, 4) || !aligned(ws, 256)) return W12_ERR_ALIGN;
+  if (!aligned(x, 16) || !aligned(w_tiled, 16) || !aligned(y, 16) || !aligned(ws, 256)) return W12_ERR_ALIGN;
   const GemmPlan p = make_plan(m, n, k, EPI_BF16, true);
   GemmArgs a;
   memset(&a, 0, sizeof(a));

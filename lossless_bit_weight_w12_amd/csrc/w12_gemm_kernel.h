@@ -287,8 +287,13 @@ struct XStage {
   u32x4 v[kUnits];
 };
 
-// Every lane issues the same loads on every path (addresses clamped into range,
-// out-of-range units zeroed after the load), so the compiler's wait counts stay exact.
+// Every lane issues the same loads on every path, with the row clamped to m_rows - 1 and
+// the column to the last one of the K-range, so the compiler's wait counts stay exact.
+// The loaded values are used as they are: a clamped row only feeds MFMA output columns
+// m >= m_rows, which are never stored (each output column depends on its own x row
+// only), and a column past the range is never multiplied.  Zeroing them would put a
+// select on the load result next to the load, and the compiler then waits for the load
+// right there, in front of the next prefetch.
 template <int MT>
 __device__ __forceinline__ void x_load(XStage<MT>& st, const uint16_t* __restrict__ x,
                                        uint32_t k, uint32_t m_rows, uint32_t g, uint32_t gb,
@@ -298,10 +303,8 @@ __device__ __forceinline__ void x_load(XStage<MT>& st, const uint16_t* __restric
     const uint32_t u = (uint32_t)lane + 64u * i;
     const uint32_t uu = u < 16u * MT ? u : u % (16u * MT);
     const uint32_t m = uu >> 4, cu = uu & 15u;
-    const bool ok = m < m_rows && g < gb;
     const uint32_t ml = min(m, m_rows - 1u), gl = min(g, gb - 1u);
-    const u32x4 v = *reinterpret_cast<const u32x4*>(x + (size_t)ml * k + 128u * gl + 8u * cu);
-    st.v[i] = ok ? v : u32x4{0u, 0u, 0u, 0u};
+    st.v[i] = *reinterpret_cast<const u32x4*>(x + (size_t)ml * k + 128u * gl + 8u * cu);
   }
 }
 
@@ -437,10 +440,14 @@ __global__ __launch_bounds__(NWV * 64) void k_gemm(
 
   // ---- main loop.  Wave w streams tile columns ga+w, ga+w+4, ... of its row-blocks
   // independently of the other waves (x goes through the wave's own LDS slot, so no
-  // workgroup barrier): column g computes while column g+4's x and tiles are in flight.
-  // Every iteration issues the same loads (past the last column the addresses are
-  // clamped to the last tile column, still in L2, and x is zeroed), so the wait before
-  // each compute is a fixed count and never drains the prefetch.
+  // workgroup barrier).  In source order column g+4's x and tiles are requested before
+  // column g is computed; every iteration issues the same loads (past the last column
+  // the addresses are clamped to the last tile column, still in L2, and the values are
+  // never used).  The compiler is left free to sink part of the next column's loads
+  // below the compute to reuse registers: pinning the full one-column-ahead schedule
+  // with scheduling barriers (and a single-exit loop) measured slower on these shapes
+  // (M1 down -5 %, M16 / M32 gate+up -3 to -4 %), the memory system being saturated by
+  // fewer requests in flight per wave.
   uint32_t g = ga + (uint32_t)wave;
   if (g < gb) {
     x_load<M>(xr, x, p.k, m_rows, g, gb, lane);
@@ -617,16 +624,16 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_cs(
       const uint32_t u = (uint32_t)tid + NT * i;
       const uint32_t uu = u < 16u * MT ? u : u % (16u * MT);
       const uint32_t m = uu >> 4, cu = uu & 15u;
-      const bool ok = m < m_rows && g < gb;
-      const u32x4 v = *reinterpret_cast<const u32x4*>(x + (size_t)min(m, m_rows - 1u) * p.k + 128u * gl + 8u * cu);
-      xr[i] = ok ? v : u32x4{0u, 0u, 0u, 0u};
+      // clamped row / column, used unzeroed (see x_load)
+      xr[i] = *reinterpret_cast<const u32x4*>(x + (size_t)min(m, m_rows - 1u) * p.k + 128u * gl + 8u * cu);
     }
   };
   auto xstore = [&](uint32_t slot) {
 #pragma unroll
     for (int i = 0; i < kUnits; ++i) {
       const uint32_t u = (uint32_t)tid + NT * i;
-      if (u < 16u * MT) {
+      // (a compile-time true test when the units divide evenly: no exec-masked branch)
+      if (kUnits * NT == 16 * MT || u < 16u * MT) {
         const uint32_t m = u >> 4, cu = u & 15u;
         *reinterpret_cast<u32x4*>(&xs[slot][m * kXsStride + 8u * cu]) = xr[i];
       }
@@ -660,7 +667,9 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_cs(
   };
 
   // ---- main loop: every iteration issues the same loads (column g+1 clamped past the
-  // end, x zeroed), so each wait is a fixed count; one barrier per column.
+  // end, values then unused), so each wait is a fixed count; one barrier per column.
+  // As in k_gemm, the compiler's schedule (which may wait for tile g before issuing
+  // tile g+1) measured faster than a pinned deeper prefetch.
   uint32_t g = ga;
   xload(g);
   load_tile<SRC>(tA, sv.w, p, bl, g, lane);
@@ -736,17 +745,28 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_cs(
   }
 }
 
-// Sum of the split-K partials in split order (deterministic), rounded to BF16.
+// Sum of the split-K partials in split order (deterministic), rounded to BF16.  A thread
+// owns four consecutive outputs of one row (n is a multiple of 16, so all four lie in one
+// row-block of one weight) and issues every partial load before the first add.
 static __global__ __launch_bounds__(256) void k_splitk_reduce(const float* __restrict__ partial,
                                                        GemmParams p, uint32_t nsplit) {
-  const uint32_t mn = p.m * p.n;
+  const uint32_t mn = p.m * p.n, n4 = mn >> 2;
   const uint32_t stride = gridDim.x * 256u;
-  for (uint32_t i = blockIdx.x * 256u + threadIdx.x; i < mn; i += stride) {
-    float s = 0.f;
-    for (uint32_t sp = 0; sp < nsplit; ++sp) s += partial[(size_t)sp * mn + i];
-    const uint32_t m = i / p.n, row = i - m * p.n;
+  for (uint32_t i4 = blockIdx.x * 256u + threadIdx.x; i4 < n4; i4 += stride) {
+    f32x4 v[kMaxSplit];
+#pragma unroll
+    for (uint32_t sp = 0; sp < kMaxSplit; ++sp)
+      v[sp] = sp < nsplit ? *reinterpret_cast<const f32x4*>(partial + (size_t)sp * mn + 4u * i4)
+                          : f32x4{0.f, 0.f, 0.f, 0.f};
+    f32x4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (uint32_t sp = 0; sp < kMaxSplit; ++sp)
+      if (sp < nsplit) s += v[sp];
+    const uint32_t i = 4u * i4, m = i / p.n, row = i - m * p.n;
     const SegView sv = seg_view(p, row >> 4);
-    sv.y[(size_t)m * sv.n + row - 16u * sv.rb0] = f32_to_bf16_rne(s);
+    const uint32_t lo = (uint32_t)f32_to_bf16_rne(s[0]) | ((uint32_t)f32_to_bf16_rne(s[1]) << 16);
+    const uint32_t hi = (uint32_t)f32_to_bf16_rne(s[2]) | ((uint32_t)f32_to_bf16_rne(s[3]) << 16);
+    *reinterpret_cast<uint2*>(sv.y + (size_t)m * sv.n + row - 16u * sv.rb0) = make_uint2(lo, hi);
   }
 }
 
@@ -811,8 +831,8 @@ hipError_t launch_gemm_src(const GemmArgs& a, int epi, const GemmPlan& pl, hipSt
 #undef W12_L
   hipError_t e = hipGetLastError();
   if (e == hipSuccess && epi == EPI_BF16 && pl.nsplit > 1) {
-    const uint32_t mn = p.m * p.n;
-    uint32_t blocks = (mn + 255u) / 256u;
+    const uint32_t n4 = p.m * p.n / 4u;
+    uint32_t blocks = (n4 + 255u) / 256u;
     if (blocks > 1024u) blocks = 1024u;
     hipLaunchKernelGGL(k_splitk_reduce, dim3(blocks), dim3(256), 0, s, a.partial, p, pl.nsplit);
     e = hipGetLastError();

@@ -32,6 +32,8 @@ enum Epi : int {
 // share K (a group), their row-blocks numbered consecutively; a single GEMM is a group
 // of one.
 constexpr int kMaxSeg = 4;
+// Most K splits a launch takes (the reduce kernel keeps one partial per split in registers).
+constexpr uint32_t kMaxSplit = 8;
 struct Seg {
   const uint8_t* w;         // W12 tiles, or BF16 rows [n][k]
   const uint32_t* esc_off;  // [n/16 + 1] (W12)

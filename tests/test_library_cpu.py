@@ -99,6 +99,7 @@ def test_gemm_validation(L):
     assert gemm(L, m=16, wsb=0, d=desc(n=64, k=4096)) == -5     # split-K needs partials
     assert gemm(L, x=FAKE + 2) == -7
     assert gemm(L, ws=FAKE + 16) == -7
+    assert gemm(L, y=FAKE + 8) == -7          # y must be 16-byte aligned
     mis = desc()
     mis.tiles = FAKE + 4
     assert gemm(L, d=mis) == -7
@@ -118,6 +119,9 @@ def test_gemm_group_validation(L):
     assert f(FAKE, 33, darr, 3, yarr, FAKE, big, None) == -3
     assert f(FAKE, 1, darr, 3, yarr, FAKE, 0, None) == -5           # split-K needs partials
     assert f(FAKE + 2, 1, darr, 3, yarr, FAKE, big, None) == -7
+    yarr[2] = FAKE + 8
+    assert f(FAKE, 1, darr, 3, yarr, FAKE, big, None) == -7
+    yarr[2] = FAKE
     yarr[1] = None
     assert f(FAKE, 1, darr, 3, yarr, FAKE, big, None) == -1
     yarr[1] = FAKE
@@ -135,6 +139,7 @@ def test_gemm_bf16_validation(L):
     assert f(FAKE, 1, FAKE, 1000, 1024, FAKE, FAKE, 1 << 30, None) == -2
     assert f(FAKE, 40, FAKE, 1024, 1024, FAKE, FAKE, 1 << 30, None) == -3
     assert f(FAKE, 1, FAKE + 8, 1024, 1024, FAKE, FAKE, 1 << 30, None) == -7
+    assert f(FAKE, 1, FAKE, 1024, 1024, FAKE + 8, FAKE, 1 << 30, None) == -7
 
 
 def test_bf16_tiled_validation(L):
