@@ -101,10 +101,11 @@ size_t w12_tiles_bytes(uint64_t n, uint64_t k);
  * n x k weight; 0 for an invalid op or shape, and 0 when the op needs none (DECODE,
  * and GEMM shapes that are not split along K).  GEMM split along K needs FP32
  * partials [splits][m][n]; VERIFY holds, each region starting on a 256-byte boundary
- * in this order: per-row candidate counts (int32 [m]), FP32 logits [m][n], their
- * error scales sum_k |x_k||w_k| (FP32 [m][n]), per-row-block maxima and candidate
- * lists (readable after a call for diagnostics); ENCODE holds the histogram and
- * per-tile escape counts. */
+ * in this order: per-row diagnostic counts (int32 [m][2]: candidate logits, those left
+ * after the FP64 screen), the per-row-block records of the first pass (largest FP32
+ * logit, second largest, largest sum_k |x_k||w_k|, each FP32 [m][n/16]; index of the
+ * largest, int32 [m][n/16]) and the candidate lists (int32 [m][n]); all readable after
+ * a call for diagnostics.  ENCODE holds the histogram and per-tile escape counts. */
 size_t w12_workspace_bytes(int op, uint32_t m, uint64_t n, uint64_t k);
 
 /* Zero-fills `ws` on `stream` with a kernel (no hipMemset); a convenience, no call
@@ -179,15 +180,25 @@ w12_status w12_gemm_bf16_tiled(const uint16_t* x, uint32_t m, const void* w_tile
  * device int32 [n_draft] (n_draft <= m).  Writes argmax_out device int32 [m]: the index
  * v maximising the EXACT logit sum_k x[row,k]*W[v,k], lowest index on exact ties; and
  * accepted_out device int32 [1]: the first i < n_draft with argmax[i] != draft[i], or
- * n_draft.  FP32 logits z^_v and S_v = sum_k |x_k||w_vk| are computed once; with
- * B(S) a bound on |z^ - z| for any summation order, every v whose upper bound
- * z^_v + B(S_v) reaches the lower bound z^* - B(S_*) of the computed maximum is
- * recomputed exactly, so the result does not depend on the reduction order.  A row
- * whose logits are not finite gets argmax -1. */
+ * n_draft.  A first pass streams the head once and keeps, per 16-row block, the two
+ * largest FP32 logits z^ and the largest S = sum_k |x_k||w_vk|; with B(S) a bound on
+ * |z^ - z| for any summation order, every logit whose z^ + B(S) can reach the lower
+ * bound z^* - B(S*) of the computed maximum is recomputed in FP64 from the W12 tiles,
+ * and those that the FP64 intervals cannot separate are summed exactly, so the result
+ * does not depend on the reduction order.  A row whose logits are not finite gets
+ * argmax -1.  ws: w12_workspace_bytes(W12_OP_VERIFY, m, n, k). */
 w12_status w12_lmhead_verify(const uint16_t* x, uint32_t m, const w12_desc* d,
                              const int32_t* draft, uint32_t n_draft, int32_t* argmax_out,
                              int32_t* accepted_out, void* ws, size_t ws_bytes,
                              void* stream);
+
+/* The first pass of w12_lmhead_verify with its full output (for tests of the certified
+ * bound, and as an FP32-output GEMM): logits_out = FP32 z^ [m][n] and sabs_out = FP32
+ * sum_k |x_k||w_vk| [m][n] (device, 16-byte aligned), from the same kernels in the same
+ * summation order as the verification; ws as for W12_OP_VERIFY (its block maxima are
+ * overwritten).  Errors as w12_lmhead_verify. */
+w12_status w12_logits_f32(const uint16_t* x, uint32_t m, const w12_desc* d, float* logits_out,
+                          float* sabs_out, void* ws, size_t ws_bytes, void* stream);
 
 /* Harness op for the layer chain: y[row] = bf16(x[row] / sqrt(mean(x[row]^2))) in FP32,
  * x, y device BF16 [m][k] (16-byte aligned, k % 8 == 0, 0 < k < 2^20, m <= 2^20;

@@ -124,24 +124,34 @@ size_t group_ws_bytes(uint32_t m, uint64_t n_total, uint64_t k) {
   return cap > 1 ? align256((size_t)cap * m * n_total * 4) : 0;
 }
 
-// Verify workspace: per-row candidate counts first (a fixed place for diagnostics),
-// then FP32 logits and S = sum |x||w| per logit, per-row-block maxima, candidate lists.
+// Verify workspace: per-row diagnostic counts first (a fixed place), then the
+// per-row-block records of pass 1 and the candidate lists of pass 2.
 struct VerifyLayout {
-  size_t ncand, logits, sabs, rbmax_v, rbmax_s, rbmax_i, cand, total;
+  size_t ncand, bm_v, bm_v2, bm_s, bm_i, cand, total;
 };
 
 VerifyLayout verify_layout(uint32_t m, uint64_t n) {
   VerifyLayout L;
   const uint64_t nb = n / 16;
   L.ncand = 0;
-  L.logits = L.ncand + align256((size_t)m * 4);
-  L.sabs = L.logits + align256((size_t)m * n * 4);
-  L.rbmax_v = L.sabs + align256((size_t)m * n * 4);
-  L.rbmax_s = L.rbmax_v + align256((size_t)m * nb * 4);
-  L.rbmax_i = L.rbmax_s + align256((size_t)m * nb * 4);
-  L.cand = L.rbmax_i + align256((size_t)m * nb * 4);
+  L.bm_v = L.ncand + align256((size_t)m * 8);
+  L.bm_v2 = L.bm_v + align256((size_t)m * nb * 4);
+  L.bm_s = L.bm_v2 + align256((size_t)m * nb * 4);
+  L.bm_i = L.bm_s + align256((size_t)m * nb * 4);
+  L.cand = L.bm_i + align256((size_t)m * nb * 4);
   L.total = L.cand + align256((size_t)m * n * 4);
   return L;
+}
+
+BlockMax block_max(uint8_t* base, const VerifyLayout& L) {
+  BlockMax bm;
+  bm.v = (float*)(base + L.bm_v);
+  bm.v2 = (float*)(base + L.bm_v2);
+  bm.s = (float*)(base + L.bm_s);
+  bm.i = (int32_t*)(base + L.bm_i);
+  bm.accepted = nullptr;
+  bm.n_draft = 0;
+  return bm;
 }
 
 struct EncodeLayout {
@@ -424,11 +434,11 @@ w12_status w12_lmhead_verify(const uint16_t* x, uint32_t m, const w12_desc* d, c
   a.x = x;
   a.p.seg[0] = w12_seg(d, nullptr, 0);
   fill_params(a.p, m, d->k, d->n, 1);
-  a.logits = (float*)(base + L.logits);
-  a.sabs = (float*)(base + L.sabs);
-  a.rbmax_v = (float*)(base + L.rbmax_v);
-  a.rbmax_s = (float*)(base + L.rbmax_s);
-  a.rbmax_i = (int32_t*)(base + L.rbmax_i);
+  a.logits = nullptr;          // pass 2 works from the block records and the tiles
+  a.sabs = nullptr;
+  a.bm = block_max(base, L);
+  a.bm.accepted = accepted_out;   // pass 1 sets it to n_draft, pass 2 lowers it
+  a.bm.n_draft = n_draft;
   const int src = codebook_is_run(d->codebook) ? SRC_RUN : SRC_LUT;
   hipError_t e = launch_gemm(a, src, EPI_LOGITS, p, s);
   VerifyArgs v;
@@ -437,11 +447,10 @@ w12_status w12_lmhead_verify(const uint16_t* x, uint32_t m, const w12_desc* d, c
   v.tiles = (const uint8_t*)d->tiles;
   v.esc_off = d->esc_off;
   v.esc = d->esc;
-  v.logits = a.logits;
-  v.sabs = a.sabs;
-  v.rbmax_v = a.rbmax_v;
-  v.rbmax_s = a.rbmax_s;
-  v.rbmax_i = a.rbmax_i;
+  v.rbmax_v = a.bm.v;
+  v.rbmax_v2 = a.bm.v2;
+  v.rbmax_s = a.bm.s;
+  v.rbmax_i = a.bm.i;
   v.cand = (int32_t*)(base + L.cand);
   v.ncand = (int32_t*)(base + L.ncand);
   v.argmax = argmax_out;
@@ -456,8 +465,31 @@ w12_status w12_lmhead_verify(const uint16_t* x, uint32_t m, const w12_desc* d, c
   v.e_max = d->e_max;
   for (int i = 0; i < 4; ++i) v.lut[i] = a.p.seg[0].lut[i];
   if (e == hipSuccess) e = launch_verify_pass2(v, s);
-  if (e == hipSuccess) e = launch_accept(v, s);
   return hip_status(e);
+}
+
+w12_status w12_logits_f32(const uint16_t* x, uint32_t m, const w12_desc* d, float* logits_out,
+                          float* sabs_out, void* ws, size_t ws_bytes, void* stream) {
+  if (!x || !logits_out || !sabs_out || !ws) return W12_ERR_NULL;
+  w12_status st = check_desc(d, true);
+  if (st != W12_OK) return st;
+  if (m < 1 || m > W12_MAX_M) return W12_ERR_RANGE;
+  const VerifyLayout L = verify_layout(m, d->n);
+  if (ws_bytes < L.total) return W12_ERR_WORKSPACE;
+  if (!aligned(x, 16) || !aligned(ws, 256) || !aligned(logits_out, 16) || !aligned(sabs_out, 16))
+    return W12_ERR_ALIGN;
+  uint8_t* base = (uint8_t*)ws;
+  GemmPlan p = make_plan(m, d->n, d->k, EPI_LOGITS);
+  GemmArgs a;
+  memset(&a, 0, sizeof(a));
+  a.x = x;
+  a.p.seg[0] = w12_seg(d, nullptr, 0);
+  fill_params(a.p, m, d->k, d->n, 1);
+  a.logits = logits_out;
+  a.sabs = sabs_out;
+  a.bm = block_max(base, L);
+  const int src = codebook_is_run(d->codebook) ? SRC_RUN : SRC_LUT;
+  return hip_status(launch_gemm(a, src, EPI_LOGITS, p, (hipStream_t)stream));
 }
 
 w12_status w12_rms_rescale(const uint16_t* x, uint32_t m, uint64_t k, uint16_t* y, void* stream) {

@@ -327,7 +327,7 @@ __device__ __forceinline__ void x_store(const XStage<MT>& st, uint16_t* xw, int 
 template <int M, int MT, bool MF, int RBW, int NWV, int SRC, int EPI>
 __global__ __launch_bounds__(NWV * 64) void k_gemm(
     const uint16_t* __restrict__ x, float* __restrict__ out_f32, float* __restrict__ out_s,
-    float* __restrict__ rbmax_v, float* __restrict__ rbmax_s, int32_t* __restrict__ rbmax_i,
+    BlockMax bm,
     GemmParams p) {
   constexpr int NH = MF ? MT / 16 : 1;
   // the logits epilogue also accumulates S = sum_k |x_k||w_k| per output (the scale of
@@ -534,28 +534,33 @@ __global__ __launch_bounds__(NWV * 64) void k_gemm(
       const float v = final_value(red, o), sv = final_value(red + kRed, o);
       fin[o] = v;
       fin_s[o] = sv;
-      if (b < p.nb && (uint32_t)m < m_rows) {
+      if (out_f32 && b < p.nb && (uint32_t)m < m_rows) {   // full logits only when asked for
         out_f32[(size_t)m * p.n + 16u * b + rr] = v;
         out_s[(size_t)m * p.n + 16u * b + rr] = sv;
       }
     }
     __syncthreads();
+    if (bm.accepted && blockIdx.x == 0 && blockIdx.y == 0 && tid == 0)
+      *bm.accepted = (int32_t)bm.n_draft;   // verification pass 2 lowers it
     for (int o = tid; o < RBW * MT; o += (NWV * 64)) {
       const int rb = o / MT, m = o % MT;
       const uint32_t b = b0 + rb;
       if (b >= p.nb || (uint32_t)m >= m_rows) continue;
-      float best = fin[o * 16], smax = fin_s[o * 16];
+      // largest (lowest row on ties) and second largest logit of the block
+      float best = fin[o * 16], second = -__builtin_inff(), smax = fin_s[o * 16];
       int bi = 0;
       bool finite = __builtin_isfinite(best);
       for (int rr = 1; rr < 16; ++rr) {
         const float v = fin[o * 16 + rr];
         finite = finite && __builtin_isfinite(v);
-        if (v > best) { best = v; bi = rr; }
+        if (v > best) { second = best; best = v; bi = rr; }
+        else if (v > second) second = v;
         smax = fmaxf(smax, fin_s[o * 16 + rr]);
       }
-      rbmax_v[(size_t)m * p.nb + b] = finite ? best : __builtin_nanf("");
-      rbmax_s[(size_t)m * p.nb + b] = smax;
-      rbmax_i[(size_t)m * p.nb + b] = (int32_t)(16u * b + bi);
+      bm.v[(size_t)m * p.nb + b] = finite ? best : __builtin_nanf("");
+      bm.v2[(size_t)m * p.nb + b] = finite ? second : __builtin_nanf("");
+      bm.s[(size_t)m * p.nb + b] = smax;
+      bm.i[(size_t)m * p.nb + b] = (int32_t)(16u * b + bi);
     }
   } else {
     const bool direct = gridDim.y == 1;
@@ -589,7 +594,7 @@ __global__ __launch_bounds__(NWV * 64) void k_gemm(
 template <int MT, int NW, int SRC, int EPI>
 __global__ __launch_bounds__(NW * 64) void k_gemm_cs(
     const uint16_t* __restrict__ x, float* __restrict__ out_f32, float* __restrict__ out_s,
-    float* __restrict__ rbmax_v, float* __restrict__ rbmax_s, int32_t* __restrict__ rbmax_i,
+    BlockMax bm,
     GemmParams p) {
   constexpr int NH = MT / 16;
   constexpr bool kS = EPI == EPI_LOGITS;   // also accumulate S = sum |x||w| per output
@@ -694,37 +699,53 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_cs(
   const uint32_t n0 = 16u * b + 4u * (uint32_t)q;       // launch numbering (logits, partials)
   const uint32_t n0l = 16u * bl + 4u * (uint32_t)q;     // inside the weight (y)
   if constexpr (EPI == EPI_LOGITS) {
+    if (bm.accepted && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0)
+      *bm.accepted = (int32_t)bm.n_draft;   // verification pass 2 lowers it
     if (!bvalid) return;
 #pragma unroll
     for (int h = 0; h < NH; ++h) {
       const uint32_t m = 16u * h + (uint32_t)r;
-      // best of this lane's 4 rows, lowest row on ties; non-finite poisons the block
-      float best = acc[h][0], smax = sacc[h][0];
+      // largest (lowest row on ties) and second largest of this lane's 4 rows;
+      // non-finite poisons the block
+      float best = acc[h][0], second = -__builtin_inff(), smax = sacc[h][0];
       int bi = 0;
       bool finite = __builtin_isfinite(acc[h][0]);
 #pragma unroll
       for (int i = 1; i < 4; ++i) {
         finite = finite && __builtin_isfinite(acc[h][i]);
-        if (acc[h][i] > best) { best = acc[h][i]; bi = i; }
+        if (acc[h][i] > best) { second = best; best = acc[h][i]; bi = i; }
+        else if (acc[h][i] > second) second = acc[h][i];
         smax = fmaxf(smax, sacc[h][i]);
       }
       int row = 4 * q + bi;
+      // merge with the lanes holding the block's other rows: the better first wins,
+      // the second is the larger of its own second and the other's first
 #pragma unroll
       for (int off = 16; off <= 32; off <<= 1) {
         const float ob = __shfl_xor(best, off);
+        const float o2 = __shfl_xor(second, off);
         const int orow = __shfl_xor(row, off);
         const int ofin = __shfl_xor((int)finite, off);
         smax = fmaxf(smax, __shfl_xor(smax, off));
         finite = finite && ofin;
-        if (ob > best || (ob == best && orow < row)) { best = ob; row = orow; }
+        if (ob > best || (ob == best && orow < row)) {
+          second = fmaxf(o2, best);
+          best = ob;
+          row = orow;
+        } else {
+          second = fmaxf(second, ob);
+        }
       }
       if (m < m_rows) {
-        *reinterpret_cast<f32x4*>(out_f32 + (size_t)m * p.n + n0) = acc[h];
-        *reinterpret_cast<f32x4*>(out_s + (size_t)m * p.n + n0) = sacc[h];
+        if (out_f32) {   // full logits and S only when asked for (verification needs the maxima)
+          *reinterpret_cast<f32x4*>(out_f32 + (size_t)m * p.n + n0) = acc[h];
+          *reinterpret_cast<f32x4*>(out_s + (size_t)m * p.n + n0) = sacc[h];
+        }
         if (q == 0) {
-          rbmax_v[(size_t)m * p.nb + b] = finite ? best : __builtin_nanf("");
-          rbmax_s[(size_t)m * p.nb + b] = smax;
-          rbmax_i[(size_t)m * p.nb + b] = (int32_t)(16u * b + row);
+          bm.v[(size_t)m * p.nb + b] = finite ? best : __builtin_nanf("");
+          bm.v2[(size_t)m * p.nb + b] = finite ? second : __builtin_nanf("");
+          bm.s[(size_t)m * p.nb + b] = smax;
+          bm.i[(size_t)m * p.nb + b] = (int32_t)(16u * b + row);
         }
       }
     }
@@ -779,7 +800,7 @@ hipError_t launch_gemm_src(const GemmArgs& a, int epi, const GemmPlan& pl, hipSt
   float* f32 = epi == EPI_LOGITS ? a.logits : a.partial;
 #define W12_L(M_, MT_, MF_, RBW_, NWV_, EPI_)                                                     \
   hipLaunchKernelGGL((k_gemm<M_, MT_, MF_, RBW_, NWV_, SRC, EPI_>), grid, dim3(NWV_ * 64), 0, s, \
-                     a.x, f32, a.sabs, a.rbmax_v, a.rbmax_s, a.rbmax_i, p)
+                     a.x, f32, a.sabs, a.bm, p)
 #define W12_RBW(M_, MT_, MF_, EPI_)                   \
   do {                                                \
     if (pl.rbw == 2) W12_L(M_, MT_, MF_, 2, 4, EPI_); \
@@ -794,10 +815,10 @@ hipError_t launch_gemm_src(const GemmArgs& a, int epi, const GemmPlan& pl, hipSt
   do {                                                                                        \
     if (pl.nw == 8)                                                                           \
       hipLaunchKernelGGL((k_gemm_cs<MT_, 8, SRC, EPI_>), grid, dim3(512), 0, s, a.x, f32,     \
-                         a.sabs, a.rbmax_v, a.rbmax_s, a.rbmax_i, p);                         \
+                         a.sabs, a.bm, p);                         \
     else                                                                                      \
       hipLaunchKernelGGL((k_gemm_cs<MT_, 4, SRC, EPI_>), grid, dim3(256), 0, s, a.x, f32,     \
-                         a.sabs, a.rbmax_v, a.rbmax_s, a.rbmax_i, p);                         \
+                         a.sabs, a.bm, p);                         \
   } while (0)
 #define W12_CS_EPI(MT_)                                                     \
   do {                                                                      \

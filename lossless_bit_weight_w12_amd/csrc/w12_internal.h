@@ -25,7 +25,7 @@ enum Src : int {
 // Epilogue of the GEMM kernel family.
 enum Epi : int {
   EPI_BF16 = 0,    // y = bf16(x . W^T)
-  EPI_LOGITS = 1,  // fp32 logits [m][n] + per-row-block maxima (verification pass 1)
+  EPI_LOGITS = 1,  // per-row-block maxima (+ fp32 logits [m][n] when asked for): verification pass 1
 };
 
 // One weight of a launch.  A launch multiplies one x by up to kMaxSeg weights that
@@ -53,13 +53,21 @@ struct GemmParams {
   Seg seg[kMaxSeg];
 };
 
+// Per-row-block records of the logits epilogue (verification pass 1), [m][nb] each.
+struct BlockMax {
+  float* v;                 // largest logit of the row-block (NaN if any is not finite)
+  float* v2;                // second largest (equal to v on a tie)
+  float* s;                 // largest sum_k |x_k||w_k| of the row-block
+  int32_t* i;               // index of v, lowest on ties
+  int32_t* accepted;        // set to n_draft by the first workgroup (NULL: untouched)
+  uint32_t n_draft;
+};
+
 struct GemmArgs {
   const uint16_t* x;        // [m][k] BF16
-  float* logits;            // [m][n] (EPI_LOGITS)
-  float* sabs;              // [m][n] sum_k |x_k||w_k| per logit (EPI_LOGITS)
-  float* rbmax_v;           // [m][nb] largest logit of each row-block (EPI_LOGITS)
-  float* rbmax_s;           // [m][nb] largest sabs of each row-block (EPI_LOGITS)
-  int32_t* rbmax_i;         // [m][nb] index of rbmax_v, lowest on ties (EPI_LOGITS)
+  float* logits;            // [m][n] (EPI_LOGITS; NULL: not written)
+  float* sabs;              // [m][n] sum_k |x_k||w_k| per logit (with logits)
+  BlockMax bm;              // EPI_LOGITS
   float* partial;           // [nsplit][m][n] split-K partial sums (launch numbering)
   GemmParams p;
 };
@@ -125,14 +133,14 @@ struct VerifyArgs {
   const uint8_t* tiles;
   const uint32_t* esc_off;
   const uint32_t* esc;
-  const float* logits;      // [m][n]
-  const float* sabs;        // [m][n]
   const float* rbmax_v;     // [m][nb]
+  const float* rbmax_v2;    // [m][nb]
   const float* rbmax_s;     // [m][nb]
   const int32_t* rbmax_i;   // [m][nb]
-  int32_t* cand;            // [m][n] candidate lists
+  int32_t* cand;            // [m][n] candidate logits
   int32_t* argmax;          // [m]
-  int32_t* ncand;           // [m] candidates recomputed exactly (diagnostic; may be NULL)
+  int32_t* ncand;           // [m][2]: candidate logits, those left after the FP64 screen
+                            // (diagnostic; may be NULL)
   const int32_t* draft;
   int32_t* accepted;
   uint32_t m, n, k, g_cols, nb, n_draft;
@@ -140,7 +148,6 @@ struct VerifyArgs {
   uint32_t lut[4];
 };
 hipError_t launch_verify_pass2(const VerifyArgs& a, hipStream_t s);
-hipError_t launch_accept(const VerifyArgs& a, hipStream_t s);
 
 hipError_t launch_rms_rescale(const uint16_t* x, uint32_t m, uint32_t k, uint16_t* y,
                               hipStream_t s);

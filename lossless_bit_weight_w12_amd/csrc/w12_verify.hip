@@ -1,10 +1,12 @@
 // Greedy verification epilogue: certified exact argmax over the LM-head logits and
 // the accepted-prefix length.
 //
-// Pass 1 (the GEMM kernel family with the logits epilogue) leaves FP32 logits z^[m][v],
-// S^[m][v] = the same kernel's FP32 sum of |x_k||w_vk|, and per 16-row block the
-// largest z^ (with its index) and the largest S^.  Pass 2 (one workgroup per row):
-//   1. z* = max z^ over the block maxima (lowest index on ties), S* its S^;
+// Pass 1 (the GEMM kernel family with the logits epilogue) leaves, per row and per
+// 16-row block of the head, the largest FP32 logit z^ (with its index), the second
+// largest, and the largest S^ = the same kernel's FP32 sum of |x_k||w_vk| over the
+// block's rows.  Pass 2 (one workgroup per row):
+//   1. z* = max z^ over the block maxima (lowest index on ties), S* the largest S^ of
+//      its block (an upper bound of its own S^);
 //   2. the error bound.  A product of two BF16 values is exact in FP32 unless it
 //      underflows.  Whatever the summation order, each of the K products of a logit
 //      passes through at most D = K + 64 additions (the slack covers the accumulators'
@@ -14,25 +16,33 @@
 //      A = D 2^-126 (1 + Xmax + Wmax) covering flushed denormal inputs, products and
 //      partial sums (Xmax = max |x_k|, Wmax = 2^(e_max-126) > |w|).  S^ sums the same
 //      nonnegative terms, so S <= S^/(1-g) + A, and B(S^) = g (S^/(1-g) + A) + A,
-//      inflated by 2^-20 for its FP64 evaluation, bounds |z^ - z|;
-//   3. L = z* - B(S*) is below the true maximum, so every v with z^_v + B(S^_v) >= L is
-//      a candidate (the exact argmax always is); whole blocks are skipped when their
-//      largest z^ plus B(largest S^) falls below L;
-//   4. each candidate's logit is recomputed exactly: sum_k x_k w_vk as an integer in
-//      units of 2^-266 (a BF16 product is +-Mx*Mw*2^(Ex+Ew) with 8-bit significands),
-//      accumulated in 64-bit LDS limbs; the largest exact value wins, lowest index on
-//      an exact tie.
+//      inflated by 2^-20 for its FP64 evaluation, bounds |z^ - z|; B grows with S^;
+//   3. L = z* - B(S*) is below the true maximum, so every v with z^_v + B(S^_v) >= L
+//      is a candidate (the exact argmax always is).  With the block's largest S^ in B,
+//      a block adds its largest logit when that reaches L, and all of its rows when its
+//      second largest does too (otherwise no other row of it can);
+//   4. FP64 screen: each candidate's logit is recomputed from the W12 tiles in FP64 (a
+//      BF16 product is exact in FP64; escape corrections add two terms each), within
+//      g64 S64 of the exact value; only the candidates whose FP64 upper bound reaches
+//      the largest FP64 lower bound survive;
+//   5. when more than one survives, each survivor's logit is recomputed exactly:
+//      sum_k x_k w_vk as an integer in units of 2^-266 (a BF16 product is
+//      +-Mx*Mw*2^(Ex+Ew) with 8-bit significands), accumulated in 64-bit LDS limbs; the
+//      largest exact value wins, lowest index on an exact tie.
 // The review page ("The mechanisms it found") names a certified exact-argmax LM head,
 // and its caveats note that reduction order can flip near-ties: the exact logit makes
 // the answer independent of the order.  Accept: first i < n_draft with
 // argmax[i] != draft[i], else n_draft ("StargazerX0/SpecPilot", "Results and
-// verification": every committed token is the target's own choice).
+// verification": every committed token is the target's own choice): pass 1 sets it to
+// n_draft and every row i < n_draft whose argmax differs from the draft lowers it to i
+// with an atomic minimum.
 #include "w12_internal.h"
 
 namespace w12 {
 
 constexpr int kLimbs = 18;   // 18 x 32 bits > 542 bits (largest |sum| for K < 2^20)
 constexpr uint32_t kScreenMax = 512;   // candidates screened in FP64 (more: all go exact)
+constexpr uint32_t kGroup = 4;         // candidates screened at once, kT / kGroup threads each
 
 __device__ __forceinline__ bool exact_parts(uint32_t bits, int& sgn, uint32_t& mant, int& ex) {
   const uint32_t e = (bits >> 7) & 0xFFu, m = bits & 0x7Fu;
@@ -71,6 +81,8 @@ __device__ __forceinline__ void limb_add(unsigned long long* limbs, int sgn, uin
 constexpr uint32_t kT = 512;   // threads of the pass-2 workgroup (one workgroup per row)
 
 __global__ __launch_bounds__(kT) void k_verify_pass2(VerifyArgs a) {
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  constexpr uint32_t kPer = kT / kGroup;   // threads per screened candidate (two waves)
   __shared__ float s_bv[kT];
   __shared__ int32_t s_bi[kT];
   __shared__ double s_d0[kT], s_d1[kT];
@@ -80,17 +92,21 @@ __global__ __launch_bounds__(kT) void k_verify_pass2(VerifyArgs a) {
   __shared__ int32_t s_best_v, s_best_sign;
   __shared__ uint32_t s_cnt, s_bad, s_nsurv;
   __shared__ double s_z64[kScreenMax], s_b64[kScreenMax];
-  const uint32_t row = blockIdx.x, tid = threadIdx.x;
+  const uint32_t row = blockIdx.x, tid = threadIdx.x, lane = tid & 63u, wave = tid >> 6;
   const uint16_t* xr = a.x + (uint64_t)row * a.k;
   const float* rv = a.rbmax_v + (uint64_t)row * a.nb;
+  const float* rv2 = a.rbmax_v2 + (uint64_t)row * a.nb;
   const float* rs = a.rbmax_s + (uint64_t)row * a.nb;
   const int32_t* ri = a.rbmax_i + (uint64_t)row * a.nb;
+  int32_t* cand = a.cand + (uint64_t)row * a.n;
+  int32_t result = -1;
+  uint32_t ncand = 0, nsurv = 0;
 
   // 1. z* and its index over the block maxima (NaN marks a non-finite block)
   float bv = -__builtin_inff();
   int32_t bi = 0x7FFFFFFF;
   bool bad = false;
-#pragma unroll 4
+#pragma unroll 8
   for (uint32_t b = tid; b < a.nb; b += kT) {
     const float v = rv[b];
     const int32_t i = ri[b];
@@ -99,7 +115,7 @@ __global__ __launch_bounds__(kT) void k_verify_pass2(VerifyArgs a) {
   }
   // 2. Xmax (and finiteness of x)
   double xm = 0.0;
-#pragma unroll 4
+#pragma unroll 8
   for (uint32_t i = tid; i < a.k; i += kT) {
     const uint32_t bits = xr[i];
     if (((bits >> 7) & 0xFFu) == 0xFFu) bad = true;
@@ -108,7 +124,7 @@ __global__ __launch_bounds__(kT) void k_verify_pass2(VerifyArgs a) {
   s_bv[tid] = bv;
   s_bi[tid] = bi;
   s_d0[tid] = xm;
-  if (tid == 0) { s_cnt = 0; s_bad = 0; }
+  if (tid == 0) { s_cnt = 0; s_bad = 0; s_best_v = -1; }
   __syncthreads();
   if (bad) atomicOr(&s_bad, 1u);
   for (uint32_t off = kT / 2; off > 0; off >>= 1) {
@@ -128,179 +144,195 @@ __global__ __launch_bounds__(kT) void k_verify_pass2(VerifyArgs a) {
   const double infl = 1.0 + ldexp(1.0, -20);
   // B(S^) = (g (S^/(1-g) + A) + A) * infl = c1 S^ + c0
   const double c1 = gam / (1.0 - gam) * infl, c0 = (gam * absb + absb) * infl;
-  const uint64_t vstar = s_bi[0] >= 0 && (uint32_t)s_bi[0] < a.n ? (uint32_t)s_bi[0] : 0u;
-  const double lo = (double)zmax - (c1 * (double)a.sabs[(uint64_t)row * a.n + vstar] + c0);
-  if (s_bad || !__builtin_isfinite(zmax) || lo != lo) {
-    if (tid == 0) { a.argmax[row] = -1; if (a.ncand) a.ncand[row] = 0; }
-    return;
-  }
-  // 3. candidates
-  int32_t* cand = a.cand + (uint64_t)row * a.n;
-#pragma unroll 4
-  for (uint32_t b = tid; b < a.nb; b += kT) {
-    if ((double)rv[b] + (c1 * (double)rs[b] + c0) < lo) continue;
-    for (uint32_t rr = 0; rr < 16; ++rr) {
-      const uint64_t vo = (uint64_t)row * a.n + 16u * b + rr;
-      if ((double)a.logits[vo] + (c1 * (double)a.sabs[vo] + c0) >= lo)
-        cand[atomicAdd(&s_cnt, 1u)] = (int32_t)(16u * b + rr);
+  const uint32_t bstar = s_bi[0] >= 0 && (uint32_t)s_bi[0] < a.n ? (uint32_t)s_bi[0] >> 4 : 0u;
+  const double lo = (double)zmax - (c1 * (double)rs[bstar] + c0);
+  const bool row_ok = !s_bad && __builtin_isfinite(zmax) && lo == lo;
+  if (row_ok) {
+    // 3. candidates: a block's largest logit, and all its rows when its second largest
+    // also reaches L
+#pragma unroll 8
+    for (uint32_t b = tid; b < a.nb; b += kT) {
+      const double bb = c1 * (double)rs[b] + c0;
+      if ((double)rv[b] + bb < lo) continue;
+      const int32_t i1 = ri[b];
+      cand[atomicAdd(&s_cnt, 1u)] = i1;
+      if ((double)rv2[b] + bb >= lo)
+        for (uint32_t rr = 0; rr < 16; ++rr)
+          if ((int32_t)(16u * b + rr) != i1) cand[atomicAdd(&s_cnt, 1u)] = (int32_t)(16u * b + rr);
     }
-  }
-  __syncthreads();
-  const uint32_t ncand = s_cnt;
-  if (tid == 0) { s_best_v = -1; if (a.ncand) a.ncand[row] = (int32_t)ncand; }
+    __syncthreads();
+    ncand = s_cnt;
 
-  // 4. FP64 screen.  A BF16 product is exact in FP64; summed in any order with the
-  // escape corrections as extra terms (K' = K + 2 * escapes of the row terms), the FP64
-  // logit is within g64 * S64 of the exact one, g64 = (K'+8) 2^-53 / (1 - (K'+8) 2^-53).
-  // Only the candidates whose FP64 intervals reach the best lower bound go on to the
-  // exact integer sum; usually that is one, and it is the answer.
-  const bool screen = ncand <= kScreenMax;
-  if (screen) {
-    for (uint32_t c = 0; c < ncand; ++c) {
-      const uint32_t v = (uint32_t)cand[c];
-      const uint32_t b = v >> 4, r = v & 15u;
-      double z = 0.0, sa = 0.0;
-      uint32_t code;
-#pragma unroll 4
-      for (uint32_t kk = tid; kk < a.k; kk += kT) {
-        const uint32_t wb = decode_w(a.tiles, a.g_cols, v, kk, a.lut, &code);
-        const double p = (double)__uint_as_float((uint32_t)xr[kk] << 16) *
-                         (double)__uint_as_float(wb << 16);
-        z += p;
-        sa += fabs(p);
-      }
-      uint32_t nesc = 0;
-      const uint32_t e0 = a.esc_off[b], e1 = a.esc_off[b + 1];
-      for (uint32_t i = e0 + tid; i < e1; i += kT) {
-        const uint32_t rec = a.esc[i];
-        if ((rec >> 28) != r) continue;
-        const uint32_t kk = (rec >> 8) & 0xFFFFFu;
-        const uint32_t wb = decode_w(a.tiles, a.g_cols, v, kk, a.lut, &code);
-        const uint32_t wt = (wb & 0x807Fu) | ((rec & 0xFFu) << 7);
-        const double xv = (double)__uint_as_float((uint32_t)xr[kk] << 16);
-        const double pw = xv * (double)__uint_as_float(wb << 16);
-        const double pt = xv * (double)__uint_as_float(wt << 16);
-        z += pt - pw;          // two more rounded additions: counted in K'
-        sa += fabs(pt) + fabs(pw);
-        ++nesc;
-      }
-      s_d0[tid] = z;
-      s_d1[tid] = sa;
-      s_u0[tid] = nesc;
-      __syncthreads();
-      for (uint32_t off = kT / 2; off > 0; off >>= 1) {
-        if (tid < off) {
-          s_d0[tid] += s_d0[tid + off];
-          s_d1[tid] += s_d1[tid + off];
-          s_u0[tid] += s_u0[tid + off];
+    // 4. FP64 screen, kGroup candidates at a time, kPer threads each.  Thread u of a
+    // candidate v = 16b + r takes lane slots (g, q) = j / 4, j % 4 for j = u, u + kPer,
+    // ...: slot l = 16q + r of tile (b, g) holds row r's columns 128g + 32jj + 8q + i
+    // (jj < 4, i < 8), sign/mantissa bytes at 16l and 1024 + 16l, code nibbles in the
+    // dwords at 2048 + 16l.  The threads also take the block's escape records of row r
+    // (the product decoded with code 0 is replaced).  Partial sums meet in fixed
+    // shuffle and LDS trees, so the screen is deterministic.  Summed in any order, the K
+    // products and two terms per escape (K' terms) give an FP64 logit within g64 S64 of
+    // the exact one, g64 = (K'+8) 2^-53 / (1 - (K'+8) 2^-53), S64 the sum of the terms'
+    // magnitudes.
+    const bool screen = ncand <= kScreenMax;
+    if (screen) {
+      const uint32_t cc = tid / kPer, u = tid % kPer;
+      for (uint32_t c0i = 0; c0i < ncand; c0i += kGroup) {
+        const uint32_t c = c0i + cc;
+        const bool active = c < ncand;
+        double z = 0.0, sa = 0.0;
+        uint32_t nesc = 0;
+        if (active) {
+          const uint32_t v = (uint32_t)cand[c], b = v >> 4, r = v & 15u;
+          for (uint32_t j = u; j < 4u * a.g_cols; j += kPer) {
+            const uint32_t g = j >> 2, q = j & 3u, l = 16u * q + r;
+            const uint8_t* tb = a.tiles + ((uint64_t)b * a.g_cols + g) * 3072u + 16u * l;
+            const u32x4 s_lo = *reinterpret_cast<const u32x4*>(tb);
+            const u32x4 s_hi = *reinterpret_cast<const u32x4*>(tb + 1024);
+            const u32x4 cw = *reinterpret_cast<const u32x4*>(tb + 2048);
+#pragma unroll
+            for (uint32_t jj = 0; jj < 4; ++jj) {
+              const u32x4 xv = *reinterpret_cast<const u32x4*>(xr + 128u * g + 32u * jj + 8u * q);
+#pragma unroll
+              for (uint32_t i = 0; i < 8; ++i) {
+                const uint32_t t = 8u * jj + i;
+                const uint32_t sword = t < 16u ? s_lo[(t & 15u) >> 2] : s_hi[(t & 15u) >> 2];
+                const uint32_t sm = (sword >> (8u * (t & 3u))) & 0xFFu;
+                const uint32_t code = (cw[jj] >> (4u * (i >> 1) + 16u * (i & 1u))) & 0xFu;
+                const uint32_t e = (a.lut[code >> 2] >> (8u * (code & 3u))) & 0xFFu;
+                const uint32_t wb = ((sm & 0x80u) << 8) | (e << 7) | (sm & 0x7Fu);
+                const uint32_t xb = (xv[i >> 1] >> (16u * (i & 1u))) & 0xFFFFu;
+                const double pr = (double)__uint_as_float(xb << 16) * (double)__uint_as_float(wb << 16);
+                z += pr;
+                sa += fabs(pr);
+              }
+            }
+          }
+          const uint32_t e0 = a.esc_off[b], e1 = a.esc_off[b + 1];
+          for (uint32_t i = e0 + u; i < e1; i += kPer) {
+            const uint32_t rec = a.esc[i];
+            const uint32_t kk = (rec >> 8) & 0xFFFFFu;
+            if ((rec >> 28) != r || kk >= a.k) continue;   // another row, or malformed
+            uint32_t code;
+            const uint32_t wb = decode_w(a.tiles, a.g_cols, v, kk, a.lut, &code);
+            const uint32_t wt = (wb & 0x807Fu) | ((rec & 0xFFu) << 7);
+            const double xv = (double)__uint_as_float((uint32_t)xr[kk] << 16);
+            const double pw = xv * (double)__uint_as_float(wb << 16);
+            const double pt = xv * (double)__uint_as_float(wt << 16);
+            z += pt - pw;
+            sa += fabs(pt) + fabs(pw);
+            ++nesc;
+          }
+        }
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) {
+          z += __shfl_xor(z, off);
+          sa += __shfl_xor(sa, off);
+          nesc += __shfl_xor(nesc, off);
+        }
+        if (lane == 0) { s_d0[wave] = z; s_d1[wave] = sa; s_u0[wave] = nesc; }
+        __syncthreads();
+        if (active && u == 0) {
+          const uint32_t w0 = cc * (kPer / 64u);
+          double zz = 0.0, ss = 0.0;
+          uint32_t ne = 0;
+          for (uint32_t w = 0; w < kPer / 64u; ++w) { zz += s_d0[w0 + w]; ss += s_d1[w0 + w]; ne += s_u0[w0 + w]; }
+          const double kk2 = (double)a.k + 2.0 * (double)ne + 8.0;
+          const double g64 = kk2 * ldexp(1.0, -53) / (1.0 - kk2 * ldexp(1.0, -53));
+          s_z64[c] = zz;
+          s_b64[c] = g64 * ss / (1.0 - g64) * infl;
         }
         __syncthreads();
       }
+      // survivors: every candidate whose upper bound reaches the largest lower bound
       if (tid == 0) {
-        const double kk2 = (double)a.k + 2.0 * (double)s_u0[0] + 8.0;
-        const double g64 = kk2 * ldexp(1.0, -53) / (1.0 - kk2 * ldexp(1.0, -53));
-        s_z64[c] = s_d0[0];
-        s_b64[c] = g64 * s_d1[0] / (1.0 - g64) * (1.0 + ldexp(1.0, -20));
+        double lo64 = -__builtin_inf();
+        for (uint32_t c = 0; c < ncand; ++c) lo64 = fmax(lo64, s_z64[c] - s_b64[c]);
+        uint32_t ns = 0;
+        for (uint32_t c = 0; c < ncand; ++c)
+          if (s_z64[c] + s_b64[c] >= lo64) cand[ns++] = cand[c];
+        s_nsurv = ns;
       }
-      __syncthreads();
-    }
-    // survivors: every candidate whose upper bound reaches the largest lower bound
-    if (tid == 0) {
-      double lo64 = -__builtin_inf();
-      for (uint32_t c = 0; c < ncand; ++c) lo64 = fmax(lo64, s_z64[c] - s_b64[c]);
-      uint32_t ns = 0;
-      for (uint32_t c = 0; c < ncand; ++c)
-        if (s_z64[c] + s_b64[c] >= lo64) cand[ns++] = cand[c];
-      s_nsurv = ns;
+    } else if (tid == 0) {
+      s_nsurv = ncand;   // too many to screen: every candidate goes exact
     }
     __syncthreads();
-  } else if (tid == 0) {
-    s_nsurv = ncand;
+    nsurv = s_nsurv;
+    if (nsurv == 1u) {
+      result = cand[0];
+    } else {
+      // 5. exact recompute of the survivors
+      for (uint32_t c = 0; c < nsurv; ++c) {
+        const uint32_t v = (uint32_t)cand[c];
+        if (tid < kLimbs) limbs[tid] = 0ull;
+        __syncthreads();
+        uint32_t code;
+        for (uint32_t kk = tid; kk < a.k; kk += kT) {
+          const uint32_t wb = decode_w(a.tiles, a.g_cols, v, kk, a.lut, &code);
+          int sx_, sw_, ex_, ew_;
+          uint32_t mx_, mw_;
+          const bool okx = exact_parts(xr[kk], sx_, mx_, ex_);
+          const bool okw = exact_parts(wb, sw_, mw_, ew_);
+          if (!okx || !okw) atomicOr(&s_bad, 1u);
+          limb_add(limbs, sx_ * sw_, mx_ * mw_, ex_ + ew_ + 266, false);
+        }
+        // escapes of this row: replace the product decoded with the stored code
+        const uint32_t b = v >> 4, r = v & 15u;
+        const uint32_t e0 = a.esc_off[b], e1 = a.esc_off[b + 1];
+        for (uint32_t i = e0 + tid; i < e1; i += kT) {
+          const uint32_t rec = a.esc[i];
+          if ((rec >> 28) != r || ((rec >> 8) & 0xFFFFFu) >= a.k) continue;
+          const uint32_t kk = (rec >> 8) & 0xFFFFFu;
+          const uint32_t wb = decode_w(a.tiles, a.g_cols, v, kk, a.lut, &code);
+          const uint32_t wt = (wb & 0x807Fu) | ((rec & 0xFFu) << 7);
+          int sx_, sw_, ex_, ew_;
+          uint32_t mx_, mw_;
+          exact_parts(xr[kk], sx_, mx_, ex_);
+          if (exact_parts(wb, sw_, mw_, ew_)) limb_add(limbs, sx_ * sw_, mx_ * mw_, ex_ + ew_ + 266, true);
+          if (!exact_parts(wt, sw_, mw_, ew_)) atomicOr(&s_bad, 1u);
+          limb_add(limbs, sx_ * sw_, mx_ * mw_, ex_ + ew_ + 266, false);
+        }
+        __syncthreads();
+        if (tid == 0) {
+          // normalise to 32-bit digits; the final carry is the sign (0 or -1)
+          uint32_t dig[kLimbs];
+          long long carry = 0;
+          for (int i = 0; i < kLimbs; ++i) {
+            const long long t = (long long)limbs[i] + carry;
+            dig[i] = (uint32_t)(t & 0xFFFFFFFFll);
+            carry = t >> 32;
+          }
+          bool better;
+          if (s_best_v < 0) {
+            better = true;
+          } else if ((int32_t)carry != s_best_sign) {
+            better = (int32_t)carry > s_best_sign;
+          } else {
+            int cmp = 0;
+            for (int i = kLimbs - 1; i >= 0 && cmp == 0; --i)
+              cmp = dig[i] > best[i] ? 1 : (dig[i] < best[i] ? -1 : 0);
+            better = cmp > 0 || (cmp == 0 && (int32_t)v < s_best_v);
+          }
+          if (better) {
+            for (int i = 0; i < kLimbs; ++i) best[i] = dig[i];
+            s_best_sign = (int32_t)carry;
+            s_best_v = (int32_t)v;
+          }
+        }
+        __syncthreads();
+      }
+      result = s_bad ? -1 : s_best_v;
+    }
   }
-  __syncthreads();
-  const uint32_t nsurv = s_nsurv;
-  if (nsurv == 1u) {
-    if (tid == 0) a.argmax[row] = s_bad ? -1 : cand[0];
-    return;
+  if (tid == 0) {
+    a.argmax[row] = result;
+    if (a.ncand) { a.ncand[2 * row] = (int32_t)ncand; a.ncand[2 * row + 1] = (int32_t)nsurv; }
+    // accepted-prefix length: pass 1 set it to n_draft; the first mismatching row wins
+    if (row < a.n_draft && result != a.draft[row]) atomicMin(a.accepted, (int32_t)row);
   }
-  // 5. exact recompute of the survivors
-  for (uint32_t c = 0; c < nsurv; ++c) {
-    const uint32_t v = (uint32_t)cand[c];
-    if (tid < kLimbs) limbs[tid] = 0ull;
-    __syncthreads();
-    uint32_t code;
-    for (uint32_t kk = tid; kk < a.k; kk += kT) {
-      const uint32_t wb = decode_w(a.tiles, a.g_cols, v, kk, a.lut, &code);
-      int sx_, sw_, ex_, ew_;
-      uint32_t mx_, mw_;
-      const bool okx = exact_parts(xr[kk], sx_, mx_, ex_);
-      const bool okw = exact_parts(wb, sw_, mw_, ew_);
-      if (!okx || !okw) atomicOr(&s_bad, 1u);
-      limb_add(limbs, sx_ * sw_, mx_ * mw_, ex_ + ew_ + 266, false);
-    }
-    // escapes of this row: replace the product decoded with the stored code
-    const uint32_t b = v >> 4, r = v & 15u;
-    const uint32_t e0 = a.esc_off[b], e1 = a.esc_off[b + 1];
-    for (uint32_t i = e0 + tid; i < e1; i += kT) {
-      const uint32_t rec = a.esc[i];
-      if ((rec >> 28) != r) continue;
-      const uint32_t kk = (rec >> 8) & 0xFFFFFu;
-      const uint32_t wb = decode_w(a.tiles, a.g_cols, v, kk, a.lut, &code);
-      const uint32_t wt = (wb & 0x807Fu) | ((rec & 0xFFu) << 7);
-      int sx_, sw_, ex_, ew_;
-      uint32_t mx_, mw_;
-      exact_parts(xr[kk], sx_, mx_, ex_);
-      if (exact_parts(wb, sw_, mw_, ew_)) limb_add(limbs, sx_ * sw_, mx_ * mw_, ex_ + ew_ + 266, true);
-      if (!exact_parts(wt, sw_, mw_, ew_)) atomicOr(&s_bad, 1u);
-      limb_add(limbs, sx_ * sw_, mx_ * mw_, ex_ + ew_ + 266, false);
-    }
-    __syncthreads();
-    if (tid == 0) {
-      // normalise to 32-bit digits; the final carry is the sign (0 or -1)
-      uint32_t dig[kLimbs];
-      long long carry = 0;
-      for (int i = 0; i < kLimbs; ++i) {
-        const long long t = (long long)limbs[i] + carry;
-        dig[i] = (uint32_t)(t & 0xFFFFFFFFll);
-        carry = t >> 32;
-      }
-      bool better;
-      if (s_best_v < 0) {
-        better = true;
-      } else if ((int32_t)carry != s_best_sign) {
-        better = (int32_t)carry > s_best_sign;
-      } else {
-        int cmp = 0;
-        for (int i = kLimbs - 1; i >= 0 && cmp == 0; --i)
-          cmp = dig[i] > best[i] ? 1 : (dig[i] < best[i] ? -1 : 0);
-        better = cmp > 0 || (cmp == 0 && (int32_t)v < s_best_v);
-      }
-      if (better) {
-        for (int i = 0; i < kLimbs; ++i) best[i] = dig[i];
-        s_best_sign = (int32_t)carry;
-        s_best_v = (int32_t)v;
-      }
-    }
-    __syncthreads();
-  }
-  if (tid == 0) a.argmax[row] = s_bad ? -1 : s_best_v;
-}
-
-__global__ void k_accept(const int32_t* argmax, const int32_t* draft, uint32_t n_draft,
-                         int32_t* accepted) {
-  if (threadIdx.x != 0) return;
-  uint32_t i = 0;
-  while (i < n_draft && argmax[i] == draft[i]) ++i;
-  *accepted = (int32_t)i;
 }
 
 hipError_t launch_verify_pass2(const VerifyArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(k_verify_pass2, dim3(a.m), dim3(kT), 0, s, a);
-  return hipGetLastError();
-}
-
-hipError_t launch_accept(const VerifyArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(k_accept, dim3(1), dim3(64), 0, s, a.argmax, a.draft, a.n_draft, a.accepted);
   return hipGetLastError();
 }
 

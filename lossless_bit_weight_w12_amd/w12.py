@@ -21,7 +21,7 @@ STATUS = {0: "W12_OK", -1: "W12_ERR_NULL", -2: "W12_ERR_SHAPE", -3: "W12_ERR_RAN
           -4: "W12_ERR_FORMAT", -5: "W12_ERR_WORKSPACE", -6: "W12_ERR_HIP", -7: "W12_ERR_ALIGN"}
 EXPORTS = ("w12_tiles_bytes", "w12_workspace_bytes", "w12_workspace_init", "w12_encode_count",
            "w12_encode", "w12_decode", "w12_gemm", "w12_gemm_group", "w12_gemm_bf16", "w12_bf16_tile",
-           "w12_gemm_bf16_tiled", "w12_lmhead_verify",
+           "w12_gemm_bf16_tiled", "w12_lmhead_verify", "w12_logits_f32",
            "w12_rms_rescale", "w12_status_str", "w12_version")
 
 
@@ -79,6 +79,9 @@ def lib():
         L.w12_lmhead_verify.restype = c_int32
         L.w12_lmhead_verify.argtypes = [c_void_p, c_uint32, ctypes.POINTER(W12Desc), c_void_p,
                                         c_uint32, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]
+        L.w12_logits_f32.restype = c_int32
+        L.w12_logits_f32.argtypes = [c_void_p, c_uint32, ctypes.POINTER(W12Desc), c_void_p,
+                                     c_void_p, c_void_p, c_size_t, c_void_p]
         L.w12_rms_rescale.restype = c_int32
         L.w12_rms_rescale.argtypes = [c_void_p, c_uint32, c_uint64, c_void_p, c_void_p]
         L.w12_status_str.restype = ctypes.c_char_p
@@ -318,25 +321,26 @@ def lmhead_verify(x, t: W12Tensor, draft, argmax_out=None, accepted_out=None):
 
 
 def verify_candidates(t: W12Tensor, m: int):
-    """Per-row count of logits recomputed exactly by the last verification on this
-    device's workspace (diagnostic)."""
+    """Per-row diagnostic counts of the last verification on this device's workspace:
+    int32 [m, 2] = (candidate logits screened in FP64, those left after the screen; 1
+    means no exact sum was needed)."""
     torch = _torch()
     ws = workspace(workspace_bytes(OP_VERIFY, m, t.n, t.k), t.device, "verify")
-    return ws[:4 * m].view(torch.int32).clone()     # the counts open the verify workspace
+    return ws[:8 * m].view(torch.int32).view(m, 2).clone()   # the counts open the workspace
 
 
-def verify_pass1(t: W12Tensor, m: int):
-    """FP32 logits z^ [m, n] and their error scales S^ = sum_k |x_k||w_vk| [m, n] left by
-    the last verification on this device's workspace (diagnostic; layout as documented
-    for the VERIFY workspace: int32 counts [m], then logits, then S, each from a
-    256-byte boundary)."""
+def logits_f32(x, t: W12Tensor):
+    """FP32 logits z^ [m, n] and error scales S^ = sum_k |x_k||w_vk| [m, n] from the
+    first pass of the verification (same kernels, same summation order)."""
     torch = _torch()
-    ws = workspace(workspace_bytes(OP_VERIFY, m, t.n, t.k), t.device, "verify")
-    a = lambda v: (v + 255) // 256 * 256
-    o_logits = a(4 * m)
-    o_s = o_logits + a(4 * m * t.n)
-    z = ws[o_logits:o_logits + 4 * m * t.n].view(torch.float32).view(m, t.n).clone()
-    s = ws[o_s:o_s + 4 * m * t.n].view(torch.float32).view(m, t.n).clone()
+    x = _as_bits(x)
+    m = x.shape[0]
+    z = torch.empty((m, t.n), dtype=torch.float32, device=x.device)
+    s = torch.empty((m, t.n), dtype=torch.float32, device=x.device)
+    ws = workspace(workspace_bytes(OP_VERIFY, m, t.n, t.k), x.device, "verify")
+    d = t.desc()
+    _check("w12_logits_f32", lib().w12_logits_f32(_ptr(x), m, ctypes.byref(d), _ptr(z), _ptr(s),
+                                                  _ptr(ws), ws.numel(), _stream(x.device)))
     return z, s
 
 

@@ -159,8 +159,9 @@ def test_config4_lm_head_verify(env, lm_head):
         assert am.cpu().numpy().tolist() == ref.tolist()
         assert int(acc.item()) == o.accepted_length(ref, draft) == p
         nc = w12.verify_candidates(t, 16).cpu().numpy()
-        say("config 4 batch", b, "GPU candidates per row", nc.tolist())
-        assert (nc >= 1).all()
+        say("config 4 batch", b, "GPU candidates / left after the FP64 screen",
+            nc.tolist())
+        assert (nc[:, 0] >= 1).all() and (nc[:, 1] >= 1).all()
 
 
 SAMPLED_LAYERS = (0, 21, 42, 63)

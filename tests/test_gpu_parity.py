@@ -286,7 +286,7 @@ def test_verify_matches_oracle(env, m):
         assert am.cpu().numpy().tolist() == am_ref.tolist()
         assert int(acc.item()) == o.accepted_length(am_ref, draft) == p
     nc = w12.verify_candidates(t, m).cpu().numpy()
-    assert (nc >= 1).all()
+    assert (nc[:, 0] >= 1).all() and (nc[:, 1] >= 1).all() and (nc[:, 1] <= 16 * nc[:, 0]).all()
 
 
 def _certified_bound(s_hat, k, e_max, xmax):
@@ -302,9 +302,10 @@ def _certified_bound(s_hat, k, e_max, xmax):
 @pytest.mark.parametrize("m,kind", [(1, "gauss"), (3, "wide"), (7, "gauss"), (16, "outliers"),
                                     (24, "gauss"), (32, "wide")])
 def test_verify_pass1_error_within_certified_bound(env, m, kind):
-    """The FP32 logits of verification pass 1 stay within the certified bound of the
-    exact values on every output (the assumption the exact-argmax filter rests on), and
-    the kernel's sum |x||w| is a valid scale for it."""
+    """The FP32 logits of verification pass 1 (w12_logits_f32: the same kernels and
+    summation order) stay within the certified bound of the exact values on every
+    output (the assumption the exact-argmax filter rests on), and the kernel's
+    sum |x||w| is a valid scale for it."""
     torch, w12 = env
     g = np.random.default_rng(9000 + m)
     n, k = 2048, 5120
@@ -317,8 +318,7 @@ def test_verify_pass1_error_within_certified_bound(env, m, kind):
     x = wi.gaussian_bf16((m, k), 1.0, g)
     t = w12.encode(to_dev(w, torch))
     say("pass-1 bound", m, kind, "codebook", t.codebook)
-    w12.lmhead_verify(to_dev(x, torch), t, torch.zeros(0, dtype=torch.int32, device="cuda:0"))
-    z_hat, s_hat = (v.cpu().numpy().astype(np.float64) for v in w12.verify_pass1(t, m))
+    z_hat, s_hat = (v.cpu().numpy().astype(np.float64) for v in w12.logits_f32(to_dev(x, torch), t))
     z, s = o.gemm_reference(x, w)
     xmax = np.abs(wi.bf16_bits_to_f32(x).astype(np.float64)).max()
     bound, gam, a = _certified_bound(s_hat, k, t.e_max, xmax)

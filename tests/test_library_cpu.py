@@ -57,7 +57,8 @@ def test_workspace_sizes(L):
     assert w12.workspace_bytes(99, 1, 1024, 1024) == 0
     n, k, m = 151936, 5120, 16
     v = w12.workspace_bytes(w12.OP_VERIFY, m, n, k)
-    assert v >= 4 * m * n * 3 + 12 * m * (n // 16) + 4 * m   # logits, S, candidates, maxima
+    assert v >= 16 * m * (n // 16) + 4 * m * n + 8 * m   # block records, candidate lists, counts
+    assert v < 8 * m * n                                  # no full logits or S
     assert w12.workspace_bytes(w12.OP_ENCODE, 1, n, k) >= 8 * (n // 16) * (k // 128)
 
 
@@ -162,6 +163,22 @@ def test_verify_validation(L):
     assert f(FAKE, 4, ctypes.byref(d), FAKE, 5, FAKE, FAKE, FAKE, big, None) == -3   # n_draft > m
     assert f(FAKE, 0, ctypes.byref(d), FAKE, 0, FAKE, FAKE, FAKE, big, None) == -3
     assert f(FAKE, 4, ctypes.byref(d), FAKE, 4, FAKE, FAKE, FAKE, 100, None) == -5
+
+
+def test_logits_f32_validation(L):
+    f = L.w12_logits_f32
+    d = desc(n=2048, k=512)
+    big = 1 << 34
+    assert f(None, 4, ctypes.byref(d), FAKE, FAKE, FAKE, big, None) == -1
+    assert f(FAKE, 4, ctypes.byref(d), None, FAKE, FAKE, big, None) == -1
+    assert f(FAKE, 4, ctypes.byref(d), FAKE, FAKE, None, big, None) == -1
+    assert f(FAKE, 4, None, FAKE, FAKE, FAKE, big, None) == -1
+    assert f(FAKE, 0, ctypes.byref(d), FAKE, FAKE, FAKE, big, None) == -3
+    assert f(FAKE, 33, ctypes.byref(d), FAKE, FAKE, FAKE, big, None) == -3
+    assert f(FAKE, 4, ctypes.byref(desc(n=1000, k=512)), FAKE, FAKE, FAKE, big, None) == -2
+    assert f(FAKE, 4, ctypes.byref(d), FAKE, FAKE, FAKE, 100, None) == -5
+    assert f(FAKE, 4, ctypes.byref(d), FAKE + 8, FAKE, FAKE, big, None) == -7
+    assert f(FAKE, 4, ctypes.byref(d), FAKE, FAKE + 4, FAKE, big, None) == -7
 
 
 def test_encode_decode_validation(L):
