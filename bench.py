@@ -227,7 +227,9 @@ def extra_workloads(torch, w12, wi, np, dev, args):
     y16 = torch.empty((16, vocab), dtype=torch.bfloat16, device=dev)
     gcall = w12.prepare_gemm(x16, head, y16)
     ms_gemm16 = time_calls(torch, gcall, 50)
-    v_bytes = head.nbytes() + 2 * 16 * hid + 8 * 16 * vocab + 4 * 16
+    # the verification's algorithmic bytes: the W12 head, x, the per-block records of
+    # pass 1 (16 B per row and 16-row block, written and read) and the argmax
+    v_bytes = head.nbytes() + 2 * 16 * hid + 2 * 16 * 16 * (vocab // 16) + 4 * 16
     g_bytes = head.nbytes() + 2 * 16 * hid + 2 * 16 * vocab
     verify = {
         "workload": f"LM head [{vocab}x{hid}] W12, M=16, greedy verify of a 16-token draft",

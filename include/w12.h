@@ -100,7 +100,8 @@ size_t w12_tiles_bytes(uint64_t n, uint64_t k);
 /* Workspace bytes needed by `op` for m rows (ignored by ENCODE/DECODE) and an
  * n x k weight; 0 for an invalid op or shape, and 0 when the op needs none (DECODE,
  * and GEMM shapes that are not split along K).  GEMM split along K needs FP32
- * partials [splits][m][n]; VERIFY holds, each region starting on a 256-byte boundary
+ * partials [splits][m][n] and the splits' row sums of x^2 [splits][m] (RMS launches),
+ * each from a 256-byte boundary; VERIFY holds, each region starting on a 256-byte boundary
  * in this order: per-row diagnostic counts (int32 [m][2]: candidate logits, those left
  * after the FP64 screen), the per-row-block records of the first pass (largest FP32
  * logit, second largest, largest sum_k |x_k||w_k|, each FP32 [m][n/16]; index of the
@@ -153,6 +154,20 @@ w12_status w12_gemm(const uint16_t* x, uint32_t m, const w12_desc* d, uint16_t* 
 w12_status w12_gemm_group(const uint16_t* x, uint32_t m, const w12_desc* const* descs,
                           uint32_t n_w, uint16_t* const* ys, void* ws, size_t ws_bytes,
                           void* stream);
+
+/* The same products of the row-wise RMS-normalised input, for the layer chain whose
+ * every GEMM consumes the RMS-rescaled output of the previous one (w12_rms_rescale):
+ * y[row] = bf16((x[row] . W^T) / r), r = sqrt(mean_k x[row,k]^2) in FP32, the division
+ * applied to the FP32 accumulators (equal to the product of the rescaled row up to
+ * rounding; the rescaled row itself is never rounded to BF16).  r comes from the x values
+ * each launch streams anyway, summed in a fixed order.  Arguments, workspace
+ * (W12_OP_GEMM / W12_OP_GEMM_GROUP), errors and determinism as w12_gemm /
+ * w12_gemm_group.  Not part of the W12 method itself. */
+w12_status w12_gemm_rms(const uint16_t* x, uint32_t m, const w12_desc* d, uint16_t* y,
+                        void* ws, size_t ws_bytes, void* stream);
+w12_status w12_gemm_group_rms(const uint16_t* x, uint32_t m, const w12_desc* const* descs,
+                              uint32_t n_w, uint16_t* const* ys, void* ws, size_t ws_bytes,
+                              void* stream);
 
 /* The same kernel family reading plain BF16 weights w [n][k] row-major (the baseline
  * W12 is measured against: plain BF16 decoding in "What it is").  Workspace as for

@@ -110,10 +110,14 @@ GemmPlan make_plan(uint32_t m, uint64_t n, uint64_t k, int epi, bool bf16_src = 
 }
 
 // GEMM workspace when K is split: FP32 partials [nsplit][m][n], summed by the reduce
-// kernel; no state survives a call.
+// kernel, then (RMS launches) each split's sum of x^2 per row [nsplit][m]; no state
+// survives a call.
+size_t split_ws_bytes(uint64_t nsplit, uint32_t m, uint64_t n) {
+  return nsplit > 1 ? align256((size_t)nsplit * m * n * 4) + align256((size_t)nsplit * m * 4) : 0;
+}
+
 size_t gemm_ws_bytes(uint32_t m, uint64_t n, uint64_t k, bool bf16_src = false) {
-  const GemmPlan p = make_plan(m, n, k, EPI_BF16, bf16_src);
-  return p.nsplit > 1 ? align256((size_t)p.nsplit * m * n * 4) : 0;
+  return split_ws_bytes(make_plan(m, n, k, EPI_BF16, bf16_src).nsplit, m, n);
 }
 
 // A group may run as two launches (one per codebook kind), each over part of the rows:
@@ -121,7 +125,7 @@ size_t gemm_ws_bytes(uint32_t m, uint64_t n, uint64_t k, bool bf16_src = false) 
 size_t group_ws_bytes(uint32_t m, uint64_t n_total, uint64_t k) {
   const uint64_t g = k / 128;
   const uint64_t cap = std::min<uint64_t>(W12_NS_CAP, std::max<uint64_t>(g / 4, 1));
-  return cap > 1 ? align256((size_t)cap * m * n_total * 4) : 0;
+  return split_ws_bytes(cap, m, n_total);
 }
 
 // Verify workspace: per-row diagnostic counts first (a fixed place), then the
@@ -197,11 +201,15 @@ void fill_params(GemmParams& p, uint32_t m, uint64_t k, uint64_t n_total, uint32
   p.n = (uint32_t)n_total;
   p.nb = (uint32_t)(n_total / 16);
   p.nseg = nseg;
+  p.rms = 0;
+  p.ss = nullptr;
 }
 
-// One launch over segments ds[0..nseg) (same k, same codebook kind): y_i = x . W_i^T.
+// One launch over segments ds[0..nseg) (same k, same codebook kind): y_i = x . W_i^T,
+// each row divided by the RMS of its x row when rms is set.
 hipError_t launch_w12_group(const uint16_t* x, uint32_t m, const w12_desc* const* ds,
-                            uint16_t* const* ys, uint32_t nseg, void* ws, hipStream_t s) {
+                            uint16_t* const* ys, uint32_t nseg, void* ws, hipStream_t s,
+                            bool rms) {
   GemmArgs a;
   memset(&a, 0, sizeof(a));
   a.x = x;
@@ -213,8 +221,59 @@ hipError_t launch_w12_group(const uint16_t* x, uint32_t m, const w12_desc* const
   }
   fill_params(a.p, m, ds[0]->k, n_total, nseg);
   const GemmPlan p = make_plan(m, n_total, ds[0]->k, EPI_BF16);
+  a.p.rms = rms ? 1u : 0u;
+  if (p.nsplit > 1)
+    a.p.ss = (float*)((uint8_t*)ws + align256((size_t)p.nsplit * m * n_total * 4));
   const int src = codebook_is_run(ds[0]->codebook) ? SRC_RUN : SRC_LUT;
   return launch_gemm(a, src, EPI_BF16, p, s);
+}
+
+w12_status gemm_impl(const uint16_t* x, uint32_t m, const w12_desc* d, uint16_t* y, void* ws,
+                     size_t ws_bytes, void* stream, bool rms) {
+  if (!x || !y) return W12_ERR_NULL;
+  w12_status st = check_desc(d, true);
+  if (st != W12_OK) return st;
+  if (m < 1 || m > W12_MAX_M) return W12_ERR_RANGE;
+  const size_t need = gemm_ws_bytes(m, d->n, d->k);
+  if (ws_bytes < need) return W12_ERR_WORKSPACE;
+  if (need > 0 && !ws) return W12_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(y, 16) || !aligned(ws, 256)) return W12_ERR_ALIGN;
+  return hip_status(launch_w12_group(x, m, &d, &y, 1, ws, (hipStream_t)stream, rms));
+}
+
+w12_status gemm_group_impl(const uint16_t* x, uint32_t m, const w12_desc* const* descs,
+                           uint32_t n_w, uint16_t* const* ys, void* ws, size_t ws_bytes,
+                           void* stream, bool rms) {
+  if (!x || !descs || !ys) return W12_ERR_NULL;
+  if (n_w < 1 || n_w > W12_MAX_GROUP || m < 1 || m > W12_MAX_M) return W12_ERR_RANGE;
+  uint64_t n_total = 0;
+  for (uint32_t i = 0; i < n_w; ++i) {
+    w12_status st = check_desc(descs[i], true);
+    if (st != W12_OK) return st;
+    if (!ys[i]) return W12_ERR_NULL;
+    if (descs[i]->k != descs[0]->k) return W12_ERR_SHAPE;
+    if (!aligned(ys[i], 16)) return W12_ERR_ALIGN;
+    n_total += descs[i]->n;
+  }
+  if (n_total >= kMaxN) return W12_ERR_SHAPE;
+  const size_t need = group_ws_bytes(m, n_total, descs[0]->k);
+  if (ws_bytes < need) return W12_ERR_WORKSPACE;
+  if (need > 0 && !ws) return W12_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(ws, 256)) return W12_ERR_ALIGN;
+  // one launch per codebook kind (run / lookup table), in the callers' order within each
+  const w12_desc* dd[2][W12_MAX_GROUP];
+  uint16_t* yy[2][W12_MAX_GROUP];
+  uint32_t cnt[2] = {0, 0};
+  for (uint32_t i = 0; i < n_w; ++i) {
+    const int kind = codebook_is_run(descs[i]->codebook) ? 0 : 1;
+    dd[kind][cnt[kind]] = descs[i];
+    yy[kind][cnt[kind]++] = ys[i];
+  }
+  hipError_t e = hipSuccess;
+  for (int kind = 0; kind < 2 && e == hipSuccess; ++kind)
+    if (cnt[kind])
+      e = launch_w12_group(x, m, dd[kind], yy[kind], cnt[kind], ws, (hipStream_t)stream, rms);
+  return hip_status(e);
 }
 
 }  // namespace
@@ -319,49 +378,24 @@ w12_status w12_decode(const w12_desc* d, uint16_t* w_out, void* stream) {
 
 w12_status w12_gemm(const uint16_t* x, uint32_t m, const w12_desc* d, uint16_t* y, void* ws,
                     size_t ws_bytes, void* stream) {
-  if (!x || !y) return W12_ERR_NULL;
-  w12_status st = check_desc(d, true);
-  if (st != W12_OK) return st;
-  if (m < 1 || m > W12_MAX_M) return W12_ERR_RANGE;
-  const size_t need = gemm_ws_bytes(m, d->n, d->k);
-  if (ws_bytes < need) return W12_ERR_WORKSPACE;
-  if (need > 0 && !ws) return W12_ERR_NULL;
-  if (!aligned(x, 16) || !aligned(y, 16) || !aligned(ws, 256)) return W12_ERR_ALIGN;
-  return hip_status(launch_w12_group(x, m, &d, &y, 1, ws, (hipStream_t)stream));
+  return gemm_impl(x, m, d, y, ws, ws_bytes, stream, false);
+}
+
+w12_status w12_gemm_rms(const uint16_t* x, uint32_t m, const w12_desc* d, uint16_t* y, void* ws,
+                        size_t ws_bytes, void* stream) {
+  return gemm_impl(x, m, d, y, ws, ws_bytes, stream, true);
 }
 
 w12_status w12_gemm_group(const uint16_t* x, uint32_t m, const w12_desc* const* descs,
                           uint32_t n_w, uint16_t* const* ys, void* ws, size_t ws_bytes,
                           void* stream) {
-  if (!x || !descs || !ys) return W12_ERR_NULL;
-  if (n_w < 1 || n_w > W12_MAX_GROUP || m < 1 || m > W12_MAX_M) return W12_ERR_RANGE;
-  uint64_t n_total = 0;
-  for (uint32_t i = 0; i < n_w; ++i) {
-    w12_status st = check_desc(descs[i], true);
-    if (st != W12_OK) return st;
-    if (!ys[i]) return W12_ERR_NULL;
-    if (descs[i]->k != descs[0]->k) return W12_ERR_SHAPE;
-    if (!aligned(ys[i], 16)) return W12_ERR_ALIGN;
-    n_total += descs[i]->n;
-  }
-  if (n_total >= kMaxN) return W12_ERR_SHAPE;
-  const size_t need = group_ws_bytes(m, n_total, descs[0]->k);
-  if (ws_bytes < need) return W12_ERR_WORKSPACE;
-  if (need > 0 && !ws) return W12_ERR_NULL;
-  if (!aligned(x, 16) || !aligned(ws, 256)) return W12_ERR_ALIGN;
-  // one launch per codebook kind (run / lookup table), in the callers' order within each
-  const w12_desc* dd[2][W12_MAX_GROUP];
-  uint16_t* yy[2][W12_MAX_GROUP];
-  uint32_t cnt[2] = {0, 0};
-  for (uint32_t i = 0; i < n_w; ++i) {
-    const int kind = codebook_is_run(descs[i]->codebook) ? 0 : 1;
-    dd[kind][cnt[kind]] = descs[i];
-    yy[kind][cnt[kind]++] = ys[i];
-  }
-  hipError_t e = hipSuccess;
-  for (int kind = 0; kind < 2 && e == hipSuccess; ++kind)
-    if (cnt[kind]) e = launch_w12_group(x, m, dd[kind], yy[kind], cnt[kind], ws, (hipStream_t)stream);
-  return hip_status(e);
+  return gemm_group_impl(x, m, descs, n_w, ys, ws, ws_bytes, stream, false);
+}
+
+w12_status w12_gemm_group_rms(const uint16_t* x, uint32_t m, const w12_desc* const* descs,
+                              uint32_t n_w, uint16_t* const* ys, void* ws, size_t ws_bytes,
+                              void* stream) {
+  return gemm_group_impl(x, m, descs, n_w, ys, ws, ws_bytes, stream, true);
 }
 
 w12_status w12_gemm_bf16(const uint16_t* x, uint32_t m, const uint16_t* w, uint64_t n,

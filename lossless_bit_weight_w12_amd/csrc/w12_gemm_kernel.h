@@ -280,6 +280,21 @@ __device__ __forceinline__ void esc_apply(EscCursor& c, const uint32_t* __restri
   }
 }
 
+// Sum of squares of the 8 BF16 of a 16-byte x unit, in FP32, in a fixed order (RMS
+// launches: the row's mean square is accumulated from the staged x units).
+__device__ __forceinline__ float unit_sumsq(const u32x4& v) {
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float lo = __uint_as_float(v[i] << 16), hi = __uint_as_float(v[i] & 0xFFFF0000u);
+    s += lo * lo + hi * hi;
+  }
+  return s;
+}
+
+// 1 / RMS of a row from its sum of squares over K (the RMS rescale's formula).
+__device__ __forceinline__ float rms_of(float ss, uint32_t k) { return sqrtf(ss / (float)k); }
+
 // One wave's x column: MT rows x 128 BF16 = 16*MT units of 16 bytes over 64 lanes.
 template <int MT>
 struct XStage {
@@ -448,6 +463,17 @@ __global__ __launch_bounds__(NWV * 64) void k_gemm(
   // with scheduling barriers (and a single-exit loop) measured slower on these shapes
   // (M1 down -5 %, M16 / M32 gate+up -3 to -4 %), the memory system being saturated by
   // fewer requests in flight per wave.
+  // RMS launches: per-unit sums of x^2 over the wave's columns, in column order
+  constexpr int kXU = XStage<M>::kUnits;
+  float ssq[kXU];
+#pragma unroll
+  for (int i = 0; i < kXU; ++i) ssq[i] = 0.f;
+  auto xsumsq = [&](bool in_range) {
+    if (EPI == EPI_BF16 && p.rms && in_range) {   // (RMS launches have the BF16 epilogue)
+#pragma unroll
+      for (int i = 0; i < kXU; ++i) ssq[i] += unit_sumsq(xr.v[i]);
+    }
+  };
   uint32_t g = ga + (uint32_t)wave;
   if (g < gb) {
     x_load<M>(xr, x, p.k, m_rows, g, gb, lane);
@@ -458,12 +484,14 @@ __global__ __launch_bounds__(NWV * 64) void k_gemm(
 #pragma unroll
       for (int rb = 0; rb < RBW; ++rb) esc_begin(ec[rb], sv[rb].esc_off, sv[rb].esc, bl[rb], ga * 128u);
     }
+    xsumsq(true);
     x_store<M>(xr, xw, lane);
     __builtin_amdgcn_wave_barrier();
     for (;;) {
       x_load<M>(xr, x, p.k, m_rows, g + NWV, gb, lane);
       load_tiles(tB, g + NWV);
       compute(tA, g);
+      xsumsq(g + NWV < gb);
       __builtin_amdgcn_wave_barrier();
       x_store<M>(xr, xw, lane);
       __builtin_amdgcn_wave_barrier();
@@ -472,6 +500,7 @@ __global__ __launch_bounds__(NWV * 64) void k_gemm(
       x_load<M>(xr, x, p.k, m_rows, g + NWV, gb, lane);
       load_tiles(tA, g + NWV);
       compute(tB, g);
+      xsumsq(g + NWV < gb);
       __builtin_amdgcn_wave_barrier();
       x_store<M>(xr, xw, lane);
       __builtin_amdgcn_wave_barrier();
@@ -479,7 +508,28 @@ __global__ __launch_bounds__(NWV * 64) void k_gemm(
       if (g >= gb) break;
     }
   }
+  // RMS launches: each row's sum of x^2 per wave (its 16 unit lanes meet in a fixed
+  // shuffle tree), then over the waves in wave order where it is used
+  __shared__ float s_ssw[NWV][M];
+  if (EPI == EPI_BF16 && p.rms) {
+#pragma unroll
+    for (int i = 0; i < kXU; ++i) {
+      float v = ssq[i];
+#pragma unroll
+      for (int off = 8; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+      const uint32_t u = (uint32_t)lane + 64u * i;
+      if (u < 16u * M && (u & 15u) == 0u) s_ssw[wave][u >> 4] = v;
+    }
+  }
+  auto row_ss = [&](int m) {
+    float t = 0.f;
+#pragma unroll
+    for (int wv = 0; wv < NWV; ++wv) t += s_ssw[wv][m];
+    return t;
+  };
   __syncthreads();   // LDS x no longer read: reuse it for the cross-wave reduction
+  if (EPI == EPI_BF16 && p.rms && gridDim.y > 1 && blockIdx.x == 0 && tid < M && (uint32_t)tid < m_rows)
+    p.ss[(size_t)blockIdx.y * m_rows + tid] = row_ss(tid);   // this split's part, for the reduce
 
   // ---- cross-lane / cross-wave reduction into red[] (aliases xs); the S sums, when
   // kept, go to a second region of the same size
@@ -574,7 +624,7 @@ __global__ __launch_bounds__(NWV * 64) void k_gemm(
         uint16_t* yy = second ? sv[RBW - 1].y : sv[0].y;
         const uint32_t nn = second ? sv[RBW - 1].n : sv[0].n;
         const uint32_t bb = second ? bl[RBW - 1] : bl[0];
-        yy[(size_t)m * nn + 16u * bb + rr] = f32_to_bf16_rne(v);
+        yy[(size_t)m * nn + 16u * bb + rr] = f32_to_bf16_rne(p.rms ? v / rms_of(row_ss(m), p.k) : v);
       } else {
         out_f32[((size_t)split * m_rows + m) * p.n + 16u * b + rr] = v;
       }
@@ -633,6 +683,16 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_cs(
       xr[i] = *reinterpret_cast<const u32x4*>(x + (size_t)min(m, m_rows - 1u) * p.k + 128u * gl + 8u * cu);
     }
   };
+  // RMS launches: per-unit sums of x^2 over the K-range, in column order
+  float ssq[kUnits];
+#pragma unroll
+  for (int i = 0; i < kUnits; ++i) ssq[i] = 0.f;
+  auto xsumsq = [&](bool in_range) {
+    if (EPI == EPI_BF16 && p.rms && in_range) {   // (RMS launches have the BF16 epilogue)
+#pragma unroll
+      for (int i = 0; i < kUnits; ++i) ssq[i] += unit_sumsq(xr[i]);
+    }
+  };
   auto xstore = [&](uint32_t slot) {
 #pragma unroll
     for (int i = 0; i < kUnits; ++i) {
@@ -679,21 +739,44 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_cs(
   xload(g);
   load_tile<SRC>(tA, sv.w, p, bl, g, lane);
   if constexpr (!plain_bf16(SRC)) esc_begin(ec, sv.esc_off, sv.esc, bl, ga * 128u);
+  xsumsq(true);
   xstore(g & 1u);
   __syncthreads();
   for (;;) {
     xload(g + 1);
     load_tile<SRC>(tB, sv.w, p, bl, min(g + 1, gb - 1u), lane);
     compute(tA, g);
+    xsumsq(g + 1 < gb);
     xstore((g + 1) & 1u);
     __syncthreads();
     if (++g >= gb) break;
     xload(g + 1);
     load_tile<SRC>(tA, sv.w, p, bl, min(g + 1, gb - 1u), lane);
     compute(tB, g);
+    xsumsq(g + 1 < gb);
     xstore((g + 1) & 1u);
     __syncthreads();
     if (++g >= gb) break;
+  }
+
+  // RMS launches: each row's sum of x^2 over the K-range: the 16 threads of a row's units
+  // (consecutive lanes) meet in a fixed shuffle tree; one value per row in LDS.  With K
+  // split, the first workgroup of each split leaves it for the reduce kernel.
+  __shared__ float s_ss[MT];
+  if (EPI == EPI_BF16 && p.rms) {
+#pragma unroll
+    for (int i = 0; i < kUnits; ++i) {
+      float v = ssq[i];
+#pragma unroll
+      for (int off = 8; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+      const uint32_t u = (uint32_t)tid + NT * i;
+      if ((kUnits * NT == 16 * MT || u < 16u * MT) && (u & 15u) == 0u) {
+        s_ss[u >> 4] = v;
+        if (gridDim.y > 1 && blockIdx.x == 0 && (u >> 4) < m_rows)
+          p.ss[(size_t)blockIdx.y * m_rows + (u >> 4)] = v;
+      }
+    }
+    __syncthreads();
   }
 
   const uint32_t n0 = 16u * b + 4u * (uint32_t)q;       // launch numbering (logits, partials)
@@ -751,7 +834,12 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_cs(
     }
   } else {
     const bool direct = gridDim.y == 1;
-    auto store_y = [&](uint32_t m, const f32x4& v) {
+    auto store_y = [&](uint32_t m, f32x4 v) {
+      if (p.rms) {
+        const float rms = rms_of(s_ss[m], p.k);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = v[i] / rms;
+      }
       const uint32_t lo = (uint32_t)f32_to_bf16_rne(v[0]) | ((uint32_t)f32_to_bf16_rne(v[1]) << 16);
       const uint32_t hi = (uint32_t)f32_to_bf16_rne(v[2]) | ((uint32_t)f32_to_bf16_rne(v[3]) << 16);
       *reinterpret_cast<uint2*>(sv.y + (size_t)m * sv.n + n0l) = make_uint2(lo, hi);
@@ -766,9 +854,10 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_cs(
   }
 }
 
-// Sum of the split-K partials in split order (deterministic), rounded to BF16.  A thread
-// owns four consecutive outputs of one row (n is a multiple of 16, so all four lie in one
-// row-block of one weight) and issues every partial load before the first add.
+// Sum of the split-K partials in split order (deterministic), divided by the row's RMS on
+// RMS launches, rounded to BF16.  A thread owns four consecutive outputs of one row (n is
+// a multiple of 16, so all four lie in one row-block of one weight) and issues every
+// partial load before the first add.
 static __global__ __launch_bounds__(256) void k_splitk_reduce(const float* __restrict__ partial,
                                                        GemmParams p, uint32_t nsplit) {
   const uint32_t mn = p.m * p.n, n4 = mn >> 2;
@@ -784,6 +873,13 @@ static __global__ __launch_bounds__(256) void k_splitk_reduce(const float* __res
     for (uint32_t sp = 0; sp < kMaxSplit; ++sp)
       if (sp < nsplit) s += v[sp];
     const uint32_t i = 4u * i4, m = i / p.n, row = i - m * p.n;
+    if (p.rms) {   // the row's sum of x^2: the splits' parts in split order
+      float ss = 0.f;
+      for (uint32_t sp = 0; sp < nsplit; ++sp) ss += p.ss[sp * p.m + m];
+      const float rms = rms_of(ss, p.k);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) s[j] = s[j] / rms;
+    }
     const SegView sv = seg_view(p, row >> 4);
     const uint32_t lo = (uint32_t)f32_to_bf16_rne(s[0]) | ((uint32_t)f32_to_bf16_rne(s[1]) << 16);
     const uint32_t hi = (uint32_t)f32_to_bf16_rne(s[2]) | ((uint32_t)f32_to_bf16_rne(s[3]) << 16);

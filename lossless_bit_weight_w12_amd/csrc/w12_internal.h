@@ -50,6 +50,10 @@ struct GemmParams {
   uint32_t m, k, g_cols;
   uint32_t nb, n;           // row-blocks and rows of all the launch's weights together
   uint32_t nseg;
+  // RMS launches (rms = 1): y = (x . W^T) / sqrt(mean_k x^2) per row; when K is split,
+  // each split's sum of x^2 per row goes to ss[split][m] for the reduce kernel
+  uint32_t rms;
+  float* ss;
   Seg seg[kMaxSeg];
 };
 

@@ -20,7 +20,8 @@ MAX_GROUP = 4
 STATUS = {0: "W12_OK", -1: "W12_ERR_NULL", -2: "W12_ERR_SHAPE", -3: "W12_ERR_RANGE",
           -4: "W12_ERR_FORMAT", -5: "W12_ERR_WORKSPACE", -6: "W12_ERR_HIP", -7: "W12_ERR_ALIGN"}
 EXPORTS = ("w12_tiles_bytes", "w12_workspace_bytes", "w12_workspace_init", "w12_encode_count",
-           "w12_encode", "w12_decode", "w12_gemm", "w12_gemm_group", "w12_gemm_bf16", "w12_bf16_tile",
+           "w12_encode", "w12_decode", "w12_gemm", "w12_gemm_group", "w12_gemm_rms",
+           "w12_gemm_group_rms", "w12_gemm_bf16", "w12_bf16_tile",
            "w12_gemm_bf16_tiled", "w12_lmhead_verify", "w12_logits_f32",
            "w12_rms_rescale", "w12_status_str", "w12_version")
 
@@ -68,6 +69,10 @@ def lib():
         L.w12_gemm_group.restype = c_int32
         L.w12_gemm_group.argtypes = [c_void_p, c_uint32, c_void_p, c_uint32, c_void_p, c_void_p,
                                      c_size_t, c_void_p]
+        L.w12_gemm_rms.restype = c_int32
+        L.w12_gemm_rms.argtypes = L.w12_gemm.argtypes
+        L.w12_gemm_group_rms.restype = c_int32
+        L.w12_gemm_group_rms.argtypes = L.w12_gemm_group.argtypes
         L.w12_gemm_bf16.restype = c_int32
         L.w12_gemm_bf16.argtypes = [c_void_p, c_uint32, c_void_p, c_uint64, c_uint64, c_void_p,
                                     c_void_p, c_size_t, c_void_p]
@@ -219,8 +224,9 @@ def decode(t: W12Tensor, out=None):
     return out
 
 
-def gemm(x, t: W12Tensor, out=None):
-    """y = x . W^T, x BF16 [m, k] (m <= 32), y BF16 [m, n]."""
+def gemm(x, t: W12Tensor, out=None, rms: bool = False):
+    """y = x . W^T, x BF16 [m, k] (m <= 32), y BF16 [m, n].  rms: each output row divided
+    by the RMS of its x row (w12_gemm_rms)."""
     torch = _torch()
     x = _as_bits(x)
     m = x.shape[0]
@@ -230,8 +236,9 @@ def gemm(x, t: W12Tensor, out=None):
         out = torch.empty((m, t.n), dtype=torch.bfloat16, device=x.device)
     ws = workspace(max(workspace_bytes(OP_GEMM, m, t.n, t.k), 256), x.device)
     d = t.desc()
-    _check("w12_gemm", lib().w12_gemm(_ptr(x), m, ctypes.byref(d), _ptr(_as_bits(out)), _ptr(ws),
-                                      ws.numel(), _stream(x.device)))
+    fn = "w12_gemm_rms" if rms else "w12_gemm"
+    _check(fn, getattr(lib(), fn)(_ptr(x), m, ctypes.byref(d), _ptr(_as_bits(out)), _ptr(ws),
+                                  ws.numel(), _stream(x.device)))
     return out
 
 
@@ -255,10 +262,12 @@ def _group_args(x, ts, outs):
     return args, outs, (x, ts, outs, ws, descs, darr, yarr)
 
 
-def gemm_group(x, ts, outs=None):
-    """y_i = x . W_i^T for the weights ts (1..4, same k) in one launch per codebook kind."""
+def gemm_group(x, ts, outs=None, rms: bool = False):
+    """y_i = x . W_i^T for the weights ts (1..4, same k) in one launch per codebook kind;
+    rms as for gemm (w12_gemm_group_rms)."""
     args, outs, keep = _group_args(x, ts, outs)
-    _check("w12_gemm_group", lib().w12_gemm_group(*args))
+    fn = "w12_gemm_group_rms" if rms else "w12_gemm_group"
+    _check(fn, getattr(lib(), fn)(*args))
     return outs
 
 
@@ -370,7 +379,7 @@ class Prepared:
             raise W12Error(self.name, st)
 
 
-def prepare_gemm(x, t: W12Tensor, out) -> Prepared:
+def prepare_gemm(x, t: W12Tensor, out, rms: bool = False) -> Prepared:
     x, out = _as_bits(x), _as_bits(out)
     m = x.shape[0]
     if x.shape[1] != t.k or tuple(out.shape) != (m, t.n):
@@ -378,12 +387,14 @@ def prepare_gemm(x, t: W12Tensor, out) -> Prepared:
     ws = workspace(max(workspace_bytes(OP_GEMM, m, t.n, t.k), 256), x.device)
     d = t.desc()
     args = (_ptr(x), m, ctypes.byref(d), _ptr(out), _ptr(ws), ws.numel(), _stream(x.device))
-    return Prepared("w12_gemm", lib().w12_gemm, args, (x, t, out, ws, d))
+    fn = "w12_gemm_rms" if rms else "w12_gemm"
+    return Prepared(fn, getattr(lib(), fn), args, (x, t, out, ws, d))
 
 
-def prepare_gemm_group(x, ts, outs) -> Prepared:
+def prepare_gemm_group(x, ts, outs, rms: bool = False) -> Prepared:
     args, outs, keep = _group_args(x, ts, outs)
-    return Prepared("w12_gemm_group", lib().w12_gemm_group, args, keep)
+    fn = "w12_gemm_group_rms" if rms else "w12_gemm_group"
+    return Prepared(fn, getattr(lib(), fn), args, keep)
 
 
 def prepare_rms(x, out) -> Prepared:

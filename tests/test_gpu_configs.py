@@ -9,9 +9,11 @@
    with planted near-ties): codebook, escape count and decode of the whole head, bytes of
    sampled row-block bands, argmax and accepted length of every row against the oracle.
 5  Decode step: 64 layers of q, k, v, o, gate, up, down + LM head drawn on the device,
-   M = 24, RMS-chained; at layers 0, 21, 42, 63 every GEMM output is checked against the
-   oracle on the captured inputs and every weight's decode against its regenerated
-   source; the final verification against the oracle's exact argmax.
+   M = 24, RMS-chained (the rescales folded into the consuming GEMMs); at layers 0, 21,
+   42, 63 every GEMM output is checked against the oracle on the captured inputs
+   (divided by the input rows' RMS where the GEMM applies it) and every weight's decode
+   against its regenerated source; the final verification against the oracle's exact
+   argmax.
 
 Bars as in the other GPU tests: bytes, bits, argmax and accepted length exact; GEMM
 outputs by oracle.gemm_accept."""
@@ -21,7 +23,7 @@ import pytest
 from oracle import w12_oracle as o
 import w12_inputs as wi
 import plant
-from gpu_util import say, to_dev, to_host
+from gpu_util import rms_reference, say, to_dev, to_host
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
@@ -190,7 +192,6 @@ def test_config5_decode_step(env):
     h, am, acc, caps = stack.step(to_dev(x0, torch), torch.from_numpy(draft).to("cuda:0"),
                                   capture=SAMPLED_LAYERS)
     torch.cuda.synchronize()
-    inputs = {"q": "h", "k": "h", "v": "h", "o": "a", "gate": "b", "up": "b", "down": "c"}
     for li in SAMPLED_LAYERS:
         cap = caps[li]
         for mi, name in enumerate(MATS):
@@ -199,12 +200,14 @@ def test_config5_decode_step(env):
             src = wi.device_layer_weight(torch, li, mi, n, k)
             assert torch.equal(w12.decode(layers[li][name]).view(torch.int16), src.view(torch.int16))
             w_host = to_host(src)
-            _check_gemm(cap[name], to_host(cap[inputs[name]]), w_host)
-        # the chain's rescaled rows have unit mean square (BF16 rounding aside)
-        for key in ("a", "b", "c"):
-            v = cap[key].float()
-            ms = (v * v).mean(dim=1)
-            assert torch.all((ms - 1).abs() < 1e-2), (li, key, ms)
+            x_in, rms = cap["in"][name]
+            x_host = to_host(x_in)
+            z, s = rms_reference(x_host, w_host) if rms else o.gemm_reference(x_host, w_host)
+            ok = o.gemm_accept(to_host(cap[name]), z, s)
+            assert ok.all(), (li, name, int((~ok).sum()))
+    # the final h (rescaled on its own) has unit mean square, BF16 rounding aside
+    v = h.float()
+    assert torch.all(((v * v).mean(dim=1) - 1).abs() < 1e-2)
     # final verification against the oracle on the captured final h
     say("config 5 LM head verify")
     w_head = to_host(wi.device_lm_head(torch, vocab, hid))

@@ -13,7 +13,7 @@ import pytest
 
 from oracle import w12_oracle as o
 import w12_inputs as wi
-from gpu_util import narrow_exponents, say, to_dev, to_host, wide_exponents
+from gpu_util import narrow_exponents, rms_reference, say, to_dev, to_host, wide_exponents
 
 pytestmark = pytest.mark.gpu
 
@@ -127,6 +127,29 @@ def test_gemm_group(env, m):
         for w, y in zip(ws, outs):
             z, s = o.gemm_reference(x, w)
             assert o.gemm_accept(to_host(y), z, s).all()
+
+
+@pytest.mark.parametrize("m", [1, 3, 4, 8, 15, 16, 24, 32])
+def test_gemm_rms(env, m):
+    """RMS GEMM (harness op of the layer chain): grouped and single launches, split and
+    whole K, against the oracle's product divided by the row's RMS."""
+    torch, w12 = env
+    g = np.random.default_rng(7300 + m)
+    for shapes in GROUPS + [[(512, 17408)]]:
+        k = shapes[0][1]
+        say("gemm rms", m, shapes)
+        ws = [wi.gaussian_bf16(sh, 0.02, g) for sh in shapes]
+        x = wi.gaussian_bf16((m, k), 3.0, g)
+        ts = [w12.encode(to_dev(w, torch)) for w in ws]
+        xt = to_dev(x, torch)
+        outs = w12.gemm_group(xt, ts, rms=True)
+        single = w12.gemm(xt, ts[0], rms=True)
+        torch.cuda.synchronize()
+        for w, y in zip(ws, outs):
+            z, s = rms_reference(x, w)
+            assert o.gemm_accept(to_host(y), z, s).all()
+        z, s = rms_reference(x, ws[0])
+        assert o.gemm_accept(to_host(single), z, s).all()
 
 
 def test_gemm_group_mixed_codebooks(env):

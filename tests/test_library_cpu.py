@@ -106,6 +106,23 @@ def test_gemm_validation(L):
     assert gemm(L, d=mis) == -7
 
 
+def test_gemm_rms_validation(L):
+    """The RMS entry points validate exactly as their plain counterparts."""
+    d = desc()
+    assert L.w12_gemm_rms(None, 1, ctypes.byref(d), FAKE, FAKE, 1 << 30, None) == -1
+    assert L.w12_gemm_rms(FAKE, 33, ctypes.byref(d), FAKE, FAKE, 1 << 30, None) == -3
+    assert L.w12_gemm_rms(FAKE, 1, ctypes.byref(desc(n=1000)), FAKE, FAKE, 1 << 30, None) == -2
+    assert L.w12_gemm_rms(FAKE, 1, ctypes.byref(d), FAKE + 8, FAKE, 1 << 30, None) == -7
+    assert L.w12_gemm_rms(FAKE, 16, ctypes.byref(desc(n=64, k=4096)), FAKE, FAKE, 0, None) == -5
+    darr = (ctypes.POINTER(B.W12Desc) * 2)(ctypes.pointer(desc()), ctypes.pointer(desc()))
+    yarr = (ctypes.c_void_p * 2)(FAKE, FAKE)
+    f = L.w12_gemm_group_rms
+    assert f(FAKE, 1, darr, 0, yarr, FAKE, 1 << 30, None) == -3
+    assert f(FAKE + 2, 1, darr, 2, yarr, FAKE, 1 << 30, None) == -7
+    odd = (ctypes.POINTER(B.W12Desc) * 2)(ctypes.pointer(desc(k=1024)), ctypes.pointer(desc(k=2048)))
+    assert f(FAKE, 1, odd, 2, yarr, FAKE, 1 << 30, None) == -2
+
+
 def test_gemm_group_validation(L):
     f = L.w12_gemm_group
     ds = [desc(n=1024, k=1024), desc(n=256, k=1024), desc(n=256, k=1024)]
