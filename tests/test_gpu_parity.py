@@ -397,3 +397,36 @@ def test_rms_rescale(env, k):
     xf = wi.bf16_bits_to_f32(x).astype(np.float64)
     ref = xf / np.sqrt(np.mean(xf * xf, axis=1, keepdims=True))
     assert np.all(np.abs(yf - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-30)
+
+
+@pytest.mark.parametrize("fused", [True, False])
+def test_decode_stack_small(env, fused):
+    """The layer chain on small shapes (hidden 512, MLP 1536, 3 layers, vocab 4096), with
+    the RMS rescale folded into the GEMMs and as separate launches: every GEMM of every
+    layer against the oracle on its captured input (divided by the input rows' RMS where
+    the GEMM applies it), and the final verification against the oracle's exact argmax."""
+    torch, w12 = env
+    from lossless_bit_weight_w12_amd.decode_step import DecodeStack, MATS
+    g = np.random.default_rng(8800 + int(fused))
+    hid, mlp, kv, vocab, m, nl = 512, 1536, 128, 4096, 24, 3
+    shapes = {"q": (hid, hid), "k": (kv, hid), "v": (kv, hid), "o": (hid, hid),
+              "gate": (mlp, hid), "up": (mlp, hid), "down": (hid, mlp)}
+    host = [{name: wi.gaussian_bf16(shapes[name], 0.02, g) for name in MATS} for _ in range(nl)]
+    layers = [{name: w12.encode(to_dev(L[name], torch)) for name in MATS} for L in host]
+    head_w = wi.gaussian_bf16((vocab, hid), 0.02, g)
+    stack = DecodeStack(layers, w12.encode(to_dev(head_w, torch)), m, fused_rms=fused)
+    x0 = wi.gaussian_bf16((m, hid), 1.0, g)
+    draft = g.integers(0, vocab, size=m).astype(np.int32)
+    say("decode stack small, fused", fused)
+    h, am, acc, caps = stack.step(to_dev(x0, torch), torch.from_numpy(draft).to("cuda:0"),
+                                  capture=range(nl))
+    torch.cuda.synchronize()
+    for li in range(nl):
+        for name in MATS:
+            x_in, rms = caps[li]["in"][name]
+            xh = to_host(x_in)
+            z, s = rms_reference(xh, host[li][name]) if rms else o.gemm_reference(xh, host[li][name])
+            assert o.gemm_accept(to_host(caps[li][name]), z, s).all(), (li, name)
+    am_ref, _ = o.argmax_exact(to_host(h), head_w)
+    assert am.cpu().numpy().tolist() == am_ref.tolist()
+    assert int(acc.item()) == o.accepted_length(am_ref, draft)
