@@ -26,13 +26,18 @@
 // m < W12_MFMA_MIN_M: VALU path, v_dot2 (2 MACs per instruction) with x pairs read from
 //   LDS as broadcast ds_read_b128; partial sums are reduced across the 4 lanes that
 //   share a row with cross-lane shuffles, then across waves.
-// Otherwise MFMA: W tile as the 16-row A operand, x as the B operand (16 or 32 columns,
-//   rows >= m zero-filled in LDS).
+// Otherwise MFMA: W tile as the 16-row A operand, x as the B operand (16 or 32 columns;
+//   padding columns carry a copy of the last x row or zeros and are never stored).
 // Escapes (exponents outside the codebook) are patched into the unpacked registers by
 //   the owning lane, walking the row-block's sorted escape list through a 4-record
 //   window in scalar registers.
 // Split-K (gridDim.y > 1): FP32 partials go to the workspace and k_splitk_reduce sums
 //   them in split order (deterministic).
+// RMS launches (p.rms): the output rows are divided by the RMS of their x rows, summed
+//   from the staged x units (harness op of the layer chain, not the W12 method).
+// The logits epilogue (verification pass 1) keeps per row-block the two largest logits,
+//   the index of the largest and the largest sum |x||w|; the full FP32 logits only when
+//   the caller passes a buffer for them.
 #pragma once
 
 #include "w12_internal.h"

@@ -43,6 +43,7 @@ namespace w12 {
 constexpr int kLimbs = 18;   // 18 x 32 bits > 542 bits (largest |sum| for K < 2^20)
 constexpr uint32_t kScreenMax = 512;   // candidates screened in FP64 (more: all go exact)
 constexpr uint32_t kGroup = 4;         // candidates screened at once, kT / kGroup threads each
+constexpr uint32_t kCache = 9728;      // block maxima kept in LDS for the candidate scan
 
 __device__ __forceinline__ bool exact_parts(uint32_t bits, int& sgn, uint32_t& mant, int& ex) {
   const uint32_t e = (bits >> 7) & 0xFFu, m = bits & 0x7Fu;
@@ -92,6 +93,7 @@ __global__ __launch_bounds__(kT) void k_verify_pass2(VerifyArgs a) {
   __shared__ int32_t s_best_v, s_best_sign;
   __shared__ uint32_t s_cnt, s_bad, s_nsurv;
   __shared__ double s_z64[kScreenMax], s_b64[kScreenMax];
+  __shared__ float s_rv[kCache], s_rs[kCache];
   const uint32_t row = blockIdx.x, tid = threadIdx.x, lane = tid & 63u, wave = tid >> 6;
   const uint16_t* xr = a.x + (uint64_t)row * a.k;
   const float* rv = a.rbmax_v + (uint64_t)row * a.nb;
@@ -102,49 +104,73 @@ __global__ __launch_bounds__(kT) void k_verify_pass2(VerifyArgs a) {
   int32_t result = -1;
   uint32_t ncand = 0, nsurv = 0;
 
-  // 1. z* and its index over the block maxima (NaN marks a non-finite block)
+  // 1. z* and its index over the block maxima (NaN marks a non-finite block); the
+  // maxima and their S are kept in LDS for the candidate scan (up to kCache blocks)
   float bv = -__builtin_inff();
   int32_t bi = 0x7FFFFFFF;
   bool bad = false;
-#pragma unroll 8
-  for (uint32_t b = tid; b < a.nb; b += kT) {
-    const float v = rv[b];
-    const int32_t i = ri[b];
+  auto take = [&](uint32_t b, float v, int32_t i, float sb) {
+    if (b < kCache) { s_rv[b] = v; s_rs[b] = sb; }
     if (v != v) bad = true;
     else if (v > bv || (v == bv && i < bi)) { bv = v; bi = i; }
-  }
-  // 2. Xmax (and finiteness of x)
-  double xm = 0.0;
+  };
+  if ((a.nb & 3u) == 0u) {   // rows start on 16-byte boundaries: four blocks per load
+    typedef float f32x4v __attribute__((ext_vector_type(4)));
+    typedef int32_t i32x4v __attribute__((ext_vector_type(4)));
 #pragma unroll 8
-  for (uint32_t i = tid; i < a.k; i += kT) {
-    const uint32_t bits = xr[i];
-    if (((bits >> 7) & 0xFFu) == 0xFFu) bad = true;
-    xm = fmax(xm, fabs((double)__uint_as_float(bits << 16)));
+    for (uint32_t b4 = tid; b4 < a.nb / 4u; b4 += kT) {
+      const f32x4v v = reinterpret_cast<const f32x4v*>(rv)[b4];
+      const i32x4v i = reinterpret_cast<const i32x4v*>(ri)[b4];
+      const f32x4v sb = reinterpret_cast<const f32x4v*>(rs)[b4];
+#pragma unroll
+      for (uint32_t j = 0; j < 4; ++j) take(4u * b4 + j, v[j], i[j], sb[j]);
+    }
+  } else {
+#pragma unroll 8
+    for (uint32_t b = tid; b < a.nb; b += kT) take(b, rv[b], ri[b], rs[b]);
   }
-  s_bv[tid] = bv;
-  s_bi[tid] = bi;
-  s_d0[tid] = xm;
+  // 2. Xmax (and finiteness of x), eight BF16 per load (k is a multiple of 128)
+  double xm = 0.0;
+#pragma unroll 4
+  for (uint32_t u = tid; u < a.k / 8u; u += kT) {
+    const u32x4 xv = reinterpret_cast<const u32x4*>(xr)[u];
+#pragma unroll
+    for (uint32_t h = 0; h < 8; ++h) {
+      const uint32_t bits = (xv[h >> 1] >> (16u * (h & 1u))) & 0xFFFFu;
+      if (((bits >> 7) & 0xFFu) == 0xFFu) bad = true;
+      xm = fmax(xm, fabs((double)__uint_as_float(bits << 16)));
+    }
+  }
+  // wave trees (fixed pattern; every lane ends with the wave's result), then the waves'
+  // results in wave order
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const float v2 = __shfl_xor(bv, off);
+    const int32_t i2 = __shfl_xor(bi, off);
+    if (v2 > bv || (v2 == bv && i2 < bi)) { bv = v2; bi = i2; }
+    xm = fmax(xm, __shfl_xor(xm, off));
+  }
   if (tid == 0) { s_cnt = 0; s_bad = 0; s_best_v = -1; }
+  if (lane == 0) { s_bv[wave] = bv; s_bi[wave] = bi; s_d0[wave] = xm; }
   __syncthreads();
   if (bad) atomicOr(&s_bad, 1u);
-  for (uint32_t off = kT / 2; off > 0; off >>= 1) {
-    if (tid < off) {
-      const float v2 = s_bv[tid + off];
-      const int32_t i2 = s_bi[tid + off];
-      if (v2 > s_bv[tid] || (v2 == s_bv[tid] && i2 < s_bi[tid])) { s_bv[tid] = v2; s_bi[tid] = i2; }
-      s_d0[tid] = fmax(s_d0[tid], s_d0[tid + off]);
-    }
-    __syncthreads();
+  bv = s_bv[0];
+  bi = s_bi[0];
+  xm = s_d0[0];
+  for (uint32_t w = 1; w < kT / 64u; ++w) {
+    if (s_bv[w] > bv || (s_bv[w] == bv && s_bi[w] < bi)) { bv = s_bv[w]; bi = s_bi[w]; }
+    xm = fmax(xm, s_d0[w]);
   }
-  const float zmax = s_bv[0];
+  __syncthreads();   // s_bad complete; s_bv / s_bi / s_d0 free again
+  const float zmax = bv;
   const double dd = (double)a.k + 64.0;
   const double gam = dd * ldexp(1.0, -23) / (1.0 - dd * ldexp(1.0, -23));
   const double wmax = ldexp(1.0, (int)a.e_max - 126);
-  const double absb = dd * ldexp(1.0, -126) * (1.0 + s_d0[0] + wmax);
+  const double absb = dd * ldexp(1.0, -126) * (1.0 + xm + wmax);
   const double infl = 1.0 + ldexp(1.0, -20);
   // B(S^) = (g (S^/(1-g) + A) + A) * infl = c1 S^ + c0
   const double c1 = gam / (1.0 - gam) * infl, c0 = (gam * absb + absb) * infl;
-  const uint32_t bstar = s_bi[0] >= 0 && (uint32_t)s_bi[0] < a.n ? (uint32_t)s_bi[0] >> 4 : 0u;
+  const uint32_t bstar = bi >= 0 && (uint32_t)bi < a.n ? (uint32_t)bi >> 4 : 0u;
   const double lo = (double)zmax - (c1 * (double)rs[bstar] + c0);
   const bool row_ok = !s_bad && __builtin_isfinite(zmax) && lo == lo;
   if (row_ok) {
@@ -152,8 +178,8 @@ __global__ __launch_bounds__(kT) void k_verify_pass2(VerifyArgs a) {
     // also reaches L
 #pragma unroll 8
     for (uint32_t b = tid; b < a.nb; b += kT) {
-      const double bb = c1 * (double)rs[b] + c0;
-      if ((double)rv[b] + bb < lo) continue;
+      const double bb = c1 * (double)(b < kCache ? s_rs[b] : rs[b]) + c0;
+      if ((double)(b < kCache ? s_rv[b] : rv[b]) + bb < lo) continue;
       const int32_t i1 = ri[b];
       cand[atomicAdd(&s_cnt, 1u)] = i1;
       if ((double)rv2[b] + bb >= lo)
