@@ -76,8 +76,10 @@ def _gemm_case(env, w, x, which):
     return yb
 
 
-# (n, k): ragged row-block counts, partial 4-column chunks, split-K, long K
-SHAPES = [(16, 128), (272, 1280), (48, 640), (64, 4096), (2080, 512)]
+# (n, k): ragged row-block counts, partial 4-column chunks, split-K, long K, and 1025
+# row-blocks over two tile columns (the many-row kernels: an odd row-block count for two
+# row-blocks per wave, waves with no column)
+SHAPES = [(16, 128), (272, 1280), (48, 640), (64, 4096), (2080, 512), (16400, 256)]
 
 
 @pytest.mark.parametrize("m", list(range(1, 33)))
@@ -107,7 +109,8 @@ def test_gemm_lut_codebook_and_escapes(env, m):
 GROUPS = [[(320, 512), (64, 512), (64, 512)],
           [(1088, 1280), (1088, 1280)],
           [(48, 640), (16, 640), (32, 640), (272, 640)],
-          [(16, 4096)]]
+          [(16, 4096)],
+          [(8192, 256), (8208, 256)]]
 
 
 @pytest.mark.parametrize("m", [1, 2, 3, 4, 8, 15, 16, 24, 32])
