@@ -329,6 +329,24 @@ def test_accepted_length_cases():
     assert o.accepted_length(am, np.array([], dtype=np.int64)) == 0
 
 
+def test_accepted_lengths_batched_cases():
+    # four requests over ten rows, worked by hand: request 0 mismatches at its second
+    # token, request 1 accepts both, request 2 mismatches at its third of four, request 3
+    # drafts nothing (its row is the bonus row only)
+    am = np.array([5, 6, 7, 1, 2, 9, 9, 9, 9, 4])
+    draft = np.array([5, 0, 7, 1, 2, 9, 9, 3, 9, 8])
+    row_off, n_draft = [0, 3, 5, 9, 10], [2, 2, 4, 0]
+    assert list(o.accepted_lengths_batched(am, draft, row_off, n_draft)) == [1, 2, 2, 0]
+    # tokens past a request's n_draft are not compared (row 2 of request 0, row 9)
+    d2 = draft.copy(); d2[2] = 99; d2[9] = 4
+    assert list(o.accepted_lengths_batched(am, d2, row_off, n_draft)) == [1, 2, 2, 0]
+    # requests are independent: fixing request 0's mismatch moves only its own length
+    d3 = draft.copy(); d3[1] = 6
+    assert list(o.accepted_lengths_batched(am, d3, row_off, n_draft)) == [2, 2, 2, 0]
+    # one request over all rows is the single-request rule
+    assert list(o.accepted_lengths_batched(am, draft, [0, 10], [10])) == [o.accepted_length(am, draft)] == [1]
+
+
 # ----------------------------------------------------------------------------- mutations
 def _pins_fail(fn):
     try:
@@ -399,3 +417,12 @@ def test_mutation_subnormal_exponent_is_caught(monkeypatch):
         return s, mant, np.where(mant < 128, ex - 1, ex)
     monkeypatch.setattr(o, "exact_parts", bad)
     assert _pins_fail(test_exact_logit_matches_rationals)
+
+
+def test_mutation_batched_accept_offsets_are_caught(monkeypatch):
+    # a request reading its draft from the batch's first row instead of its own
+    def bad(argmax, draft, row_off, n_draft):
+        return np.array([o.accepted_length(argmax[int(a):int(a) + int(nd)], draft[:int(nd)])
+                         for a, nd in zip(row_off, n_draft)], dtype=np.int64)
+    monkeypatch.setattr(o, "accepted_lengths_batched", bad)
+    assert _pins_fail(test_accepted_lengths_batched_cases)
