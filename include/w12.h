@@ -1,8 +1,9 @@
 /*
  * w12.h -- C ABI of libw12.so: the W12 lossless 12-bit weight format on MI355X
  * (gfx950): encode, bit-exact decode, the memory-bound decode/verification GEMM
- * (M = 1..32 rows of BF16 x against W12 weights, FP32 accumulate, BF16 out) and the
- * greedy verification epilogue (exact-logit argmax per row, accepted-prefix length).
+ * (M = 1..32 rows of BF16 x against W12 weights, FP32 accumulate, BF16 out; up to 128
+ * rows for several requests verified together) and the greedy verification epilogue
+ * (exact-logit argmax per row, accepted-prefix length per request).
  *
  * Sources (pages cited by title and section):
  *  - "StargazerX0/SpecPilot" (hotrepo.ai), "What it is": W12 is a 12-bit weight
@@ -63,14 +64,16 @@ typedef int32_t w12_status;
 
 #define W12_OK             0
 #define W12_ERR_NULL      -1  /* a required pointer is NULL */
-#define W12_ERR_SHAPE     -2  /* n % 16, k % 128, k >= 2^20, n == 0, size overflow */
-#define W12_ERR_RANGE     -3  /* m outside 1..32, n_draft > m, unknown op */
+#define W12_ERR_SHAPE     -2  /* n % 16, k % 128, k >= 2^20, n == 0, m * n >= 2^32 */
+#define W12_ERR_RANGE     -3  /* m outside 1..W12_MAX_M, n_draft > m, n_req outside 1..m */
 #define W12_ERR_FORMAT    -4  /* codebook not strictly ascending, e_max >= 255 */
 #define W12_ERR_WORKSPACE -5  /* workspace smaller than w12_workspace_bytes() */
 #define W12_ERR_HIP       -6  /* a HIP runtime call or kernel launch failed */
 #define W12_ERR_ALIGN     -7  /* tiles/x/w/y/ws not aligned as documented */
 
-#define W12_MAX_M 32
+/* Rows of one call: decode-sized batches (1..32) and the batched regime of several
+ * requests verified together (16 to 24 requests of a few draft tokens each). */
+#define W12_MAX_M 128
 #define W12_MAX_GROUP 4   /* weights of one w12_gemm_group call, at most */
 
 /* Host-side descriptor of one W12 tensor (device buffers + host metadata). */
@@ -133,7 +136,8 @@ w12_status w12_encode(const uint16_t* w, const w12_desc* d, void* ws, size_t ws_
 w12_status w12_decode(const w12_desc* d, uint16_t* w_out, void* stream);
 
 /* y = x . W^T with W decoded in registers ("StargazerX0/SpecPilot", "What it is"):
- * x device BF16 [m][k], y device BF16 [m][n] (row-major, 16-byte aligned), m in 1..32,
+ * x device BF16 [m][k], y device BF16 [m][n] (row-major, 16-byte aligned), m in
+ * 1..W12_MAX_M,
  * FP32 accumulation, round-to-nearest-even to BF16.  IEEE propagation for non-finite
  * inputs.  ws: w12_workspace_bytes(W12_OP_GEMM, ...) bytes (may be NULL when that is
  * 0; no initialization needed); calls that share a workspace must be ordered on one
@@ -191,7 +195,7 @@ w12_status w12_gemm_bf16_tiled(const uint16_t* x, uint32_t m, const void* w_tile
 /* Greedy verification over the LM head (review page, "The mechanisms it found":
  * certified exact-argmax LM head; "StargazerX0/SpecPilot", "Results and
  * verification": committed tokens are the target's own choice).
- * x device BF16 [m][k] (m in 1..32, finite), W12 head d (finite weights), draft
+ * x device BF16 [m][k] (m in 1..W12_MAX_M, finite), W12 head d (finite weights), draft
  * device int32 [n_draft] (n_draft <= m).  Writes argmax_out device int32 [m]: the index
  * v maximising the EXACT logit sum_k x[row,k]*W[v,k], lowest index on exact ties; and
  * accepted_out device int32 [1]: the first i < n_draft with argmax[i] != draft[i], or
@@ -206,6 +210,27 @@ w12_status w12_lmhead_verify(const uint16_t* x, uint32_t m, const w12_desc* d,
                              const int32_t* draft, uint32_t n_draft, int32_t* argmax_out,
                              int32_t* accepted_out, void* ws, size_t ws_bytes,
                              void* stream);
+
+/* Greedy verification of several requests in one pass over the LM head (review page,
+ * "Where the numbers come from": batched decoding of 16, 20 and 24 requests; "The
+ * mechanisms it found": ragged drafts, a drafter block length per request).  The
+ * argmax is w12_lmhead_verify's over all m rows of x.  Request r (0 <= r < n_req,
+ * 1 <= n_req <= m) owns rows req_off[r] .. req_off[r+1]-1, and its draft tokens are
+ * draft[req_off[r] + i] for i < req_ndraft[r].  req_off (int32 [n_req + 1]), req_ndraft
+ * (int32 [n_req]) and draft (int32 [m]) are device arrays read on the stream, so one
+ * prepared call can serve new batches.  accepted_out (device int32 [n_req]) gets, per
+ * request, the first i < req_ndraft[r] with argmax[req_off[r] + i] != draft[req_off[r]
+ * + i], or req_ndraft[r] when there is none.  An entry is valid when 0 <= req_off[r] <=
+ * req_off[r+1] <= m and 0 <= req_ndraft[r] <= req_off[r+1] - req_off[r]; an invalid one
+ * gets accepted -1 (the kernels read nothing outside the three arrays).  Rows before
+ * req_off[0] or from req_off[n_req] on belong to no request and are only argmax'd.
+ * ws: w12_workspace_bytes(W12_OP_VERIFY, m, n, k).  Errors as w12_lmhead_verify, plus
+ * W12_ERR_RANGE for n_req outside 1..m. */
+w12_status w12_lmhead_verify_batched(const uint16_t* x, uint32_t m, const w12_desc* d,
+                                     const int32_t* req_off, const int32_t* req_ndraft,
+                                     uint32_t n_req, const int32_t* draft,
+                                     int32_t* argmax_out, int32_t* accepted_out, void* ws,
+                                     size_t ws_bytes, void* stream);
 
 /* The first pass of w12_lmhead_verify with its full output (for tests of the certified
  * bound, and as an FP32-output GEMM): logits_out = FP32 z^ [m][n] and sabs_out = FP32

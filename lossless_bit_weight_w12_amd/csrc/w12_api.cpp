@@ -37,6 +37,9 @@ inline bool shape_ok(uint64_t n, uint64_t k) {
 
 inline bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
+// Element counts of [m][n] outputs and workspaces stay below 2^32 (32-bit indexing).
+inline bool mn_ok(uint32_t m, uint64_t n) { return (uint64_t)m * n < (1ull << 32); }
+
 w12_status check_desc(const w12_desc* d, bool need_data) {
   if (!d) return W12_ERR_NULL;
   if (!shape_ok(d->n, d->k)) return W12_ERR_SHAPE;
@@ -149,12 +152,11 @@ VerifyLayout verify_layout(uint32_t m, uint64_t n) {
 
 BlockMax block_max(uint8_t* base, const VerifyLayout& L) {
   BlockMax bm;
+  memset(&bm, 0, sizeof(bm));   // no accept, no request table
   bm.v = (float*)(base + L.bm_v);
   bm.v2 = (float*)(base + L.bm_v2);
   bm.s = (float*)(base + L.bm_s);
   bm.i = (int32_t*)(base + L.bm_i);
-  bm.accepted = nullptr;
-  bm.n_draft = 0;
   return bm;
 }
 
@@ -234,6 +236,7 @@ w12_status gemm_impl(const uint16_t* x, uint32_t m, const w12_desc* d, uint16_t*
   w12_status st = check_desc(d, true);
   if (st != W12_OK) return st;
   if (m < 1 || m > W12_MAX_M) return W12_ERR_RANGE;
+  if (!mn_ok(m, d->n)) return W12_ERR_SHAPE;
   const size_t need = gemm_ws_bytes(m, d->n, d->k);
   if (ws_bytes < need) return W12_ERR_WORKSPACE;
   if (need > 0 && !ws) return W12_ERR_NULL;
@@ -255,7 +258,7 @@ w12_status gemm_group_impl(const uint16_t* x, uint32_t m, const w12_desc* const*
     if (!aligned(ys[i], 16)) return W12_ERR_ALIGN;
     n_total += descs[i]->n;
   }
-  if (n_total >= kMaxN) return W12_ERR_SHAPE;
+  if (n_total >= kMaxN || !mn_ok(m, n_total)) return W12_ERR_SHAPE;
   const size_t need = group_ws_bytes(m, n_total, descs[0]->k);
   if (ws_bytes < need) return W12_ERR_WORKSPACE;
   if (need > 0 && !ws) return W12_ERR_NULL;
@@ -276,6 +279,69 @@ w12_status gemm_group_impl(const uint16_t* x, uint32_t m, const w12_desc* const*
   return hip_status(e);
 }
 
+// Both verification entry points: one request over all rows (req_off NULL, n_draft
+// tokens) or a request table (req_off, req_ndraft: n_req entries, device).
+w12_status verify_impl(const uint16_t* x, uint32_t m, const w12_desc* d, const int32_t* draft,
+                       uint32_t n_draft, const int32_t* req_off, const int32_t* req_ndraft,
+                       uint32_t n_req, int32_t* argmax_out, int32_t* accepted_out, void* ws,
+                       size_t ws_bytes, void* stream) {
+  if (!x || !argmax_out || !accepted_out || !ws) return W12_ERR_NULL;
+  w12_status st = check_desc(d, true);
+  if (st != W12_OK) return st;
+  if (m < 1 || m > W12_MAX_M) return W12_ERR_RANGE;
+  if (!mn_ok(m, d->n)) return W12_ERR_SHAPE;
+  const VerifyLayout L = verify_layout(m, d->n);
+  if (ws_bytes < L.total) return W12_ERR_WORKSPACE;
+  if (!aligned(x, 16) || !aligned(ws, 256) || !aligned(argmax_out, 4) || !aligned(accepted_out, 4))
+    return W12_ERR_ALIGN;
+  hipStream_t s = (hipStream_t)stream;
+  uint8_t* base = (uint8_t*)ws;
+  GemmPlan p = make_plan(m, d->n, d->k, EPI_LOGITS);
+  GemmArgs a;
+  memset(&a, 0, sizeof(a));
+  a.x = x;
+  a.p.seg[0] = w12_seg(d, nullptr, 0);
+  fill_params(a.p, m, d->k, d->n, 1);
+  a.logits = nullptr;          // pass 2 works from the block records and the tiles
+  a.sabs = nullptr;
+  a.bm = block_max(base, L);
+  a.bm.accepted = accepted_out;   // pass 1 sets the draft lengths, pass 2 lowers them
+  a.bm.n_draft = n_draft;
+  a.bm.req_off = req_off;
+  a.bm.req_ndraft = req_ndraft;
+  a.bm.n_req = n_req;
+  const int src = codebook_is_run(d->codebook) ? SRC_RUN : SRC_LUT;
+  hipError_t e = launch_gemm(a, src, EPI_LOGITS, p, s);
+  VerifyArgs v;
+  memset(&v, 0, sizeof(v));
+  v.x = x;
+  v.tiles = (const uint8_t*)d->tiles;
+  v.esc_off = d->esc_off;
+  v.esc = d->esc;
+  v.rbmax_v = a.bm.v;
+  v.rbmax_v2 = a.bm.v2;
+  v.rbmax_s = a.bm.s;
+  v.rbmax_i = a.bm.i;
+  v.cand = (int32_t*)(base + L.cand);
+  v.ncand = (int32_t*)(base + L.ncand);
+  v.argmax = argmax_out;
+  v.draft = draft;
+  v.accepted = accepted_out;
+  v.m = m;
+  v.n = a.p.n;
+  v.k = a.p.k;
+  v.g_cols = a.p.g_cols;
+  v.nb = a.p.nb;
+  v.n_draft = n_draft;
+  v.req_off = req_off;
+  v.req_ndraft = req_ndraft;
+  v.n_req = n_req;
+  v.e_max = d->e_max;
+  for (int i = 0; i < 4; ++i) v.lut[i] = a.p.seg[0].lut[i];
+  if (e == hipSuccess) e = launch_verify_pass2(v, s);
+  return hip_status(e);
+}
+
 }  // namespace
 
 extern "C" {
@@ -292,13 +358,13 @@ size_t w12_workspace_bytes(int op, uint32_t m, uint64_t n, uint64_t k) {
     case W12_OP_DECODE: return 0;
     case W12_OP_GEMM:
     case W12_OP_GEMM_BF16:
-      if (m < 1 || m > W12_MAX_M) return 0;
+      if (m < 1 || m > W12_MAX_M || !mn_ok(m, n)) return 0;
       return gemm_ws_bytes(m, n, k, op == W12_OP_GEMM_BF16);
     case W12_OP_VERIFY:
-      if (m < 1 || m > W12_MAX_M) return 0;
+      if (m < 1 || m > W12_MAX_M || !mn_ok(m, n)) return 0;
       return verify_layout(m, n).total;
     case W12_OP_GEMM_GROUP:
-      if (m < 1 || m > W12_MAX_M) return 0;
+      if (m < 1 || m > W12_MAX_M || !mn_ok(m, n)) return 0;
       return group_ws_bytes(m, n, k);
     default: return 0;
   }
@@ -403,6 +469,7 @@ w12_status w12_gemm_bf16(const uint16_t* x, uint32_t m, const uint16_t* w, uint6
   if (!x || !w || !y) return W12_ERR_NULL;
   if (!shape_ok(n, k)) return W12_ERR_SHAPE;
   if (m < 1 || m > W12_MAX_M) return W12_ERR_RANGE;
+  if (!mn_ok(m, n)) return W12_ERR_SHAPE;
   const size_t need = gemm_ws_bytes(m, n, k, true);
   if (ws_bytes < need) return W12_ERR_WORKSPACE;
   if (need > 0 && !ws) return W12_ERR_NULL;
@@ -432,6 +499,7 @@ w12_status w12_gemm_bf16_tiled(const uint16_t* x, uint32_t m, const void* w_tile
   if (!x || !w_tiled || !y) return W12_ERR_NULL;
   if (!shape_ok(n, k)) return W12_ERR_SHAPE;
   if (m < 1 || m > W12_MAX_M) return W12_ERR_RANGE;
+  if (!mn_ok(m, n)) return W12_ERR_SHAPE;
   const size_t need = gemm_ws_bytes(m, n, k, true);
   if (ws_bytes < need) return W12_ERR_WORKSPACE;
   if (need > 0 && !ws) return W12_ERR_NULL;
@@ -451,55 +519,22 @@ w12_status w12_gemm_bf16_tiled(const uint16_t* x, uint32_t m, const void* w_tile
 w12_status w12_lmhead_verify(const uint16_t* x, uint32_t m, const w12_desc* d, const int32_t* draft,
                              uint32_t n_draft, int32_t* argmax_out, int32_t* accepted_out,
                              void* ws, size_t ws_bytes, void* stream) {
-  if (!x || !argmax_out || !accepted_out || !ws) return W12_ERR_NULL;
   if (n_draft > 0 && !draft) return W12_ERR_NULL;
-  w12_status st = check_desc(d, true);
-  if (st != W12_OK) return st;
-  if (m < 1 || m > W12_MAX_M || n_draft > m) return W12_ERR_RANGE;
-  const VerifyLayout L = verify_layout(m, d->n);
-  if (ws_bytes < L.total) return W12_ERR_WORKSPACE;
-  if (!aligned(x, 16) || !aligned(ws, 256) || !aligned(argmax_out, 4) || !aligned(accepted_out, 4))
-    return W12_ERR_ALIGN;
-  hipStream_t s = (hipStream_t)stream;
-  uint8_t* base = (uint8_t*)ws;
-  GemmPlan p = make_plan(m, d->n, d->k, EPI_LOGITS);
-  GemmArgs a;
-  memset(&a, 0, sizeof(a));
-  a.x = x;
-  a.p.seg[0] = w12_seg(d, nullptr, 0);
-  fill_params(a.p, m, d->k, d->n, 1);
-  a.logits = nullptr;          // pass 2 works from the block records and the tiles
-  a.sabs = nullptr;
-  a.bm = block_max(base, L);
-  a.bm.accepted = accepted_out;   // pass 1 sets it to n_draft, pass 2 lowers it
-  a.bm.n_draft = n_draft;
-  const int src = codebook_is_run(d->codebook) ? SRC_RUN : SRC_LUT;
-  hipError_t e = launch_gemm(a, src, EPI_LOGITS, p, s);
-  VerifyArgs v;
-  memset(&v, 0, sizeof(v));
-  v.x = x;
-  v.tiles = (const uint8_t*)d->tiles;
-  v.esc_off = d->esc_off;
-  v.esc = d->esc;
-  v.rbmax_v = a.bm.v;
-  v.rbmax_v2 = a.bm.v2;
-  v.rbmax_s = a.bm.s;
-  v.rbmax_i = a.bm.i;
-  v.cand = (int32_t*)(base + L.cand);
-  v.ncand = (int32_t*)(base + L.ncand);
-  v.argmax = argmax_out;
-  v.draft = draft;
-  v.accepted = accepted_out;
-  v.m = m;
-  v.n = a.p.n;
-  v.k = a.p.k;
-  v.g_cols = a.p.g_cols;
-  v.nb = a.p.nb;
-  v.n_draft = n_draft;
-  v.e_max = d->e_max;
-  for (int i = 0; i < 4; ++i) v.lut[i] = a.p.seg[0].lut[i];
-  if (e == hipSuccess) e = launch_verify_pass2(v, s);
-  return hip_status(e);
+  if (m >= 1 && n_draft > m) return W12_ERR_RANGE;
+  return verify_impl(x, m, d, draft, n_draft, nullptr, nullptr, 1, argmax_out, accepted_out,
+                     ws, ws_bytes, stream);
+}
+
+w12_status w12_lmhead_verify_batched(const uint16_t* x, uint32_t m, const w12_desc* d,
+                                     const int32_t* req_off, const int32_t* req_ndraft,
+                                     uint32_t n_req, const int32_t* draft,
+                                     int32_t* argmax_out, int32_t* accepted_out, void* ws,
+                                     size_t ws_bytes, void* stream) {
+  if (!req_off || !req_ndraft || !draft) return W12_ERR_NULL;
+  if (n_req < 1 || n_req > m) return W12_ERR_RANGE;
+  if (!aligned(req_off, 4) || !aligned(req_ndraft, 4) || !aligned(draft, 4)) return W12_ERR_ALIGN;
+  return verify_impl(x, m, d, draft, 0, req_off, req_ndraft, n_req, argmax_out, accepted_out,
+                     ws, ws_bytes, stream);
 }
 
 w12_status w12_logits_f32(const uint16_t* x, uint32_t m, const w12_desc* d, float* logits_out,
@@ -508,6 +543,7 @@ w12_status w12_logits_f32(const uint16_t* x, uint32_t m, const w12_desc* d, floa
   w12_status st = check_desc(d, true);
   if (st != W12_OK) return st;
   if (m < 1 || m > W12_MAX_M) return W12_ERR_RANGE;
+  if (!mn_ok(m, d->n)) return W12_ERR_SHAPE;
   const VerifyLayout L = verify_layout(m, d->n);
   if (ws_bytes < L.total) return W12_ERR_WORKSPACE;
   if (!aligned(x, 16) || !aligned(ws, 256) || !aligned(logits_out, 16) || !aligned(sabs_out, 16))
@@ -539,7 +575,7 @@ const char* w12_status_str(w12_status s) {
     case W12_OK: return "ok";
     case W12_ERR_NULL: return "null pointer";
     case W12_ERR_SHAPE: return "bad shape (n % 16, k % 128, 0 < k < 2^20)";
-    case W12_ERR_RANGE: return "value out of range (m in 1..32, n_draft <= m)";
+    case W12_ERR_RANGE: return "value out of range (m in 1..128, n_draft <= m, n_req in 1..m)";
     case W12_ERR_FORMAT: return "bad W12 descriptor (codebook not ascending, e_max, n_esc)";
     case W12_ERR_WORKSPACE: return "workspace too small";
     case W12_ERR_HIP: return "HIP runtime error";

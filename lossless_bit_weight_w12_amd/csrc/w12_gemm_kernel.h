@@ -595,8 +595,8 @@ __global__ __launch_bounds__(NWV * 64) void k_gemm(
       }
     }
     __syncthreads();
-    if (bm.accepted && blockIdx.x == 0 && blockIdx.y == 0 && tid == 0)
-      *bm.accepted = (int32_t)bm.n_draft;   // verification pass 2 lowers it
+    if (bm.accepted && blockIdx.x == 0 && blockIdx.y == 0)
+      accept_init(bm, p.m, (uint32_t)tid, NWV * 64u);   // verification pass 2 lowers them
     for (int o = tid; o < RBW * MT; o += (NWV * 64)) {
       const int rb = o / MT, m = o % MT;
       const uint32_t b = b0 + rb;
@@ -787,8 +787,8 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_cs(
   const uint32_t n0 = 16u * b + 4u * (uint32_t)q;       // launch numbering (logits, partials)
   const uint32_t n0l = 16u * bl + 4u * (uint32_t)q;     // inside the weight (y)
   if constexpr (EPI == EPI_LOGITS) {
-    if (bm.accepted && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0)
-      *bm.accepted = (int32_t)bm.n_draft;   // verification pass 2 lowers it
+    if (bm.accepted && blockIdx.x == 0 && blockIdx.y == 0)
+      accept_init(bm, p.m, (uint32_t)tid, NT);   // verification pass 2 lowers them
     if (!bvalid) return;
 #pragma unroll
     for (int h = 0; h < NH; ++h) {
@@ -928,7 +928,9 @@ hipError_t launch_gemm_src(const GemmArgs& a, int epi, const GemmPlan& pl, hipSt
   } while (0)
   if (pl.kind == KIND_COLUMN_SYNC) {
     if (p.m <= 16) W12_CS_EPI(16);
-    else W12_CS_EPI(32);
+    else if (p.m <= 32) W12_CS_EPI(32);
+    else if (p.m <= 64) W12_CS_EPI(64);
+    else W12_CS_EPI(128);
   } else if (pl.mfma) {
     if (p.m <= 4) W12_EPI(4, 16, true);
     else if (p.m <= 8) W12_EPI(8, 16, true);

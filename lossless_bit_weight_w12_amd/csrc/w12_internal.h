@@ -63,9 +63,33 @@ struct BlockMax {
   float* v2;                // second largest (equal to v on a tie)
   float* s;                 // largest sum_k |x_k||w_k| of the row-block
   int32_t* i;               // index of v, lowest on ties
-  int32_t* accepted;        // set to n_draft by the first workgroup (NULL: untouched)
-  uint32_t n_draft;
+  int32_t* accepted;        // [n_req]: set by the first workgroup (NULL: untouched)
+  uint32_t n_draft;         // one request over all rows (req_off NULL): its draft length
+  const int32_t* req_off;   // batched: request r owns rows req_off[r] .. req_off[r+1]-1
+  const int32_t* req_ndraft;   // batched: draft tokens of request r
+  uint32_t n_req;
 };
+
+// Request r of a batched verification: its first row lo and draft length nd; false for
+// an entry outside 0 <= req_off[r] <= req_off[r+1] <= m, 0 <= nd <= its row count.
+__device__ __forceinline__ bool req_entry(const int32_t* req_off, const int32_t* req_ndraft,
+                                          uint32_t r, uint32_t m, int32_t& lo, int32_t& nd) {
+  lo = req_off[r];
+  const int32_t hi = req_off[r + 1];
+  nd = req_ndraft[r];
+  return lo >= 0 && lo <= hi && hi <= (int32_t)m && nd >= 0 && nd <= hi - lo;
+}
+
+// Starting value of each request's accepted length, written by verification pass 1:
+// the draft length (lowered by pass 2 at the first mismatch), -1 for an invalid entry.
+__device__ __forceinline__ void accept_init(const BlockMax& bm, uint32_t m, uint32_t tid,
+                                            uint32_t nthreads) {
+  for (uint32_t r = tid; r < bm.n_req; r += nthreads) {
+    int32_t lo, nd;
+    bm.accepted[r] = !bm.req_off ? (int32_t)bm.n_draft
+                                 : (req_entry(bm.req_off, bm.req_ndraft, r, m, lo, nd) ? nd : -1);
+  }
+}
 
 struct GemmArgs {
   const uint16_t* x;        // [m][k] BF16
@@ -145,8 +169,11 @@ struct VerifyArgs {
   int32_t* argmax;          // [m]
   int32_t* ncand;           // [m][2]: candidate logits, those left after the FP64 screen
                             // (diagnostic; may be NULL)
-  const int32_t* draft;
-  int32_t* accepted;
+  const int32_t* draft;     // [m] (batched) or [n_draft]
+  int32_t* accepted;        // [n_req]
+  const int32_t* req_off;   // NULL: one request over rows 0..m-1 with n_draft tokens
+  const int32_t* req_ndraft;
+  uint32_t n_req;
   uint32_t m, n, k, g_cols, nb, n_draft;
   uint32_t e_max;
   uint32_t lut[4];

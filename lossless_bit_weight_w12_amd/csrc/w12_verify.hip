@@ -35,7 +35,8 @@
 // argmax[i] != draft[i], else n_draft ("StargazerX0/SpecPilot", "Results and
 // verification": every committed token is the target's own choice): pass 1 sets it to
 // n_draft and every row i < n_draft whose argmax differs from the draft lowers it to i
-// with an atomic minimum.
+// with an atomic minimum.  Batched, each request applies the same rule to its own rows
+// (its i counted from its first row), with its own accepted length.
 #include "w12_internal.h"
 
 namespace w12 {
@@ -349,11 +350,25 @@ __global__ __launch_bounds__(kT) void k_verify_pass2(VerifyArgs a) {
       result = s_bad ? -1 : s_best_v;
     }
   }
+  __shared__ int32_t s_result;
   if (tid == 0) {
     a.argmax[row] = result;
     if (a.ncand) { a.ncand[2 * row] = (int32_t)ncand; a.ncand[2 * row + 1] = (int32_t)nsurv; }
-    // accepted-prefix length: pass 1 set it to n_draft; the first mismatching row wins
-    if (row < a.n_draft && result != a.draft[row]) atomicMin(a.accepted, (int32_t)row);
+    s_result = result;
+  }
+  __syncthreads();
+  result = s_result;
+  // accepted-prefix lengths: pass 1 set each to its draft length; the first mismatching
+  // row of a request wins.  One request over all rows, or one thread per request entry.
+  if (!a.req_off) {
+    if (tid == 0 && row < a.n_draft && result != a.draft[row]) atomicMin(a.accepted, (int32_t)row);
+  } else {
+    for (uint32_t r = tid; r < a.n_req; r += kT) {
+      int32_t lo, nd;
+      if (req_entry(a.req_off, a.req_ndraft, r, a.m, lo, nd) && (int32_t)row >= lo &&
+          (int32_t)row < lo + nd && result != a.draft[row])
+        atomicMin(a.accepted + r, (int32_t)row - lo);
+    }
   }
 }
 

@@ -15,14 +15,15 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libw12.so"
 _LIB = None
 
 OP_ENCODE, OP_DECODE, OP_GEMM, OP_GEMM_BF16, OP_VERIFY, OP_GEMM_GROUP = 0, 1, 2, 3, 4, 5
-MAX_M = 32
+MAX_M = 128
 MAX_GROUP = 4
 STATUS = {0: "W12_OK", -1: "W12_ERR_NULL", -2: "W12_ERR_SHAPE", -3: "W12_ERR_RANGE",
           -4: "W12_ERR_FORMAT", -5: "W12_ERR_WORKSPACE", -6: "W12_ERR_HIP", -7: "W12_ERR_ALIGN"}
 EXPORTS = ("w12_tiles_bytes", "w12_workspace_bytes", "w12_workspace_init", "w12_encode_count",
            "w12_encode", "w12_decode", "w12_gemm", "w12_gemm_group", "w12_gemm_rms",
            "w12_gemm_group_rms", "w12_gemm_bf16", "w12_bf16_tile",
-           "w12_gemm_bf16_tiled", "w12_lmhead_verify", "w12_logits_f32",
+           "w12_gemm_bf16_tiled", "w12_lmhead_verify", "w12_lmhead_verify_batched",
+           "w12_logits_f32",
            "w12_rms_rescale", "w12_status_str", "w12_version")
 
 
@@ -84,6 +85,10 @@ def lib():
         L.w12_lmhead_verify.restype = c_int32
         L.w12_lmhead_verify.argtypes = [c_void_p, c_uint32, ctypes.POINTER(W12Desc), c_void_p,
                                         c_uint32, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]
+        L.w12_lmhead_verify_batched.restype = c_int32
+        L.w12_lmhead_verify_batched.argtypes = [c_void_p, c_uint32, ctypes.POINTER(W12Desc), c_void_p,
+                                                c_void_p, c_uint32, c_void_p, c_void_p, c_void_p,
+                                                c_void_p, c_size_t, c_void_p]
         L.w12_logits_f32.restype = c_int32
         L.w12_logits_f32.argtypes = [c_void_p, c_uint32, ctypes.POINTER(W12Desc), c_void_p,
                                      c_void_p, c_void_p, c_size_t, c_void_p]
@@ -329,6 +334,37 @@ def lmhead_verify(x, t: W12Tensor, draft, argmax_out=None, accepted_out=None):
     return argmax_out, accepted_out
 
 
+def _batched_args(x, t: W12Tensor, req_off, req_ndraft, draft, argmax_out, accepted_out):
+    torch = _torch()
+    x = _as_bits(x)
+    m = x.shape[0]
+    n_req = int(req_ndraft.numel())
+    for name, a, size in (("req_off", req_off, n_req + 1), ("req_ndraft", req_ndraft, n_req),
+                          ("draft", draft, m)):
+        if a.dtype != torch.int32 or a.numel() != size or a.device != x.device:
+            raise ValueError(f"lmhead_verify_batched: {name} must be int32 [{size}] on {x.device}")
+    if argmax_out is None:
+        argmax_out = torch.empty(m, dtype=torch.int32, device=x.device)
+    if accepted_out is None:
+        accepted_out = torch.empty(n_req, dtype=torch.int32, device=x.device)
+    ws = workspace(workspace_bytes(OP_VERIFY, m, t.n, t.k), x.device, "verify")
+    d = t.desc()
+    args = (_ptr(x), m, ctypes.byref(d), _ptr(req_off), _ptr(req_ndraft), n_req, _ptr(draft),
+            _ptr(argmax_out), _ptr(accepted_out), _ptr(ws), ws.numel(), _stream(x.device))
+    return args, (x, t, req_off, req_ndraft, draft, argmax_out, accepted_out, ws, d)
+
+
+def lmhead_verify_batched(x, t: W12Tensor, req_off, req_ndraft, draft, argmax_out=None,
+                          accepted_out=None):
+    """Several requests verified in one pass: request r owns rows req_off[r] ..
+    req_off[r+1]-1 and drafts draft[req_off[r] + i] for i < req_ndraft[r] (int32 device
+    tensors [n_req+1], [n_req], [m]).  Returns (argmax [m], accepted [n_req]); an invalid
+    request entry gets accepted -1."""
+    args, keep = _batched_args(x, t, req_off, req_ndraft, draft, argmax_out, accepted_out)
+    _check("w12_lmhead_verify_batched", lib().w12_lmhead_verify_batched(*args))
+    return keep[5], keep[6]
+
+
 def verify_candidates(t: W12Tensor, m: int):
     """Per-row diagnostic counts of the last verification on this device's workspace:
     int32 [m, 2] = (candidate logits screened in FP64, those left after the screen; 1
@@ -414,3 +450,9 @@ def prepare_verify(x, t: W12Tensor, draft, argmax_out, accepted_out) -> Prepared
             _ptr(argmax_out), _ptr(accepted_out), _ptr(ws), ws.numel(), _stream(x.device))
     return Prepared("w12_lmhead_verify", lib().w12_lmhead_verify, args,
                     (x, t, draft, argmax_out, accepted_out, ws, d))
+
+
+def prepare_verify_batched(x, t: W12Tensor, req_off, req_ndraft, draft, argmax_out,
+                           accepted_out) -> Prepared:
+    args, keep = _batched_args(x, t, req_off, req_ndraft, draft, argmax_out, accepted_out)
+    return Prepared("w12_lmhead_verify_batched", lib().w12_lmhead_verify_batched, args, keep)

@@ -82,7 +82,8 @@ def _gemm_case(env, w, x, which):
 SHAPES = [(16, 128), (272, 1280), (48, 640), (64, 4096), (2080, 512), (16400, 256)]
 
 
-@pytest.mark.parametrize("m", list(range(1, 33)))
+# every decode size, then the batched sizes (64- and 128-column tiles, ragged in both)
+@pytest.mark.parametrize("m", list(range(1, 33)) + [33, 48, 64, 65, 100, 128])
 def test_gemm_all_m_run_codebook(env, m):
     g = np.random.default_rng(1000 + m)
     for n, k in SHAPES:
@@ -92,7 +93,7 @@ def test_gemm_all_m_run_codebook(env, m):
         _gemm_case(env, w, x, "w12")
 
 
-@pytest.mark.parametrize("m", [1, 2, 3, 4, 7, 8, 9, 15, 16, 17, 24, 31, 32])
+@pytest.mark.parametrize("m", [1, 2, 3, 4, 7, 8, 9, 15, 16, 17, 24, 31, 32, 40, 64, 120, 128])
 def test_gemm_lut_codebook_and_escapes(env, m):
     g = np.random.default_rng(2000 + m)
     for n, k in [(48, 640), (320, 1280), (64, 4096)]:
@@ -113,7 +114,7 @@ GROUPS = [[(320, 512), (64, 512), (64, 512)],
           [(8192, 256), (8208, 256)]]
 
 
-@pytest.mark.parametrize("m", [1, 2, 3, 4, 8, 15, 16, 24, 32])
+@pytest.mark.parametrize("m", [1, 2, 3, 4, 8, 15, 16, 24, 32, 64, 128])
 def test_gemm_group(env, m):
     torch, w12 = env
     g = np.random.default_rng(7000 + m)
@@ -132,7 +133,7 @@ def test_gemm_group(env, m):
             assert o.gemm_accept(to_host(y), z, s).all()
 
 
-@pytest.mark.parametrize("m", [1, 3, 4, 8, 15, 16, 24, 32])
+@pytest.mark.parametrize("m", [1, 3, 4, 8, 15, 16, 24, 32, 48, 128])
 def test_gemm_rms(env, m):
     """RMS GEMM (harness op of the layer chain): grouped and single launches, split and
     whole K, against the oracle's product divided by the row's RMS."""
@@ -175,7 +176,7 @@ def test_gemm_group_mixed_codebooks(env):
             assert o.gemm_accept(to_host(y), z, s).all()
 
 
-@pytest.mark.parametrize("m", [1, 2, 4, 5, 8, 12, 15, 16, 20, 32])
+@pytest.mark.parametrize("m", [1, 2, 4, 5, 8, 12, 15, 16, 20, 32, 64, 128])
 def test_gemm_bf16_baseline(env, m):
     g = np.random.default_rng(3000 + m)
     for n, k in SHAPES:
@@ -194,7 +195,7 @@ def tiled_reference(w):
     return np.ascontiguousarray(t).reshape(-1).view(np.uint8)
 
 
-@pytest.mark.parametrize("m", [1, 2, 4, 8, 16, 24, 32])
+@pytest.mark.parametrize("m", [1, 2, 4, 8, 16, 24, 32, 96, 128])
 def test_gemm_bf16_tiled_baseline(env, m):
     torch, w12 = env
     g = np.random.default_rng(3500 + m)
@@ -291,7 +292,7 @@ def plant_pairs(x, w, rows, g):
     return w
 
 
-@pytest.mark.parametrize("m", [1, 2, 7, 15, 16, 24, 32])
+@pytest.mark.parametrize("m", [1, 2, 7, 15, 16, 24, 32, 33, 64, 128])
 def test_verify_matches_oracle(env, m):
     torch, w12 = env
     g = np.random.default_rng(5000 + m)
@@ -315,6 +316,65 @@ def test_verify_matches_oracle(env, m):
     assert (nc[:, 0] >= 1).all() and (nc[:, 1] >= 1).all() and (nc[:, 1] <= 16 * nc[:, 0]).all()
 
 
+def test_verify_batched_requests(env):
+    """Several requests verified in one call (the batched regime: 24 requests of 1..5
+    rows, 16-24 requests in the pages' batched rows): the argmax is the oracle's on every
+    row, each valid request's accepted length is the oracle's per-request rule, an entry
+    whose draft is longer than its rows gets -1 (the documented rule for invalid
+    entries), and a second table over the same rows -- rows in no request, an empty
+    draft -- is read from the device on the next call."""
+    torch, w12 = env
+    g = np.random.default_rng(5600)
+    n, k = 4096, 512
+    rows = g.integers(1, 6, 24)
+    off = np.concatenate([[0], np.cumsum(rows)]).astype(np.int32)
+    m = int(off[-1])
+    x = wi.gaussian_bf16((m, k), 1.0, g)
+    w = plant_pairs(x, wi.gaussian_bf16((n, k), 0.02, g), list(range(0, m, 3)), g)
+    say("verify batched", m, n, k, "requests", len(rows))
+    am_ref, _ = o.argmax_exact(x, w)
+    t = w12.encode(to_dev(w, torch))
+    xt = to_dev(x, torch)
+    nd = np.maximum(rows - 1, 0).astype(np.int32)     # the last row of each is the bonus row
+    nd[3] = rows[3]                                     # a request drafting on every row
+    nd[7] = 0                                           # a request with no draft
+    draft = am_ref.astype(np.int32).copy()
+    for r in range(len(rows)):
+        p = int(g.integers(0, nd[r] + 1))                # p == nd[r]: no mismatch
+        if p < nd[r]:
+            i = off[r] + p
+            draft[i] = (draft[i] + 1 + int(g.integers(0, n - 1))) % n
+    nd_bad = nd.copy()
+    nd_bad[11] = rows[11] + 1                           # invalid: more draft than rows
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to("cuda:0")
+    off_t, nd_t, draft_t = dev(off), dev(nd_bad), dev(draft)
+    am, acc = w12.lmhead_verify_batched(xt, t, off_t, nd_t, draft_t)
+    torch.cuda.synchronize()
+    assert am.cpu().numpy().tolist() == am_ref.tolist()
+    want = o.accepted_lengths_batched(am_ref, draft, off, nd_bad)
+    want[11] = -1
+    assert acc.cpu().numpy().tolist() == want.tolist()
+    assert (want[np.arange(24) != 11] < nd[np.arange(24) != 11]).any()   # mismatches were planted
+    # a second table on the same rows through one prepared call: new device contents;
+    # rows 0-1 and the padding entries (empty requests at row m) belong to no request
+    call = w12.prepare_verify_batched(xt, t, off_t, nd_t, draft_t, am, acc)
+    off2 = np.array([2, m // 4, m // 2, m - 3, m], dtype=np.int32)
+    nd2 = np.array([m // 4 - 2, 0, 2, 3], dtype=np.int32)
+    off_t.copy_(torch.from_numpy(np.concatenate([off2, np.full(len(off) - len(off2), m, np.int32)])))
+    nd_t.copy_(torch.from_numpy(np.concatenate([nd2, np.zeros(len(nd) - len(nd2), np.int32)])))
+    call()
+    torch.cuda.synchronize()
+    got = acc.cpu().numpy()
+    assert got[:4].tolist() == o.accepted_lengths_batched(am_ref, draft, off2, nd2).tolist()
+    assert (got[4:] == 0).all()
+    # one request over every row is the single-request entry point
+    am1, acc1 = w12.lmhead_verify(xt, t, dev(draft[:m]))
+    am2, acc2 = w12.lmhead_verify_batched(xt, t, dev([0, m]), dev([m]), dev(draft))
+    torch.cuda.synchronize()
+    assert am1.cpu().tolist() == am2.cpu().tolist() == am_ref.tolist()
+    assert int(acc1.item()) == int(acc2.item()) == o.accepted_length(am_ref, draft)
+
+
 def _certified_bound(s_hat, k, e_max, xmax):
     """The bound the verification relies on, as its header states it: any summation
     order of K exact products, each addition with relative error below 2^-23, at most
@@ -326,7 +386,7 @@ def _certified_bound(s_hat, k, e_max, xmax):
 
 
 @pytest.mark.parametrize("m,kind", [(1, "gauss"), (3, "wide"), (7, "gauss"), (16, "outliers"),
-                                    (24, "gauss"), (32, "wide")])
+                                    (24, "gauss"), (32, "wide"), (64, "outliers"), (128, "wide")])
 def test_verify_pass1_error_within_certified_bound(env, m, kind):
     """The FP32 logits of verification pass 1 (w12_logits_f32: the same kernels and
     summation order) stay within the certified bound of the exact values on every

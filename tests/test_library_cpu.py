@@ -53,7 +53,8 @@ def test_bad_shapes_report_zero(L, n, k):
 
 def test_workspace_sizes(L):
     assert w12.workspace_bytes(w12.OP_GEMM, 0, 1024, 1024) == 0
-    assert w12.workspace_bytes(w12.OP_GEMM, 33, 1024, 1024) == 0
+    assert w12.workspace_bytes(w12.OP_GEMM, w12.MAX_M + 1, 1024, 1024) == 0
+    assert w12.workspace_bytes(w12.OP_VERIFY, w12.MAX_M, 1 << 25, 128) == 0   # m * n >= 2^32
     assert w12.workspace_bytes(99, 1, 1024, 1024) == 0
     n, k, m = 151936, 5120, 16
     v = w12.workspace_bytes(w12.OP_VERIFY, m, n, k)
@@ -90,7 +91,9 @@ def test_gemm_validation(L):
     assert gemm(L, d=desc(k=1000)) == -2
     assert gemm(L, d=desc(k=1 << 20)) == -2
     assert gemm(L, m=0) == -3
-    assert gemm(L, m=33) == -3
+    assert gemm(L, m=129) == -3
+    assert gemm(L, m=128, d=desc(n=1 << 25, k=128)) == -2      # m * n >= 2^32
+    assert gemm(L, m=127, d=desc(n=1 << 25, k=128), x=FAKE + 2) == -7   # shape passes
     assert gemm(L, d=desc(cb=(5,) * 16)) == -4
     assert gemm(L, d=desc(cb=tuple(range(115, 99, -1)))) == -4
     assert gemm(L, d=desc(e_max=255)) == -4
@@ -110,7 +113,7 @@ def test_gemm_rms_validation(L):
     """The RMS entry points validate exactly as their plain counterparts."""
     d = desc()
     assert L.w12_gemm_rms(None, 1, ctypes.byref(d), FAKE, FAKE, 1 << 30, None) == -1
-    assert L.w12_gemm_rms(FAKE, 33, ctypes.byref(d), FAKE, FAKE, 1 << 30, None) == -3
+    assert L.w12_gemm_rms(FAKE, 129, ctypes.byref(d), FAKE, FAKE, 1 << 30, None) == -3
     assert L.w12_gemm_rms(FAKE, 1, ctypes.byref(desc(n=1000)), FAKE, FAKE, 1 << 30, None) == -2
     assert L.w12_gemm_rms(FAKE, 1, ctypes.byref(d), FAKE + 8, FAKE, 1 << 30, None) == -7
     assert L.w12_gemm_rms(FAKE, 16, ctypes.byref(desc(n=64, k=4096)), FAKE, FAKE, 0, None) == -5
@@ -134,7 +137,7 @@ def test_gemm_group_validation(L):
     assert f(FAKE, 1, darr, 3, None, FAKE, big, None) == -1
     assert f(FAKE, 1, darr, 0, yarr, FAKE, big, None) == -3
     assert f(FAKE, 1, darr, 5, yarr, FAKE, big, None) == -3
-    assert f(FAKE, 33, darr, 3, yarr, FAKE, big, None) == -3
+    assert f(FAKE, 129, darr, 3, yarr, FAKE, big, None) == -3
     assert f(FAKE, 1, darr, 3, yarr, FAKE, 0, None) == -5           # split-K needs partials
     assert f(FAKE + 2, 1, darr, 3, yarr, FAKE, big, None) == -7
     yarr[2] = FAKE + 8
@@ -155,7 +158,7 @@ def test_gemm_bf16_validation(L):
     f = L.w12_gemm_bf16
     assert f(None, 1, FAKE, 1024, 1024, FAKE, FAKE, 1 << 30, None) == -1
     assert f(FAKE, 1, FAKE, 1000, 1024, FAKE, FAKE, 1 << 30, None) == -2
-    assert f(FAKE, 40, FAKE, 1024, 1024, FAKE, FAKE, 1 << 30, None) == -3
+    assert f(FAKE, 129, FAKE, 1024, 1024, FAKE, FAKE, 1 << 30, None) == -3
     assert f(FAKE, 1, FAKE + 8, 1024, 1024, FAKE, FAKE, 1 << 30, None) == -7
     assert f(FAKE, 1, FAKE, 1024, 1024, FAKE + 8, FAKE, 1 << 30, None) == -7
 
@@ -182,6 +185,26 @@ def test_verify_validation(L):
     assert f(FAKE, 4, ctypes.byref(d), FAKE, 4, FAKE, FAKE, FAKE, 100, None) == -5
 
 
+def test_verify_batched_validation(L):
+    f = L.w12_lmhead_verify_batched
+    d = desc(n=2048, k=512)
+    big = 1 << 34
+    #      x     m  desc            off   nd    nreq draft argmax acc   ws    wsb
+    assert f(None, 8, ctypes.byref(d), FAKE, FAKE, 3, FAKE, FAKE, FAKE, FAKE, big, None) == -1
+    assert f(FAKE, 8, ctypes.byref(d), None, FAKE, 3, FAKE, FAKE, FAKE, FAKE, big, None) == -1
+    assert f(FAKE, 8, ctypes.byref(d), FAKE, None, 3, FAKE, FAKE, FAKE, FAKE, big, None) == -1
+    assert f(FAKE, 8, ctypes.byref(d), FAKE, FAKE, 3, None, FAKE, FAKE, FAKE, big, None) == -1
+    assert f(FAKE, 8, ctypes.byref(d), FAKE, FAKE, 3, FAKE, None, FAKE, FAKE, big, None) == -1
+    assert f(FAKE, 8, ctypes.byref(d), FAKE, FAKE, 3, FAKE, FAKE, None, FAKE, big, None) == -1
+    assert f(FAKE, 8, ctypes.byref(d), FAKE, FAKE, 0, FAKE, FAKE, FAKE, FAKE, big, None) == -3
+    assert f(FAKE, 8, ctypes.byref(d), FAKE, FAKE, 9, FAKE, FAKE, FAKE, FAKE, big, None) == -3   # n_req > m
+    assert f(FAKE, 129, ctypes.byref(d), FAKE, FAKE, 3, FAKE, FAKE, FAKE, FAKE, big, None) == -3
+    assert f(FAKE, 8, ctypes.byref(d), FAKE + 2, FAKE, 3, FAKE, FAKE, FAKE, FAKE, big, None) == -7
+    assert f(FAKE, 8, ctypes.byref(d), FAKE, FAKE, 3, FAKE, FAKE, FAKE, FAKE, 100, None) == -5
+    assert f(FAKE, 8, ctypes.byref(desc(n=1000, k=512)), FAKE, FAKE, 3, FAKE, FAKE, FAKE, FAKE, big,
+             None) == -2
+
+
 def test_logits_f32_validation(L):
     f = L.w12_logits_f32
     d = desc(n=2048, k=512)
@@ -191,7 +214,7 @@ def test_logits_f32_validation(L):
     assert f(FAKE, 4, ctypes.byref(d), FAKE, FAKE, None, big, None) == -1
     assert f(FAKE, 4, None, FAKE, FAKE, FAKE, big, None) == -1
     assert f(FAKE, 0, ctypes.byref(d), FAKE, FAKE, FAKE, big, None) == -3
-    assert f(FAKE, 33, ctypes.byref(d), FAKE, FAKE, FAKE, big, None) == -3
+    assert f(FAKE, 129, ctypes.byref(d), FAKE, FAKE, FAKE, big, None) == -3
     assert f(FAKE, 4, ctypes.byref(desc(n=1000, k=512)), FAKE, FAKE, FAKE, big, None) == -2
     assert f(FAKE, 4, ctypes.byref(d), FAKE, FAKE, FAKE, 100, None) == -5
     assert f(FAKE, 4, ctypes.byref(d), FAKE + 8, FAKE, FAKE, big, None) == -7
