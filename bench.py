@@ -38,6 +38,7 @@ sys.path.insert(0, ROOT)
 METRIC = "W12 GEMM achieved HBM GB/s (% of peak) and speedup vs BF16, M=1..32"
 PEAK_GBPS = 8000.0          # MI355X HBM3E peak
 MS = (1, 4, 8, 16, 32)
+BATCHED_MS = (64, 128)      # batched regime (several requests' rows at once), reported beside
 N_GU, K_GU = 34816, 5120
 N_DN, K_DN = 5120, 17408
 
@@ -175,6 +176,17 @@ def time_calls(torch, fn, reps: int, warmup: int = 3) -> float:
     return e0.elapsed_time(e1) / reps
 
 
+def _rot(fn):
+    """A call-counting wrapper: fn(i) with i = 0, 1, 2, ... on successive calls (to
+    rotate weight copies under time_calls)."""
+    state = {"i": 0}
+
+    def call():
+        fn(state["i"])
+        state["i"] += 1
+    return call
+
+
 def build_decode_stack(torch, w12, wi, np, dev, head=None):
     """The 64-layer stack (+ LM head) of the decode step, drawn on the device and
     encoded by the library, prepared for M = 24 with the seeded draft."""
@@ -241,8 +253,36 @@ def extra_workloads(torch, w12, wi, np, dev, args):
         "verify_overhead_us": round((ms_verify - ms_gemm16) * 1e3, 1),
         "accepted": accepted, "planted_mismatch_at": p,
         "accepted_matches_plant": accepted == p}
-    log(f"bench: verify {verify['us_per_verify']} us ({verify['gbps_verify']} GB/s); "
-        f"building the 64-layer stack ...")
+    log(f"bench: verify {verify['us_per_verify']} us ({verify['gbps_verify']} GB/s)")
+
+    # ---- batched verification: 24 requests x 5 rows in one pass over the head
+    xb = torch.from_numpy(wi.batched_verify_x().view(np.int16)).to(dev)
+    mb = xb.shape[0]
+    off, nd, pb, rb = wi.batched_verify_table(vocab)
+    amb, _ = w12.lmhead_verify(xb, head, torch.zeros(0, dtype=torch.int32, device=dev))
+    draft_b = amb.cpu().numpy().astype(np.int32)
+    for r in range(len(nd)):
+        if pb[r] < nd[r]:
+            i = off[r] + pb[r]
+            draft_b[i] = (draft_b[i] + 1 + rb[r]) % vocab
+    t_i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
+    amb_out = torch.empty(mb, dtype=torch.int32, device=dev)
+    accb_out = torch.empty(len(nd), dtype=torch.int32, device=dev)
+    bcall = w12.prepare_verify_batched(xb, head, t_i32(off), t_i32(nd), t_i32(draft_b), amb_out,
+                                       accb_out)
+    ms_vb = time_calls(torch, bcall, 30)
+    accb = accb_out.cpu().numpy()
+    vb_bytes = head.nbytes() + 2 * mb * hid + 2 * 16 * mb * (vocab // 16) + 4 * mb + 4 * len(nd)
+    verify_batched = {
+        "workload": f"LM head [{vocab}x{hid}] W12, {len(nd)} requests x {mb // len(nd)} rows "
+                    f"(M={mb}), per-request greedy verify of {int(nd[0])}-token drafts",
+        "us_per_verify": round(ms_vb * 1e3, 1),
+        "gbps_verify": round(vb_bytes / (ms_vb * 1e-3) / 1e9, 1),
+        "us_per_request": round(ms_vb * 1e3 / len(nd), 2),
+        "accepted_match_plants": bool((accb == np.minimum(pb, nd)).all()),
+        "argmax_equals_single_request_call": bool(torch.equal(amb_out, amb))}
+    verify["batched"] = verify_batched
+    log(f"bench: batched verify {verify_batched}; building the 64-layer stack ...")
 
     # ---- decode step, 64 layers + head, M = 24
     t0 = time.time()
@@ -493,6 +533,23 @@ def main():
                 "us_bf16_tiled": round(res["bf16t"], 2),
                 "gbps_bf16_tiled": round(bf16_bytes(tl[0].n, tl[0].k, m) / res["bf16t"] / 1e3, 1),
                 "speedup_vs_bf16_tiled": round(res["bf16t"] / res["w12"], 3)}
+    # batched regime: the same matrices at 64 and 128 rows (several requests' draft
+    # rows verified together), W12 against the tiled BF16 kernel
+    batched = {}
+    for m in BATCHED_MS:
+        for name, tl, btl, k in (("gate_up", t_gu, bt_gu, K_GU), ("down", t_dn, bt_dn, K_DN)):
+            xb = torch.from_numpy(wi.activations(3, wi.T_X if name == "gate_up" else wi.T_X2,
+                                                 m, k).view(np.int16)).to(dev)
+            yb_ = torch.empty((m, tl[0].n), dtype=torch.bfloat16, device=dev)
+            nn = tl[0].n
+            us_w = 1e3 * time_calls(torch, _rot(lambda i: w12.gemm(xb, tl[i % len(tl)], out=yb_)), reps)
+            us_b = 1e3 * time_calls(torch, _rot(lambda i: w12.gemm_bf16_tiled(
+                xb, btl[i % len(btl)], nn, k, out=yb_)), reps)
+            batched[f"M{m}_{name}"] = {
+                "us_w12": round(us_w, 2), "gbps_w12": round(gemm_bytes(tl[0], m) / us_w / 1e3, 1),
+                "us_bf16_tiled": round(us_b, 2), "speedup_vs_bf16_tiled": round(us_b / us_w, 3)}
+    log(f"bench: batched GEMMs {batched}")
+
     # dominant kernel = the (M, matrix) GEMM with the largest share of the step
     dom_key = max(per, key=lambda kk: per[kk]["us_w12"])
     dom = per[dom_key]
@@ -528,6 +585,7 @@ def main():
         "bf16_tiled_gbps": round(step_bytes_bf16 / (ms_bf16t * 1e-3) / 1e9, 1),
         "w12_equals_bf16_bitwise": same,
         "per_gemm": per,
+        "batched_gemm": batched,
         "encode": encode_info,
         "roofline": roofline,
         "cpu_baseline": None,

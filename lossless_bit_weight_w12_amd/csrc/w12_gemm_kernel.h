@@ -53,8 +53,11 @@ constexpr uint32_t kAbs2 = 0x7FFF7FFFu;   // clears the sign bits of two packed 
 // Plain BF16 sources (row-major or tiled): no decode, no escapes.
 constexpr bool plain_bf16(int src) { return src == SRC_BF16 || src == SRC_BF16T; }
 
-constexpr int kXsStride = 128 + 8;   // BF16 per LDS row of one wave's x column (+16 B pad:
-                                     // no bank conflicts for the MFMA B reads)
+// BF16 per LDS row of an x column: +16 B pad (3.2 bank-conflict cycles per MFMA B read,
+// measured; +32 B has none but is no faster up to 64 columns), +32 B for the 64- and
+// 128-column tiles of k_gemm_cs, where the B reads bound the kernel (4% at 128 columns).
+constexpr int kXsStride = 128 + 8;
+constexpr int xs_stride(int mt) { return mt >= 64 ? 128 + 16 : kXsStride; }
 
 
 // The weight a row-block belongs to, selected from the launch's table with constant
@@ -655,7 +658,8 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_cs(
   constexpr bool kS = EPI == EPI_LOGITS;   // also accumulate S = sum |x||w| per output
   constexpr int NT = NW * 64;
   constexpr int kUnits = (16 * MT + NT - 1) / NT;     // 16-byte x units per thread
-  __shared__ __align__(16) uint16_t xs[2][MT * kXsStride];
+  constexpr int kXs = xs_stride(MT);
+  __shared__ __align__(16) uint16_t xs[2][MT * kXs];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -705,7 +709,7 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_cs(
       // (a compile-time true test when the units divide evenly: no exec-masked branch)
       if (kUnits * NT == 16 * MT || u < 16u * MT) {
         const uint32_t m = u >> 4, cu = u & 15u;
-        *reinterpret_cast<u32x4*>(&xs[slot][m * kXsStride + 8u * cu]) = xr[i];
+        *reinterpret_cast<u32x4*>(&xs[slot][m * kXs + 8u * cu]) = xr[i];
       }
     }
   };
@@ -721,7 +725,7 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_cs(
       const u32x4 av = {P[4 * j], P[4 * j + 1], P[4 * j + 2], P[4 * j + 3]};
 #pragma unroll
       for (int h = 0; h < NH; ++h) {
-        const u32x4 xv = *reinterpret_cast<const u32x4*>(xrow + (16 * h + r) * kXsStride + 32 * j);
+        const u32x4 xv = *reinterpret_cast<const u32x4*>(xrow + (16 * h + r) * kXs + 32 * j);
         acc[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av),
                                                          __builtin_bit_cast(bf16x8_t, xv), acc[h], 0, 0, 0);
         if constexpr (kS)

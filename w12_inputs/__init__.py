@@ -163,6 +163,28 @@ def verify_mismatch(b: int, vocab: int, m: int = 16):
     return p, r
 
 
+# Batched verification: 24 requests (the largest of the batched request counts the
+# pages report, 16, 20 and 24) of 5 rows each: 4 drafted tokens and the bonus row.
+BATCHED_REQUESTS, BATCHED_ROWS = 24, 5
+
+
+def batched_verify_x(n_req: int = BATCHED_REQUESTS, rows: int = BATCHED_ROWS,
+                     k: int = 5120) -> np.ndarray:
+    """Hidden rows of the batched verification, request after request (~N(0,1) BF16)."""
+    return gaussian_bf16((n_req * rows, k), 1.0, rng(4, T_X, 200))
+
+
+def batched_verify_table(vocab: int, n_req: int = BATCHED_REQUESTS, rows: int = BATCHED_ROWS):
+    """Request table and planted mismatches: row offsets [n_req + 1], draft lengths
+    [n_req] (rows - 1 each), and per request the first mismatch position p in
+    0..rows-1 (rows - 1 = none) with the offset r in [0, vocab - 2] of the wrong token."""
+    off = (np.arange(n_req + 1) * rows).astype(np.int32)
+    nd = np.full(n_req, rows - 1, dtype=np.int32)
+    p = rng(4, T_P, 200).integers(0, rows, n_req)
+    r = rng(4, T_R, 200).integers(0, vocab - 1, n_req)
+    return off, nd, p, r
+
+
 def tie_rng(b: int, row: int) -> np.random.Generator:
     """Random choices of the near-tie plant for row `row` of batch b."""
     return rng(4, T_TIE, 1000 * b + row)
