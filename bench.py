@@ -356,6 +356,8 @@ def main():
                     help="skip the HIP-graph replay of the decode step")
     ap.add_argument("--profile-decode", action="store_true",
                     help="build the 64-layer decode stack, run --steps steps and exit (for rocprofv3)")
+    ap.add_argument("--profile-batched", action="store_true",
+                    help="run --steps batched GEMMs (M = 64, 128) and batched verifications and exit")
     ap.add_argument("--profile-verify", action="store_true",
                     help="run --steps LM-head verifications (M = 16) and exit (for rocprofv3)")
     args = ap.parse_args()
@@ -380,6 +382,28 @@ def main():
             w12.lmhead_verify(x16, head, draft)
         torch.cuda.synchronize()
         log("bench: profile-verify run done")
+        return
+    if args.profile_batched:
+        # batched regime: the MLP matrices at 64 and 128 rows, then the 24-request
+        # verification on the LM head
+        for name, t, k in (("gate_up", (N_GU, K_GU), wi.T_W), ("down", (N_DN, K_DN), wi.T_W2)):
+            tt = w12.encode(torch.from_numpy(wi.weight(3, k, t).view(np.int16)).to(dev))
+            for m in BATCHED_MS:
+                xb = torch.from_numpy(wi.activations(3, wi.T_X, m, t[1]).view(np.int16)).to(dev)
+                yb_ = torch.empty((m, t[0]), dtype=torch.bfloat16, device=dev)
+                for _ in range(args.steps):
+                    w12.gemm(xb, tt, out=yb_)
+            del tt
+        c5 = wi.CONFIG_SHAPES[5]
+        head = w12.encode(wi.device_lm_head(torch, c5["vocab"], c5["hidden"]))
+        xb = torch.from_numpy(wi.batched_verify_x().view(np.int16)).to(dev)
+        off, nd, _, _ = wi.batched_verify_table(c5["vocab"])
+        t_i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
+        draft = torch.zeros(xb.shape[0], dtype=torch.int32, device=dev)
+        for _ in range(args.steps):
+            w12.lmhead_verify_batched(xb, head, t_i32(off), t_i32(nd), draft)
+        torch.cuda.synchronize()
+        log("bench: profile-batched run done")
         return
     if args.profile_decode:
         stack, h0 = build_decode_stack(torch, w12, wi, np, dev)
