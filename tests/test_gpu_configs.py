@@ -124,6 +124,24 @@ def test_config3_mlp_block(env, name):
         _check_gemm(yb, x, w)
 
 
+@pytest.mark.parametrize("name", ["gate_up", "down"])
+def test_config3_mlp_block_batched(env, name):
+    """The MLP matrices at the batched sizes the bench times (M = 64 and 128: several
+    requests' draft rows at once), every output against the oracle, W12 and BF16."""
+    torch, w12 = env
+    w = wi.weight(3, wi.T_W if name == "gate_up" else wi.T_W2, wi.CONFIG_SHAPES[3][name])
+    n, k = w.shape
+    wd = to_dev(w, torch)
+    t = w12.encode(wd)
+    wt = w12.bf16_tile(wd)
+    for m in (64, 128):
+        say("config 3 batched", name, "m", m)
+        x = wi.activations(3, wi.T_X if name == "gate_up" else wi.T_X2, m, k)
+        xt = to_dev(x, torch)
+        _check_gemm(w12.gemm(xt, t), x, w)
+        _check_gemm(w12.gemm_bf16_tiled(xt, wt, n, k), x, w)
+
+
 @pytest.fixture(scope="module")
 def lm_head():
     """Workload 4's head with the 32 near-tie rows of batches 1-2 planted, and the three
@@ -164,6 +182,32 @@ def test_config4_lm_head_verify(env, lm_head):
         say("config 4 batch", b, "GPU candidates / left after the FP64 screen",
             nc.tolist())
         assert (nc[:, 0] >= 1).all() and (nc[:, 1] >= 1).all()
+
+
+def test_config4_lm_head_verify_batched(env, lm_head):
+    """Workload 4's head (near ties planted) verifying 24 requests x 5 rows in one call,
+    as the bench times it: every row's argmax is the oracle's exact-logit argmax and every
+    request's accepted length the oracle's per-request rule, with the planted first
+    mismatches."""
+    torch, w12 = env
+    w, _ = lm_head
+    vocab = w.shape[0]
+    t = w12.encode(to_dev(w, torch))
+    x = wi.batched_verify_x()
+    off, nd, pb, rb = wi.batched_verify_table(vocab)
+    say("config 4 batched: oracle argmax of", x.shape[0], "rows")
+    am_ref, _ = o.argmax_exact(x, w)
+    draft = am_ref.astype(np.int32).copy()
+    for r in range(len(nd)):
+        if pb[r] < nd[r]:
+            i = off[r] + pb[r]
+            draft[i] = (draft[i] + 1 + rb[r]) % vocab
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to("cuda:0")
+    am, acc = w12.lmhead_verify_batched(to_dev(x, torch), t, dev(off), dev(nd), dev(draft))
+    torch.cuda.synchronize()
+    assert am.cpu().numpy().tolist() == am_ref.tolist()
+    want = o.accepted_lengths_batched(am_ref, draft, off, nd)
+    assert acc.cpu().numpy().tolist() == want.tolist() == np.minimum(pb, nd).tolist()
 
 
 SAMPLED_LAYERS = (0, 21, 42, 63)
