@@ -17,8 +17,13 @@ constexpr uint64_t kMaxN = 1ull << 31;
 #define W12_TARGET_WG 1024
 #endif
 #ifndef W12_CS_FEW_NW
-#define W12_CS_FEW_NW 4
+#define W12_CS_FEW_NW 5
 #endif
+#ifndef W12_CS_NW
+#define W12_CS_NW 5
+#endif
+static_assert((W12_CS_NW == 4 || W12_CS_NW == 5) && (W12_CS_FEW_NW == 4 || W12_CS_FEW_NW == 5),
+              "column-synchronous launches are instantiated for 4 and 5 waves");
 #ifndef W12_NS_CAP
 #define W12_NS_CAP 8
 #endif
@@ -70,10 +75,18 @@ inline bool codebook_is_run(const uint8_t* c) {
 // Kernel choice, measured on the MLP-block shapes (gate+up 2176 row-blocks x 40 tile
 // columns, down 320 x 136):
 //  - m < W12_MFMA_MIN_M: VALU path, waves stream their own columns;
-//  - few row-blocks (long K): column-synchronous MFMA with 8 waves per workgroup (x is
-//    shared by 8 row-blocks; at m = 32 the down projection goes 3.1 -> 4.3 TB/s);
+//  - few row-blocks (long K): column-synchronous MFMA, K split;
 //  - many row-blocks: wave-column MFMA below m = 16 (no per-column barrier), column-
-//    synchronous with 4 waves from m = 16 (x traffic dominates).
+//    synchronous from m = 16 (x traffic dominates).
+// Column-synchronous workgroups take 5 row-blocks (5 waves).  Every workgroup of a launch
+// is resident at once, so the CU holding the most row-blocks sets the time: gate+up with
+// 4 per workgroup is 544 workgroups, up to 3 on a CU (12 row-blocks against 8.5 on
+// average); with 5 it is 436, at most 2 (10).  Measured: gate+up M16 / M24 / M32 5.44 /
+// 4.87 / 4.60 -> 5.82 / 5.21 / 5.13 TB/s, and the split down launches (64 groups x 8
+// splits = 2 workgroups per CU) M32 4.18 -> 4.44; 6 or 7 waves (12 and 14 row-blocks per
+// CU) are slower, 3 ties on gate+up and loses on down.  The logits epilogue and the
+// 128-column x tiles (m > 64: 74 KB of LDS per workgroup; gate+up M128 135 -> 164 us with
+// 5) keep 4.
 GemmPlan make_plan(uint32_t m, uint64_t n, uint64_t k, int epi, bool bf16_src = false) {
   GemmPlan p;
   const uint64_t nb = n / 16, g = k / 128;
@@ -85,7 +98,7 @@ GemmPlan make_plan(uint32_t m, uint64_t n, uint64_t k, int epi, bool bf16_src = 
   const bool few_rows = nb < W12_RBW2_MIN_NB;
   if (p.mfma && (few_rows || m >= 16)) {
     p.kind = KIND_COLUMN_SYNC;
-    p.nw = few_rows ? W12_CS_FEW_NW : 4;
+    p.nw = epi != EPI_BF16 || m > 64 ? 4 : (few_rows ? W12_CS_FEW_NW : W12_CS_NW);
     p.n_rbg = (uint32_t)((nb + p.nw - 1) / p.nw);
     units = (uint64_t)p.n_rbg * p.nw / 4;     // in 4-wave workgroup equivalents
     min_cols = W12_CS_MIN_COLS;

@@ -918,8 +918,8 @@ hipError_t launch_gemm_src(const GemmArgs& a, int epi, const GemmPlan& pl, hipSt
   } while (0)
 #define W12_CS(MT_, EPI_)                                                                     \
   do {                                                                                        \
-    if (pl.nw == 8)                                                                           \
-      hipLaunchKernelGGL((k_gemm_cs<MT_, 8, SRC, EPI_>), grid, dim3(512), 0, s, a.x, f32,     \
+    if (pl.nw == 5)                                                                           \
+      hipLaunchKernelGGL((k_gemm_cs<MT_, 5, SRC, EPI_>), grid, dim3(320), 0, s, a.x, f32,     \
                          a.sabs, a.bm, p);                         \
     else                                                                                      \
       hipLaunchKernelGGL((k_gemm_cs<MT_, 4, SRC, EPI_>), grid, dim3(256), 0, s, a.x, f32,     \
