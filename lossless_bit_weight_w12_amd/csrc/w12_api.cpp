@@ -78,13 +78,20 @@ inline bool codebook_is_run(const uint8_t* c) {
 //  - few row-blocks (long K): column-synchronous MFMA, K split;
 //  - many row-blocks: wave-column MFMA below m = 16 (no per-column barrier), column-
 //    synchronous from m = 16 (x traffic dominates).
+// W12 launches with the BF16 epilogue take the column-synchronous kernel at every m: with
+// 5-wave workgroups it beats the wave-column kernels there too (gate+up M1 / M4 / M8
+// 47.2 / 47.5 / 48.6 -> 43.4 / 43.5 / 43.5 us, down M1 26.6 -> 25.8 us).  The BF16
+// baselines and the logits epilogue keep the wave-column kernels below m = 16, which are
+// faster for them (tiled BF16 gate+up M1 57.1 us against 61.9; LM-head verification M1
+// 193 us against 201).
 // Column-synchronous workgroups take 5 row-blocks (5 waves).  Every workgroup of a launch
 // is resident at once, so the CU holding the most row-blocks sets the time: gate+up with
 // 4 per workgroup is 544 workgroups, up to 3 on a CU (12 row-blocks against 8.5 on
 // average); with 5 it is 436, at most 2 (10).  Measured: gate+up M16 / M24 / M32 5.44 /
 // 4.87 / 4.60 -> 5.82 / 5.21 / 5.13 TB/s, and the split down launches (64 groups x 8
 // splits = 2 workgroups per CU) M32 4.18 -> 4.44; 6 or 7 waves (12 and 14 row-blocks per
-// CU) are slower, 3 ties on gate+up and loses on down.  The logits epilogue and the
+// CU) are slower, 3 ties on gate+up and loses on down, 9 or 10 (one workgroup per CU)
+// tie with 5 and 8 (272 workgroups) loses.  The logits epilogue and the
 // 128-column x tiles (m > 64: 74 KB of LDS per workgroup; gate+up M128 135 -> 164 us with
 // 5) keep 4.
 GemmPlan make_plan(uint32_t m, uint64_t n, uint64_t k, int epi, bool bf16_src = false) {
@@ -96,7 +103,8 @@ GemmPlan make_plan(uint32_t m, uint64_t n, uint64_t k, int epi, bool bf16_src = 
   p.rbw = 1;
   p.nw = 4;
   const bool few_rows = nb < W12_RBW2_MIN_NB;
-  if (p.mfma && (few_rows || m >= 16)) {
+  const bool w12_bf16_out = !bf16_src && epi == EPI_BF16;
+  if (w12_bf16_out || (p.mfma && (few_rows || m >= 16))) {
     p.kind = KIND_COLUMN_SYNC;
     p.nw = epi != EPI_BF16 || m > 64 ? 4 : (few_rows ? W12_CS_FEW_NW : W12_CS_NW);
     p.n_rbg = (uint32_t)((nb + p.nw - 1) / p.nw);

@@ -159,6 +159,28 @@ __device__ __forceinline__ void load_tile(TileRegs<SRC>& t, const uint8_t* __res
   }
 }
 
+// Raw buffer resources (gfx9 layout: 48-bit base, stride 0, size in bytes, dword 3 =
+// 32-bit data format, which untyped loads ignore).  A load past the size returns zeros.
+constexpr int kRsrcWord3 = 0x00020000;
+constexpr int kCpolNT = 2;   // cache policy of a buffer load: nontemporal (streaming)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRsrcWord3);
+}
+
+// Tile column g of one row-block through a buffer resource over that row-block's tiles
+// (W12 or 4 KB BF16 tiles): the column enters as a scalar offset, so advancing a column
+// writes no vector registers.
+template <int SRC>
+__device__ __forceinline__ void load_tile_rs(TileRegs<SRC>& t, __amdgpu_buffer_rsrc_t rs,
+                                             uint32_t g, int lane) {
+  static_assert(SRC != SRC_BF16, "row-major BF16 has no per-row-block tile range");
+  constexpr uint32_t kTileB = SRC == SRC_BF16T ? 4096u : 3072u;
+#pragma unroll
+  for (int s = 0; s < (plain_bf16(SRC) ? 4 : 3); ++s)
+    t.v[s] = __builtin_amdgcn_raw_buffer_load_b128(rs, (uint32_t)lane * 16u + 1024u * s,
+                                                   g * kTileB, kCpolNT);
+}
+
 // Registers -> 16 BF16 pairs (P[4j+p] = element 2p in the low half, 2p+1 in the high).
 template <int SRC>
 __device__ __forceinline__ void unpack_tile(const TileRegs<SRC>& t, const SegView& a,
@@ -681,16 +703,31 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_cs(
   u32x4 xr[kUnits];
   EscCursor ec;
 
+  // Loads go through buffer resources (the row-block's tiles, x) with the column as a
+  // scalar offset: with 64-bit per-lane addresses recomputed every column, the compiler
+  // waited for the previous column's loads before issuing the next column's.
+  constexpr bool kRs = SRC != SRC_BF16;
+  constexpr uint32_t kTileB = SRC == SRC_BF16T ? 4096u : 3072u;
+  __amdgpu_buffer_rsrc_t wrs;
+  if constexpr (kRs) wrs = make_rsrc(sv.w + (size_t)bl * p.g_cols * kTileB, p.g_cols * kTileB);
+  const __amdgpu_buffer_rsrc_t xrs = make_rsrc(x, m_rows * (uint32_t)p.k * 2u);
+  uint32_t xoff[kUnits];   // byte offset of the thread's x units in column 0
+#pragma unroll
+  for (int i = 0; i < kUnits; ++i) {
+    const uint32_t u = (uint32_t)tid + NT * i;
+    const uint32_t uu = u < 16u * MT ? u : u % (16u * MT);
+    const uint32_t m = uu >> 4, cu = uu & 15u;
+    // clamped row / column, used unzeroed (see x_load)
+    xoff[i] = (min(m, m_rows - 1u) * (uint32_t)p.k + 8u * cu) * 2u;
+  }
   auto xload = [&](uint32_t g) {
     const uint32_t gl = min(g, gb - 1u);
 #pragma unroll
-    for (int i = 0; i < kUnits; ++i) {
-      const uint32_t u = (uint32_t)tid + NT * i;
-      const uint32_t uu = u < 16u * MT ? u : u % (16u * MT);
-      const uint32_t m = uu >> 4, cu = uu & 15u;
-      // clamped row / column, used unzeroed (see x_load)
-      xr[i] = *reinterpret_cast<const u32x4*>(x + (size_t)min(m, m_rows - 1u) * p.k + 128u * gl + 8u * cu);
-    }
+    for (int i = 0; i < kUnits; ++i) xr[i] = __builtin_amdgcn_raw_buffer_load_b128(xrs, xoff[i], 256u * gl, 0);
+  };
+  auto tload = [&](TileRegs<SRC>& t, uint32_t g) {
+    if constexpr (kRs) load_tile_rs<SRC>(t, wrs, g, lane);
+    else load_tile<SRC>(t, sv.w, p, bl, g, lane);
   };
   // RMS launches: per-unit sums of x^2 over the K-range, in column order
   float ssq[kUnits];
@@ -746,21 +783,21 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_cs(
   // tile g+1) measured faster than a pinned deeper prefetch.
   uint32_t g = ga;
   xload(g);
-  load_tile<SRC>(tA, sv.w, p, bl, g, lane);
+  tload(tA, g);
   if constexpr (!plain_bf16(SRC)) esc_begin(ec, sv.esc_off, sv.esc, bl, ga * 128u);
   xsumsq(true);
   xstore(g & 1u);
   __syncthreads();
   for (;;) {
     xload(g + 1);
-    load_tile<SRC>(tB, sv.w, p, bl, min(g + 1, gb - 1u), lane);
+    tload(tB, min(g + 1, gb - 1u));
     compute(tA, g);
     xsumsq(g + 1 < gb);
     xstore((g + 1) & 1u);
     __syncthreads();
     if (++g >= gb) break;
     xload(g + 1);
-    load_tile<SRC>(tA, sv.w, p, bl, min(g + 1, gb - 1u), lane);
+    tload(tA, min(g + 1, gb - 1u));
     compute(tB, g);
     xsumsq(g + 1 < gb);
     xstore((g + 1) & 1u);
