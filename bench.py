@@ -524,7 +524,11 @@ def main():
     same = {f"M{m}_{name}": bool(torch.equal(ys[m][i].view(torch.int16), yb[m][i].view(torch.int16)))
             for m in MS for i, name in ((0, "gate_up"), (1, "down"))}
 
-    # per-(M, matrix) launch durations, each over R launches on rotating copies
+    # per-(M, matrix) launch durations, each over R launches on rotating copies.  The host
+    # comparisons above leave the GPU idle long enough for its clock to drop, so a burst
+    # of whole steps comes first and every kind gets 20 untimed launches.
+    for i in range(20):
+        w12_step(i)
     per = {}
     reps = 100
     for m in MS:
@@ -538,7 +542,7 @@ def main():
                 "bf16t": lambda i: w12.gemm_bf16_tiled(xs[m][xi], btl[i % len(btl)], nn, kk,
                                                        out=yb[m][xi])}
             for kind, fn in launch.items():
-                for i in range(5):
+                for i in range(20):
                     fn(i)
                 e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 e0.record()

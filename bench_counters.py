@@ -2,6 +2,7 @@
 the per-launch HBM traffic record that bench.py reports as `roofline.traffic`.
 
     python bench_counters.py FETCH_DIR WRITE_DIR "<profile command>" PROFILE_LOG
+    python bench_counters.py --stats DIR OUT.md TITLE "<profile command>" DESCRIPTION
 
 FETCH_DIR / WRITE_DIR hold run_counter_collection.csv from
     rocprofv3 --pmc FETCH_SIZE -d FETCH_DIR -o run --output-format csv -- python3 bench.py --profile-only --steps 2 --calibrate-copy
@@ -10,6 +11,9 @@ from the known-size kernels at the end of the run: the 1 GiB device-to-device co
 (reads 1 GiB) and the 1 GiB fill before it (writes 1 GiB).  A `w12_gemm` launch is its
 GEMM kernel plus, when K is split, the reduction kernel that follows it.  Writes
 profiles/w12_gemm_traffic.json and profiles/w12_gemm_mlp_block_traffic.md.
+
+With --stats it summarises a `rocprofv3 --kernel-trace --stats` run instead: the stats
+table and the average duration of every (kernel, grid) launch shape, as markdown.
 """
 from __future__ import annotations
 
@@ -118,5 +122,40 @@ def main():
     print(json.dumps({k: v["hbm_bytes"] for k, v in rec["launches"].items()}))
 
 
+def stats_main():
+    """--stats DIR OUT TITLE COMMAND DESCRIPTION: kernel-duration summary of a
+    `rocprofv3 --kernel-trace --stats -d DIR -o run --output-format csv` run as markdown."""
+    d, out, title, command, desc = sys.argv[2:7]
+    with open(os.path.join(d, "run_kernel_stats.csv")) as f:
+        stats = list(csv.DictReader(f))
+    lines = [f"# {title}", "", "Command (from the repository root, on one MI355X):", "",
+             f"    {command}", "", desc, "", "rocprofv3 `--stats` summary:", "",
+             "| kernel | calls | avg us | min us | max us | share |", "|---|---|---|---|---|---|"]
+    for r in stats:
+        name = r["Name"].split("(")[0].replace("void ", "")
+        lines.append(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
+                     f"{float(r['Percentage']):.1f} % |")
+    shapes = {}
+    with open(os.path.join(d, "run_kernel_trace.csv")) as f:
+        for r in csv.DictReader(f):
+            name = r["Kernel_Name"].split("(")[0].replace("void ", "")
+            if "w12::" not in name:
+                continue
+            wg = int(r["Workgroup_Size_X"])
+            key = (name, int(r["Grid_Size_X"]) // wg, int(r["Grid_Size_Y"]), wg)
+            shapes.setdefault(key, []).append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    lines += ["", "Per launch shape (same run, from the kernel trace; workgroups x splits):", "",
+              "| kernel | grid | calls | avg us | min us |", "|---|---|---|---|---|"]
+    for (name, gx, gy, wg), ts in sorted(shapes.items(), key=lambda kv: -sum(kv[1])):
+        lines.append(f"| `{name}` | {gx} x {gy} wg of {wg} | {len(ts)} | "
+                     f"{sum(ts) / len(ts) / 1e3:.2f} | {min(ts) / 1e3:.2f} |")
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
 if __name__ == "__main__":
-    main()
+    if len(sys.argv) > 1 and sys.argv[1] == "--stats":
+        stats_main()
+    else:
+        main()
