@@ -493,3 +493,42 @@ def test_decode_stack_small(env, fused):
     am_ref, _ = o.argmax_exact(to_host(h), head_w)
     assert am.cpu().numpy().tolist() == am_ref.tolist()
     assert int(acc.item()) == o.accepted_length(am_ref, draft)
+
+
+@pytest.mark.parametrize("m", [1, 17, 128])
+def test_gemm_max_k(env, m):
+    """The longest K the format allows (2^20 - 128, 8191 tile columns): 32-bit tile and x
+    offsets at their largest, K split over the few row-blocks, escapes spread over every
+    column; W12, tiled and row-major BF16 against the oracle."""
+    torch, w12 = env
+    g = np.random.default_rng(7000 + m)
+    n, k = 32, (1 << 20) - 128
+    w = wide_exponents((n, k), g, 110, 130)
+    x = wi.gaussian_bf16((m, k), 1.0, g)
+    say("gemm max k", m, n, k)
+    yb = _gemm_case(env, w, x, "w12")
+    z, s = o.gemm_reference(x, w)
+    xt, wt = to_dev(x, torch), to_dev(w, torch)
+    for y in (w12.gemm_bf16(xt, wt), w12.gemm_bf16_tiled(xt, w12.bf16_tile(wt), n, k)):
+        torch.cuda.synchronize()
+        assert o.gemm_accept(to_host(y), z, s).all()
+    assert yb.shape == (m, n)
+
+
+def test_verify_max_k(env):
+    """Greedy verification at the longest K: exact argmax and accepted length."""
+    torch, w12 = env
+    g = np.random.default_rng(7100)
+    m, n, k = 3, 64, (1 << 20) - 128
+    x = wi.gaussian_bf16((m, k), 1.0, g)
+    w = wi.gaussian_bf16((n, k), 0.02, g)
+    w[5] = w[40]        # an exact tie between rows 5 and 40 (lower index wins if it is the max)
+    say("verify max k", m, n, k)
+    am_ref, _ = o.argmax_exact(x, w)
+    draft = am_ref.copy().astype(np.int32)
+    draft[1] = (draft[1] + 1) % n
+    am, acc = w12.lmhead_verify(to_dev(x, torch), w12.encode(to_dev(w, torch)),
+                                torch.from_numpy(draft).to("cuda:0"))
+    torch.cuda.synchronize()
+    assert am.cpu().numpy().tolist() == am_ref.tolist()
+    assert int(acc.item()) == o.accepted_length(am_ref, draft) == 1
