@@ -84,7 +84,6 @@ constexpr uint32_t kT = 512;   // threads of the pass-2 workgroup (one workgroup
 
 __global__ __launch_bounds__(kT) void k_verify_pass2(VerifyArgs a) {
   typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-  constexpr uint32_t kPer = kT / kGroup;   // threads per screened candidate (two waves)
   __shared__ float s_bv[kT];
   __shared__ int32_t s_bi[kT];
   __shared__ double s_d0[kT], s_d1[kT];
@@ -95,6 +94,7 @@ __global__ __launch_bounds__(kT) void k_verify_pass2(VerifyArgs a) {
   __shared__ uint32_t s_cnt, s_bad, s_nsurv;
   __shared__ double s_z64[kScreenMax], s_b64[kScreenMax];
   __shared__ float s_rv[kCache], s_rs[kCache];
+  __shared__ int32_t s_cand[kScreenMax];   // the first candidates (the rest in global memory)
   const uint32_t row = blockIdx.x, tid = threadIdx.x, lane = tid & 63u, wave = tid >> 6;
   const uint16_t* xr = a.x + (uint64_t)row * a.k;
   const float* rv = a.rbmax_v + (uint64_t)row * a.nb;
@@ -102,6 +102,8 @@ __global__ __launch_bounds__(kT) void k_verify_pass2(VerifyArgs a) {
   const float* rs = a.rbmax_s + (uint64_t)row * a.nb;
   const int32_t* ri = a.rbmax_i + (uint64_t)row * a.nb;
   int32_t* cand = a.cand + (uint64_t)row * a.n;
+  auto put = [&](uint32_t c, int32_t v) { if (c < kScreenMax) s_cand[c] = v; else cand[c] = v; };
+  auto get = [&](uint32_t c) { return c < kScreenMax ? s_cand[c] : cand[c]; };
   int32_t result = -1;
   uint32_t ncand = 0, nsurv = 0;
 
@@ -115,31 +117,70 @@ __global__ __launch_bounds__(kT) void k_verify_pass2(VerifyArgs a) {
     if (v != v) bad = true;
     else if (v > bv || (v == bv && i < bi)) { bv = v; bi = i; }
   };
+  // Every scan below issues all of a thread's loads of a chunk (clamped indices) before
+  // using any, so a chunk costs one memory latency; the result does not depend on the
+  // order (largest value, lowest index on ties).
   if ((a.nb & 3u) == 0u) {   // rows start on 16-byte boundaries: four blocks per load
     typedef float f32x4v __attribute__((ext_vector_type(4)));
     typedef int32_t i32x4v __attribute__((ext_vector_type(4)));
-#pragma unroll 8
-    for (uint32_t b4 = tid; b4 < a.nb / 4u; b4 += kT) {
-      const f32x4v v = reinterpret_cast<const f32x4v*>(rv)[b4];
-      const i32x4v i = reinterpret_cast<const i32x4v*>(ri)[b4];
-      const f32x4v sb = reinterpret_cast<const f32x4v*>(rs)[b4];
+    constexpr uint32_t kU = 6;
+    const uint32_t nb4 = a.nb / 4u;
+    for (uint32_t base = 0; base < nb4; base += kT * kU) {
+      f32x4v v[kU], sb[kU];
+      i32x4v iv[kU];
 #pragma unroll
-      for (uint32_t j = 0; j < 4; ++j) take(4u * b4 + j, v[j], i[j], sb[j]);
+      for (uint32_t u = 0; u < kU; ++u) {
+        const uint32_t b4 = min(base + u * kT + tid, nb4 - 1u);
+        v[u] = reinterpret_cast<const f32x4v*>(rv)[b4];
+        iv[u] = reinterpret_cast<const i32x4v*>(ri)[b4];
+        sb[u] = reinterpret_cast<const f32x4v*>(rs)[b4];
+      }
+#pragma unroll
+      for (uint32_t u = 0; u < kU; ++u) {
+        const uint32_t b4 = base + u * kT + tid;
+        if (b4 < nb4) {
+#pragma unroll
+          for (uint32_t j = 0; j < 4; ++j) take(4u * b4 + j, v[u][j], iv[u][j], sb[u][j]);
+        }
+      }
     }
   } else {
-#pragma unroll 8
-    for (uint32_t b = tid; b < a.nb; b += kT) take(b, rv[b], ri[b], rs[b]);
+    constexpr uint32_t kU = 8;
+    for (uint32_t base = 0; base < a.nb; base += kT * kU) {
+      float v[kU], sb[kU];
+      int32_t iv[kU];
+#pragma unroll
+      for (uint32_t u = 0; u < kU; ++u) {
+        const uint32_t b = min(base + u * kT + tid, a.nb - 1u);
+        v[u] = rv[b];
+        iv[u] = ri[b];
+        sb[u] = rs[b];
+      }
+#pragma unroll
+      for (uint32_t u = 0; u < kU; ++u)
+        if (base + u * kT + tid < a.nb) take(base + u * kT + tid, v[u], iv[u], sb[u]);
+    }
   }
   // 2. Xmax (and finiteness of x), eight BF16 per load (k is a multiple of 128)
   double xm = 0.0;
-#pragma unroll 4
-  for (uint32_t u = tid; u < a.k / 8u; u += kT) {
-    const u32x4 xv = reinterpret_cast<const u32x4*>(xr)[u];
+  {
+    constexpr uint32_t kU = 4;
+    const uint32_t nx = a.k / 8u;
+    for (uint32_t base = 0; base < nx; base += kT * kU) {
+      u32x4 xv[kU];
 #pragma unroll
-    for (uint32_t h = 0; h < 8; ++h) {
-      const uint32_t bits = (xv[h >> 1] >> (16u * (h & 1u))) & 0xFFFFu;
-      if (((bits >> 7) & 0xFFu) == 0xFFu) bad = true;
-      xm = fmax(xm, fabs((double)__uint_as_float(bits << 16)));
+      for (uint32_t u = 0; u < kU; ++u)
+        xv[u] = reinterpret_cast<const u32x4*>(xr)[min(base + u * kT + tid, nx - 1u)];
+#pragma unroll
+      for (uint32_t u = 0; u < kU; ++u) {
+        if (base + u * kT + tid >= nx) continue;
+#pragma unroll
+        for (uint32_t h = 0; h < 8; ++h) {
+          const uint32_t bits = (xv[u][h >> 1] >> (16u * (h & 1u))) & 0xFFFFu;
+          if (((bits >> 7) & 0xFFu) == 0xFFu) bad = true;
+          xm = fmax(xm, fabs((double)__uint_as_float(bits << 16)));
+        }
+      }
     }
   }
   // wave trees (fixed pattern; every lane ends with the wave's result), then the waves'
@@ -182,16 +223,19 @@ __global__ __launch_bounds__(kT) void k_verify_pass2(VerifyArgs a) {
       const double bb = c1 * (double)(b < kCache ? s_rs[b] : rs[b]) + c0;
       if ((double)(b < kCache ? s_rv[b] : rv[b]) + bb < lo) continue;
       const int32_t i1 = ri[b];
-      cand[atomicAdd(&s_cnt, 1u)] = i1;
-      if ((double)rv2[b] + bb >= lo)
+      const float v2 = rv2[b];   // (both loads in flight together)
+      put(atomicAdd(&s_cnt, 1u), i1);
+      if ((double)v2 + bb >= lo)
         for (uint32_t rr = 0; rr < 16; ++rr)
-          if ((int32_t)(16u * b + rr) != i1) cand[atomicAdd(&s_cnt, 1u)] = (int32_t)(16u * b + rr);
+          if ((int32_t)(16u * b + rr) != i1) put(atomicAdd(&s_cnt, 1u), (int32_t)(16u * b + rr));
     }
     __syncthreads();
     ncand = s_cnt;
 
-    // 4. FP64 screen, kGroup candidates at a time, kPer threads each.  Thread u of a
-    // candidate v = 16b + r takes lane slots (g, q) = j / 4, j % 4 for j = u, u + kPer,
+    // 4. FP64 screen, up to kGroup candidates at a time (one or two when there are no
+    // more, so each has more threads and its loads take fewer rounds), per threads each;
+    // a candidate's escape offsets are requested with its tile loads.  Thread u of a
+    // candidate v = 16b + r takes lane slots (g, q) = j / 4, j % 4 for j = u, u + per,
     // ...: slot l = 16q + r of tile (b, g) holds row r's columns 128g + 32jj + 8q + i
     // (jj < 4, i < 8), sign/mantissa bytes at 16l and 1024 + 16l, code nibbles in the
     // dwords at 2048 + 16l.  The threads also take the block's escape records of row r
@@ -202,15 +246,17 @@ __global__ __launch_bounds__(kT) void k_verify_pass2(VerifyArgs a) {
     // magnitudes.
     const bool screen = ncand <= kScreenMax;
     if (screen) {
-      const uint32_t cc = tid / kPer, u = tid % kPer;
-      for (uint32_t c0i = 0; c0i < ncand; c0i += kGroup) {
+      const uint32_t grp = ncand <= 1u ? 1u : (ncand <= 2u ? 2u : kGroup);
+      const uint32_t per = kT / grp, cc = tid / per, u = tid % per;
+      for (uint32_t c0i = 0; c0i < ncand; c0i += grp) {
         const uint32_t c = c0i + cc;
         const bool active = c < ncand;
         double z = 0.0, sa = 0.0;
         uint32_t nesc = 0;
         if (active) {
-          const uint32_t v = (uint32_t)cand[c], b = v >> 4, r = v & 15u;
-          for (uint32_t j = u; j < 4u * a.g_cols; j += kPer) {
+          const uint32_t v = (uint32_t)s_cand[c], b = v >> 4, r = v & 15u;
+          const uint32_t e0 = a.esc_off[b], e1 = a.esc_off[b + 1];
+          for (uint32_t j = u; j < 4u * a.g_cols; j += per) {
             const uint32_t g = j >> 2, q = j & 3u, l = 16u * q + r;
             const uint8_t* tb = a.tiles + ((uint64_t)b * a.g_cols + g) * 3072u + 16u * l;
             const u32x4 s_lo = *reinterpret_cast<const u32x4*>(tb);
@@ -234,8 +280,7 @@ __global__ __launch_bounds__(kT) void k_verify_pass2(VerifyArgs a) {
               }
             }
           }
-          const uint32_t e0 = a.esc_off[b], e1 = a.esc_off[b + 1];
-          for (uint32_t i = e0 + u; i < e1; i += kPer) {
+          for (uint32_t i = e0 + u; i < e1; i += per) {
             const uint32_t rec = a.esc[i];
             const uint32_t kk = (rec >> 8) & 0xFFFFFu;
             if ((rec >> 28) != r || kk >= a.k) continue;   // another row, or malformed
@@ -259,10 +304,10 @@ __global__ __launch_bounds__(kT) void k_verify_pass2(VerifyArgs a) {
         if (lane == 0) { s_d0[wave] = z; s_d1[wave] = sa; s_u0[wave] = nesc; }
         __syncthreads();
         if (active && u == 0) {
-          const uint32_t w0 = cc * (kPer / 64u);
+          const uint32_t w0 = cc * (per / 64u);
           double zz = 0.0, ss = 0.0;
           uint32_t ne = 0;
-          for (uint32_t w = 0; w < kPer / 64u; ++w) { zz += s_d0[w0 + w]; ss += s_d1[w0 + w]; ne += s_u0[w0 + w]; }
+          for (uint32_t w = 0; w < per / 64u; ++w) { zz += s_d0[w0 + w]; ss += s_d1[w0 + w]; ne += s_u0[w0 + w]; }
           const double kk2 = (double)a.k + 2.0 * (double)ne + 8.0;
           const double g64 = kk2 * ldexp(1.0, -53) / (1.0 - kk2 * ldexp(1.0, -53));
           s_z64[c] = zz;
@@ -276,7 +321,7 @@ __global__ __launch_bounds__(kT) void k_verify_pass2(VerifyArgs a) {
         for (uint32_t c = 0; c < ncand; ++c) lo64 = fmax(lo64, s_z64[c] - s_b64[c]);
         uint32_t ns = 0;
         for (uint32_t c = 0; c < ncand; ++c)
-          if (s_z64[c] + s_b64[c] >= lo64) cand[ns++] = cand[c];
+          if (s_z64[c] + s_b64[c] >= lo64) s_cand[ns++] = s_cand[c];
         s_nsurv = ns;
       }
     } else if (tid == 0) {
@@ -285,11 +330,11 @@ __global__ __launch_bounds__(kT) void k_verify_pass2(VerifyArgs a) {
     __syncthreads();
     nsurv = s_nsurv;
     if (nsurv == 1u) {
-      result = cand[0];
+      result = get(0);
     } else {
       // 5. exact recompute of the survivors
       for (uint32_t c = 0; c < nsurv; ++c) {
-        const uint32_t v = (uint32_t)cand[c];
+        const uint32_t v = (uint32_t)get(c);
         if (tid < kLimbs) limbs[tid] = 0ull;
         __syncthreads();
         uint32_t code;
