@@ -3,6 +3,7 @@ the per-launch HBM traffic record that bench.py reports as `roofline.traffic`.
 
     python bench_counters.py FETCH_DIR WRITE_DIR "<profile command>" PROFILE_LOG
     python bench_counters.py --stats DIR OUT.md TITLE "<profile command>" DESCRIPTION
+    python bench_counters.py --mfma DIR OUT.md "<profile command>"
 
 FETCH_DIR / WRITE_DIR hold run_counter_collection.csv from
     rocprofv3 --pmc FETCH_SIZE -d FETCH_DIR -o run --output-format csv -- python3 bench.py --profile-only --steps 2 --calibrate-copy
@@ -13,7 +14,8 @@ GEMM kernel plus, when K is split, the reduction kernel that follows it.  Writes
 profiles/w12_gemm_traffic.json and profiles/w12_gemm_mlp_block_traffic.md.
 
 With --stats it summarises a `rocprofv3 --kernel-trace --stats` run instead: the stats
-table and the average duration of every (kernel, grid) launch shape, as markdown.
+table and the average duration of every (kernel, grid) launch shape, as markdown; with
+--mfma, a counter pass of the MFMA counters (flops counted, busy fraction) per launch shape.
 """
 from __future__ import annotations
 
@@ -154,8 +156,50 @@ def stats_main():
         f.write("\n".join(lines) + "\n")
 
 
+def mfma_main():
+    """--mfma DIR OUT COMMAND: MFMA use per launch shape from one counter pass
+    (SQ_INSTS_VALU_MFMA_MOPS_BF16, SQ_VALU_MFMA_BUSY_CYCLES, GRBM_GUI_ACTIVE) over the W12
+    and BF16 GEMM kernels, as markdown."""
+    d, out, command = sys.argv[2:5]
+    per = {}
+    with open(os.path.join(d, "run_counter_collection.csv")) as f:
+        for r in csv.DictReader(f):
+            e = per.setdefault(int(r["Dispatch_Id"]), {"name": r["Kernel_Name"].split("(")[0].replace("void ", ""),
+                                                      "grid": int(r["Grid_Size"]), "wg": int(r["Workgroup_Size"]),
+                                                      "ns": int(r["End_Timestamp"]) - int(r["Start_Timestamp"])})
+            e[r["Counter_Name"]] = float(r["Counter_Value"])
+    shapes = {}
+    for e in per.values():
+        if "k_gemm" not in e["name"]:
+            continue
+        shapes.setdefault((e["name"], e["grid"] // e["wg"], e["wg"]), []).append(e)
+    lines = ["# MFMA use per launch: MLP block GEMMs (rocprofv3 counters)", "",
+             "Command (from the repository root, on one MI355X):", "", f"    {command}", "",
+             "`SQ_INSTS_VALU_MFMA_MOPS_BF16` counts BF16 MFMA work in units of 512 flops (it "
+             "equals 2 x 16 x padded rows x K for the 16-column launches: the MFMA tiles include "
+             "the padding columns and waves).  `GRBM_GUI_ACTIVE` is summed over the 8 XCDs, so "
+             "the busy fraction is `SQ_VALU_MFMA_BUSY_CYCLES` / (`GRBM_GUI_ACTIVE` / 8 x 1024 "
+             "SIMDs).  TFLOP/s = the counted flops / the dispatch duration under counter "
+             "collection, against the 2.5 PFLOP/s dense BF16 peak.  Every launch is bound by HBM "
+             "(the roofline), not by the matrix cores.", "",
+             "| kernel | workgroups | dispatches | MFMA GFLOP | TFLOP/s | % of 2.5 PFLOP/s | MFMA busy % |",
+             "|---|---|---|---|---|---|---|"]
+    for (name, nwg, wg), es in sorted(shapes.items(), key=lambda kv: (kv[0][0], kv[0][1])):
+        fl = sum(e.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0) for e in es) / len(es) * 512
+        ns = sum(e["ns"] for e in es) / len(es)
+        busy = sum(e.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / max(e.get("GRBM_GUI_ACTIVE", 1.0) / 8 * 1024, 1.0)
+                   for e in es) / len(es)
+        tf = fl / ns / 1e3
+        lines.append(f"| `{name}` | {nwg} x {wg} | {len(es)} | {fl / 1e9:.2f} | {tf:.1f} | "
+                     f"{100 * tf / 2500:.1f} | {100 * busy:.1f} |")
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
 if __name__ == "__main__":
     if len(sys.argv) > 1 and sys.argv[1] == "--stats":
         stats_main()
+    elif len(sys.argv) > 1 and sys.argv[1] == "--mfma":
+        mfma_main()
     else:
         main()
