@@ -24,7 +24,8 @@
  *    to the smaller field), strictly ascending.  Element code = index of its exponent
  *    in C; an exponent outside C is an escape (code 0 stored, true exponent listed).
  *  - Tile (b, g) = rows 16b..16b+15 x columns 128g..128g+127, 3072 bytes at byte
- *    offset (b*(k/128) + g)*3072.  Lane slot l = 0..63 (r = l%16, q = l/16) holds
+ *    offset (g*(n/16) + b)*3072: column-major tile order, so the row-blocks' tiles of
+ *    one column are adjacent.  Lane slot l = 0..63 (r = l%16, q = l/16) holds
  *    32 elements t = 0..31 (j = t/8, i = t%8) at column 128g + 32j + 8q + i of row
  *    16b + r.  Byte 1024*(t/16) + 16l + t%16 holds sm = (sign<<7) | mantissa; the
  *    little-endian u32 at 2048 + 16l + 4j holds the 8 codes of j, code of i at bit
@@ -183,8 +184,8 @@ w12_status w12_gemm_bf16(const uint16_t* x, uint32_t m, const uint16_t* w, uint6
  * the same streaming loads as W12 tiles (every wave instruction reads 1 KB of whole
  * lines).  w12_bf16_tile writes the tiled copy of row-major w [n][k] (device, 16-byte
  * aligned) into w_tiled (device, n*k*2 bytes, 16-byte aligned): tile (b, g) at
- * (b*(k/128) + g)*4096, lane slot l (r = l%16, q = l/16) of group j at 1024j + 16l
- * holding row 16b + r, columns 128g + 32j + 8q .. +7.  w12_gemm_bf16_tiled takes that
+ * (g*(n/16) + b)*4096 (column-major, as the W12 tiles), lane slot l (r = l%16,
+ * q = l/16) of group j at 1024j + 16l holding row 16b + r, columns 128g + 32j + 8q .. +7.  w12_gemm_bf16_tiled takes that
  * copy; workspace as for w12_gemm_bf16 (W12_OP_GEMM_BF16).  Shapes and errors as
  * w12_gemm_bf16. */
 w12_status w12_bf16_tile(const uint16_t* w, uint64_t n, uint64_t k, void* w_tiled, void* stream);

@@ -215,8 +215,10 @@ hipError_t launch_encode_scan(const uint32_t* tile_cnt, uint32_t n_tiles, uint32
 }
 
 // ---------------------------------------------------------------- 5. pack
+// One workgroup per tile, numbered row-block major (the escape order); the tile's bytes
+// go to its column-major place, (g * nb + b) * 3072.
 // Thread t = 4l + j builds slot l's elements 8j..8j+7: columns 32j + 8q + 0..7 of row r.
-__global__ __launch_bounds__(256) void k_pack(const uint16_t* w, uint32_t g_cols,
+__global__ __launch_bounds__(256) void k_pack(const uint16_t* w, uint32_t nb, uint32_t g_cols,
                                               Codebook16 codebook,
                                               const uint32_t* tile_off, uint8_t* tiles,
                                               uint32_t* esc, uint64_t esc_cap) {
@@ -247,7 +249,7 @@ __global__ __launch_bounds__(256) void k_pack(const uint16_t* w, uint32_t g_cols
     cw |= (is_esc ? 0u : cd) << (4 * (i >> 1) + 16 * (i & 1));
     ex[(kap0 + i) * 16 + r] = is_esc ? (uint16_t)e : (uint16_t)0xFFFF;
   }
-  uint8_t* tb = tiles + tile * 3072u;
+  uint8_t* tb = tiles + ((uint64_t)g * nb + b) * 3072u;
   *reinterpret_cast<u32x2*>(tb + 1024 * (j >> 1) + 16 * l + 8 * (j & 1)) = u32x2{sm_lo, sm_hi};
   *reinterpret_cast<uint32_t*>(tb + 2048 + 16 * l + 4 * j) = cw;
   __syncthreads();
@@ -287,14 +289,14 @@ hipError_t launch_encode_pack(const uint16_t* w, uint32_t nb, uint32_t g_cols,
                               uint8_t* tiles, uint32_t* esc, uint64_t esc_cap,
                               hipStream_t s) {
   const uint64_t n_tiles = (uint64_t)nb * g_cols;
-  hipLaunchKernelGGL(k_pack, dim3((unsigned)n_tiles), dim3(256), 0, s, w, g_cols, codebook,
+  hipLaunchKernelGGL(k_pack, dim3((unsigned)n_tiles), dim3(256), 0, s, w, nb, g_cols, codebook,
                      tile_off, tiles, esc, esc_cap);
   return hipGetLastError();
 }
 
 // ---------------------------------------------------------------- decode
 __global__ __launch_bounds__(256) void k_decode(const uint8_t* tiles, const uint32_t* esc_off,
-                                                const uint32_t* esc, uint32_t g_cols,
+                                                const uint32_t* esc, uint32_t nb, uint32_t g_cols,
                                                 Codebook16 cb, uint16_t* w_out) {
   __shared__ uint16_t ovr[2048];     // escape exponent at kappa*16 + r, 0xFFFF = none
   __shared__ uint32_t s_range[2];
@@ -327,7 +329,7 @@ __global__ __launch_bounds__(256) void k_decode(const uint8_t* tiles, const uint
   __syncthreads();
   const int l = tid >> 2, j = tid & 3, r = l & 15, q = l >> 4;
   const uint32_t kap0 = 32u * j + 8u * q;
-  const uint8_t* tb = tiles + tile * 3072u;
+  const uint8_t* tb = tiles + ((uint64_t)g * nb + b) * 3072u;
   const u32x2 sm = *reinterpret_cast<const u32x2*>(tb + 1024 * (j >> 1) + 16 * l + 8 * (j & 1));
   const uint32_t cw = *reinterpret_cast<const uint32_t*>(tb + 2048 + 16 * l + 4 * j);
   uint32_t out[4] = {0u, 0u, 0u, 0u};
@@ -350,7 +352,7 @@ hipError_t launch_decode(const uint8_t* tiles, const uint32_t* esc_off, const ui
                          uint16_t* w_out, hipStream_t s) {
   const uint64_t n_tiles = (uint64_t)nb * g_cols;
   hipLaunchKernelGGL(k_decode, dim3((unsigned)n_tiles), dim3(256), 0, s, tiles, esc_off, esc,
-                     g_cols, cb, w_out);
+                     nb, g_cols, cb, w_out);
   return hipGetLastError();
 }
 
@@ -397,7 +399,8 @@ __global__ __launch_bounds__(256) void k_rms(const uint16_t* __restrict__ x, uin
   }
 }
 
-// Row-major BF16 -> 4 KB tiles: tile (b, g) at (b * g_cols + g) * 4096, lane slot l
+// Row-major BF16 -> 4 KB tiles: tile (b, g) at (g * nb + b) * 4096 (column-major, as
+// the W12 tiles), lane slot l
 // (r = l % 16, q = l / 16) of group j at 1024 j + 16 l holding row 16b + r, columns
 // 128g + 32j + 8q .. +7.  One thread per 16-byte unit.
 __global__ __launch_bounds__(256) void k_bf16_tile(const uint16_t* __restrict__ w, uint32_t nb,
@@ -412,7 +415,7 @@ __global__ __launch_bounds__(256) void k_bf16_tile(const uint16_t* __restrict__ 
     const uint64_t b = tile / g_cols, g = tile % g_cols;
     const uint32_t r = l & 15u, q = l >> 4;
     const u32x4 v = *reinterpret_cast<const u32x4*>(w + (16u * b + r) * k + 128u * g + 32u * j + 8u * q);
-    *reinterpret_cast<u32x4*>(out + tile * 4096u + 1024u * j + 16u * l) = v;
+    *reinterpret_cast<u32x4*>(out + (g * nb + b) * 4096u + 1024u * j + 16u * l) = v;
   }
 }
 

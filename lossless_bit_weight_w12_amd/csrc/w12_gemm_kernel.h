@@ -133,9 +133,13 @@ struct TileRegs {
   u32x4 v[plain_bf16(SRC) ? 4 : 3];
 };
 
+// Tile (b, g) of a weight of nbw row-blocks: W12 and 4 KB BF16 tiles are stored column
+// by column, tile (b, g) at (g * nbw + b) * tile bytes, so the workgroups streaming one
+// column at a time read adjacent tiles.
 template <int SRC>
 __device__ __forceinline__ void load_tile(TileRegs<SRC>& t, const uint8_t* __restrict__ w,
-                                          const GemmParams& p, uint32_t b, uint32_t g, int lane) {
+                                          const GemmParams& p, uint32_t b, uint32_t g, int lane,
+                                          uint32_t nbw) {
   if constexpr (SRC == SRC_BF16) {
     const int r = lane & 15, q = lane >> 4;
     const uint8_t* base = w + ((size_t)(16u * b + r) * p.k + 128u * g + 8u * q) * 2u;
@@ -146,12 +150,12 @@ __device__ __forceinline__ void load_tile(TileRegs<SRC>& t, const uint8_t* __res
   } else if constexpr (SRC == SRC_BF16T) {
     // 4 KB tiles: the lane's 16 bytes of group j at 1024 j + 16 lane, so every wave
     // instruction reads 1 KB of whole lines (streaming loads, as for W12 tiles)
-    const uint8_t* base = w + ((size_t)b * p.g_cols + g) * 4096u + (uint32_t)lane * 16u;
+    const uint8_t* base = w + ((size_t)g * nbw + b) * 4096u + (uint32_t)lane * 16u;
 #pragma unroll
     for (int j = 0; j < 4; ++j)
       t.v[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + 1024 * j));
   } else {
-    const uint8_t* base = w + ((size_t)b * p.g_cols + g) * 3072u + (uint32_t)lane * 16u;
+    const uint8_t* base = w + ((size_t)g * nbw + b) * 3072u + (uint32_t)lane * 16u;
 #pragma unroll
     // streaming (nontemporal) loads: every instruction reads 1 KB of whole lines
     for (int s = 0; s < 3; ++s)
@@ -167,18 +171,17 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRsrcWord3);
 }
 
-// Tile column g of one row-block through a buffer resource over that row-block's tiles
-// (W12 or 4 KB BF16 tiles): the column enters as a scalar offset, so advancing a column
-// writes no vector registers.
+// One tile (W12 or 4 KB BF16) through a buffer resource over exactly its bytes, built
+// from a wave-uniform address: advancing a column changes scalar registers only, and the
+// lanes' offsets stay fixed.
 template <int SRC>
-__device__ __forceinline__ void load_tile_rs(TileRegs<SRC>& t, __amdgpu_buffer_rsrc_t rs,
-                                             uint32_t g, int lane) {
-  static_assert(SRC != SRC_BF16, "row-major BF16 has no per-row-block tile range");
+__device__ __forceinline__ void load_tile_rs(TileRegs<SRC>& t, const uint8_t* tile, int lane) {
+  static_assert(SRC != SRC_BF16, "row-major BF16 rows are not tiles");
   constexpr uint32_t kTileB = SRC == SRC_BF16T ? 4096u : 3072u;
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(tile, kTileB);
 #pragma unroll
   for (int s = 0; s < (plain_bf16(SRC) ? 4 : 3); ++s)
-    t.v[s] = __builtin_amdgcn_raw_buffer_load_b128(rs, (uint32_t)lane * 16u + 1024u * s,
-                                                   g * kTileB, kCpolNT);
+    t.v[s] = __builtin_amdgcn_raw_buffer_load_b128(rs, (uint32_t)lane * 16u + 1024u * s, 0, kCpolNT);
 }
 
 // Registers -> 16 BF16 pairs (P[4j+p] = element 2p in the low half, 2p+1 in the high).
@@ -420,7 +423,7 @@ __global__ __launch_bounds__(NWV * 64) void k_gemm(
   auto load_tiles = [&](TileRegs<SRC>* t, uint32_t g) {
     const uint32_t gl = min(g, gb - 1u);
 #pragma unroll
-    for (int rb = 0; rb < RBW; ++rb) load_tile<SRC>(t[rb], sv[rb].w, p, bl[rb], gl, lane);
+    for (int rb = 0; rb < RBW; ++rb) load_tile<SRC>(t[rb], sv[rb].w, p, bl[rb], gl, lane, sv[rb].n / 16u);
   };
 
   auto compute = [&](const TileRegs<SRC>* t, uint32_t g) {
@@ -703,13 +706,13 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_cs(
   u32x4 xr[kUnits];
   EscCursor ec;
 
-  // Loads go through buffer resources (the row-block's tiles, x) with the column as a
-  // scalar offset: with 64-bit per-lane addresses recomputed every column, the compiler
-  // waited for the previous column's loads before issuing the next column's.
+  // Loads go through buffer resources (the current tile, x) with fixed lane offsets and
+  // the column in scalar registers: with 64-bit per-lane addresses recomputed every
+  // column, the compiler waited for the previous column's loads before issuing the next
+  // column's.
   constexpr bool kRs = SRC != SRC_BF16;
   constexpr uint32_t kTileB = SRC == SRC_BF16T ? 4096u : 3072u;
-  __amdgpu_buffer_rsrc_t wrs;
-  if constexpr (kRs) wrs = make_rsrc(sv.w + (size_t)bl * p.g_cols * kTileB, p.g_cols * kTileB);
+  const uint32_t nbw = sv.n / 16u;   // row-blocks of this wave's weight (tile column stride)
   const __amdgpu_buffer_rsrc_t xrs = make_rsrc(x, m_rows * (uint32_t)p.k * 2u);
   uint32_t xoff[kUnits];   // byte offset of the thread's x units in column 0
 #pragma unroll
@@ -726,8 +729,8 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_cs(
     for (int i = 0; i < kUnits; ++i) xr[i] = __builtin_amdgcn_raw_buffer_load_b128(xrs, xoff[i], 256u * gl, 0);
   };
   auto tload = [&](TileRegs<SRC>& t, uint32_t g) {
-    if constexpr (kRs) load_tile_rs<SRC>(t, wrs, g, lane);
-    else load_tile<SRC>(t, sv.w, p, bl, g, lane);
+    if constexpr (kRs) load_tile_rs<SRC>(t, sv.w + ((size_t)g * nbw + bl) * kTileB, lane);
+    else load_tile<SRC>(t, sv.w, p, bl, g, lane, nbw);
   };
   // RMS launches: per-unit sums of x^2 over the K-range, in column order
   float ssq[kUnits];

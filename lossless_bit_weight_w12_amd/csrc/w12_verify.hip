@@ -54,13 +54,14 @@ __device__ __forceinline__ bool exact_parts(uint32_t bits, int& sgn, uint32_t& m
   return e != 0xFFu;
 }
 
-__device__ __forceinline__ uint32_t decode_w(const uint8_t* tiles, uint32_t g_cols, uint32_t v,
+// Weight (v, kk) of a head of nb row-blocks (tile (b, g) at (g * nb + b) * 3072).
+__device__ __forceinline__ uint32_t decode_w(const uint8_t* tiles, uint32_t nb, uint32_t v,
                                              uint32_t kk, const uint32_t lut[4],
                                              uint32_t* code_out) {
   const uint32_t b = v >> 4, r = v & 15u, g = kk >> 7, kap = kk & 127u;
   const uint32_t q = (kap >> 3) & 3u, j = kap >> 5, i = kap & 7u;
   const uint32_t l = 16u * q + r, t = 8u * j + i;
-  const uint8_t* tb = tiles + ((uint64_t)b * g_cols + g) * 3072u;
+  const uint8_t* tb = tiles + ((uint64_t)g * nb + b) * 3072u;
   const uint32_t sm = tb[1024u * (t >> 4) + 16u * l + (t & 15u)];
   const uint32_t cw = *reinterpret_cast<const uint32_t*>(tb + 2048u + 16u * l + 4u * j);
   const uint32_t code = (cw >> (4u * (i >> 1) + 16u * (i & 1u))) & 0xFu;
@@ -258,7 +259,7 @@ __global__ __launch_bounds__(kT) void k_verify_pass2(VerifyArgs a) {
           const uint32_t e0 = a.esc_off[b], e1 = a.esc_off[b + 1];
           for (uint32_t j = u; j < 4u * a.g_cols; j += per) {
             const uint32_t g = j >> 2, q = j & 3u, l = 16u * q + r;
-            const uint8_t* tb = a.tiles + ((uint64_t)b * a.g_cols + g) * 3072u + 16u * l;
+            const uint8_t* tb = a.tiles + ((uint64_t)g * a.nb + b) * 3072u + 16u * l;
             const u32x4 s_lo = *reinterpret_cast<const u32x4*>(tb);
             const u32x4 s_hi = *reinterpret_cast<const u32x4*>(tb + 1024);
             const u32x4 cw = *reinterpret_cast<const u32x4*>(tb + 2048);
@@ -285,7 +286,7 @@ __global__ __launch_bounds__(kT) void k_verify_pass2(VerifyArgs a) {
             const uint32_t kk = (rec >> 8) & 0xFFFFFu;
             if ((rec >> 28) != r || kk >= a.k) continue;   // another row, or malformed
             uint32_t code;
-            const uint32_t wb = decode_w(a.tiles, a.g_cols, v, kk, a.lut, &code);
+            const uint32_t wb = decode_w(a.tiles, a.nb, v, kk, a.lut, &code);
             const uint32_t wt = (wb & 0x807Fu) | ((rec & 0xFFu) << 7);
             const double xv = (double)__uint_as_float((uint32_t)xr[kk] << 16);
             const double pw = xv * (double)__uint_as_float(wb << 16);
@@ -339,7 +340,7 @@ __global__ __launch_bounds__(kT) void k_verify_pass2(VerifyArgs a) {
         __syncthreads();
         uint32_t code;
         for (uint32_t kk = tid; kk < a.k; kk += kT) {
-          const uint32_t wb = decode_w(a.tiles, a.g_cols, v, kk, a.lut, &code);
+          const uint32_t wb = decode_w(a.tiles, a.nb, v, kk, a.lut, &code);
           int sx_, sw_, ex_, ew_;
           uint32_t mx_, mw_;
           const bool okx = exact_parts(xr[kk], sx_, mx_, ex_);
@@ -354,7 +355,7 @@ __global__ __launch_bounds__(kT) void k_verify_pass2(VerifyArgs a) {
           const uint32_t rec = a.esc[i];
           if ((rec >> 28) != r || ((rec >> 8) & 0xFFFFFu) >= a.k) continue;
           const uint32_t kk = (rec >> 8) & 0xFFFFFu;
-          const uint32_t wb = decode_w(a.tiles, a.g_cols, v, kk, a.lut, &code);
+          const uint32_t wb = decode_w(a.tiles, a.nb, v, kk, a.lut, &code);
           const uint32_t wt = (wb & 0x807Fu) | ((rec & 0xFFu) << 7);
           int sx_, sw_, ex_, ew_;
           uint32_t mx_, mw_;

@@ -34,7 +34,8 @@ weight, contradicting the 12.01-12.02 figure):
              true exponent goes to the escape list
   tiles      W [N out, K in] row-major, N % 16 == 0, K % 128 == 0.  Tile (b, g)
              covers rows 16b..16b+15 and columns 128g..128g+127, 3072 bytes at offset
-             (b*(K/128) + g)*3072.  Lane slot l = 0..63: r = l % 16, q = l // 16.
+             (g*(N/16) + b)*3072 (column-major tile order: the tiles of one column of
+             every row-block are adjacent).  Lane slot l = 0..63: r = l % 16, q = l // 16.
              Element t = 0..31 of slot l: j = t // 8, i = t % 8,
              kappa = 32j + 8q + i  (row 16b + r, column 128g + kappa).
              sm byte at 1024*(t // 16) + 16*l + (t % 16);
@@ -136,10 +137,11 @@ def check_shape(n: int, k: int):
 def encode(w: np.ndarray, rows_per_chunk: int = 4096, codebook=None) -> W12Blob:
     """W12 v1 encode of BF16 bits w [N, K] (uint16).
 
-    The bytes of a row-block depend only on its 16 rows and the tensor's codebook, so
-    passing the codebook of a larger tensor encodes a band of its row-blocks exactly as
-    the whole-tensor encode would (escape offsets then count from the band's start;
-    e_max stays that of the rows given)."""
+    The bytes of a row-block's tiles depend only on its 16 rows and the tensor's
+    codebook, so passing the codebook of a larger tensor encodes a band of its row-blocks
+    exactly as the whole-tensor encode would: the band's tiles are those of rows
+    b0..b1-1 in every column (escape offsets then count from the band's start; e_max
+    stays that of the rows given)."""
     w = np.ascontiguousarray(w, dtype=np.uint16)
     n, k = w.shape
     check_shape(n, k)
@@ -196,8 +198,17 @@ def encode(w: np.ndarray, rows_per_chunk: int = 4096, codebook=None) -> W12Blob:
     counts = np.bincount(blk, minlength=nb) if blk.size else np.zeros(nb, dtype=np.int64)
     esc_off = np.zeros(nb + 1, dtype=np.uint32)
     esc_off[1:] = np.cumsum(counts)
+    # stored column-major: tile (b, g) at (g*nb + b)*3072
     return W12Blob(n=n, k=k, codebook=cb, e_max=finite_e_max(hist),
-                   tiles=tiles.reshape(-1), esc_off=esc_off, esc=esc)
+                   tiles=np.ascontiguousarray(tiles.transpose(1, 0, 2)).reshape(-1),
+                   esc_off=esc_off, esc=esc)
+
+
+def band_tiles(tiles: np.ndarray, n: int, k: int, b0: int, b1: int) -> np.ndarray:
+    """The tile bytes of row-blocks b0..b1-1 of an [n, k] tensor's (column-major) tile
+    array, in the order a band encode of those rows stores them."""
+    t = np.asarray(tiles).reshape(k // TILE_K, n // TILE_ROWS, TILE_BYTES)
+    return np.ascontiguousarray(t[:, b0:b1]).reshape(-1)
 
 
 # ----------------------------------------------------------------------------- decode
@@ -206,7 +217,7 @@ def decode(blob: W12Blob, blocks_per_chunk: int = 256) -> np.ndarray:
     n, k = blob.n, blob.k
     nb, gk = n // 16, k // 128
     r_ix, kap, sm_pos, word_pos, bit = slot_layout()
-    tiles_all = blob.tiles.reshape(nb, gk, TILE_BYTES)
+    tiles_all = blob.tiles.reshape(gk, nb, TILE_BYTES).transpose(1, 0, 2)   # [b, g, byte]
     out = np.empty((n, k), dtype=np.uint16)
     for b0 in range(0, nb, blocks_per_chunk):
         b1 = min(nb, b0 + blocks_per_chunk)

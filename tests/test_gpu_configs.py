@@ -66,11 +66,12 @@ def _check_summary(torch, w12, t, w_host, w_dev, bands):
     assert t.e_max == o.finite_e_max(hist)
     assert t.n_esc == int(hist.sum() - hist[cb.astype(np.int64)].sum())
     assert torch.equal(w12.decode(t).view(torch.int16), w_dev.view(torch.int16))
-    gk = t.k // 128
     esc_off = t.esc_off.cpu().numpy().view(np.uint32)
+    # column-major tiles: the band's tiles of every column, read column by column
+    tiles = t.tiles.view(t.k // 128, t.n // 16, 3072)
     for b0, b1 in bands:
         ref = o.encode(w_host[16 * b0:16 * b1], codebook=cb)
-        got = t.tiles[b0 * gk * 3072:b1 * gk * 3072].cpu().numpy()
+        got = tiles[:, b0:b1].contiguous().cpu().numpy().reshape(-1)
         assert np.array_equal(got, ref.tiles), (b0, b1)
         lo, hi = int(esc_off[b0]), int(esc_off[b1])
         assert np.array_equal(esc_off[b0:b1 + 1] - lo, ref.esc_off)

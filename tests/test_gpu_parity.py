@@ -187,11 +187,12 @@ def test_gemm_bf16_baseline(env, m):
 
 
 def tiled_reference(w):
-    """The documented 4 KB tile layout built with numpy: tile (b, g), group j, lane
-    l = 16q + r holds row 16b + r, columns 128g + 32j + 8q .. +7."""
+    """The documented 4 KB tile layout built with numpy: tiles in column-major order
+    (tile (b, g) at (g * n/16 + b) * 4096), group j, lane l = 16q + r holds row 16b + r,
+    columns 128g + 32j + 8q .. +7."""
     n, k = w.shape
     t = w.reshape(n // 16, 16, k // 128, 4, 4, 8)          # b, r, g, j, q, e
-    t = t.transpose(0, 2, 3, 4, 1, 5)                      # b, g, j, q, r, e
+    t = t.transpose(2, 0, 3, 4, 1, 5)                      # g, b, j, q, r, e
     return np.ascontiguousarray(t).reshape(-1).view(np.uint8)
 
 

@@ -155,8 +155,13 @@ def test_band_encode_with_tensor_codebook_is_a_slice():
     full = o.encode(w)
     for b0, b1 in [(0, 1), (3, 7), (9, 10)]:
         band = o.encode(w[16 * b0:16 * b1], codebook=full.codebook)
-        gk = 384 // 128
-        assert np.array_equal(band.tiles, full.tiles[b0 * gk * 3072:b1 * gk * 3072])
+        assert np.array_equal(band.tiles, o.band_tiles(full.tiles, 160, 384, b0, b1))
+        # column-major tile order: row-block b's tile of column g at (g * 10 + b) * 3072
+        for g in range(3):
+            for b in range(b0, b1):
+                off = (g * 10 + b) * 3072
+                assert np.array_equal(full.tiles[off:off + 3072],
+                                      band.tiles[(g * (b1 - b0) + b - b0) * 3072:][:3072])
         lo, hi = full.esc_off[b0], full.esc_off[b1]
         assert np.array_equal(band.esc, full.esc[lo:hi])
         assert np.array_equal(band.esc_off, full.esc_off[b0:b1 + 1] - lo)
