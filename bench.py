@@ -544,13 +544,18 @@ def main():
             for kind, fn in launch.items():
                 for i in range(20):
                     fn(i)
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                e0.record()
-                for i in range(reps):
-                    fn(i)
-                e1.record()
-                torch.cuda.synchronize()
-                res[kind] = e0.elapsed_time(e1) / reps * 1e3     # us per launch
+                # three rounds of R launches, each between one event pair; the median
+                # round (the first can still pay the clock ramp after an idle gap)
+                rounds = []
+                for _ in range(3):
+                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    e0.record()
+                    for i in range(reps):
+                        fn(i)
+                    e1.record()
+                    torch.cuda.synchronize()
+                    rounds.append(e0.elapsed_time(e1) / reps * 1e3)     # us per launch
+                res[kind] = sorted(rounds)[1]
             nbytes = gemm_bytes(tl[0], m)
             per[f"M{m}_{name}"] = {
                 "us_w12": round(res["w12"], 2), "us_bf16": round(res["bf16"], 2),
