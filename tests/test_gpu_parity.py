@@ -533,3 +533,60 @@ def test_verify_max_k(env):
     torch.cuda.synchronize()
     assert am.cpu().numpy().tolist() == am_ref.tolist()
     assert int(acc.item()) == o.accepted_length(am_ref, draft) == 1
+
+
+def test_graph_capture_replays_match_eager(env):
+    """Prepared calls captured in a HIP graph (split-K GEMM with its reduce, grouped RMS
+    GEMM, verification with its accept initialisation): every replay, with new inputs
+    copied in eagerly between replays, equals the eager calls bit for bit."""
+    torch, w12 = env
+    g = np.random.default_rng(7400)
+    dev = "cuda:0"
+    w_split = wi.gaussian_bf16((320, 4096), 0.02, g)            # few row-blocks: K split
+    ws_grp = [wi.gaussian_bf16(sh, 0.02, g) for sh in [(320, 512), (64, 512), (64, 512)]]
+    w_head = wi.gaussian_bf16((4096, 512), 0.02, g)
+    t_split = w12.encode(to_dev(w_split, torch))
+    t_grp = [w12.encode(to_dev(w, torch)) for w in ws_grp]
+    t_head = w12.encode(to_dev(w_head, torch))
+    xs = [(wi.gaussian_bf16((7, 4096), 1.0, g), wi.gaussian_bf16((24, 512), 2.0, g),
+           wi.gaussian_bf16((16, 512), 1.0, g)) for _ in range(3)]
+    x1, x2, x3 = (to_dev(a, torch) for a in xs[0])
+    y1 = torch.empty((7, 320), dtype=torch.bfloat16, device=dev)
+    y2 = [torch.empty((24, w.shape[0]), dtype=torch.bfloat16, device=dev) for w in ws_grp]
+    am = torch.empty(16, dtype=torch.int32, device=dev)
+    acc = torch.empty(1, dtype=torch.int32, device=dev)
+    draft = torch.zeros(16, dtype=torch.int32, device=dev)
+
+    def calls():
+        return [w12.prepare_gemm(x1, t_split, y1), w12.prepare_gemm_group(x2, t_grp, y2, rms=True),
+                w12.prepare_verify(x3, t_head, draft, am, acc)]
+
+    def snapshot():
+        return [y1.clone(), *[y.clone() for y in y2], am.clone(), acc.clone()]
+
+    eager = []
+    for a, b, c in xs:                       # eager answers for each input set
+        x1.copy_(to_dev(a, torch)); x2.copy_(to_dev(b, torch)); x3.copy_(to_dev(c, torch))
+        for f in calls():
+            f()
+        torch.cuda.synchronize()
+        eager.append(snapshot())
+    say("graph capture")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fs = calls()                         # marshalled on the capture stream
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=side):
+            for f in fs:
+                f()
+    torch.cuda.current_stream().wait_stream(side)
+    for r in (1, 0, 2, 1):
+        a, b, c = xs[r]
+        x1.copy_(to_dev(a, torch)); x2.copy_(to_dev(b, torch)); x3.copy_(to_dev(c, torch))
+        graph.replay()
+        torch.cuda.synchronize()
+        for got, want in zip(snapshot(), eager[r]):
+            assert torch.equal(got.view(torch.int16) if got.dtype == torch.bfloat16 else got,
+                               want.view(torch.int16) if want.dtype == torch.bfloat16 else want), r
+        torch.zeros(1, device=dev).add_(1)  # eager work between the replays
