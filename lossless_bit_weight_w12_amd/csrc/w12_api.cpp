@@ -22,8 +22,12 @@ constexpr uint64_t kMaxN = 1ull << 31;
 #ifndef W12_CS_NW
 #define W12_CS_NW 5
 #endif
-static_assert((W12_CS_NW == 4 || W12_CS_NW == 5) && (W12_CS_FEW_NW == 4 || W12_CS_FEW_NW == 5),
-              "column-synchronous launches are instantiated for 4 and 5 waves");
+#ifndef W12_CS_NW32
+#define W12_CS_NW32 10   // 17..32 x columns on many row-blocks
+#endif
+static_assert((W12_CS_NW == 4 || W12_CS_NW == 5) && (W12_CS_FEW_NW == 4 || W12_CS_FEW_NW == 5) &&
+              (W12_CS_NW32 == 5 || W12_CS_NW32 == 10),
+              "column-synchronous launches are instantiated for 4 and 5 waves (and 10 at 32 columns)");
 #ifndef W12_NS_CAP
 #define W12_NS_CAP 8
 #endif
@@ -90,8 +94,11 @@ inline bool codebook_is_run(const uint8_t* c) {
 // average); with 5 it is 436, at most 2 (10).  Measured: gate+up M16 / M24 / M32 5.44 /
 // 4.87 / 4.60 -> 5.82 / 5.21 / 5.13 TB/s, and the split down launches (64 groups x 8
 // splits = 2 workgroups per CU) M32 4.18 -> 4.44; 6 or 7 waves (12 and 14 row-blocks per
-// CU) are slower, 3 ties on gate+up and loses on down, 9 or 10 (one workgroup per CU)
-// tie with 5 and 8 (272 workgroups) loses.  The logits epilogue and the
+// CU) are slower, 3 ties on gate+up and loses on down, 8 (272 workgroups) loses.  With
+// 32-column x tiles on 2048..2560 row-blocks, 10 waves (at most one workgroup per CU, K
+// whole, half the x requests per row-block) are faster: gate+up M32 tiled BF16 69.2 ->
+// 64.0 us, row-major BF16 86.3 -> 78.4 us, W12 M24 / M32 49.3 / 48.9 -> 48.0 / 48.5 us
+// (16 columns: 5 stays ahead).  The logits epilogue and the
 // 128-column x tiles (m > 64: 74 KB of LDS per workgroup; gate+up M128 135 -> 164 us with
 // 5) keep 4.
 GemmPlan make_plan(uint32_t m, uint64_t n, uint64_t k, int epi, bool bf16_src = false) {
@@ -106,7 +113,9 @@ GemmPlan make_plan(uint32_t m, uint64_t n, uint64_t k, int epi, bool bf16_src = 
   const bool w12_bf16_out = !bf16_src && epi == EPI_BF16;
   if (w12_bf16_out || (p.mfma && (few_rows || m >= 16))) {
     p.kind = KIND_COLUMN_SYNC;
-    p.nw = epi != EPI_BF16 || m > 64 ? 4 : (few_rows ? W12_CS_FEW_NW : W12_CS_NW);
+    // 17..32 columns: 10 waves where that is at most one workgroup per CU with K whole
+    const bool ten = m > 16 && m <= 32 && nb >= 2048 && (nb + 9) / 10 <= 256;
+    p.nw = epi != EPI_BF16 || m > 64 ? 4 : few_rows ? W12_CS_FEW_NW : (ten ? W12_CS_NW32 : W12_CS_NW);
     p.n_rbg = (uint32_t)((nb + p.nw - 1) / p.nw);
     units = (uint64_t)p.n_rbg * p.nw / 4;     // in 4-wave workgroup equivalents
     min_cols = W12_CS_MIN_COLS;

@@ -76,10 +76,11 @@ def _gemm_case(env, w, x, which):
     return yb
 
 
-# (n, k): ragged row-block counts, partial 4-column chunks, split-K, long K, and 1025
+# (n, k): ragged row-block counts, partial 4-column chunks, split-K, long K, 1025
 # row-blocks over two tile columns (the many-row kernels: an odd row-block count for two
-# row-blocks per wave, waves with no column)
-SHAPES = [(16, 128), (272, 1280), (48, 640), (64, 4096), (2080, 512), (16400, 256)]
+# row-blocks per wave, waves with no column), and 2049 row-blocks (one 10-wave workgroup
+# per CU at 17..32 rows, the last one nine of its waves idle)
+SHAPES = [(16, 128), (272, 1280), (48, 640), (64, 4096), (2080, 512), (16400, 256), (32784, 128)]
 
 
 # every decode size, then the batched sizes (64- and 128-column tiles, ragged in both)
@@ -111,7 +112,8 @@ GROUPS = [[(320, 512), (64, 512), (64, 512)],
           [(1088, 1280), (1088, 1280)],
           [(48, 640), (16, 640), (32, 640), (272, 640)],
           [(16, 4096)],
-          [(8192, 256), (8208, 256)]]
+          [(8192, 256), (8208, 256)],
+          [(17408, 256), (17408, 256)]]     # 2176 row-blocks: 10-wave workgroups at 17..32 rows
 
 
 @pytest.mark.parametrize("m", [1, 2, 3, 4, 8, 15, 16, 24, 32, 64, 128])
