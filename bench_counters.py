@@ -6,7 +6,7 @@ the per-launch HBM traffic record that bench.py reports as `roofline.traffic`.
     python bench_counters.py --mfma DIR OUT.md "<profile command>"
 
 FETCH_DIR / WRITE_DIR hold run_counter_collection.csv from
-    rocprofv3 --pmc FETCH_SIZE -d FETCH_DIR -o run --output-format csv -- python3 bench.py --profile-only --steps 2 --calibrate-copy
+    rocprofv3 --pmc FETCH_SIZE -d FETCH_DIR -o run --output-format csv -- python3 bench.py --profile-only --steps 2 --warmup 0 --calibrate-copy
 and the same with WRITE_SIZE.  Both counters are per dispatch, in KiB.  The scales come
 from the known-size kernels at the end of the run: the 1 GiB device-to-device copy
 (reads 1 GiB) and the 1 GiB fill before it (writes 1 GiB).  A `w12_gemm` launch is its

@@ -97,8 +97,9 @@ inline bool codebook_is_run(const uint8_t* c) {
 // CU) are slower, 3 ties on gate+up and loses on down, 8 (272 workgroups) loses.  With
 // 32-column x tiles on 2048..2560 row-blocks, 10 waves (at most one workgroup per CU, K
 // whole, half the x requests per row-block) are faster: gate+up M32 tiled BF16 69.2 ->
-// 64.0 us, row-major BF16 86.3 -> 78.4 us, W12 M24 / M32 49.3 / 48.9 -> 48.0 / 48.5 us
-// (16 columns: 5 stays ahead).  The logits epilogue and the
+// 64.0 us, row-major BF16 86.3 -> 78.4 us, W12 M24 / M32 49.3 / 48.9 -> 48.0 / 48.5 us;
+// at 16 columns the BF16 baselines gain too (tiled 62.0 -> 58.5 us, row-major 79.3 ->
+// 75.1 us) and W12 does not (43.3 us either way).  The logits epilogue and the
 // 128-column x tiles (m > 64: 74 KB of LDS per workgroup; gate+up M128 135 -> 164 us with
 // 5) keep 4.
 GemmPlan make_plan(uint32_t m, uint64_t n, uint64_t k, int epi, bool bf16_src = false) {
@@ -113,8 +114,9 @@ GemmPlan make_plan(uint32_t m, uint64_t n, uint64_t k, int epi, bool bf16_src = 
   const bool w12_bf16_out = !bf16_src && epi == EPI_BF16;
   if (w12_bf16_out || (p.mfma && (few_rows || m >= 16))) {
     p.kind = KIND_COLUMN_SYNC;
-    // 17..32 columns: 10 waves where that is at most one workgroup per CU with K whole
-    const bool ten = m > 16 && m <= 32 && nb >= 2048 && (nb + 9) / 10 <= 256;
+    // 17..32 columns (16..32 for the BF16 baselines): 10 waves where that is at most one
+    // workgroup per CU with K whole
+    const bool ten = (m > 16 || bf16_src) && m <= 32 && nb >= 2048 && (nb + 9) / 10 <= 256;
     p.nw = epi != EPI_BF16 || m > 64 ? 4 : few_rows ? W12_CS_FEW_NW : (ten ? W12_CS_NW32 : W12_CS_NW);
     p.n_rbg = (uint32_t)((nb + p.nw - 1) / p.nw);
     units = (uint64_t)p.n_rbg * p.nw / 4;     // in 4-wave workgroup equivalents
