@@ -362,8 +362,9 @@ def main():
                     help="run --steps LM-head verifications (M = 16) and exit (for rocprofv3)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported (this path has no "
-              f"multi-GPU sharding; every box here has one MI355X)", file=sys.stderr)
+        print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported (the library "
+              f"runs each GEMM and verification on one MI355X; it has no multi-GPU sharding)",
+              file=sys.stderr)
         sys.exit(2)
 
     import numpy as np

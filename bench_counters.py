@@ -104,9 +104,9 @@ def main():
         json.dump(rec, f, indent=1)
     lines = ["# HBM traffic per launch: MLP block GEMMs (rocprofv3 counters)", "",
              "Commands (from the repository root, on one MI355X):", "",
-             f"    {command.replace('PMC', 'FETCH_SIZE').replace('DIR', 'gpurun_out/pmc_fetch')}",
-             f"    {command.replace('PMC', 'WRITE_SIZE').replace('DIR', 'gpurun_out/pmc_write')}",
-             f"    python bench_counters.py gpurun_out/pmc_fetch gpurun_out/pmc_write \"<command>\"",
+             f"    {command.replace('PMC', 'FETCH_SIZE').replace('DIR', fetch_dir)}",
+             f"    {command.replace('PMC', 'WRITE_SIZE').replace('DIR', write_dir)}",
+             f"    python bench_counters.py {fetch_dir} {write_dir} \"<command>\" <profile log>",
              "",
              f"Scales: FETCH_SIZE x {fetch_scale:.4f} (a 1 GiB device copy, `{copy_f[1][:40]}`, "
              f"reads {copy_f[3]:.0f} KiB), WRITE_SIZE x {write_scale:.4f} (a 1 GiB fill, "
