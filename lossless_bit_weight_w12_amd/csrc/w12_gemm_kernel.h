@@ -962,6 +962,8 @@ hipError_t launch_gemm_src(const GemmArgs& a, int epi, const GemmPlan& pl, hipSt
       if constexpr ((MT_ == 32 || (MT_ == 16 && plain_bf16(SRC))) && EPI_ == EPI_BF16)        \
         hipLaunchKernelGGL((k_gemm_cs<MT_, 10, SRC, EPI_BF16>), grid, dim3(640), 0, s, a.x, f32, \
                            a.sabs, a.bm, p);                                                  \
+      else                                                                                    \
+        return hipErrorInvalidValue; /* not instantiated: the plan never asks for it */      \
     } else if (pl.nw == 5)                                                                    \
       hipLaunchKernelGGL((k_gemm_cs<MT_, 5, SRC, EPI_>), grid, dim3(320), 0, s, a.x, f32,     \
                          a.sabs, a.bm, p);                         \
