@@ -148,10 +148,11 @@ def stats_main():
             key = (name, int(r["Grid_Size_X"]) // wg, int(r["Grid_Size_Y"]), wg)
             shapes.setdefault(key, []).append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
     lines += ["", "Per launch shape (same run, from the kernel trace; workgroups x splits):", "",
-              "| kernel | grid | calls | avg us | min us |", "|---|---|---|---|---|"]
+              "| kernel | grid | calls | avg us | median us | min us |", "|---|---|---|---|---|---|"]
     for (name, gx, gy, wg), ts in sorted(shapes.items(), key=lambda kv: -sum(kv[1])):
+        med = sorted(ts)[len(ts) // 2]
         lines.append(f"| `{name}` | {gx} x {gy} wg of {wg} | {len(ts)} | "
-                     f"{sum(ts) / len(ts) / 1e3:.2f} | {min(ts) / 1e3:.2f} |")
+                     f"{sum(ts) / len(ts) / 1e3:.2f} | {med / 1e3:.2f} | {min(ts) / 1e3:.2f} |")
     with open(out, "w") as f:
         f.write("\n".join(lines) + "\n")
 
