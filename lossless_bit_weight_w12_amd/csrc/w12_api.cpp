@@ -23,11 +23,11 @@ constexpr uint64_t kMaxN = 1ull << 31;
 #define W12_CS_NW 5
 #endif
 #ifndef W12_CS_NW32
-#define W12_CS_NW32 10   // 17..32 x columns on many row-blocks
+#define W12_CS_NW32 10   // 17..128 x columns on 2048..2560 row-blocks
 #endif
 static_assert((W12_CS_NW == 4 || W12_CS_NW == 5) && (W12_CS_FEW_NW == 4 || W12_CS_FEW_NW == 5) &&
               (W12_CS_NW32 == 5 || W12_CS_NW32 == 10),
-              "column-synchronous launches are instantiated for 4 and 5 waves (and 10 at 32 columns)");
+              "column-synchronous launches are instantiated for 4 and 5 waves (and 10 from 32 columns)");
 #ifndef W12_NS_CAP
 #define W12_NS_CAP 8
 #endif
@@ -99,9 +99,10 @@ inline bool codebook_is_run(const uint8_t* c) {
 // whole, half the x requests per row-block) are faster: gate+up M32 tiled BF16 69.2 ->
 // 64.0 us, row-major BF16 86.3 -> 78.4 us, W12 M24 / M32 49.3 / 48.9 -> 48.0 / 48.5 us;
 // at 16 columns the BF16 baselines gain too (tiled 62.0 -> 58.5 us, row-major 79.3 ->
-// 75.1 us) and W12 does not (43.3 us either way).  The logits epilogue and the
-// 128-column x tiles (m > 64: 74 KB of LDS per workgroup; gate+up M128 135 -> 164 us with
-// 5) keep 4.
+// 75.1 us) and W12 does not (43.3 us either way); at 64 and 128 columns both gain (W12
+// gate+up M64 / M128 63.5 / 128.8 -> 59.7 / 84.3 us, tiled BF16 84.0 / 122.7 -> 73.1 /
+// 107.8 us).  The logits epilogue keeps 4 waves, and so do other shapes at 128 columns
+// (74 KB of LDS per workgroup; gate+up M128 135 -> 164 us with 5).
 GemmPlan make_plan(uint32_t m, uint64_t n, uint64_t k, int epi, bool bf16_src = false) {
   GemmPlan p;
   const uint64_t nb = n / 16, g = k / 128;
@@ -114,10 +115,12 @@ GemmPlan make_plan(uint32_t m, uint64_t n, uint64_t k, int epi, bool bf16_src = 
   const bool w12_bf16_out = !bf16_src && epi == EPI_BF16;
   if (w12_bf16_out || (p.mfma && (few_rows || m >= 16))) {
     p.kind = KIND_COLUMN_SYNC;
-    // 17..32 columns (16..32 for the BF16 baselines): 10 waves where that is at most one
+    // 17..128 columns (16..128 for the BF16 baselines): 10 waves where that is at most one
     // workgroup per CU with K whole
-    const bool ten = (m > 16 || bf16_src) && m <= 32 && nb >= 2048 && (nb + 9) / 10 <= 256;
-    p.nw = epi != EPI_BF16 || m > 64 ? 4 : few_rows ? W12_CS_FEW_NW : (ten ? W12_CS_NW32 : W12_CS_NW);
+    const bool ten = (m > 16 || bf16_src) && nb >= 2048 && (nb + 9) / 10 <= 256;
+    p.nw = epi != EPI_BF16 ? 4
+           : few_rows ? (m > 64 ? 4 : W12_CS_FEW_NW)
+           : ten ? W12_CS_NW32 : (m > 64 ? 4 : W12_CS_NW);
     p.n_rbg = (uint32_t)((nb + p.nw - 1) / p.nw);
     units = (uint64_t)p.n_rbg * p.nw / 4;     // in 4-wave workgroup equivalents
     min_cols = W12_CS_MIN_COLS;

@@ -959,7 +959,7 @@ hipError_t launch_gemm_src(const GemmArgs& a, int epi, const GemmPlan& pl, hipSt
 #define W12_CS(MT_, EPI_)                                                                     \
   do {                                                                                        \
     if (pl.nw == 10) {                                                                        \
-      if constexpr ((MT_ == 32 || (MT_ == 16 && plain_bf16(SRC))) && EPI_ == EPI_BF16)        \
+      if constexpr ((MT_ >= 32 || (MT_ == 16 && plain_bf16(SRC))) && EPI_ == EPI_BF16)        \
         hipLaunchKernelGGL((k_gemm_cs<MT_, 10, SRC, EPI_BF16>), grid, dim3(640), 0, s, a.x, f32, \
                            a.sabs, a.bm, p);                                                  \
       else                                                                                    \
