@@ -959,8 +959,14 @@ hipError_t launch_gemm_src(const GemmArgs& a, int epi, const GemmPlan& pl, hipSt
 #define W12_CS(MT_, EPI_)                                                                     \
   do {                                                                                        \
     if (pl.nw == 10) {                                                                        \
-      if constexpr ((MT_ >= 32 || (MT_ == 16 && plain_bf16(SRC))) && EPI_ == EPI_BF16)        \
+      if constexpr (EPI_ == EPI_BF16 && (MT_ >= 32 || (MT_ == 16 && plain_bf16(SRC))))       \
         hipLaunchKernelGGL((k_gemm_cs<MT_, 10, SRC, EPI_BF16>), grid, dim3(640), 0, s, a.x, f32, \
+                           a.sabs, a.bm, p);                                                  \
+      else                                                                                    \
+        return hipErrorInvalidValue; /* not instantiated: the plan never asks for it */      \
+    } else if (pl.nw == 8) {                                                                  \
+      if constexpr (EPI_ == EPI_LOGITS && MT_ >= 64)                                          \
+        hipLaunchKernelGGL((k_gemm_cs<MT_, 8, SRC, EPI_LOGITS>), grid, dim3(512), 0, s, a.x, f32, \
                            a.sabs, a.bm, p);                                                  \
       else                                                                                    \
         return hipErrorInvalidValue; /* not instantiated: the plan never asks for it */      \
