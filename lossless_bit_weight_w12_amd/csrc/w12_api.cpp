@@ -101,9 +101,9 @@ inline bool codebook_is_run(const uint8_t* c) {
 // at 16 columns the BF16 baselines gain too (tiled 62.0 -> 58.5 us, row-major 79.3 ->
 // 75.1 us) and W12 does not (43.3 us either way); at 64 and 128 columns both gain (W12
 // gate+up M64 / M128 63.5 / 128.8 -> 59.7 / 84.3 us, tiled BF16 84.0 / 122.7 -> 73.1 /
-// 107.8 us).  The logits epilogue keeps 4 waves up to 32 columns (5 is slower) and takes
-// 8 above (LM head, M = 120: 793 us with 4 waves, 522 with 10, 519 with 8, 933 with 16;
-// M = 64: 358 / 329 / 292 / 317 us).  Few row-blocks at 65..128 columns (K split 8 ways)
+// 107.8 us).  The logits epilogue takes 8 waves (LM head, M = 16: 214 us with 4 waves, 200
+// with 8, 208 with 10, 5 slower than 4; M = 24: 238 / 222 / 246 us; M = 120: 793 / 519 /
+// 522 us, 933 with 16; M = 64: 358 / 292 / 329 / 317 us).  Few row-blocks at 65..128 columns (K split 8 ways)
 // take 10 waves as well, one workgroup per CU (down M128 W12 65.1 -> 48.6 us, tiled BF16
 // 69.2 -> 50.7 us; at 64 columns 5 stays ahead); other shapes keep 4 at 128 columns (74 KB
 // of LDS per workgroup; gate+up M128 135 -> 164 us with 5).
@@ -122,7 +122,7 @@ GemmPlan make_plan(uint32_t m, uint64_t n, uint64_t k, int epi, bool bf16_src = 
     // 17..128 columns (16..128 for the BF16 baselines): 10 waves where that is at most one
     // workgroup per CU with K whole
     const bool ten = (m > 16 || bf16_src) && nb >= 2048 && (nb + 9) / 10 <= 256;
-    p.nw = epi != EPI_BF16 ? (m > 32 ? 8 : 4)
+    p.nw = epi != EPI_BF16 ? 8
            : few_rows ? (m > 64 ? W12_CS_NW32 : W12_CS_FEW_NW)
            : ten ? W12_CS_NW32 : (m > 64 ? 4 : W12_CS_NW);
     p.n_rbg = (uint32_t)((nb + p.nw - 1) / p.nw);

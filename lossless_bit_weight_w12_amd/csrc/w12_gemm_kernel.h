@@ -965,7 +965,7 @@ hipError_t launch_gemm_src(const GemmArgs& a, int epi, const GemmPlan& pl, hipSt
       else                                                                                    \
         return hipErrorInvalidValue; /* not instantiated: the plan never asks for it */      \
     } else if (pl.nw == 8) {                                                                  \
-      if constexpr (EPI_ == EPI_LOGITS && MT_ >= 64)                                          \
+      if constexpr (EPI_ == EPI_LOGITS)                                                       \
         hipLaunchKernelGGL((k_gemm_cs<MT_, 8, SRC, EPI_LOGITS>), grid, dim3(512), 0, s, a.x, f32, \
                            a.sabs, a.bm, p);                                                  \
       else                                                                                    \
