@@ -325,8 +325,11 @@ def bf16_round(v: np.ndarray) -> np.ndarray:
 def within_tolerance_rounded(y_bits: np.ndarray, z: np.ndarray, s: np.ndarray):
     """Rounding-aware acceptance: y is the BF16 rounding of some t with
     |t - z| <= 2e-3*S + 1e-6, i.e. RNE(z - tau) <= y <= RNE(z + tau) (RNE is monotone).
-    Needed where one product dominates a row (|z| close to S): the BF16 unit roundoff
-    2^-8 alone then exceeds 2e-3*S, so no BF16 output meets the literal rule."""
+    A BF16 y that meets the literal rule is its own rounding (RNE(y) = y), so this set
+    contains the literal one; it adds at most the half BF16 step that the final
+    rounding of an in-tolerance accumulator can add.  Where one product dominates a
+    row (|z| close to S) the BF16 step exceeds 2e-3*S and no BF16 value may meet the
+    literal rule at all; this rule still accepts the roundings of in-tolerance sums."""
     tau = REL_TOL * s + ABS_TOL
     y = bf16_to_f64(y_bits)
     lo = bf16_to_f64(bf16_round(z - tau))
@@ -335,9 +338,11 @@ def within_tolerance_rounded(y_bits: np.ndarray, z: np.ndarray, s: np.ndarray):
 
 
 def gemm_accept(y_bits: np.ndarray, z: np.ndarray, s: np.ndarray):
-    """Per-element GEMM acceptance: the literal rule, or, where the literal rule is out of
-    reach of any BF16 value, the rounding-aware rule."""
-    return within_tolerance(y_bits, z, s) | within_tolerance_rounded(y_bits, z, s)
+    """Per-element GEMM acceptance of a BF16 output: the tolerance bounds the FP32
+    accumulation before its final round-to-nearest-even, so y is accepted iff it is the
+    BF16 rounding of a value within 2e-3*S + 1e-6 of the exact z
+    (within_tolerance_rounded; every y the literal rule accepts is accepted too)."""
+    return within_tolerance_rounded(y_bits, z, s)
 
 
 # ----------------------------------------------------------------------------- exact
@@ -372,20 +377,27 @@ def exact_logit(x_row: np.ndarray, w_row: np.ndarray) -> int:
     return total
 
 
+def fp64_filter_width(k: int, s_max: float) -> float:
+    """Width of the rigorous float64 filter of argmax_exact: any summation order of K
+    products, each exact in float64, is within gamma*S of the exact sum with
+    gamma = (K+2)*2^-52; two logits (the maximum's and a candidate's) each carry that
+    error, so 2*gamma*max S covers every row."""
+    return 2.0 * (k + 2) * 2.0 ** -52 * s_max
+
+
 def argmax_exact(x: np.ndarray, w: np.ndarray, rows_per_chunk: int = 8192):
     """Per row m: the index v maximising the exact logit sum_k x[m,k]*W[v,k], lowest
     index on an exact tie.  Steps: float64 logits z64 and S64 for every v; a rigorous
-    filter keeps v with z64_v >= max z64 - 2*gamma*max S64, gamma = (K+2)*2^-52 (the
-    float64 error of any summation order is below gamma*S); exact integer logits of
-    the survivors decide.  Returns (argmax int64[M], candidate counts)."""
+    filter keeps v with z64_v >= max z64 - fp64_filter_width(K, max S64) (the float64
+    error of any summation order is below gamma*S); exact integer logits of the
+    survivors decide.  Returns (argmax int64[M], candidate counts)."""
     k = x.shape[1]
     z64, s64 = gemm_reference(x, w, rows_per_chunk)
-    gamma = (k + 2) * 2.0 ** -52
     out = np.empty(x.shape[0], dtype=np.int64)
     ncand = np.empty(x.shape[0], dtype=np.int64)
     for mi in range(x.shape[0]):
         zmax = z64[mi].max()
-        thr = zmax - 2.0 * gamma * s64[mi].max()
+        thr = zmax - fp64_filter_width(k, s64[mi].max())
         cand = np.nonzero(z64[mi] >= thr)[0]
         ncand[mi] = cand.size
         best_v, best_z = -1, None

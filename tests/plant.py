@@ -27,8 +27,7 @@ def _fp32_ulp(v: float) -> float:
 def _argmax_among(x_row, w, z64, s64, k):
     """The oracle's exact argmax for one row, given float64 logits of the current W:
     the oracle's rigorous filter picks the candidates, exact logits decide."""
-    gamma = (k + 2) * 2.0 ** -52
-    thr = z64.max() - 2.0 * gamma * s64.max()
+    thr = z64.max() - o.fp64_filter_width(k, s64.max())
     cand = np.nonzero(z64 >= thr)[0]
     sub, _ = o.argmax_exact(x_row[None, :], w[cand])
     return int(cand[int(sub[0])])

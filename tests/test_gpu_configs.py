@@ -185,6 +185,40 @@ def test_config4_lm_head_verify(env, lm_head):
         assert (nc[:, 0] >= 1).all() and (nc[:, 1] >= 1).all()
 
 
+@pytest.mark.parametrize("m", [1, 8])
+def test_config4_lm_head_verify_small_m(env, lm_head, m):
+    """Workload 4's head verified at 1 and 8 rows (single-request drafts shorter than 16:
+    the first pass takes the wave-column kernels, two row-blocks per wave, VALU at 1 row
+    and MFMA at 8): the first m planted near-tie rows of batch 1, argmax and accepted
+    length against the oracle; and the certified bound on every FP32 logit of the same
+    first pass (w12_logits_f32)."""
+    torch, w12 = env
+    w, xs = lm_head
+    vocab, k = w.shape
+    x = xs[1][:m]
+    t = w12.encode(to_dev(w, torch))
+    say("config 4 small m", m, "oracle argmax")
+    am_ref, _ = o.argmax_exact(x, w)
+    draft = am_ref.astype(np.int32).copy()
+    p = m // 2
+    draft[p] = (draft[p] + 1 + 12345) % vocab
+    xt = to_dev(x, torch)
+    am, acc = w12.lmhead_verify(xt, t, torch.from_numpy(draft).to("cuda:0"))
+    torch.cuda.synchronize()
+    assert am.cpu().numpy().tolist() == am_ref.tolist()
+    assert int(acc.item()) == o.accepted_length(am_ref, draft) == p
+    say("config 4 small m", m, "pass-1 bound")
+    z_hat, s_hat = (v.cpu().numpy().astype(np.float64) for v in w12.logits_f32(xt, t))
+    z, s = o.gemm_reference(x, w)
+    xmax = np.abs(wi.bf16_bits_to_f32(x).astype(np.float64)).max()
+    d = k + 64.0
+    gam = d * 2.0 ** -23 / (1 - d * 2.0 ** -23)
+    a = d * 2.0 ** -126 * (1 + xmax + 2.0 ** (t.e_max - 126))
+    bound = gam * (s_hat / (1 - gam) + a) + a
+    assert (np.abs(z_hat - z) <= bound).all()
+    assert (s <= s_hat / (1 - gam) + a).all()
+
+
 def test_config4_lm_head_verify_batched(env, lm_head):
     """Workload 4's head (near ties planted) verifying 24 requests x 5 rows in one call,
     as the bench times it: every row's argmax is the oracle's exact-logit argmax and every

@@ -417,6 +417,139 @@ def test_verify_pass1_error_within_certified_bound(env, m, kind):
     say("pass-1 bound", m, kind, "max |z^-z| / (g S) =", float((err / (gam * s + 1e-300)).max()))
 
 
+# 1025 row-blocks: from 1024 row-blocks the first pass below 16 rows runs the wave-column
+# kernel with two row-blocks per wave (v_dot2 at 1..3 rows, MFMA at 4..15), here with an
+# odd row-block count so the last wave's second row-block is past the end
+BIG_HEAD = (16400, 512)
+
+
+@pytest.mark.parametrize("m", [1, 2, 3, 4, 8, 15])
+def test_verify_small_m_large_head(env, m):
+    """Verification below 16 rows on a head with more than 1024 row-blocks, near ties
+    planted on every row: argmax and accepted length against the oracle."""
+    torch, w12 = env
+    g = np.random.default_rng(5300 + m)
+    n, k = BIG_HEAD
+    x = wi.gaussian_bf16((m, k), 1.0, g)
+    w = plant_pairs(x, wi.gaussian_bf16((n, k), 0.02, g), list(range(m)), g)
+    say("verify large head", m, n, k)
+    am_ref, _ = o.argmax_exact(x, w)
+    t = w12.encode(to_dev(w, torch))
+    xt = to_dev(x, torch)
+    for p in sorted({0, m // 2, m}):
+        draft = am_ref.copy().astype(np.int32)
+        if p < m:
+            draft[p] = (draft[p] + 1 + int(g.integers(0, n - 1))) % n
+        am, acc = w12.lmhead_verify(xt, t, torch.from_numpy(draft).to("cuda:0"))
+        torch.cuda.synchronize()
+        assert am.cpu().numpy().tolist() == am_ref.tolist()
+        assert int(acc.item()) == o.accepted_length(am_ref, draft) == p
+
+
+@pytest.mark.parametrize("m,kind", [(1, "gauss"), (2, "wide"), (3, "outliers"), (4, "gauss"),
+                                    (8, "wide"), (15, "outliers")])
+def test_verify_pass1_bound_small_m_large_head(env, m, kind):
+    """The certified bound on the first pass's FP32 logits below 16 rows on a head with
+    more than 1024 row-blocks (the wave-column logits kernels, VALU and MFMA)."""
+    torch, w12 = env
+    g = np.random.default_rng(9300 + m)
+    n, k = BIG_HEAD[0], 1280
+    if kind == "gauss":
+        w = wi.gaussian_bf16((n, k), 0.02, g)
+    elif kind == "wide":
+        w = wide_exponents((n, k), g, 104, 126)
+    else:
+        w = wi.add_exponent_outliers(wi.gaussian_bf16((n, k), 0.02, g), 0.01, 3)
+    x = wi.gaussian_bf16((m, k), 1.0, g)
+    t = w12.encode(to_dev(w, torch))
+    say("pass-1 bound large head", m, kind, "codebook", t.codebook)
+    z_hat, s_hat = (v.cpu().numpy().astype(np.float64) for v in w12.logits_f32(to_dev(x, torch), t))
+    z, s = o.gemm_reference(x, w)
+    xmax = np.abs(wi.bf16_bits_to_f32(x).astype(np.float64)).max()
+    bound, gam, a = _certified_bound(s_hat, k, t.e_max, xmax)
+    err = np.abs(z_hat - z)
+    assert (err <= bound).all(), float((err / bound).max())
+    assert (s <= s_hat / (1 - gam) + a).all()
+
+
+def sub_fp64_head(g):
+    """The oracle pin's sub-FP64 near tie (test_oracle.sub_fp64_near_tie) inside a head of
+    16400 rows: columns 0..255 of every row take the construction's pattern for an
+    uninvolved row (logit -1 for both construction rows of x), its rows 2 and 3 go to
+    head rows 9002 and 9003 (one row-block) and its rows 5 and 11 to head rows 700 and
+    12011; the rest of the head is Gaussian.  Expected: 9003 for x row 0, 700 for row 1."""
+    xs, ws, _ = __import__("test_oracle").sub_fp64_near_tie()
+    n, k = BIG_HEAD
+    w = wi.gaussian_bf16((n, k), 0.02, g)
+    w[:, :256] = ws[0]
+    for src, dst in ((2, 9002), (3, 9003), (5, 700), (11, 12011)):
+        w[dst, :256] = ws[src]
+    x = np.zeros((2, k), dtype=np.uint16)
+    x[:, :256] = xs
+    return x, w, [9003, 700]
+
+
+@pytest.mark.parametrize("m", [2, 5, 16])
+def test_verify_sub_fp64_near_tie(env, m):
+    """Two logits that float64 summation misorders (exact 2^-60 against 2^-61, the
+    larger one a cancellation 1 + 2^-60 - 1): the FP32 pass and the FP64 screen cannot
+    separate them and the exact integer sums decide.  Rows beyond the first two are
+    Gaussian; at m = 5 and 16 one extra row is all +0 and one all -0 (every exact logit
+    0, so index 0)."""
+    torch, w12 = env
+    g = np.random.default_rng(5400 + m)
+    x2, w, want = sub_fp64_head(g)
+    k = w.shape[1]
+    x = np.concatenate([x2, wi.gaussian_bf16((m - 2, k), 1.0, g)]) if m > 2 else x2
+    if m >= 5:
+        x[2] = 0
+        x[3] = 0x8000
+    say("verify sub-fp64 near tie", m)
+    am_ref, _ = o.argmax_exact(x, w)
+    assert am_ref[:2].tolist() == want
+    if m >= 5:
+        assert am_ref[2] == 0 and am_ref[3] == 0
+    t = w12.encode(to_dev(w, torch))
+    draft = am_ref.astype(np.int32)
+    am, acc = w12.lmhead_verify(to_dev(x, torch), t, torch.from_numpy(draft).to("cuda:0"))
+    torch.cuda.synchronize()
+    assert am.cpu().numpy().tolist() == am_ref.tolist()
+    assert int(acc.item()) == m
+    nc = w12.verify_candidates(t, m).cpu().numpy()
+    assert nc[0, 1] >= 2 and nc[1, 1] >= 2          # the pair reached the exact sums
+
+
+def test_verify_zero_rows_are_fast(env):
+    """Rows of x that are all zero (padding rows of a batch) make every exact logit 0:
+    the answer is index 0 and must not cost an exact sum per head row.  Four rows (two
+    zero, one -0, one Gaussian) on the 16400-row head, timed after a warm-up call."""
+    torch, w12 = env
+    g = np.random.default_rng(5500)
+    n, k = BIG_HEAD
+    w = wi.gaussian_bf16((n, k), 0.02, g)
+    x = wi.gaussian_bf16((4, k), 1.0, g)
+    x[0] = 0
+    x[2] = 0x8000
+    x[3] = 0
+    say("verify zero rows")
+    am_ref, _ = o.argmax_exact(x, w)
+    assert am_ref[[0, 2, 3]].tolist() == [0, 0, 0]
+    t = w12.encode(to_dev(w, torch))
+    xt = to_dev(x, torch)
+    draft = torch.from_numpy(am_ref.astype(np.int32)).to("cuda:0")
+    am, acc = w12.lmhead_verify(xt, t, draft)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    am, acc = w12.lmhead_verify(xt, t, draft)
+    e1.record()
+    torch.cuda.synchronize()
+    assert am.cpu().numpy().tolist() == am_ref.tolist() and int(acc.item()) == 4
+    ms = e0.elapsed_time(e1)
+    say("verify zero rows", ms, "ms")
+    assert ms < 2.0, ms
+
+
 def test_verify_exact_tie_lowest_index_and_escapes(env):
     """Rows tie exactly (copies), the head is escape-heavy (lookup-table codebook)."""
     torch, w12 = env

@@ -262,6 +262,52 @@ def test_rounded_rule_accepts_correct_rounding_only():
     assert not o.within_tolerance_rounded(far.astype(np.uint16), z, s).any()
 
 
+def _golden_vector(spec, k):
+    v = np.zeros(k, dtype=np.uint16)
+    for key, val in spec.items():
+        lo, _, hi = key.partition("..")
+        v[int(lo):int(hi or lo) + 1] = int(val, 16)
+    return v
+
+
+def test_acceptance_boundary_golden():
+    """Hand-worked boundary of the acceptance rule (tests/golden/gemm_acceptance_boundary.json):
+    z and S of each case are exact, the last accepted BF16 value at z + tau and the next one
+    beyond are known, and so are the cases where only the rounding-aware rule can accept."""
+    g = json.load(open(os.path.join(GOLDEN, "gemm_acceptance_boundary.json")))
+    k = g["k"]
+    for case in g["cases"]:
+        x = _golden_vector(case["x"], k)[None, :]
+        w = _golden_vector(case["w"], k)[None, :]
+        z, s = o.gemm_reference(x, w)
+        assert Fraction(z[0, 0]) == Fraction(case["z"]) and Fraction(s[0, 0]) == Fraction(case["s"])
+        tau = o.REL_TOL * s + o.ABS_TOL
+        assert Fraction(tau[0, 0]) == Fraction(float(Fraction(case["tau"])))
+        for key, rule, want in (("accepted", o.gemm_accept, True), ("rejected", o.gemm_accept, False),
+                                ("literal_accepted", o.within_tolerance, True),
+                                ("literal_rejected", o.within_tolerance, False)):
+            for y in case[key]:
+                got = bool(rule(np.array([[int(y, 16)]], dtype=np.uint16), z, s)[0, 0])
+                assert got == want, (case["name"], key, y)
+
+
+def test_rounded_rule_contains_literal_rule():
+    """Every BF16 value the literal rule accepts is accepted by the rounding-aware rule
+    (it is its own rounding and RNE is monotone), on random rows with and without
+    dominating products and on every BF16 value near each z."""
+    g = np.random.default_rng(23)
+    x = wi.gaussian_bf16((3, 256), 1.0, g)
+    w = wi.add_exponent_outliers(wi.gaussian_bf16((48, 256), 0.02, g), 0.02, 4)
+    z, s = o.gemm_reference(x, w)
+    base = o.bf16_round(z).astype(np.int32)
+    for d in range(-40, 41):
+        y = np.clip(base + d, 0, 0xFFFF).astype(np.uint16)
+        # stay on the side of zero z is on (adding to the bits moves away from zero)
+        y = np.where((base >> 15) == (y.astype(np.int32) >> 15), y, base.astype(np.uint16))
+        lit = o.within_tolerance(y, z, s)
+        assert (o.gemm_accept(y, z, s) | ~lit).all()
+
+
 # ----------------------------------------------------------------------------- exact argmax
 def test_exact_logit_matches_rationals():
     g = np.random.default_rng(11)
@@ -323,6 +369,48 @@ def test_argmax_planted_one_ulp_pair():
         w2[v2, kk] = int(w2[v2, kk]) + bump
         am, _ = o.argmax_exact(x, w2)
         assert am[0] == (v2 if raise_it else v1)
+
+
+def sub_fp64_near_tie():
+    """A head on which float64 summation misorders the top two exact logits.  With x = 1
+    at columns 0, 64 and 128 (zero elsewhere), row 3's products are {1, 2^-60, -1} (exact
+    logit 2^-60) and row 2's {2^-61} (exact 2^-61); every other row's logit is -1.  A
+    float64 sum that adds 2^-60 to 1 before the -1 arrives loses it (1 + 2^-60 rounds to
+    1) and gets 0 < 2^-61; the columns are 64 apart so that any blocked summation with up
+    to 64 running sums keeps the three terms in one of them, in column order.  Row 11 of
+    a second x row repeats the construction with the winner at the lower index (row 5
+    {1, 2^-60, -1} at columns 1, 65, 129 against row 11's {2^-61}).  Expected answers by
+    construction: 3 and 5."""
+    one, m_one, e60, e61 = 0x3F80, 0xBF80, 0x2180, 0x2100      # 1, -1, 2^-60, 2^-61
+    k = 256
+    x = np.zeros((2, k), dtype=np.uint16)
+    x[0, [0, 64, 128]] = one
+    x[1, [1, 65, 129]] = one
+    w = np.zeros((16, k), dtype=np.uint16)
+    w[:, 0] = m_one
+    w[:, 1] = m_one
+    w[3, [0, 64, 128]] = [one, e60, m_one]
+    w[2, 0] = e61
+    w[5, [1, 65, 129]] = [one, e60, m_one]
+    w[11, 1] = e61
+    for v in (3, 2):
+        w[v, 1] = 0          # rows 2, 3 take no part in the second construction
+    for v in (5, 11):
+        w[v, 0] = 0
+    return x, w, [3, 5]
+
+
+def test_argmax_sub_fp64_near_tie():
+    """Pins the width of the oracle's float64 filter: the exact winner's float64 logit is
+    below the float64 maximum, so a filter that keeps only the float64 maximum answers
+    wrongly; the exact answer (by construction, and by rational brute force) is kept."""
+    x, w, want = sub_fp64_near_tie()
+    z, _ = o.gemm_reference(x, w)
+    # the construction does what it is for: float64 misorders both pairs here
+    assert z[0, 3] < z[0, 2] and z[1, 5] < z[1, 11], (z[0, [2, 3]], z[1, [5, 11]])
+    am, ncand = o.argmax_exact(x, w)
+    assert am.tolist() == want == brute_argmax(x, w)
+    assert (ncand >= 2).all()
 
 
 def test_accepted_length_cases():
@@ -431,3 +519,32 @@ def test_mutation_batched_accept_offsets_are_caught(monkeypatch):
                          for a, nd in zip(row_off, n_draft)], dtype=np.int64)
     monkeypatch.setattr(o, "accepted_lengths_batched", bad)
     assert _pins_fail(test_accepted_lengths_batched_cases)
+
+
+def test_mutation_tolerance_tenfold_is_caught(monkeypatch):
+    monkeypatch.setattr(o, "REL_TOL", 2e-2)
+    assert _pins_fail(test_acceptance_boundary_golden)
+
+
+def test_mutation_tolerance_doubled_is_caught(monkeypatch):
+    monkeypatch.setattr(o, "REL_TOL", 4e-3)
+    assert _pins_fail(test_acceptance_boundary_golden)
+
+
+def test_mutation_rounded_rule_one_ulp_wider_is_caught(monkeypatch):
+    def bad(y_bits, z, s):
+        tau = o.REL_TOL * s + o.ABS_TOL
+        y = o.bf16_to_f64(y_bits)
+        lo_b = o.bf16_round(z - tau).astype(np.int32)
+        hi_b = o.bf16_round(z + tau).astype(np.int32)
+        # one BF16 step further out on each side (away from zero: +1 on the bits)
+        lo = o.bf16_to_f64(np.where(lo_b >= 0x8000, lo_b + 1, np.where(lo_b == 0, 0x8001, lo_b - 1)).astype(np.uint16))
+        hi = o.bf16_to_f64(np.where(hi_b >= 0x8000, np.where(hi_b == 0x8000, 0x0001, hi_b - 1), hi_b + 1).astype(np.uint16))
+        return (lo <= y) & (y <= hi)
+    monkeypatch.setattr(o, "within_tolerance_rounded", bad)
+    assert _pins_fail(test_acceptance_boundary_golden)
+
+
+def test_mutation_zero_width_fp64_filter_is_caught(monkeypatch):
+    monkeypatch.setattr(o, "fp64_filter_width", lambda k, s_max: 0.0)
+    assert _pins_fail(test_argmax_sub_fp64_near_tie)
