@@ -109,8 +109,10 @@ size_t w12_tiles_bytes(uint64_t n, uint64_t k);
  * in this order: per-row diagnostic counts (int32 [m][2]: candidate logits, those left
  * after the FP64 screen), the per-row-block records of the first pass (largest FP32
  * logit, second largest, largest sum_k |x_k||w_k|, each FP32 [m][n/16]; index of the
- * largest, int32 [m][n/16]) and the candidate lists (int32 [m][n]); all readable after
- * a call for diagnostics.  ENCODE holds the histogram and per-tile escape counts. */
+ * largest, int32 [m][n/16]), its per-workgroup group records (largest logit, its index,
+ * that row-block's sum, an upper bound of logit + bound slope * sum over the group:
+ * four arrays of [m][n/16] 4-byte entries, the first ngroups of each row used) and the
+ * candidate lists (int32 [m][n]); all readable after a call for diagnostics.  ENCODE holds the histogram and per-tile escape counts. */
 size_t w12_workspace_bytes(int op, uint32_t m, uint64_t n, uint64_t k);
 
 /* Zero-fills `ws` on `stream` with a kernel (no hipMemset); a convenience, no call
@@ -201,12 +203,15 @@ w12_status w12_gemm_bf16_tiled(const uint16_t* x, uint32_t m, const void* w_tile
  * v maximising the EXACT logit sum_k x[row,k]*W[v,k], lowest index on exact ties; and
  * accepted_out device int32 [1]: the first i < n_draft with argmax[i] != draft[i], or
  * n_draft.  A first pass streams the head once and keeps, per 16-row block, the two
- * largest FP32 logits z^ and the largest S = sum_k |x_k||w_vk|; with B(S) a bound on
- * |z^ - z| for any summation order, every logit whose z^ + B(S) can reach the lower
- * bound z^* - B(S*) of the computed maximum is recomputed in FP64 from the W12 tiles,
- * and those that the FP64 intervals cannot separate are summed exactly, so the result
- * does not depend on the reduction order.  A row whose logits are not finite gets
- * argmax -1.  ws: w12_workspace_bytes(W12_OP_VERIFY, m, n, k). */
+ * largest FP32 logits z^ and the largest S = sum_k |x_k||w_vk| (and per workgroup of
+ * blocks their maximum and bound); with B(S) a bound on |z^ - z| for any summation
+ * order, every logit whose z^ + B(S) can reach the lower bound z^* - B(S*) of the
+ * computed maximum is a candidate; a single candidate is the answer, several are
+ * recomputed in FP64 from the W12 tiles, and those that the FP64 intervals cannot
+ * separate are summed exactly, so the result does not depend on the reduction order.
+ * A row of x that is all +-0 gets index 0 (every logit is exactly 0) without a search;
+ * any number of candidates is screened, in chunks.  A row whose logits are not finite
+ * gets argmax -1.  ws: w12_workspace_bytes(W12_OP_VERIFY, m, n, k). */
 w12_status w12_lmhead_verify(const uint16_t* x, uint32_t m, const w12_desc* d,
                              const int32_t* draft, uint32_t n_draft, int32_t* argmax_out,
                              int32_t* accepted_out, void* ws, size_t ws_bytes,

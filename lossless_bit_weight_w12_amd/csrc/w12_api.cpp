@@ -171,32 +171,49 @@ size_t group_ws_bytes(uint32_t m, uint64_t n_total, uint64_t k) {
 }
 
 // Verify workspace: per-row diagnostic counts first (a fixed place), then the
-// per-row-block records of pass 1 and the candidate lists of pass 2.
+// per-row-block records of pass 1, its group records (one per workgroup of pass 1: at
+// most one per row-block) and the candidate lists of pass 2.
 struct VerifyLayout {
-  size_t ncand, bm_v, bm_v2, bm_s, bm_i, cand, total;
+  size_t ncand, bm_v, bm_v2, bm_s, bm_i, g_v, g_i, g_s, g_u, cand, total;
 };
 
 VerifyLayout verify_layout(uint32_t m, uint64_t n) {
   VerifyLayout L;
   const uint64_t nb = n / 16;
+  const size_t rec = align256((size_t)m * nb * 4);
   L.ncand = 0;
   L.bm_v = L.ncand + align256((size_t)m * 8);
-  L.bm_v2 = L.bm_v + align256((size_t)m * nb * 4);
-  L.bm_s = L.bm_v2 + align256((size_t)m * nb * 4);
-  L.bm_i = L.bm_s + align256((size_t)m * nb * 4);
-  L.cand = L.bm_i + align256((size_t)m * nb * 4);
+  L.bm_v2 = L.bm_v + rec;
+  L.bm_s = L.bm_v2 + rec;
+  L.bm_i = L.bm_s + rec;
+  L.g_v = L.bm_i + rec;
+  L.g_i = L.g_v + rec;
+  L.g_s = L.g_i + rec;
+  L.g_u = L.g_s + rec;
+  L.cand = L.g_u + rec;
   L.total = L.cand + align256((size_t)m * n * 4);
   return L;
 }
 
-BlockMax block_max(uint8_t* base, const VerifyLayout& L) {
+// Records of pass 1 for a launch of plan p (group records: one per row-block group).
+BlockMax block_max(uint8_t* base, const VerifyLayout& L, const GemmPlan& p) {
   BlockMax bm;
   memset(&bm, 0, sizeof(bm));   // no accept, no request table
   bm.v = (float*)(base + L.bm_v);
   bm.v2 = (float*)(base + L.bm_v2);
   bm.s = (float*)(base + L.bm_s);
   bm.i = (int32_t*)(base + L.bm_i);
+  bm.gv = (float*)(base + L.g_v);
+  bm.gi = (int32_t*)(base + L.g_i);
+  bm.gs = (float*)(base + L.g_s);
+  bm.gu = (float*)(base + L.g_u);
+  bm.ngrp = p.n_rbg;
   return bm;
+}
+
+// Row-blocks per group record of a logits launch.
+inline uint32_t blocks_per_group(const GemmPlan& p) {
+  return p.kind == KIND_COLUMN_SYNC ? (uint32_t)p.nw : (uint32_t)p.rbw;
 }
 
 struct EncodeLayout {
@@ -336,6 +353,7 @@ w12_status verify_impl(const uint16_t* x, uint32_t m, const w12_desc* d, const i
   hipStream_t s = (hipStream_t)stream;
   uint8_t* base = (uint8_t*)ws;
   GemmPlan p = make_plan(m, d->n, d->k, EPI_LOGITS);
+  if (blocks_per_group(p) > kMaxBpg) return W12_ERR_HIP;   // (no plan asks for more)
   GemmArgs a;
   memset(&a, 0, sizeof(a));
   a.x = x;
@@ -343,7 +361,7 @@ w12_status verify_impl(const uint16_t* x, uint32_t m, const w12_desc* d, const i
   fill_params(a.p, m, d->k, d->n, 1);
   a.logits = nullptr;          // pass 2 works from the block records and the tiles
   a.sabs = nullptr;
-  a.bm = block_max(base, L);
+  a.bm = block_max(base, L, p);
   a.bm.accepted = accepted_out;   // pass 1 sets the draft lengths, pass 2 lowers them
   a.bm.n_draft = n_draft;
   a.bm.req_off = req_off;
@@ -361,6 +379,12 @@ w12_status verify_impl(const uint16_t* x, uint32_t m, const w12_desc* d, const i
   v.rbmax_v2 = a.bm.v2;
   v.rbmax_s = a.bm.s;
   v.rbmax_i = a.bm.i;
+  v.grp_v = a.bm.gv;
+  v.grp_i = a.bm.gi;
+  v.grp_s = a.bm.gs;
+  v.grp_u = a.bm.gu;
+  v.ngrp = a.bm.ngrp;
+  v.bpg = blocks_per_group(p);
   v.cand = (int32_t*)(base + L.cand);
   v.ncand = (int32_t*)(base + L.ncand);
   v.argmax = argmax_out;
@@ -596,7 +620,7 @@ w12_status w12_logits_f32(const uint16_t* x, uint32_t m, const w12_desc* d, floa
   fill_params(a.p, m, d->k, d->n, 1);
   a.logits = logits_out;
   a.sabs = sabs_out;
-  a.bm = block_max(base, L);
+  a.bm = block_max(base, L, p);
   const int src = codebook_is_run(d->codebook) ? SRC_RUN : SRC_LUT;
   return hip_status(launch_gemm(a, src, EPI_LOGITS, p, (hipStream_t)stream));
 }

@@ -625,10 +625,14 @@ __global__ __launch_bounds__(NWV * 64) void k_gemm(
     __syncthreads();
     if (bm.accepted && blockIdx.x == 0 && blockIdx.y == 0)
       accept_init(bm, p.m, (uint32_t)tid, NWV * 64u);   // verification pass 2 lowers them
+    // per (row-block, output row) records, kept in LDS for the workgroup's group record
+    __shared__ float s_gv[RBW][MT], s_gs[RBW][MT], s_gu[RBW][MT];
+    __shared__ int32_t s_gi[RBW][MT];
+    const double c1 = bound_slope(p.k);
     for (int o = tid; o < RBW * MT; o += (NWV * 64)) {
       const int rb = o / MT, m = o % MT;
       const uint32_t b = b0 + rb;
-      if (b >= p.nb || (uint32_t)m >= m_rows) continue;
+      const bool live = b < p.nb && (uint32_t)m < m_rows;
       // largest (lowest row on ties) and second largest logit of the block
       float best = fin[o * 16], second = -__builtin_inff(), smax = fin_s[o * 16];
       int bi = 0;
@@ -640,10 +644,35 @@ __global__ __launch_bounds__(NWV * 64) void k_gemm(
         else if (v > second) second = v;
         smax = fmaxf(smax, fin_s[o * 16 + rr]);
       }
+      s_gv[rb][m] = !live ? -__builtin_inff() : (finite ? best : __builtin_nanf(""));
+      s_gi[rb][m] = (int32_t)(16u * b + bi);
+      s_gs[rb][m] = smax;
+      s_gu[rb][m] = !live ? -__builtin_inff()
+                          : (finite ? f32_round_up((double)best + c1 * (double)smax)
+                                    : __builtin_nanf(""));
+      if (!live) continue;
       bm.v[(size_t)m * p.nb + b] = finite ? best : __builtin_nanf("");
       bm.v2[(size_t)m * p.nb + b] = finite ? second : __builtin_nanf("");
       bm.s[(size_t)m * p.nb + b] = smax;
       bm.i[(size_t)m * p.nb + b] = (int32_t)(16u * b + bi);
+    }
+    __syncthreads();
+    if ((uint32_t)tid < MT && (uint32_t)tid < m_rows) {
+      float v = s_gv[0][tid], u = s_gu[0][tid], sv = s_gs[0][tid];
+      int32_t vi = s_gi[0][tid];
+      bool nan = v != v || u != u;
+#pragma unroll
+      for (int rb = 1; rb < RBW; ++rb) {
+        const float vw = s_gv[rb][tid], uw = s_gu[rb][tid];
+        nan = nan || vw != vw || uw != uw;
+        if (vw > v) { v = vw; vi = s_gi[rb][tid]; sv = s_gs[rb][tid]; }   // ties: the lower row-block
+        u = fmaxf(u, uw);
+      }
+      const size_t og = (size_t)tid * bm.ngrp + blockIdx.x;
+      bm.gv[og] = nan ? __builtin_nanf("") : v;
+      bm.gi[og] = vi;
+      bm.gs[og] = sv;
+      bm.gu[og] = nan ? __builtin_nanf("") : u;
     }
   } else {
     const bool direct = gridDim.y == 1;
@@ -833,7 +862,10 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_cs(
   if constexpr (EPI == EPI_LOGITS) {
     if (bm.accepted && blockIdx.x == 0 && blockIdx.y == 0)
       accept_init(bm, p.m, (uint32_t)tid, NT);   // verification pass 2 lowers them
-    if (!bvalid) return;
+    // the workgroup's group record per output row: its waves' row-blocks in order
+    __shared__ float s_gv[NW][MT], s_gs[NW][MT], s_gu[NW][MT];
+    __shared__ int32_t s_gi[NW][MT];
+    const double c1 = bound_slope(p.k);
 #pragma unroll
     for (int h = 0; h < NH; ++h) {
       const uint32_t m = 16u * h + (uint32_t)r;
@@ -868,7 +900,7 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_cs(
           second = fmaxf(second, ob);
         }
       }
-      if (m < m_rows) {
+      if (m < m_rows && bvalid) {
         if (out_f32) {   // full logits and S only when asked for (verification needs the maxima)
           *reinterpret_cast<f32x4*>(out_f32 + (size_t)m * p.n + n0) = acc[h];
           *reinterpret_cast<f32x4*>(out_s + (size_t)m * p.n + n0) = sacc[h];
@@ -880,6 +912,33 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_cs(
           bm.i[(size_t)m * p.nb + b] = (int32_t)(16u * b + row);
         }
       }
+      if (q == 0) {   // a row-block past the end takes no part in the group record
+        const bool live = bvalid && m < m_rows;
+        s_gv[wave][m] = !live ? -__builtin_inff() : (finite ? best : __builtin_nanf(""));
+        s_gi[wave][m] = (int32_t)(16u * b + row);
+        s_gs[wave][m] = smax;
+        s_gu[wave][m] = !live ? -__builtin_inff()
+                              : (finite ? f32_round_up((double)best + c1 * (double)smax)
+                                        : __builtin_nanf(""));
+      }
+    }
+    __syncthreads();
+    if ((uint32_t)tid < MT && (uint32_t)tid < m_rows) {
+      float v = s_gv[0][tid], u = s_gu[0][tid], sv = s_gs[0][tid];
+      int32_t vi = s_gi[0][tid];
+      bool nan = v != v || u != u;
+#pragma unroll
+      for (int w = 1; w < NW; ++w) {
+        const float vw = s_gv[w][tid], uw = s_gu[w][tid];
+        nan = nan || vw != vw || uw != uw;
+        if (vw > v) { v = vw; vi = s_gi[w][tid]; sv = s_gs[w][tid]; }   // ties: the lower row-block
+        u = fmaxf(u, uw);
+      }
+      const size_t o = (size_t)tid * bm.ngrp + blockIdx.x;
+      bm.gv[o] = nan ? __builtin_nanf("") : v;
+      bm.gi[o] = vi;
+      bm.gs[o] = sv;
+      bm.gu[o] = nan ? __builtin_nanf("") : u;
     }
   } else {
     const bool direct = gridDim.y == 1;

@@ -34,6 +34,8 @@ enum Epi : int {
 constexpr int kMaxSeg = 4;
 // Most K splits a launch takes (the reduce kernel keeps one partial per split in registers).
 constexpr uint32_t kMaxSplit = 8;
+// Most row-blocks in one group record of verification pass 1 (its workgroup's row-blocks).
+constexpr uint32_t kMaxBpg = 8;
 struct Seg {
   const uint8_t* w;         // W12 tiles, or BF16 rows [n][k]
   const uint32_t* esc_off;  // [n/16 + 1] (W12)
@@ -57,12 +59,43 @@ struct GemmParams {
   Seg seg[kMaxSeg];
 };
 
-// Per-row-block records of the logits epilogue (verification pass 1), [m][nb] each.
+// Slope of the certified bound on an FP32 logit computed in any summation order,
+// B(S^) = c1 S^ + c0 (derivation in w12_verify.hip): each of the K products passes
+// through at most D = K + 64 additions with relative error below 2^-23, g = D 2^-23 /
+// (1 - D 2^-23), c1 = g / (1 - g), inflated by 2^-20 for its FP64 evaluation.  Pass 1
+// and pass 2 evaluate it with the same operations.
+__host__ __device__ inline double bound_slope(uint32_t k) {
+  const double dd = (double)k + 64.0;
+  const double gam = dd * 0x1p-23 / (1.0 - dd * 0x1p-23);
+  return gam / (1.0 - gam) * (1.0 + 0x1p-20);
+}
+
+// Smallest FP32 value >= d (finite or infinite d).
+__device__ inline float f32_round_up(double d) {
+  float f = (float)d;
+  if ((double)f < d) {
+    uint32_t u = __float_as_uint(f);
+    if (f == 0.0f) u = 1u;          // +-0 -> the smallest positive subnormal
+    else if (f > 0.0f) u += 1u;
+    else u -= 1u;
+    f = __uint_as_float(u);
+  }
+  return f;
+}
+
+// Per-row-block records of the logits epilogue (verification pass 1), [m][nb] each, and
+// one record per workgroup ("group": its consecutive row-blocks), [m][ngrp] each.
 struct BlockMax {
   float* v;                 // largest logit of the row-block (NaN if any is not finite)
   float* v2;                // second largest (equal to v on a tie)
   float* s;                 // largest sum_k |x_k||w_k| of the row-block
   int32_t* i;               // index of v, lowest on ties
+  float* gv;                // group: largest logit (NaN if any of its logits is not finite)
+  int32_t* gi;              // group: index of gv, lowest on ties
+  float* gs;                // group: s of the row-block holding gv
+  float* gu;                // group: an FP32 upper bound of v + bound_slope(k) * s over its
+                            // row-blocks (NaN if any logit is not finite)
+  uint32_t ngrp;            // groups per row (the grid's row-block groups)
   int32_t* accepted;        // [n_req]: set by the first workgroup (NULL: untouched)
   uint32_t n_draft;         // one request over all rows (req_off NULL): its draft length
   const int32_t* req_off;   // batched: request r owns rows req_off[r] .. req_off[r+1]-1
@@ -165,6 +198,11 @@ struct VerifyArgs {
   const float* rbmax_v2;    // [m][nb]
   const float* rbmax_s;     // [m][nb]
   const int32_t* rbmax_i;   // [m][nb]
+  const float* grp_v;       // [m][ngrp] group records of pass 1
+  const int32_t* grp_i;
+  const float* grp_s;
+  const float* grp_u;
+  uint32_t ngrp, bpg;       // groups per row, row-blocks per group (<= kMaxBpg)
   int32_t* cand;            // [m][n] candidate logits
   int32_t* argmax;          // [m]
   int32_t* ncand;           // [m][2]: candidate logits, those left after the FP64 screen

@@ -4,8 +4,10 @@
 // Pass 1 (the GEMM kernel family with the logits epilogue) leaves, per row and per
 // 16-row block of the head, the largest FP32 logit z^ (with its index), the second
 // largest, and the largest S^ = the same kernel's FP32 sum of |x_k||w_vk| over the
-// block's rows.  Pass 2 (one workgroup per row):
-//   1. z* = max z^ over the block maxima (lowest index on ties), S* the largest S^ of
+// block's rows; and per workgroup of pass 1 (a group of consecutive row-blocks) the
+// group's largest logit, its index and block's S^, and an FP32 upper bound U of
+// z^_b + c1 S^_b over its row-blocks.  Pass 2 (one workgroup per row):
+//   1. z* = max z^ over the group records (lowest index on ties), S* the largest S^ of
 //      its block (an upper bound of its own S^);
 //   2. the error bound.  A product of two BF16 values is exact in FP32 unless it
 //      underflows.  Whatever the summation order, each of the K products of a logit
@@ -16,19 +18,28 @@
 //      A = D 2^-126 (1 + Xmax + Wmax) covering flushed denormal inputs, products and
 //      partial sums (Xmax = max |x_k|, Wmax = 2^(e_max-126) > |w|).  S^ sums the same
 //      nonnegative terms, so S <= S^/(1-g) + A, and B(S^) = g (S^/(1-g) + A) + A,
-//      inflated by 2^-20 for its FP64 evaluation, bounds |z^ - z|; B grows with S^;
+//      inflated by 2^-20 for its FP64 evaluation, bounds |z^ - z|: B = c1 S^ + c0 with
+//      c1 = bound_slope(K).  B grows with S^;
 //   3. L = z* - B(S*) is below the true maximum, so every v with z^_v + B(S^_v) >= L
-//      is a candidate (the exact argmax always is).  With the block's largest S^ in B,
-//      a block adds its largest logit when that reaches L, and all of its rows when its
-//      second largest does too (otherwise no other row of it can);
-//   4. FP64 screen: each candidate's logit is recomputed from the W12 tiles in FP64 (a
+//      is a candidate (the exact argmax always is).  A group whose U + c0 is below L
+//      holds none; in the others, with the block's largest S^ in B, a block adds its
+//      largest logit when that reaches L, and all of its rows when its second largest
+//      does too (otherwise no other row of it can);
+//   4. a single candidate is the argmax.  Otherwise the FP64 screen: each candidate's
+//      logit is recomputed from the W12 tiles in FP64 (a
 //      BF16 product is exact in FP64; escape corrections add two terms each), within
 //      g64 S64 of the exact value; only the candidates whose FP64 upper bound reaches
-//      the largest FP64 lower bound survive;
-//   5. when more than one survives, each survivor's logit is recomputed exactly:
-//      sum_k x_k w_vk as an integer in units of 2^-266 (a BF16 product is
-//      +-Mx*Mw*2^(Ex+Ew) with 8-bit significands), accumulated in 64-bit LDS limbs; the
-//      largest exact value wins, lowest index on an exact tie.
+//      the largest FP64 lower bound survive.  Candidates are screened in chunks, so
+//      any number of them is screened (a first sweep finds the largest lower bound, a
+//      second keeps the survivors); a survivor whose bound g64 S64 is zero has an exact
+//      FP64 sum (every term is zero);
+//   5. when more than one survives and not all of them are exact in FP64, each
+//      survivor's logit is recomputed exactly: sum_k x_k w_vk as an integer in units of
+//      2^-266 (a BF16 product is +-Mx*Mw*2^(Ex+Ew) with 8-bit significands), one wave
+//      per survivor, each lane adding its products into its own column of 64-bit limbs
+//      in LDS, the columns then summed and carried; the largest exact value wins,
+//      lowest index on an exact tie.
+// A row of x whose every entry is +-0 has every exact logit 0: its argmax is index 0.
 // The review page ("The mechanisms it found") names a certified exact-argmax LM head,
 // and its caveats note that reduction order can flip near-ties: the exact logit makes
 // the answer independent of the order.  Accept: first i < n_draft with
@@ -41,10 +52,13 @@
 
 namespace w12 {
 
-constexpr int kLimbs = 18;   // 18 x 32 bits > 542 bits (largest |sum| for K < 2^20)
-constexpr uint32_t kScreenMax = 512;   // candidates screened in FP64 (more: all go exact)
-constexpr uint32_t kGroup = 4;         // candidates screened at once, kT / kGroup threads each
-constexpr uint32_t kCache = 9728;      // block maxima kept in LDS for the candidate scan
+constexpr int kLimbs = 18;             // 18 x 32 bits > 542 bits (largest |sum| for K < 2^20)
+constexpr uint32_t kT = 512;           // threads of the pass-2 workgroup (one workgroup per row)
+constexpr uint32_t kWaves = kT / 64u;
+constexpr uint32_t kScreenMax = 512;   // candidates screened per chunk (ids and results in LDS)
+constexpr uint32_t kUCache = 8192;     // group upper bounds kept in LDS for the group scan
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ bool exact_parts(uint32_t bits, int& sgn, uint32_t& mant, int& ex) {
   const uint32_t e = (bits >> 7) & 0xFFu, m = bits & 0x7Fu;
@@ -56,8 +70,7 @@ __device__ __forceinline__ bool exact_parts(uint32_t bits, int& sgn, uint32_t& m
 
 // Weight (v, kk) of a head of nb row-blocks (tile (b, g) at (g * nb + b) * 3072).
 __device__ __forceinline__ uint32_t decode_w(const uint8_t* tiles, uint32_t nb, uint32_t v,
-                                             uint32_t kk, const uint32_t lut[4],
-                                             uint32_t* code_out) {
+                                             uint32_t kk, const uint32_t lut[4]) {
   const uint32_t b = v >> 4, r = v & 15u, g = kk >> 7, kap = kk & 127u;
   const uint32_t q = (kap >> 3) & 3u, j = kap >> 5, i = kap & 7u;
   const uint32_t l = 16u * q + r, t = 8u * j + i;
@@ -66,118 +79,122 @@ __device__ __forceinline__ uint32_t decode_w(const uint8_t* tiles, uint32_t nb, 
   const uint32_t cw = *reinterpret_cast<const uint32_t*>(tb + 2048u + 16u * l + 4u * j);
   const uint32_t code = (cw >> (4u * (i >> 1) + 16u * (i & 1u))) & 0xFu;
   const uint32_t e = (lut[code >> 2] >> (8u * (code & 3u))) & 0xFFu;
-  *code_out = code;
   return ((sm & 0x80u) << 8) | (e << 7) | (sm & 0x7Fu);
 }
 
-__device__ __forceinline__ void limb_add(unsigned long long* limbs, int sgn, uint32_t prod, int sh,
-                                         bool subtract) {
-  if (prod == 0) return;
-  const unsigned long long v = (unsigned long long)prod << (sh & 31);
-  const int idx = sh >> 5;
-  long long lo = (long long)(v & 0xFFFFFFFFull), hi = (long long)(v >> 32);
-  if ((sgn < 0) != subtract) { lo = -lo; hi = -hi; }
-  if (lo) atomicAdd(limbs + idx, (unsigned long long)lo);
-  if (hi) atomicAdd(limbs + idx + 1, (unsigned long long)hi);
+// The BF16 weight of element t (0..31) of lane slot l from the slot's sign/mantissa
+// words (s_lo: t < 16, s_hi: t >= 16) and its four code words.
+__device__ __forceinline__ uint32_t slot_weight(const u32x4& s_lo, const u32x4& s_hi,
+                                                const u32x4& cw, uint32_t t,
+                                                const uint32_t lut[4]) {
+  const uint32_t jj = t >> 3, i = t & 7u;
+  const uint32_t sword = t < 16u ? s_lo[(t & 15u) >> 2] : s_hi[(t & 15u) >> 2];
+  const uint32_t sm = (sword >> (8u * (t & 3u))) & 0xFFu;
+  const uint32_t code = (cw[jj] >> (4u * (i >> 1) + 16u * (i & 1u))) & 0xFu;
+  const uint32_t e = (lut[code >> 2] >> (8u * (code & 3u))) & 0xFFu;
+  return ((sm & 0x80u) << 8) | (e << 7) | (sm & 0x7Fu);
 }
 
-constexpr uint32_t kT = 512;   // threads of the pass-2 workgroup (one workgroup per row)
+// Add sign * x * w (BF16 bits) to a lane's column of limbs (units of 2^-266); false if
+// either value is not finite.
+__device__ __forceinline__ bool limb_term(unsigned long long* col, uint32_t xb, uint32_t wb,
+                                          bool subtract) {
+  int sx, sw, ex, ew;
+  uint32_t mx, mw;
+  const bool okx = exact_parts(xb, sx, mx, ex), okw = exact_parts(wb, sw, mw, ew);
+  const uint32_t prod = mx * mw;   // < 2^16
+  if (prod != 0u) {
+    const int sh = ex + ew + 266;   // 0 .. 506
+    const unsigned long long v = (unsigned long long)prod << (sh & 31);
+    long long lo = (long long)(v & 0xFFFFFFFFull), hi = (long long)(v >> 32);
+    if (((sx * sw) < 0) != subtract) { lo = -lo; hi = -hi; }
+    const int idx = sh >> 5;
+    col[idx * 64] += (unsigned long long)lo;
+    col[(idx + 1) * 64] += (unsigned long long)hi;
+  }
+  return okx && okw;
+}
 
 __global__ __launch_bounds__(kT) void k_verify_pass2(VerifyArgs a) {
-  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-  __shared__ float s_bv[kT];
-  __shared__ int32_t s_bi[kT];
-  __shared__ double s_d0[kT], s_d1[kT];
-  __shared__ uint32_t s_u0[kT];
-  __shared__ unsigned long long limbs[kLimbs];
+  __shared__ float s_u[kUCache];
+  __shared__ int32_t s_cand[kScreenMax];   // the first candidates (the rest in global memory)
+  __shared__ uint32_t s_ce0[kScreenMax], s_ce1[kScreenMax];   // their escape ranges
+  __shared__ int32_t s_chunk[kScreenMax];  // ids of the chunk being screened
+  __shared__ uint32_t s_ke0[kScreenMax], s_ke1[kScreenMax];   // the chunk's escape ranges
+  __shared__ double s_z64[kScreenMax], s_b64[kScreenMax];
+  __shared__ double s_d0[kWaves], s_d1[kWaves];
+  __shared__ float s_wv[kWaves], s_ws[kWaves];
+  __shared__ int32_t s_wi[kWaves];
+  __shared__ uint32_t s_u0[kWaves];
+  __shared__ unsigned long long s_limb[kWaves][kLimbs * 64];   // one limb column per lane
+  __shared__ uint32_t s_dig[kWaves][kLimbs];
+  __shared__ int32_t s_sgn[kWaves], s_vid[kWaves];
   __shared__ uint32_t best[kLimbs];
   __shared__ int32_t s_best_v, s_best_sign;
-  __shared__ uint32_t s_cnt, s_bad, s_nsurv;
-  __shared__ double s_z64[kScreenMax], s_b64[kScreenMax];
-  __shared__ float s_rv[kCache], s_rs[kCache];
-  __shared__ int32_t s_cand[kScreenMax];   // the first candidates (the rest in global memory)
+  __shared__ uint32_t s_cnt, s_bad, s_nsurv, s_allexact;
+  __shared__ double s_lo64;
+  __shared__ int32_t s_result;
   const uint32_t row = blockIdx.x, tid = threadIdx.x, lane = tid & 63u, wave = tid >> 6;
   const uint16_t* xr = a.x + (uint64_t)row * a.k;
+  const float* gv = a.grp_v + (uint64_t)row * a.ngrp;
+  const int32_t* gi = a.grp_i + (uint64_t)row * a.ngrp;
+  const float* gs = a.grp_s + (uint64_t)row * a.ngrp;
+  const float* gu = a.grp_u + (uint64_t)row * a.ngrp;
   const float* rv = a.rbmax_v + (uint64_t)row * a.nb;
   const float* rv2 = a.rbmax_v2 + (uint64_t)row * a.nb;
   const float* rs = a.rbmax_s + (uint64_t)row * a.nb;
   const int32_t* ri = a.rbmax_i + (uint64_t)row * a.nb;
   int32_t* cand = a.cand + (uint64_t)row * a.n;
-  auto put = [&](uint32_t c, int32_t v) { if (c < kScreenMax) s_cand[c] = v; else cand[c] = v; };
+  // candidate ids; the first kScreenMax also keep their row-block's escape range
+  auto put = [&](uint32_t c, int32_t v, uint32_t e0, uint32_t e1) {
+    if (c < kScreenMax) { s_cand[c] = v; s_ce0[c] = e0; s_ce1[c] = e1; } else cand[c] = v;
+  };
   auto get = [&](uint32_t c) { return c < kScreenMax ? s_cand[c] : cand[c]; };
-  int32_t result = -1;
   uint32_t ncand = 0, nsurv = 0;
+  if (tid == 0) { s_cnt = 0; s_bad = 0; s_best_v = -1; s_result = -1; }
 
-  // 1. z* and its index over the block maxima (NaN marks a non-finite block); the
-  // maxima and their S are kept in LDS for the candidate scan (up to kCache blocks)
-  float bv = -__builtin_inff();
+  // 1. z*, its index and S* over the group records (NaN marks a group with a non-finite
+  // logit); the upper bounds U stay in LDS for the scan.  Every scan issues all of a
+  // thread's loads of a chunk (clamped indices) before using any; the result does not
+  // depend on the order (largest value, lowest index on ties).
+  float bv = -__builtin_inff(), bs = 0.f;
   int32_t bi = 0x7FFFFFFF;
   bool bad = false;
-  auto take = [&](uint32_t b, float v, int32_t i, float sb) {
-    if (b < kCache) { s_rv[b] = v; s_rs[b] = sb; }
-    if (v != v) bad = true;
-    else if (v > bv || (v == bv && i < bi)) { bv = v; bi = i; }
-  };
-  // Every scan below issues all of a thread's loads of a chunk (clamped indices) before
-  // using any, so a chunk costs one memory latency; the result does not depend on the
-  // order (largest value, lowest index on ties).
-  if ((a.nb & 3u) == 0u) {   // rows start on 16-byte boundaries: four blocks per load
-    typedef float f32x4v __attribute__((ext_vector_type(4)));
-    typedef int32_t i32x4v __attribute__((ext_vector_type(4)));
-    constexpr uint32_t kU = 6;
-    const uint32_t nb4 = a.nb / 4u;
-    for (uint32_t base = 0; base < nb4; base += kT * kU) {
-      f32x4v v[kU], sb[kU];
-      i32x4v iv[kU];
-#pragma unroll
-      for (uint32_t u = 0; u < kU; ++u) {
-        const uint32_t b4 = min(base + u * kT + tid, nb4 - 1u);
-        v[u] = reinterpret_cast<const f32x4v*>(rv)[b4];
-        iv[u] = reinterpret_cast<const i32x4v*>(ri)[b4];
-        sb[u] = reinterpret_cast<const f32x4v*>(rs)[b4];
-      }
-#pragma unroll
-      for (uint32_t u = 0; u < kU; ++u) {
-        const uint32_t b4 = base + u * kT + tid;
-        if (b4 < nb4) {
-#pragma unroll
-          for (uint32_t j = 0; j < 4; ++j) take(4u * b4 + j, v[u][j], iv[u][j], sb[u][j]);
-        }
-      }
-    }
-  } else {
-    constexpr uint32_t kU = 8;
-    for (uint32_t base = 0; base < a.nb; base += kT * kU) {
-      float v[kU], sb[kU];
-      int32_t iv[kU];
-#pragma unroll
-      for (uint32_t u = 0; u < kU; ++u) {
-        const uint32_t b = min(base + u * kT + tid, a.nb - 1u);
-        v[u] = rv[b];
-        iv[u] = ri[b];
-        sb[u] = rs[b];
-      }
-#pragma unroll
-      for (uint32_t u = 0; u < kU; ++u)
-        if (base + u * kT + tid < a.nb) take(base + u * kT + tid, v[u], iv[u], sb[u]);
-    }
-  }
-  // 2. Xmax (and finiteness of x), eight BF16 per load (k is a multiple of 128)
-  double xm = 0.0;
+  double xm = 0.0;   // Xmax (and finiteness of x), eight BF16 per load (k is a multiple of 128)
   {
-    constexpr uint32_t kU = 4;
+    constexpr uint32_t kU = 4, kXU = 2;
     const uint32_t nx = a.k / 8u;
-    for (uint32_t base = 0; base < nx; base += kT * kU) {
-      u32x4 xv[kU];
+    const uint32_t rounds = max((a.ngrp + kT * kU - 1) / (kT * kU), (nx + kT * kXU - 1) / (kT * kXU));
+    for (uint32_t rd = 0; rd < rounds; ++rd) {
+      const uint32_t base = rd * kT * kU, xbase = rd * kT * kXU;
+      float v[kU], s[kU], u[kU];
+      int32_t iv[kU];
+      u32x4 xv[kXU];
 #pragma unroll
-      for (uint32_t u = 0; u < kU; ++u)
-        xv[u] = reinterpret_cast<const u32x4*>(xr)[min(base + u * kT + tid, nx - 1u)];
+      for (uint32_t q = 0; q < kXU; ++q)
+        xv[q] = reinterpret_cast<const u32x4*>(xr)[min(xbase + q * kT + tid, nx - 1u)];
 #pragma unroll
-      for (uint32_t u = 0; u < kU; ++u) {
-        if (base + u * kT + tid >= nx) continue;
+      for (uint32_t q = 0; q < kU; ++q) {
+        const uint32_t G = min(base + q * kT + tid, a.ngrp - 1u);
+        v[q] = gv[G];
+        iv[q] = gi[G];
+        s[q] = gs[G];
+        u[q] = gu[G];
+      }
+#pragma unroll
+      for (uint32_t q = 0; q < kU; ++q) {
+        const uint32_t G = base + q * kT + tid;
+        if (G >= a.ngrp) continue;
+        if (G < kUCache) s_u[G] = u[q];
+        if (v[q] != v[q] || u[q] != u[q]) bad = true;
+        else if (v[q] > bv || (v[q] == bv && iv[q] < bi)) { bv = v[q]; bi = iv[q]; bs = s[q]; }
+      }
+#pragma unroll
+      for (uint32_t q = 0; q < kXU; ++q) {
+        if (xbase + q * kT + tid >= nx) continue;
 #pragma unroll
         for (uint32_t h = 0; h < 8; ++h) {
-          const uint32_t bits = (xv[u][h >> 1] >> (16u * (h & 1u))) & 0xFFFFu;
+          const uint32_t bits = (xv[q][h >> 1] >> (16u * (h & 1u))) & 0xFFFFu;
           if (((bits >> 7) & 0xFFu) == 0xFFu) bad = true;
           xm = fmax(xm, fabs((double)__uint_as_float(bits << 16)));
         }
@@ -188,105 +205,121 @@ __global__ __launch_bounds__(kT) void k_verify_pass2(VerifyArgs a) {
   // results in wave order
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) {
-    const float v2 = __shfl_xor(bv, off);
+    const float v2 = __shfl_xor(bv, off), s2 = __shfl_xor(bs, off);
     const int32_t i2 = __shfl_xor(bi, off);
-    if (v2 > bv || (v2 == bv && i2 < bi)) { bv = v2; bi = i2; }
+    if (v2 > bv || (v2 == bv && i2 < bi)) { bv = v2; bi = i2; bs = s2; }
     xm = fmax(xm, __shfl_xor(xm, off));
   }
-  if (tid == 0) { s_cnt = 0; s_bad = 0; s_best_v = -1; }
-  if (lane == 0) { s_bv[wave] = bv; s_bi[wave] = bi; s_d0[wave] = xm; }
-  __syncthreads();
+  __syncthreads();   // s_cnt, s_bad initialised
   if (bad) atomicOr(&s_bad, 1u);
-  bv = s_bv[0];
-  bi = s_bi[0];
+  if (lane == 0) { s_wv[wave] = bv; s_wi[wave] = bi; s_ws[wave] = bs; s_d0[wave] = xm; }
+  __syncthreads();
+  bv = s_wv[0];
+  bi = s_wi[0];
+  bs = s_ws[0];
   xm = s_d0[0];
-  for (uint32_t w = 1; w < kT / 64u; ++w) {
-    if (s_bv[w] > bv || (s_bv[w] == bv && s_bi[w] < bi)) { bv = s_bv[w]; bi = s_bi[w]; }
+  for (uint32_t w = 1; w < kWaves; ++w) {
+    if (s_wv[w] > bv || (s_wv[w] == bv && s_wi[w] < bi)) { bv = s_wv[w]; bi = s_wi[w]; bs = s_ws[w]; }
     xm = fmax(xm, s_d0[w]);
   }
-  __syncthreads();   // s_bad complete; s_bv / s_bi / s_d0 free again
   const float zmax = bv;
   const double dd = (double)a.k + 64.0;
   const double gam = dd * ldexp(1.0, -23) / (1.0 - dd * ldexp(1.0, -23));
   const double wmax = ldexp(1.0, (int)a.e_max - 126);
   const double absb = dd * ldexp(1.0, -126) * (1.0 + xm + wmax);
   const double infl = 1.0 + ldexp(1.0, -20);
-  // B(S^) = (g (S^/(1-g) + A) + A) * infl = c1 S^ + c0
-  const double c1 = gam / (1.0 - gam) * infl, c0 = (gam * absb + absb) * infl;
-  const uint32_t bstar = bi >= 0 && (uint32_t)bi < a.n ? (uint32_t)bi >> 4 : 0u;
-  const double lo = (double)zmax - (c1 * (double)rs[bstar] + c0);
+  const double c1 = bound_slope(a.k), c0 = (gam * absb + absb) * infl;
+  const double lo = (double)zmax - (c1 * (double)bs + c0);
   const bool row_ok = !s_bad && __builtin_isfinite(zmax) && lo == lo;
-  if (row_ok) {
-    // 3. candidates: a block's largest logit, and all its rows when its second largest
-    // also reaches L
-#pragma unroll 8
-    for (uint32_t b = tid; b < a.nb; b += kT) {
-      const double bb = c1 * (double)(b < kCache ? s_rs[b] : rs[b]) + c0;
-      if ((double)(b < kCache ? s_rv[b] : rv[b]) + bb < lo) continue;
-      const int32_t i1 = ri[b];
-      const float v2 = rv2[b];   // (both loads in flight together)
-      put(atomicAdd(&s_cnt, 1u), i1);
-      if ((double)v2 + bb >= lo)
-        for (uint32_t rr = 0; rr < 16; ++rr)
-          if ((int32_t)(16u * b + rr) != i1) put(atomicAdd(&s_cnt, 1u), (int32_t)(16u * b + rr));
+  const bool zero_row = row_ok && xm == 0.0;   // every product is +-0: every logit is 0
+  if (row_ok && !zero_row) {
+    // 2. candidates from the groups whose bound reaches L: a block's largest logit, and
+    // all its rows when its second largest also reaches L
+    for (uint32_t G = tid; G < a.ngrp; G += kT) {
+      const float u = G < kUCache ? s_u[G] : gu[G];
+      if ((double)u + c0 < lo) continue;
+      const uint32_t b0 = G * a.bpg;
+      float v[kMaxBpg], v2[kMaxBpg], sb[kMaxBpg];
+      int32_t i1[kMaxBpg];
+      uint32_t eo[kMaxBpg + 1];   // eo[q] = esc_off[b0 + q] (index clamped to nb)
+#pragma unroll
+      for (uint32_t q = 0; q < kMaxBpg; ++q) {   // every load of the group in flight at once
+        const uint32_t b = min(b0 + min(q, a.bpg - 1u), a.nb - 1u);
+        v[q] = rv[b];
+        v2[q] = rv2[b];
+        sb[q] = rs[b];
+        i1[q] = ri[b];
+      }
+#pragma unroll
+      for (uint32_t q = 0; q <= kMaxBpg; ++q) eo[q] = a.esc_off[min(b0 + q, a.nb)];
+#pragma unroll
+      for (uint32_t q = 0; q < kMaxBpg; ++q) {
+        const uint32_t b = b0 + q;
+        if (q >= a.bpg || b >= a.nb) continue;
+        const uint32_t e1 = eo[q + 1];   // esc_off[b + 1]
+        const double bb = c1 * (double)sb[q] + c0;
+        if ((double)v[q] + bb < lo) continue;
+        put(atomicAdd(&s_cnt, 1u), i1[q], eo[q], e1);
+        if ((double)v2[q] + bb >= lo)
+          for (uint32_t rr = 0; rr < 16; ++rr)
+            if ((int32_t)(16u * b + rr) != i1[q]) put(atomicAdd(&s_cnt, 1u), (int32_t)(16u * b + rr), eo[q], e1);
+      }
     }
     __syncthreads();
     ncand = s_cnt;
 
-    // 4. FP64 screen, up to kGroup candidates at a time (one or two when there are no
-    // more, so each has more threads and its loads take fewer rounds), per threads each;
-    // a candidate's escape offsets are requested with its tile loads.  Thread u of a
-    // candidate v = 16b + r takes lane slots (g, q) = j / 4, j % 4 for j = u, u + per,
-    // ...: slot l = 16q + r of tile (b, g) holds row r's columns 128g + 32jj + 8q + i
-    // (jj < 4, i < 8), sign/mantissa bytes at 16l and 1024 + 16l, code nibbles in the
-    // dwords at 2048 + 16l.  The threads also take the block's escape records of row r
-    // (the product decoded with code 0 is replaced).  Partial sums meet in fixed
-    // shuffle and LDS trees, so the screen is deterministic.  Summed in any order, the K
-    // products and two terms per escape (K' terms) give an FP64 logit within g64 S64 of
-    // the exact one, g64 = (K'+8) 2^-53 / (1 - (K'+8) 2^-53), S64 the sum of the terms'
-    // magnitudes.
-    const bool screen = ncand <= kScreenMax;
-    if (screen) {
-      const uint32_t grp = ncand <= 1u ? 1u : (ncand <= 2u ? 2u : kGroup);
+    // 3. FP64 screen of the chunk's candidates [c0i, c0i + nc): up to 8 at a time (fewer
+    // when there are fewer, so each has more threads and its loads take fewer rounds),
+    // kT / grp threads each.  Thread u of a candidate v = 16b + r takes 8-weight units
+    // U = u, u + per, ... of lane slots (g, q) = (U / 4) / 4, (U / 4) % 4: slot
+    // l = 16q + r of tile (b, g) holds row r's columns 128g + 32jj + 8q + i (jj < 4,
+    // i < 8), sign/mantissa bytes at 16l and 1024 + 16l, code nibbles in the dwords at
+    // 2048 + 16l.  The threads also
+    // take the block's escape records of row r (the product decoded with code 0 is
+    // replaced).  Partial sums meet in fixed shuffle and LDS trees, so the screen is
+    // deterministic.  Summed in any order, the K products and two terms per escape (K'
+    // terms) give an FP64 logit within g64 S64 of the exact one, g64 = (K'+8) 2^-53 /
+    // (1 - (K'+8) 2^-53), S64 the sum of the terms' magnitudes.
+    auto screen = [&](uint32_t nc) {   // ids in s_chunk[0, nc) -> s_z64, s_b64
+      const uint32_t grp = nc <= 1u ? 1u : (nc <= 2u ? 2u : (nc <= 4u ? 4u : 8u));
       const uint32_t per = kT / grp, cc = tid / per, u = tid % per;
-      for (uint32_t c0i = 0; c0i < ncand; c0i += grp) {
+      for (uint32_t c0i = 0; c0i < nc; c0i += grp) {
         const uint32_t c = c0i + cc;
-        const bool active = c < ncand;
+        const bool active = c < nc;
         double z = 0.0, sa = 0.0;
         uint32_t nesc = 0;
         if (active) {
-          const uint32_t v = (uint32_t)s_cand[c], b = v >> 4, r = v & 15u;
-          const uint32_t e0 = a.esc_off[b], e1 = a.esc_off[b + 1];
-          for (uint32_t j = u; j < 4u * a.g_cols; j += per) {
-            const uint32_t g = j >> 2, q = j & 3u, l = 16u * q + r;
+          const uint32_t v = (uint32_t)s_chunk[c], b = v >> 4, r = v & 15u;
+          const uint32_t e0 = s_ke0[c], e1 = s_ke1[c];
+          // the thread's first escape record, requested with its tiles
+          const uint32_t rec0 = e0 + u < e1 ? a.esc[e0 + u] : 0u;
+          // units of 8 weights: unit U = 4j + jj of slot j = (g, q) is group jj of row r's
+          // columns 128g + 32jj + 8q .. +7: its sign/mantissa bytes are 8 consecutive bytes
+          // of the slot's 16-byte row (t = 8jj + i: bytes 16l + (t & 15) + 1024 (t >= 16)),
+          // its codes one dword at 2048 + 16l + 4jj, its x values one 16-byte load
+          for (uint32_t U = u; U < 16u * a.g_cols; U += per) {
+            const uint32_t j = U >> 2, jj = U & 3u, g = j >> 2, q = j & 3u, l = 16u * q + r;
             const uint8_t* tb = a.tiles + ((uint64_t)g * a.nb + b) * 3072u + 16u * l;
-            const u32x4 s_lo = *reinterpret_cast<const u32x4*>(tb);
-            const u32x4 s_hi = *reinterpret_cast<const u32x4*>(tb + 1024);
-            const u32x4 cw = *reinterpret_cast<const u32x4*>(tb + 2048);
+            const uint2 smv = *reinterpret_cast<const uint2*>(tb + 1024u * (jj >> 1) + 8u * (jj & 1u));
+            const uint32_t cwj = *reinterpret_cast<const uint32_t*>(tb + 2048u + 4u * jj);
+            const u32x4 xv = *reinterpret_cast<const u32x4*>(xr + 128u * g + 32u * jj + 8u * q);
 #pragma unroll
-            for (uint32_t jj = 0; jj < 4; ++jj) {
-              const u32x4 xv = *reinterpret_cast<const u32x4*>(xr + 128u * g + 32u * jj + 8u * q);
-#pragma unroll
-              for (uint32_t i = 0; i < 8; ++i) {
-                const uint32_t t = 8u * jj + i;
-                const uint32_t sword = t < 16u ? s_lo[(t & 15u) >> 2] : s_hi[(t & 15u) >> 2];
-                const uint32_t sm = (sword >> (8u * (t & 3u))) & 0xFFu;
-                const uint32_t code = (cw[jj] >> (4u * (i >> 1) + 16u * (i & 1u))) & 0xFu;
-                const uint32_t e = (a.lut[code >> 2] >> (8u * (code & 3u))) & 0xFFu;
-                const uint32_t wb = ((sm & 0x80u) << 8) | (e << 7) | (sm & 0x7Fu);
-                const uint32_t xb = (xv[i >> 1] >> (16u * (i & 1u))) & 0xFFFFu;
-                const double pr = (double)__uint_as_float(xb << 16) * (double)__uint_as_float(wb << 16);
-                z += pr;
-                sa += fabs(pr);
-              }
+            for (uint32_t i = 0; i < 8; ++i) {
+              const uint32_t sm = ((i < 4u ? smv.x : smv.y) >> (8u * (i & 3u))) & 0xFFu;
+              const uint32_t code = (cwj >> (4u * (i >> 1) + 16u * (i & 1u))) & 0xFu;
+              const uint32_t e = (a.lut[code >> 2] >> (8u * (code & 3u))) & 0xFFu;
+              const uint32_t wb = ((sm & 0x80u) << 8) | (e << 7) | (sm & 0x7Fu);
+              const uint32_t xb = (xv[i >> 1] >> (16u * (i & 1u))) & 0xFFFFu;
+              const double pr = (double)__uint_as_float(xb << 16) * (double)__uint_as_float(wb << 16);
+              z += pr;
+              sa += fabs(pr);
             }
           }
           for (uint32_t i = e0 + u; i < e1; i += per) {
-            const uint32_t rec = a.esc[i];
+            const uint32_t rec = i == e0 + u ? rec0 : a.esc[i];
             const uint32_t kk = (rec >> 8) & 0xFFFFFu;
             if ((rec >> 28) != r || kk >= a.k) continue;   // another row, or malformed
-            uint32_t code;
-            const uint32_t wb = decode_w(a.tiles, a.nb, v, kk, a.lut, &code);
+            const uint32_t wb = decode_w(a.tiles, a.nb, v, kk, a.lut);
             const uint32_t wt = (wb & 0x807Fu) | ((rec & 0xFFu) << 7);
             const double xv = (double)__uint_as_float((uint32_t)xr[kk] << 16);
             const double pw = xv * (double)__uint_as_float(wb << 16);
@@ -316,104 +349,165 @@ __global__ __launch_bounds__(kT) void k_verify_pass2(VerifyArgs a) {
         }
         __syncthreads();
       }
-      // survivors: every candidate whose upper bound reaches the largest lower bound
-      if (tid == 0) {
-        double lo64 = -__builtin_inf();
-        for (uint32_t c = 0; c < ncand; ++c) lo64 = fmax(lo64, s_z64[c] - s_b64[c]);
-        uint32_t ns = 0;
-        for (uint32_t c = 0; c < ncand; ++c)
-          if (s_z64[c] + s_b64[c] >= lo64) s_cand[ns++] = s_cand[c];
-        s_nsurv = ns;
+    };
+    // first sweep: the largest FP64 lower bound; second sweep: the survivors, compacted
+    // into the candidate list (a survivor's position never passes its own, so the
+    // chunk's ids, copied to s_chunk first, are never overwritten before they are read).
+    // A survivor whose bound is zero has S64 = 0: every term is zero and its logit is
+    // exactly 0; when every survivor is such, the lowest index among them wins.
+    // A single candidate is the argmax (the exact argmax is always a candidate).
+    if (tid == 0) {
+      s_lo64 = -__builtin_inf();
+      s_nsurv = ncand == 1u ? 1u : 0u;
+      s_allexact = 1;
+      s_result = 0x7FFFFFFF;
+    }
+    const bool one_chunk = ncand <= kScreenMax;
+    for (int sweep = ncand == 1u ? 2 : (one_chunk ? 1 : 0); sweep < 2; ++sweep) {
+      for (uint32_t cb = 0; cb < ncand; cb += kScreenMax) {
+        const uint32_t nc = min(ncand - cb, kScreenMax);
+        __syncthreads();   // the previous chunk's ids and results are consumed
+        for (uint32_t c = tid; c < nc; c += kT) {
+          const uint32_t cc = cb + c;
+          const int32_t v = get(cc);
+          s_chunk[c] = v;
+          s_ke0[c] = cc < kScreenMax ? s_ce0[cc] : a.esc_off[(uint32_t)v >> 4];
+          s_ke1[c] = cc < kScreenMax ? s_ce1[cc] : a.esc_off[((uint32_t)v >> 4) + 1u];
+        }
+        __syncthreads();
+        screen(nc);
+        if (tid == 0) {
+          if (sweep == 0 || one_chunk) {
+            double l64 = s_lo64;
+            for (uint32_t c = 0; c < nc; ++c) l64 = fmax(l64, s_z64[c] - s_b64[c]);
+            s_lo64 = l64;
+          }
+          if (sweep == 1) {
+            const double l64 = s_lo64;
+            uint32_t ns = s_nsurv;
+            for (uint32_t c = 0; c < nc; ++c) {
+              if (s_z64[c] + s_b64[c] < l64) continue;
+              put(ns++, s_chunk[c], s_ke0[c], s_ke1[c]);
+              if (s_b64[c] != 0.0) s_allexact = 0;
+              s_result = min(s_result, s_chunk[c]);   // the lowest survivor
+            }
+            s_nsurv = ns;
+          }
+        }
       }
-    } else if (tid == 0) {
-      s_nsurv = ncand;   // too many to screen: every candidate goes exact
     }
     __syncthreads();
     nsurv = s_nsurv;
-    if (nsurv == 1u) {
-      result = get(0);
+    const bool need_exact = nsurv > 1u && !s_allexact;
+    const int32_t lowest = s_result;
+    __syncthreads();   // every thread has read s_result before it is rewritten
+    if (!need_exact) {
+      if (tid == 0) s_result = nsurv == 1u ? get(0) : lowest;
     } else {
-      // 5. exact recompute of the survivors
-      for (uint32_t c = 0; c < nsurv; ++c) {
-        const uint32_t v = (uint32_t)get(c);
-        if (tid < kLimbs) limbs[tid] = 0ull;
-        __syncthreads();
-        uint32_t code;
-        for (uint32_t kk = tid; kk < a.k; kk += kT) {
-          const uint32_t wb = decode_w(a.tiles, a.nb, v, kk, a.lut, &code);
-          int sx_, sw_, ex_, ew_;
-          uint32_t mx_, mw_;
-          const bool okx = exact_parts(xr[kk], sx_, mx_, ex_);
-          const bool okw = exact_parts(wb, sw_, mw_, ew_);
-          if (!okx || !okw) atomicOr(&s_bad, 1u);
-          limb_add(limbs, sx_ * sw_, mx_ * mw_, ex_ + ew_ + 266, false);
+      // 4. exact recompute of the survivors, one wave each (kWaves at a time); lane l
+      // adds its products into limb column l (no two lanes share a word), then 18 lanes
+      // sum the columns and lane 0 carries them into 32-bit digits and a sign
+      for (uint32_t c0i = 0; c0i < nsurv; c0i += kWaves) {
+        const uint32_t c = c0i + wave;
+        unsigned long long* col = &s_limb[wave][lane];
+#pragma unroll
+        for (int i = 0; i < kLimbs; ++i) col[i * 64] = 0ull;
+        bool ok = true;
+        if (c < nsurv) {
+          const uint32_t v = (uint32_t)get(c), b = v >> 4, r = v & 15u;
+          for (uint32_t j = lane; j < 4u * a.g_cols; j += 64u) {
+            const uint32_t g = j >> 2, q = j & 3u, l = 16u * q + r;
+            const uint8_t* tb = a.tiles + ((uint64_t)g * a.nb + b) * 3072u + 16u * l;
+            const u32x4 s_lo = *reinterpret_cast<const u32x4*>(tb);
+            const u32x4 s_hi = *reinterpret_cast<const u32x4*>(tb + 1024);
+            const u32x4 cw = *reinterpret_cast<const u32x4*>(tb + 2048);
+#pragma unroll
+            for (uint32_t jj = 0; jj < 4; ++jj) {
+              const u32x4 xv = *reinterpret_cast<const u32x4*>(xr + 128u * g + 32u * jj + 8u * q);
+#pragma unroll
+              for (uint32_t i = 0; i < 8; ++i) {
+                const uint32_t wb = slot_weight(s_lo, s_hi, cw, 8u * jj + i, a.lut);
+                const uint32_t xb = (xv[i >> 1] >> (16u * (i & 1u))) & 0xFFFFu;
+                ok = limb_term(col, xb, wb, false) && ok;
+              }
+            }
+          }
+          // escapes of this row: replace the product decoded with the stored code
+          const uint32_t e0 = c < kScreenMax ? s_ce0[c] : a.esc_off[b];
+          const uint32_t e1 = c < kScreenMax ? s_ce1[c] : a.esc_off[b + 1];
+          for (uint32_t i = e0 + lane; i < e1; i += 64u) {
+            const uint32_t rec = a.esc[i];
+            const uint32_t kk = (rec >> 8) & 0xFFFFFu;
+            if ((rec >> 28) != r || kk >= a.k) continue;
+            const uint32_t wb = decode_w(a.tiles, a.nb, v, kk, a.lut);
+            const uint32_t wt = (wb & 0x807Fu) | ((rec & 0xFFu) << 7);
+            limb_term(col, xr[kk], wb, true);
+            ok = limb_term(col, xr[kk], wt, false) && ok;
+          }
+          if (!ok) atomicOr(&s_bad, 1u);
         }
-        // escapes of this row: replace the product decoded with the stored code
-        const uint32_t b = v >> 4, r = v & 15u;
-        const uint32_t e0 = a.esc_off[b], e1 = a.esc_off[b + 1];
-        for (uint32_t i = e0 + tid; i < e1; i += kT) {
-          const uint32_t rec = a.esc[i];
-          if ((rec >> 28) != r || ((rec >> 8) & 0xFFFFFu) >= a.k) continue;
-          const uint32_t kk = (rec >> 8) & 0xFFFFFu;
-          const uint32_t wb = decode_w(a.tiles, a.nb, v, kk, a.lut, &code);
-          const uint32_t wt = (wb & 0x807Fu) | ((rec & 0xFFu) << 7);
-          int sx_, sw_, ex_, ew_;
-          uint32_t mx_, mw_;
-          exact_parts(xr[kk], sx_, mx_, ex_);
-          if (exact_parts(wb, sw_, mw_, ew_)) limb_add(limbs, sx_ * sw_, mx_ * mw_, ex_ + ew_ + 266, true);
-          if (!exact_parts(wt, sw_, mw_, ew_)) atomicOr(&s_bad, 1u);
-          limb_add(limbs, sx_ * sw_, mx_ * mw_, ex_ + ew_ + 266, false);
+        __syncthreads();   // every lane's column is written
+        if (c < nsurv && lane < (uint32_t)kLimbs) {
+          long long t = 0;
+          for (uint32_t l = 0; l < 64u; ++l) t += (long long)s_limb[wave][lane * 64u + l];
+          s_limb[wave][lane * 64u] = (unsigned long long)t;   // column 0 of limb `lane`: the row sum
         }
-        __syncthreads();
-        if (tid == 0) {
+        __syncthreads();   // the column sums are written
+        if (c < nsurv && lane == 0) {
           // normalise to 32-bit digits; the final carry is the sign (0 or -1)
-          uint32_t dig[kLimbs];
           long long carry = 0;
           for (int i = 0; i < kLimbs; ++i) {
-            const long long t = (long long)limbs[i] + carry;
-            dig[i] = (uint32_t)(t & 0xFFFFFFFFll);
+            const long long t = (long long)s_limb[wave][i * 64] + carry;
+            s_dig[wave][i] = (uint32_t)(t & 0xFFFFFFFFll);
             carry = t >> 32;
           }
-          bool better;
-          if (s_best_v < 0) {
-            better = true;
-          } else if ((int32_t)carry != s_best_sign) {
-            better = (int32_t)carry > s_best_sign;
-          } else {
-            int cmp = 0;
-            for (int i = kLimbs - 1; i >= 0 && cmp == 0; --i)
-              cmp = dig[i] > best[i] ? 1 : (dig[i] < best[i] ? -1 : 0);
-            better = cmp > 0 || (cmp == 0 && (int32_t)v < s_best_v);
-          }
-          if (better) {
-            for (int i = 0; i < kLimbs; ++i) best[i] = dig[i];
-            s_best_sign = (int32_t)carry;
-            s_best_v = (int32_t)v;
+          s_sgn[wave] = (int32_t)carry;
+          s_vid[wave] = (int32_t)get(c);
+        }
+        __syncthreads();
+        if (tid == 0) {   // this round's survivors against the best so far
+          for (uint32_t w = 0; w < kWaves && c0i + w < nsurv; ++w) {
+            bool better;
+            if (s_best_v < 0) {
+              better = true;
+            } else if (s_sgn[w] != s_best_sign) {
+              better = s_sgn[w] > s_best_sign;
+            } else {
+              int cmp = 0;
+              for (int i = kLimbs - 1; i >= 0 && cmp == 0; --i)
+                cmp = s_dig[w][i] > best[i] ? 1 : (s_dig[w][i] < best[i] ? -1 : 0);
+              better = cmp > 0 || (cmp == 0 && s_vid[w] < s_best_v);
+            }
+            if (better) {
+              for (int i = 0; i < kLimbs; ++i) best[i] = s_dig[w][i];
+              s_best_sign = s_sgn[w];
+              s_best_v = s_vid[w];
+            }
           }
         }
         __syncthreads();
       }
-      result = s_bad ? -1 : s_best_v;
+      if (tid == 0) s_result = s_bad ? -1 : s_best_v;
     }
+  } else if (tid == 0) {
+    s_result = zero_row ? 0 : -1;
   }
-  __shared__ int32_t s_result;
+  __syncthreads();
+  const int32_t result = s_result;
   if (tid == 0) {
     a.argmax[row] = result;
     if (a.ncand) { a.ncand[2 * row] = (int32_t)ncand; a.ncand[2 * row + 1] = (int32_t)nsurv; }
-    s_result = result;
   }
-  __syncthreads();
-  result = s_result;
   // accepted-prefix lengths: pass 1 set each to its draft length; the first mismatching
   // row of a request wins.  One request over all rows, or one thread per request entry.
   if (!a.req_off) {
     if (tid == 0 && row < a.n_draft && result != a.draft[row]) atomicMin(a.accepted, (int32_t)row);
   } else {
     for (uint32_t r = tid; r < a.n_req; r += kT) {
-      int32_t lo, nd;
-      if (req_entry(a.req_off, a.req_ndraft, r, a.m, lo, nd) && (int32_t)row >= lo &&
-          (int32_t)row < lo + nd && result != a.draft[row])
-        atomicMin(a.accepted + r, (int32_t)row - lo);
+      int32_t lo_r, nd;
+      if (req_entry(a.req_off, a.req_ndraft, r, a.m, lo_r, nd) && (int32_t)row >= lo_r &&
+          (int32_t)row < lo_r + nd && result != a.draft[row])
+        atomicMin(a.accepted + r, (int32_t)row - lo_r);
     }
   }
 }
