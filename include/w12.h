@@ -47,9 +47,12 @@
  *    launched and outputs are untouched.  Launch failures return W12_ERR_HIP; device
  *    faults surface at the caller's next synchronisation.
  *  - The workspace `ws` (device, w12_workspace_bytes(op, ...) bytes, 256-byte aligned;
- *    may be NULL when that size is 0) holds intermediate results only: its contents
- *    need no initialisation and are not meaningful after the call.  Two calls that run
- *    concurrently must not share a workspace.
+ *    may be NULL when that size is 0) holds intermediate results.  GEMM workspaces
+ *    (W12_OP_GEMM, W12_OP_GEMM_BF16, W12_OP_GEMM_GROUP) begin with the split-K tickets
+ *    (4096 bytes), which must be zero before the first call that uses the workspace
+ *    (a zero-filled allocation, or w12_workspace_init); every call leaves them zero, so
+ *    one zeroing serves every later call of any shape.  Nothing else in any workspace
+ *    needs initialisation.  Two calls that run concurrently must not share a workspace.
  */
 #ifndef W12_H
 #define W12_H
@@ -103,9 +106,9 @@ size_t w12_tiles_bytes(uint64_t n, uint64_t k);
 
 /* Workspace bytes needed by `op` for m rows (ignored by ENCODE/DECODE) and an
  * n x k weight; 0 for an invalid op or shape, and 0 when the op needs none (DECODE,
- * and GEMM shapes that are not split along K).  GEMM split along K needs FP32
- * partials [splits][m][n] and the splits' row sums of x^2 [splits][m] (RMS launches),
- * each from a 256-byte boundary; VERIFY holds, each region starting on a 256-byte boundary
+ * and GEMM shapes that are not split along K).  GEMM split along K needs the tickets
+ * (4096 bytes), FP32 partials [splits][m][n] and the row-block groups' row sums of x^2
+ * [groups][splits][m] (RMS launches), each from a 256-byte boundary; VERIFY holds, each region starting on a 256-byte boundary
  * in this order: per-row diagnostic counts (int32 [m][2]: candidate logits, those left
  * after the FP64 screen), the per-row-block records of the first pass (largest FP32
  * logit, second largest, largest sum_k |x_k||w_k|, each FP32 [m][n/16]; index of the
@@ -115,8 +118,8 @@ size_t w12_tiles_bytes(uint64_t n, uint64_t k);
  * candidate lists (int32 [m][n]); all readable after a call for diagnostics.  ENCODE holds the histogram and per-tile escape counts. */
 size_t w12_workspace_bytes(int op, uint32_t m, uint64_t n, uint64_t k);
 
-/* Zero-fills `ws` on `stream` with a kernel (no hipMemset); a convenience, no call
- * requires a zeroed workspace. */
+/* Zero-fills `ws` on `stream` with a kernel (no hipMemset): prepares a GEMM workspace
+ * whose memory was not allocated zero-filled (its split-K tickets must start at zero). */
 w12_status w12_workspace_init(void* ws, size_t ws_bytes, void* stream);
 
 /* Encode, first half (exponent histogram -> codebook, e_max, n_esc).
@@ -143,9 +146,9 @@ w12_status w12_decode(const w12_desc* d, uint16_t* w_out, void* stream);
  * 1..W12_MAX_M,
  * FP32 accumulation, round-to-nearest-even to BF16.  IEEE propagation for non-finite
  * inputs.  ws: w12_workspace_bytes(W12_OP_GEMM, ...) bytes (may be NULL when that is
- * 0; no initialization needed); calls that share a workspace must be ordered on one
- * stream.  The result is deterministic: when K is split, a second kernel sums the FP32
- * partials in split order. */
+ * 0; its tickets zeroed once, see above); calls that share a workspace must be ordered on
+ * one stream.  The result is deterministic: when K is split, the split that finishes last
+ * in each row-block group sums the FP32 partials of all splits in split order. */
 w12_status w12_gemm(const uint16_t* x, uint32_t m, const w12_desc* d, uint16_t* y,
                     void* ws, size_t ws_bytes, void* stream);
 

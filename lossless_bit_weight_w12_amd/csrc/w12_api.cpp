@@ -31,7 +31,7 @@ static_assert((W12_CS_NW == 4 || W12_CS_NW == 5) && (W12_CS_FEW_NW == 4 || W12_C
 #ifndef W12_NS_CAP
 #define W12_NS_CAP 8
 #endif
-static_assert(W12_NS_CAP >= 1 && W12_NS_CAP <= w12::kMaxSplit, "split cap within the reduce kernel's limit");
+static_assert(W12_NS_CAP >= 1 && W12_NS_CAP <= w12::kMaxSplit, "split cap within the completing split's limit");
 #ifndef W12_CS_MIN_COLS
 #define W12_CS_MIN_COLS 4
 #endif
@@ -136,7 +136,7 @@ GemmPlan make_plan(uint32_t m, uint64_t n, uint64_t k, int epi, bool bf16_src = 
   }
   uint64_t ns = 1;
   // W12 column-synchronous launches that already fill the chip (>= 512 four-wave
-  // workgroups) keep K whole: the reduce kernel and the partials cost more than the
+  // workgroups) keep K whole: the partials and their completion cost more than the
   // extra parallelism gains.  The BF16 kernel (4 KB tiles) is faster split: measured
   // on the MLP gate+up at M16 / M32, 81 / 92 us split in two against 87 / 100 us whole.
   const bool keep_k = !bf16_src && p.kind == KIND_COLUMN_SYNC &&
@@ -151,23 +151,43 @@ GemmPlan make_plan(uint32_t m, uint64_t n, uint64_t k, int epi, bool bf16_src = 
   return p;
 }
 
-// GEMM workspace when K is split: FP32 partials [nsplit][m][n], summed by the reduce
-// kernel, then (RMS launches) each split's sum of x^2 per row [nsplit][m]; no state
-// survives a call.
-size_t split_ws_bytes(uint64_t nsplit, uint32_t m, uint64_t n) {
-  return nsplit > 1 ? align256((size_t)nsplit * m * n * 4) + align256((size_t)nsplit * m * 4) : 0;
+// GEMM workspace when K is split: the row-block groups' tickets (a fixed 4 KB region at the
+// start: they must be zero before the first split launch and every launch leaves them
+// zero), the FP32 partials [nsplit][m][n], and (RMS launches) each group's per-split sums
+// of x^2 [groups][nsplit][m].  A split launch has fewer than 1024 row-block groups (it is
+// split because it has fewer than kTargetWorkgroups four-wave workgroup equivalents).
+constexpr size_t kTicketBytes = 4096;
+constexpr uint32_t kMaxTickets = kTicketBytes / 4;
+
+size_t split_ws_bytes(uint64_t nsplit, uint32_t m, uint64_t n, uint64_t groups) {
+  return nsplit > 1 ? kTicketBytes + align256((size_t)nsplit * m * n * 4) +
+                          align256((size_t)groups * nsplit * m * 4)
+                    : 0;
 }
 
 size_t gemm_ws_bytes(uint32_t m, uint64_t n, uint64_t k, bool bf16_src = false) {
-  return split_ws_bytes(make_plan(m, n, k, EPI_BF16, bf16_src).nsplit, m, n);
+  const GemmPlan p = make_plan(m, n, k, EPI_BF16, bf16_src);
+  return split_ws_bytes(p.nsplit, m, n, p.n_rbg);
 }
 
 // A group may run as two launches (one per codebook kind), each over part of the rows:
-// enough for the most splits any part can take.
+// enough for the most splits any part can take, and for the most row-block groups (W12
+// launches take at least four row-blocks per workgroup).
 size_t group_ws_bytes(uint32_t m, uint64_t n_total, uint64_t k) {
   const uint64_t g = k / 128;
   const uint64_t cap = std::min<uint64_t>(W12_NS_CAP, std::max<uint64_t>(g / 4, 1));
-  return split_ws_bytes(cap, m, n_total);
+  const uint64_t groups = std::min<uint64_t>((n_total / 16 + 3) / 4, kMaxTickets);
+  return split_ws_bytes(cap, m, n_total, groups);
+}
+
+// Point a launch's split-K state into the workspace (nothing when K is whole).
+bool set_split_ws(GemmArgs& a, void* ws, const GemmPlan& p, uint32_t m, uint64_t n) {
+  if (p.nsplit <= 1) return true;
+  if (p.n_rbg > kMaxTickets) return false;   // (no plan splits that many groups)
+  a.p.tickets = (uint32_t*)ws;
+  a.partial = (float*)((uint8_t*)ws + kTicketBytes);
+  a.p.ss = (float*)((uint8_t*)a.partial + align256((size_t)p.nsplit * m * n * 4));
+  return true;
 }
 
 // Verify workspace: per-row diagnostic counts first (a fixed place), then the
@@ -261,6 +281,7 @@ void fill_params(GemmParams& p, uint32_t m, uint64_t k, uint64_t n_total, uint32
   p.nseg = nseg;
   p.rms = 0;
   p.ss = nullptr;
+  p.tickets = nullptr;
 }
 
 // One launch over segments ds[0..nseg) (same k, same codebook kind): y_i = x . W_i^T,
@@ -271,7 +292,6 @@ hipError_t launch_w12_group(const uint16_t* x, uint32_t m, const w12_desc* const
   GemmArgs a;
   memset(&a, 0, sizeof(a));
   a.x = x;
-  a.partial = (float*)ws;
   uint64_t n_total = 0;
   for (uint32_t i = 0; i < nseg; ++i) {
     a.p.seg[i] = w12_seg(ds[i], ys[i], (uint32_t)(n_total / 16));
@@ -280,8 +300,7 @@ hipError_t launch_w12_group(const uint16_t* x, uint32_t m, const w12_desc* const
   fill_params(a.p, m, ds[0]->k, n_total, nseg);
   const GemmPlan p = make_plan(m, n_total, ds[0]->k, EPI_BF16);
   a.p.rms = rms ? 1u : 0u;
-  if (p.nsplit > 1)
-    a.p.ss = (float*)((uint8_t*)ws + align256((size_t)p.nsplit * m * n_total * 4));
+  if (!set_split_ws(a, ws, p, m, n_total)) return hipErrorInvalidValue;
   const int src = codebook_is_run(ds[0]->codebook) ? SRC_RUN : SRC_LUT;
   return launch_gemm(a, src, EPI_BF16, p, s);
 }
@@ -541,11 +560,11 @@ w12_status w12_gemm_bf16(const uint16_t* x, uint32_t m, const uint16_t* w, uint6
   GemmArgs a;
   memset(&a, 0, sizeof(a));
   a.x = x;
-  a.partial = (float*)ws;
   a.p.seg[0].w = (const uint8_t*)w;
   a.p.seg[0].y = y;
   a.p.seg[0].n = (uint32_t)n;
   fill_params(a.p, m, k, n, 1);
+  if (!set_split_ws(a, ws, p, m, n)) return W12_ERR_HIP;
   return hip_status(launch_gemm(a, SRC_BF16, EPI_BF16, p, (hipStream_t)stream));
 }
 
@@ -571,11 +590,11 @@ w12_status w12_gemm_bf16_tiled(const uint16_t* x, uint32_t m, const void* w_tile
   GemmArgs a;
   memset(&a, 0, sizeof(a));
   a.x = x;
-  a.partial = (float*)ws;
   a.p.seg[0].w = (const uint8_t*)w_tiled;
   a.p.seg[0].y = y;
   a.p.seg[0].n = (uint32_t)n;
   fill_params(a.p, m, k, n, 1);
+  if (!set_split_ws(a, ws, p, m, n)) return W12_ERR_HIP;
   return hip_status(launch_gemm(a, SRC_BF16T, EPI_BF16, p, (hipStream_t)stream));
 }
 

@@ -31,8 +31,9 @@
 // Escapes (exponents outside the codebook) are patched into the unpacked registers by
 //   the owning lane, walking the row-block's sorted escape list through a 4-record
 //   window in scalar registers.
-// Split-K (gridDim.y > 1): FP32 partials go to the workspace and k_splitk_reduce sums
-//   them in split order (deterministic).
+// Split-K (gridDim.y > 1): FP32 partials go to the workspace at device scope and the
+//   split that finishes last in its row-block group sums them in split order
+//   (deterministic; see split_last).
 // RMS launches (p.rms): the output rows are divided by the RMS of their x rows, summed
 //   from the staged x units (harness op of the layer chain, not the W12 method).
 // The logits epilogue (verification pass 1) keeps per row-block the two largest logits,
@@ -169,6 +170,48 @@ constexpr int kRsrcWord3 = 0x00020000;
 constexpr int kCpolNT = 2;   // cache policy of a buffer load: nontemporal (streaming)
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRsrcWord3);
+}
+
+// Split-K completion inside the GEMM launch.  The K splits of one row-block group run on
+// any XCDs, whose L2 caches are not coherent with one another for plain accesses.  Every
+// split writes its FP32 partials (and, on RMS launches, its rows' sums of x^2) with
+// device-scope stores (cache policy sc1: written through to device-coherent memory),
+// waits until they are complete, and then takes a ticket with a device-scope atomic; the
+// split that takes the last ticket resets it to zero for the next launch and reads every
+// split's partials with device-scope loads (sc1: never served from a stale cache line),
+// summing them in split order, so the result is the same whichever split finishes last.
+// No workgroup ever waits for another.  Tickets start at zero (a zeroed workspace) and
+// every launch leaves them at zero.
+constexpr int kCpolDevice = 16;   // sc1: coherent at device scope
+__device__ __forceinline__ void st_dev(__amdgpu_buffer_rsrc_t rs, uint32_t off, f32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rs, off, 0, kCpolDevice);
+}
+__device__ __forceinline__ void st_dev(__amdgpu_buffer_rsrc_t rs, uint32_t off, float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rs, off, 0, kCpolDevice);
+}
+__device__ __forceinline__ f32x4 ld_dev4(__amdgpu_buffer_rsrc_t rs, uint32_t off) {
+  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, kCpolDevice));
+}
+__device__ __forceinline__ float ld_dev1(__amdgpu_buffer_rsrc_t rs, uint32_t off) {
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, kCpolDevice));
+}
+
+// Called by every thread of a split workgroup after its device-scope stores: true in the
+// workgroup that finished last among the gridDim.y splits of row-block group `grp`.
+__device__ __forceinline__ bool split_last(uint32_t* tickets, uint32_t grp) {
+  __shared__ uint32_t s_last;
+  // this thread's device-scope stores are complete (visible at device scope) ...
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();   // ... and so are every other thread's of the workgroup
+  if (threadIdx.x == 0) {
+    const uint32_t old = __hip_atomic_fetch_add(tickets + grp, 1u, __ATOMIC_RELAXED,
+                                                __HIP_MEMORY_SCOPE_AGENT);
+    const bool last = old + 1u == gridDim.y;
+    if (last) __hip_atomic_store(tickets + grp, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_last = last ? 1u : 0u;
+  }
+  __syncthreads();
+  return s_last != 0u;
 }
 
 // One tile (W12 or 4 KB BF16) through a buffer resource over exactly its bytes, built
@@ -370,8 +413,8 @@ __device__ __forceinline__ void x_store(const XStage<MT>& st, uint16_t* xw, int 
 
 // M: x rows staged (compile-time; the VALU path's rows, or for MFMA 4, 8 or 16 of the
 // MT = 16 columns of the B operand); MT: LDS rows.
-// EPI_BF16 with gridDim.y > 1 writes FP32 partials [split][m][n] (reduced by
-// k_splitk_reduce); with one split it writes y directly.
+// EPI_BF16 with gridDim.y > 1 writes FP32 partials [split][m][n] and the last split of
+// the workgroup's row-block group writes y; with one split it writes y directly.
 template <int M, int MT, bool MF, int RBW, int NWV, int SRC, int EPI>
 __global__ __launch_bounds__(NWV * 64) void k_gemm(
     const uint16_t* __restrict__ x, float* __restrict__ out_f32, float* __restrict__ out_s,
@@ -561,8 +604,11 @@ __global__ __launch_bounds__(NWV * 64) void k_gemm(
     return t;
   };
   __syncthreads();   // LDS x no longer read: reuse it for the cross-wave reduction
-  if (EPI == EPI_BF16 && p.rms && gridDim.y > 1 && blockIdx.x == 0 && tid < M && (uint32_t)tid < m_rows)
-    p.ss[(size_t)blockIdx.y * m_rows + tid] = row_ss(tid);   // this split's part, for the reduce
+  // RMS launches with K split: this split's row sums in the group's slot
+  // ss[group][split][row], at device scope, for the split that completes the group
+  const __amdgpu_buffer_rsrc_t ssrs = make_rsrc(p.ss, gridDim.x * gridDim.y * m_rows * 4u);
+  if (EPI == EPI_BF16 && p.rms && gridDim.y > 1 && tid < M && (uint32_t)tid < m_rows)
+    st_dev(ssrs, ((blockIdx.x * gridDim.y + blockIdx.y) * m_rows + tid) * 4u, row_ss(tid));
 
   // ---- cross-lane / cross-wave reduction into red[] (aliases xs); the S sums, when
   // kept, go to a second region of the same size
@@ -675,20 +721,49 @@ __global__ __launch_bounds__(NWV * 64) void k_gemm(
       bm.gu[og] = nan ? __builtin_nanf("") : u;
     }
   } else {
-    const bool direct = gridDim.y == 1;
-    for (int o = tid; o < kOut; o += (NWV * 64)) {
-      const int rb = o / (MT * 16), rem = o % (MT * 16), m = rem >> 4, rr = rem & 15;
-      const uint32_t b = b0 + rb;
-      const float v = final_value(red, o);
-      if (b >= p.nb || (uint32_t)m >= m_rows) continue;
-      if (direct) {
-        const bool second = RBW == 2 && rb == 1;     // per-thread: pick the row-block's weight
-        uint16_t* yy = second ? sv[RBW - 1].y : sv[0].y;
-        const uint32_t nn = second ? sv[RBW - 1].n : sv[0].n;
-        const uint32_t bb = second ? bl[RBW - 1] : bl[0];
-        yy[(size_t)m * nn + 16u * bb + rr] = f32_to_bf16_rne(p.rms ? v / rms_of(row_ss(m), p.k) : v);
-      } else {
-        out_f32[((size_t)split * m_rows + m) * p.n + 16u * b + rr] = v;
+    auto store_y = [&](int rb, int m, int rr, float v, float ss) {
+      const bool second = RBW == 2 && rb == 1;     // per-thread: pick the row-block's weight
+      uint16_t* yy = second ? sv[RBW - 1].y : sv[0].y;
+      const uint32_t nn = second ? sv[RBW - 1].n : sv[0].n;
+      const uint32_t bb = second ? bl[RBW - 1] : bl[0];
+      yy[(size_t)m * nn + 16u * bb + rr] = f32_to_bf16_rne(p.rms ? v / rms_of(ss, p.k) : v);
+    };
+    if (gridDim.y == 1) {
+      for (int o = tid; o < kOut; o += (NWV * 64)) {
+        const int rb = o / (MT * 16), rem = o % (MT * 16), m = rem >> 4, rr = rem & 15;
+        const float v = final_value(red, o);
+        if (b0 + rb >= p.nb || (uint32_t)m >= m_rows) continue;
+        store_y(rb, m, rr, v, p.rms ? row_ss(m) : 0.f);
+      }
+    } else {
+      // K split: this split's partials [split][m][n] at device scope; the split that
+      // completes the group sums all of them in split order
+      const __amdgpu_buffer_rsrc_t prs = make_rsrc(out_f32, gridDim.y * m_rows * p.n * 4u);
+      for (int o = tid; o < kOut; o += (NWV * 64)) {
+        const int rb = o / (MT * 16), rem = o % (MT * 16), m = rem >> 4, rr = rem & 15;
+        const uint32_t b = b0 + rb;
+        const float v = final_value(red, o);
+        if (b >= p.nb || (uint32_t)m >= m_rows) continue;
+        st_dev(prs, ((split * m_rows + m) * p.n + 16u * b + rr) * 4u, v);
+      }
+      if (split_last(p.tickets, blockIdx.x)) {
+        for (int o = tid; o < kOut; o += (NWV * 64)) {
+          const int rb = o / (MT * 16), rem = o % (MT * 16), m = rem >> 4, rr = rem & 15;
+          const uint32_t b = b0 + rb;
+          if (b >= p.nb || (uint32_t)m >= m_rows) continue;
+          float v[kMaxSplit], ssp[kMaxSplit];
+#pragma unroll
+          for (uint32_t sp = 0; sp < kMaxSplit; ++sp) {   // every load in flight before the adds
+            const uint32_t spl = min(sp, gridDim.y - 1u);
+            v[sp] = ld_dev1(prs, ((spl * m_rows + m) * p.n + 16u * b + rr) * 4u);
+            ssp[sp] = p.rms ? ld_dev1(ssrs, ((blockIdx.x * gridDim.y + spl) * m_rows + m) * 4u) : 0.f;
+          }
+          float t = 0.f, ss = 0.f;
+#pragma unroll
+          for (uint32_t sp = 0; sp < kMaxSplit; ++sp)
+            if (sp < gridDim.y) { t += v[sp]; ss += ssp[sp]; }
+          store_y(rb, m, rr, t, ss);
+        }
       }
     }
   }
@@ -839,8 +914,10 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_cs(
 
   // RMS launches: each row's sum of x^2 over the K-range: the 16 threads of a row's units
   // (consecutive lanes) meet in a fixed shuffle tree; one value per row in LDS.  With K
-  // split, the first workgroup of each split leaves it for the reduce kernel.
+  // split, every workgroup also leaves its split's value in its group's slot
+  // ss[group][split][row] for the split that completes the group (device scope).
   __shared__ float s_ss[MT];
+  const __amdgpu_buffer_rsrc_t ssrs = make_rsrc(p.ss, gridDim.x * gridDim.y * m_rows * 4u);
   if (EPI == EPI_BF16 && p.rms) {
 #pragma unroll
     for (int i = 0; i < kUnits; ++i) {
@@ -850,8 +927,8 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_cs(
       const uint32_t u = (uint32_t)tid + NT * i;
       if ((kUnits * NT == 16 * MT || u < 16u * MT) && (u & 15u) == 0u) {
         s_ss[u >> 4] = v;
-        if (gridDim.y > 1 && blockIdx.x == 0 && (u >> 4) < m_rows)
-          p.ss[(size_t)blockIdx.y * m_rows + (u >> 4)] = v;
+        if (gridDim.y > 1 && (u >> 4) < m_rows)
+          st_dev(ssrs, ((blockIdx.x * gridDim.y + blockIdx.y) * m_rows + (u >> 4)) * 4u, v);
       }
     }
     __syncthreads();
@@ -941,10 +1018,9 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_cs(
       bm.gu[o] = nan ? __builtin_nanf("") : u;
     }
   } else {
-    const bool direct = gridDim.y == 1;
-    auto store_y = [&](uint32_t m, f32x4 v) {
+    auto store_y = [&](uint32_t m, f32x4 v, float ss) {
       if (p.rms) {
-        const float rms = rms_of(s_ss[m], p.k);
+        const float rms = rms_of(ss, p.k);
 #pragma unroll
         for (int i = 0; i < 4; ++i) v[i] = v[i] / rms;
       }
@@ -952,51 +1028,48 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_cs(
       const uint32_t hi = (uint32_t)f32_to_bf16_rne(v[2]) | ((uint32_t)f32_to_bf16_rne(v[3]) << 16);
       *reinterpret_cast<uint2*>(sv.y + (size_t)m * sv.n + n0l) = make_uint2(lo, hi);
     };
+    if (gridDim.y == 1) {
 #pragma unroll
-    for (int h = 0; h < NH; ++h) {
-      const uint32_t m = 16u * h + (uint32_t)r;
-      if (m >= m_rows || !bvalid) continue;
-      if (direct) store_y(m, acc[h]);
-      else *reinterpret_cast<f32x4*>(out_f32 + ((size_t)split * m_rows + m) * p.n + n0) = acc[h];
+      for (int h = 0; h < NH; ++h) {
+        const uint32_t m = 16u * h + (uint32_t)r;
+        if (m < m_rows && bvalid) store_y(m, acc[h], p.rms ? s_ss[m] : 0.f);
+      }
+    } else {
+      // K split: this split's partials [split][m][n] (launch numbering) at device scope;
+      // the split that completes the group sums all of them in split order
+      const __amdgpu_buffer_rsrc_t prs = make_rsrc(out_f32, gridDim.y * m_rows * p.n * 4u);
+#pragma unroll
+      for (int h = 0; h < NH; ++h) {
+        const uint32_t m = 16u * h + (uint32_t)r;
+        if (m < m_rows && bvalid) st_dev(prs, ((split * m_rows + m) * p.n + n0) * 4u, acc[h]);
+      }
+      if (split_last(p.tickets, blockIdx.x)) {
+#pragma unroll
+        for (int h = 0; h < NH; ++h) {
+          const uint32_t m = 16u * h + (uint32_t)r;
+          if (m >= m_rows || !bvalid) continue;
+          f32x4 v[kMaxSplit];
+          float ssp[kMaxSplit];
+#pragma unroll
+          for (uint32_t sp = 0; sp < kMaxSplit; ++sp) {   // every load in flight before the adds
+            const uint32_t spl = min(sp, gridDim.y - 1u);
+            v[sp] = ld_dev4(prs, ((spl * m_rows + m) * p.n + n0) * 4u);
+            ssp[sp] = p.rms ? ld_dev1(ssrs, ((blockIdx.x * gridDim.y + spl) * m_rows + m) * 4u) : 0.f;
+          }
+          f32x4 t = {0.f, 0.f, 0.f, 0.f};
+          float ss = 0.f;
+#pragma unroll
+          for (uint32_t sp = 0; sp < kMaxSplit; ++sp)
+            if (sp < gridDim.y) { t += v[sp]; ss += ssp[sp]; }
+          store_y(m, t, ss);
+        }
+      }
     }
-  }
-}
-
-// Sum of the split-K partials in split order (deterministic), divided by the row's RMS on
-// RMS launches, rounded to BF16.  A thread owns four consecutive outputs of one row (n is
-// a multiple of 16, so all four lie in one row-block of one weight) and issues every
-// partial load before the first add.
-static __global__ __launch_bounds__(256) void k_splitk_reduce(const float* __restrict__ partial,
-                                                       GemmParams p, uint32_t nsplit) {
-  const uint32_t mn = p.m * p.n, n4 = mn >> 2;
-  const uint32_t stride = gridDim.x * 256u;
-  for (uint32_t i4 = blockIdx.x * 256u + threadIdx.x; i4 < n4; i4 += stride) {
-    f32x4 v[kMaxSplit];
-#pragma unroll
-    for (uint32_t sp = 0; sp < kMaxSplit; ++sp)
-      v[sp] = sp < nsplit ? *reinterpret_cast<const f32x4*>(partial + (size_t)sp * mn + 4u * i4)
-                          : f32x4{0.f, 0.f, 0.f, 0.f};
-    f32x4 s = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (uint32_t sp = 0; sp < kMaxSplit; ++sp)
-      if (sp < nsplit) s += v[sp];
-    const uint32_t i = 4u * i4, m = i / p.n, row = i - m * p.n;
-    if (p.rms) {   // the row's sum of x^2: the splits' parts in split order
-      float ss = 0.f;
-      for (uint32_t sp = 0; sp < nsplit; ++sp) ss += p.ss[sp * p.m + m];
-      const float rms = rms_of(ss, p.k);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) s[j] = s[j] / rms;
-    }
-    const SegView sv = seg_view(p, row >> 4);
-    const uint32_t lo = (uint32_t)f32_to_bf16_rne(s[0]) | ((uint32_t)f32_to_bf16_rne(s[1]) << 16);
-    const uint32_t hi = (uint32_t)f32_to_bf16_rne(s[2]) | ((uint32_t)f32_to_bf16_rne(s[3]) << 16);
-    *reinterpret_cast<uint2*>(sv.y + (size_t)m * sv.n + row - 16u * sv.rb0) = make_uint2(lo, hi);
   }
 }
 
 // Host-side launcher for one weight source: dispatch on m (exact for the VALU path,
-// 16 or 32 columns for MFMA), rbw and epilogue; split-K adds the reduce kernel.
+// 16 or 32 columns for MFMA), rbw and epilogue.
 template <int SRC>
 hipError_t launch_gemm_src(const GemmArgs& a, int epi, const GemmPlan& pl, hipStream_t s) {
   dim3 grid(pl.n_rbg, pl.nsplit);
@@ -1068,15 +1141,7 @@ hipError_t launch_gemm_src(const GemmArgs& a, int epi, const GemmPlan& pl, hipSt
 #undef W12_EPI
 #undef W12_RBW
 #undef W12_L
-  hipError_t e = hipGetLastError();
-  if (e == hipSuccess && epi == EPI_BF16 && pl.nsplit > 1) {
-    const uint32_t n4 = p.m * p.n / 4u;
-    uint32_t blocks = (n4 + 255u) / 256u;
-    if (blocks > 1024u) blocks = 1024u;
-    hipLaunchKernelGGL(k_splitk_reduce, dim3(blocks), dim3(256), 0, s, a.partial, p, pl.nsplit);
-    e = hipGetLastError();
-  }
-  return e;
+  return hipGetLastError();
 }
 
 }  // namespace w12

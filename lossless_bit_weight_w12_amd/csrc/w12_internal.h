@@ -32,7 +32,7 @@ enum Epi : int {
 // share K (a group), their row-blocks numbered consecutively; a single GEMM is a group
 // of one.
 constexpr int kMaxSeg = 4;
-// Most K splits a launch takes (the reduce kernel keeps one partial per split in registers).
+// Most K splits a launch takes (the completing split keeps one partial per split in registers).
 constexpr uint32_t kMaxSplit = 8;
 // Most row-blocks in one group record of verification pass 1 (its workgroup's row-blocks).
 constexpr uint32_t kMaxBpg = 8;
@@ -53,9 +53,11 @@ struct GemmParams {
   uint32_t nb, n;           // row-blocks and rows of all the launch's weights together
   uint32_t nseg;
   // RMS launches (rms = 1): y = (x . W^T) / sqrt(mean_k x^2) per row; when K is split,
-  // each split's sum of x^2 per row goes to ss[split][m] for the reduce kernel
+  // each workgroup leaves its split's sum of x^2 per row in ss[group][split][m]
   uint32_t rms;
   float* ss;
+  // K split: one ticket per row-block group (zero before the launch, zero after it)
+  uint32_t* tickets;
   Seg seg[kMaxSeg];
 };
 

@@ -4,10 +4,9 @@ row-block counts, tile columns not a multiple of the 4-column chunk), split-K sh
 both codebook paths (run and lookup table), escape-heavy matrices, every M in 1..32,
 and greedy verification with planted exact ties and 1-ulp pairs.
 
-Bars: encode bytes, decode bits, argmax and accepted length are bit-exact; GEMM
-outputs satisfy |y - z| <= 2e-3 * sum|x||w| + 1e-6 per element, or -- where one
-product dominates a row so that no BF16 value can -- are the BF16 rounding of a value
-within that tolerance (oracle.gemm_accept)."""
+Bars: encode bytes, decode bits, argmax and accepted length are bit-exact; a GEMM
+output is the BF16 rounding (to nearest even) of a value t with
+|t - z| <= 2e-3 * sum|x||w| + 1e-6 (oracle.gemm_accept)."""
 import numpy as np
 import pytest
 
@@ -256,6 +255,81 @@ def test_gemm_workspace_reuse_across_shapes(env):
             y = w12.gemm(xt, t)
             torch.cuda.synchronize()
             assert torch.equal(y.view(torch.int16), first[i].view(torch.int16)), (rep, i)
+
+
+@pytest.mark.parametrize("which", ["w12", "bf16", "bf16t"])
+def test_split_k_completes_from_fresh_partials(env, which):
+    """K-split launches complete inside the GEMM: the split that finishes last in a
+    row-block group sums every split's partials in split order.  Between calls the
+    workspace past the 4 KB of tickets is filled with NaN bytes; each call must still
+    equal the first one bit for bit (and the oracle), leave the tickets at zero, and a
+    workspace that held NaN bytes everywhere works once w12_workspace_init has zeroed it.
+    Shapes: few row-blocks with long K (split at every m), an RMS launch, and 1..3 rows
+    on the BF16 kernels (the wave-column kernel's split path)."""
+    import ctypes
+    torch, w12 = env
+    g = np.random.default_rng(7700)
+    n, k = 320, 4096
+    w = wi.gaussian_bf16((n, k), 0.02, g)
+    wd = to_dev(w, torch)
+    t = w12.encode(wd) if which == "w12" else None
+    wt = w12.bf16_tile(wd) if which == "bf16t" else None
+    for m in (1, 3, 8, 32):
+        x = wi.gaussian_bf16((m, k), 1.0, g)
+        xt = to_dev(x, torch)
+        say("split-k completion", which, m)
+
+        def call(out, rms=False):
+            if which == "w12":
+                return w12.gemm(xt, t, out=out, rms=rms)
+            if which == "bf16":
+                return w12.gemm_bf16(xt, wd, out=out)
+            return w12.gemm_bf16_tiled(xt, wt, n, k, out=out)
+        y0 = call(None)
+        torch.cuda.synchronize()
+        ws = w12.workspace(256, xt.device)                    # the binding's cached GEMM workspace
+        assert int(ws[:4096].count_nonzero()) == 0          # tickets left at zero
+        z, s = o.gemm_reference(x, w)
+        assert o.gemm_accept(to_host(y0), z, s).all()
+        for rep in range(2):
+            ws[4096:].fill_(0xFF)                             # partials and row sums: NaN
+            y1 = call(None)
+            torch.cuda.synchronize()
+            assert torch.equal(y1.view(torch.int16), y0.view(torch.int16)), (m, rep)
+            assert int(ws[:4096].count_nonzero()) == 0
+        if which == "w12":                                    # RMS launch, K split
+            yr = call(None, rms=True)
+            torch.cuda.synchronize()
+            zr, sr = rms_reference(x, w)
+            assert o.gemm_accept(to_host(yr), zr, sr).all()
+    # a workspace of NaN bytes prepared by w12_workspace_init, through the C ABI
+    m = 8
+    x = wi.gaussian_bf16((m, k), 1.0, g)
+    xt = to_dev(x, torch)
+    op = w12.OP_GEMM if which == "w12" else w12.OP_GEMM_BF16
+    nbytes = w12.workspace_bytes(op, m, n, k)
+    assert nbytes > 4096
+    fresh = torch.full((nbytes,), 0xFF, dtype=torch.uint8, device="cuda:0")
+    L = w12.lib()
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    assert L.w12_workspace_init(ctypes.c_void_p(fresh.data_ptr()), nbytes, stream) == 0
+    y = torch.empty((m, n), dtype=torch.bfloat16, device="cuda:0")
+    if which == "w12":
+        d = t.desc()
+        st = L.w12_gemm(ctypes.c_void_p(xt.data_ptr()), m, ctypes.byref(d), ctypes.c_void_p(y.data_ptr()),
+                        ctypes.c_void_p(fresh.data_ptr()), nbytes, stream)
+    elif which == "bf16":
+        st = L.w12_gemm_bf16(ctypes.c_void_p(xt.data_ptr()), m, ctypes.c_void_p(wd.data_ptr()), n, k,
+                             ctypes.c_void_p(y.data_ptr()), ctypes.c_void_p(fresh.data_ptr()), nbytes, stream)
+    else:
+        st = L.w12_gemm_bf16_tiled(ctypes.c_void_p(xt.data_ptr()), m, ctypes.c_void_p(wt.data_ptr()), n, k,
+                                   ctypes.c_void_p(y.data_ptr()), ctypes.c_void_p(fresh.data_ptr()), nbytes,
+                                   stream)
+    assert st == 0
+    torch.cuda.synchronize()
+    z, s = o.gemm_reference(x, w)
+    assert o.gemm_accept(to_host(y), z, s).all()
+    assert int(fresh[:4096].count_nonzero()) == 0
 
 
 def test_gemm_nonfinite_propagates(env):
