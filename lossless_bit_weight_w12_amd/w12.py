@@ -50,6 +50,11 @@ def lib():
         if not os.path.exists(_LIB_PATH):
             raise RuntimeError(f"{_LIB_PATH} is not built; run "
                                "`python -m lossless_bit_weight_w12_amd.build` first")
+        # torch ships its own HIP runtime (soname libamdhip64.so.7, the one libw12.so needs).
+        # Loaded first, it is the runtime the library binds to; the other way round the
+        # process would hold two HIP runtimes, and the library's launches on torch's
+        # streams and memory would fail.
+        import torch  # noqa: F401
         L = ctypes.CDLL(_LIB_PATH)
         L.w12_tiles_bytes.restype = c_size_t
         L.w12_tiles_bytes.argtypes = [c_uint64, c_uint64]

@@ -239,3 +239,21 @@ def test_encode_decode_validation(L):
     assert L.w12_rms_rescale(FAKE, 4, 100, FAKE, None) == -2        # k % 8 != 0
     assert L.w12_rms_rescale(FAKE + 8, 4, 128, FAKE, None) == -7    # x not 16-byte aligned
     assert L.w12_workspace_init(None, 64, None) == -1
+
+
+def test_library_binds_to_torchs_hip_runtime():
+    """The binding loads torch before libw12.so, so that the library's NEEDED
+    libamdhip64.so.7 resolves to the runtime torch already holds (torch bundles its own);
+    checked in a fresh interpreter that asks for the library before importing torch."""
+    import subprocess
+    import sys
+    code = ("import sys; sys.path.insert(0, %r)\n"
+            "import lossless_bit_weight_w12_amd as w12\n"
+            "w12.lib()\n"
+            "import torch, os\n"
+            "maps = open('/proc/self/maps').read()\n"
+            "paths = {l.split()[-1] for l in maps.splitlines() if 'libamdhip64.so' in l}\n"
+            "print(len(paths))\n") % (os.path.dirname(os.path.dirname(os.path.abspath(__file__))),)
+    out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300)
+    assert out.returncode == 0, out.stderr[-2000:]
+    assert out.stdout.strip().splitlines()[-1] == "1"      # one HIP runtime in the process
