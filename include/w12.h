@@ -152,6 +152,24 @@ w12_status w12_decode(const w12_desc* d, uint16_t* w_out, void* stream);
 w12_status w12_gemm(const uint16_t* x, uint32_t m, const w12_desc* d, uint16_t* y,
                     void* ws, size_t ws_bytes, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation): w12_gemm with its K-split workspace
+ * taken from a fixed array of W12_NOALLOC_SCRATCH_BYTES inside the library instead of a
+ * caller's buffer; each GPU holds its own copy of the array from that GPU's first call
+ * until the process ends.  Arguments (the caller still passes x and y), arithmetic,
+ * results (bit-identical to w12_gemm: same kernels, same K split) and errors as w12_gemm;
+ * W12_ERR_WORKSPACE when the call needs more workspace than the array holds
+ * (w12_workspace_bytes(W12_OP_GEMM, m, n, k) > W12_NOALLOC_SCRATCH_BYTES), checked before
+ * any HIP call.  Allocates nothing.  The stream's GPU must be the current device.  The
+ * first call on a GPU looks up the array's device address (make it before capturing a
+ * graph) and clears the array's split-K tickets on `stream`; every call leaves them at
+ * zero.  All calls on one GPU share its array, which keeps the last call's contents:
+ * calls ordered on one stream are safe, calls that overlap on one GPU (other streams,
+ * other host threads) race and give undefined results. */
+#define W12_NOALLOC_SCRATCH_BYTES (32u << 20)
+w12_status w12_gemm_noalloc(const uint16_t* x, uint32_t m, const w12_desc* d, uint16_t* y,
+                            void* stream);
+
 /* Several W12 weights that read the same x (q, k and v of a layer; gate and up):
  * ys[i] = x . W_i^T for i < n_w (1..W12_MAX_GROUP), all with the same k, in one launch
  * per codebook kind (row-blocks of the weights numbered consecutively), plus the

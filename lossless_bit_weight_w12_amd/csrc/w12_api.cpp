@@ -305,18 +305,39 @@ hipError_t launch_w12_group(const uint16_t* x, uint32_t m, const w12_desc* const
   return launch_gemm(a, src, EPI_BF16, p, s);
 }
 
-w12_status gemm_impl(const uint16_t* x, uint32_t m, const w12_desc* d, uint16_t* y, void* ws,
-                     size_t ws_bytes, void* stream, bool rms) {
+}  // namespace
+
+// The argument checks of w12_gemm other than the workspace's (host only, no HIP call);
+// *need = the workspace bytes the call takes.
+w12_status w12::gemm_check(const uint16_t* x, uint32_t m, const w12_desc* d, const uint16_t* y,
+                           size_t* need) {
   if (!x || !y) return W12_ERR_NULL;
   w12_status st = check_desc(d, true);
   if (st != W12_OK) return st;
   if (m < 1 || m > W12_MAX_M) return W12_ERR_RANGE;
   if (!mn_ok(m, d->n)) return W12_ERR_SHAPE;
-  const size_t need = gemm_ws_bytes(m, d->n, d->k);
+  if (!aligned(x, 16) || !aligned(y, 16)) return W12_ERR_ALIGN;
+  *need = gemm_ws_bytes(m, d->n, d->k);
+  return W12_OK;
+}
+
+// w12_gemm after its checks: launch on a workspace of at least the needed bytes.
+w12_status w12::gemm_launch(const uint16_t* x, uint32_t m, const w12_desc* d, uint16_t* y,
+                            void* ws, void* stream, bool rms) {
+  return hip_status(launch_w12_group(x, m, &d, &y, 1, ws, (hipStream_t)stream, rms));
+}
+
+namespace {
+
+w12_status gemm_impl(const uint16_t* x, uint32_t m, const w12_desc* d, uint16_t* y, void* ws,
+                     size_t ws_bytes, void* stream, bool rms) {
+  size_t need = 0;
+  const w12_status st = gemm_check(x, m, d, y, &need);
+  if (st != W12_OK) return st;
   if (ws_bytes < need) return W12_ERR_WORKSPACE;
   if (need > 0 && !ws) return W12_ERR_NULL;
-  if (!aligned(x, 16) || !aligned(y, 16) || !aligned(ws, 256)) return W12_ERR_ALIGN;
-  return hip_status(launch_w12_group(x, m, &d, &y, 1, ws, (hipStream_t)stream, rms));
+  if (!aligned(ws, 256)) return W12_ERR_ALIGN;
+  return gemm_launch(x, m, d, y, ws, stream, rms);
 }
 
 w12_status gemm_group_impl(const uint16_t* x, uint32_t m, const w12_desc* const* descs,

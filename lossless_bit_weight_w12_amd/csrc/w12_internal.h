@@ -8,6 +8,8 @@
 // m from which the MFMA path runs; below it the VALU v_dot2 path.  Measured on the MLP
 // shapes: from m = 4 the VALU path is VALU-issue-bound and the MFMA path (x zero-padded
 // to 16 rows) is faster.
+struct w12_desc;   // the C ABI's weight descriptor (w12.h)
+
 #ifndef W12_MFMA_MIN_M
 #define W12_MFMA_MIN_M 4
 #endif
@@ -222,5 +224,12 @@ hipError_t launch_verify_pass2(const VerifyArgs& a, hipStream_t s);
 
 hipError_t launch_rms_rescale(const uint16_t* x, uint32_t m, uint32_t k, uint16_t* y,
                               hipStream_t s);
+
+// w12_gemm in two halves (host layer): argument checks with the workspace bytes the call
+// needs, then the launch on a workspace of at least that size.
+int32_t gemm_check(const uint16_t* x, uint32_t m, const ::w12_desc* d, const uint16_t* y,
+                   size_t* need);
+int32_t gemm_launch(const uint16_t* x, uint32_t m, const ::w12_desc* d, uint16_t* y, void* ws,
+                    void* stream, bool rms);
 
 }  // namespace w12

@@ -24,7 +24,8 @@ EXPORTS = ("w12_tiles_bytes", "w12_workspace_bytes", "w12_workspace_init", "w12_
            "w12_gemm_group_rms", "w12_gemm_bf16", "w12_bf16_tile",
            "w12_gemm_bf16_tiled", "w12_lmhead_verify", "w12_lmhead_verify_batched",
            "w12_logits_f32",
-           "w12_rms_rescale", "w12_status_str", "w12_version")
+           "w12_rms_rescale", "w12_status_str", "w12_version", "w12_gemm_noalloc")
+NOALLOC_SCRATCH_BYTES = 32 << 20   # W12_NOALLOC_SCRATCH_BYTES
 
 
 class W12Error(RuntimeError):
@@ -75,6 +76,8 @@ def lib():
         L.w12_gemm_group.restype = c_int32
         L.w12_gemm_group.argtypes = [c_void_p, c_uint32, c_void_p, c_uint32, c_void_p, c_void_p,
                                      c_size_t, c_void_p]
+        L.w12_gemm_noalloc.restype = c_int32
+        L.w12_gemm_noalloc.argtypes = [c_void_p, c_uint32, ctypes.POINTER(W12Desc), c_void_p, c_void_p]
         L.w12_gemm_rms.restype = c_int32
         L.w12_gemm_rms.argtypes = L.w12_gemm.argtypes
         L.w12_gemm_group_rms.restype = c_int32
@@ -249,6 +252,22 @@ def gemm(x, t: W12Tensor, out=None, rms: bool = False):
     fn = "w12_gemm_rms" if rms else "w12_gemm"
     _check(fn, getattr(lib(), fn)(_ptr(x), m, ctypes.byref(d), _ptr(_as_bits(out)), _ptr(ws),
                                   ws.numel(), _stream(x.device)))
+    return out
+
+
+def gemm_noalloc(x, t: W12Tensor, out=None):
+    """y = x . W^T through w12_gemm_noalloc: the library's own fixed scratch array instead
+    of a workspace (for callers that cannot allocate; `out` must then be given)."""
+    torch = _torch()
+    x = _as_bits(x)
+    m = x.shape[0]
+    if x.shape[1] != t.k:
+        raise ValueError(f"x has {x.shape[1]} columns, W has k = {t.k}")
+    if out is None:
+        out = torch.empty((m, t.n), dtype=torch.bfloat16, device=x.device)
+    d = t.desc()
+    _check("w12_gemm_noalloc", lib().w12_gemm_noalloc(_ptr(x), m, ctypes.byref(d), _ptr(_as_bits(out)),
+                                                      _stream(x.device)))
     return out
 
 
