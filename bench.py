@@ -9,15 +9,31 @@ resident in HBM.  The same step on plain BF16 weights with the same kernel famil
 gives the speedup.  Weight copies are rotated so that no GEMM finds its weights in the
 256 MB Infinity Cache.
 
+Protocol:
+  * before any timing, every GEMM of the step runs once on the W12 kernel and both BF16
+    kernels, and the CPU oracle, timed on a bounded sample (the `cpu_baseline` leg: the
+    first rows of both matrices at every M), checks those outputs on the same rows;
+    a mismatch stops the run;
+  * every timed loop is preceded by at least WARM_S seconds of the same or mixed work
+    (the GPU clock ramps up from idle), and the warm-up steps the caller asks for;
+  * the headline times exactly --steps W12 steps between two synchronisations (HIP
+    events on the launching stream, one per step for the CI);
+  * the speedups come from three interleaved rounds (W12, row-major BF16, tiled BF16 steps
+    in rotated order), medians per kind;
+  * per launch: three rounds of 100 launches per (M, matrix, kernel), median round; their
+    sum over the step is reported beside the step time;
+  * the streaming-read ceiling for the same byte counts (w12_stream_read, the GEMM's own
+    nontemporal loads, best of several grid sizes, rotated over 2 GiB).
+
 Two more workloads are timed in the same run and reported beside the main line:
 the LM-head greedy verification ([151936, 5120], M = 16) and a whole weight-streaming
 decode step (64 layers of q, k, v, o, gate, up, down + LM head, M = 24, RMS-chained).
 
 `roofline.traffic` is the HBM traffic of the dominant launch measured by rocprofv3
 counters (FETCH_SIZE and WRITE_SIZE passes over `--profile-only --calibrate-copy`,
-scaled by what the counters read for a 1 GiB device copy); it is read from
-profiles/w12_gemm_traffic.json and reported only while the kernel sources still hash to
-the value recorded there (null otherwise).
+scaled by what the counters read for the streaming-read kernel over 1 GiB and a 1 GiB
+fill); it is read from profiles/w12_gemm_traffic.json and reported only while the kernel
+sources still hash to the value recorded there (null otherwise).
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline] [--no-extras]
 """
@@ -29,6 +45,7 @@ import hashlib
 import json
 import os
 import platform
+import statistics
 import sys
 import time
 
@@ -41,6 +58,8 @@ MS = (1, 4, 8, 16, 32)
 BATCHED_MS = (64, 128)      # batched regime (several requests' rows at once), reported beside
 N_GU, K_GU = 34816, 5120
 N_DN, K_DN = 5120, 17408
+WARM_S = 0.3                # seconds of work before the headline loop
+SAMPLE_ROWS = 256           # rows of each matrix the oracle checks (cpu_baseline leg)
 
 
 def log(*a):
@@ -59,34 +78,41 @@ def bf16_bytes(n: int, k: int, m: int) -> int:
     return 2 * n * k + 2 * m * k + 2 * m * n
 
 
-def cpu_baseline(seconds_target: float = 12.0):
-    """The CPU oracle's W12 GEMM (bit-exact decode, then the FP64 product) on a bounded
-    sample of the gate+up matrix: the first R rows, at every M of the workload."""
+def cpu_baseline(host_w, xs_host, gpu_out, seconds_target: float = 12.0):
+    """The CPU oracle on a bounded sample of the workload: its W12 GEMM (bit-exact decode of
+    the first SAMPLE_ROWS rows of both matrices, then the FP64 product) at every M, timed
+    for about seconds_target; the same results check the GPU outputs on those rows (W12
+    and both BF16 kernels), which the run captured before any timing.  Returns the baseline
+    record and the parity record."""
     import numpy as np
     from oracle import w12_oracle as o
-    import w12_inputs as wi
     try:
         from threadpoolctl import threadpool_info
         blas_threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
     except Exception:
         blas_threads = 1
-    rows = 512
-    w = wi.weight(3, wi.T_W, (rows, K_GU))     # same stream: the first rows of gate+up
-    blob = o.encode(w)
-    xs = {m: wi.activations(3, wi.T_X, m, K_GU) for m in MS}
+    rows = SAMPLE_ROWS
+    blobs = {name: o.encode(w[:rows]) for name, w in host_w.items()}
+    parity = {}
     done_bytes, t_total, reps = 0, 0.0, 0
-    while t_total < seconds_target and reps < 50:
+    while (t_total < seconds_target and reps < 50) or reps == 0:
         for m in MS:
-            t0 = time.perf_counter()
-            o.gemm_w12(xs[m], blob)
-            t_total += time.perf_counter() - t0
-            done_bytes += o.blob_bytes(blob) + 2 * m * K_GU + 2 * m * rows
+            for name, blob in blobs.items():
+                x = xs_host[(m, name)]
+                t0 = time.perf_counter()
+                z, s = o.gemm_w12(x, blob)
+                t_total += time.perf_counter() - t0
+                done_bytes += o.blob_bytes(blob) + 2 * m * blob.k + 2 * m * rows
+                if reps == 0:
+                    parity[f"M{m}_{name}"] = {kind: bool(o.gemm_accept(y[:, :rows], z, s).all())
+                                              for kind, y in gpu_out[(m, name)].items()}
         reps += 1
-    return {"value": done_bytes / t_total / 1e9, "unit": "GB/s", "cores": int(blas_threads),
+    base = {"value": done_bytes / t_total / 1e9, "unit": "GB/s", "cores": int(blas_threads),
             "kind": "oracle",
             "sample": f"oracle W12 GEMM (decode + FP64 product) on the first {rows} rows of the "
-                      f"gate+up matrix [{rows}x{K_GU}], M in {list(MS)}, {reps} passes, "
-                      f"{t_total:.1f} s; BLAS threads {blas_threads}"}
+                      f"gate+up [{rows}x{K_GU}] and down [{rows}x{K_DN}] matrices, M in {list(MS)}, "
+                      f"{reps} passes, {t_total:.1f} s; BLAS threads {blas_threads}"}
+    return base, parity
 
 
 COPY_BYTES = 1 << 30
@@ -162,11 +188,25 @@ def gpu_state():
             "power_w": find(d, "power", "socket_power")}
 
 
-def time_calls(torch, fn, reps: int, warmup: int = 3) -> float:
-    """Mean milliseconds per call of fn() over reps calls between one event pair."""
-    for _ in range(warmup):
-        fn()
+def warm(torch, fns, seconds: float):
+    """Run fns(i) in turn for at least `seconds` of wall time, keeping the queue short so
+    the host clock follows the GPU (the GPU clock ramps up under load)."""
     torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    i = 0
+    while time.perf_counter() - t0 < seconds:
+        for f in fns:
+            f(i)
+        i += 1
+        if i % 2 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+
+
+def time_calls(torch, fn, reps: int, warm_s: float = 0.05) -> float:
+    """Mean milliseconds per call of fn() over reps calls between one event pair, after
+    warm_s seconds of the same calls."""
+    warm(torch, [lambda i: fn()], warm_s)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(reps):
@@ -176,15 +216,61 @@ def time_calls(torch, fn, reps: int, warmup: int = 3) -> float:
     return e0.elapsed_time(e1) / reps
 
 
-def _rot(fn):
-    """A call-counting wrapper: fn(i) with i = 0, 1, 2, ... on successive calls (to
-    rotate weight copies under time_calls)."""
-    state = {"i": 0}
+def timed(torch, step_fn, steps: int):
+    """Exactly `steps` steps between two synchronisations: mean ms per step over the
+    event pair around all of them, and the per-step durations from events recorded
+    between the steps (no synchronisation inside the timed region)."""
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    ev[0].record()
+    for i in range(steps):
+        step_fn(i)
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    per = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
+    return ev[0].elapsed_time(ev[steps]) / steps, per
 
-    def call():
-        fn(state["i"])
-        state["i"] += 1
-    return call
+
+def launch_rounds(torch, fn, reps: int = 100, rounds: int = 3, warm_s: float = 0.03):
+    """Per-launch microseconds of fn(i) (i rotating weight copies): rounds of `reps`
+    launches between event pairs after warm_s seconds of the same launches; returns the
+    median round and the mean over all rounds."""
+    warm(torch, [fn], warm_s)
+    res = []
+    for _ in range(rounds):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(reps):
+            fn(i)
+        e1.record()
+        torch.cuda.synchronize()
+        res.append(e0.elapsed_time(e1) / reps * 1e3)
+    return statistics.median(res), sum(res) / len(res)
+
+
+def read_ceiling(torch, w12, sizes, dev, reps: int = 20):
+    """Streaming-read ceiling for each byte count: w12_stream_read (the GEMM's nontemporal
+    16-byte buffer loads) over windows rotating through 2 GiB, so the 256 MB Infinity
+    Cache cannot serve a repeat; the best of several grid sizes, median of three rounds."""
+    span = 2 << 30
+    buf = torch.empty(span, dtype=torch.uint8, device=dev)
+    buf.fill_(1)
+    grids = (256, 512, 768, 1024, 1536, 2048, 4096)
+    sink = torch.empty(4 * max(grids), dtype=torch.int32, device=dev)
+    out = {}
+    for name, nbytes in sizes.items():
+        nb = nbytes - nbytes % 256
+        nwin = max(1, span // nb)          # windows [i nb, (i + 1) nb) inside the 2 GiB
+        per = {}
+        for wg in grids:
+            us, _ = launch_rounds(torch, lambda i: w12.stream_read(buf, (i % nwin) * nb, nb, wg, sink),
+                                  reps=reps)
+            per[wg] = round(nb / us / 1e3, 1)
+        best = max(per, key=per.get)
+        out[name] = {"bytes": nb, "gbps": per[best], "pct_of_peak": round(100 * per[best] / PEAK_GBPS, 1),
+                     "workgroups": best, "gbps_by_workgroups": per}
+    del buf
+    return out
 
 
 def build_decode_stack(torch, w12, wi, np, dev, head=None):
@@ -224,7 +310,8 @@ def extra_workloads(torch, w12, wi, np, dev, args):
     torch.cuda.synchronize()
     log(f"bench: LM head encoded in {time.time() - t0:.1f} s; timing verification ...")
 
-    # ---- LM-head greedy verification, M = 16
+    # ---- LM-head greedy verification, M = 16; the BF16-out GEMM of the same shape is timed
+    # in alternating rounds with it, so both see the same clock
     x16 = torch.from_numpy(wi.verify_batch_x(0).view(np.int16)).to(dev)
     am, _ = w12.lmhead_verify(x16, head, torch.zeros(0, dtype=torch.int32, device=dev))
     p, r = wi.verify_mismatch(0, vocab)
@@ -234,11 +321,15 @@ def extra_workloads(torch, w12, wi, np, dev, args):
     am_out = torch.empty(16, dtype=torch.int32, device=dev)
     acc_out = torch.empty(1, dtype=torch.int32, device=dev)
     vcall = w12.prepare_verify(x16, head, draft, am_out, acc_out)
-    ms_verify = time_calls(torch, vcall, 50)
-    accepted = int(acc_out.item())
     y16 = torch.empty((16, vocab), dtype=torch.bfloat16, device=dev)
     gcall = w12.prepare_gemm(x16, head, y16)
-    ms_gemm16 = time_calls(torch, gcall, 50)
+    warm(torch, [lambda i: vcall(), lambda i: gcall()], WARM_S)
+    rv, rg = [], []
+    for _ in range(5):
+        rv.append(time_calls(torch, vcall, 20, warm_s=0.0))
+        rg.append(time_calls(torch, gcall, 20, warm_s=0.0))
+    ms_verify, ms_gemm16 = statistics.median(rv), statistics.median(rg)
+    accepted = int(acc_out.item())
     # the verification's algorithmic bytes: the W12 head, x, the per-block records of
     # pass 1 (16 B per row and 16-row block, written and read) and the argmax
     v_bytes = head.nbytes() + 2 * 16 * hid + 2 * 16 * 16 * (vocab // 16) + 4 * 16
@@ -253,7 +344,8 @@ def extra_workloads(torch, w12, wi, np, dev, args):
         "verify_overhead_us": round((ms_verify - ms_gemm16) * 1e3, 1),
         "accepted": accepted, "planted_mismatch_at": p,
         "accepted_matches_plant": accepted == p}
-    log(f"bench: verify {verify['us_per_verify']} us ({verify['gbps_verify']} GB/s)")
+    log(f"bench: verify {verify['us_per_verify']} us ({verify['gbps_verify']} GB/s), "
+        f"GEMM of the same shape {verify['us_gemm_bf16_out_same_shape']} us")
 
     # ---- batched verification: 24 requests x 5 rows in one pass over the head
     xb = torch.from_numpy(wi.batched_verify_x().view(np.int16)).to(dev)
@@ -270,7 +362,7 @@ def extra_workloads(torch, w12, wi, np, dev, args):
     accb_out = torch.empty(len(nd), dtype=torch.int32, device=dev)
     bcall = w12.prepare_verify_batched(xb, head, t_i32(off), t_i32(nd), t_i32(draft_b), amb_out,
                                        accb_out)
-    ms_vb = time_calls(torch, bcall, 30)
+    ms_vb = time_calls(torch, bcall, 30, warm_s=0.1)
     accb = accb_out.cpu().numpy()
     vb_bytes = head.nbytes() + 2 * mb * hid + 2 * 16 * mb * (vocab // 16) + 4 * mb + 4 * len(nd)
     verify_batched = {
@@ -292,7 +384,7 @@ def extra_workloads(torch, w12, wi, np, dev, args):
     def one_step():
         stack.h.copy_(h0)
         stack.run()
-    ms_step = time_calls(torch, one_step, args.decode_steps, warmup=2)
+    ms_step = time_calls(torch, one_step, args.decode_steps, warm_s=WARM_S)
     am_eager, h_eager = stack.argmax.clone(), stack.h.clone()
     # the same step captured once as a HIP graph and replayed (no memset nodes: the
     # library's calls are kernels only); every replay must give the eager answer
@@ -314,7 +406,7 @@ def extra_workloads(torch, w12, wi, np, dev, args):
             graph_ok = graph_ok and bool(torch.equal(stack.argmax, am_eager)) and \
                 bool(torch.equal(stack.h.view(torch.int16), h_eager.view(torch.int16)))
             torch.zeros(1, device=dev).add_(1)    # eager work between the replays
-        ms_graph = time_calls(torch, graph.replay, args.decode_steps, warmup=2)
+        ms_graph = time_calls(torch, graph.replay, args.decode_steps, warm_s=0.1)
         stack.prepare(stack.draft)                # back to the current stream
     wb, io = stack.weight_bytes(), stack.io_bytes()
     n_params = sum(t.n * t.k for L in layers for t in L.values()) + head.n * head.k
@@ -332,7 +424,7 @@ def extra_workloads(torch, w12, wi, np, dev, args):
         "ms_per_step_hip_graph": None if ms_graph is None else round(ms_graph, 3),
         "hip_graph_replays_match_eager": graph_ok}
     log(f"bench: decode step {step['ms_per_step']} ms ({step['gbps']} GB/s)")
-    return verify, step
+    return verify, step, head.nbytes()
 
 
 def main():
@@ -343,12 +435,13 @@ def main():
     ap.add_argument("--rotate-bytes", type=float, default=float(1 << 30),
                     help="bytes of weight copies each timed loop rotates over (defeats the "
                          "256 MB Infinity Cache)")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true",
+                    help="skip the CPU oracle leg (and with it the sampled parity check)")
     ap.add_argument("--profile-only", action="store_true",
                     help="run a few W12 steps and exit (for rocprofv3)")
     ap.add_argument("--calibrate-copy", action="store_true",
-                    help="with --profile-only: also run a 1 GiB device-to-device copy, the "
-                         "known-size kernel that scales the traffic counters")
+                    help="with --profile-only: also stream 1 GiB with w12_stream_read and fill "
+                         "1 GiB, the known-size kernels that scale the traffic counters")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the LM-head verification and decode-step workloads")
     ap.add_argument("--decode-steps", type=int, default=20)
@@ -416,8 +509,9 @@ def main():
         return
     log("bench: generating the MLP-block weights (seeded, host) ...")
     t0 = time.time()
-    w_gu = torch.from_numpy(wi.weight(3, wi.T_W, (N_GU, K_GU)).view(np.int16)).to(dev)
-    w_dn = torch.from_numpy(wi.weight(3, wi.T_W2, (N_DN, K_DN)).view(np.int16)).to(dev)
+    host_w = {"gate_up": wi.weight(3, wi.T_W, (N_GU, K_GU)), "down": wi.weight(3, wi.T_W2, (N_DN, K_DN))}
+    w_gu = torch.from_numpy(host_w["gate_up"].view(np.int16)).to(dev)
+    w_dn = torch.from_numpy(host_w["down"].view(np.int16)).to(dev)
     log(f"bench: weights on device in {time.time() - t0:.1f} s; encoding to W12 ...")
     t_gu = [w12.encode(w_gu)]
     t_dn = [w12.encode(w_dn)]
@@ -440,11 +534,17 @@ def main():
     # second baseline: the same BF16 weights in 4 KB tiles (full-line streaming loads)
     bt_gu = [w12.bf16_tile(b) for b in b_gu]
     bt_dn = [w12.bf16_tile(b) for b in b_dn]
-    xs = {m: (torch.from_numpy(wi.activations(3, wi.T_X, m, K_GU).view(np.int16)).to(dev),
-              torch.from_numpy(wi.activations(3, wi.T_X2, m, K_DN).view(np.int16)).to(dev)) for m in MS}
+    xs_host = {}
+    for m in MS:
+        xs_host[(m, "gate_up")] = wi.activations(3, wi.T_X, m, K_GU)
+        xs_host[(m, "down")] = wi.activations(3, wi.T_X2, m, K_DN)
+    xs = {m: (torch.from_numpy(xs_host[(m, "gate_up")].view(np.int16)).to(dev),
+              torch.from_numpy(xs_host[(m, "down")].view(np.int16)).to(dev)) for m in MS}
     ys = {m: (torch.empty((m, N_GU), dtype=torch.bfloat16, device=dev),
               torch.empty((m, N_DN), dtype=torch.bfloat16, device=dev)) for m in MS}
     yb = {m: (torch.empty((m, N_GU), dtype=torch.bfloat16, device=dev),
+              torch.empty((m, N_DN), dtype=torch.bfloat16, device=dev)) for m in MS}
+    yt = {m: (torch.empty((m, N_GU), dtype=torch.bfloat16, device=dev),
               torch.empty((m, N_DN), dtype=torch.bfloat16, device=dev)) for m in MS}
     torch.cuda.synchronize()
     # encode throughput (one-off work, reported beside the step): the whole of
@@ -475,20 +575,25 @@ def main():
 
     def bf16t_step(c):
         for m in MS:
-            w12.gemm_bf16_tiled(xs[m][0], bt_gu[c % len(bt_gu)], N_GU, K_GU, out=yb[m][0])
-            w12.gemm_bf16_tiled(xs[m][1], bt_dn[c % len(bt_dn)], N_DN, K_DN, out=yb[m][1])
+            w12.gemm_bf16_tiled(xs[m][0], bt_gu[c % len(bt_gu)], N_GU, K_GU, out=yt[m][0])
+            w12.gemm_bf16_tiled(xs[m][1], bt_dn[c % len(bt_dn)], N_DN, K_DN, out=yt[m][1])
 
     if args.profile_only:
-        for i in range(args.warmup):     # the GPU clock ramps up over the first steps
+        warm(torch, [w12_step, bf16_step], 0.2)   # the GPU clock ramps up under load
+        for i in range(args.warmup):
             w12_step(i)
         for i in range(args.steps):
             w12_step(i)
             bf16_step(i)
         if args.calibrate_copy:
+            # known-size kernels for the counters: 1 GiB streamed with the GEMM's
+            # nontemporal loads, a 1 GiB fill, and a 1 GiB device copy
             src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev)
             dst = torch.empty_like(src)
+            sink = torch.empty(4 * 4096, dtype=torch.int32, device=dev)
             src.fill_(1)
             torch.cuda.synchronize()
+            w12.stream_read(src, 0, COPY_BYTES - 256, 4096, sink)
             dst.copy_(src)
         torch.cuda.synchronize()
         log("bench: profile-only run done")
@@ -497,68 +602,62 @@ def main():
     step_bytes = sum(gemm_bytes(t_gu[0], m) + gemm_bytes(t_dn[0], m) for m in MS)
     step_bytes_bf16 = sum(bf16_bytes(N_GU, K_GU, m) + bf16_bytes(N_DN, K_DN, m) for m in MS)
 
-    def timed(step_fn, steps, warmup):
-        """Mean ms per step over `steps` steps between one synchronised pair of events,
-        plus the per-step durations from events recorded between the steps (no
-        synchronisation inside the timed region)."""
-        for i in range(warmup):
-            step_fn(i)
-        torch.cuda.synchronize()
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
-        ev[0].record()
-        for i in range(steps):
-            step_fn(i)
-            ev[i + 1].record()
-        torch.cuda.synchronize()
-        per = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
-        return ev[0].elapsed_time(ev[steps]) / steps, per
-
-    log("bench: timing W12 steps ...")
-    ms_w12, per_w12 = timed(w12_step, args.steps, args.warmup)
-    log("bench: timing BF16 steps ...")
-    ms_bf16, _ = timed(bf16_step, args.steps, args.warmup)
-    log("bench: timing tiled-BF16 steps ...")
-    ms_bf16t, _ = timed(bf16t_step, args.steps, args.warmup)
+    # ---- one untimed pass of every kernel; the CPU oracle (cpu_baseline leg) checks sampled
+    # rows of these outputs before anything is timed
+    w12_step(0)
+    bf16_step(0)
+    bf16t_step(0)
+    torch.cuda.synchronize()
+    cpu_base, parity = None, None
+    if not args.no_cpu_baseline:
+        bits = lambda t: t[:, :SAMPLE_ROWS].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+        gpu_out = {(m, name): {"w12": bits(ys[m][i]), "bf16": bits(yb[m][i]), "bf16_tiled": bits(yt[m][i])}
+                   for m in MS for i, name in ((0, "gate_up"), (1, "down"))}
+        log("bench: CPU oracle on a bounded sample (timed), checking the GPU outputs on it ...")
+        cpu_base, parity = cpu_baseline(host_w, xs_host, gpu_out)
+        bad = {k: v for k, v in parity.items() if not all(v.values())}
+        if bad:
+            raise RuntimeError(f"GPU outputs outside the oracle's acceptance rule: {bad}")
+        log(f"bench: sampled parity ok for {len(parity)} (M, matrix) launches x 3 kernels")
     # W12 and BF16 launches that split K the same way add the same products in the same
     # order, so their outputs agree bit for bit; where the BF16 kernel splits K
     # differently the last bit can differ
-    bf16_step(0)
-    torch.cuda.synchronize()
     same = {f"M{m}_{name}": bool(torch.equal(ys[m][i].view(torch.int16), yb[m][i].view(torch.int16)))
             for m in MS for i, name in ((0, "gate_up"), (1, "down"))}
 
-    # per-(M, matrix) launch durations, each over R launches on rotating copies.  The host
-    # comparisons above leave the GPU idle long enough for its clock to drop, so a burst
-    # of whole steps comes first and every kind gets 20 untimed launches.
-    for i in range(20):
+    # ---- headline: warm-up by time, the caller's warm-up steps, exactly --steps timed steps
+    log("bench: timing W12 steps ...")
+    warm(torch, [w12_step, bf16_step, bf16t_step], WARM_S)
+    for i in range(args.warmup):
         w12_step(i)
-    per = {}
-    reps = 100
+    ms_w12, per_w12 = timed(torch, w12_step, args.steps)
+    gpu_head = gpu_state()
+
+    # ---- speedups: three interleaved rounds, kinds in rotated order, medians per kind
+    log("bench: interleaved W12 / BF16 / tiled-BF16 rounds ...")
+    fns = {"w12": w12_step, "bf16": bf16_step, "bf16t": bf16t_step}
+    rounds = {k: [] for k in fns}
+    for order in (("w12", "bf16", "bf16t"), ("bf16", "bf16t", "w12"), ("bf16t", "w12", "bf16")):
+        warm(torch, list(fns.values()), 0.1)
+        for kind in order:
+            rounds[kind].append(timed(torch, fns[kind], args.steps)[0])
+    med = {k: statistics.median(v) for k, v in rounds.items()}
+    gpu_rounds = gpu_state()
+
+    # ---- per-(M, matrix) launch durations on rotating copies
+    per, mean_us = {}, {}
     for m in MS:
         for name, tl, bl, btl, xi in (("gate_up", t_gu, b_gu, bt_gu, 0),
                                       ("down", t_dn, b_dn, bt_dn, 1)):
-            res = {}
             nn, kk = tl[0].n, tl[0].k
             launch = {
                 "w12": lambda i: w12.gemm(xs[m][xi], tl[i % len(tl)], out=ys[m][xi]),
                 "bf16": lambda i: w12.gemm_bf16(xs[m][xi], bl[i % len(bl)], out=yb[m][xi]),
                 "bf16t": lambda i: w12.gemm_bf16_tiled(xs[m][xi], btl[i % len(btl)], nn, kk,
-                                                       out=yb[m][xi])}
+                                                       out=yt[m][xi])}
+            res = {}
             for kind, fn in launch.items():
-                for i in range(20):
-                    fn(i)
-                # three rounds of R launches, each between one event pair; the median
-                # round (the first can still pay the clock ramp after an idle gap)
-                rounds = []
-                for _ in range(3):
-                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                    e0.record()
-                    for i in range(reps):
-                        fn(i)
-                    e1.record()
-                    torch.cuda.synchronize()
-                    rounds.append(e0.elapsed_time(e1) / reps * 1e3)     # us per launch
-                res[kind] = sorted(rounds)[1]
+                res[kind], mean_us[(f"M{m}_{name}", kind)] = launch_rounds(torch, fn)
             nbytes = gemm_bytes(tl[0], m)
             per[f"M{m}_{name}"] = {
                 "us_w12": round(res["w12"], 2), "us_bf16": round(res["bf16"], 2),
@@ -569,6 +668,19 @@ def main():
                 "us_bf16_tiled": round(res["bf16t"], 2),
                 "gbps_bf16_tiled": round(bf16_bytes(tl[0].n, tl[0].k, m) / res["bf16t"] / 1e3, 1),
                 "speedup_vs_bf16_tiled": round(res["bf16t"] / res["w12"], 3)}
+    launch_sum_ms = sum(v["us_w12"] for v in per.values()) / 1e3
+
+    # ---- streaming-read ceiling for the W12 byte counts (and the LM head's)
+    log("bench: streaming-read ceiling ...")
+    c5 = wi.CONFIG_SHAPES[5]
+    head_bytes = w12.tiles_bytes(c5["vocab"], c5["hidden"]) + 4 * (c5["vocab"] // 16 + 1) + 64
+    ceil_sizes = {"down_w12": t_dn[0].nbytes(), "gate_up_w12": t_gu[0].nbytes(), "lm_head_w12": head_bytes}
+    ceiling = read_ceiling(torch, w12, ceil_sizes, dev)
+    for key, v in per.items():
+        cg = ceiling["down_w12" if key.endswith("down") else "gate_up_w12"]["gbps"]
+        v["pct_of_read_ceiling_w12"] = round(100 * v["gbps_w12"] / cg, 1)
+    log(f"bench: read ceiling {ceiling}")
+
     # batched regime: the same matrices at 64 and 128 rows (several requests' draft
     # rows verified together), W12 against the tiled BF16 kernel
     batched = {}
@@ -578,26 +690,29 @@ def main():
                                                  m, k).view(np.int16)).to(dev)
             yb_ = torch.empty((m, tl[0].n), dtype=torch.bfloat16, device=dev)
             nn = tl[0].n
-            us_w = 1e3 * time_calls(torch, _rot(lambda i: w12.gemm(xb, tl[i % len(tl)], out=yb_)), reps)
-            us_b = 1e3 * time_calls(torch, _rot(lambda i: w12.gemm_bf16_tiled(
-                xb, btl[i % len(btl)], nn, k, out=yb_)), reps)
+            us_w, _ = launch_rounds(torch, lambda i: w12.gemm(xb, tl[i % len(tl)], out=yb_))
+            us_b, _ = launch_rounds(torch, lambda i: w12.gemm_bf16_tiled(xb, btl[i % len(btl)], nn, k,
+                                                                          out=yb_))
             batched[f"M{m}_{name}"] = {
                 "us_w12": round(us_w, 2), "gbps_w12": round(gemm_bytes(tl[0], m) / us_w / 1e3, 1),
                 "us_bf16_tiled": round(us_b, 2), "speedup_vs_bf16_tiled": round(us_b / us_w, 3)}
     log(f"bench: batched GEMMs {batched}")
 
-    # dominant kernel = the (M, matrix) GEMM with the largest share of the step
+    # dominant kernel = the (M, matrix) GEMM with the largest share of the step; its
+    # achieved bandwidth from the mean launch time over its timed rounds
     dom_key = max(per, key=lambda kk: per[kk]["us_w12"])
-    dom = per[dom_key]
     m_dom = int(dom_key.split("_")[0][1:])
     t_dom = t_gu[0] if dom_key.endswith("gate_up") else t_dn[0]
     alg = gemm_bytes(t_dom, m_dom)
+    avg_us = mean_us[(dom_key, "w12")]
     traffic, traffic_note = measured_traffic(dom_key)
-    roofline = {"bound": "hbm", "achieved": round(alg / dom["us_w12"] / 1e3, 1), "peak": PEAK_GBPS,
-                "unit": "GB/s", "frac": round(alg / dom["us_w12"] / 1e3 / PEAK_GBPS, 4),
+    roofline = {"bound": "hbm", "achieved": round(alg / avg_us / 1e3, 1), "peak": PEAK_GBPS,
+                "unit": "GB/s", "frac": round(alg / avg_us / 1e3 / PEAK_GBPS, 4),
                 "traffic": traffic, "traffic_note": traffic_note,
                 "kernel": f"w12_gemm {dom_key}", "alg_bytes_per_launch": alg,
-                "avg_launch_us": dom["us_w12"]}
+                "avg_launch_us": round(avg_us, 2),
+                "pct_of_read_ceiling": round(100 * alg / avg_us / 1e3 /
+                                             ceiling["down_w12" if dom_key.endswith("down") else "gate_up_w12"]["gbps"], 1)}
 
     value = step_bytes / (ms_w12 * 1e-3) / 1e9
     out = {
@@ -612,29 +727,33 @@ def main():
         "pct_of_peak": round(100 * value / PEAK_GBPS, 2),
         "step_ms_median": round(float(np.median(per_w12)), 4),
         "step_ms_ci95": bootstrap_ci(np, per_w12),
-        "gpu_state": {"before": gpu_before, "after": gpu_state()},
-        "speedup_vs_bf16": round(ms_bf16 / ms_w12, 4),
-        "bf16_ms_per_step": round(ms_bf16, 4),
-        "bf16_gbps": round(step_bytes_bf16 / (ms_bf16 * 1e-3) / 1e9, 1),
-        "speedup_vs_bf16_tiled": round(ms_bf16t / ms_w12, 4),
-        "bf16_tiled_ms_per_step": round(ms_bf16t, 4),
-        "bf16_tiled_gbps": round(step_bytes_bf16 / (ms_bf16t * 1e-3) / 1e9, 1),
+        "w12_launch_sum_ms": round(launch_sum_ms, 4),
+        "step_vs_launch_sum": round(ms_w12 / launch_sum_ms, 4),
+        "gpu_state": {"before": gpu_before, "after_headline": gpu_head, "after_rounds": gpu_rounds},
+        "interleaved_ms_per_step": {k: [round(v, 4) for v in vs] for k, vs in rounds.items()},
+        "speedup_vs_bf16": round(med["bf16"] / med["w12"], 4),
+        "bf16_ms_per_step": round(med["bf16"], 4),
+        "bf16_gbps": round(step_bytes_bf16 / (med["bf16"] * 1e-3) / 1e9, 1),
+        "speedup_vs_bf16_tiled": round(med["bf16t"] / med["w12"], 4),
+        "bf16_tiled_ms_per_step": round(med["bf16t"], 4),
+        "bf16_tiled_gbps": round(step_bytes_bf16 / (med["bf16t"] * 1e-3) / 1e9, 1),
         "w12_equals_bf16_bitwise": same,
+        "parity_sampled_vs_oracle": parity,
         "per_gemm": per,
+        "read_ceiling": ceiling,
         "batched_gemm": batched,
         "encode": encode_info,
         "roofline": roofline,
-        "cpu_baseline": None,
+        "cpu_baseline": cpu_base,
         "host": {"cpu": platform.processor() or platform.machine(),
                  "affinity_cores": len(os.sched_getaffinity(0))},
     }
     if not args.no_extras:
         del t_gu, t_dn, b_gu, b_dn, bt_gu, bt_dn, w_gu, w_dn
         torch.cuda.empty_cache()
-        out["lm_head_verify"], out["decode_step"] = extra_workloads(torch, w12, wi, np, dev, args)
-    if not args.no_cpu_baseline:
-        log("bench: timing the CPU oracle on a bounded sample ...")
-        out["cpu_baseline"] = cpu_baseline()
+        out["lm_head_verify"], out["decode_step"], head_b = extra_workloads(torch, w12, wi, np, dev, args)
+        out["lm_head_verify"]["pct_of_read_ceiling"] = round(
+            100 * out["lm_head_verify"]["gbps_verify"] / ceiling["lm_head_w12"]["gbps"], 1)
     print(json.dumps(out), flush=True)
 
 

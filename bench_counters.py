@@ -8,9 +8,11 @@ the per-launch HBM traffic record that bench.py reports as `roofline.traffic`.
 FETCH_DIR / WRITE_DIR hold run_counter_collection.csv from
     rocprofv3 --pmc FETCH_SIZE -d FETCH_DIR -o run --output-format csv -- python3 bench.py --profile-only --steps 2 --warmup 0 --calibrate-copy
 and the same with WRITE_SIZE.  Both counters are per dispatch, in KiB.  The scales come
-from the known-size kernels at the end of the run: the 1 GiB device-to-device copy
-(reads 1 GiB) and the 1 GiB fill before it (writes 1 GiB).  A `w12_gemm` launch is its
-GEMM kernel plus, when K is split, the reduction kernel that follows it.  Writes
+from the known-size kernels at the end of the run: w12_stream_read over 1 GiB - 256 B
+(read with the nontemporal 16-byte buffer loads the GEMM issues for W12 tiles) for
+FETCH_SIZE, and the 1 GiB fill before it (writes 1 GiB) for WRITE_SIZE; the 1 GiB
+device-to-device copy after it is reported as a cross-check of the read scale.  A
+`w12_gemm` launch is one GEMM kernel (K-split launches complete inside it).  Writes
 profiles/w12_gemm_traffic.json and profiles/w12_gemm_mlp_block_traffic.md.
 
 With --stats it summarises a `rocprofv3 --kernel-trace --stats` run instead: the stats
@@ -45,18 +47,18 @@ def read(d: str, counter: str):
     return rows
 
 
+def is_gemm(name: str) -> bool:
+    return "w12::k_gemm" in name
+
+
 def launches(rows):
-    """Group the GEMM-family dispatches into w12_gemm / w12_gemm_bf16 launches."""
+    """The GEMM-family dispatches, one per w12_gemm / w12_gemm_bf16 launch."""
     out = []
     for _, name, grid, val in rows:
-        if "w12::" not in name or any(k in name for k in ENCODE_KERNELS):
+        if not is_gemm(name):
             continue
         short = name.split("(")[0].replace("void ", "")
-        if "k_splitk_reduce" in short:
-            out[-1]["kernels"].append(short)
-            out[-1]["value"] += val
-        else:
-            out.append({"kernels": [short], "grid": grid, "value": val})
+        out.append({"kernels": [short], "grid": grid, "value": val})
     return out
 
 
@@ -70,19 +72,25 @@ def main():
                 w12_bytes = {t[3]: int(t[4]), t[5]: int(t[6])}
     shapes = {"gate_up": (bench.N_GU, bench.K_GU), "down": (bench.N_DN, bench.K_DN)}
     fr, wr = read(fetch_dir, "FETCH_SIZE"), read(write_dir, "WRITE_SIZE")
-    # calibration: the last copy kernel reads 1 GiB; the fill before it writes 1 GiB
-    tail_f = [r for r in fr if r[0] > max(x[0] for x in fr if "w12::" in x[1])]
-    tail_w = [r for r in wr if r[0] > max(x[0] for x in wr if "w12::" in x[1])]
-    copy_f = max(tail_f, key=lambda r: r[3])
-    fill_w = max(tail_w, key=lambda r: r[3])
-    fetch_scale = bench.COPY_BYTES / (copy_f[3] * 1024.0)
+    # calibration kernels after the last GEMM: the streaming read of 1 GiB - 256 B (the
+    # GEMM's load type) scales FETCH_SIZE, the 1 GiB fill scales WRITE_SIZE, the 1 GiB
+    # copy cross-checks the read scale
+    tail_f = [r for r in fr if r[0] > max(x[0] for x in fr if is_gemm(x[1]))]
+    tail_w = [r for r in wr if r[0] > max(x[0] for x in wr if is_gemm(x[1]))]
+    stream_f = [r for r in tail_f if "k_stream_read" in r[1]][-1]
+    copy_f = max((r for r in tail_f if "w12::" not in r[1]), key=lambda r: r[3])
+    fill_w = max((r for r in tail_w if "w12::" not in r[1]), key=lambda r: r[3])
+    fetch_scale = (bench.COPY_BYTES - 256) / (stream_f[3] * 1024.0)
     write_scale = bench.COPY_BYTES / (fill_w[3] * 1024.0)
+    copy_scale = bench.COPY_BYTES / (copy_f[3] * 1024.0)
     lf, lw = launches(fr), launches(wr)
     assert len(lf) == len(lw) and len(lf) % 20 == 0, (len(lf), len(lw))
     keys = [f"M{m}_{name}" for m in bench.MS for name in ("gate_up", "down")]
     rec = {"source_sha256": bench.kernel_source_hash(), "profile": command,
            "fetch_scale": fetch_scale, "write_scale": write_scale,
-           "calibration": {"copy_kernel": copy_f[1][:80], "copy_fetch_kib": copy_f[3],
+           "calibration": {"stream_read_fetch_kib": stream_f[3], "stream_read_bytes": bench.COPY_BYTES - 256,
+                           "copy_kernel": copy_f[1][:80], "copy_fetch_kib": copy_f[3],
+                           "copy_fetch_scale": copy_scale,
                            "fill_kernel": fill_w[1][:80], "fill_write_kib": fill_w[3],
                            "bytes": bench.COPY_BYTES},
            "launches": {}, "bf16_launches": {}}
@@ -108,10 +116,11 @@ def main():
              f"    {command.replace('PMC', 'WRITE_SIZE').replace('DIR', write_dir)}",
              f"    python bench_counters.py {fetch_dir} {write_dir} \"<command>\" <profile log>",
              "",
-             f"Scales: FETCH_SIZE x {fetch_scale:.4f} (a 1 GiB device copy, `{copy_f[1][:40]}`, "
-             f"reads {copy_f[3]:.0f} KiB), WRITE_SIZE x {write_scale:.4f} (a 1 GiB fill, "
-             f"`{fill_w[1][:40]}`, writes {fill_w[3]:.0f} KiB).  Source sha256 "
-             f"`{rec['source_sha256'][:16]}...`.", "",
+             f"Scales: FETCH_SIZE x {fetch_scale:.4f} (`w12::k_stream_read` over 1 GiB - 256 B with the "
+             f"GEMM's nontemporal 16-byte buffer loads reads {stream_f[3]:.0f} KiB; a 1 GiB device copy, "
+             f"`{copy_f[1][:40]}`, reads {copy_f[3]:.0f} KiB, scale {copy_scale:.4f}), "
+             f"WRITE_SIZE x {write_scale:.4f} (a 1 GiB fill, `{fill_w[1][:40]}`, writes "
+             f"{fill_w[3]:.0f} KiB).  Source sha256 `{rec['source_sha256'][:16]}...`.", "",
              "| launch | kernels | W12: HBM bytes | algorithmic | ratio | BF16 kernel: HBM bytes | algorithmic | ratio |",
              "|---|---|---|---|---|---|---|---|"]
     for key in keys:

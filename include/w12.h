@@ -274,6 +274,17 @@ w12_status w12_logits_f32(const uint16_t* x, uint32_t m, const w12_desc* d, floa
 w12_status w12_rms_rescale(const uint16_t* x, uint32_t m, uint64_t k, uint16_t* y,
                            void* stream);
 
+/* Measurement helper, not part of the W12 method: streams `bytes` (a multiple of 16,
+ * below 2^32) of device memory at `buf` (16-byte aligned) with the nontemporal 16-byte
+ * buffer loads the GEMM kernels use for W12 tiles, grid-stride over `workgroups`
+ * (1..65536) workgroups of 256 threads; each wave stores the XOR of what it read in
+ * sink[4 * workgroup + wave] (device, 4 * workgroups uint32, 4-byte aligned).  Its time is
+ * the streaming-read ceiling a GEMM launch of the same size is compared with, and its
+ * FETCH_SIZE counter scales the traffic counters for these loads.  Errors: W12_ERR_NULL,
+ * W12_ERR_SHAPE (bytes), W12_ERR_RANGE (workgroups), W12_ERR_ALIGN. */
+w12_status w12_stream_read(const void* buf, uint64_t bytes, uint32_t workgroups, uint32_t* sink,
+                           void* stream);
+
 /* Static description of a status code. */
 const char* w12_status_str(w12_status s);
 

@@ -6,12 +6,12 @@ from .w12 import (EXPORTS, MAX_GROUP, MAX_M, OP_DECODE, OP_ENCODE, OP_GEMM, OP_G
                   OP_GEMM_GROUP, OP_VERIFY, Prepared, W12Desc, W12Error, W12Tensor, decode,
                   bf16_tile, encode, gemm, gemm_bf16, gemm_noalloc, NOALLOC_SCRATCH_BYTES, gemm_bf16_tiled, gemm_group, lib, lib_path, lmhead_verify,
                   lmhead_verify_batched, prepare_gemm, prepare_gemm_group, prepare_rms, prepare_verify, prepare_verify_batched,
-                  rms_rescale, status_str, tiles_bytes, verify_candidates, logits_f32, workspace,
+                  rms_rescale, status_str, stream_read, tiles_bytes, verify_candidates, logits_f32, workspace,
                   workspace_bytes)
 
 __all__ = ["EXPORTS", "MAX_GROUP", "MAX_M", "OP_DECODE", "OP_ENCODE", "OP_GEMM", "OP_GEMM_BF16",
            "OP_GEMM_GROUP", "OP_VERIFY", "Prepared", "W12Desc", "W12Error", "W12Tensor",
            "bf16_tile", "decode", "encode", "gemm", "gemm_bf16", "gemm_noalloc", "NOALLOC_SCRATCH_BYTES", "gemm_bf16_tiled", "gemm_group", "lib", "lib_path",
            "lmhead_verify", "lmhead_verify_batched", "prepare_gemm", "prepare_gemm_group", "prepare_rms",
-           "prepare_verify", "prepare_verify_batched", "rms_rescale", "status_str", "tiles_bytes", "verify_candidates",
+           "prepare_verify", "prepare_verify_batched", "rms_rescale", "status_str", "stream_read", "tiles_bytes", "verify_candidates",
            "logits_f32", "workspace", "workspace_bytes"]

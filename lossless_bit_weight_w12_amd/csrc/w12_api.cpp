@@ -673,6 +673,15 @@ w12_status w12_rms_rescale(const uint16_t* x, uint32_t m, uint64_t k, uint16_t* 
   return hip_status(launch_rms_rescale(x, m, (uint32_t)k, y, (hipStream_t)stream));
 }
 
+w12_status w12_stream_read(const void* buf, uint64_t bytes, uint32_t workgroups, uint32_t* sink,
+                           void* stream) {
+  if (!buf || !sink) return W12_ERR_NULL;
+  if (bytes == 0 || bytes % 16 || bytes >= (1ull << 32)) return W12_ERR_SHAPE;
+  if (workgroups < 1 || workgroups > 65536) return W12_ERR_RANGE;
+  if (!aligned(buf, 16) || !aligned(sink, 4)) return W12_ERR_ALIGN;
+  return hip_status(launch_stream_read(buf, (uint32_t)bytes, workgroups, sink, (hipStream_t)stream));
+}
+
 const char* w12_status_str(w12_status s) {
   switch (s) {
     case W12_OK: return "ok";

@@ -224,6 +224,8 @@ hipError_t launch_verify_pass2(const VerifyArgs& a, hipStream_t s);
 
 hipError_t launch_rms_rescale(const uint16_t* x, uint32_t m, uint32_t k, uint16_t* y,
                               hipStream_t s);
+hipError_t launch_stream_read(const void* buf, uint32_t bytes, uint32_t workgroups, uint32_t* sink,
+                              hipStream_t s);
 
 // w12_gemm in two halves (host layer): argument checks with the workspace bytes the call
 // needs, then the launch on a workspace of at least that size.

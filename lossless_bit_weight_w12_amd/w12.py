@@ -24,7 +24,7 @@ EXPORTS = ("w12_tiles_bytes", "w12_workspace_bytes", "w12_workspace_init", "w12_
            "w12_gemm_group_rms", "w12_gemm_bf16", "w12_bf16_tile",
            "w12_gemm_bf16_tiled", "w12_lmhead_verify", "w12_lmhead_verify_batched",
            "w12_logits_f32",
-           "w12_rms_rescale", "w12_status_str", "w12_version", "w12_gemm_noalloc")
+           "w12_rms_rescale", "w12_status_str", "w12_version", "w12_gemm_noalloc", "w12_stream_read")
 NOALLOC_SCRATCH_BYTES = 32 << 20   # W12_NOALLOC_SCRATCH_BYTES
 
 
@@ -78,6 +78,8 @@ def lib():
                                      c_size_t, c_void_p]
         L.w12_gemm_noalloc.restype = c_int32
         L.w12_gemm_noalloc.argtypes = [c_void_p, c_uint32, ctypes.POINTER(W12Desc), c_void_p, c_void_p]
+        L.w12_stream_read.restype = c_int32
+        L.w12_stream_read.argtypes = [c_void_p, c_uint64, c_uint32, c_void_p, c_void_p]
         L.w12_gemm_rms.restype = c_int32
         L.w12_gemm_rms.argtypes = L.w12_gemm.argtypes
         L.w12_gemm_group_rms.restype = c_int32
@@ -269,6 +271,15 @@ def gemm_noalloc(x, t: W12Tensor, out=None):
     _check("w12_gemm_noalloc", lib().w12_gemm_noalloc(_ptr(x), m, ctypes.byref(d), _ptr(_as_bits(out)),
                                                       _stream(x.device)))
     return out
+
+
+def stream_read(buf, offset: int, nbytes: int, workgroups: int, sink):
+    """The streaming-read probe (w12_stream_read) over bytes [offset, offset + nbytes) of the
+    uint8 device tensor buf; sink: int32 device tensor of at least 4 * workgroups."""
+    if offset < 0 or offset + nbytes > buf.numel() or sink.numel() < 4 * workgroups:
+        raise ValueError("stream_read: range outside buf, or sink too small")
+    _check("w12_stream_read", lib().w12_stream_read(c_void_p(buf.data_ptr() + offset), nbytes,
+                                                    workgroups, _ptr(sink), _stream(buf.device)))
 
 
 def _group_args(x, ts, outs):

@@ -257,3 +257,14 @@ def test_library_binds_to_torchs_hip_runtime():
     out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300)
     assert out.returncode == 0, out.stderr[-2000:]
     assert out.stdout.strip().splitlines()[-1] == "1"      # one HIP runtime in the process
+
+
+def test_stream_read_validation(L):
+    assert L.w12_stream_read(None, 1024, 16, FAKE, None) == -1
+    assert L.w12_stream_read(FAKE, 1024, 16, None, None) == -1
+    assert L.w12_stream_read(FAKE, 0, 16, FAKE, None) == -2
+    assert L.w12_stream_read(FAKE, 1000, 16, FAKE, None) == -2
+    assert L.w12_stream_read(FAKE, 1 << 32, 16, FAKE, None) == -2
+    assert L.w12_stream_read(FAKE, 1024, 0, FAKE, None) == -3
+    assert L.w12_stream_read(FAKE, 1024, 65537, FAKE, None) == -3
+    assert L.w12_stream_read(FAKE + 8, 1024, 16, FAKE, None) == -7
