@@ -58,7 +58,7 @@ MS = (1, 4, 8, 16, 32)
 BATCHED_MS = (64, 128)      # batched regime (several requests' rows at once), reported beside
 N_GU, K_GU = 34816, 5120
 N_DN, K_DN = 5120, 17408
-WARM_S = 0.3                # seconds of work before the headline loop
+WARM_S = 1.0                # seconds of work before the headline loop (clock ramp from idle)
 SAMPLE_ROWS = 256           # rows of each matrix the oracle checks (cpu_baseline leg)
 
 
@@ -161,8 +161,11 @@ def bootstrap_ci(np, samples, n_boot: int = 10000, seed: int = 0):
 
 def gpu_state():
     """Clock, temperature and power of GPU 0 from amd-smi (None where the tool or a
-    field is unavailable)."""
+    field is unavailable).  Not under a profiler: its preloaded library would start the
+    tool's interpreter with the GPU already initialised."""
     import subprocess
+    if "rocprof" in os.environ.get("LD_PRELOAD", ""):
+        return None
     try:
         out = subprocess.run(["amd-smi", "metric", "-g", "0", "-c", "-t", "-p", "--json"],
                              capture_output=True, text=True, timeout=30)
@@ -189,17 +192,22 @@ def gpu_state():
 
 
 def warm(torch, fns, seconds: float):
-    """Run fns(i) in turn for at least `seconds` of wall time, keeping the queue short so
-    the host clock follows the GPU (the GPU clock ramps up under load)."""
+    """Run fns(i) in turn for at least `seconds` of wall time with the GPU never idle: two
+    batches stay queued (the host waits for the batch before the last one), so the GPU
+    clock ramps up under continuous load and the host clock follows the GPU."""
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     i = 0
+    pending = []
     while time.perf_counter() - t0 < seconds:
         for f in fns:
             f(i)
         i += 1
-        if i % 2 == 0:
-            torch.cuda.synchronize()
+        e = torch.cuda.Event()
+        e.record()
+        pending.append(e)
+        if len(pending) > 2:
+            pending.pop(0).synchronize()
     torch.cuda.synchronize()
 
 

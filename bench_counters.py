@@ -31,6 +31,7 @@ sys.path.insert(0, ROOT)
 
 import bench  # noqa: E402
 
+PROFILED_STEPS = 2   # --steps of the profile command
 ENCODE_KERNELS = ("k_fill_zero", "k_hist", "k_codebook", "k_count_tiles", "k_scan", "k_pack",
                   "k_bf16_tile")
 
@@ -83,8 +84,12 @@ def main():
     fetch_scale = (bench.COPY_BYTES - 256) / (stream_f[3] * 1024.0)
     write_scale = bench.COPY_BYTES / (fill_w[3] * 1024.0)
     copy_scale = bench.COPY_BYTES / (copy_f[3] * 1024.0)
+    # the profiled steps are the last PROFILED_STEPS (W12 step, BF16 step) pairs of 20
+    # launches; the time-based warm-up before them varies in length between the passes
     lf, lw = launches(fr), launches(wr)
-    assert len(lf) == len(lw) and len(lf) % 20 == 0, (len(lf), len(lw))
+    assert len(lf) % 20 == 0 and len(lw) % 20 == 0 and min(len(lf), len(lw)) >= 20 * PROFILED_STEPS
+    lf, lw = lf[-20 * PROFILED_STEPS:], lw[-20 * PROFILED_STEPS:]
+    assert [a["grid"] for a in lf] == [b["grid"] for b in lw]
     keys = [f"M{m}_{name}" for m in bench.MS for name in ("gate_up", "down")]
     rec = {"source_sha256": bench.kernel_source_hash(), "profile": command,
            "fetch_scale": fetch_scale, "write_scale": write_scale,

@@ -107,47 +107,68 @@ inline bool codebook_is_run(const uint8_t* c) {
 // take 10 waves as well, one workgroup per CU (down M128 W12 65.1 -> 48.6 us, tiled BF16
 // 69.2 -> 50.7 us; at 64 columns 5 stays ahead); other shapes keep 4 at 128 columns (74 KB
 // of LDS per workgroup; gate+up M128 135 -> 164 us with 5).
+// W12 launches with the BF16 epilogue at 1..32 rows choose the wave count among 5, 7 and
+// 9 by the same residency argument, counted in tiles: every workgroup is resident, so the
+// launch takes as long as the CU with the most tiles to stream, ceil(workgroups / 256) x
+// waves x tile columns per split; the larger wave count wins a tie (fewer x requests per
+// row-block).  Measured (one box, interleaved): the decode chain's q/k/v group (448
+// row-blocks, K split 8 ways; 5 -> 7 waves, 720 -> 512 workgroups) 19.95 -> 17.48 us at
+// M = 24, 20.42 -> 19.09 us with the RMS rescale; its gate/up group (2176 row-blocks;
+// 5 or 10 -> 9 waves, 242 workgroups) 50.78 -> 49.63 us with the RMS rescale at M = 24,
+// the MLP gate+up within 1 % at M = 1..32; down and o (320 row-blocks) keep 5.
 GemmPlan make_plan(uint32_t m, uint64_t n, uint64_t k, int epi, bool bf16_src = false) {
   GemmPlan p;
   const uint64_t nb = n / 16, g = k / 128;
-  uint64_t units, min_cols;   // min_cols: tile columns a split keeps at least
+  uint64_t min_cols;   // tile columns a split keeps at least
   p.kind = KIND_WAVE_COLUMNS;
   p.mfma = m >= W12_MFMA_MIN_M;
   p.rbw = 1;
   p.nw = 4;
   const bool few_rows = nb < W12_RBW2_MIN_NB;
   const bool w12_bf16_out = !bf16_src && epi == EPI_BF16;
+  // K splits of a launch of `groups` row-block groups (units: 4-wave workgroup equivalents)
+  auto splits = [&](uint64_t units, int kind) -> uint64_t {
+    // W12 column-synchronous launches that already fill the chip (>= 512 four-wave
+    // workgroups) keep K whole: the partials and their completion cost more than the
+    // extra parallelism gains.  The BF16 kernel (4 KB tiles) is faster split: measured
+    // on the MLP gate+up at M16 / M32, 81 / 92 us split in two against 87 / 100 us whole.
+    const bool keep_k = !bf16_src && kind == KIND_COLUMN_SYNC &&
+                        units >= (uint64_t)kTargetWorkgroups / 2;
+    if (epi != EPI_BF16 || keep_k) return 1;
+    // enough splits to reach the workgroup target, each keeping >= min_cols columns
+    uint64_t ns = ((uint64_t)kTargetWorkgroups + units - 1) / units;
+    ns = std::min<uint64_t>(ns, std::min<uint64_t>(W12_NS_CAP, g / min_cols));
+    return std::max<uint64_t>(ns, 1);
+  };
+  uint64_t units;
   if (w12_bf16_out || (p.mfma && (few_rows || m >= 16))) {
     p.kind = KIND_COLUMN_SYNC;
-    // 17..128 columns (16..128 for the BF16 baselines): 10 waves where that is at most one
-    // workgroup per CU with K whole
-    const bool ten = (m > 16 || bf16_src) && nb >= 2048 && (nb + 9) / 10 <= 256;
-    p.nw = epi != EPI_BF16 ? 8
-           : few_rows ? (m > 64 ? W12_CS_NW32 : W12_CS_FEW_NW)
-           : ten ? W12_CS_NW32 : (m > 64 ? 4 : W12_CS_NW);
-    p.n_rbg = (uint32_t)((nb + p.nw - 1) / p.nw);
-    units = (uint64_t)p.n_rbg * p.nw / 4;     // in 4-wave workgroup equivalents
     min_cols = W12_CS_MIN_COLS;
+    if (w12_bf16_out && m <= 32) {
+      uint64_t best = ~0ull;
+      for (int nw : {5, 7, 9}) {
+        const uint64_t groups = (nb + nw - 1) / nw;
+        const uint64_t ns = splits(groups * nw / 4, KIND_COLUMN_SYNC);
+        const uint64_t tiles = (groups * ns + 255) / 256 * nw * ((g + ns - 1) / ns);
+        if (tiles <= best) { best = tiles; p.nw = nw; }
+      }
+    } else {
+      // 17..128 columns (16..128 for the BF16 baselines): 10 waves where that is at most
+      // one workgroup per CU with K whole
+      const bool ten = (m > 16 || bf16_src) && nb >= 2048 && (nb + 9) / 10 <= 256;
+      p.nw = epi != EPI_BF16 ? 8
+             : few_rows ? (m > 64 ? W12_CS_NW32 : W12_CS_FEW_NW)
+             : ten ? W12_CS_NW32 : (m > 64 ? 4 : W12_CS_NW);
+    }
+    p.n_rbg = (uint32_t)((nb + p.nw - 1) / p.nw);
+    units = (uint64_t)p.n_rbg * p.nw / 4;
   } else {
+    min_cols = 4;
     p.rbw = few_rows ? 1 : 2;
     p.n_rbg = (uint32_t)((nb + p.rbw - 1) / p.rbw);
     units = p.n_rbg;
-    min_cols = 4;
   }
-  uint64_t ns = 1;
-  // W12 column-synchronous launches that already fill the chip (>= 512 four-wave
-  // workgroups) keep K whole: the partials and their completion cost more than the
-  // extra parallelism gains.  The BF16 kernel (4 KB tiles) is faster split: measured
-  // on the MLP gate+up at M16 / M32, 81 / 92 us split in two against 87 / 100 us whole.
-  const bool keep_k = !bf16_src && p.kind == KIND_COLUMN_SYNC &&
-                      units >= (uint64_t)kTargetWorkgroups / 2;
-  if (epi == EPI_BF16 && !keep_k) {
-    // enough splits to reach the workgroup target, each keeping >= min_cols columns
-    ns = ((uint64_t)kTargetWorkgroups + units - 1) / units;
-    ns = std::min<uint64_t>(ns, std::min<uint64_t>(W12_NS_CAP, g / min_cols));
-    ns = std::max<uint64_t>(ns, 1);
-  }
-  p.nsplit = (uint32_t)ns;     // the kernels deal the K range evenly over the splits
+  p.nsplit = (uint32_t)splits(units, p.kind);   // the kernels deal the K range evenly
   return p;
 }
 

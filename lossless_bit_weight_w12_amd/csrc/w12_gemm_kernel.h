@@ -1102,6 +1102,17 @@ hipError_t launch_gemm_src(const GemmArgs& a, int epi, const GemmPlan& pl, hipSt
                            a.sabs, a.bm, p);                                                  \
       else                                                                                    \
         return hipErrorInvalidValue; /* not instantiated: the plan never asks for it */      \
+    } else if (pl.nw == 9 || pl.nw == 7) {                                                    \
+      if constexpr (EPI_ == EPI_BF16 && MT_ <= 32 && !plain_bf16(SRC)) {                      \
+        if (pl.nw == 9)                                                                       \
+          hipLaunchKernelGGL((k_gemm_cs<MT_, 9, SRC, EPI_BF16>), grid, dim3(576), 0, s, a.x, f32, \
+                             a.sabs, a.bm, p);                                                \
+        else                                                                                  \
+          hipLaunchKernelGGL((k_gemm_cs<MT_, 7, SRC, EPI_BF16>), grid, dim3(448), 0, s, a.x, f32, \
+                             a.sabs, a.bm, p);                                                \
+      } else {                                                                                \
+        return hipErrorInvalidValue; /* not instantiated: the plan never asks for it */      \
+      }                                                                                       \
     } else if (pl.nw == 5)                                                                    \
       hipLaunchKernelGGL((k_gemm_cs<MT_, 5, SRC, EPI_>), grid, dim3(320), 0, s, a.x, f32,     \
                          a.sabs, a.bm, p);                         \
