@@ -131,14 +131,24 @@ w12_status w12_encode_count(const uint16_t* w, uint64_t n, uint64_t k,
                             uint8_t codebook_out[16], uint8_t* e_max_out,
                             uint64_t* n_esc_out, void* ws, size_t ws_bytes, void* stream);
 
-/* Encode, second half: writes d->tiles, d->esc_off and d->esc for w [n][k] using
- * d->codebook; d->n_esc must be the count w12_encode_count returned for that
- * codebook (escape writes are bounded by it, so a wrong value cannot overflow `esc`).
- * Output bytes are identical to the CPU oracle's. */
+/* Byte offset in an ENCODE workspace of the u32 where w12_encode leaves the true escape
+ * count of its input for d->codebook (readable once the stream has reached the call). */
+#define W12_ENCODE_TOTAL_OFFSET 2112
+
+/* Encode, second half (the W12 v1 layout above; lossless 12-bit format per "SpecPilot"
+ * glossary, "Differentiation", at about 12.01-12.02 bits per weight per the review's
+ * "The mechanisms it found"): writes d->tiles, d->esc_off and d->esc for w [n][k] using
+ * d->codebook.  d->n_esc must be the count w12_encode_count returned for that codebook.
+ * The call does not synchronise, so it cannot check that: with a wrong n_esc the encoding
+ * is wrong (escapes past n_esc are dropped) but memory-safe, since escape writes stop at
+ * n_esc and every esc_off entry is clamped to n_esc, so no later call reads past `esc`;
+ * compare the u32 at W12_ENCODE_TOTAL_OFFSET of ws with n_esc to detect it (equal for a
+ * correct call).  Output bytes are identical to the CPU oracle's. */
 w12_status w12_encode(const uint16_t* w, const w12_desc* d, void* ws, size_t ws_bytes,
                       void* stream);
 
-/* Bit-exact inverse: w_out device BF16 [n][k] row-major (16-byte aligned). */
+/* Bit-exact inverse of w12_encode (lossless per "SpecPilot" glossary, "Differentiation"):
+ * w_out device BF16 [n][k] row-major (16-byte aligned). */
 w12_status w12_decode(const w12_desc* d, uint16_t* w_out, void* stream);
 
 /* y = x . W^T with W decoded in registers ("StargazerX0/SpecPilot", "What it is"):

@@ -2,16 +2,20 @@
 verification with a certified exact-argmax LM head.  The compute lives in libw12.so
 (HIP kernels for gfx950 behind a C ABI, declared in include/w12.h); this package is its
 thin Python binding."""
-from .w12 import (EXPORTS, MAX_GROUP, MAX_M, OP_DECODE, OP_ENCODE, OP_GEMM, OP_GEMM_BF16,
-                  OP_GEMM_GROUP, OP_VERIFY, Prepared, W12Desc, W12Error, W12Tensor, decode,
-                  bf16_tile, encode, gemm, gemm_bf16, gemm_noalloc, NOALLOC_SCRATCH_BYTES, gemm_bf16_tiled, gemm_group, lib, lib_path, lmhead_verify,
-                  lmhead_verify_batched, prepare_gemm, prepare_gemm_group, prepare_rms, prepare_verify, prepare_verify_batched,
-                  rms_rescale, status_str, stream_read, tiles_bytes, verify_candidates, logits_f32, workspace,
-                  workspace_bytes)
+from .w12 import (ENCODE_TOTAL_OFFSET, EXPORTS, MAX_GROUP, MAX_M, NOALLOC_SCRATCH_BYTES,
+                  OP_DECODE, OP_ENCODE, OP_GEMM, OP_GEMM_BF16, OP_GEMM_GROUP, OP_VERIFY,
+                  Prepared, W12Desc, W12Error, W12Tensor, bf16_tile, decode, encode, gemm,
+                  gemm_bf16, gemm_bf16_tiled, gemm_group, gemm_noalloc, lib, lib_path,
+                  lmhead_verify, lmhead_verify_batched, logits_f32, prepare_gemm,
+                  prepare_gemm_group, prepare_rms, prepare_verify, prepare_verify_batched,
+                  rms_rescale, status_str, stream_read, tiles_bytes, verify_candidates,
+                  workspace, workspace_bytes)
 
-__all__ = ["EXPORTS", "MAX_GROUP", "MAX_M", "OP_DECODE", "OP_ENCODE", "OP_GEMM", "OP_GEMM_BF16",
-           "OP_GEMM_GROUP", "OP_VERIFY", "Prepared", "W12Desc", "W12Error", "W12Tensor",
-           "bf16_tile", "decode", "encode", "gemm", "gemm_bf16", "gemm_noalloc", "NOALLOC_SCRATCH_BYTES", "gemm_bf16_tiled", "gemm_group", "lib", "lib_path",
-           "lmhead_verify", "lmhead_verify_batched", "prepare_gemm", "prepare_gemm_group", "prepare_rms",
-           "prepare_verify", "prepare_verify_batched", "rms_rescale", "status_str", "stream_read", "tiles_bytes", "verify_candidates",
-           "logits_f32", "workspace", "workspace_bytes"]
+__all__ = ["ENCODE_TOTAL_OFFSET", "EXPORTS", "MAX_GROUP", "MAX_M", "NOALLOC_SCRATCH_BYTES",
+           "OP_DECODE", "OP_ENCODE", "OP_GEMM", "OP_GEMM_BF16", "OP_GEMM_GROUP", "OP_VERIFY",
+           "Prepared", "W12Desc", "W12Error", "W12Tensor", "bf16_tile", "decode", "encode",
+           "gemm", "gemm_bf16", "gemm_bf16_tiled", "gemm_group", "gemm_noalloc", "lib",
+           "lib_path", "lmhead_verify", "lmhead_verify_batched", "logits_f32", "prepare_gemm",
+           "prepare_gemm_group", "prepare_rms", "prepare_verify", "prepare_verify_batched",
+           "rms_rescale", "status_str", "stream_read", "tiles_bytes", "verify_candidates",
+           "workspace", "workspace_bytes"]

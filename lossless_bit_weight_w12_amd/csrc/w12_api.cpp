@@ -266,7 +266,7 @@ EncodeLayout encode_layout(uint64_t n, uint64_t k) {
   const uint64_t tiles = (n / 16) * (k / 128);
   L.hist = 0;                 // 256 x u64
   L.result = 2048;            // 64 bytes
-  L.total = 2048 + 64;        // u32
+  L.total = W12_ENCODE_TOTAL_OFFSET;   // u32: the true escape count (w12_encode)
   L.tile_cnt = 4096;
   L.tile_off = L.tile_cnt + align256((size_t)tiles * 4);
   L.bytes = L.tile_off + align256((size_t)tiles * 4);
@@ -548,7 +548,8 @@ w12_status w12_encode(const uint16_t* w, const w12_desc* d, void* ws, size_t ws_
   uint32_t* tile_off = (uint32_t*)(base + L.tile_off);
   hipError_t e = launch_encode_count_tiles(w, nb, g, mask, tile_cnt, s);
   if (e == hipSuccess)
-    e = launch_encode_scan(tile_cnt, nb * g, g, tile_off, d->esc_off, (uint32_t*)(base + L.total), s);
+    e = launch_encode_scan(tile_cnt, nb * g, g, tile_off, d->esc_off, (uint32_t)d->n_esc,
+                           (uint32_t*)(base + L.total), s);
   if (e == hipSuccess)
     e = launch_encode_pack(w, nb, g, cb, tile_off, (uint8_t*)d->tiles, d->esc, d->n_esc, s);
   return hip_status(e);

@@ -154,11 +154,14 @@ hipError_t launch_encode_count_tiles(const uint16_t* w, uint32_t nb, uint32_t g_
 // One workgroup walks the counts in chunks of 8192: each chunk is read coalesced into
 // LDS, every thread scans 8 consecutive counts in registers, the 1024 thread sums are
 // scanned with wave shuffles and a 16-entry LDS step, and the running total carries
-// into the next chunk.
+// into the next chunk.  Row-block offsets are clamped to the escape array's capacity, so
+// a descriptor whose n_esc is smaller than the true count never leads a later reader past
+// the end of `esc`; `total` receives the true count.
 constexpr uint32_t kScanChunk = 8192;
 __global__ __launch_bounds__(1024) void k_scan(const uint32_t* tile_cnt, uint32_t n_tiles,
                                                uint32_t g_cols, uint32_t* tile_off,
-                                               uint32_t* esc_off, uint32_t* total) {
+                                               uint32_t* esc_off, uint32_t esc_cap,
+                                               uint32_t* total) {
   __shared__ uint32_t buf[kScanChunk];
   __shared__ uint32_t wsum[16];
   const uint32_t tid = threadIdx.x, lane = tid & 63u, wave = tid >> 6;
@@ -194,23 +197,23 @@ __global__ __launch_bounds__(1024) void k_scan(const uint32_t* tile_cnt, uint32_
       const uint32_t i = base + 8u * tid + e;
       if (i < n_tiles) {
         tile_off[i] = excl + v[e];
-        if (i % g_cols == 0) esc_off[i / g_cols] = excl + v[e];
+        if (i % g_cols == 0) esc_off[i / g_cols] = min(excl + v[e], esc_cap);
       }
     }
     carry += chunk_total;
     __syncthreads();   // buf and wsum are rewritten by the next chunk
   }
   if (tid == 0) {
-    esc_off[n_tiles / g_cols] = carry;
+    esc_off[n_tiles / g_cols] = min(carry, esc_cap);
     *total = carry;
   }
 }
 
 hipError_t launch_encode_scan(const uint32_t* tile_cnt, uint32_t n_tiles, uint32_t g_cols,
-                              uint32_t* tile_off, uint32_t* esc_off, uint32_t* total,
-                              hipStream_t s) {
+                              uint32_t* tile_off, uint32_t* esc_off, uint32_t esc_cap,
+                              uint32_t* total, hipStream_t s) {
   hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, s, tile_cnt, n_tiles, g_cols, tile_off,
-                     esc_off, total);
+                     esc_off, esc_cap, total);
   return hipGetLastError();
 }
 

@@ -1083,10 +1083,17 @@ hipError_t launch_gemm_src(const GemmArgs& a, int epi, const GemmPlan& pl, hipSt
     if (pl.rbw == 2) W12_L(M_, MT_, MF_, 2, 4, EPI_); \
     else W12_L(M_, MT_, MF_, 1, 4, EPI_);             \
   } while (0)
-#define W12_EPI(M_, MT_, MF_)                                       \
-  do {                                                              \
-    if (epi == EPI_BF16) W12_RBW(M_, MT_, MF_, EPI_BF16);          \
-    else if constexpr (!plain_bf16(SRC)) W12_RBW(M_, MT_, MF_, EPI_LOGITS); \
+// (W12 GEMMs with BF16 output always run column-synchronous, and the BF16 sources have
+// no logits epilogue: neither is instantiated here)
+#define W12_EPI(M_, MT_, MF_)                                                 \
+  do {                                                                        \
+    if constexpr (plain_bf16(SRC)) {                                          \
+      if (epi != EPI_BF16) return hipErrorInvalidValue;                       \
+      W12_RBW(M_, MT_, MF_, EPI_BF16);                                        \
+    } else {                                                                  \
+      if (epi != EPI_LOGITS) return hipErrorInvalidValue;                     \
+      W12_RBW(M_, MT_, MF_, EPI_LOGITS);                                      \
+    }                                                                         \
   } while (0)
 #define W12_CS(MT_, EPI_)                                                                     \
   do {                                                                                        \

@@ -180,8 +180,8 @@ struct Codebook16 {
 hipError_t launch_encode_count_tiles(const uint16_t* w, uint32_t nb, uint32_t g_cols,
                                      const Mask256& member, uint32_t* tile_cnt, hipStream_t s);
 hipError_t launch_encode_scan(const uint32_t* tile_cnt, uint32_t n_tiles, uint32_t g_cols,
-                              uint32_t* tile_off, uint32_t* esc_off, uint32_t* total,
-                              hipStream_t s);
+                              uint32_t* tile_off, uint32_t* esc_off, uint32_t esc_cap,
+                              uint32_t* total, hipStream_t s);
 hipError_t launch_encode_pack(const uint16_t* w, uint32_t nb, uint32_t g_cols,
                               const Codebook16& cb, const uint32_t* tile_off,
                               uint8_t* tiles, uint32_t* esc, uint64_t esc_cap,

@@ -26,6 +26,7 @@ EXPORTS = ("w12_tiles_bytes", "w12_workspace_bytes", "w12_workspace_init", "w12_
            "w12_logits_f32",
            "w12_rms_rescale", "w12_status_str", "w12_version", "w12_gemm_noalloc", "w12_stream_read")
 NOALLOC_SCRATCH_BYTES = 32 << 20   # W12_NOALLOC_SCRATCH_BYTES
+ENCODE_TOTAL_OFFSET = 2112   # W12_ENCODE_TOTAL_OFFSET: true escape count in an encode workspace
 
 
 class W12Error(RuntimeError):

@@ -57,6 +57,46 @@ def test_encode_bytes_and_decode(env, name, w):
     assert np.array_equal(to_host(dec), w)
 
 
+@pytest.mark.parametrize("delta", [-5, 0, 3])
+def test_encode_wrong_escape_count_is_memory_safe(env, delta):
+    """w12_encode with a descriptor whose n_esc is off by `delta` from the true count:
+    the escape offsets stay within n_esc (no later reader passes the end of `esc`), the
+    workspace reports the true count, and with the right count the bytes equal the
+    oracle's."""
+    import ctypes
+    torch, w12 = env
+    g = np.random.default_rng(31)
+    w = wi.add_exponent_outliers(wi.gaussian_bf16((64, 512), 0.02, g), 0.01, 9)
+    ref = o.encode(w)
+    assert ref.n_esc > 10
+    n, k = w.shape
+    cap = ref.n_esc + delta
+    say("encode wrong n_esc", delta, ref.n_esc)
+    t = w12.W12Tensor(n=n, k=k, n_esc=cap, codebook=tuple(ref.codebook.tolist()), e_max=ref.e_max,
+                      tiles=torch.empty(w12.tiles_bytes(n, k), dtype=torch.uint8, device="cuda"),
+                      esc_off=torch.empty(n // 16 + 1, dtype=torch.int32, device="cuda"),
+                      esc=torch.full((cap + 8,), -1, dtype=torch.int32, device="cuda"))
+    ws = torch.zeros(w12.workspace_bytes(w12.OP_ENCODE, 1, n, k), dtype=torch.uint8, device="cuda")
+    d = t.desc()
+    st = w12.lib().w12_encode(ctypes.c_void_p(to_dev(w, torch).data_ptr()), ctypes.byref(d),
+                              ctypes.c_void_p(ws.data_ptr()), ws.numel(),
+                              ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    torch.cuda.synchronize()
+    assert st == 0
+    off0 = w12.ENCODE_TOTAL_OFFSET
+    total = int(ws[off0:off0 + 4].cpu().numpy().view(np.uint32)[0])
+    assert total == ref.n_esc
+    off = t.esc_off.cpu().numpy().view(np.uint32)
+    assert off.max() <= cap and np.all(np.diff(off.astype(np.int64)) >= 0)
+    assert np.array_equal(off, np.minimum(ref.esc_off, cap))
+    esc = t.esc.cpu().numpy()
+    assert np.all(esc[cap:] == -1)   # nothing written past n_esc
+    assert np.array_equal(t.tiles.cpu().numpy(), ref.tiles)
+    if delta >= 0:
+        assert np.array_equal(esc.view(np.uint32)[:ref.n_esc], ref.esc)
+        assert np.array_equal(to_host(w12.decode(t)), w)
+
+
 def _gemm_case(env, w, x, which):
     torch, w12 = env
     xt = to_dev(x, torch)
@@ -232,7 +272,7 @@ def test_gemm_deterministic_and_overwrites(env):
 
 def test_gemm_workspace_reuse_across_shapes(env):
     """One workspace serves split-K launches of different shapes in any order: the
-    arrival counters sit at a fixed place and every call leaves them at zero."""
+    split-K tickets sit at a fixed place and every call leaves them at zero."""
     torch, w12 = env
     g = np.random.default_rng(12)
     cases = []

@@ -268,3 +268,23 @@ def test_stream_read_validation(L):
     assert L.w12_stream_read(FAKE, 1024, 0, FAKE, None) == -3
     assert L.w12_stream_read(FAKE, 1024, 65537, FAKE, None) == -3
     assert L.w12_stream_read(FAKE + 8, 1024, 16, FAKE, None) == -7
+
+
+def test_header_constants_match_binding():
+    """The binding's copies of the header's numeric constants agree with include/w12.h."""
+    import re
+    from lossless_bit_weight_w12_amd import w12 as b
+    text = open(HEADER).read()
+
+    def define(name):
+        m = re.search(r"#define\s+%s\s+\(?(\d+)u?(?:\s*<<\s*(\d+))?\)?" % name, text)
+        assert m, name
+        return int(m.group(1)) << int(m.group(2) or 0)
+
+    assert define("W12_ENCODE_TOTAL_OFFSET") == b.ENCODE_TOTAL_OFFSET
+    assert define("W12_NOALLOC_SCRATCH_BYTES") == b.NOALLOC_SCRATCH_BYTES
+    assert define("W12_MAX_M") == b.MAX_M
+    for name, val in [("W12_OP_ENCODE", b.OP_ENCODE), ("W12_OP_DECODE", b.OP_DECODE),
+                      ("W12_OP_GEMM", b.OP_GEMM), ("W12_OP_GEMM_BF16", b.OP_GEMM_BF16),
+                      ("W12_OP_VERIFY", b.OP_VERIFY), ("W12_OP_GEMM_GROUP", b.OP_GEMM_GROUP)]:
+        assert define(name) == val, name
