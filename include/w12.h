@@ -182,8 +182,8 @@ w12_status w12_gemm_noalloc(const uint16_t* x, uint32_t m, const w12_desc* d, ui
 
 /* Several W12 weights that read the same x (q, k and v of a layer; gate and up):
  * ys[i] = x . W_i^T for i < n_w (1..W12_MAX_GROUP), all with the same k, in one launch
- * per codebook kind (row-blocks of the weights numbered consecutively), plus the
- * split-K reduce kernel when K is split.  descs: host array of n_w descriptors; ys:
+ * per codebook kind (row-blocks of the weights numbered consecutively; a K split is
+ * completed inside the launch, as in w12_gemm).  descs: host array of n_w descriptors; ys:
  * host array of n_w device BF16 outputs [m][n_i], each 16-byte aligned.  Same arithmetic, rounding and
  * determinism as w12_gemm (the K split can differ, so the last bit can too).
  * ws: w12_workspace_bytes(W12_OP_GEMM_GROUP, m, sum of n_i, k) bytes.  Errors: as

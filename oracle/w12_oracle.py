@@ -431,3 +431,116 @@ def accepted_lengths_batched(argmax: np.ndarray, draft: np.ndarray, row_off, n_d
         a, nd = int(row_off[r]), int(n_draft[r])
         out.append(accepted_length(argmax[a:a + nd], draft[a:a + nd]))
     return np.array(out, dtype=np.int64)
+
+
+# ----------------------------------------------------------------------------- screen copy
+# Two-level verification ("SpecPilot: an agent doubled speculative decoding speed, and the
+# 10.87x needs context", section "The mechanisms it found": verification in two levels,
+# with an 8-bit copy of the head; "SpecPilot" glossary, "Differentiation"): a first pass
+# over an 8-bit copy of the LM head rules out the logits that cannot be the argmax, and
+# only the rest are computed from the exact (W12) weights.  The pages give the idea and
+# the bit width only.  Screen copy v1 (defined here; implemented independently on the GPU):
+#
+#   groups   32 consecutive columns of a row: group g holds columns 32g .. 32g+31
+#   scale    s_vg = the smallest BF16 value >= (largest |w| over the group's finite
+#            weights) / 127, and at least 2^-100 (so a group of zeros gets 2^-100)
+#   code     q_vk = w_vk / s_vg rounded to the nearest integer, ties to even
+#            (|q| <= 127 by the choice of s); 0 for a non-finite weight
+#   tile     16 rows x 128 columns, 2176 bytes at (g*(N/16) + b)*2176 (column-major tile
+#            order, as W12): the int8 code of element t of lane slot l (the W12 slot
+#            layout: row r = l % 16, column 128g + 32(t//8) + 8(l//16) + t%8) at the W12
+#            sign/mantissa byte position 1024*(t//16) + 16*l + t%16, then the tile's 64
+#            scales, BF16 little-endian, row 4a+i (a, i = 0..3) and 32-column group j of
+#            the tile at 2048 + 32a + 8i + 2j
+#   rows     the per-row constants the screen's error bound needs are upper bounds of
+#            ||r_v||_2 + gamma*||w^_v||_2 (r = w - w^, w^ = q*s); they are not unique
+#            and are checked against the exact sums below, not stored here.
+#
+# The screen bound: for any x, z_v = sum_k x_k w_vk = z8_v + sum_k x_k r_vk with
+# z8_v = sum_k x_k w^_vk, and |sum_k x_k r_vk| <= ||x||_2 ||r_v||_2 (Cauchy-Schwarz); an
+# FP32 evaluation of z8 in any order with at most D = K + 64 additions per term is within
+# gamma*S8 (gamma = D*2^-23/(1 - D*2^-23), S8 = sum_k |x_k||w^_vk| <= ||x||_2 ||w^_v||_2)
+# of z8, plus underflow terms.
+SCREEN_GROUP = 32
+SCREEN_QMAX = 127
+SCREEN_S_MIN = 2.0 ** -100
+SCREEN_TILE_BYTES = 2176
+
+
+def bf16_round_up(v: np.ndarray) -> np.ndarray:
+    """The smallest BF16 value >= v for positive finite float64 v in the normal BF16
+    range, as uint16 bits: the significand rounded up to 8 bits."""
+    v = np.asarray(v, dtype=np.float64)
+    mant, ex = np.frexp(v)                                 # v = mant * 2^ex, 0.5 <= mant < 1
+    r = np.ldexp(np.ceil(np.ldexp(mant, 8)), ex - 8)       # at most 8 significant bits
+    return (r.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
+def screen_encode(w: np.ndarray):
+    """Screen copy v1 of BF16 bits w [N, K]: codes q (int8 [N, K]), scale bits (uint16
+    [N, K/32]) and whether every weight of a row is finite (bool [N]).  The quotient
+    w/s is correctly rounded in float64 and cannot cross or land on a half-integer it
+    does not equal (w and s have 8-bit significands), so rint gives the exact
+    round-to-nearest-even of w/s; likewise for the scale's quotient by 127."""
+    n, k = w.shape
+    check_shape(n, k)
+    wf = bf16_to_f64(w).reshape(n, k // SCREEN_GROUP, SCREEN_GROUP)
+    fin = np.isfinite(wf)
+    wz = np.where(fin, wf, 0.0)
+    amax = np.abs(wz).max(axis=2)
+    s_bits = bf16_round_up(np.maximum(amax / SCREEN_QMAX, SCREEN_S_MIN))
+    s = bf16_to_f64(s_bits)[:, :, None]
+    q = np.rint(wz / s)
+    return q.astype(np.int8).reshape(n, k), s_bits, fin.reshape(n, k).all(axis=1)
+
+
+def screen_weights(q: np.ndarray, s_bits: np.ndarray) -> np.ndarray:
+    """w^ = q * s in float64 (exact: a 7-bit integer times a BF16 value)."""
+    n, k = q.shape
+    s = bf16_to_f64(s_bits).reshape(n, k // SCREEN_GROUP, 1)
+    return (q.astype(np.float64).reshape(n, k // SCREEN_GROUP, SCREEN_GROUP) * s).reshape(n, k)
+
+
+def screen_pack(q: np.ndarray, s_bits: np.ndarray) -> np.ndarray:
+    """Tile bytes of the screen copy (uint8 [(N/16)*(K/128)*2176]), layout above."""
+    n, k = q.shape
+    nb, gk = n // TILE_ROWS, k // TILE_K
+    r, kappa, pos, _, _ = slot_layout()
+    out = np.zeros((gk, nb, SCREEN_TILE_BYTES), dtype=np.uint8)
+    qt = q.view(np.uint8).reshape(nb, TILE_ROWS, gk, TILE_K).transpose(2, 0, 1, 3)   # [g, b, r, kappa]
+    out[:, :, pos.ravel()] = qt[:, :, r.ravel(), kappa.ravel()]
+    st = s_bits.reshape(nb, TILE_ROWS, gk, 4).transpose(2, 0, 1, 3)                 # [g, b, row, j]
+    sb = st.astype("<u2").view(np.uint8).reshape(gk, nb, TILE_ROWS, 4, 2)
+    for row in range(TILE_ROWS):
+        a, i = row // 4, row % 4
+        for j in range(4):
+            off = 2048 + 32 * a + 8 * i + 2 * j
+            out[:, :, off:off + 2] = sb[:, :, row, j, :]
+    return out.reshape(-1)
+
+
+def screen_row_sums_exact(w_row: np.ndarray, q_row: np.ndarray, s_row_bits: np.ndarray):
+    """Exact R2 = sum_k (w_k - w^_k)^2 and Q2 = sum_k w^_k^2 of one row with finite
+    weights, as Python integers in units of 2^-266 (every BF16 value and every w^ is a
+    multiple of 2^-133, and r = w - w^ is exact in float64: it has at most 8 significant
+    bits)."""
+    wf = bf16_to_f64(w_row)
+    what = screen_weights(q_row[None, :], s_row_bits[None, :])[0]
+    r = wf - what
+    r2 = sum(int(v) ** 2 for v in np.ldexp(r, 133))
+    q2 = sum(int(v) ** 2 for v in np.ldexp(what, 133))
+    return r2, q2
+
+
+def screen_gamma(k: int) -> float:
+    """gamma of the screen bound for K columns (D = K + 64 additions per term)."""
+    d = (k + 64) * 2.0 ** -23
+    return d / (1.0 - d)
+
+
+def screen_logits_reference(x: np.ndarray, q: np.ndarray, s_bits: np.ndarray):
+    """z8 = x . w^T and S8 = |x| . |w^|^T in float64 for BF16 bits x [M, K] (each product
+    is exact in float64: 8-bit x 15-bit significands)."""
+    xf = bf16_to_f64(x)
+    what = screen_weights(q, s_bits)
+    return xf @ what.T, np.abs(xf) @ np.abs(what).T

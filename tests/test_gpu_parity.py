@@ -785,7 +785,7 @@ def test_verify_max_k(env):
 
 
 def test_graph_capture_replays_match_eager(env):
-    """Prepared calls captured in a HIP graph (split-K GEMM with its reduce, grouped RMS
+    """Prepared calls captured in a HIP graph (split-K GEMM completed in the kernel, grouped RMS
     GEMM, verification with its accept initialisation): every replay, with new inputs
     copied in eagerly between replays, equals the eager calls bit for bit."""
     torch, w12 = env

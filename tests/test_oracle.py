@@ -440,6 +440,148 @@ def test_accepted_lengths_batched_cases():
     assert list(o.accepted_lengths_batched(am, draft, [0, 10], [10])) == [o.accepted_length(am, draft)] == [1]
 
 
+# ----------------------------------------------------------------------------- screen copy
+def _golden_screen():
+    g = json.load(open(os.path.join(GOLDEN, "screen_copy_worked_example.json")))
+    w = np.zeros((g["n"], g["k"]), dtype=np.uint16)
+    for r, c, b in g["weights"]:
+        w[r, c] = int(b, 16)
+    return g, w
+
+
+def _units(pairs):
+    """sum of coef * 2^exp in units of 2^-266."""
+    return sum(int(c) << (int(e) + 266) for c, e in pairs)
+
+
+def test_screen_worked_example_golden():
+    g, w = _golden_screen()
+    q, s_bits, fin = o.screen_encode(w)
+    for r, j, b in g["scales"]:
+        assert int(s_bits[r, j]) == int(b, 16), (r, j)
+    for r, c, v in g["codes"]:
+        assert int(q[r, c]) == v, (r, c)
+    for r, f in g["rows_finite"].items():
+        assert bool(fin[int(r)]) == f, r
+    tiles = o.screen_pack(q, s_bits)
+    assert tiles.size == o.SCREEN_TILE_BYTES
+    for off, b in g["tile_bytes"]:
+        assert int(tiles[off]) == int(b, 16), off
+    # every other code byte is zero, every other scale 2^-100
+    listed = {off for off, _ in g["tile_bytes"]}
+    assert all(tiles[i] == 0 for i in range(2048) if i not in listed)
+    for r, sums in g["exact_sums_units_2^-266"].items():
+        r2, q2 = o.screen_row_sums_exact(w[int(r)], q[int(r)], s_bits[int(r)])
+        assert r2 == _units(sums["R2"]) and q2 == _units(sums["Q2"]), r
+
+
+def _screen_mats():
+    g = np.random.default_rng(77)
+    yield wi.gaussian_bf16((32, 512), 0.02, g)
+    yield wi.add_exponent_outliers(wi.gaussian_bf16((16, 384), 0.02, g), 0.02, 9)
+    yield wi.random_bits((16, 256), g)                       # every pattern, non-finite included
+    sub = wi.random_bits((16, 256), g) & np.uint16(0x807F)   # zeros and subnormals only
+    yield sub
+    tiny = wi.gaussian_bf16((16, 128), 1.0, g)
+    tiny = (tiny & np.uint16(0x807F)) | np.uint16(20 << 7)    # exponents far below 2^-100 * 127
+    yield tiny
+
+
+def _prev_bf16(bits):
+    return (bits.astype(np.int64) - 1).astype(np.uint16)
+
+
+def test_screen_invariants():
+    for w in _screen_mats():
+        n, k = w.shape
+        q, s_bits, fin = o.screen_encode(w)
+        wf = o.bf16_to_f64(w)
+        finite = np.isfinite(wf)
+        assert np.array_equal(fin, finite.all(axis=1))
+        assert np.all(q[~finite] == 0)
+        s = np.repeat(o.bf16_to_f64(s_bits), 32, axis=1)
+        assert np.all(np.abs(q.astype(np.int64)) <= 127)
+        assert np.all(s >= 2.0 ** -100)
+        wz = np.where(finite, wf, 0.0)
+        amax = np.abs(wz).reshape(n, k // 32, 32).max(axis=2)
+        s_g = o.bf16_to_f64(s_bits)
+        assert np.all(amax <= 127 * s_g)                      # exact: 127 * s has 15 bits
+        above = s_g > 2.0 ** -100
+        prev = o.bf16_to_f64(_prev_bf16(s_bits))
+        assert np.all(127 * prev[above] < amax[above])        # s is the smallest such BF16
+        r = wz - q * s                                        # exact (at most 8 significant bits)
+        assert np.all(np.abs(r) <= s / 2)
+        tie = np.abs(r) == s / 2
+        assert np.all(q[tie] % 2 == 0)
+
+
+def test_screen_codes_sit_at_w12_sign_mantissa_positions():
+    """The screen copy puts each code where W12 v1 puts the sign/mantissa byte of the same
+    element: weights whose sm byte equals the code (one exponent, no escapes) encode to W12
+    tiles whose first 2048 bytes equal the screen tiles' code bytes."""
+    g = np.random.default_rng(5)
+    n, k = 32, 256
+    q = g.integers(-127, 128, size=(n, k)).astype(np.int8)
+    sm = q.view(np.uint8).astype(np.uint32)
+    w = (((sm >> 7) << 15) | (120 << 7) | (sm & 0x7F)).astype(np.uint16)
+    blob = o.encode(w)
+    assert blob.n_esc == 0
+    w12_tiles = blob.tiles.reshape(-1, o.TILE_BYTES)[:, :2048]
+    s_bits = np.full((n, k // 32), 0x3C00, dtype=np.uint16)
+    scr = o.screen_pack(q, s_bits).reshape(-1, o.SCREEN_TILE_BYTES)[:, :2048]
+    assert np.array_equal(w12_tiles, scr)
+
+
+def test_screen_exact_sums_closed_forms():
+    g = np.random.default_rng(9)
+    k = 256
+    for e in (-20, -7, 3):
+        # w = q * 2^e with one |w| = 127 * 2^e per group: s = 2^e, codes = q, r = 0
+        q = g.integers(-127, 128, size=(1, k))
+        q[0, ::32] = 127
+        w = o.bf16_round(np.ldexp(q.astype(np.float64), e))
+        qq, s_bits, _ = o.screen_encode(np.vstack([w] * 16))
+        assert np.all(s_bits == o.bf16_round(np.array([2.0 ** e]))[0])
+        assert np.array_equal(qq[0], q[0].astype(np.int8))
+        r2, q2 = o.screen_row_sums_exact(w[0], qq[0], s_bits[0])
+        assert r2 == 0
+        assert Fraction(q2, 2 ** 266) == sum(bf16_fraction(b) ** 2 for b in w[0])
+    # random rows: R2 <= K (s_max / 2)^2
+    w = wi.gaussian_bf16((16, k), 0.02, g)
+    qq, s_bits, _ = o.screen_encode(w)
+    for r in range(16):
+        r2, _ = o.screen_row_sums_exact(w[r], qq[r], s_bits[r])
+        smax = Fraction(float(o.bf16_to_f64(s_bits[r]).max()))
+        assert Fraction(r2, 2 ** 266) <= k * (smax / 2) ** 2
+
+
+def test_screen_bound_holds_and_is_tight():
+    """|z - z8| <= ||x||_2 ||r||_2 for any x, with near equality when x is parallel to r
+    (so a bound missing a factor would fail), and the float64 z8 reference is within
+    K 2^-53 S8 of the exact screen logit."""
+    g = np.random.default_rng(21)
+    k = 512
+    w = wi.gaussian_bf16((16, k), 0.02, g)
+    q, s_bits, _ = o.screen_encode(w)
+    what = o.screen_weights(q, s_bits)
+    for r in range(4):
+        rr = o.bf16_to_f64(w[r]) - what[r]
+        xs = [wi.gaussian_bf16((1, k), 1.0, g)[0],
+              o.bf16_round(rr / np.abs(rr).max())]            # parallel to r
+        for t, x in enumerate(xs):
+            xf = [bf16_fraction(b) for b in x]
+            d = sum(a * Fraction(float(v)) for a, v in zip(xf, rr))      # z - z8, exact
+            x2 = sum(a * a for a in xf)
+            r2, _ = o.screen_row_sums_exact(w[r], q[r], s_bits[r])
+            bound2 = x2 * Fraction(r2, 2 ** 266)
+            assert d * d <= bound2
+            if t == 1:
+                assert d * d >= Fraction(98, 100) * bound2
+            z8, s8 = o.screen_logits_reference(x[None, :], q[r:r + 1], s_bits[r:r + 1])
+            z8x = sum(a * Fraction(float(v)) for a, v in zip(xf, what[r]))
+            assert abs(Fraction(float(z8[0, 0])) - z8x) <= Fraction(k * 2.0 ** -53 * float(s8[0, 0]))
+
+
 # ----------------------------------------------------------------------------- mutations
 def _pins_fail(fn):
     try:
@@ -548,3 +690,32 @@ def test_mutation_rounded_rule_one_ulp_wider_is_caught(monkeypatch):
 def test_mutation_zero_width_fp64_filter_is_caught(monkeypatch):
     monkeypatch.setattr(o, "fp64_filter_width", lambda k, s_max: 0.0)
     assert _pins_fail(test_argmax_sub_fp64_near_tie)
+
+
+def test_mutation_screen_scale_rounded_to_nearest_is_caught(monkeypatch):
+    monkeypatch.setattr(o, "bf16_round_up", lambda v: o.bf16_round(v))
+    assert _pins_fail(test_screen_invariants)
+
+
+def test_mutation_screen_ties_away_from_zero_is_caught(monkeypatch):
+    monkeypatch.setattr(o.np, "rint", lambda v: np.sign(v) * np.floor(np.abs(v) + 0.5))
+    assert _pins_fail(test_screen_worked_example_golden)
+
+
+def test_mutation_screen_groups_strided_is_caught(monkeypatch):
+    orig = o.screen_encode
+
+    def bad(w):
+        n, k = w.shape
+        perm = np.arange(k).reshape(k // 32, 32).T.reshape(-1)   # groups of every (k/32)-th column
+        q, s, f = orig(w[:, perm])
+        inv = np.argsort(perm)
+        return q[:, inv], s, f
+    monkeypatch.setattr(o, "screen_encode", bad)
+    assert _pins_fail(test_screen_worked_example_golden)
+
+
+def test_mutation_screen_residual_halved_is_caught(monkeypatch):
+    orig = o.screen_row_sums_exact
+    monkeypatch.setattr(o, "screen_row_sums_exact", lambda w, q, s: (orig(w, q, s)[0] // 4, orig(w, q, s)[1]))
+    assert _pins_fail(test_screen_bound_holds_and_is_tight)
