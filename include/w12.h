@@ -100,6 +100,7 @@ typedef struct w12_desc {
 #define W12_OP_GEMM_BF16 3
 #define W12_OP_VERIFY    4
 #define W12_OP_GEMM_GROUP 5   /* n = the group's rows added up */
+#define W12_OP_VERIFY2   6   /* two-level verification (w12_lmhead_verify2) */
 
 /* Bytes of the tile array: (n/16)*(k/128)*3072; 0 if the shape is invalid. */
 size_t w12_tiles_bytes(uint64_t n, uint64_t k);
@@ -276,6 +277,78 @@ w12_status w12_lmhead_verify_batched(const uint16_t* x, uint32_t m, const w12_de
  * overwritten).  Errors as w12_lmhead_verify. */
 w12_status w12_logits_f32(const uint16_t* x, uint32_t m, const w12_desc* d, float* logits_out,
                           float* sabs_out, void* ws, size_t ws_bytes, void* stream);
+
+/* ---- Two-level verification ("SpecPilot: an agent doubled speculative decoding speed,
+ * and the 10.87x needs context", "The mechanisms it found": verification in two levels
+ * with an 8-bit copy of the head; "SpecPilot" glossary, "Differentiation").  A screen
+ * copy of the LM head (8-bit codes) is streamed first; a certified bound rules out every
+ * logit that cannot be the argmax, and only the others are computed from the W12 head
+ * (FP64, then exact sums where FP64 cannot separate them).
+ *
+ * Screen copy v1 (one device buffer of w12_screen_bytes(n, k) bytes):
+ *  - per row v and group g of 32 consecutive columns, a scale s_vg = the smallest BF16
+ *    value >= (largest |w| over the group's finite weights) / 127, and at least 2^-100;
+ *    codes q = w / s_vg rounded to the nearest integer, ties to even (int8, |q| <= 127; 0
+ *    for a non-finite w);
+ *  - tiles of 16 rows x 128 columns, 2176 bytes, tile (b, g) at (g*(n/16) + b)*2176: the
+ *    code of element t of lane slot l (the W12 slot layout above) at 1024*(t/16) + 16l +
+ *    t%16, then the tile's 64 scales (BF16, little-endian), row 4a+i (a, i = 0..3) and
+ *    32-column group j of the tile at 2048 + 32a + 8i + 2j;
+ *  - from the next 256-byte boundary, FP32 C[n]: C_v >= ||w_v - q_v s_v||_2 +
+ *    gamma ||q_v s_v||_2 (gamma = D 2^-23 / (1 - D 2^-23), D = k + 64), +Inf for a row with
+ *    a non-finite weight; from the next 256-byte boundary, FP32 A[n] >= (k/32)(max_g s_vg
+ *    2^-113 + 2^-125), the allowance for flushed denormals.
+ * For any x row and any FP32 evaluation of the screen logit z8^_v = sum_k x_k q_vk s_vg(k)
+ * with at most D additions per term, |z8^_v - z_v| <= ||x||_2 C_v + A_v (z_v the exact
+ * logit): Cauchy-Schwarz on the code residuals, plus the rounding of the sum. */
+size_t w12_screen_bytes(uint64_t n, uint64_t k);
+
+/* Builds the screen copy of BF16 weights w [n][k] (device, row-major, 16-byte aligned;
+ * shape as W12: n % 16 == 0, k % 128 == 0, 0 < k < 2^20) into `screen` (device, 256-byte
+ * aligned, screen_bytes >= w12_screen_bytes(n, k), else W12_ERR_WORKSPACE).  Codes and
+ * scales are identical to the CPU oracle's; C and A are computed in FP64 with rounding
+ * margins and rounded up (certified upper bounds, not unique values). */
+w12_status w12_screen_encode(const uint16_t* w, uint64_t n, uint64_t k, void* screen,
+                             size_t screen_bytes, void* stream);
+
+/* Greedy verification in two levels: the same results as w12_lmhead_verify (the exact
+ * argmax per row, lowest index on exact ties; the accepted length), from the W12 head d and
+ * `screen`, its screen copy (w12_screen_encode of the same weights: the results are exact
+ * only if it is).  Pass 1 streams the screen copy (0.71 of the W12 tile bytes) and keeps,
+ * per x row and 16-row block, the certified intervals' largest and second largest upper
+ * ends z8^ + ||x|| C + A (||x|| bounded from above from the staged x) and, per group of 8
+ * blocks, the largest upper and lower ends; pass 2 (32 workgroups per x row) drops every
+ * logit whose upper end is below the row's largest lower end, recomputes the others in
+ * FP64 from the W12 tiles (one wave each), and the workgroup that finishes a row last keeps
+ * those whose FP64 intervals reach the largest FP64 lower bound, summing them exactly when
+ * more than one is left and any is inexact.  A row of x that is all +-0 gets 0; a row with
+ * a non-finite x or candidate logit gets -1.  x, m, d, draft, n_draft, argmax_out and
+ * accepted_out as for w12_lmhead_verify; screen 256-byte aligned.
+ * ws: w12_workspace_bytes(W12_OP_VERIFY2, m, n, k) bytes, 256-byte aligned; it begins with
+ * 4096 bytes of per-row tickets that must be zero before its first use
+ * (w12_workspace_init) and that every call leaves zero; calls sharing a workspace must be
+ * ordered on one stream.  Errors as w12_lmhead_verify. */
+w12_status w12_lmhead_verify2(const uint16_t* x, uint32_t m, const w12_desc* d,
+                              const void* screen, const int32_t* draft, uint32_t n_draft,
+                              int32_t* argmax_out, int32_t* accepted_out, void* ws,
+                              size_t ws_bytes, void* stream);
+
+/* Several requests in one two-level pass: requests and results as
+ * w12_lmhead_verify_batched, verification as w12_lmhead_verify2. */
+w12_status w12_lmhead_verify2_batched(const uint16_t* x, uint32_t m, const w12_desc* d,
+                                      const void* screen, const int32_t* req_off,
+                                      const int32_t* req_ndraft, uint32_t n_req,
+                                      const int32_t* draft, int32_t* argmax_out,
+                                      int32_t* accepted_out, void* ws, size_t ws_bytes,
+                                      void* stream);
+
+/* Pass 1 of w12_lmhead_verify2 with its full output (for tests of the screen bound):
+ * logits_out = the FP32 screen logits z8^ [m][n] and bound_out = their FP32 bounds
+ * ||x|| C_v + A_v rounded up [m][n] (device, 16-byte aligned).  d supplies the shape only
+ * (its buffers are not read).  ws as for W12_OP_VERIFY2 (its records are overwritten). */
+w12_status w12_screen_logits_f32(const uint16_t* x, uint32_t m, const w12_desc* d,
+                                 const void* screen, float* logits_out, float* bound_out,
+                                 void* ws, size_t ws_bytes, void* stream);
 
 /* Harness op for the layer chain: y[row] = bf16(x[row] / sqrt(mean(x[row]^2))) in FP32,
  * x, y device BF16 [m][k] (16-byte aligned, k % 8 == 0, 0 < k < 2^20, m <= 2^20;

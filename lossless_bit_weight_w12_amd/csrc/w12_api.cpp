@@ -466,6 +466,138 @@ w12_status verify_impl(const uint16_t* x, uint32_t m, const w12_desc* d, const i
   return hip_status(e);
 }
 
+// Screen copy of a head: tiles, then C [n], then A [n] (each from a 256-byte boundary).
+struct ScreenLayout {
+  size_t coef, abse, total;
+};
+
+ScreenLayout screen_layout(uint64_t n, uint64_t k) {
+  ScreenLayout L;
+  L.coef = align256((size_t)(n / 16) * (k / 128) * kScreenTileBytes);
+  L.abse = L.coef + align256((size_t)n * 4);
+  L.total = L.abse + align256((size_t)n * 4);
+  return L;
+}
+
+// Two-level verification workspace: the row tickets (a fixed 4 KB region at the start,
+// zero before the first use, left zero by every call), diagnostic counts, the first
+// pass's block and group records, each slice's candidates with their FP64 values, and
+// each row's survivors.  A slice holds at most 16 rows of each block of its groups.
+struct Verify2Layout {
+  size_t ncand, hi1, hi2, idx, gh, gl, sc_cnt, sc_lo, sc_v, sc_z, sc_b, surv, total;
+  uint32_t ngrp, cap;
+};
+
+Verify2Layout verify2_layout(uint32_t m, uint64_t n) {
+  Verify2Layout L;
+  const uint64_t nb = n / 16;
+  L.ngrp = (uint32_t)((nb + kScreenNW - 1) / kScreenNW);
+  L.cap = 16u * kScreenNW * ((L.ngrp + kScreenSlices - 1) / kScreenSlices);
+  const size_t rec = align256((size_t)m * nb * 4), grec = align256((size_t)m * L.ngrp * 4);
+  const size_t sl = (size_t)m * kScreenSlices, ent = sl * L.cap;
+  L.ncand = kTicketBytes;
+  L.hi1 = L.ncand + align256((size_t)m * 8);
+  L.hi2 = L.hi1 + rec;
+  L.idx = L.hi2 + rec;
+  L.gh = L.idx + rec;
+  L.gl = L.gh + grec;
+  L.sc_cnt = L.gl + grec;
+  L.sc_lo = L.sc_cnt + align256(sl * 4);
+  L.sc_v = L.sc_lo + align256(sl * 8);
+  L.sc_z = L.sc_v + align256(ent * 4);
+  L.sc_b = L.sc_z + align256(ent * 8);
+  L.surv = L.sc_b + align256(ent * 8);
+  L.total = L.surv + align256((size_t)m * n * 4);
+  return L;
+}
+
+// Two-level verification (pass 1 only when full_z is set: the screen logits and bounds).
+w12_status verify2_impl(const uint16_t* x, uint32_t m, const w12_desc* d, const void* screen,
+                        const int32_t* draft, uint32_t n_draft, const int32_t* req_off,
+                        const int32_t* req_ndraft, uint32_t n_req, int32_t* argmax_out,
+                        int32_t* accepted_out, void* ws, size_t ws_bytes, void* stream,
+                        float* full_z, float* full_b) {
+  if (!x || !screen || !ws) return W12_ERR_NULL;
+  if (!full_z && (!argmax_out || !accepted_out)) return W12_ERR_NULL;
+  w12_status st = check_desc(d, !full_z);
+  if (st != W12_OK) return st;
+  if (m < 1 || m > W12_MAX_M) return W12_ERR_RANGE;
+  if (!mn_ok(m, d->n)) return W12_ERR_SHAPE;
+  const Verify2Layout L = verify2_layout(m, d->n);
+  if (ws_bytes < L.total) return W12_ERR_WORKSPACE;
+  if (!aligned(x, 16) || !aligned(ws, 256) || !aligned(screen, 256)) return W12_ERR_ALIGN;
+  if (full_z && (!aligned(full_z, 16) || !aligned(full_b, 16))) return W12_ERR_ALIGN;
+  if (!full_z && (!aligned(argmax_out, 4) || !aligned(accepted_out, 4))) return W12_ERR_ALIGN;
+  hipStream_t s = (hipStream_t)stream;
+  uint8_t* base = (uint8_t*)ws;
+  const ScreenLayout SL = screen_layout(d->n, d->k);
+  ScreenArgs a;
+  memset(&a, 0, sizeof(a));
+  a.x = x;
+  a.tiles = (const uint8_t*)screen;
+  a.coef = (const float*)((const uint8_t*)screen + SL.coef);
+  a.abse = (const float*)((const uint8_t*)screen + SL.abse);
+  a.hi1 = (float*)(base + L.hi1);
+  a.hi2 = (float*)(base + L.hi2);
+  a.idx = (int32_t*)(base + L.idx);
+  a.gh = (float*)(base + L.gh);
+  a.gl = (float*)(base + L.gl);
+  a.full_z = full_z;
+  a.full_b = full_b;
+  if (!full_z) {
+    a.acc.accepted = accepted_out;   // pass 1 sets the draft lengths, pass 2 lowers them
+    a.acc.n_draft = n_draft;
+    a.acc.req_off = req_off;
+    a.acc.req_ndraft = req_ndraft;
+    a.acc.n_req = n_req;
+  }
+  a.m = m;
+  a.n = (uint32_t)d->n;
+  a.k = (uint32_t)d->k;
+  a.nb = (uint32_t)(d->n / 16);
+  a.g_cols = (uint32_t)(d->k / 128);
+  a.ngrp = L.ngrp;
+  hipError_t e = launch_screen_pass1(a, s);
+  if (full_z || e != hipSuccess) return hip_status(e);
+  SelectArgs v;
+  memset(&v, 0, sizeof(v));
+  v.x = x;
+  v.tiles = (const uint8_t*)d->tiles;
+  v.esc_off = d->esc_off;
+  v.esc = d->esc;
+  v.hi1 = a.hi1;
+  v.hi2 = a.hi2;
+  v.idx = a.idx;
+  v.gh = a.gh;
+  v.gl = a.gl;
+  v.tickets = (uint32_t*)base;
+  v.sc_cnt = (int32_t*)(base + L.sc_cnt);
+  v.sc_lo = (double*)(base + L.sc_lo);
+  v.sc_v = (int32_t*)(base + L.sc_v);
+  v.sc_z = (double*)(base + L.sc_z);
+  v.sc_b = (double*)(base + L.sc_b);
+  v.surv = (int32_t*)(base + L.surv);
+  v.cap = L.cap;
+  v.argmax = argmax_out;
+  v.ncand = (int32_t*)(base + L.ncand);
+  v.draft = draft;
+  v.accepted = accepted_out;
+  v.req_off = req_off;
+  v.req_ndraft = req_ndraft;
+  v.n_req = n_req;
+  v.m = m;
+  v.n = a.n;
+  v.k = a.k;
+  v.g_cols = a.g_cols;
+  v.nb = a.nb;
+  v.ngrp = L.ngrp;
+  v.bpg = kScreenNW;
+  v.n_draft = n_draft;
+  const Seg sg = w12_seg(d, nullptr, 0);
+  for (int i = 0; i < 4; ++i) v.lut[i] = sg.lut[i];
+  return hip_status(launch_screen_pass2(v, s));
+}
+
 }  // namespace
 
 extern "C" {
@@ -490,6 +622,9 @@ size_t w12_workspace_bytes(int op, uint32_t m, uint64_t n, uint64_t k) {
     case W12_OP_GEMM_GROUP:
       if (m < 1 || m > W12_MAX_M || !mn_ok(m, n)) return 0;
       return group_ws_bytes(m, n, k);
+    case W12_OP_VERIFY2:
+      if (m < 1 || m > W12_MAX_M || !mn_ok(m, n)) return 0;
+      return verify2_layout(m, n).total;
     default: return 0;
   }
 }
@@ -685,6 +820,55 @@ w12_status w12_logits_f32(const uint16_t* x, uint32_t m, const w12_desc* d, floa
   a.bm = block_max(base, L, p);
   const int src = codebook_is_run(d->codebook) ? SRC_RUN : SRC_LUT;
   return hip_status(launch_gemm(a, src, EPI_LOGITS, p, (hipStream_t)stream));
+}
+
+size_t w12_screen_bytes(uint64_t n, uint64_t k) {
+  if (!shape_ok(n, k)) return 0;
+  return screen_layout(n, k).total;
+}
+
+w12_status w12_screen_encode(const uint16_t* w, uint64_t n, uint64_t k, void* screen,
+                             size_t screen_bytes, void* stream) {
+  if (!w || !screen) return W12_ERR_NULL;
+  if (!shape_ok(n, k)) return W12_ERR_SHAPE;
+  const ScreenLayout L = screen_layout(n, k);
+  if (screen_bytes < L.total) return W12_ERR_WORKSPACE;
+  if (!aligned(w, 16) || !aligned(screen, 256)) return W12_ERR_ALIGN;
+  uint8_t* base = (uint8_t*)screen;
+  return hip_status(launch_screen_encode(w, (uint32_t)(n / 16), (uint32_t)(k / 128), base,
+                                         (float*)(base + L.coef), (float*)(base + L.abse),
+                                         (hipStream_t)stream));
+}
+
+w12_status w12_lmhead_verify2(const uint16_t* x, uint32_t m, const w12_desc* d,
+                              const void* screen, const int32_t* draft, uint32_t n_draft,
+                              int32_t* argmax_out, int32_t* accepted_out, void* ws,
+                              size_t ws_bytes, void* stream) {
+  if (n_draft > 0 && !draft) return W12_ERR_NULL;
+  if (m >= 1 && n_draft > m) return W12_ERR_RANGE;
+  return verify2_impl(x, m, d, screen, draft, n_draft, nullptr, nullptr, 1, argmax_out,
+                      accepted_out, ws, ws_bytes, stream, nullptr, nullptr);
+}
+
+w12_status w12_lmhead_verify2_batched(const uint16_t* x, uint32_t m, const w12_desc* d,
+                                      const void* screen, const int32_t* req_off,
+                                      const int32_t* req_ndraft, uint32_t n_req,
+                                      const int32_t* draft, int32_t* argmax_out,
+                                      int32_t* accepted_out, void* ws, size_t ws_bytes,
+                                      void* stream) {
+  if (!req_off || !req_ndraft || !draft) return W12_ERR_NULL;
+  if (n_req < 1 || n_req > m) return W12_ERR_RANGE;
+  if (!aligned(req_off, 4) || !aligned(req_ndraft, 4) || !aligned(draft, 4)) return W12_ERR_ALIGN;
+  return verify2_impl(x, m, d, screen, draft, 0, req_off, req_ndraft, n_req, argmax_out,
+                      accepted_out, ws, ws_bytes, stream, nullptr, nullptr);
+}
+
+w12_status w12_screen_logits_f32(const uint16_t* x, uint32_t m, const w12_desc* d,
+                                 const void* screen, float* logits_out, float* bound_out,
+                                 void* ws, size_t ws_bytes, void* stream) {
+  if (!logits_out || !bound_out) return W12_ERR_NULL;
+  return verify2_impl(x, m, d, screen, nullptr, 0, nullptr, nullptr, 0, nullptr, nullptr, ws,
+                      ws_bytes, stream, logits_out, bound_out);
 }
 
 w12_status w12_rms_rescale(const uint16_t* x, uint32_t m, uint64_t k, uint16_t* y, void* stream) {

@@ -222,6 +222,62 @@ struct VerifyArgs {
 };
 hipError_t launch_verify_pass2(const VerifyArgs& a, hipStream_t s);
 
+// Two-level verification (w12_screen.hip): the screen copy of the head (8-bit codes, a
+// BF16 scale per 32 columns) and its two passes.
+constexpr uint32_t kScreenTileBytes = 2176;   // 2048 code bytes + 64 BF16 scales
+constexpr uint32_t kScreenSlices = 32;        // workgroups per x row in the second pass
+constexpr uint32_t kScreenNW = 8;             // row-blocks (waves) per first-pass workgroup
+
+struct ScreenArgs {         // first pass: the screen GEMM with the interval epilogue
+  const uint16_t* x;        // [m][k]
+  const uint8_t* tiles;     // screen tiles
+  const float* coef;        // C [n]
+  const float* abse;        // A [n]
+  float* hi1;               // [m][nb] largest upper end of the row-block's intervals
+  float* hi2;               // [m][nb] second largest
+  int32_t* idx;             // [m][nb] row of hi1 (lowest on ties)
+  float* gh;                // [m][ngrp] largest hi1 of the group (workgroup)
+  float* gl;                // [m][ngrp] largest lower end of the group's intervals
+  float* full_z;            // [m][n] screen logits (NULL: not written)
+  float* full_b;            // [m][n] their bounds
+  BlockMax acc;             // accept fields only (accepted, n_draft, req_*)
+  uint32_t m, n, k, nb, g_cols, ngrp;
+};
+
+struct SelectArgs {         // second pass: candidates, FP64 from W12, exact, accept
+  const uint16_t* x;
+  const uint8_t* tiles;     // the W12 head
+  const uint32_t* esc_off;
+  const uint32_t* esc;
+  const float* hi1;
+  const float* hi2;
+  const int32_t* idx;
+  const float* gh;
+  const float* gl;
+  uint32_t* tickets;        // [m]: zero before the launch, zero after it
+  int32_t* sc_cnt;          // [m][slices] survivors kept by each slice
+  double* sc_lo;            // [m][slices] largest FP64 lower bound of each slice
+  int32_t* sc_v;            // [m][slices][cap]
+  double* sc_z;             // [m][slices][cap]
+  double* sc_b;             // [m][slices][cap]
+  int32_t* surv;            // [m][n] survivors of the row (the last workgroup)
+  uint32_t cap;
+  int32_t* argmax;          // [m]
+  int32_t* ncand;           // [m][2]: candidates after the screen, after FP64 (may be NULL)
+  const int32_t* draft;
+  int32_t* accepted;
+  const int32_t* req_off;
+  const int32_t* req_ndraft;
+  uint32_t n_req;
+  uint32_t m, n, k, g_cols, nb, ngrp, bpg, n_draft;
+  uint32_t lut[4];
+};
+
+hipError_t launch_screen_encode(const uint16_t* w, uint32_t nb, uint32_t g_cols, uint8_t* tiles,
+                                float* coef, float* abse, hipStream_t s);
+hipError_t launch_screen_pass1(const ScreenArgs& a, hipStream_t s);
+hipError_t launch_screen_pass2(const SelectArgs& a, hipStream_t s);
+
 hipError_t launch_rms_rescale(const uint16_t* x, uint32_t m, uint32_t k, uint16_t* y,
                               hipStream_t s);
 hipError_t launch_stream_read(const void* buf, uint32_t bytes, uint32_t workgroups, uint32_t* sink,

@@ -48,72 +48,15 @@
 // n_draft and every row i < n_draft whose argmax differs from the draft lowers it to i
 // with an atomic minimum.  Batched, each request applies the same rule to its own rows
 // (its i counted from its first row), with its own accepted length.
-#include "w12_internal.h"
+#include "w12_exact.h"
 
 namespace w12 {
 
-constexpr int kLimbs = 18;             // 18 x 32 bits > 542 bits (largest |sum| for K < 2^20)
 constexpr uint32_t kT = 512;           // threads of the pass-2 workgroup (one workgroup per row)
 constexpr uint32_t kWaves = kT / 64u;
+static_assert(kWaves == kExactWaves, "the exact stage runs one wave per candidate");
 constexpr uint32_t kScreenMax = 512;   // candidates screened per chunk (ids and results in LDS)
 constexpr uint32_t kUCache = 8192;     // group upper bounds kept in LDS for the group scan
-
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ bool exact_parts(uint32_t bits, int& sgn, uint32_t& mant, int& ex) {
-  const uint32_t e = (bits >> 7) & 0xFFu, m = bits & 0x7Fu;
-  sgn = (bits >> 15) ? -1 : 1;
-  mant = e ? (m | 0x80u) : m;
-  ex = e ? (int)e - 134 : -133;
-  return e != 0xFFu;
-}
-
-// Weight (v, kk) of a head of nb row-blocks (tile (b, g) at (g * nb + b) * 3072).
-__device__ __forceinline__ uint32_t decode_w(const uint8_t* tiles, uint32_t nb, uint32_t v,
-                                             uint32_t kk, const uint32_t lut[4]) {
-  const uint32_t b = v >> 4, r = v & 15u, g = kk >> 7, kap = kk & 127u;
-  const uint32_t q = (kap >> 3) & 3u, j = kap >> 5, i = kap & 7u;
-  const uint32_t l = 16u * q + r, t = 8u * j + i;
-  const uint8_t* tb = tiles + ((uint64_t)g * nb + b) * 3072u;
-  const uint32_t sm = tb[1024u * (t >> 4) + 16u * l + (t & 15u)];
-  const uint32_t cw = *reinterpret_cast<const uint32_t*>(tb + 2048u + 16u * l + 4u * j);
-  const uint32_t code = (cw >> (4u * (i >> 1) + 16u * (i & 1u))) & 0xFu;
-  const uint32_t e = (lut[code >> 2] >> (8u * (code & 3u))) & 0xFFu;
-  return ((sm & 0x80u) << 8) | (e << 7) | (sm & 0x7Fu);
-}
-
-// The BF16 weight of element t (0..31) of lane slot l from the slot's sign/mantissa
-// words (s_lo: t < 16, s_hi: t >= 16) and its four code words.
-__device__ __forceinline__ uint32_t slot_weight(const u32x4& s_lo, const u32x4& s_hi,
-                                                const u32x4& cw, uint32_t t,
-                                                const uint32_t lut[4]) {
-  const uint32_t jj = t >> 3, i = t & 7u;
-  const uint32_t sword = t < 16u ? s_lo[(t & 15u) >> 2] : s_hi[(t & 15u) >> 2];
-  const uint32_t sm = (sword >> (8u * (t & 3u))) & 0xFFu;
-  const uint32_t code = (cw[jj] >> (4u * (i >> 1) + 16u * (i & 1u))) & 0xFu;
-  const uint32_t e = (lut[code >> 2] >> (8u * (code & 3u))) & 0xFFu;
-  return ((sm & 0x80u) << 8) | (e << 7) | (sm & 0x7Fu);
-}
-
-// Add sign * x * w (BF16 bits) to a lane's column of limbs (units of 2^-266); false if
-// either value is not finite.
-__device__ __forceinline__ bool limb_term(unsigned long long* col, uint32_t xb, uint32_t wb,
-                                          bool subtract) {
-  int sx, sw, ex, ew;
-  uint32_t mx, mw;
-  const bool okx = exact_parts(xb, sx, mx, ex), okw = exact_parts(wb, sw, mw, ew);
-  const uint32_t prod = mx * mw;   // < 2^16
-  if (prod != 0u) {
-    const int sh = ex + ew + 266;   // 0 .. 506
-    const unsigned long long v = (unsigned long long)prod << (sh & 31);
-    long long lo = (long long)(v & 0xFFFFFFFFull), hi = (long long)(v >> 32);
-    if (((sx * sw) < 0) != subtract) { lo = -lo; hi = -hi; }
-    const int idx = sh >> 5;
-    col[idx * 64] += (unsigned long long)lo;
-    col[(idx + 1) * 64] += (unsigned long long)hi;
-  }
-  return okx && okw;
-}
 
 __global__ __launch_bounds__(kT) void k_verify_pass2(VerifyArgs a) {
   __shared__ float s_u[kUCache];
@@ -126,11 +69,7 @@ __global__ __launch_bounds__(kT) void k_verify_pass2(VerifyArgs a) {
   __shared__ float s_wv[kWaves], s_ws[kWaves];
   __shared__ int32_t s_wi[kWaves];
   __shared__ uint32_t s_u0[kWaves];
-  __shared__ unsigned long long s_limb[kWaves][kLimbs * 64];   // one limb column per lane
-  __shared__ uint32_t s_dig[kWaves][kLimbs];
-  __shared__ int32_t s_sgn[kWaves], s_vid[kWaves];
-  __shared__ uint32_t best[kLimbs];
-  __shared__ int32_t s_best_v, s_best_sign;
+  __shared__ ExactShared s_ex;
   __shared__ uint32_t s_cnt, s_bad, s_nsurv, s_allexact;
   __shared__ double s_lo64;
   __shared__ int32_t s_result;
@@ -151,7 +90,7 @@ __global__ __launch_bounds__(kT) void k_verify_pass2(VerifyArgs a) {
   };
   auto get = [&](uint32_t c) { return c < kScreenMax ? s_cand[c] : cand[c]; };
   uint32_t ncand = 0, nsurv = 0;
-  if (tid == 0) { s_cnt = 0; s_bad = 0; s_best_v = -1; s_result = -1; }
+  if (tid == 0) { s_cnt = 0; s_bad = 0; s_result = -1; }
 
   // 1. z*, its index and S* over the group records (NaN marks a group with a non-finite
   // logit); the upper bounds U stay in LDS for the scan.  Every scan issues all of a
@@ -404,90 +343,14 @@ __global__ __launch_bounds__(kT) void k_verify_pass2(VerifyArgs a) {
     if (!need_exact) {
       if (tid == 0) s_result = nsurv == 1u ? get(0) : lowest;
     } else {
-      // 4. exact recompute of the survivors, one wave each (kWaves at a time); lane l
-      // adds its products into limb column l (no two lanes share a word), then 18 lanes
-      // sum the columns and lane 0 carries them into 32-bit digits and a sign
-      for (uint32_t c0i = 0; c0i < nsurv; c0i += kWaves) {
-        const uint32_t c = c0i + wave;
-        unsigned long long* col = &s_limb[wave][lane];
-#pragma unroll
-        for (int i = 0; i < kLimbs; ++i) col[i * 64] = 0ull;
-        bool ok = true;
-        if (c < nsurv) {
-          const uint32_t v = (uint32_t)get(c), b = v >> 4, r = v & 15u;
-          for (uint32_t j = lane; j < 4u * a.g_cols; j += 64u) {
-            const uint32_t g = j >> 2, q = j & 3u, l = 16u * q + r;
-            const uint8_t* tb = a.tiles + ((uint64_t)g * a.nb + b) * 3072u + 16u * l;
-            const u32x4 s_lo = *reinterpret_cast<const u32x4*>(tb);
-            const u32x4 s_hi = *reinterpret_cast<const u32x4*>(tb + 1024);
-            const u32x4 cw = *reinterpret_cast<const u32x4*>(tb + 2048);
-#pragma unroll
-            for (uint32_t jj = 0; jj < 4; ++jj) {
-              const u32x4 xv = *reinterpret_cast<const u32x4*>(xr + 128u * g + 32u * jj + 8u * q);
-#pragma unroll
-              for (uint32_t i = 0; i < 8; ++i) {
-                const uint32_t wb = slot_weight(s_lo, s_hi, cw, 8u * jj + i, a.lut);
-                const uint32_t xb = (xv[i >> 1] >> (16u * (i & 1u))) & 0xFFFFu;
-                ok = limb_term(col, xb, wb, false) && ok;
-              }
-            }
-          }
-          // escapes of this row: replace the product decoded with the stored code
-          const uint32_t e0 = c < kScreenMax ? s_ce0[c] : a.esc_off[b];
-          const uint32_t e1 = c < kScreenMax ? s_ce1[c] : a.esc_off[b + 1];
-          for (uint32_t i = e0 + lane; i < e1; i += 64u) {
-            const uint32_t rec = a.esc[i];
-            const uint32_t kk = (rec >> 8) & 0xFFFFFu;
-            if ((rec >> 28) != r || kk >= a.k) continue;
-            const uint32_t wb = decode_w(a.tiles, a.nb, v, kk, a.lut);
-            const uint32_t wt = (wb & 0x807Fu) | ((rec & 0xFFu) << 7);
-            limb_term(col, xr[kk], wb, true);
-            ok = limb_term(col, xr[kk], wt, false) && ok;
-          }
-          if (!ok) atomicOr(&s_bad, 1u);
-        }
-        __syncthreads();   // every lane's column is written
-        if (c < nsurv && lane < (uint32_t)kLimbs) {
-          long long t = 0;
-          for (uint32_t l = 0; l < 64u; ++l) t += (long long)s_limb[wave][lane * 64u + l];
-          s_limb[wave][lane * 64u] = (unsigned long long)t;   // column 0 of limb `lane`: the row sum
-        }
-        __syncthreads();   // the column sums are written
-        if (c < nsurv && lane == 0) {
-          // normalise to 32-bit digits; the final carry is the sign (0 or -1)
-          long long carry = 0;
-          for (int i = 0; i < kLimbs; ++i) {
-            const long long t = (long long)s_limb[wave][i * 64] + carry;
-            s_dig[wave][i] = (uint32_t)(t & 0xFFFFFFFFll);
-            carry = t >> 32;
-          }
-          s_sgn[wave] = (int32_t)carry;
-          s_vid[wave] = (int32_t)get(c);
-        }
-        __syncthreads();
-        if (tid == 0) {   // this round's survivors against the best so far
-          for (uint32_t w = 0; w < kWaves && c0i + w < nsurv; ++w) {
-            bool better;
-            if (s_best_v < 0) {
-              better = true;
-            } else if (s_sgn[w] != s_best_sign) {
-              better = s_sgn[w] > s_best_sign;
-            } else {
-              int cmp = 0;
-              for (int i = kLimbs - 1; i >= 0 && cmp == 0; --i)
-                cmp = s_dig[w][i] > best[i] ? 1 : (s_dig[w][i] < best[i] ? -1 : 0);
-              better = cmp > 0 || (cmp == 0 && s_vid[w] < s_best_v);
-            }
-            if (better) {
-              for (int i = 0; i < kLimbs; ++i) best[i] = s_dig[w][i];
-              s_best_sign = s_sgn[w];
-              s_best_v = s_vid[w];
-            }
-          }
-        }
-        __syncthreads();
-      }
-      if (tid == 0) s_result = s_bad ? -1 : s_best_v;
+      // 4. exact recompute of the survivors (w12_exact.h), one wave each
+      const ExactRow er{xr, a.tiles, a.esc, a.nb, a.g_cols, a.k, a.lut};
+      const int32_t rbest = exact_best(s_ex, er, nsurv, get, [&](uint32_t c, uint32_t& e0, uint32_t& e1) {
+        const uint32_t b = (uint32_t)get(c) >> 4;
+        e0 = c < kScreenMax ? s_ce0[c] : a.esc_off[b];
+        e1 = c < kScreenMax ? s_ce1[c] : a.esc_off[b + 1];
+      });
+      if (tid == 0) s_result = rbest;
     }
   } else if (tid == 0) {
     s_result = zero_row ? 0 : -1;

@@ -14,7 +14,7 @@ from dataclasses import dataclass
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libw12.so")
 _LIB = None
 
-OP_ENCODE, OP_DECODE, OP_GEMM, OP_GEMM_BF16, OP_VERIFY, OP_GEMM_GROUP = 0, 1, 2, 3, 4, 5
+OP_ENCODE, OP_DECODE, OP_GEMM, OP_GEMM_BF16, OP_VERIFY, OP_GEMM_GROUP, OP_VERIFY2 = 0, 1, 2, 3, 4, 5, 6
 MAX_M = 128
 MAX_GROUP = 4
 STATUS = {0: "W12_OK", -1: "W12_ERR_NULL", -2: "W12_ERR_SHAPE", -3: "W12_ERR_RANGE",
@@ -24,7 +24,9 @@ EXPORTS = ("w12_tiles_bytes", "w12_workspace_bytes", "w12_workspace_init", "w12_
            "w12_gemm_group_rms", "w12_gemm_bf16", "w12_bf16_tile",
            "w12_gemm_bf16_tiled", "w12_lmhead_verify", "w12_lmhead_verify_batched",
            "w12_logits_f32",
-           "w12_rms_rescale", "w12_status_str", "w12_version", "w12_gemm_noalloc", "w12_stream_read")
+           "w12_rms_rescale", "w12_status_str", "w12_version", "w12_gemm_noalloc", "w12_stream_read",
+           "w12_screen_bytes", "w12_screen_encode", "w12_lmhead_verify2", "w12_lmhead_verify2_batched",
+           "w12_screen_logits_f32")
 NOALLOC_SCRATCH_BYTES = 32 << 20   # W12_NOALLOC_SCRATCH_BYTES
 ENCODE_TOTAL_OFFSET = 2112   # W12_ENCODE_TOTAL_OFFSET: true escape count in an encode workspace
 
@@ -103,6 +105,21 @@ def lib():
         L.w12_logits_f32.restype = c_int32
         L.w12_logits_f32.argtypes = [c_void_p, c_uint32, ctypes.POINTER(W12Desc), c_void_p,
                                      c_void_p, c_void_p, c_size_t, c_void_p]
+        L.w12_screen_bytes.restype = c_size_t
+        L.w12_screen_bytes.argtypes = [c_uint64, c_uint64]
+        L.w12_screen_encode.restype = c_int32
+        L.w12_screen_encode.argtypes = [c_void_p, c_uint64, c_uint64, c_void_p, c_size_t, c_void_p]
+        L.w12_lmhead_verify2.restype = c_int32
+        L.w12_lmhead_verify2.argtypes = [c_void_p, c_uint32, ctypes.POINTER(W12Desc), c_void_p,
+                                         c_void_p, c_uint32, c_void_p, c_void_p, c_void_p,
+                                         c_size_t, c_void_p]
+        L.w12_lmhead_verify2_batched.restype = c_int32
+        L.w12_lmhead_verify2_batched.argtypes = [c_void_p, c_uint32, ctypes.POINTER(W12Desc),
+                                                 c_void_p, c_void_p, c_void_p, c_uint32, c_void_p,
+                                                 c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]
+        L.w12_screen_logits_f32.restype = c_int32
+        L.w12_screen_logits_f32.argtypes = [c_void_p, c_uint32, ctypes.POINTER(W12Desc), c_void_p,
+                                            c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]
         L.w12_rms_rescale.restype = c_int32
         L.w12_rms_rescale.argtypes = [c_void_p, c_uint32, c_uint64, c_void_p, c_void_p]
         L.w12_status_str.restype = ctypes.c_char_p
@@ -370,7 +387,8 @@ def lmhead_verify(x, t: W12Tensor, draft, argmax_out=None, accepted_out=None):
     return argmax_out, accepted_out
 
 
-def _batched_args(x, t: W12Tensor, req_off, req_ndraft, draft, argmax_out, accepted_out):
+def _batched_checked(x, t: W12Tensor, req_off, req_ndraft, draft, argmax_out, accepted_out):
+    """Validated batched-verification tensors (the outputs allocated when not given)."""
     torch = _torch()
     x = _as_bits(x)
     m = x.shape[0]
@@ -383,6 +401,12 @@ def _batched_args(x, t: W12Tensor, req_off, req_ndraft, draft, argmax_out, accep
         argmax_out = torch.empty(m, dtype=torch.int32, device=x.device)
     if accepted_out is None:
         accepted_out = torch.empty(n_req, dtype=torch.int32, device=x.device)
+    return x, m, n_req, argmax_out, accepted_out
+
+
+def _batched_args(x, t: W12Tensor, req_off, req_ndraft, draft, argmax_out, accepted_out):
+    x, m, n_req, argmax_out, accepted_out = _batched_checked(x, t, req_off, req_ndraft, draft,
+                                                             argmax_out, accepted_out)
     ws = workspace(workspace_bytes(OP_VERIFY, m, t.n, t.k), x.device, "verify")
     d = t.desc()
     args = (_ptr(x), m, ctypes.byref(d), _ptr(req_off), _ptr(req_ndraft), n_req, _ptr(draft),
@@ -399,6 +423,109 @@ def lmhead_verify_batched(x, t: W12Tensor, req_off, req_ndraft, draft, argmax_ou
     args, keep = _batched_args(x, t, req_off, req_ndraft, draft, argmax_out, accepted_out)
     _check("w12_lmhead_verify_batched", lib().w12_lmhead_verify_batched(*args))
     return keep[5], keep[6]
+
+
+@dataclass
+class ScreenCopy:
+    """The screen copy of an LM head for two-level verification (w12_screen_encode):
+    8-bit codes with a BF16 scale per 32 columns, plus the per-row bound constants."""
+    n: int
+    k: int
+    buf: object        # torch.uint8 [w12_screen_bytes(n, k)]
+
+    def nbytes(self) -> int:
+        return int(self.buf.numel())
+
+
+def screen_encode(w) -> ScreenCopy:
+    """Screen copy of BF16 weights w [n, k] (CUDA) on the same device."""
+    torch = _torch()
+    w = _as_bits(w)
+    n, k = w.shape
+    nbytes = int(lib().w12_screen_bytes(n, k))
+    if nbytes == 0:
+        raise ValueError(f"screen copy needs n % 16 == 0, k % 128 == 0, 0 < k < 2^20 (got {n}x{k})")
+    buf = torch.empty(nbytes, dtype=torch.uint8, device=w.device)
+    _check("w12_screen_encode", lib().w12_screen_encode(_ptr(w), n, k, _ptr(buf), nbytes,
+                                                        _stream(w.device)))
+    return ScreenCopy(n=n, k=k, buf=buf)
+
+
+def _verify2_ws(m: int, t: W12Tensor, dev):
+    # zero-filled on allocation: its row tickets start at zero (every call leaves them so)
+    return workspace(workspace_bytes(OP_VERIFY2, m, t.n, t.k), dev, "verify2")
+
+
+def _check_screen(t: W12Tensor, sc: ScreenCopy):
+    if (sc.n, sc.k) != (t.n, t.k):
+        raise ValueError(f"screen copy is {sc.n}x{sc.k}, the head {t.n}x{t.k}")
+
+
+def lmhead_verify2(x, t: W12Tensor, sc: ScreenCopy, draft, argmax_out=None, accepted_out=None):
+    """Two-level verification: the same results as lmhead_verify, from the screen copy
+    first and the W12 head for the logits it cannot rule out."""
+    torch = _torch()
+    _check_screen(t, sc)
+    x = _as_bits(x)
+    m = x.shape[0]
+    if argmax_out is None:
+        argmax_out = torch.empty(m, dtype=torch.int32, device=x.device)
+    if accepted_out is None:
+        accepted_out = torch.empty(1, dtype=torch.int32, device=x.device)
+    n_draft = int(draft.numel())
+    ws = _verify2_ws(m, t, x.device)
+    d = t.desc()
+    _check("w12_lmhead_verify2", lib().w12_lmhead_verify2(
+        _ptr(x), m, ctypes.byref(d), _ptr(sc.buf), _ptr(draft) if n_draft else None, n_draft,
+        _ptr(argmax_out), _ptr(accepted_out), _ptr(ws), ws.numel(), _stream(x.device)))
+    return argmax_out, accepted_out
+
+
+def _batched2_args(x, t: W12Tensor, sc: ScreenCopy, req_off, req_ndraft, draft, argmax_out,
+                   accepted_out):
+    _check_screen(t, sc)
+    x, m, n_req, argmax_out, accepted_out = _batched_checked(x, t, req_off, req_ndraft, draft,
+                                                             argmax_out, accepted_out)
+    ws = _verify2_ws(m, t, x.device)
+    d = t.desc()
+    args = (_ptr(x), m, ctypes.byref(d), _ptr(sc.buf), _ptr(req_off), _ptr(req_ndraft), n_req,
+            _ptr(draft), _ptr(argmax_out), _ptr(accepted_out), _ptr(ws), ws.numel(),
+            _stream(x.device))
+    return args, (x, t, sc, req_off, req_ndraft, draft, argmax_out, accepted_out, ws, d)
+
+
+def lmhead_verify2_batched(x, t: W12Tensor, sc: ScreenCopy, req_off, req_ndraft, draft,
+                           argmax_out=None, accepted_out=None):
+    """Several requests in one two-level pass (requests as lmhead_verify_batched)."""
+    args, keep = _batched2_args(x, t, sc, req_off, req_ndraft, draft, argmax_out, accepted_out)
+    _check("w12_lmhead_verify2_batched", lib().w12_lmhead_verify2_batched(*args))
+    return keep[6], keep[7]
+
+
+def screen_logits_f32(x, t: W12Tensor, sc: ScreenCopy):
+    """The screen logits z8^ [m, n] and their certified bounds [m, n] (FP32) from the first
+    pass of the two-level verification."""
+    torch = _torch()
+    _check_screen(t, sc)
+    x = _as_bits(x)
+    m = x.shape[0]
+    z = torch.empty((m, t.n), dtype=torch.float32, device=x.device)
+    bnd = torch.empty((m, t.n), dtype=torch.float32, device=x.device)
+    ws = _verify2_ws(m, t, x.device)
+    d = t.desc()
+    _check("w12_screen_logits_f32", lib().w12_screen_logits_f32(
+        _ptr(x), m, ctypes.byref(d), _ptr(sc.buf), _ptr(z), _ptr(bnd), _ptr(ws), ws.numel(),
+        _stream(x.device)))
+    return z, bnd
+
+
+def verify2_candidates(t: W12Tensor, m: int):
+    """Per-row diagnostic counts of the last two-level verification on this device's
+    workspace: int32 [m, 2] = (logits the screen could not rule out, those left after the
+    FP64 recomputation; 1 means no exact sum was needed)."""
+    torch = _torch()
+    ws = _verify2_ws(m, t, t.device)
+    return ws[4096:4096 + 8 * m].view(torch.int32).view(m, 2).clone()
 
 
 def verify_candidates(t: W12Tensor, m: int):
@@ -486,6 +613,25 @@ def prepare_verify(x, t: W12Tensor, draft, argmax_out, accepted_out) -> Prepared
             _ptr(argmax_out), _ptr(accepted_out), _ptr(ws), ws.numel(), _stream(x.device))
     return Prepared("w12_lmhead_verify", lib().w12_lmhead_verify, args,
                     (x, t, draft, argmax_out, accepted_out, ws, d))
+
+
+def prepare_verify2(x, t: W12Tensor, sc: ScreenCopy, draft, argmax_out, accepted_out) -> Prepared:
+    _check_screen(t, sc)
+    x = _as_bits(x)
+    m = x.shape[0]
+    n_draft = int(draft.numel())
+    ws = _verify2_ws(m, t, x.device)
+    d = t.desc()
+    args = (_ptr(x), m, ctypes.byref(d), _ptr(sc.buf), _ptr(draft) if n_draft else None, n_draft,
+            _ptr(argmax_out), _ptr(accepted_out), _ptr(ws), ws.numel(), _stream(x.device))
+    return Prepared("w12_lmhead_verify2", lib().w12_lmhead_verify2, args,
+                    (x, t, sc, draft, argmax_out, accepted_out, ws, d))
+
+
+def prepare_verify2_batched(x, t: W12Tensor, sc: ScreenCopy, req_off, req_ndraft, draft,
+                            argmax_out, accepted_out) -> Prepared:
+    args, keep = _batched2_args(x, t, sc, req_off, req_ndraft, draft, argmax_out, accepted_out)
+    return Prepared("w12_lmhead_verify2_batched", lib().w12_lmhead_verify2_batched, args, keep)
 
 
 def prepare_verify_batched(x, t: W12Tensor, req_off, req_ndraft, draft, argmax_out,

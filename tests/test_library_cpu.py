@@ -288,3 +288,94 @@ def test_header_constants_match_binding():
                       ("W12_OP_GEMM", b.OP_GEMM), ("W12_OP_GEMM_BF16", b.OP_GEMM_BF16),
                       ("W12_OP_VERIFY", b.OP_VERIFY), ("W12_OP_GEMM_GROUP", b.OP_GEMM_GROUP)]:
         assert define(name) == val, name
+
+
+def _screen_bytes_closed_form(n, k):
+    a = lambda v: (v + 255) // 256 * 256
+    return a((n // 16) * (k // 128) * 2176) + 2 * a(4 * n)
+
+
+@pytest.mark.parametrize("n,k", [(16, 128), (2048, 512), (151936, 5120), (16400, 512)])
+def test_screen_bytes_closed_form(L, n, k):
+    assert L.w12_screen_bytes(n, k) == _screen_bytes_closed_form(n, k)
+    # the screen tiles are 17/24 of the W12 tiles (2176 against 3072 bytes per 16 x 128)
+    assert (n // 16) * (k // 128) * 2176 * 24 == w12.tiles_bytes(n, k) * 17
+
+
+@pytest.mark.parametrize("n,k", [(0, 128), (15, 128), (16, 100), (16, 1 << 20)])
+def test_screen_bad_shapes(L, n, k):
+    assert L.w12_screen_bytes(n, k) == 0
+    assert w12.workspace_bytes(w12.OP_VERIFY2, 1, n, k) == 0
+
+
+def test_screen_encode_validation(L):
+    f = L.w12_screen_encode
+    big = 1 << 34
+    assert f(None, 2048, 512, FAKE, big, None) == -1
+    assert f(FAKE, 2048, 512, None, big, None) == -1
+    assert f(FAKE, 2008, 512, FAKE, big, None) == -2
+    assert f(FAKE, 2048, 500, FAKE, big, None) == -2
+    assert f(FAKE, 2048, 512, FAKE, L.w12_screen_bytes(2048, 512) - 1, None) == -5
+    assert f(FAKE + 8, 2048, 512, FAKE, big, None) == -7
+    assert f(FAKE, 2048, 512, FAKE + 16, big, None) == -7
+
+
+def test_verify2_workspace_sizes(L):
+    assert w12.workspace_bytes(w12.OP_VERIFY2, 0, 2048, 512) == 0
+    assert w12.workspace_bytes(w12.OP_VERIFY2, w12.MAX_M + 1, 2048, 512) == 0
+    assert w12.workspace_bytes(w12.OP_VERIFY2, w12.MAX_M, 1 << 25, 128) == 0   # m * n >= 2^32
+    a = lambda v: (v + 255) // 256 * 256
+    for m, n in [(1, 2048), (16, 151936), (120, 151936), (5, 16400)]:
+        nb = n // 16
+        ngrp = (nb + 7) // 8
+        cap = 16 * 8 * ((ngrp + 31) // 32)
+        sl, ent = m * 32, m * 32 * cap
+        want = (4096 + a(8 * m) + 3 * a(4 * m * nb) + 2 * a(4 * m * ngrp) + a(4 * sl) + a(8 * sl)
+                + a(4 * ent) + 2 * a(8 * ent) + a(4 * m * n))
+        assert w12.workspace_bytes(w12.OP_VERIFY2, m, n, 512) == want, (m, n)
+
+
+def test_verify2_validation(L):
+    f = L.w12_lmhead_verify2
+    d = desc(n=2048, k=512)
+    big = 1 << 34
+    #        x     m  desc            screen draft nd argmax acc   ws    wsb
+    assert f(None, 4, ctypes.byref(d), FAKE, FAKE, 4, FAKE, FAKE, FAKE, big, None) == -1
+    assert f(FAKE, 4, ctypes.byref(d), None, FAKE, 4, FAKE, FAKE, FAKE, big, None) == -1
+    assert f(FAKE, 4, ctypes.byref(d), FAKE, None, 2, FAKE, FAKE, FAKE, big, None) == -1
+    assert f(FAKE, 4, ctypes.byref(d), FAKE, FAKE, 4, None, FAKE, FAKE, big, None) == -1
+    assert f(FAKE, 4, ctypes.byref(d), FAKE, FAKE, 4, FAKE, None, FAKE, big, None) == -1
+    assert f(FAKE, 4, ctypes.byref(d), FAKE, FAKE, 4, FAKE, FAKE, None, big, None) == -1
+    assert f(FAKE, 4, None, FAKE, FAKE, 4, FAKE, FAKE, FAKE, big, None) == -1
+    assert f(FAKE, 4, ctypes.byref(d), FAKE, FAKE, 5, FAKE, FAKE, FAKE, big, None) == -3   # n_draft > m
+    assert f(FAKE, 0, ctypes.byref(d), FAKE, FAKE, 0, FAKE, FAKE, FAKE, big, None) == -3
+    assert f(FAKE, 129, ctypes.byref(d), FAKE, FAKE, 4, FAKE, FAKE, FAKE, big, None) == -3
+    assert f(FAKE, 4, ctypes.byref(desc(n=1000, k=512)), FAKE, FAKE, 4, FAKE, FAKE, FAKE, big, None) == -2
+    need = w12.workspace_bytes(w12.OP_VERIFY2, 4, 2048, 512)
+    assert f(FAKE, 4, ctypes.byref(d), FAKE, FAKE, 4, FAKE, FAKE, FAKE, need - 1, None) == -5
+    assert f(FAKE + 8, 4, ctypes.byref(d), FAKE, FAKE, 4, FAKE, FAKE, FAKE, big, None) == -7
+    assert f(FAKE, 4, ctypes.byref(d), FAKE + 16, FAKE, 4, FAKE, FAKE, FAKE, big, None) == -7
+    assert f(FAKE, 4, ctypes.byref(d), FAKE, FAKE, 4, FAKE, FAKE, FAKE + 16, big, None) == -7
+    assert f(FAKE, 4, ctypes.byref(d), FAKE, FAKE, 4, FAKE + 2, FAKE, FAKE, big, None) == -7
+
+
+def test_verify2_batched_and_logits_validation(L):
+    f = L.w12_lmhead_verify2_batched
+    d = desc(n=2048, k=512)
+    big = 1 << 34
+    #        x     m  desc            screen off   nd    nreq draft argmax acc   ws    wsb
+    assert f(FAKE, 8, ctypes.byref(d), FAKE, None, FAKE, 3, FAKE, FAKE, FAKE, FAKE, big, None) == -1
+    assert f(FAKE, 8, ctypes.byref(d), FAKE, FAKE, None, 3, FAKE, FAKE, FAKE, FAKE, big, None) == -1
+    assert f(FAKE, 8, ctypes.byref(d), FAKE, FAKE, FAKE, 3, None, FAKE, FAKE, FAKE, big, None) == -1
+    assert f(FAKE, 8, ctypes.byref(d), None, FAKE, FAKE, 3, FAKE, FAKE, FAKE, FAKE, big, None) == -1
+    assert f(FAKE, 8, ctypes.byref(d), FAKE, FAKE, FAKE, 0, FAKE, FAKE, FAKE, FAKE, big, None) == -3
+    assert f(FAKE, 8, ctypes.byref(d), FAKE, FAKE, FAKE, 9, FAKE, FAKE, FAKE, FAKE, big, None) == -3
+    assert f(FAKE, 8, ctypes.byref(d), FAKE, FAKE + 2, FAKE, 3, FAKE, FAKE, FAKE, FAKE, big, None) == -7
+    assert f(FAKE, 8, ctypes.byref(d), FAKE, FAKE, FAKE, 3, FAKE, FAKE, FAKE, FAKE, 100, None) == -5
+    g = L.w12_screen_logits_f32
+    assert g(FAKE, 4, ctypes.byref(d), FAKE, None, FAKE, FAKE, big, None) == -1
+    assert g(FAKE, 4, ctypes.byref(d), FAKE, FAKE, None, FAKE, big, None) == -1
+    assert g(FAKE, 4, ctypes.byref(d), None, FAKE, FAKE, FAKE, big, None) == -1
+    assert g(FAKE, 0, ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, big, None) == -3
+    assert g(FAKE, 4, ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, 100, None) == -5
+    assert g(FAKE, 4, ctypes.byref(d), FAKE, FAKE + 8, FAKE, FAKE, big, None) == -7
