@@ -314,9 +314,12 @@ def extra_workloads(torch, w12, wi, np, dev, args):
     c5 = wi.CONFIG_SHAPES[5]
     vocab, hid, m5 = c5["vocab"], c5["hidden"], c5["m"][0]
     t0 = time.time()
-    head = w12.encode(wi.device_lm_head(torch, vocab, hid))
+    head_bf16 = wi.device_lm_head(torch, vocab, hid)
+    head = w12.encode(head_bf16)
+    screen = w12.screen_encode(head_bf16)   # the 8-bit screen copy of two-level verification
     torch.cuda.synchronize()
-    log(f"bench: LM head encoded in {time.time() - t0:.1f} s; timing verification ...")
+    del head_bf16
+    log(f"bench: LM head encoded (W12 and screen copy) in {time.time() - t0:.1f} s; timing verification ...")
 
     # ---- LM-head greedy verification, M = 16; the BF16-out GEMM of the same shape is timed
     # in alternating rounds with it, so both see the same clock
@@ -329,14 +332,18 @@ def extra_workloads(torch, w12, wi, np, dev, args):
     am_out = torch.empty(16, dtype=torch.int32, device=dev)
     acc_out = torch.empty(1, dtype=torch.int32, device=dev)
     vcall = w12.prepare_verify(x16, head, draft, am_out, acc_out)
+    am2_out = torch.empty(16, dtype=torch.int32, device=dev)
+    acc2_out = torch.empty(1, dtype=torch.int32, device=dev)
+    v2call = w12.prepare_verify2(x16, head, screen, draft, am2_out, acc2_out)
     y16 = torch.empty((16, vocab), dtype=torch.bfloat16, device=dev)
     gcall = w12.prepare_gemm(x16, head, y16)
-    warm(torch, [lambda i: vcall(), lambda i: gcall()], WARM_S)
-    rv, rg = [], []
+    warm(torch, [lambda i: vcall(), lambda i: v2call(), lambda i: gcall()], WARM_S)
+    rv, rv2, rg = [], [], []
     for _ in range(5):
         rv.append(time_calls(torch, vcall, 20, warm_s=0.0))
+        rv2.append(time_calls(torch, v2call, 20, warm_s=0.0))
         rg.append(time_calls(torch, gcall, 20, warm_s=0.0))
-    ms_verify, ms_gemm16 = statistics.median(rv), statistics.median(rg)
+    ms_verify, ms_v2, ms_gemm16 = statistics.median(rv), statistics.median(rv2), statistics.median(rg)
     accepted = int(acc_out.item())
     # the verification's algorithmic bytes: the W12 head, x, the per-block records of
     # pass 1 (16 B per row and 16-row block, written and read) and the argmax
@@ -355,6 +362,42 @@ def extra_workloads(torch, w12, wi, np, dev, args):
     log(f"bench: verify {verify['us_per_verify']} us ({verify['gbps_verify']} GB/s), "
         f"GEMM of the same shape {verify['us_gemm_bf16_out_same_shape']} us")
 
+    # ---- two-level verification (the screen copy first, W12 rows only for the logits the
+    # screen cannot rule out), timed in the same alternating rounds, and at 1 and 8 rows
+    nc2 = w12.verify2_candidates(head, 16).cpu().numpy()
+    two = {"workload": verify["workload"] + ", two levels (8-bit screen copy, then W12)",
+           "us_per_verify": round(ms_v2 * 1e3, 1),
+           "speedup_vs_single_level": round(ms_verify / ms_v2, 3),
+           "screen_copy_bytes": screen.nbytes(),
+           "screen_bytes_vs_w12": round(screen.nbytes() / head.nbytes(), 4),
+           "candidates_per_row_mean": round(float(nc2[:, 0].mean()), 1),
+           "candidates_per_row_max": int(nc2[:, 0].max()),
+           "rows_needing_exact_sums": int((nc2[:, 1] > 1).sum()),
+           "argmax_equals_single_level": bool(torch.equal(am2_out, am_out)),
+           "accepted": int(acc2_out.item()), "accepted_matches_plant": int(acc2_out.item()) == p}
+    by_m = {}
+    for mm in (1, 8):
+        xm_ = torch.from_numpy(wi.verify_batch_x(0)[:mm].copy().view(np.int16)).to(dev)
+        am_a = torch.empty(mm, dtype=torch.int32, device=dev)
+        am_b = torch.empty(mm, dtype=torch.int32, device=dev)
+        acc_a = torch.empty(1, dtype=torch.int32, device=dev)
+        acc_b = torch.empty(1, dtype=torch.int32, device=dev)
+        d_m = draft[:mm].contiguous()
+        c1 = w12.prepare_verify(xm_, head, d_m, am_a, acc_a)
+        c2 = w12.prepare_verify2(xm_, head, screen, d_m, am_b, acc_b)
+        warm(torch, [lambda i: c1(), lambda i: c2()], 0.2)
+        r1, r2 = [], []
+        for _ in range(3):
+            r1.append(time_calls(torch, c1, 20, warm_s=0.0))
+            r2.append(time_calls(torch, c2, 20, warm_s=0.0))
+        m1_, m2_ = statistics.median(r1), statistics.median(r2)
+        by_m[f"M{mm}"] = {"us_single_level": round(m1_ * 1e3, 1), "us_two_level": round(m2_ * 1e3, 1),
+                          "speedup": round(m1_ / m2_, 3),
+                          "argmax_equal": bool(torch.equal(am_a, am_b)) and int(acc_a.item()) == int(acc_b.item())}
+    two["by_m"] = by_m
+    verify["two_level"] = two
+    log(f"bench: two-level verify {two}")
+
     # ---- batched verification: 24 requests x 5 rows in one pass over the head
     xb = torch.from_numpy(wi.batched_verify_x().view(np.int16)).to(dev)
     mb = xb.shape[0]
@@ -372,6 +415,11 @@ def extra_workloads(torch, w12, wi, np, dev, args):
                                        accb_out)
     ms_vb = time_calls(torch, bcall, 30, warm_s=0.1)
     accb = accb_out.cpu().numpy()
+    amb2_out = torch.empty(mb, dtype=torch.int32, device=dev)
+    accb2_out = torch.empty(len(nd), dtype=torch.int32, device=dev)
+    bcall2 = w12.prepare_verify2_batched(xb, head, screen, t_i32(off), t_i32(nd), t_i32(draft_b),
+                                         amb2_out, accb2_out)
+    ms_vb2 = time_calls(torch, bcall2, 30, warm_s=0.1)
     vb_bytes = head.nbytes() + 2 * mb * hid + 2 * 16 * mb * (vocab // 16) + 4 * mb + 4 * len(nd)
     verify_batched = {
         "workload": f"LM head [{vocab}x{hid}] W12, {len(nd)} requests x {mb // len(nd)} rows "
@@ -380,7 +428,10 @@ def extra_workloads(torch, w12, wi, np, dev, args):
         "gbps_verify": round(vb_bytes / (ms_vb * 1e-3) / 1e9, 1),
         "us_per_request": round(ms_vb * 1e3 / len(nd), 2),
         "accepted_match_plants": bool((accb == np.minimum(pb, nd)).all()),
-        "argmax_equals_single_request_call": bool(torch.equal(amb_out, amb))}
+        "argmax_equals_single_request_call": bool(torch.equal(amb_out, amb)),
+        "us_two_level": round(ms_vb2 * 1e3, 1),
+        "two_level_equals_single_level": bool(torch.equal(amb2_out, amb_out)) and
+                                         bool(torch.equal(accb2_out, accb_out))}
     verify["batched"] = verify_batched
     log(f"bench: batched verify {verify_batched}; building the 64-layer stack ...")
 
@@ -477,11 +528,15 @@ def main():
     dev = torch.device("cuda:0")
     if args.profile_verify:
         c5 = wi.CONFIG_SHAPES[5]
-        head = w12.encode(wi.device_lm_head(torch, c5["vocab"], c5["hidden"]))
+        head_bf16 = wi.device_lm_head(torch, c5["vocab"], c5["hidden"])
+        head = w12.encode(head_bf16)
+        screen = w12.screen_encode(head_bf16)
+        del head_bf16
         x16 = torch.from_numpy(wi.verify_batch_x(0).view(np.int16)).to(dev)
         draft = torch.zeros(16, dtype=torch.int32, device=dev)
-        for _ in range(args.steps):
+        for _ in range(args.steps):   # single level, then two levels, alternating
             w12.lmhead_verify(x16, head, draft)
+            w12.lmhead_verify2(x16, head, screen, draft)
         torch.cuda.synchronize()
         log("bench: profile-verify run done")
         return

@@ -295,12 +295,14 @@ w12_status w12_logits_f32(const uint16_t* x, uint32_t m, const w12_desc* d, floa
  *    t%16, then the tile's 64 scales (BF16, little-endian), row 4a+i (a, i = 0..3) and
  *    32-column group j of the tile at 2048 + 32a + 8i + 2j;
  *  - from the next 256-byte boundary, FP32 C[n]: C_v >= ||w_v - q_v s_v||_2 +
- *    gamma ||q_v s_v||_2 (gamma = D 2^-23 / (1 - D 2^-23), D = k + 64), +Inf for a row with
+ *    gamma ||q_v s_v||_2 (gamma = D 2^-23 / (1 - D 2^-23), D = k/32 + 64), +Inf for a row with
  *    a non-finite weight; from the next 256-byte boundary, FP32 A[n] >= (k/32)(max_g s_vg
  *    2^-113 + 2^-125), the allowance for flushed denormals.
- * For any x row and any FP32 evaluation of the screen logit z8^_v = sum_k x_k q_vk s_vg(k)
- * with at most D additions per term, |z8^_v - z_v| <= ||x||_2 C_v + A_v (z_v the exact
- * logit): Cauchy-Schwarz on the code residuals, plus the rounding of the sum. */
+ * For any x row and any FP32 evaluation of the screen logit z8^_v = sum_g s_vg (sum over
+ * the group's 32 columns of x_k q_vk) in which each term passes through at most D
+ * additions (a 32-term group sum, then one scaled addition per group),
+ * |z8^_v - z_v| <= ||x||_2 C_v + A_v (z_v the exact logit): Cauchy-Schwarz on the code
+ * residuals, plus the rounding of the sum. */
 size_t w12_screen_bytes(uint64_t n, uint64_t k);
 
 /* Builds the screen copy of BF16 weights w [n][k] (device, row-major, 16-byte aligned;

@@ -485,16 +485,17 @@ ScreenLayout screen_layout(uint64_t n, uint64_t k) {
 // each row's survivors.  A slice holds at most 16 rows of each block of its groups.
 struct Verify2Layout {
   size_t ncand, hi1, hi2, idx, gh, gl, sc_cnt, sc_lo, sc_v, sc_z, sc_b, surv, total;
-  uint32_t ngrp, cap;
+  uint32_t ngrp, cap, slices;
 };
 
 Verify2Layout verify2_layout(uint32_t m, uint64_t n) {
   Verify2Layout L;
   const uint64_t nb = n / 16;
   L.ngrp = (uint32_t)((nb + kScreenNW - 1) / kScreenNW);
-  L.cap = 16u * kScreenNW * ((L.ngrp + kScreenSlices - 1) / kScreenSlices);
+  L.slices = screen_slices(m);
+  L.cap = 16u * kScreenNW * ((L.ngrp + L.slices - 1) / L.slices);
   const size_t rec = align256((size_t)m * nb * 4), grec = align256((size_t)m * L.ngrp * 4);
-  const size_t sl = (size_t)m * kScreenSlices, ent = sl * L.cap;
+  const size_t sl = (size_t)m * L.slices, ent = sl * L.cap;
   L.ncand = kTicketBytes;
   L.hi1 = L.ncand + align256((size_t)m * 8);
   L.hi2 = L.hi1 + rec;
@@ -578,6 +579,7 @@ w12_status verify2_impl(const uint16_t* x, uint32_t m, const w12_desc* d, const 
   v.sc_b = (double*)(base + L.sc_b);
   v.surv = (int32_t*)(base + L.surv);
   v.cap = L.cap;
+  v.slices = L.slices;
   v.argmax = argmax_out;
   v.ncand = (int32_t*)(base + L.ncand);
   v.draft = draft;

@@ -225,7 +225,15 @@ hipError_t launch_verify_pass2(const VerifyArgs& a, hipStream_t s);
 // Two-level verification (w12_screen.hip): the screen copy of the head (8-bit codes, a
 // BF16 scale per 32 columns) and its two passes.
 constexpr uint32_t kScreenTileBytes = 2176;   // 2048 code bytes + 64 BF16 scales
-constexpr uint32_t kScreenSlices = 32;        // workgroups per x row in the second pass
+// Workgroups per x row in the second pass: more for few rows (each workgroup takes the
+// candidates of its share of the row's groups), fewer when many rows fill the chip anyway.
+#ifndef W12_SCREEN_SLICES
+#define W12_SCREEN_SLICES 32u, 16u, 8u, 4u   // m <= 16, <= 32, <= 64, more
+#endif
+__host__ __device__ inline uint32_t screen_slices(uint32_t m) {
+  constexpr uint32_t t[4] = {W12_SCREEN_SLICES};
+  return m <= 16 ? t[0] : (m <= 32 ? t[1] : (m <= 64 ? t[2] : t[3]));
+}
 constexpr uint32_t kScreenNW = 8;             // row-blocks (waves) per first-pass workgroup
 
 struct ScreenArgs {         // first pass: the screen GEMM with the interval epilogue
@@ -261,7 +269,7 @@ struct SelectArgs {         // second pass: candidates, FP64 from W12, exact, ac
   double* sc_z;             // [m][slices][cap]
   double* sc_b;             // [m][slices][cap]
   int32_t* surv;            // [m][n] survivors of the row (the last workgroup)
-  uint32_t cap;
+  uint32_t cap, slices;      // entries per slice, slices per row (screen_slices(m))
   int32_t* argmax;          // [m]
   int32_t* ncand;           // [m][2]: candidates after the screen, after FP64 (may be NULL)
   const int32_t* draft;

@@ -9,15 +9,16 @@
 // least 2^-100) and codes q = rne(w / s) (int8, |q| <= 127, 0 for a non-finite w), in
 // tiles of 16 rows x 128 columns (2176 bytes: the codes at the W12 sign/mantissa byte
 // positions, then the tile's 64 scales); per row C_v >= ||r_v||_2 + gamma ||w^_v||_2
-// (w^ = q s, r = w - w^, gamma = D 2^-23 / (1 - D 2^-23), D = K + 64; +Inf for a row with a
+// (w^ = q s, r = w - w^, gamma = D 2^-23 / (1 - D 2^-23), D = K/32 + 64; +Inf for a row with a
 // non-finite weight) and A_v = (K/32)(max_g s_vg 2^-113 + 2^-125), rounded up.
 //
 // Why the interval holds: z_v = sum_k x_k w_vk = z8_v + sum_k x_k r_vk with z8 = x . w^,
 // and |sum_k x_k r_vk| <= ||x||_2 ||r_v||_2 (Cauchy-Schwarz).  The first pass computes
 // z8^ = sum_g s_vg (sum_{k in g} x_k q_vk): each inner sum is one MFMA step on exact
-// products (a BF16 x times an integer |q| <= 127 is exact in FP32), scaled and added with
-// one FMA, so each term passes through at most D additions with relative error below
-// 2^-23 and |z8^ - z8| <= gamma S8 + A_v with S8 = sum_k |x_k||w^_vk| <= ||x||_2 ||w^_v||_2
+// products (a BF16 x times an integer |q| <= 127 is exact in FP32; at most 31 additions),
+// scaled and added to the running total with one FMA (at most K/32 more), so each term
+// passes through at most D = K/32 + 64 additions with relative error below 2^-23 and
+// |z8^ - z8| <= gamma S8 + A_v with S8 = sum_k |x_k||w^_vk| <= ||x||_2 ||w^_v||_2
 // (A_v covers flushed denormal products, partial sums and scaled sums).  With X >= ||x||_2
 // (from the staged x, rounded up), |z8^ - z_v| <= X C_v + A_v.  A non-finite z8^ (FP32
 // overflow) gives the interval (-Inf, +Inf).
@@ -129,7 +130,7 @@ __global__ __launch_bounds__(256) void k_screen_encode(const uint16_t* w, uint32
     // each square is exact (at most 16 significant bits); K terms summed in FP64 are
     // within K 2^-53 < 2^-33 of the exact sums, and sqrt, the product and the sum add a
     // few units of 2^-53: widened by 2^-30 and 2^-50, rounded up to FP32
-    const double dd = (double)k + 64.0;
+    const double dd = (double)(k / 32u) + 64.0;   // D of the screen sum (see above)
     const double gam = dd * 0x1p-23 / (1.0 - dd * 0x1p-23);
     const double rn = sqrt(r2 * (1.0 + 0x1p-30)) * (1.0 + 0x1p-50);
     const double qn = sqrt(q2 * (1.0 + 0x1p-30)) * (1.0 + 0x1p-50);
@@ -376,59 +377,10 @@ hipError_t launch_screen_pass1(const ScreenArgs& a, hipStream_t s) {
 // ------------------------------------------------------------------ pass 2
 constexpr uint32_t kSelT = 512;
 constexpr uint32_t kSelW = kSelT / 64u;
+constexpr uint32_t kSelMaxSlices = 32;
+constexpr uint32_t kUnitChunk = 8;    // 8-weight units per thread with loads in flight together
+constexpr uint32_t kSelCandLds = 512; // candidate ids of a slice kept in LDS (the rest re-read)
 static_assert(kSelW == kExactWaves, "the exact stage runs one wave per candidate");
-
-// FP64 logit of head row v against x row xr, by one wave (the lanes take 8-weight units
-// U = lane, lane + 64, ... of row r's lane slots (g, q) = (U / 4) / 4, (U / 4) % 4, group
-// jj = U % 4; escapes of row r replace the product decoded with code 0).  Each product is
-// exact in FP64; summed in any order, the K products and two terms per escape (K' terms)
-// are within g64 S64 of the exact logit, g64 = (K'+8) 2^-53 / (1 - (K'+8) 2^-53), S64 the
-// sum of the terms' magnitudes.  Every lane ends with z, S64 and the escape count.
-__device__ void fp64_logit_wave(const ExactRow& c, const uint32_t* esc_off, uint32_t v,
-                                uint32_t lane, double& z, double& sa, uint32_t& nesc) {
-  const uint32_t b = v >> 4, r = v & 15u;
-  z = 0.0;
-  sa = 0.0;
-  nesc = 0;
-  const uint32_t e0 = esc_off[b], e1 = esc_off[b + 1];
-  for (uint32_t U = lane; U < 16u * c.g_cols; U += 64u) {
-    const uint32_t j = U >> 2, jj = U & 3u, g = j >> 2, q = j & 3u, l = 16u * q + r;
-    const uint8_t* tb = c.tiles + ((uint64_t)g * c.nb + b) * 3072u + 16u * l;
-    const uint2 smv = *reinterpret_cast<const uint2*>(tb + 1024u * (jj >> 1) + 8u * (jj & 1u));
-    const uint32_t cwj = *reinterpret_cast<const uint32_t*>(tb + 2048u + 4u * jj);
-    const u32x4 xv = *reinterpret_cast<const u32x4*>(c.xr + 128u * g + 32u * jj + 8u * q);
-#pragma unroll
-    for (uint32_t i = 0; i < 8; ++i) {
-      const uint32_t sm = ((i < 4u ? smv.x : smv.y) >> (8u * (i & 3u))) & 0xFFu;
-      const uint32_t code = (cwj >> (4u * (i >> 1) + 16u * (i & 1u))) & 0xFu;
-      const uint32_t e = (c.lut[code >> 2] >> (8u * (code & 3u))) & 0xFFu;
-      const uint32_t wb = ((sm & 0x80u) << 8) | (e << 7) | (sm & 0x7Fu);
-      const uint32_t xb = (xv[i >> 1] >> (16u * (i & 1u))) & 0xFFFFu;
-      const double pr = (double)__uint_as_float(xb << 16) * (double)__uint_as_float(wb << 16);
-      z += pr;
-      sa += fabs(pr);
-    }
-  }
-  for (uint32_t i = e0 + lane; i < e1; i += 64u) {
-    const uint32_t rec = c.esc[i];
-    const uint32_t kk = (rec >> 8) & 0xFFFFFu;
-    if ((rec >> 28) != r || kk >= c.k) continue;   // another row, or malformed
-    const uint32_t wb = decode_w(c.tiles, c.nb, v, kk, c.lut);
-    const uint32_t wt = (wb & 0x807Fu) | ((rec & 0xFFu) << 7);
-    const double xv = (double)__uint_as_float((uint32_t)c.xr[kk] << 16);
-    const double pw = xv * (double)__uint_as_float(wb << 16);
-    const double pt = xv * (double)__uint_as_float(wt << 16);
-    z += pt - pw;
-    sa += fabs(pt) + fabs(pw);
-    ++nesc;
-  }
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    z += __shfl_xor(z, off);
-    sa += __shfl_xor(sa, off);
-    nesc += __shfl_xor(nesc, off);
-  }
-}
 
 // Device-scope (agent) stores and loads: the data one workgroup leaves for the workgroup
 // that completes the row, which may run on another XCD.
@@ -441,10 +393,103 @@ __device__ __forceinline__ T ld_agent(const T* p) {
   return __hip_atomic_load(const_cast<T*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// FP64 logits of candidates [0, nc) of this workgroup (ids from get(c)) from the W12 tiles:
+// up to 8 candidates at a time, kSelT / G threads each (G = candidates of the round, a
+// power of two), so that a thread's share of a row (8-weight units U = u, u + per, ... of
+// row r's lane slots (g, q) = (U / 4) / 4, (U / 4) % 4, group jj = U % 4) is at most a
+// chunk or two, its loads issued together.  Each product is exact in FP64; summed in any
+// order, the K products and two terms per escape (K' terms) are within g64 S64 of the exact
+// logit, g64 = (K'+8) 2^-53 / (1 - (K'+8) 2^-53), S64 the sum of the terms' magnitudes.
+// Partial sums meet in fixed shuffle and LDS trees.  put(c, z, b64) runs in one thread per
+// candidate.
+template <class Get, class Put>
+__device__ void fp64_logits_wg(const ExactRow& c, const uint32_t* esc_off, uint32_t nc, Get get,
+                               Put put, double* s_d0, double* s_d1, uint32_t* s_u0) {
+  const uint32_t tid = threadIdx.x, lane = tid & 63u, wave = tid >> 6;
+  const uint32_t nunits = 16u * c.g_cols;
+  for (uint32_t c0 = 0; c0 < nc; c0 += 8u) {
+    const uint32_t left = nc - c0;
+    const uint32_t G = left >= 8u ? 8u : (left > 4u ? 8u : (left > 2u ? 4u : left));
+    const uint32_t per = kSelT / G, cc = tid / per, u = tid % per;
+    const bool active = cc < left;
+    double z = 0.0, sa = 0.0;
+    uint32_t nesc = 0;
+    if (active) {
+      const uint32_t v = (uint32_t)get(c0 + cc), b = v >> 4, r = v & 15u;
+      const uint32_t e0 = esc_off[b], e1 = esc_off[b + 1];
+      for (uint32_t U0 = u; U0 < nunits; U0 += kUnitChunk * per) {
+        uint2 smv[kUnitChunk];
+        uint32_t cwv[kUnitChunk];
+        u32x4 xv[kUnitChunk];
+#pragma unroll
+        for (uint32_t i = 0; i < kUnitChunk; ++i) {
+          const uint32_t U = min(U0 + i * per, nunits - 1u);   // clamped: loaded, not added
+          const uint32_t j = U >> 2, jj = U & 3u, g = j >> 2, q = j & 3u, l = 16u * q + r;
+          const uint8_t* tb = c.tiles + ((uint64_t)g * c.nb + b) * 3072u + 16u * l;
+          smv[i] = *reinterpret_cast<const uint2*>(tb + 1024u * (jj >> 1) + 8u * (jj & 1u));
+          cwv[i] = *reinterpret_cast<const uint32_t*>(tb + 2048u + 4u * jj);
+          xv[i] = *reinterpret_cast<const u32x4*>(c.xr + 128u * g + 32u * jj + 8u * q);
+        }
+#pragma unroll
+        for (uint32_t i = 0; i < kUnitChunk; ++i) {
+          if (U0 + i * per >= nunits) continue;
+#pragma unroll
+          for (uint32_t e = 0; e < 8; ++e) {
+            const uint32_t sm = ((e < 4u ? smv[i].x : smv[i].y) >> (8u * (e & 3u))) & 0xFFu;
+            const uint32_t code = (cwv[i] >> (4u * (e >> 1) + 16u * (e & 1u))) & 0xFu;
+            const uint32_t ex = (c.lut[code >> 2] >> (8u * (code & 3u))) & 0xFFu;
+            const uint32_t wb = ((sm & 0x80u) << 8) | (ex << 7) | (sm & 0x7Fu);
+            const uint32_t xb = (xv[i][e >> 1] >> (16u * (e & 1u))) & 0xFFFFu;
+            const double pr = (double)__uint_as_float(xb << 16) * (double)__uint_as_float(wb << 16);
+            z += pr;
+            sa += fabs(pr);
+          }
+        }
+      }
+      for (uint32_t i = e0 + u; i < e1; i += per) {
+        const uint32_t rec = c.esc[i];
+        const uint32_t kk = (rec >> 8) & 0xFFFFFu;
+        if ((rec >> 28) != r || kk >= c.k) continue;   // another row, or malformed
+        const uint32_t wb = decode_w(c.tiles, c.nb, v, kk, c.lut);
+        const uint32_t wt = (wb & 0x807Fu) | ((rec & 0xFFu) << 7);
+        const double xd = (double)__uint_as_float((uint32_t)c.xr[kk] << 16);
+        const double pw = xd * (double)__uint_as_float(wb << 16);
+        const double pt = xd * (double)__uint_as_float(wt << 16);
+        z += pt - pw;
+        sa += fabs(pt) + fabs(pw);
+        ++nesc;
+      }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      z += __shfl_xor(z, off);
+      sa += __shfl_xor(sa, off);
+      nesc += __shfl_xor(nesc, off);
+    }
+    if (lane == 0) { s_d0[wave] = z; s_d1[wave] = sa; s_u0[wave] = nesc; }
+    __syncthreads();
+    if (active && u == 0) {
+      const uint32_t w0 = cc * (per / 64u);
+      double zz = 0.0, ss = 0.0;
+      uint32_t ne = 0;
+      for (uint32_t w = 0; w < per / 64u; ++w) { zz += s_d0[w0 + w]; ss += s_d1[w0 + w]; ne += s_u0[w0 + w]; }
+      const double kk2 = (double)c.k + 2.0 * (double)ne + 8.0;
+      const double g64 = kk2 * 0x1p-53 / (1.0 - kk2 * 0x1p-53);
+      put(c0 + cc, zz, g64 * ss / (1.0 - g64) * (1.0 + 0x1p-20));
+    }
+    __syncthreads();   // s_d0.. are rewritten by the next round
+  }
+}
+
 __global__ __launch_bounds__(kSelT) void k_screen_select(SelectArgs a) {
   __shared__ ExactShared s_ex;
+  __shared__ int32_t s_cand[kSelCandLds];   // this slice's first candidates (all in sc_v too)
   __shared__ float s_lf[kSelW];
-  __shared__ double s_lo64[kSelW];
+  __shared__ double s_d0[kSelW], s_d1[kSelW];
+  __shared__ uint32_t s_u0[kSelW];
+  __shared__ double s_lo64[8];
+  __shared__ int32_t s_scnt[kSelMaxSlices], s_soff[kSelMaxSlices + 1];
+  __shared__ double s_slo[kSelMaxSlices];
   __shared__ uint32_t s_flag, s_cnt, s_last, s_nsurv, s_allexact;
   __shared__ int32_t s_low;
   const uint32_t slice = blockIdx.x, row = blockIdx.y, tid = threadIdx.x;
@@ -453,22 +498,39 @@ __global__ __launch_bounds__(kSelT) void k_screen_select(SelectArgs a) {
   const uint16_t* xr = a.x + (uint64_t)row * a.k;
   const size_t sbase = ((size_t)row * S + slice) * a.cap;
   if (tid == 0) { s_flag = 0; s_cnt = 0; }
+  if (tid < 8) s_lo64[tid] = -__builtin_inf();
   __syncthreads();
 
   // 1. the x row: nonzero (bit 0) and non-finite (bit 1) entries; L = the row's largest
-  // lower end over the group records
+  // lower end over the group records (all loads of a thread issued before any use)
   uint32_t fl = 0;
-  for (uint32_t u = tid; u < a.k / 8u; u += kSelT) {
-    const u32x4 xv = reinterpret_cast<const u32x4*>(xr)[u];
+  float lm = -__builtin_inff();
+  {
+    constexpr uint32_t kXU = 2, kGU = 4;
+    const uint32_t nx = a.k / 8u;
+    // round r covers x units [r * kXU * kSelT, +kXU * kSelT) and groups [r * kGU * kSelT, +kGU * kSelT)
+    static_assert(kGU == 2 * kXU, "one round covers half as many x units as groups");
+    for (uint32_t base = 0; base < max(2u * nx, a.ngrp); base += kSelT * kGU) {
+      u32x4 xv[kXU];
+      float gv[kGU];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const uint32_t bits = (xv[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
-      if (bits & 0x7FFFu) fl |= 1u;
-      if (((bits >> 7) & 0xFFu) == 0xFFu) fl |= 2u;
+      for (uint32_t i = 0; i < kXU; ++i) xv[i] = reinterpret_cast<const u32x4*>(xr)[min(base / 2u + i * kSelT + tid, nx - 1u)];
+#pragma unroll
+      for (uint32_t i = 0; i < kGU; ++i) gv[i] = a.gl[(size_t)row * a.ngrp + min(base + i * kSelT + tid, a.ngrp - 1u)];
+#pragma unroll
+      for (uint32_t i = 0; i < kXU; ++i) {
+        if (base / 2u + i * kSelT + tid >= nx) continue;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t bits = (xv[i][e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+          if (bits & 0x7FFFu) fl |= 1u;
+          if (((bits >> 7) & 0xFFu) == 0xFFu) fl |= 2u;
+        }
+      }
+#pragma unroll
+      for (uint32_t i = 0; i < kGU; ++i) lm = fmaxf(lm, gv[i]);   // clamped repeats are harmless
     }
   }
-  float lm = -__builtin_inff();
-  for (uint32_t G = tid; G < a.ngrp; G += kSelT) lm = fmaxf(lm, a.gl[(size_t)row * a.ngrp + G]);
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) lm = fmaxf(lm, __shfl_xor(lm, off));
   if (fl) atomicOr(&s_flag, fl);
@@ -479,54 +541,60 @@ __global__ __launch_bounds__(kSelT) void k_screen_select(SelectArgs a) {
   const uint32_t flags = s_flag;
   const bool work = (flags & 1u) && !(flags & 2u);   // nonzero and finite
 
-  const double kinfl = 1.0 + 0x1p-20;
   if (work) {
     // 2. candidates of this slice's groups (slice, slice + S, ...): a row v whose upper
     // end hi_v is below L is not the argmax; a block holds such rows only, its best row,
     // or (second best reaching L) possibly any row
+    auto put = [&](int32_t v) {
+      const uint32_t c = atomicAdd(&s_cnt, 1u);
+      if (c < kSelCandLds) s_cand[c] = v;
+      st_agent(a.sc_v + sbase + c, v);
+    };
     for (uint32_t t0 = 0; slice + S * t0 < a.ngrp; t0 += kSelT) {
       const uint32_t G = slice + S * (t0 + tid);
-      if (G < a.ngrp && a.gh[(size_t)row * a.ngrp + G] >= L) {
+      if (G < a.ngrp) {
+        // the group's upper end and its blocks' records, all requested at once
+        const float gh = a.gh[(size_t)row * a.ngrp + G];
         const uint32_t b0 = G * a.bpg;
-        for (uint32_t qb = 0; qb < a.bpg && b0 + qb < a.nb; ++qb) {
-          const uint32_t b = b0 + qb;
-          const size_t o = (size_t)row * a.nb + b;
-          const float h1 = a.hi1[o], h2 = a.hi2[o];
-          const int32_t i1 = a.idx[o];
-          if (!(h1 >= L)) continue;
-          st_agent(a.sc_v + sbase + atomicAdd(&s_cnt, 1u), i1);
-          if (h2 >= L)
-            for (uint32_t rr = 0; rr < 16; ++rr)
-              if ((int32_t)(16u * b + rr) != i1) st_agent(a.sc_v + sbase + atomicAdd(&s_cnt, 1u), (int32_t)(16u * b + rr));
+        float h1[kMaxBpg], h2[kMaxBpg];
+        int32_t i1[kMaxBpg];
+#pragma unroll
+        for (uint32_t qb = 0; qb < kMaxBpg; ++qb) {
+          const size_t o = (size_t)row * a.nb + min(b0 + min(qb, a.bpg - 1u), a.nb - 1u);
+          h1[qb] = a.hi1[o];
+          h2[qb] = a.hi2[o];
+          i1[qb] = a.idx[o];
+        }
+        if (gh >= L) {
+#pragma unroll
+          for (uint32_t qb = 0; qb < kMaxBpg; ++qb) {
+            const uint32_t b = b0 + qb;
+            if (qb >= a.bpg || b >= a.nb || !(h1[qb] >= L)) continue;
+            put(i1[qb]);
+            if (h2[qb] >= L)
+              for (uint32_t rr = 0; rr < 16; ++rr)
+                if ((int32_t)(16u * b + rr) != i1[qb]) put((int32_t)(16u * b + rr));
+          }
         }
       }
     }
     __syncthreads();
     const uint32_t nc = s_cnt;
-    // 3. FP64 logits, one wave per candidate
+    // 3. their FP64 logits, the whole workgroup on up to 8 at a time
     const ExactRow er{xr, a.tiles, a.esc, a.nb, a.g_cols, a.k, a.lut};
-    double wlo = -__builtin_inf();
-    bool wbad = false;
-    for (uint32_t c = wave; c < nc; c += kSelW) {
-      const int32_t v = ld_agent(a.sc_v + sbase + c);
-      double z, sa;
-      uint32_t ne;
-      fp64_logit_wave(er, a.esc_off, (uint32_t)v, lane, z, sa, ne);
-      const double kk2 = (double)a.k + 2.0 * (double)ne + 8.0;
-      const double g64 = kk2 * 0x1p-53 / (1.0 - kk2 * 0x1p-53);
-      const double b64 = g64 * sa / (1.0 - g64) * kinfl;
-      if (lane == 0) {
-        st_agent(a.sc_z + sbase + c, z);
-        st_agent(a.sc_b + sbase + c, b64);
-      }
-      if (!__builtin_isfinite(z) || !__builtin_isfinite(b64)) wbad = true;
-      else wlo = fmax(wlo, z - b64);
-    }
-    if (lane == 0) s_lo64[wave] = wbad ? __builtin_nan("") : wlo;
-    __syncthreads();
+    fp64_logits_wg(er, a.esc_off, nc,
+                   [&](uint32_t c) { return c < kSelCandLds ? s_cand[c] : ld_agent(a.sc_v + sbase + c); },
+                   [&](uint32_t c, double z, double b64) {
+                     st_agent(a.sc_z + sbase + c, z);
+                     st_agent(a.sc_b + sbase + c, b64);
+                     const double lo = (__builtin_isfinite(z) && __builtin_isfinite(b64)) ? z - b64 : __builtin_nan("");
+                     double& slot = s_lo64[c & 7u];   // one writer per slot and round
+                     slot = (slot != slot || lo != lo) ? __builtin_nan("") : fmax(slot, lo);
+                   },
+                   s_d0, s_d1, s_u0);
     if (tid == 0) {
       double lo = s_lo64[0];
-      for (uint32_t w = 1; w < kSelW; ++w) lo = (lo != lo || s_lo64[w] != s_lo64[w]) ? __builtin_nan("") : fmax(lo, s_lo64[w]);
+      for (uint32_t w = 1; w < 8; ++w) lo = (lo != lo || s_lo64[w] != s_lo64[w]) ? __builtin_nan("") : fmax(lo, s_lo64[w]);
       st_agent(a.sc_cnt + (size_t)row * S + slice, (int32_t)nc);
       st_agent(a.sc_lo + (size_t)row * S + slice, lo);
     }
@@ -549,33 +617,40 @@ __global__ __launch_bounds__(kSelT) void k_screen_select(SelectArgs a) {
   if (!work) {
     result = (flags & 2u) ? -1 : 0;   // non-finite x: -1; all +-0: every logit is 0
   } else {
-    // 5. survivors: candidates whose FP64 interval reaches the largest FP64 lower bound
+    // 5. the slices' counts and largest FP64 lower bounds (one thread each), then the
+    // survivors: candidates whose FP64 interval reaches the largest lower bound
+    if (tid < S) {
+      const int32_t cnt = ld_agent(a.sc_cnt + (size_t)row * S + tid);
+      s_scnt[tid] = max(cnt, 0);
+      s_slo[tid] = cnt > 0 ? ld_agent(a.sc_lo + (size_t)row * S + tid) : -__builtin_inf();
+    }
     if (tid == 0) { s_nsurv = 0; s_allexact = 1; s_low = 0x7FFFFFFF; }
+    __syncthreads();
     double L64 = -__builtin_inf();
     bool bad = false;
     for (uint32_t s = 0; s < S; ++s) {
-      const double lo = ld_agent(a.sc_lo + (size_t)row * S + s);
-      const int32_t cnt = ld_agent(a.sc_cnt + (size_t)row * S + s);
-      if (cnt > 0) {
-        if (lo != lo) bad = true;
-        else L64 = fmax(L64, lo);
-      }
-      ntot += (uint32_t)max(cnt, 0);
+      if (s_slo[s] != s_slo[s]) bad = true;
+      else L64 = fmax(L64, s_slo[s]);
+      ntot += (uint32_t)s_scnt[s];
+    }
+    if (tid == 0) {
+      int32_t acc = 0;
+      for (uint32_t s = 0; s < S; ++s) { s_soff[s] = acc; acc += s_scnt[s]; }
+      s_soff[S] = acc;
     }
     __syncthreads();
     if (!bad) {
       int32_t* surv = a.surv + (size_t)row * a.n;
-      for (uint32_t s = 0; s < S; ++s) {
-        const int32_t cnt = ld_agent(a.sc_cnt + (size_t)row * S + s);
-        const size_t base = ((size_t)row * S + s) * a.cap;
-        for (uint32_t c = tid; c < (uint32_t)max(cnt, 0); c += kSelT) {
-          const double z = ld_agent(a.sc_z + base + c), bb = ld_agent(a.sc_b + base + c);
-          if (z + bb < L64) continue;
-          const int32_t v = ld_agent(a.sc_v + base + c);
-          surv[atomicAdd(&s_nsurv, 1u)] = v;
-          if (bb != 0.0) s_allexact = 0;
-          atomicMin(&s_low, v);
-        }
+      for (uint32_t i = tid; i < ntot; i += kSelT) {
+        uint32_t s = 0;
+        while ((uint32_t)s_soff[s + 1] <= i) ++s;
+        const size_t e = ((size_t)row * S + s) * a.cap + (i - (uint32_t)s_soff[s]);
+        const double z = ld_agent(a.sc_z + e), bb = ld_agent(a.sc_b + e);
+        const int32_t v = ld_agent(a.sc_v + e);
+        if (z + bb < L64) continue;
+        surv[atomicAdd(&s_nsurv, 1u)] = v;
+        if (bb != 0.0) s_allexact = 0;
+        atomicMin(&s_low, v);
       }
     }
     __syncthreads();
@@ -614,7 +689,8 @@ __global__ __launch_bounds__(kSelT) void k_screen_select(SelectArgs a) {
 }
 
 hipError_t launch_screen_pass2(const SelectArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(k_screen_select, dim3(kScreenSlices, a.m), dim3(kSelT), 0, s, a);
+  if (a.slices < 1 || a.slices > kSelMaxSlices) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_screen_select, dim3(a.slices, a.m), dim3(kSelT), 0, s, a);
   return hipGetLastError();
 }
 

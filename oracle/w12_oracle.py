@@ -457,10 +457,13 @@ def accepted_lengths_batched(argmax: np.ndarray, draft: np.ndarray, row_off, n_d
 #            and are checked against the exact sums below, not stored here.
 #
 # The screen bound: for any x, z_v = sum_k x_k w_vk = z8_v + sum_k x_k r_vk with
-# z8_v = sum_k x_k w^_vk, and |sum_k x_k r_vk| <= ||x||_2 ||r_v||_2 (Cauchy-Schwarz); an
-# FP32 evaluation of z8 in any order with at most D = K + 64 additions per term is within
-# gamma*S8 (gamma = D*2^-23/(1 - D*2^-23), S8 = sum_k |x_k||w^_vk| <= ||x||_2 ||w^_v||_2)
-# of z8, plus underflow terms.
+# z8_v = sum_k x_k w^_vk, and |sum_k x_k r_vk| <= ||x||_2 ||r_v||_2 (Cauchy-Schwarz).  z8
+# is evaluated in FP32 as sum_g s_vg (sum_{k in g} x_k q_vk): a 32-term sum of exact
+# products per group (at most 31 additions), then one scaled addition per group into the
+# running total (at most K/32 more), so each term passes through at most D = K/32 + 64
+# additions (with slack); in any such order the result is within gamma*S8 (gamma =
+# D*2^-23/(1 - D*2^-23), S8 = sum_k |x_k||w^_vk| <= ||x||_2 ||w^_v||_2) of z8, plus
+# underflow terms.
 SCREEN_GROUP = 32
 SCREEN_QMAX = 127
 SCREEN_S_MIN = 2.0 ** -100
@@ -533,8 +536,9 @@ def screen_row_sums_exact(w_row: np.ndarray, q_row: np.ndarray, s_row_bits: np.n
 
 
 def screen_gamma(k: int) -> float:
-    """gamma of the screen bound for K columns (D = K + 64 additions per term)."""
-    d = (k + 64) * 2.0 ** -23
+    """gamma of the screen bound for K columns (D = K/32 + 64 additions per term: one
+    32-term group sum, then one scaled addition per group)."""
+    d = (k // SCREEN_GROUP + 64) * 2.0 ** -23
     return d / (1.0 - d)
 
 

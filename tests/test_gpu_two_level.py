@@ -48,7 +48,7 @@ def screen_parts(sc, n, k):
 
 def exact_coef(w_row, q_row, s_row, k):
     r2, q2 = o.screen_row_sums_exact(w_row, q_row, s_row)
-    d = Decimal(k + 64) * Decimal(2) ** -23
+    d = Decimal(k // 32 + 64) * Decimal(2) ** -23
     gam = d / (1 - d)
     unit = Decimal(2) ** -133
     return Decimal(r2).sqrt() * unit + gam * Decimal(q2).sqrt() * unit

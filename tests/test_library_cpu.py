@@ -328,8 +328,9 @@ def test_verify2_workspace_sizes(L):
     for m, n in [(1, 2048), (16, 151936), (120, 151936), (5, 16400)]:
         nb = n // 16
         ngrp = (nb + 7) // 8
-        cap = 16 * 8 * ((ngrp + 31) // 32)
-        sl, ent = m * 32, m * 32 * cap
+        slices = 32 if m <= 16 else 16 if m <= 32 else 8 if m <= 64 else 4
+        cap = 16 * 8 * ((ngrp + slices - 1) // slices)
+        sl, ent = m * slices, m * slices * cap
         want = (4096 + a(8 * m) + 3 * a(4 * m * nb) + 2 * a(4 * m * ngrp) + a(4 * sl) + a(8 * sl)
                 + a(4 * ent) + 2 * a(8 * ent) + a(4 * m * n))
         assert w12.workspace_bytes(w12.OP_VERIFY2, m, n, 512) == want, (m, n)
