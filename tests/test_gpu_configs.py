@@ -245,6 +245,74 @@ def test_config4_lm_head_verify_batched(env, lm_head):
     assert acc.cpu().numpy().tolist() == want.tolist() == np.minimum(pb, nd).tolist()
 
 
+def test_config4_two_level_verify(env, lm_head):
+    """Two-level verification on workload 4's head with the planted near ties: the screen
+    copy's codes and scales equal the oracle's on sampled row-blocks, every screen logit
+    of batch 0 lies within its certified bound of the float64 logit, and every batch's
+    argmax and accepted length equal the oracle's (and the single-level call's); then 1
+    and 8 rows, and the 24-request batch."""
+    torch, w12 = env
+    w, xs = lm_head
+    vocab, k = w.shape
+    wd = to_dev(w, torch)
+    t = w12.encode(wd)
+    sc = w12.screen_encode(wd)
+    torch.cuda.synchronize()
+    del wd
+    # codes and scales of three sampled row-blocks (tiles of every column)
+    nb, gk = vocab // 16, k // 128
+    buf = sc.buf.cpu().numpy()
+    for b in (0, nb // 2, nb - 1):
+        q, s_bits, _ = o.screen_encode(w[16 * b:16 * b + 16])
+        want = o.screen_pack(q, s_bits).reshape(gk, o.SCREEN_TILE_BYTES)
+        got = np.stack([buf[(g * nb + b) * o.SCREEN_TILE_BYTES:(g * nb + b + 1) * o.SCREEN_TILE_BYTES]
+                        for g in range(gk)])
+        assert np.array_equal(got, want), b
+    say("config 4 two-level: screen bound on batch 0")
+    z8, bnd = (v.cpu().numpy().astype(np.float64) for v in w12.screen_logits_f32(to_dev(xs[0], torch), t, sc))
+    z, s = o.gemm_reference(xs[0], w)
+    assert (np.abs(z8 - z) <= bnd + (k + 2) * 2.0 ** -52 * s).all()
+    x_all = np.concatenate(xs)
+    am_ref, _ = o.argmax_exact(x_all, w)
+    for b, x in enumerate(xs):
+        ref = am_ref[16 * b:16 * b + 16]
+        p, r = wi.verify_mismatch(b, vocab)
+        draft = ref.astype(np.int32).copy()
+        if p < 16:
+            draft[p] = (draft[p] + 1 + r) % vocab
+        say("config 4 two-level batch", b, "p", p)
+        am, acc = w12.lmhead_verify2(to_dev(x, torch), t, sc, torch.from_numpy(draft).to("cuda:0"))
+        torch.cuda.synchronize()
+        assert am.cpu().numpy().tolist() == ref.tolist()
+        assert int(acc.item()) == o.accepted_length(ref, draft) == p
+        nc = w12.verify2_candidates(t, 16).cpu().numpy()
+        say("config 4 two-level batch", b, "candidates / left after FP64", nc.tolist())
+        assert (nc[:, 0] >= 1).all() and (nc[:, 1] >= 1).all()
+    for m in (1, 8):
+        x = xs[1][:m]
+        ref = am_ref[16:16 + m]
+        draft = ref.astype(np.int32).copy()
+        draft[m // 2] = (draft[m // 2] + 1 + 12345) % vocab
+        am, acc = w12.lmhead_verify2(to_dev(x, torch), t, sc, torch.from_numpy(draft).to("cuda:0"))
+        torch.cuda.synchronize()
+        assert am.cpu().numpy().tolist() == ref.tolist()
+        assert int(acc.item()) == m // 2
+    xb = wi.batched_verify_x()
+    off, nd, pb, rb = wi.batched_verify_table(vocab)
+    say("config 4 two-level batched: oracle argmax of", xb.shape[0], "rows")
+    amb_ref, _ = o.argmax_exact(xb, w)
+    draft = amb_ref.astype(np.int32).copy()
+    for r in range(len(nd)):
+        if pb[r] < nd[r]:
+            i = off[r] + pb[r]
+            draft[i] = (draft[i] + 1 + rb[r]) % vocab
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to("cuda:0")
+    am, acc = w12.lmhead_verify2_batched(to_dev(xb, torch), t, sc, dev(off), dev(nd), dev(draft))
+    torch.cuda.synchronize()
+    assert am.cpu().numpy().tolist() == amb_ref.tolist()
+    assert acc.cpu().numpy().tolist() == np.minimum(pb, nd).tolist()
+
+
 SAMPLED_LAYERS = (0, 21, 42, 63)
 
 

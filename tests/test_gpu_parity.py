@@ -786,8 +786,9 @@ def test_verify_max_k(env):
 
 def test_graph_capture_replays_match_eager(env):
     """Prepared calls captured in a HIP graph (split-K GEMM completed in the kernel, grouped RMS
-    GEMM, verification with its accept initialisation): every replay, with new inputs
-    copied in eagerly between replays, equals the eager calls bit for bit."""
+    GEMM, verification with its accept initialisation, two-level verification with its row
+    tickets): every replay, with new inputs copied in eagerly between replays, equals the
+    eager calls bit for bit."""
     torch, w12 = env
     g = np.random.default_rng(7400)
     dev = "cuda:0"
@@ -797,6 +798,7 @@ def test_graph_capture_replays_match_eager(env):
     t_split = w12.encode(to_dev(w_split, torch))
     t_grp = [w12.encode(to_dev(w, torch)) for w in ws_grp]
     t_head = w12.encode(to_dev(w_head, torch))
+    sc_head = w12.screen_encode(to_dev(w_head, torch))
     xs = [(wi.gaussian_bf16((7, 4096), 1.0, g), wi.gaussian_bf16((24, 512), 2.0, g),
            wi.gaussian_bf16((16, 512), 1.0, g)) for _ in range(3)]
     x1, x2, x3 = (to_dev(a, torch) for a in xs[0])
@@ -804,14 +806,17 @@ def test_graph_capture_replays_match_eager(env):
     y2 = [torch.empty((24, w.shape[0]), dtype=torch.bfloat16, device=dev) for w in ws_grp]
     am = torch.empty(16, dtype=torch.int32, device=dev)
     acc = torch.empty(1, dtype=torch.int32, device=dev)
+    am2 = torch.empty(16, dtype=torch.int32, device=dev)
+    acc2 = torch.empty(1, dtype=torch.int32, device=dev)
     draft = torch.zeros(16, dtype=torch.int32, device=dev)
 
     def calls():
         return [w12.prepare_gemm(x1, t_split, y1), w12.prepare_gemm_group(x2, t_grp, y2, rms=True),
-                w12.prepare_verify(x3, t_head, draft, am, acc)]
+                w12.prepare_verify(x3, t_head, draft, am, acc),
+                w12.prepare_verify2(x3, t_head, sc_head, draft, am2, acc2)]
 
     def snapshot():
-        return [y1.clone(), *[y.clone() for y in y2], am.clone(), acc.clone()]
+        return [y1.clone(), *[y.clone() for y in y2], am.clone(), acc.clone(), am2.clone(), acc2.clone()]
 
     eager = []
     for a, b, c in xs:                       # eager answers for each input set
@@ -820,6 +825,7 @@ def test_graph_capture_replays_match_eager(env):
             f()
         torch.cuda.synchronize()
         eager.append(snapshot())
+        assert torch.equal(eager[-1][-2], eager[-1][-4]) and torch.equal(eager[-1][-1], eager[-1][-3])
     say("graph capture")
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
