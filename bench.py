@@ -40,7 +40,6 @@ sources still hash to the value recorded there (null otherwise).
 from __future__ import annotations
 
 import argparse
-import glob
 import hashlib
 import json
 import os
@@ -119,12 +118,18 @@ COPY_BYTES = 1 << 30
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "w12_gemm_traffic.json")
 
 
+# Sources the GEMM launches of the counter record are built and planned from (the GEMM
+# kernel family, its instantiations, the host layer that plans and launches them, the
+# internal header, and the streaming-read kernel that calibrates the counters).
+TRAFFIC_SOURCES = ("w12_gemm_kernel.h", "w12_gemm_run.hip", "w12_gemm_lut.hip", "w12_gemm_bf16.hip",
+                   "w12_gemm_bf16t.hip", "w12_internal.h", "w12_api.cpp", "w12_stream.hip")
+
+
 def kernel_source_hash() -> str:
-    """sha256 over the library's sources and header: counters taken on other sources
-    do not describe the kernels that run now."""
+    """sha256 over the sources of the GEMM launches: counters taken on other sources do
+    not describe the kernels that run now."""
     h = hashlib.sha256()
-    files = sorted(glob.glob(os.path.join(ROOT, "lossless_bit_weight_w12_amd", "csrc", "*")))
-    files.append(os.path.join(ROOT, "include", "w12.h"))
+    files = [os.path.join(ROOT, "lossless_bit_weight_w12_amd", "csrc", f) for f in TRAFFIC_SOURCES]
     for f in files:
         h.update(os.path.basename(f).encode())
         with open(f, "rb") as fh:

@@ -125,7 +125,7 @@ def main():
              f"GEMM's nontemporal 16-byte buffer loads reads {stream_f[3]:.0f} KiB; a 1 GiB device copy, "
              f"`{copy_f[1][:40]}`, reads {copy_f[3]:.0f} KiB, scale {copy_scale:.4f}), "
              f"WRITE_SIZE x {write_scale:.4f} (a 1 GiB fill, `{fill_w[1][:40]}`, writes "
-             f"{fill_w[3]:.0f} KiB).  Source sha256 `{rec['source_sha256'][:16]}...`.", "",
+             f"{fill_w[3]:.0f} KiB).  GEMM sources sha256 `{rec['source_sha256'][:16]}...`.", "",
              "| launch | kernels | W12: HBM bytes | algorithmic | ratio | BF16 kernel: HBM bytes | algorithmic | ratio |",
              "|---|---|---|---|---|---|---|---|"]
     for key in keys:
