@@ -884,8 +884,12 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_cs(
     }
   };
 
-  // ---- main loop: every iteration issues the same loads (column g+1 clamped past the
-  // end, values then unused), so each wait is a fixed count; one barrier per column.
+  // ---- main loop: every iteration but the last issues the same loads (the next column's
+  // x and tiles), so each wait is a fixed count; one barrier per column.  Up to 32
+  // columns the last column is computed without a prefetch (a uniform branch): a dead
+  // prefetch past the end would hold the workgroup's exit and its split completion, which
+  // wait for every load (gate+up M32 47.2 -> 45.7 us, down and the decode chain's small
+  // launches 0.2-0.6 us faster).
   // As in k_gemm, the compiler's schedule (which may wait for tile g before issuing
   // tile g+1) measured faster than a pinned deeper prefetch.
   uint32_t g = ga;
@@ -895,21 +899,46 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_cs(
   xsumsq(true);
   xstore(g & 1u);
   __syncthreads();
-  for (;;) {
-    xload(g + 1);
-    tload(tB, min(g + 1, gb - 1u));
-    compute(tA, g);
-    xsumsq(g + 1 < gb);
-    xstore((g + 1) & 1u);
-    __syncthreads();
-    if (++g >= gb) break;
-    xload(g + 1);
-    tload(tA, min(g + 1, gb - 1u));
-    compute(tB, g);
-    xsumsq(g + 1 < gb);
-    xstore((g + 1) & 1u);
-    __syncthreads();
-    if (++g >= gb) break;
+  if constexpr (MT <= 32) {
+    for (;;) {
+      if (g + 1 >= gb) { compute(tA, g); break; }
+      xload(g + 1);
+      tload(tB, g + 1);
+      compute(tA, g);
+      xsumsq(true);
+      xstore((g + 1) & 1u);
+      __syncthreads();
+      ++g;
+      if (g + 1 >= gb) { compute(tB, g); break; }
+      xload(g + 1);
+      tload(tA, g + 1);
+      compute(tB, g);
+      xsumsq(true);
+      xstore((g + 1) & 1u);
+      __syncthreads();
+      ++g;
+    }
+    __syncthreads();   // every wave is done with the x slots
+  } else {
+    // 64 and 128 columns: the peeled column's second copy of the compute raised these
+    // instantiations' registers past an occupancy step (the tiled BF16 kernel at 64 rows:
+    // 94 -> 130 VGPRs, down 41 -> 54 us), so the loop keeps a clamped dead prefetch
+    for (;;) {
+      xload(g + 1);
+      tload(tB, min(g + 1, gb - 1u));
+      compute(tA, g);
+      xsumsq(g + 1 < gb);
+      xstore((g + 1) & 1u);
+      __syncthreads();
+      if (++g >= gb) break;
+      xload(g + 1);
+      tload(tA, min(g + 1, gb - 1u));
+      compute(tB, g);
+      xsumsq(g + 1 < gb);
+      xstore((g + 1) & 1u);
+      __syncthreads();
+      if (++g >= gb) break;
+    }
   }
 
   // RMS launches: each row's sum of x^2 over the K-range: the 16 threads of a row's units

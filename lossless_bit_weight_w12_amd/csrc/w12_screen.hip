@@ -253,6 +253,9 @@ __global__ __launch_bounds__(kScreenNW * 64) void k_screen(ScreenArgs a) {
   xsumsq(true);
   xstore(0);
   __syncthreads();
+  // every iteration issues the same loads (the next column, clamped past the end): fixed
+  // wait counts.  (Peeling the last column, as the GEMM does, raised this kernel's
+  // registers from 68 to 104 and slowed it by about 10 %.)
   for (;;) {
     xload(g + 1);
     tload(tB, min(g + 1, gb - 1u));
