@@ -330,3 +330,24 @@ def test_verify2_workspace_reuse_and_tickets(env):
     call()
     torch.cuda.synchronize()
     assert am.cpu().numpy().tolist() == o.argmax_exact(x_new, heads[hi])[0].tolist()
+
+
+def test_verify2_max_k(env):
+    """Two-level verification at the longest K (2^20 - 128: 8191 tile columns, the screen's
+    32-bit tile offsets, the FP64 loop over 131056 units of a row) with an exact tie."""
+    torch, w12 = env
+    g = np.random.default_rng(9100)
+    m, n, k = 3, 64, (1 << 20) - 128
+    x = wi.gaussian_bf16((m, k), 1.0, g)
+    w = wi.gaussian_bf16((n, k), 0.02, g)
+    w[5] = w[40]
+    say("verify2 max k", m, n, k)
+    am_ref, _ = o.argmax_exact(x, w)
+    draft = am_ref.copy().astype(np.int32)
+    draft[1] = (draft[1] + 1) % n
+    _check_verify2(torch, w12, x, w, am_ref, draft)
+    # the screen copy's codes and scales at this K
+    sc = w12.screen_encode(to_dev(w, torch))
+    q, s_bits, _ = o.screen_encode(w)
+    tiles, _, _ = screen_parts(sc, n, k)
+    assert np.array_equal(tiles, o.screen_pack(q, s_bits))
