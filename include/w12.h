@@ -112,9 +112,9 @@ size_t w12_tiles_bytes(uint64_t n, uint64_t k);
  * [groups][splits][m] (RMS launches), each from a 256-byte boundary; VERIFY holds, each region starting on a 256-byte boundary
  * in this order: per-row diagnostic counts (int32 [m][2]: candidate logits, those left
  * after the FP64 screen), the per-row-block records of the first pass (largest FP32
- * logit, second largest, largest sum_k |x_k||w_k|, each FP32 [m][n/16]; index of the
- * largest, int32 [m][n/16]), its per-workgroup group records (largest logit, its index,
- * that row-block's sum, an upper bound of logit + bound slope * sum over the group:
+ * logit, second largest, largest row norm bound W_v (w12_lmhead_verify), each FP32
+ * [m][n/16]; index of the largest, int32 [m][n/16]), its per-workgroup group records
+ * (largest logit, its index, that row-block's norm bound, the group's largest norm bound:
  * four arrays of [m][n/16] 4-byte entries, the first ngroups of each row used) and the
  * candidate lists (int32 [m][n]); all readable after a call for diagnostics.  ENCODE holds the histogram and per-tile escape counts. */
 size_t w12_workspace_bytes(int op, uint32_t m, uint64_t n, uint64_t k);
@@ -235,8 +235,10 @@ w12_status w12_gemm_bf16_tiled(const uint16_t* x, uint32_t m, const void* w_tile
  * v maximising the EXACT logit sum_k x[row,k]*W[v,k], lowest index on exact ties; and
  * accepted_out device int32 [1]: the first i < n_draft with argmax[i] != draft[i], or
  * n_draft.  A first pass streams the head once and keeps, per 16-row block, the two
- * largest FP32 logits z^ and the largest S = sum_k |x_k||w_vk| (and per workgroup of
- * blocks their maximum and bound); with B(S) a bound on |z^ - z| for any summation
+ * largest FP32 logits z^ and the largest FP32 upper bound W_v of ||w_v||_2 (the same pass
+ * sums the squares of the weights it streams), and per workgroup of blocks their maxima.
+ * The error scale of a logit is S = X W_v >= sum_k |x_k||w_vk| (Cauchy-Schwarz), X an
+ * upper bound of ||x||_2 taken in the second pass.  With B(S) a bound on |z^ - z| for any summation
  * order, every logit whose z^ + B(S) can reach the lower bound z^* - B(S*) of the
  * computed maximum is a candidate; a single candidate is the answer, several are
  * recomputed in FP64 from the W12 tiles, and those that the FP64 intervals cannot
@@ -271,10 +273,10 @@ w12_status w12_lmhead_verify_batched(const uint16_t* x, uint32_t m, const w12_de
                                      size_t ws_bytes, void* stream);
 
 /* The first pass of w12_lmhead_verify with its full output (for tests of the certified
- * bound, and as an FP32-output GEMM): logits_out = FP32 z^ [m][n] and sabs_out = FP32
- * sum_k |x_k||w_vk| [m][n] (device, 16-byte aligned), from the same kernels in the same
- * summation order as the verification; ws as for W12_OP_VERIFY (its block maxima are
- * overwritten).  Errors as w12_lmhead_verify. */
+ * bound, and as an FP32-output GEMM): logits_out = FP32 z^ [m][n] and sabs_out = the
+ * FP32 error scales S = X W_v [m][n] of w12_lmhead_verify, rounded up (device, 16-byte
+ * aligned), from the same kernels in the same summation order as the verification; ws as
+ * for W12_OP_VERIFY (its block maxima are overwritten).  Errors as w12_lmhead_verify. */
 w12_status w12_logits_f32(const uint16_t* x, uint32_t m, const w12_desc* d, float* logits_out,
                           float* sabs_out, void* ws, size_t ws_bytes, void* stream);
 

@@ -215,7 +215,7 @@ bool set_split_ws(GemmArgs& a, void* ws, const GemmPlan& p, uint32_t m, uint64_t
 // per-row-block records of pass 1, its group records (one per workgroup of pass 1: at
 // most one per row-block) and the candidate lists of pass 2.
 struct VerifyLayout {
-  size_t ncand, bm_v, bm_v2, bm_s, bm_i, g_v, g_i, g_s, g_u, cand, total;
+  size_t ncand, bm_v, bm_v2, bm_s, bm_i, g_v, g_i, g_s, g_w, cand, total;
 };
 
 VerifyLayout verify_layout(uint32_t m, uint64_t n) {
@@ -230,8 +230,8 @@ VerifyLayout verify_layout(uint32_t m, uint64_t n) {
   L.g_v = L.bm_i + rec;
   L.g_i = L.g_v + rec;
   L.g_s = L.g_i + rec;
-  L.g_u = L.g_s + rec;
-  L.cand = L.g_u + rec;
+  L.g_w = L.g_s + rec;
+  L.cand = L.g_w + rec;
   L.total = L.cand + align256((size_t)m * n * 4);
   return L;
 }
@@ -247,7 +247,7 @@ BlockMax block_max(uint8_t* base, const VerifyLayout& L, const GemmPlan& p) {
   bm.gv = (float*)(base + L.g_v);
   bm.gi = (int32_t*)(base + L.g_i);
   bm.gs = (float*)(base + L.g_s);
-  bm.gu = (float*)(base + L.g_u);
+  bm.gw = (float*)(base + L.g_w);
   bm.ngrp = p.n_rbg;
   return bm;
 }
@@ -443,7 +443,7 @@ w12_status verify_impl(const uint16_t* x, uint32_t m, const w12_desc* d, const i
   v.grp_v = a.bm.gv;
   v.grp_i = a.bm.gi;
   v.grp_s = a.bm.gs;
-  v.grp_u = a.bm.gu;
+  v.grp_w = a.bm.gw;
   v.ngrp = a.bm.ngrp;
   v.bpg = blocks_per_group(p);
   v.cand = (int32_t*)(base + L.cand);
@@ -818,10 +818,12 @@ w12_status w12_logits_f32(const uint16_t* x, uint32_t m, const w12_desc* d, floa
   a.p.seg[0] = w12_seg(d, nullptr, 0);
   fill_params(a.p, m, d->k, d->n, 1);
   a.logits = logits_out;
-  a.sabs = sabs_out;
+  a.sabs = sabs_out;   // the row norms first, then scaled by each row's bound of ||x||_2
   a.bm = block_max(base, L, p);
   const int src = codebook_is_run(d->codebook) ? SRC_RUN : SRC_LUT;
-  return hip_status(launch_gemm(a, src, EPI_LOGITS, p, (hipStream_t)stream));
+  hipError_t e = launch_gemm(a, src, EPI_LOGITS, p, (hipStream_t)stream);
+  if (e == hipSuccess) e = launch_scale_norms(x, m, d->k, sabs_out, (uint32_t)d->n, (hipStream_t)stream);
+  return hip_status(e);
 }
 
 size_t w12_screen_bytes(uint64_t n, uint64_t k) {

@@ -49,7 +49,6 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-constexpr uint32_t kAbs2 = 0x7FFF7FFFu;   // clears the sign bits of two packed BF16
 
 // Plain BF16 sources (row-major or tiled): no decode, no escapes.
 constexpr bool plain_bf16(int src) { return src == SRC_BF16 || src == SRC_BF16T; }
@@ -421,12 +420,14 @@ __global__ __launch_bounds__(NWV * 64) void k_gemm(
     BlockMax bm,
     GemmParams p) {
   constexpr int NH = MF ? MT / 16 : 1;
-  // the logits epilogue also accumulates S = sum_k |x_k||w_k| per output (the scale of
-  // its rounding-error bound)
-  constexpr bool kS = EPI == EPI_LOGITS;
+  // the logits epilogue also records per weight row an upper bound of ||w_v||_2 (the
+  // scale of its rounding-error bound is ||x||_2 ||w_v||_2, verification pass 2 supplies
+  // ||x||_2): the squares summed by v_dot2 of the weights with themselves (VALU path) or
+  // by an MFMA of the A operand with itself, its diagonal (MFMA path)
+  constexpr bool kWn = EPI == EPI_LOGITS;
   __shared__ __align__(16) uint16_t xs[NWV * MT * kXsStride];   // one x column per wave
-  __shared__ float fin[kS ? RBW * MT * 16 : 1];
-  __shared__ float fin_s[kS ? RBW * MT * 16 : 1];
+  __shared__ float fin[kWn ? RBW * MT * 16 : 1];
+  __shared__ float s_wn[kWn ? RBW * 16 : 1];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform, in an SGPR
@@ -438,14 +439,18 @@ __global__ __launch_bounds__(NWV * 64) void k_gemm(
   const uint32_t gb = (uint32_t)(((uint64_t)(split + 1u) * p.g_cols) / gridDim.y);
   const uint32_t m_rows = MF ? p.m : (uint32_t)M;
 
-  float vacc[RBW][MF ? 1 : M], vsacc[RBW][MF ? 1 : M];
-  f32x4 macc[RBW][NH], msacc[RBW][NH];
+  float vacc[RBW][MF ? 1 : M];
+  f32x4 macc[RBW][NH];
+  float wsq[RBW];     // kWn, VALU: this lane's sum of squares of row r's weights
+  f32x4 nacc[RBW];    // kWn, MFMA: W W^T of the row-block over the wave's columns
 #pragma unroll
   for (int rb = 0; rb < RBW; ++rb) {
 #pragma unroll
-    for (int m = 0; m < (MF ? 1 : M); ++m) vacc[rb][m] = vsacc[rb][m] = 0.f;
+    for (int m = 0; m < (MF ? 1 : M); ++m) vacc[rb][m] = 0.f;
 #pragma unroll
-    for (int h = 0; h < NH; ++h) macc[rb][h] = msacc[rb][h] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int h = 0; h < NH; ++h) macc[rb][h] = f32x4{0.f, 0.f, 0.f, 0.f};
+    wsq[rb] = 0.f;
+    nacc[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
   EscCursor ec[RBW];
@@ -479,6 +484,22 @@ __global__ __launch_bounds__(NWV * 64) void k_gemm(
       }
     }
     const uint16_t* xrow = xw + 8 * q;
+    // logits: the column's sums chain from zero and are then added to the running sums,
+    // so a product meets at most 4 MFMA accumulations or 16 v_dot2 (whatever their
+    // internal order) and one addition per later column: the certified bound's depth
+    f32x4 mcol[RBW][NH];
+    float vcol[RBW][MF ? 1 : M];
+    auto mc = [&](int rb, int h) -> f32x4& { return kWn ? mcol[rb][h] : macc[rb][h]; };
+    auto vc = [&](int rb, int m) -> float& { return kWn ? vcol[rb][m] : vacc[rb][m]; };
+    if constexpr (kWn) {
+#pragma unroll
+      for (int rb = 0; rb < RBW; ++rb) {
+#pragma unroll
+        for (int h = 0; h < NH; ++h) mcol[rb][h] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int m = 0; m < (MF ? 1 : M); ++m) vcol[rb][m] = 0.f;
+      }
+    }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       if constexpr (MF) {
@@ -493,12 +514,16 @@ __global__ __launch_bounds__(NWV * 64) void k_gemm(
 #pragma unroll
           for (int rb = 0; rb < RBW; ++rb) {
             const u32x4 av = {P[rb][4 * j], P[rb][4 * j + 1], P[rb][4 * j + 2], P[rb][4 * j + 3]};
-            macc[rb][h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                __builtin_bit_cast(bf16x8_t, av), bv, macc[rb][h], 0, 0, 0);
-            if constexpr (kS)
-              msacc[rb][h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                  __builtin_bit_cast(bf16x8_t, av & kAbs2), __builtin_bit_cast(bf16x8_t, xv & kAbs2),
-                  msacc[rb][h], 0, 0, 0);
+            mc(rb, h) = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                __builtin_bit_cast(bf16x8_t, av), bv, mc(rb, h), 0, 0, 0);
+          }
+        }
+        if constexpr (kWn) {
+#pragma unroll
+          for (int rb = 0; rb < RBW; ++rb) {
+            const u32x4 av = {P[rb][4 * j], P[rb][4 * j + 1], P[rb][4 * j + 2], P[rb][4 * j + 3]};
+            nacc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                __builtin_bit_cast(bf16x8_t, av), __builtin_bit_cast(bf16x8_t, av), nacc[rb], 0, 0, 0);
           }
         }
       } else {
@@ -509,14 +534,27 @@ __global__ __launch_bounds__(NWV * 64) void k_gemm(
           for (int rb = 0; rb < RBW; ++rb)
 #pragma unroll
             for (int pp = 0; pp < 4; ++pp) {
-              vacc[rb][m] = __builtin_amdgcn_fdot2_f32_bf16(
-                  as_bf16x2(P[rb][4 * j + pp]), as_bf16x2(xv[pp]), vacc[rb][m], false);
-              if constexpr (kS)
-                vsacc[rb][m] = __builtin_amdgcn_fdot2_f32_bf16(
-                    as_bf16x2(P[rb][4 * j + pp] & 0x7FFF7FFFu), as_bf16x2(xv[pp] & 0x7FFF7FFFu),
-                    vsacc[rb][m], false);
+              vc(rb, m) = __builtin_amdgcn_fdot2_f32_bf16(
+                  as_bf16x2(P[rb][4 * j + pp]), as_bf16x2(xv[pp]), vc(rb, m), false);
             }
         }
+        if constexpr (kWn) {
+#pragma unroll
+          for (int rb = 0; rb < RBW; ++rb)
+#pragma unroll
+            for (int pp = 0; pp < 4; ++pp)
+              wsq[rb] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(P[rb][4 * j + pp]),
+                                                        as_bf16x2(P[rb][4 * j + pp]), wsq[rb], false);
+        }
+      }
+    }
+    if constexpr (kWn) {
+#pragma unroll
+      for (int rb = 0; rb < RBW; ++rb) {
+#pragma unroll
+        for (int h = 0; h < NH; ++h) macc[rb][h] += mcol[rb][h];
+#pragma unroll
+        for (int m = 0; m < (MF ? 1 : M); ++m) vacc[rb][m] += vcol[rb][m];
       }
     }
     if constexpr (!plain_bf16(SRC)) {
@@ -610,11 +648,11 @@ __global__ __launch_bounds__(NWV * 64) void k_gemm(
   if (EPI == EPI_BF16 && p.rms && gridDim.y > 1 && tid < M && (uint32_t)tid < m_rows)
     st_dev(ssrs, ((blockIdx.x * gridDim.y + blockIdx.y) * m_rows + tid) * 4u, row_ss(tid));
 
-  // ---- cross-lane / cross-wave reduction into red[] (aliases xs); the S sums, when
-  // kept, go to a second region of the same size
+  // ---- cross-lane / cross-wave reduction into red[] (aliases xs); the row sums of
+  // squares, when kept, follow as [wave][rb][row]
   float* red = reinterpret_cast<float*>(xs);
   constexpr int kRed = MF ? NWV * RBW * NH * 4 * 64 : NWV * RBW * M * 16;
-  static_assert((kS ? 2 : 1) * kRed * sizeof(float) <= sizeof(xs), "reduction fits in xs");
+  static_assert((kRed + (kWn ? NWV * RBW * 16 : 0)) * sizeof(float) <= sizeof(xs), "reduction fits in xs");
   auto to_red = [&](float* dst, float (*va)[MF ? 1 : M], f32x4 (*ma)[NH]) {
     if constexpr (MF) {
 #pragma unroll
@@ -637,7 +675,23 @@ __global__ __launch_bounds__(NWV * 64) void k_gemm(
     }
   };
   to_red(red, vacc, macc);
-  if constexpr (kS) to_red(red + kRed, vsacc, msacc);
+  if constexpr (kWn) {
+#pragma unroll
+    for (int rb = 0; rb < RBW; ++rb) {
+      float* dst = red + kRed + (wave * RBW + rb) * 16;
+      if constexpr (MF) {
+        // D[c][c] sits in lane c + 16 (c / 4), element c % 4
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (r == 4 * q + i) dst[r] = nacc[rb][i];
+      } else {
+        float v = wsq[rb];
+        v += __shfl_xor(v, 16);
+        v += __shfl_xor(v, 32);
+        if (q == 0) dst[r] = v;
+      }
+    }
+  }
   __syncthreads();
 
   constexpr int kOut = RBW * MT * 16;   // (rb, m, row) outputs of this workgroup
@@ -657,30 +711,34 @@ __global__ __launch_bounds__(NWV * 64) void k_gemm(
   };
 
   if constexpr (EPI == EPI_LOGITS) {
-    for (int o = tid; o < kOut; o += (NWV * 64)) {
-      const int rb = o / (MT * 16), rem = o % (MT * 16), m = rem >> 4, rr = rem & 15;
-      const uint32_t b = b0 + rb;
-      const float v = final_value(red, o), sv = final_value(red + kRed, o);
-      fin[o] = v;
-      fin_s[o] = sv;
-      if (out_f32 && b < p.nb && (uint32_t)m < m_rows) {   // full logits only when asked for
-        out_f32[(size_t)m * p.n + 16u * b + rr] = v;
-        out_s[(size_t)m * p.n + 16u * b + rr] = sv;
+    if (tid < RBW * 16) {   // the waves' partial sums of squares in wave order
+      float t = 0.f;
+#pragma unroll
+      for (int wv = 0; wv < NWV; ++wv) t += red[kRed + (wv * RBW + (tid >> 4)) * 16 + (tid & 15)];
+      s_wn[tid] = l2_norm_up(t, p.k);
+    }
+    for (int o = tid; o < kOut; o += (NWV * 64)) fin[o] = final_value(red, o);
+    __syncthreads();
+    if (out_f32) {   // full logits and norms only when asked for
+      for (int o = tid; o < kOut; o += (NWV * 64)) {
+        const int rb = o / (MT * 16), rem = o % (MT * 16), m = rem >> 4, rr = rem & 15;
+        const uint32_t b = b0 + rb;
+        if (b >= p.nb || (uint32_t)m >= m_rows) continue;
+        out_f32[(size_t)m * p.n + 16u * b + rr] = fin[o];
+        out_s[(size_t)m * p.n + 16u * b + rr] = s_wn[rb * 16 + rr];
       }
     }
-    __syncthreads();
     if (bm.accepted && blockIdx.x == 0 && blockIdx.y == 0)
       accept_init(bm, p.m, (uint32_t)tid, NWV * 64u);   // verification pass 2 lowers them
     // per (row-block, output row) records, kept in LDS for the workgroup's group record
-    __shared__ float s_gv[RBW][MT], s_gs[RBW][MT], s_gu[RBW][MT];
+    __shared__ float s_gv[RBW][MT], s_gs[RBW][MT];
     __shared__ int32_t s_gi[RBW][MT];
-    const double c1 = bound_slope(p.k);
     for (int o = tid; o < RBW * MT; o += (NWV * 64)) {
       const int rb = o / MT, m = o % MT;
       const uint32_t b = b0 + rb;
       const bool live = b < p.nb && (uint32_t)m < m_rows;
       // largest (lowest row on ties) and second largest logit of the block
-      float best = fin[o * 16], second = -__builtin_inff(), smax = fin_s[o * 16];
+      float best = fin[o * 16], second = -__builtin_inff(), smax = s_wn[rb * 16];
       int bi = 0;
       bool finite = __builtin_isfinite(best);
       for (int rr = 1; rr < 16; ++rr) {
@@ -688,14 +746,11 @@ __global__ __launch_bounds__(NWV * 64) void k_gemm(
         finite = finite && __builtin_isfinite(v);
         if (v > best) { second = best; best = v; bi = rr; }
         else if (v > second) second = v;
-        smax = fmaxf(smax, fin_s[o * 16 + rr]);
+        smax = fmaxf(smax, s_wn[rb * 16 + rr]);
       }
       s_gv[rb][m] = !live ? -__builtin_inff() : (finite ? best : __builtin_nanf(""));
       s_gi[rb][m] = (int32_t)(16u * b + bi);
-      s_gs[rb][m] = smax;
-      s_gu[rb][m] = !live ? -__builtin_inff()
-                          : (finite ? f32_round_up((double)best + c1 * (double)smax)
-                                    : __builtin_nanf(""));
+      s_gs[rb][m] = live ? smax : 0.f;
       if (!live) continue;
       bm.v[(size_t)m * p.nb + b] = finite ? best : __builtin_nanf("");
       bm.v2[(size_t)m * p.nb + b] = finite ? second : __builtin_nanf("");
@@ -704,21 +759,21 @@ __global__ __launch_bounds__(NWV * 64) void k_gemm(
     }
     __syncthreads();
     if ((uint32_t)tid < MT && (uint32_t)tid < m_rows) {
-      float v = s_gv[0][tid], u = s_gu[0][tid], sv = s_gs[0][tid];
+      float v = s_gv[0][tid], sv = s_gs[0][tid], wg = s_gs[0][tid];
       int32_t vi = s_gi[0][tid];
-      bool nan = v != v || u != u;
+      bool nan = v != v;
 #pragma unroll
       for (int rb = 1; rb < RBW; ++rb) {
-        const float vw = s_gv[rb][tid], uw = s_gu[rb][tid];
-        nan = nan || vw != vw || uw != uw;
+        const float vw = s_gv[rb][tid];
+        nan = nan || vw != vw;
         if (vw > v) { v = vw; vi = s_gi[rb][tid]; sv = s_gs[rb][tid]; }   // ties: the lower row-block
-        u = fmaxf(u, uw);
+        wg = fmaxf(wg, s_gs[rb][tid]);
       }
       const size_t og = (size_t)tid * bm.ngrp + blockIdx.x;
       bm.gv[og] = nan ? __builtin_nanf("") : v;
       bm.gi[og] = vi;
       bm.gs[og] = sv;
-      bm.gu[og] = nan ? __builtin_nanf("") : u;
+      bm.gw[og] = wg;
     }
   } else {
     auto store_y = [&](int rb, int m, int rr, float v, float ss) {
@@ -784,7 +839,13 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_cs(
     BlockMax bm,
     GemmParams p) {
   constexpr int NH = MT / 16;
-  constexpr bool kS = EPI == EPI_LOGITS;   // also accumulate S = sum |x||w| per output
+  // The logits epilogue records, per weight row, an upper bound of ||w_v||_2 (the error
+  // scale is ||x||_2 ||w_v||_2 >= sum_k |x_k||w_vk| by Cauchy-Schwarz, and verification
+  // pass 2 supplies ||x||_2).  The squares are summed by an MFMA of the A operand with
+  // itself (its diagonal): one per 32 columns, whatever the number of x columns, where
+  // a second MFMA on sign-cleared operands took one per x column block, and no x norms
+  // here (summing them in every workgroup cost more than the rest of the bound).
+  constexpr bool kWn = EPI == EPI_LOGITS;
   constexpr int NT = NW * 64;
   constexpr int kUnits = (16 * MT + NT - 1) / NT;     // 16-byte x units per thread
   constexpr int kXs = xs_stride(MT);
@@ -803,9 +864,10 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_cs(
   const uint32_t gb = (uint32_t)(((uint64_t)(split + 1u) * p.g_cols) / gridDim.y);
   const uint32_t m_rows = p.m;
 
-  f32x4 acc[NH], sacc[NH];
+  f32x4 acc[NH];
 #pragma unroll
-  for (int h = 0; h < NH; ++h) acc[h] = sacc[h] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int h = 0; h < NH; ++h) acc[h] = f32x4{0.f, 0.f, 0.f, 0.f};
+  f32x4 nacc = {0.f, 0.f, 0.f, 0.f};   // kWn: D = W W^T over the K-range, diagonal used
   TileRegs<SRC> tA, tB;
   u32x4 xr[kUnits];
   EscCursor ec;
@@ -864,18 +926,31 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_cs(
       if (bvalid) esc_apply(ec, sv.esc, g, lane, P);
     }
     const uint16_t* xrow = &xs[g & 1u][8 * q];
+    // logits: the column's 4 MFMAs chain from zero and the column sum is added to the
+    // running sum, so a product meets at most 4 MFMA accumulations (whatever their
+    // internal order) and one addition per later column: the certified bound's depth
+    f32x4 col[NH];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const u32x4 av = {P[4 * j], P[4 * j + 1], P[4 * j + 2], P[4 * j + 3]};
 #pragma unroll
       for (int h = 0; h < NH; ++h) {
         const u32x4 xv = *reinterpret_cast<const u32x4*>(xrow + (16 * h + r) * kXs + 32 * j);
-        acc[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av),
-                                                         __builtin_bit_cast(bf16x8_t, xv), acc[h], 0, 0, 0);
-        if constexpr (kS)
-          sacc[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av & kAbs2),
-                                                            __builtin_bit_cast(bf16x8_t, xv & kAbs2),
-                                                            sacc[h], 0, 0, 0);
+        f32x4& c = kWn ? col[h] : acc[h];
+        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av), __builtin_bit_cast(bf16x8_t, xv),
+                                                    (kWn && j == 0) ? f32x4{0.f, 0.f, 0.f, 0.f} : c, 0, 0, 0);
+      }
+    }
+    if constexpr (kWn) {
+#pragma unroll
+      for (int h = 0; h < NH; ++h) acc[h] += col[h];
+    }
+    if constexpr (kWn) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const u32x4 av = {P[4 * j], P[4 * j + 1], P[4 * j + 2], P[4 * j + 3]};
+        nacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av),
+                                                       __builtin_bit_cast(bf16x8_t, av), nacc, 0, 0, 0);
       }
     }
     if constexpr (!plain_bf16(SRC)) {
@@ -969,15 +1044,22 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_cs(
     if (bm.accepted && blockIdx.x == 0 && blockIdx.y == 0)
       accept_init(bm, p.m, (uint32_t)tid, NT);   // verification pass 2 lowers them
     // the workgroup's group record per output row: its waves' row-blocks in order
-    __shared__ float s_gv[NW][MT], s_gs[NW][MT], s_gu[NW][MT];
+    __shared__ float s_gv[NW][MT], s_gs[NW][MT];
     __shared__ int32_t s_gi[NW][MT];
-    const double c1 = bound_slope(p.k);
+    // ||w_v||_2 bounds of the lane's rows 4q+i: D[c][c] sits in lane c + 16 (c / 4),
+    // element c % 4
+    f32x4 wn;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) wn[i] = l2_norm_up(__shfl(nacc[i], 20 * q + i), p.k);
+    float wmax = fmaxf(fmaxf(wn[0], wn[1]), fmaxf(wn[2], wn[3]));
+    wmax = fmaxf(wmax, __shfl_xor(wmax, 16));
+    wmax = fmaxf(wmax, __shfl_xor(wmax, 32));   // the row-block's largest
 #pragma unroll
     for (int h = 0; h < NH; ++h) {
       const uint32_t m = 16u * h + (uint32_t)r;
       // largest (lowest row on ties) and second largest of this lane's 4 rows;
       // non-finite poisons the block
-      float best = acc[h][0], second = -__builtin_inff(), smax = sacc[h][0];
+      float best = acc[h][0], second = -__builtin_inff();
       int bi = 0;
       bool finite = __builtin_isfinite(acc[h][0]);
 #pragma unroll
@@ -985,7 +1067,6 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_cs(
         finite = finite && __builtin_isfinite(acc[h][i]);
         if (acc[h][i] > best) { second = best; best = acc[h][i]; bi = i; }
         else if (acc[h][i] > second) second = acc[h][i];
-        smax = fmaxf(smax, sacc[h][i]);
       }
       int row = 4 * q + bi;
       // merge with the lanes holding the block's other rows: the better first wins,
@@ -996,7 +1077,6 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_cs(
         const float o2 = __shfl_xor(second, off);
         const int orow = __shfl_xor(row, off);
         const int ofin = __shfl_xor((int)finite, off);
-        smax = fmaxf(smax, __shfl_xor(smax, off));
         finite = finite && ofin;
         if (ob > best || (ob == best && orow < row)) {
           second = fmaxf(o2, best);
@@ -1007,14 +1087,14 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_cs(
         }
       }
       if (m < m_rows && bvalid) {
-        if (out_f32) {   // full logits and S only when asked for (verification needs the maxima)
+        if (out_f32) {   // full logits and norms only when asked for (verification needs the maxima)
           *reinterpret_cast<f32x4*>(out_f32 + (size_t)m * p.n + n0) = acc[h];
-          *reinterpret_cast<f32x4*>(out_s + (size_t)m * p.n + n0) = sacc[h];
+          *reinterpret_cast<f32x4*>(out_s + (size_t)m * p.n + n0) = wn;
         }
         if (q == 0) {
           bm.v[(size_t)m * p.nb + b] = finite ? best : __builtin_nanf("");
           bm.v2[(size_t)m * p.nb + b] = finite ? second : __builtin_nanf("");
-          bm.s[(size_t)m * p.nb + b] = smax;
+          bm.s[(size_t)m * p.nb + b] = wmax;
           bm.i[(size_t)m * p.nb + b] = (int32_t)(16u * b + row);
         }
       }
@@ -1022,29 +1102,26 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_cs(
         const bool live = bvalid && m < m_rows;
         s_gv[wave][m] = !live ? -__builtin_inff() : (finite ? best : __builtin_nanf(""));
         s_gi[wave][m] = (int32_t)(16u * b + row);
-        s_gs[wave][m] = smax;
-        s_gu[wave][m] = !live ? -__builtin_inff()
-                              : (finite ? f32_round_up((double)best + c1 * (double)smax)
-                                        : __builtin_nanf(""));
+        s_gs[wave][m] = live ? wmax : 0.f;
       }
     }
     __syncthreads();
     if ((uint32_t)tid < MT && (uint32_t)tid < m_rows) {
-      float v = s_gv[0][tid], u = s_gu[0][tid], sv = s_gs[0][tid];
+      float v = s_gv[0][tid], sv = s_gs[0][tid], wg = s_gs[0][tid];
       int32_t vi = s_gi[0][tid];
-      bool nan = v != v || u != u;
+      bool nan = v != v;
 #pragma unroll
       for (int w = 1; w < NW; ++w) {
-        const float vw = s_gv[w][tid], uw = s_gu[w][tid];
-        nan = nan || vw != vw || uw != uw;
+        const float vw = s_gv[w][tid];
+        nan = nan || vw != vw;
         if (vw > v) { v = vw; vi = s_gi[w][tid]; sv = s_gs[w][tid]; }   // ties: the lower row-block
-        u = fmaxf(u, uw);
+        wg = fmaxf(wg, s_gs[w][tid]);
       }
       const size_t o = (size_t)tid * bm.ngrp + blockIdx.x;
       bm.gv[o] = nan ? __builtin_nanf("") : v;
       bm.gi[o] = vi;
       bm.gs[o] = sv;
-      bm.gu[o] = nan ? __builtin_nanf("") : u;
+      bm.gw[o] = wg;
     }
   } else {
     auto store_y = [&](uint32_t m, f32x4 v, float ss) {

@@ -63,13 +63,19 @@ struct GemmParams {
   Seg seg[kMaxSeg];
 };
 
-// Slope of the certified bound on an FP32 logit computed in any summation order,
-// B(S^) = c1 S^ + c0 (derivation in w12_verify.hip): each of the K products passes
-// through at most D = K + 64 additions with relative error below 2^-23, g = D 2^-23 /
-// (1 - D 2^-23), c1 = g / (1 - g), inflated by 2^-20 for its FP64 evaluation.  Pass 1
-// and pass 2 evaluate it with the same operations.
+// Depth of the certified bound on an FP32 logit of verification pass 1 (derivation in
+// w12_verify.hip): the logits kernels sum each 128-column tile column from zero, 4 MFMAs
+// or 16 v_dot2 in a chain, then add it to the running sum.  Whatever order the hardware
+// adds inside one instruction (not documented), a value entering an MFMA meets at most
+// 32 roundings in it and one entering a v_dot2 at most 2, so a product meets at most 128
+// within its column, then one addition per column (K/128 of them), then at most 64 in
+// the cross-lane and cross-wave sums: D = K/128 + 192.
+__host__ __device__ inline double bound_depth(uint32_t k) { return (double)(k / 128u) + 192.0; }
+
+// Slope of that bound, B(S) = c1 S + c0: g = D 2^-23 / (1 - D 2^-23), c1 = g / (1 - g),
+// inflated by 2^-20 for its FP64 evaluation.
 __host__ __device__ inline double bound_slope(uint32_t k) {
-  const double dd = (double)k + 64.0;
+  const double dd = bound_depth(k);
   const double gam = dd * 0x1p-23 / (1.0 - dd * 0x1p-23);
   return gam / (1.0 - gam) * (1.0 + 0x1p-20);
 }
@@ -87,18 +93,35 @@ __device__ inline float f32_round_up(double d) {
   return f;
 }
 
+// FP32 upper bound of the 2-norm of K BF16 values from the FP32 sum of their squares in
+// any order: a square is exact unless it falls below 2^-126, each term passes through at
+// most D = K + 64 additions with relative error below 2^-23, and flushes below 2^-126
+// (squares and partial sums, 2D of them) lose less than 2^-126 each.
+__device__ inline float l2_norm_up(float sumsq, uint32_t k) {
+  const double dd = (double)k + 64.0;
+  const double gam = dd * 0x1p-23 / (1.0 - dd * 0x1p-23);
+  const double t = ((double)sumsq + 2.0 * dd * 0x1p-126) * (1.0 + 2.0 * gam);
+  return f32_round_up(sqrt(t) * (1.0 + 0x1p-50));
+}
+
+// FP64 upper bound of ||x||_2 from the FP64 sum of the exact squares of K < 2^20 BF16
+// values in any order (relative error below K 2^-53 < 2^-33, and sqrt and the product
+// add below 2^-52).
+__device__ inline double x_norm_up(double sumsq) {
+  return sqrt(sumsq * (1.0 + 0x1p-30)) * (1.0 + 0x1p-50);
+}
+
 // Per-row-block records of the logits epilogue (verification pass 1), [m][nb] each, and
 // one record per workgroup ("group": its consecutive row-blocks), [m][ngrp] each.
 struct BlockMax {
   float* v;                 // largest logit of the row-block (NaN if any is not finite)
   float* v2;                // second largest (equal to v on a tie)
-  float* s;                 // largest sum_k |x_k||w_k| of the row-block
+  float* s;                 // largest FP32 upper bound of ||w_v||_2 over the row-block
   int32_t* i;               // index of v, lowest on ties
   float* gv;                // group: largest logit (NaN if any of its logits is not finite)
   int32_t* gi;              // group: index of gv, lowest on ties
   float* gs;                // group: s of the row-block holding gv
-  float* gu;                // group: an FP32 upper bound of v + bound_slope(k) * s over its
-                            // row-blocks (NaN if any logit is not finite)
+  float* gw;                // group: largest s over its row-blocks
   uint32_t ngrp;            // groups per row (the grid's row-block groups)
   int32_t* accepted;        // [n_req]: set by the first workgroup (NULL: untouched)
   uint32_t n_draft;         // one request over all rows (req_off NULL): its draft length
@@ -131,7 +154,7 @@ __device__ __forceinline__ void accept_init(const BlockMax& bm, uint32_t m, uint
 struct GemmArgs {
   const uint16_t* x;        // [m][k] BF16
   float* logits;            // [m][n] (EPI_LOGITS; NULL: not written)
-  float* sabs;              // [m][n] sum_k |x_k||w_k| per logit (with logits)
+  float* sabs;              // [m][n] with logits: the row norm bound W_v in every row
   BlockMax bm;              // EPI_LOGITS
   float* partial;           // [nsplit][m][n] split-K partial sums (launch numbering)
   GemmParams p;
@@ -205,7 +228,7 @@ struct VerifyArgs {
   const float* grp_v;       // [m][ngrp] group records of pass 1
   const int32_t* grp_i;
   const float* grp_s;
-  const float* grp_u;
+  const float* grp_w;
   uint32_t ngrp, bpg;       // groups per row, row-blocks per group (<= kMaxBpg)
   int32_t* cand;            // [m][n] candidate logits
   int32_t* argmax;          // [m]
@@ -221,6 +244,9 @@ struct VerifyArgs {
   uint32_t lut[4];
 };
 hipError_t launch_verify_pass2(const VerifyArgs& a, hipStream_t s);
+// s [m][n]: row norms W_v in every row -> X_m W_v (the first pass's full output)
+hipError_t launch_scale_norms(const uint16_t* x, uint32_t m, uint32_t k, float* s, uint32_t n,
+                              hipStream_t st);
 
 // Two-level verification (w12_screen.hip): the screen copy of the head (8-bit codes, a
 // BF16 scale per 32 columns) and its two passes.

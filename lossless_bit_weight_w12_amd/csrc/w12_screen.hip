@@ -285,18 +285,13 @@ __global__ __launch_bounds__(kScreenNW * 64) void k_screen(ScreenArgs a) {
   if (a.acc.accepted && blockIdx.x == 0) accept_init(a.acc, m_rows, (uint32_t)tid, NT);
   __syncthreads();
 
-  // X >= ||x||_2: the FP32 sum of K exact squares has at most D additions, relative error
-  // below gamma, and flushes below 2^-126 (squares and partial sums: 2D terms)
-  const double dd = (double)a.k + 64.0;
-  const double gam = dd * 0x1p-23 / (1.0 - dd * 0x1p-23);
   const uint32_t v0 = 16u * bl + 4u * (uint32_t)q;
   const f32x4 cc = *reinterpret_cast<const f32x4*>(a.coef + v0);
   const f32x4 aa = *reinterpret_cast<const f32x4*>(a.abse + v0);
 #pragma unroll
   for (int h = 0; h < NH; ++h) {
     const uint32_t m = 16u * h + (uint32_t)r;
-    const double ssd = ((double)s_ss[m] + 2.0 * dd * 0x1p-126) * (1.0 + 2.0 * gam);
-    const float X = f32_round_up(sqrt(ssd) * (1.0 + 0x1p-50));
+    const float X = l2_norm_up(s_ss[m], a.k);   // >= ||x||_2
     float hi[4], lo[4], bf[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {

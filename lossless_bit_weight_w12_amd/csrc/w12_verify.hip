@@ -3,28 +3,32 @@
 //
 // Pass 1 (the GEMM kernel family with the logits epilogue) leaves, per row and per
 // 16-row block of the head, the largest FP32 logit z^ (with its index), the second
-// largest, and the largest S^ = the same kernel's FP32 sum of |x_k||w_vk| over the
-// block's rows; and per workgroup of pass 1 (a group of consecutive row-blocks) the
-// group's largest logit, its index and block's S^, and an FP32 upper bound U of
-// z^_b + c1 S^_b over its row-blocks.  Pass 2 (one workgroup per row):
-//   1. z* = max z^ over the group records (lowest index on ties), S* the largest S^ of
-//      its block (an upper bound of its own S^);
+// largest, and W_b = the largest FP32 upper bound of ||w_v||_2 over the block's rows
+// (the same kernel sums the squares of the weights it streams); and per workgroup of
+// pass 1 (a group of consecutive row-blocks) the group's largest logit, its index, that
+// block's W_b, and the group's largest W_b.  Pass 2 (one workgroup per row):
+//   1. z* = max z^ over the group records (lowest index on ties), W* the W_b of its
+//      block; X >= ||x||_2 from the FP64 sum of the exact squares of x;
 //   2. the error bound.  A product of two BF16 values is exact in FP32 unless it
-//      underflows.  Whatever the summation order, each of the K products of a logit
-//      passes through at most D = K + 64 additions (the slack covers the accumulators'
-//      zero starts and the cross-wave sums), each with relative error below
-//      eps = 2^-23 (round-to-nearest or toward zero), so with g = D eps / (1 - D eps)
-//        |z^ - z| <= g S + A,   S = sum_k |x_k w_k|,
-//      A = D 2^-126 (1 + Xmax + Wmax) covering flushed denormal inputs, products and
-//      partial sums (Xmax = max |x_k|, Wmax = 2^(e_max-126) > |w|).  S^ sums the same
-//      nonnegative terms, so S <= S^/(1-g) + A, and B(S^) = g (S^/(1-g) + A) + A,
-//      inflated by 2^-20 for its FP64 evaluation, bounds |z^ - z|: B = c1 S^ + c0 with
-//      c1 = bound_slope(K).  B grows with S^;
-//   3. L = z* - B(S*) is below the true maximum, so every v with z^_v + B(S^_v) >= L
-//      is a candidate (the exact argmax always is).  A group whose U + c0 is below L
-//      holds none; in the others, with the block's largest S^ in B, a block adds its
-//      largest logit when that reaches L, and all of its rows when its second largest
-//      does too (otherwise no other row of it can);
+//      underflows.  Each of the K products of a logit passes through at most
+//      D = bound_depth(K) = K/128 + 192 additions (pass 1 sums every tile column from
+//      zero and then adds it to the running sum, so the undocumented order inside an
+//      MFMA costs at most 32 roundings per instruction of the column's chain of 4),
+//      each with relative error below eps = 2^-23 (round-to-nearest or toward zero), so
+//      with g = D eps / (1 - D eps)
+//        |z^ - z| <= g S + A,   S = sum_k |x_k w_k| <= ||x||_2 ||w_v||_2 <= X W_v
+//      (Cauchy-Schwarz), A = (2K + D) 2^-126 (1 + Xmax + Wmax) covering flushed denormal
+//      inputs and products (K terms) and partial sums (at most K + D additions), each
+//      losing less than 2^-126 (1 + Xmax + Wmax) (Xmax = max |x_k|,
+//      Wmax = 2^(e_max-126) > |w|).
+//      B(S') = c1 S' + c0 with c1 = bound_slope(K) >= g and c0 = (g A + A) 2^-20-inflated
+//      is at least g S + A for any S' >= S, the inflation covering its FP64 evaluation;
+//      S' = X W_b for a row of block b;
+//   3. L = z* - B(X W*) is below the true maximum, so every v with z^_v + B(X W_v) >= L
+//      is a candidate (the exact argmax always is).  A group whose largest logit plus
+//      B(X times its largest W_b) is below L holds none; in the others, with W_b in B,
+//      a block adds its largest logit when that reaches L, and all of its rows when its
+//      second largest does too (otherwise no other row of it can);
 //   4. a single candidate is the argmax.  Otherwise the FP64 screen: each candidate's
 //      logit is recomputed from the W12 tiles in FP64 (a
 //      BF16 product is exact in FP64; escape corrections add two terms each), within
@@ -56,10 +60,10 @@ constexpr uint32_t kT = 512;           // threads of the pass-2 workgroup (one w
 constexpr uint32_t kWaves = kT / 64u;
 static_assert(kWaves == kExactWaves, "the exact stage runs one wave per candidate");
 constexpr uint32_t kScreenMax = 512;   // candidates screened per chunk (ids and results in LDS)
-constexpr uint32_t kUCache = 8192;     // group upper bounds kept in LDS for the group scan
+constexpr uint32_t kGCache = 6144;     // group records (largest logit, norm) kept in LDS for the scan
 
 __global__ __launch_bounds__(kT) void k_verify_pass2(VerifyArgs a) {
-  __shared__ float s_u[kUCache];
+  __shared__ float s_gvc[kGCache], s_gwc[kGCache];
   __shared__ int32_t s_cand[kScreenMax];   // the first candidates (the rest in global memory)
   __shared__ uint32_t s_ce0[kScreenMax], s_ce1[kScreenMax];   // their escape ranges
   __shared__ int32_t s_chunk[kScreenMax];  // ids of the chunk being screened
@@ -78,7 +82,7 @@ __global__ __launch_bounds__(kT) void k_verify_pass2(VerifyArgs a) {
   const float* gv = a.grp_v + (uint64_t)row * a.ngrp;
   const int32_t* gi = a.grp_i + (uint64_t)row * a.ngrp;
   const float* gs = a.grp_s + (uint64_t)row * a.ngrp;
-  const float* gu = a.grp_u + (uint64_t)row * a.ngrp;
+  const float* gw = a.grp_w + (uint64_t)row * a.ngrp;
   const float* rv = a.rbmax_v + (uint64_t)row * a.nb;
   const float* rv2 = a.rbmax_v2 + (uint64_t)row * a.nb;
   const float* rs = a.rbmax_s + (uint64_t)row * a.nb;
@@ -92,21 +96,22 @@ __global__ __launch_bounds__(kT) void k_verify_pass2(VerifyArgs a) {
   uint32_t ncand = 0, nsurv = 0;
   if (tid == 0) { s_cnt = 0; s_bad = 0; s_result = -1; }
 
-  // 1. z*, its index and S* over the group records (NaN marks a group with a non-finite
-  // logit); the upper bounds U stay in LDS for the scan.  Every scan issues all of a
-  // thread's loads of a chunk (clamped indices) before using any; the result does not
-  // depend on the order (largest value, lowest index on ties).
+  // 1. z*, its index and W* over the group records (NaN marks a group with a non-finite
+  // logit), which stay in LDS for the scan, and Xmax, ||x||_2^2 and the finiteness of x.
+  // Every scan issues all of a thread's loads of a chunk (clamped indices) before using
+  // any; the result does not depend on the order (largest value, lowest index on ties).
   float bv = -__builtin_inff(), bs = 0.f;
   int32_t bi = 0x7FFFFFFF;
   bool bad = false;
-  double xm = 0.0;   // Xmax (and finiteness of x), eight BF16 per load (k is a multiple of 128)
+  double xm = 0.0;    // Xmax, eight BF16 per load (k is a multiple of 128)
+  double ssx = 0.0;   // sum of x_k^2 (each square exact in FP64)
   {
-    constexpr uint32_t kU = 4, kXU = 2;
+    constexpr uint32_t kU = 8, kXU = 2;
     const uint32_t nx = a.k / 8u;
     const uint32_t rounds = max((a.ngrp + kT * kU - 1) / (kT * kU), (nx + kT * kXU - 1) / (kT * kXU));
     for (uint32_t rd = 0; rd < rounds; ++rd) {
       const uint32_t base = rd * kT * kU, xbase = rd * kT * kXU;
-      float v[kU], s[kU], u[kU];
+      float v[kU], s[kU], u[kU];   // largest logit, its block's norm, the group's largest norm
       int32_t iv[kU];
       u32x4 xv[kXU];
 #pragma unroll
@@ -114,18 +119,20 @@ __global__ __launch_bounds__(kT) void k_verify_pass2(VerifyArgs a) {
         xv[q] = reinterpret_cast<const u32x4*>(xr)[min(xbase + q * kT + tid, nx - 1u)];
 #pragma unroll
       for (uint32_t q = 0; q < kU; ++q) {
-        const uint32_t G = min(base + q * kT + tid, a.ngrp - 1u);
-        v[q] = gv[G];
-        iv[q] = gi[G];
-        s[q] = gs[G];
-        u[q] = gu[G];
+        const uint32_t G = base + q * kT + tid;
+        if (G < a.ngrp) {   // (uniform over a wave but the last: no duplicate loads)
+          v[q] = gv[G];
+          iv[q] = gi[G];
+          s[q] = gs[G];
+          u[q] = gw[G];
+        }
       }
 #pragma unroll
       for (uint32_t q = 0; q < kU; ++q) {
         const uint32_t G = base + q * kT + tid;
         if (G >= a.ngrp) continue;
-        if (G < kUCache) s_u[G] = u[q];
-        if (v[q] != v[q] || u[q] != u[q]) bad = true;
+        if (G < kGCache) { s_gvc[G] = v[q]; s_gwc[G] = u[q]; }
+        if (v[q] != v[q]) bad = true;
         else if (v[q] > bv || (v[q] == bv && iv[q] < bi)) { bv = v[q]; bi = iv[q]; bs = s[q]; }
       }
 #pragma unroll
@@ -135,7 +142,9 @@ __global__ __launch_bounds__(kT) void k_verify_pass2(VerifyArgs a) {
         for (uint32_t h = 0; h < 8; ++h) {
           const uint32_t bits = (xv[q][h >> 1] >> (16u * (h & 1u))) & 0xFFFFu;
           if (((bits >> 7) & 0xFFu) == 0xFFu) bad = true;
-          xm = fmax(xm, fabs((double)__uint_as_float(bits << 16)));
+          const double xv64 = (double)__uint_as_float(bits << 16);
+          xm = fmax(xm, fabs(xv64));
+          ssx += xv64 * xv64;
         }
       }
     }
@@ -148,35 +157,40 @@ __global__ __launch_bounds__(kT) void k_verify_pass2(VerifyArgs a) {
     const int32_t i2 = __shfl_xor(bi, off);
     if (v2 > bv || (v2 == bv && i2 < bi)) { bv = v2; bi = i2; bs = s2; }
     xm = fmax(xm, __shfl_xor(xm, off));
+    ssx += __shfl_xor(ssx, off);
   }
   __syncthreads();   // s_cnt, s_bad initialised
   if (bad) atomicOr(&s_bad, 1u);
-  if (lane == 0) { s_wv[wave] = bv; s_wi[wave] = bi; s_ws[wave] = bs; s_d0[wave] = xm; }
+  if (lane == 0) { s_wv[wave] = bv; s_wi[wave] = bi; s_ws[wave] = bs; s_d0[wave] = xm; s_d1[wave] = ssx; }
   __syncthreads();
   bv = s_wv[0];
   bi = s_wi[0];
   bs = s_ws[0];
   xm = s_d0[0];
+  ssx = s_d1[0];
   for (uint32_t w = 1; w < kWaves; ++w) {
     if (s_wv[w] > bv || (s_wv[w] == bv && s_wi[w] < bi)) { bv = s_wv[w]; bi = s_wi[w]; bs = s_ws[w]; }
     xm = fmax(xm, s_d0[w]);
+    ssx += s_d1[w];
   }
   const float zmax = bv;
-  const double dd = (double)a.k + 64.0;
+  const double dd = bound_depth(a.k);
   const double gam = dd * ldexp(1.0, -23) / (1.0 - dd * ldexp(1.0, -23));
   const double wmax = ldexp(1.0, (int)a.e_max - 126);
-  const double absb = dd * ldexp(1.0, -126) * (1.0 + xm + wmax);
+  const double absb = (2.0 * (double)a.k + dd) * ldexp(1.0, -126) * (1.0 + xm + wmax);
   const double infl = 1.0 + ldexp(1.0, -20);
   const double c1 = bound_slope(a.k), c0 = (gam * absb + absb) * infl;
-  const double lo = (double)zmax - (c1 * (double)bs + c0);
+  const double xn = x_norm_up(ssx);   // >= ||x||_2: the scale of row v is xn * W_v
+  const double lo = (double)zmax - (c1 * (xn * (double)bs) + c0);
   const bool row_ok = !s_bad && __builtin_isfinite(zmax) && lo == lo;
   const bool zero_row = row_ok && xm == 0.0;   // every product is +-0: every logit is 0
   if (row_ok && !zero_row) {
     // 2. candidates from the groups whose bound reaches L: a block's largest logit, and
     // all its rows when its second largest also reaches L
     for (uint32_t G = tid; G < a.ngrp; G += kT) {
-      const float u = G < kUCache ? s_u[G] : gu[G];
-      if ((double)u + c0 < lo) continue;
+      const float gzv = G < kGCache ? s_gvc[G] : gv[G];
+      const float gwv = G < kGCache ? s_gwc[G] : gw[G];
+      if ((double)gzv + c1 * (xn * (double)gwv) + c0 < lo) continue;   // none of its rows reaches L
       const uint32_t b0 = G * a.bpg;
       float v[kMaxBpg], v2[kMaxBpg], sb[kMaxBpg];
       int32_t i1[kMaxBpg];
@@ -196,7 +210,7 @@ __global__ __launch_bounds__(kT) void k_verify_pass2(VerifyArgs a) {
         const uint32_t b = b0 + q;
         if (q >= a.bpg || b >= a.nb) continue;
         const uint32_t e1 = eo[q + 1];   // esc_off[b + 1]
-        const double bb = c1 * (double)sb[q] + c0;
+        const double bb = c1 * (xn * (double)sb[q]) + c0;
         if ((double)v[q] + bb < lo) continue;
         put(atomicAdd(&s_cnt, 1u), i1[q], eo[q], e1);
         if ((double)v2[q] + bb >= lo)
@@ -236,22 +250,38 @@ __global__ __launch_bounds__(kT) void k_verify_pass2(VerifyArgs a) {
           // columns 128g + 32jj + 8q .. +7: its sign/mantissa bytes are 8 consecutive bytes
           // of the slot's 16-byte row (t = 8jj + i: bytes 16l + (t & 15) + 1024 (t >= 16)),
           // its codes one dword at 2048 + 16l + 4jj, its x values one 16-byte load
-          for (uint32_t U = u; U < 16u * a.g_cols; U += per) {
-            const uint32_t j = U >> 2, jj = U & 3u, g = j >> 2, q = j & 3u, l = 16u * q + r;
-            const uint8_t* tb = a.tiles + ((uint64_t)g * a.nb + b) * 3072u + 16u * l;
-            const uint2 smv = *reinterpret_cast<const uint2*>(tb + 1024u * (jj >> 1) + 8u * (jj & 1u));
-            const uint32_t cwj = *reinterpret_cast<const uint32_t*>(tb + 2048u + 4u * jj);
-            const u32x4 xv = *reinterpret_cast<const u32x4*>(xr + 128u * g + 32u * jj + 8u * q);
+          // kSB units per thread have their loads in flight together (the tiles come
+          // from HBM: one round trip per unit made the screen latency-bound); a unit past
+          // the end loads the last one again and is not used
+          constexpr uint32_t kSB = 4;
+          const uint32_t nU = 16u * a.g_cols;
+          for (uint32_t U0 = u; U0 < nU; U0 += kSB * per) {
+            uint2 smv[kSB];
+            uint32_t cwj[kSB];
+            u32x4 xv[kSB];
 #pragma unroll
-            for (uint32_t i = 0; i < 8; ++i) {
-              const uint32_t sm = ((i < 4u ? smv.x : smv.y) >> (8u * (i & 3u))) & 0xFFu;
-              const uint32_t code = (cwj >> (4u * (i >> 1) + 16u * (i & 1u))) & 0xFu;
-              const uint32_t e = (a.lut[code >> 2] >> (8u * (code & 3u))) & 0xFFu;
-              const uint32_t wb = ((sm & 0x80u) << 8) | (e << 7) | (sm & 0x7Fu);
-              const uint32_t xb = (xv[i >> 1] >> (16u * (i & 1u))) & 0xFFFFu;
-              const double pr = (double)__uint_as_float(xb << 16) * (double)__uint_as_float(wb << 16);
-              z += pr;
-              sa += fabs(pr);
+            for (uint32_t sb = 0; sb < kSB; ++sb) {
+              const uint32_t U = min(U0 + sb * per, nU - 1u);
+              const uint32_t j = U >> 2, jj = U & 3u, g = j >> 2, q = j & 3u, l = 16u * q + r;
+              const uint8_t* tb = a.tiles + ((uint64_t)g * a.nb + b) * 3072u + 16u * l;
+              smv[sb] = *reinterpret_cast<const uint2*>(tb + 1024u * (jj >> 1) + 8u * (jj & 1u));
+              cwj[sb] = *reinterpret_cast<const uint32_t*>(tb + 2048u + 4u * jj);
+              xv[sb] = *reinterpret_cast<const u32x4*>(xr + 128u * g + 32u * jj + 8u * q);
+            }
+#pragma unroll
+            for (uint32_t sb = 0; sb < kSB; ++sb) {
+              if (U0 + sb * per >= nU) break;
+#pragma unroll
+              for (uint32_t i = 0; i < 8; ++i) {
+                const uint32_t sm = ((i < 4u ? smv[sb].x : smv[sb].y) >> (8u * (i & 3u))) & 0xFFu;
+                const uint32_t code = (cwj[sb] >> (4u * (i >> 1) + 16u * (i & 1u))) & 0xFu;
+                const uint32_t e = (a.lut[code >> 2] >> (8u * (code & 3u))) & 0xFFu;
+                const uint32_t wb = ((sm & 0x80u) << 8) | (e << 7) | (sm & 0x7Fu);
+                const uint32_t xb = (xv[sb][i >> 1] >> (16u * (i & 1u))) & 0xFFFFu;
+                const double pr = (double)__uint_as_float(xb << 16) * (double)__uint_as_float(wb << 16);
+                z += pr;
+                sa += fabs(pr);
+              }
             }
           }
           for (uint32_t i = e0 + u; i < e1; i += per) {
@@ -377,6 +407,34 @@ __global__ __launch_bounds__(kT) void k_verify_pass2(VerifyArgs a) {
 
 hipError_t launch_verify_pass2(const VerifyArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(k_verify_pass2, dim3(a.m), dim3(kT), 0, s, a);
+  return hipGetLastError();
+}
+
+// The full first-pass output's error scales: row m of s holds the row norms W_v (the
+// same for every row) and becomes X_m W_v rounded up to FP32, X_m the bound of ||x_m||_2
+// that pass 2 uses (one workgroup per row; x finite, as verification requires).
+__global__ __launch_bounds__(256) void k_scale_norms(const uint16_t* __restrict__ x, uint32_t k,
+                                                     float* __restrict__ s, uint32_t n) {
+  __shared__ double s_part[4];
+  const uint32_t row = blockIdx.x, tid = threadIdx.x;
+  const uint16_t* xr = x + (uint64_t)row * k;
+  double ss = 0.0;
+  for (uint32_t i = tid; i < k; i += 256u) {
+    const double v = (double)__uint_as_float((uint32_t)xr[i] << 16);
+    ss += v * v;
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off);
+  if ((tid & 63u) == 0u) s_part[tid >> 6] = ss;
+  __syncthreads();
+  const double xn = x_norm_up((s_part[0] + s_part[1]) + (s_part[2] + s_part[3]));
+  float* sr = s + (uint64_t)row * n;
+  for (uint32_t v = tid; v < n; v += 256u) sr[v] = f32_round_up(xn * (double)sr[v] * (1.0 + 0x1p-50));
+}
+
+hipError_t launch_scale_norms(const uint16_t* x, uint32_t m, uint32_t k, float* s, uint32_t n,
+                              hipStream_t st) {
+  hipLaunchKernelGGL(k_scale_norms, dim3(m), dim3(256), 0, st, x, k, s, n);
   return hipGetLastError();
 }
 

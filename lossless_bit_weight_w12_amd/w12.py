@@ -538,8 +538,10 @@ def verify_candidates(t: W12Tensor, m: int):
 
 
 def logits_f32(x, t: W12Tensor):
-    """FP32 logits z^ [m, n] and error scales S^ = sum_k |x_k||w_vk| [m, n] from the
-    first pass of the verification (same kernels, same summation order)."""
+    """FP32 logits z^ [m, n] and error scales S [m, n] from the first pass of the
+    verification (same kernels, same summation order).  S = X_m W_v rounded up, an upper
+    bound of sum_k |x_k||w_vk| (Cauchy-Schwarz): W_v the first pass's bound of
+    ||w_v||_2, X_m the second pass's bound of ||x_m||_2."""
     torch = _torch()
     x = _as_bits(x)
     m = x.shape[0]

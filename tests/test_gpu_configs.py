@@ -211,9 +211,9 @@ def test_config4_lm_head_verify_small_m(env, lm_head, m):
     z_hat, s_hat = (v.cpu().numpy().astype(np.float64) for v in w12.logits_f32(xt, t))
     z, s = o.gemm_reference(x, w)
     xmax = np.abs(wi.bf16_bits_to_f32(x).astype(np.float64)).max()
-    d = k + 64.0
+    d = k // 128 + 192.0   # the certified depth (tile columns summed from zero)
     gam = d * 2.0 ** -23 / (1 - d * 2.0 ** -23)
-    a = d * 2.0 ** -126 * (1 + xmax + 2.0 ** (t.e_max - 126))
+    a = (2 * k + d) * 2.0 ** -126 * (1 + xmax + 2.0 ** (t.e_max - 126))
     bound = gam * (s_hat / (1 - gam) + a) + a
     assert (np.abs(z_hat - z) <= bound).all()
     assert (s <= s_hat / (1 - gam) + a).all()

@@ -493,12 +493,13 @@ def test_verify_batched_requests(env):
 
 
 def _certified_bound(s_hat, k, e_max, xmax):
-    """The bound the verification relies on, as its header states it: any summation
-    order of K exact products, each addition with relative error below 2^-23, at most
-    D = K + 64 additions on a path, plus flushed denormals."""
-    d = k + 64.0
+    """The bound the verification relies on, as its header states it: K exact products,
+    each passing through at most D = K/128 + 192 additions (every tile column summed from
+    zero, then added to the running sum) with relative error below 2^-23, plus flushed
+    denormals (2K + D events)."""
+    d = k // 128 + 192.0
     gam = d * 2.0 ** -23 / (1 - d * 2.0 ** -23)
-    a = d * 2.0 ** -126 * (1 + xmax + 2.0 ** (e_max - 126))
+    a = (2 * k + d) * 2.0 ** -126 * (1 + xmax + 2.0 ** (e_max - 126))
     return gam * (s_hat / (1 - gam) + a) + a, gam, a
 
 
@@ -528,7 +529,20 @@ def test_verify_pass1_error_within_certified_bound(env, m, kind):
     err = np.abs(z_hat - z)
     assert (err <= bound).all(), float((err / bound).max())
     assert (s <= s_hat / (1 - gam) + a).all()
+    _check_scale_is_cauchy_schwarz(s_hat, x, w, k)
     say("pass-1 bound", m, kind, "max |z^-z| / (g S) =", float((err / (gam * s + 1e-300)).max()))
+
+
+def _check_scale_is_cauchy_schwarz(s_hat, x, w, k):
+    """The first pass's error scale is ||x_m||_2 ||w_v||_2 rounded up (Cauchy-Schwarz
+    bounds sum_k |x_k||w_vk| by it): at least that product, and above it by less than
+    the slack of the FP32 sums of squares (depth K + 64)."""
+    gam = (k + 64.0) * 2.0 ** -23 / (1 - (k + 64.0) * 2.0 ** -23)
+    xf = wi.bf16_bits_to_f32(x).astype(np.float64)
+    wf = wi.bf16_bits_to_f32(w).astype(np.float64)
+    cs = np.sqrt((xf * xf).sum(1))[:, None] * np.sqrt((wf * wf).sum(1))[None, :]
+    assert (s_hat >= cs * (1 - 1e-12)).all(), float((s_hat / cs).min())
+    assert (s_hat <= cs * (1 + 2 * gam) + 1e-30).all(), float((s_hat / cs).max())
 
 
 # 1025 row-blocks: from 1024 row-blocks the first pass below 16 rows runs the wave-column
@@ -584,6 +598,7 @@ def test_verify_pass1_bound_small_m_large_head(env, m, kind):
     err = np.abs(z_hat - z)
     assert (err <= bound).all(), float((err / bound).max())
     assert (s <= s_hat / (1 - gam) + a).all()
+    _check_scale_is_cauchy_schwarz(s_hat, x, w, k)
 
 
 def sub_fp64_head(g):
