@@ -141,7 +141,10 @@ GemmPlan make_plan(uint32_t m, uint64_t n, uint64_t k, int epi, bool bf16_src = 
     return std::max<uint64_t>(ns, 1);
   };
   uint64_t units;
-  if (w12_bf16_out || (p.mfma && (few_rows || m >= 16))) {
+  // the logits epilogue runs column-synchronous from 4 rows on (151936-row LM head:
+  // M4 / M8 196.6 / 205.6 -> 192.6 / 192.4 us against the wave-column MFMA kernel); at
+  // 1..3 rows the wave-column VALU kernel is 1 us faster (189.2 against 190.3 us)
+  if (w12_bf16_out || (p.mfma && (epi == EPI_LOGITS || few_rows || m >= 16))) {
     p.kind = KIND_COLUMN_SYNC;
     min_cols = W12_CS_MIN_COLS;
     if (w12_bf16_out && m <= 32) {

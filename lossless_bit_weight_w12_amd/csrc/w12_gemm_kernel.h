@@ -420,11 +420,12 @@ __global__ __launch_bounds__(NWV * 64) void k_gemm(
     BlockMax bm,
     GemmParams p) {
   constexpr int NH = MF ? MT / 16 : 1;
-  // the logits epilogue also records per weight row an upper bound of ||w_v||_2 (the
-  // scale of its rounding-error bound is ||x||_2 ||w_v||_2, verification pass 2 supplies
-  // ||x||_2): the squares summed by v_dot2 of the weights with themselves (VALU path) or
-  // by an MFMA of the A operand with itself, its diagonal (MFMA path)
+  // the logits epilogue (VALU path only: from W12_MFMA_MIN_M rows on it runs in k_gemm_cs)
+  // also records per weight row an upper bound of ||w_v||_2 (the scale of its
+  // rounding-error bound is ||x||_2 ||w_v||_2, verification pass 2 supplies ||x||_2): the
+  // squares summed by v_dot2 of the weights with themselves
   constexpr bool kWn = EPI == EPI_LOGITS;
+  static_assert(!(kWn && MF), "the logits epilogue runs column-synchronous with MFMA");
   __shared__ __align__(16) uint16_t xs[NWV * MT * kXsStride];   // one x column per wave
   __shared__ float fin[kWn ? RBW * MT * 16 : 1];
   __shared__ float s_wn[kWn ? RBW * 16 : 1];
@@ -441,8 +442,7 @@ __global__ __launch_bounds__(NWV * 64) void k_gemm(
 
   float vacc[RBW][MF ? 1 : M];
   f32x4 macc[RBW][NH];
-  float wsq[RBW];     // kWn, VALU: this lane's sum of squares of row r's weights
-  f32x4 nacc[RBW];    // kWn, MFMA: W W^T of the row-block over the wave's columns
+  float wsq[RBW];     // kWn: this lane's sum of squares of row r's weights
 #pragma unroll
   for (int rb = 0; rb < RBW; ++rb) {
 #pragma unroll
@@ -450,7 +450,6 @@ __global__ __launch_bounds__(NWV * 64) void k_gemm(
 #pragma unroll
     for (int h = 0; h < NH; ++h) macc[rb][h] = f32x4{0.f, 0.f, 0.f, 0.f};
     wsq[rb] = 0.f;
-    nacc[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
   EscCursor ec[RBW];
@@ -485,20 +484,15 @@ __global__ __launch_bounds__(NWV * 64) void k_gemm(
     }
     const uint16_t* xrow = xw + 8 * q;
     // logits: the column's sums chain from zero and are then added to the running sums,
-    // so a product meets at most 4 MFMA accumulations or 16 v_dot2 (whatever their
-    // internal order) and one addition per later column: the certified bound's depth
-    f32x4 mcol[RBW][NH];
+    // so a product meets at most 16 v_dot2 (2 roundings each, whatever their internal
+    // order) and one addition per later column: the certified bound's depth
     float vcol[RBW][MF ? 1 : M];
-    auto mc = [&](int rb, int h) -> f32x4& { return kWn ? mcol[rb][h] : macc[rb][h]; };
     auto vc = [&](int rb, int m) -> float& { return kWn ? vcol[rb][m] : vacc[rb][m]; };
     if constexpr (kWn) {
 #pragma unroll
-      for (int rb = 0; rb < RBW; ++rb) {
-#pragma unroll
-        for (int h = 0; h < NH; ++h) mcol[rb][h] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int rb = 0; rb < RBW; ++rb)
 #pragma unroll
         for (int m = 0; m < (MF ? 1 : M); ++m) vcol[rb][m] = 0.f;
-      }
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -514,16 +508,8 @@ __global__ __launch_bounds__(NWV * 64) void k_gemm(
 #pragma unroll
           for (int rb = 0; rb < RBW; ++rb) {
             const u32x4 av = {P[rb][4 * j], P[rb][4 * j + 1], P[rb][4 * j + 2], P[rb][4 * j + 3]};
-            mc(rb, h) = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                __builtin_bit_cast(bf16x8_t, av), bv, mc(rb, h), 0, 0, 0);
-          }
-        }
-        if constexpr (kWn) {
-#pragma unroll
-          for (int rb = 0; rb < RBW; ++rb) {
-            const u32x4 av = {P[rb][4 * j], P[rb][4 * j + 1], P[rb][4 * j + 2], P[rb][4 * j + 3]};
-            nacc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                __builtin_bit_cast(bf16x8_t, av), __builtin_bit_cast(bf16x8_t, av), nacc[rb], 0, 0, 0);
+            macc[rb][h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                __builtin_bit_cast(bf16x8_t, av), bv, macc[rb][h], 0, 0, 0);
           }
         }
       } else {
@@ -550,12 +536,9 @@ __global__ __launch_bounds__(NWV * 64) void k_gemm(
     }
     if constexpr (kWn) {
 #pragma unroll
-      for (int rb = 0; rb < RBW; ++rb) {
-#pragma unroll
-        for (int h = 0; h < NH; ++h) macc[rb][h] += mcol[rb][h];
+      for (int rb = 0; rb < RBW; ++rb)
 #pragma unroll
         for (int m = 0; m < (MF ? 1 : M); ++m) vacc[rb][m] += vcol[rb][m];
-      }
     }
     if constexpr (!plain_bf16(SRC)) {
       // refill after the tile's last LDS read: a pending scalar load would otherwise
@@ -678,18 +661,10 @@ __global__ __launch_bounds__(NWV * 64) void k_gemm(
   if constexpr (kWn) {
 #pragma unroll
     for (int rb = 0; rb < RBW; ++rb) {
-      float* dst = red + kRed + (wave * RBW + rb) * 16;
-      if constexpr (MF) {
-        // D[c][c] sits in lane c + 16 (c / 4), element c % 4
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (r == 4 * q + i) dst[r] = nacc[rb][i];
-      } else {
-        float v = wsq[rb];
-        v += __shfl_xor(v, 16);
-        v += __shfl_xor(v, 32);
-        if (q == 0) dst[r] = v;
-      }
+      float v = wsq[rb];
+      v += __shfl_xor(v, 16);
+      v += __shfl_xor(v, 32);
+      if (q == 0) red[kRed + (wave * RBW + rb) * 16 + r] = v;
     }
   }
   __syncthreads();
@@ -1189,16 +1164,19 @@ hipError_t launch_gemm_src(const GemmArgs& a, int epi, const GemmPlan& pl, hipSt
     if (pl.rbw == 2) W12_L(M_, MT_, MF_, 2, 4, EPI_); \
     else W12_L(M_, MT_, MF_, 1, 4, EPI_);             \
   } while (0)
-// (W12 GEMMs with BF16 output always run column-synchronous, and the BF16 sources have
-// no logits epilogue: neither is instantiated here)
+// (W12 GEMMs with BF16 output, and the logits epilogue from W12_MFMA_MIN_M rows on, always
+// run column-synchronous, and the BF16 sources have no logits epilogue: none of them is
+// instantiated here)
 #define W12_EPI(M_, MT_, MF_)                                                 \
   do {                                                                        \
     if constexpr (plain_bf16(SRC)) {                                          \
       if (epi != EPI_BF16) return hipErrorInvalidValue;                       \
       W12_RBW(M_, MT_, MF_, EPI_BF16);                                        \
-    } else {                                                                  \
+    } else if constexpr (!MF_) {                                              \
       if (epi != EPI_LOGITS) return hipErrorInvalidValue;                     \
       W12_RBW(M_, MT_, MF_, EPI_LOGITS);                                      \
+    } else {                                                                  \
+      return hipErrorInvalidValue;                                            \
     }                                                                         \
   } while (0)
 #define W12_CS(MT_, EPI_)                                                                     \

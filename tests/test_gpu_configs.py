@@ -188,8 +188,8 @@ def test_config4_lm_head_verify(env, lm_head):
 @pytest.mark.parametrize("m", [1, 8])
 def test_config4_lm_head_verify_small_m(env, lm_head, m):
     """Workload 4's head verified at 1 and 8 rows (single-request drafts shorter than 16:
-    the first pass takes the wave-column kernels, two row-blocks per wave, VALU at 1 row
-    and MFMA at 8): the first m planted near-tie rows of batch 1, argmax and accepted
+    the first pass takes the wave-column VALU kernel with two row-blocks per wave at 1 row,
+    the column-synchronous MFMA kernel at 8): the first m planted near-tie rows of batch 1, argmax and accepted
     length against the oracle; and the certified bound on every FP32 logit of the same
     first pass (w12_logits_f32)."""
     torch, w12 = env

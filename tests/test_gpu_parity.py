@@ -545,9 +545,9 @@ def _check_scale_is_cauchy_schwarz(s_hat, x, w, k):
     assert (s_hat <= cs * (1 + 2 * gam) + 1e-30).all(), float((s_hat / cs).max())
 
 
-# 1025 row-blocks: from 1024 row-blocks the first pass below 16 rows runs the wave-column
-# kernel with two row-blocks per wave (v_dot2 at 1..3 rows, MFMA at 4..15), here with an
-# odd row-block count so the last wave's second row-block is past the end
+# 1025 row-blocks: from 1024 row-blocks the first pass at 1..3 rows runs the wave-column
+# VALU kernel with two row-blocks per wave (the column-synchronous MFMA kernel from 4 rows
+# on), here with an odd row-block count so the last wave's second row-block is past the end
 BIG_HEAD = (16400, 512)
 
 
@@ -578,7 +578,8 @@ def test_verify_small_m_large_head(env, m):
                                     (8, "wide"), (15, "outliers")])
 def test_verify_pass1_bound_small_m_large_head(env, m, kind):
     """The certified bound on the first pass's FP32 logits below 16 rows on a head with
-    more than 1024 row-blocks (the wave-column logits kernels, VALU and MFMA)."""
+    more than 1024 row-blocks (the wave-column VALU kernel at 1..3 rows, then the
+    column-synchronous MFMA kernel)."""
     torch, w12 = env
     g = np.random.default_rng(9300 + m)
     n, k = BIG_HEAD[0], 1280
