@@ -244,7 +244,10 @@ w12_status w12_gemm_bf16_tiled(const uint16_t* x, uint32_t m, const void* w_tile
  * recomputed in FP64 from the W12 tiles, and those that the FP64 intervals cannot
  * separate are summed exactly, so the result does not depend on the reduction order.
  * A row of x that is all +-0 gets index 0 (every logit is exactly 0) without a search;
- * any number of candidates is screened, in chunks.  A row whose logits are not finite
+ * any number of candidates is screened, in chunks (weights whose squares sum past the FP32
+ * range, |w| of about 2^57 at k = 5120, make W_v infinite: the answer stays exact, but
+ * every row of such a block, or of the whole head when it holds the largest logit, is
+ * screened).  A row whose logits are not finite
  * gets argmax -1.  ws: w12_workspace_bytes(W12_OP_VERIFY, m, n, k). */
 w12_status w12_lmhead_verify(const uint16_t* x, uint32_t m, const w12_desc* d,
                              const int32_t* draft, uint32_t n_draft, int32_t* argmax_out,
