@@ -114,8 +114,9 @@ size_t w12_tiles_bytes(uint64_t n, uint64_t k);
  * after the FP64 screen), the per-row-block records of the first pass (largest FP32
  * logit, second largest, largest row norm bound W_v (w12_lmhead_verify), each FP32
  * [m][n/16]; index of the largest, int32 [m][n/16]), its per-workgroup group records
- * (largest logit, its index, that row-block's norm bound, the group's largest norm bound:
- * four arrays of [m][n/16] 4-byte entries, the first ngroups of each row used) and the
+ * (largest logit, second largest, its index, that row-block's norm bound, the group's
+ * largest norm bound: five arrays of [m][n/16] 4-byte entries, the first ngroups of each
+ * row used) and the
  * candidate lists (int32 [m][n]); all readable after a call for diagnostics.  ENCODE holds the histogram and per-tile escape counts. */
 size_t w12_workspace_bytes(int op, uint32_t m, uint64_t n, uint64_t k);
 

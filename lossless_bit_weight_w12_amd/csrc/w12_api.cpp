@@ -218,7 +218,7 @@ bool set_split_ws(GemmArgs& a, void* ws, const GemmPlan& p, uint32_t m, uint64_t
 // per-row-block records of pass 1, its group records (one per workgroup of pass 1: at
 // most one per row-block) and the candidate lists of pass 2.
 struct VerifyLayout {
-  size_t ncand, bm_v, bm_v2, bm_s, bm_i, g_v, g_i, g_s, g_w, cand, total;
+  size_t ncand, bm_v, bm_v2, bm_s, bm_i, g_v, g_v2, g_i, g_s, g_w, cand, total;
 };
 
 VerifyLayout verify_layout(uint32_t m, uint64_t n) {
@@ -231,7 +231,8 @@ VerifyLayout verify_layout(uint32_t m, uint64_t n) {
   L.bm_s = L.bm_v2 + rec;
   L.bm_i = L.bm_s + rec;
   L.g_v = L.bm_i + rec;
-  L.g_i = L.g_v + rec;
+  L.g_v2 = L.g_v + rec;
+  L.g_i = L.g_v2 + rec;
   L.g_s = L.g_i + rec;
   L.g_w = L.g_s + rec;
   L.cand = L.g_w + rec;
@@ -248,6 +249,7 @@ BlockMax block_max(uint8_t* base, const VerifyLayout& L, const GemmPlan& p) {
   bm.s = (float*)(base + L.bm_s);
   bm.i = (int32_t*)(base + L.bm_i);
   bm.gv = (float*)(base + L.g_v);
+  bm.gv2 = (float*)(base + L.g_v2);
   bm.gi = (int32_t*)(base + L.g_i);
   bm.gs = (float*)(base + L.g_s);
   bm.gw = (float*)(base + L.g_w);
@@ -444,6 +446,7 @@ w12_status verify_impl(const uint16_t* x, uint32_t m, const w12_desc* d, const i
   v.rbmax_s = a.bm.s;
   v.rbmax_i = a.bm.i;
   v.grp_v = a.bm.gv;
+  v.grp_v2 = a.bm.gv2;
   v.grp_i = a.bm.gi;
   v.grp_s = a.bm.gs;
   v.grp_w = a.bm.gw;

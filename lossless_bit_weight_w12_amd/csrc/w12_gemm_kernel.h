@@ -706,7 +706,7 @@ __global__ __launch_bounds__(NWV * 64) void k_gemm(
     if (bm.accepted && blockIdx.x == 0 && blockIdx.y == 0)
       accept_init(bm, p.m, (uint32_t)tid, NWV * 64u);   // verification pass 2 lowers them
     // per (row-block, output row) records, kept in LDS for the workgroup's group record
-    __shared__ float s_gv[RBW][MT], s_gs[RBW][MT];
+    __shared__ float s_gv[RBW][MT], s_gv2[RBW][MT], s_gs[RBW][MT];
     __shared__ int32_t s_gi[RBW][MT];
     for (int o = tid; o < RBW * MT; o += (NWV * 64)) {
       const int rb = o / MT, m = o % MT;
@@ -724,6 +724,7 @@ __global__ __launch_bounds__(NWV * 64) void k_gemm(
         smax = fmaxf(smax, s_wn[rb * 16 + rr]);
       }
       s_gv[rb][m] = !live ? -__builtin_inff() : (finite ? best : __builtin_nanf(""));
+      s_gv2[rb][m] = !live ? -__builtin_inff() : second;
       s_gi[rb][m] = (int32_t)(16u * b + bi);
       s_gs[rb][m] = live ? smax : 0.f;
       if (!live) continue;
@@ -734,18 +735,22 @@ __global__ __launch_bounds__(NWV * 64) void k_gemm(
     }
     __syncthreads();
     if ((uint32_t)tid < MT && (uint32_t)tid < m_rows) {
-      float v = s_gv[0][tid], sv = s_gs[0][tid], wg = s_gs[0][tid];
+      // the group's two largest logits: a block whose best beats the current best brings
+      // its own second, an equal best makes the second equal to it (a tie)
+      float v = s_gv[0][tid], v2 = s_gv2[0][tid], sv = s_gs[0][tid], wg = s_gs[0][tid];
       int32_t vi = s_gi[0][tid];
       bool nan = v != v;
 #pragma unroll
       for (int rb = 1; rb < RBW; ++rb) {
         const float vw = s_gv[rb][tid];
         nan = nan || vw != vw;
-        if (vw > v) { v = vw; vi = s_gi[rb][tid]; sv = s_gs[rb][tid]; }   // ties: the lower row-block
+        if (vw > v) { v2 = fmaxf(v, s_gv2[rb][tid]); v = vw; vi = s_gi[rb][tid]; sv = s_gs[rb][tid]; }   // ties: the lower row-block
+        else v2 = fmaxf(v2, vw);
         wg = fmaxf(wg, s_gs[rb][tid]);
       }
       const size_t og = (size_t)tid * bm.ngrp + blockIdx.x;
       bm.gv[og] = nan ? __builtin_nanf("") : v;
+      bm.gv2[og] = nan ? __builtin_nanf("") : v2;
       bm.gi[og] = vi;
       bm.gs[og] = sv;
       bm.gw[og] = wg;
@@ -1019,7 +1024,7 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_cs(
     if (bm.accepted && blockIdx.x == 0 && blockIdx.y == 0)
       accept_init(bm, p.m, (uint32_t)tid, NT);   // verification pass 2 lowers them
     // the workgroup's group record per output row: its waves' row-blocks in order
-    __shared__ float s_gv[NW][MT], s_gs[NW][MT];
+    __shared__ float s_gv[NW][MT], s_gv2[NW][MT], s_gs[NW][MT];
     __shared__ int32_t s_gi[NW][MT];
     // ||w_v||_2 bounds of the lane's rows 4q+i: D[c][c] sits in lane c + 16 (c / 4),
     // element c % 4
@@ -1076,24 +1081,29 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_cs(
       if (q == 0) {   // a row-block past the end takes no part in the group record
         const bool live = bvalid && m < m_rows;
         s_gv[wave][m] = !live ? -__builtin_inff() : (finite ? best : __builtin_nanf(""));
+        s_gv2[wave][m] = !live ? -__builtin_inff() : second;
         s_gi[wave][m] = (int32_t)(16u * b + row);
         s_gs[wave][m] = live ? wmax : 0.f;
       }
     }
     __syncthreads();
     if ((uint32_t)tid < MT && (uint32_t)tid < m_rows) {
-      float v = s_gv[0][tid], sv = s_gs[0][tid], wg = s_gs[0][tid];
+      // the group's two largest logits: a block whose best beats the current best brings
+      // its own second, an equal best makes the second equal to it (a tie)
+      float v = s_gv[0][tid], v2 = s_gv2[0][tid], sv = s_gs[0][tid], wg = s_gs[0][tid];
       int32_t vi = s_gi[0][tid];
       bool nan = v != v;
 #pragma unroll
       for (int w = 1; w < NW; ++w) {
         const float vw = s_gv[w][tid];
         nan = nan || vw != vw;
-        if (vw > v) { v = vw; vi = s_gi[w][tid]; sv = s_gs[w][tid]; }   // ties: the lower row-block
+        if (vw > v) { v2 = fmaxf(v, s_gv2[w][tid]); v = vw; vi = s_gi[w][tid]; sv = s_gs[w][tid]; }   // ties: the lower row-block
+        else v2 = fmaxf(v2, vw);
         wg = fmaxf(wg, s_gs[w][tid]);
       }
       const size_t o = (size_t)tid * bm.ngrp + blockIdx.x;
       bm.gv[o] = nan ? __builtin_nanf("") : v;
+      bm.gv2[o] = nan ? __builtin_nanf("") : v2;
       bm.gi[o] = vi;
       bm.gs[o] = sv;
       bm.gw[o] = wg;

@@ -120,6 +120,7 @@ struct BlockMax {
   int32_t* i;               // index of v, lowest on ties
   float* gv;                // group: largest logit (NaN if any of its logits is not finite)
   int32_t* gi;              // group: index of gv, lowest on ties
+  float* gv2;               // group: second largest logit over its rows (gv on a tie)
   float* gs;                // group: s of the row-block holding gv
   float* gw;                // group: largest s over its row-blocks
   uint32_t ngrp;            // groups per row (the grid's row-block groups)
@@ -226,6 +227,7 @@ struct VerifyArgs {
   const float* rbmax_s;     // [m][nb]
   const int32_t* rbmax_i;   // [m][nb]
   const float* grp_v;       // [m][ngrp] group records of pass 1
+  const float* grp_v2;
   const int32_t* grp_i;
   const float* grp_s;
   const float* grp_w;

@@ -5,8 +5,9 @@
 // 16-row block of the head, the largest FP32 logit z^ (with its index), the second
 // largest, and W_b = the largest FP32 upper bound of ||w_v||_2 over the block's rows
 // (the same kernel sums the squares of the weights it streams); and per workgroup of
-// pass 1 (a group of consecutive row-blocks) the group's largest logit, its index, that
-// block's W_b, and the group's largest W_b.  Pass 2 (one workgroup per row):
+// pass 1 (a group of consecutive row-blocks) the group's largest and second largest
+// logit, the index of the largest, that block's W_b, and the group's largest W_b.  Pass 2
+// (one workgroup per row):
 //   1. z* = max z^ over the group records (lowest index on ties), W* the W_b of its
 //      block; X >= ||x||_2 from the FP64 sum of the exact squares of x;
 //   2. the error bound.  A product of two BF16 values is exact in FP32 unless it
@@ -28,7 +29,9 @@
 //      is a candidate (the exact argmax always is).  A group whose largest logit plus
 //      B(X times its largest W_b) is below L holds none; in the others, with W_b in B,
 //      a block adds its largest logit when that reaches L, and all of its rows when its
-//      second largest does too (otherwise no other row of it can);
+//      second largest does too (otherwise no other row of it can).  The group holding z*
+//      adds z* alone, without reading its block records, when its second largest logit
+//      plus B(X times its largest W_b) is below L;
 //   4. a single candidate is the argmax.  Otherwise the FP64 screen: each candidate's
 //      logit is recomputed from the W12 tiles in FP64 (a
 //      BF16 product is exact in FP64; escape corrections add two terms each), within
@@ -61,6 +64,7 @@ constexpr uint32_t kWaves = kT / 64u;
 static_assert(kWaves == kExactWaves, "the exact stage runs one wave per candidate");
 constexpr uint32_t kScreenMax = 512;   // candidates screened per chunk (ids and results in LDS)
 constexpr uint32_t kGCache = 6144;     // group records (largest logit, norm) kept in LDS for the scan
+constexpr uint32_t kEscUnread = 0xFFFFFFFFu;   // a candidate's escape range not read yet
 
 __global__ __launch_bounds__(kT) void k_verify_pass2(VerifyArgs a) {
   __shared__ float s_gvc[kGCache], s_gwc[kGCache];
@@ -70,7 +74,7 @@ __global__ __launch_bounds__(kT) void k_verify_pass2(VerifyArgs a) {
   __shared__ uint32_t s_ke0[kScreenMax], s_ke1[kScreenMax];   // the chunk's escape ranges
   __shared__ double s_z64[kScreenMax], s_b64[kScreenMax];
   __shared__ double s_d0[kWaves], s_d1[kWaves];
-  __shared__ float s_wv[kWaves], s_ws[kWaves];
+  __shared__ float s_wv[kWaves], s_ws[kWaves], s_w2[kWaves];
   __shared__ int32_t s_wi[kWaves];
   __shared__ uint32_t s_u0[kWaves];
   __shared__ ExactShared s_ex;
@@ -80,6 +84,7 @@ __global__ __launch_bounds__(kT) void k_verify_pass2(VerifyArgs a) {
   const uint32_t row = blockIdx.x, tid = threadIdx.x, lane = tid & 63u, wave = tid >> 6;
   const uint16_t* xr = a.x + (uint64_t)row * a.k;
   const float* gv = a.grp_v + (uint64_t)row * a.ngrp;
+  const float* gv2 = a.grp_v2 + (uint64_t)row * a.ngrp;
   const int32_t* gi = a.grp_i + (uint64_t)row * a.ngrp;
   const float* gs = a.grp_s + (uint64_t)row * a.ngrp;
   const float* gw = a.grp_w + (uint64_t)row * a.ngrp;
@@ -96,22 +101,24 @@ __global__ __launch_bounds__(kT) void k_verify_pass2(VerifyArgs a) {
   uint32_t ncand = 0, nsurv = 0;
   if (tid == 0) { s_cnt = 0; s_bad = 0; s_result = -1; }
 
-  // 1. z*, its index and W* over the group records (NaN marks a group with a non-finite
-  // logit), which stay in LDS for the scan, and Xmax, ||x||_2^2 and the finiteness of x.
-  // Every scan issues all of a thread's loads of a chunk (clamped indices) before using
-  // any; the result does not depend on the order (largest value, lowest index on ties).
-  float bv = -__builtin_inff(), bs = 0.f;
+  // 1. z*, its index, W* and the second largest logit of its group over the group
+  // records (NaN marks a group with a non-finite logit), which stay in LDS for the scan,
+  // and Xmax, ||x||_2^2 and the finiteness of x.  Every scan issues all of a thread's
+  // loads of a round before using any; the result does not depend on the order (largest
+  // value, lowest index on ties).
+  float bv = -__builtin_inff(), bs = 0.f, b2 = -__builtin_inff();
   int32_t bi = 0x7FFFFFFF;
   bool bad = false;
   double xm = 0.0;    // Xmax, eight BF16 per load (k is a multiple of 128)
   double ssx = 0.0;   // sum of x_k^2 (each square exact in FP64)
   {
-    constexpr uint32_t kU = 8, kXU = 2;
+    constexpr uint32_t kU = 10, kXU = 2;   // 5120 groups per round: 151936 rows in one at 2 row-blocks per group
     const uint32_t nx = a.k / 8u;
     const uint32_t rounds = max((a.ngrp + kT * kU - 1) / (kT * kU), (nx + kT * kXU - 1) / (kT * kXU));
     for (uint32_t rd = 0; rd < rounds; ++rd) {
       const uint32_t base = rd * kT * kU, xbase = rd * kT * kXU;
-      float v[kU], s[kU], u[kU];   // largest logit, its block's norm, the group's largest norm
+      // largest logit, second largest, its block's norm, the group's largest norm
+      float v[kU], vs2[kU], s[kU], u[kU];
       int32_t iv[kU];
       u32x4 xv[kXU];
 #pragma unroll
@@ -122,6 +129,7 @@ __global__ __launch_bounds__(kT) void k_verify_pass2(VerifyArgs a) {
         const uint32_t G = base + q * kT + tid;
         if (G < a.ngrp) {   // (uniform over a wave but the last: no duplicate loads)
           v[q] = gv[G];
+          vs2[q] = gv2[G];
           iv[q] = gi[G];
           s[q] = gs[G];
           u[q] = gw[G];
@@ -133,7 +141,7 @@ __global__ __launch_bounds__(kT) void k_verify_pass2(VerifyArgs a) {
         if (G >= a.ngrp) continue;
         if (G < kGCache) { s_gvc[G] = v[q]; s_gwc[G] = u[q]; }
         if (v[q] != v[q]) bad = true;
-        else if (v[q] > bv || (v[q] == bv && iv[q] < bi)) { bv = v[q]; bi = iv[q]; bs = s[q]; }
+        else if (v[q] > bv || (v[q] == bv && iv[q] < bi)) { bv = v[q]; bi = iv[q]; bs = s[q]; b2 = vs2[q]; }
       }
 #pragma unroll
       for (uint32_t q = 0; q < kXU; ++q) {
@@ -153,23 +161,31 @@ __global__ __launch_bounds__(kT) void k_verify_pass2(VerifyArgs a) {
   // results in wave order
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) {
-    const float v2 = __shfl_xor(bv, off), s2 = __shfl_xor(bs, off);
+    const float v2 = __shfl_xor(bv, off), s2 = __shfl_xor(bs, off), t2 = __shfl_xor(b2, off);
     const int32_t i2 = __shfl_xor(bi, off);
-    if (v2 > bv || (v2 == bv && i2 < bi)) { bv = v2; bi = i2; bs = s2; }
+    if (v2 > bv || (v2 == bv && i2 < bi)) { bv = v2; bi = i2; bs = s2; b2 = t2; }
     xm = fmax(xm, __shfl_xor(xm, off));
     ssx += __shfl_xor(ssx, off);
   }
   __syncthreads();   // s_cnt, s_bad initialised
   if (bad) atomicOr(&s_bad, 1u);
-  if (lane == 0) { s_wv[wave] = bv; s_wi[wave] = bi; s_ws[wave] = bs; s_d0[wave] = xm; s_d1[wave] = ssx; }
+  if (lane == 0) {
+    s_wv[wave] = bv;
+    s_wi[wave] = bi;
+    s_ws[wave] = bs;
+    s_w2[wave] = b2;
+    s_d0[wave] = xm;
+    s_d1[wave] = ssx;
+  }
   __syncthreads();
   bv = s_wv[0];
   bi = s_wi[0];
   bs = s_ws[0];
+  b2 = s_w2[0];
   xm = s_d0[0];
   ssx = s_d1[0];
   for (uint32_t w = 1; w < kWaves; ++w) {
-    if (s_wv[w] > bv || (s_wv[w] == bv && s_wi[w] < bi)) { bv = s_wv[w]; bi = s_wi[w]; bs = s_ws[w]; }
+    if (s_wv[w] > bv || (s_wv[w] == bv && s_wi[w] < bi)) { bv = s_wv[w]; bi = s_wi[w]; bs = s_ws[w]; b2 = s_w2[w]; }
     xm = fmax(xm, s_d0[w]);
     ssx += s_d1[w];
   }
@@ -187,10 +203,19 @@ __global__ __launch_bounds__(kT) void k_verify_pass2(VerifyArgs a) {
   if (row_ok && !zero_row) {
     // 2. candidates from the groups whose bound reaches L: a block's largest logit, and
     // all its rows when its second largest also reaches L
+    const uint32_t gstar = ((uint32_t)bi >> 4) / a.bpg;   // the group holding z*
     for (uint32_t G = tid; G < a.ngrp; G += kT) {
       const float gzv = G < kGCache ? s_gvc[G] : gv[G];
       const float gwv = G < kGCache ? s_gwc[G] : gw[G];
-      if ((double)gzv + c1 * (xn * (double)gwv) + c0 < lo) continue;   // none of its rows reaches L
+      const double gbound = c1 * (xn * (double)gwv) + c0;
+      if ((double)gzv + gbound < lo) continue;   // none of its rows reaches L
+      if (G == gstar && (double)b2 + gbound < lo) {
+        // every other row of z*'s group is at most its second largest logit and has at
+        // most its largest norm: z* alone, without the block records (its escape range
+        // is read later, only if the FP64 screen needs it)
+        put(atomicAdd(&s_cnt, 1u), bi, kEscUnread, kEscUnread);
+        continue;
+      }
       const uint32_t b0 = G * a.bpg;
       float v[kMaxBpg], v2[kMaxBpg], sb[kMaxBpg];
       int32_t i1[kMaxBpg];
@@ -340,8 +365,9 @@ __global__ __launch_bounds__(kT) void k_verify_pass2(VerifyArgs a) {
           const uint32_t cc = cb + c;
           const int32_t v = get(cc);
           s_chunk[c] = v;
-          s_ke0[c] = cc < kScreenMax ? s_ce0[cc] : a.esc_off[(uint32_t)v >> 4];
-          s_ke1[c] = cc < kScreenMax ? s_ce1[cc] : a.esc_off[((uint32_t)v >> 4) + 1u];
+          const bool known = cc < kScreenMax && s_ce0[cc] != kEscUnread;
+          s_ke0[c] = known ? s_ce0[cc] : a.esc_off[(uint32_t)v >> 4];
+          s_ke1[c] = known ? s_ce1[cc] : a.esc_off[((uint32_t)v >> 4) + 1u];
         }
         __syncthreads();
         screen(nc);
@@ -377,8 +403,9 @@ __global__ __launch_bounds__(kT) void k_verify_pass2(VerifyArgs a) {
       const ExactRow er{xr, a.tiles, a.esc, a.nb, a.g_cols, a.k, a.lut};
       const int32_t rbest = exact_best(s_ex, er, nsurv, get, [&](uint32_t c, uint32_t& e0, uint32_t& e1) {
         const uint32_t b = (uint32_t)get(c) >> 4;
-        e0 = c < kScreenMax ? s_ce0[c] : a.esc_off[b];
-        e1 = c < kScreenMax ? s_ce1[c] : a.esc_off[b + 1];
+        const bool known = c < kScreenMax && s_ce0[c] != kEscUnread;
+        e0 = known ? s_ce0[c] : a.esc_off[b];
+        e1 = known ? s_ce1[c] : a.esc_off[b + 1];
       });
       if (tid == 0) s_result = rbest;
     }

@@ -701,6 +701,29 @@ def test_verify_exact_tie_lowest_index_and_escapes(env):
     assert int(acc.item()) == m
 
 
+def test_verify_row_norms_beyond_fp32(env):
+    """Weights so large that the FP32 sums of their squares overflow (|w| in [2^53, 2^63)
+    at k = 640) make every row norm bound infinite: every logit of the head is then a
+    candidate, screened in FP64 in chunks of 512, and the answer is still the exact argmax
+    (the wave-column VALU kernel at 2 rows, the column-synchronous kernel at 5)."""
+    torch, w12 = env
+    g = np.random.default_rng(61)
+    n, k = 2048, 640
+    w = wide_exponents((n, k), g, 180, 190)
+    t = w12.encode(to_dev(w, torch))
+    for m in (2, 5):
+        x = wi.gaussian_bf16((m, k), 1.0, g)
+        am_ref, _ = o.argmax_exact(x, w)
+        say("verify infinite row norms", n, k, m)
+        draft = am_ref.astype(np.int32)
+        am, acc = w12.lmhead_verify(to_dev(x, torch), t, torch.from_numpy(draft).to("cuda:0"))
+        torch.cuda.synchronize()
+        assert am.cpu().numpy().tolist() == am_ref.tolist()
+        assert int(acc.item()) == m
+        nc = w12.verify_candidates(t, m).cpu().numpy()
+        assert (nc[:, 0] == n).all(), nc[:, 0].tolist()
+
+
 def test_verify_nonfinite_row_reports_minus_one(env):
     torch, w12 = env
     g = np.random.default_rng(7)
