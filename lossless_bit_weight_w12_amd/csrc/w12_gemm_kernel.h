@@ -899,13 +899,31 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_cs(
       }
     }
   };
+  // The column's x fragments are read from LDS before the tile is decoded, so their
+  // latency hides under the decode instead of stalling the MFMAs (the compiler placed
+  // the reads after the decode, each pair waited for before its MFMAs): MLP gate+up
+  // M1 / M16 / M32 41.8 / 42.2 / 46.1 -> 40.5 / 41.0 / 44.7 us.  Only where the extra 16
+  // or 32 registers keep the occupancy the launches need: 16 columns, and 32 with one x
+  // unit per thread and the BF16 epilogue (with 5 or 7 waves, or the logits epilogue,
+  // the 32-column kernel reached 129-135 VGPRs and lost a workgroup per CU: down M32
+  // 28.2 -> 39.2 us).
+  constexpr bool kEarlyX = MT == 16 || (MT == 32 && kUnits == 1 && EPI == EPI_BF16);
   auto compute = [&](const TileRegs<SRC>& t, uint32_t g) {
+    const uint16_t* xrow = &xs[g & 1u][8 * q];
+    u32x4 xvs[4][NH];
+    if constexpr (kEarlyX) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int h = 0; h < NH; ++h)
+          xvs[j][h] = *reinterpret_cast<const u32x4*>(xrow + (16 * h + r) * kXs + 32 * j);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     uint32_t P[16];
     unpack_tile<SRC>(t, sv, P);
     if constexpr (!plain_bf16(SRC)) {
       if (bvalid) esc_apply(ec, sv.esc, g, lane, P);
     }
-    const uint16_t* xrow = &xs[g & 1u][8 * q];
     // logits: the column's 4 MFMAs chain from zero and the column sum is added to the
     // running sum, so a product meets at most 4 MFMA accumulations (whatever their
     // internal order) and one addition per later column: the certified bound's depth
@@ -915,7 +933,8 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_cs(
       const u32x4 av = {P[4 * j], P[4 * j + 1], P[4 * j + 2], P[4 * j + 3]};
 #pragma unroll
       for (int h = 0; h < NH; ++h) {
-        const u32x4 xv = *reinterpret_cast<const u32x4*>(xrow + (16 * h + r) * kXs + 32 * j);
+        const u32x4 xv =
+            kEarlyX ? xvs[j][h] : *reinterpret_cast<const u32x4*>(xrow + (16 * h + r) * kXs + 32 * j);
         f32x4& c = kWn ? col[h] : acc[h];
         c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av), __builtin_bit_cast(bf16x8_t, xv),
                                                     (kWn && j == 0) ? f32x4{0.f, 0.f, 0.f, 0.f} : c, 0, 0, 0);
