@@ -36,9 +36,10 @@
 //   (deterministic; see split_last).
 // RMS launches (p.rms): the output rows are divided by the RMS of their x rows, summed
 //   from the staged x units (harness op of the layer chain, not the W12 method).
-// The logits epilogue (verification pass 1) keeps per row-block the two largest logits,
-//   the index of the largest and the largest sum |x||w|; the full FP32 logits only when
-//   the caller passes a buffer for them.
+// The logits epilogue (verification pass 1) sums every tile column from zero before
+//   adding it to the running sum, and keeps per row-block the two largest logits, the
+//   index of the largest and the largest bound of a row's 2-norm; the full FP32 logits
+//   only when the caller passes a buffer for them.
 #pragma once
 
 #include "w12_internal.h"

@@ -508,8 +508,8 @@ def _certified_bound(s_hat, k, e_max, xmax):
 def test_verify_pass1_error_within_certified_bound(env, m, kind):
     """The FP32 logits of verification pass 1 (w12_logits_f32: the same kernels and
     summation order) stay within the certified bound of the exact values on every
-    output (the assumption the exact-argmax filter rests on), and the kernel's
-    sum |x||w| is a valid scale for it."""
+    output (the assumption the exact-argmax filter rests on), and its error scale
+    X_m W_v is a valid scale for it."""
     torch, w12 = env
     g = np.random.default_rng(9000 + m)
     n, k = 2048, 5120
