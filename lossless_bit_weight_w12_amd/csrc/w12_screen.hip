@@ -228,6 +228,20 @@ __global__ __launch_bounds__(kScreenNW * 64) void k_screen(ScreenArgs a) {
         sc[i][j] = __uint_as_float((j & 1) ? (dw & 0xFFFF0000u) : (dw << 16));
       }
     const uint16_t* xrow = &xs[slot][8 * q];
+    // up to 32 columns the column's x fragments are read from LDS before the codes are
+    // converted, so their latency hides under the conversion (two levels at M = 32:
+    // 222 -> 208 us; 16 columns within 1 %); at 64 and 128 columns the registers are
+    // not there
+    constexpr bool kEarly = MT <= 32;
+    u32x4 xvs[4][NH];
+    if constexpr (kEarly) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int h = 0; h < NH; ++h)
+          xvs[j][h] = *reinterpret_cast<const u32x4*>(xrow + (16 * h + r) * kXs + 32 * j);
+      __builtin_amdgcn_sched_barrier(0);
+    }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const u32x4 cw = t[j >> 1];
@@ -237,7 +251,8 @@ __global__ __launch_bounds__(kScreenNW * 64) void k_screen(ScreenArgs a) {
       const u32x4 av = {a0, a1, a2, a3};
 #pragma unroll
       for (int h = 0; h < NH; ++h) {
-        const u32x4 xv = *reinterpret_cast<const u32x4*>(xrow + (16 * h + r) * kXs + 32 * j);
+        const u32x4 xv =
+            kEarly ? xvs[j][h] : *reinterpret_cast<const u32x4*>(xrow + (16 * h + r) * kXs + 32 * j);
         const f32x4 part = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
             __builtin_bit_cast(bf16x8_t, av), __builtin_bit_cast(bf16x8_t, xv),
             f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
