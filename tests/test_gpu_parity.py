@@ -701,6 +701,65 @@ def test_verify_exact_tie_lowest_index_and_escapes(env):
     assert int(acc.item()) == m
 
 
+@pytest.mark.parametrize("m", [2, 5])
+def test_verify_group_second_logit(env, m):
+    """The group record's second largest logit decides whether pass 2 opens the block
+    records of z*'s group.  Each row's winning head row is copied (an exact tie, so the
+    lowest index must win) into: row 0 the same 16-row block, row 1 another block of the
+    same pass-1 group (eight row-blocks at 5 rows, two at 2), row 2.. another group; a
+    second set of rows gets a runner-up one BF16 step below the winner on one weight in
+    the same group.  Argmax, accepted length and candidate counts against the oracle."""
+    torch, w12 = env
+    g = np.random.default_rng(7700 + m)
+    n, k = BIG_HEAD
+    w = wi.gaussian_bf16((n, k), 0.02, g)
+    x = wi.gaussian_bf16((m, k), 1.0, g)
+    z, _ = o.gemm_reference(x, w)
+    bpg = 8 if m >= 4 else 2
+    for mi in range(m):
+        v1 = int(np.argmax(z[mi]))
+        blk, grp = v1 // 16, v1 // (16 * bpg)
+        if mi == 0:
+            dst = 16 * blk + (v1 % 16 + 5) % 16                       # same block
+        elif mi == 1:
+            b2 = grp * bpg + (blk - grp * bpg + 1) % bpg              # same group, other block
+            dst = 16 * b2 + 3
+        else:
+            dst = (v1 + 16 * bpg * 7 + 16 * mi) % n                   # another group
+        w[dst] = w[v1]
+    am_ref, _ = o.argmax_exact(x, w)
+    t = w12.encode(to_dev(w, torch))
+    say("verify group second logit", m, n, k)
+    draft = am_ref.astype(np.int32)
+    am, acc = w12.lmhead_verify(to_dev(x, torch), t, torch.from_numpy(draft).to("cuda:0"))
+    torch.cuda.synchronize()
+    assert am.cpu().numpy().tolist() == am_ref.tolist()
+    assert int(acc.item()) == m
+    nc = w12.verify_candidates(t, m).cpu().numpy()
+    assert (nc[:, 0] >= 2).all(), nc[:, 0].tolist()   # both copies reached the FP64 screen
+    # a runner-up one BF16 step below on a single weight of the winner's row, same group
+    w2 = w.copy()
+    for mi in range(m):
+        v1 = int(am_ref[mi])
+        blk, grp = v1 // 16, v1 // (16 * bpg)
+        b2 = grp * bpg + (blk - grp * bpg + 1) % bpg
+        dst = 16 * b2 + 7
+        if dst // 16 == blk:
+            dst = 16 * blk + (v1 % 16 + 1) % 16
+        w2[dst] = w2[v1]
+        kk = int(np.argmax(np.abs(wi.bf16_bits_to_f32(x[mi]))))
+        sgn = 1 if wi.bf16_bits_to_f32(x[mi, kk:kk + 1])[0] > 0 else -1
+        bits = int(w2[dst, kk])
+        # one BF16 step toward a smaller product x*w
+        mag_up = (bits & 0x8000 == 0) == (sgn < 0)
+        w2[dst, kk] = np.uint16(bits + 1 if mag_up else bits - 1) if bits & 0x7FFF else bits
+    am_ref2, _ = o.argmax_exact(x, w2)
+    t2 = w12.encode(to_dev(w2, torch))
+    am2, _ = w12.lmhead_verify(to_dev(x, torch), t2, torch.from_numpy(am_ref2.astype(np.int32)).to("cuda:0"))
+    torch.cuda.synchronize()
+    assert am2.cpu().numpy().tolist() == am_ref2.tolist()
+
+
 def test_verify_row_norms_beyond_fp32(env):
     """Weights so large that the FP32 sums of their squares overflow (|w| in [2^53, 2^63)
     at k = 640) make every row norm bound infinite: every logit of the head is then a
