@@ -903,12 +903,14 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_cs(
   // The column's x fragments are read from LDS before the tile is decoded, so their
   // latency hides under the decode instead of stalling the MFMAs (the compiler placed
   // the reads after the decode, each pair waited for before its MFMAs): MLP gate+up
-  // M1 / M16 / M32 41.8 / 42.2 / 46.1 -> 40.5 / 41.0 / 44.7 us.  Only where the extra 16
-  // or 32 registers keep the occupancy the launches need: 16 columns, and 32 with one x
-  // unit per thread and the BF16 epilogue (with 5 or 7 waves, or the logits epilogue,
-  // the 32-column kernel reached 129-135 VGPRs and lost a workgroup per CU: down M32
-  // 28.2 -> 39.2 us).
-  constexpr bool kEarlyX = MT == 16 || (MT == 32 && kUnits == 1 && EPI == EPI_BF16);
+  // M1 / M16 / M32 41.8 / 42.2 / 46.1 -> 40.5 / 41.0 / 44.7 us.  Only where the extra
+  // registers keep the occupancy the launches need: 16 columns, 32 with one x unit per
+  // thread and the BF16 epilogue (with 5 or 7 waves, or the logits epilogue, the
+  // 32-column kernel reached 129-135 VGPRs and lost a workgroup per CU: down M32
+  // 28.2 -> 39.2 us), and 64 in the 10-wave workgroups that run one per CU (163 VGPRs;
+  // gate+up M48 / M64 58.9 / 58.8 -> 56.6 / 57.8 us).
+  constexpr bool kEarlyX = MT == 16 || (MT == 32 && kUnits == 1 && EPI == EPI_BF16) ||
+                           (MT == 64 && NW == 10 && EPI == EPI_BF16);
   auto compute = [&](const TileRegs<SRC>& t, uint32_t g) {
     const uint16_t* xrow = &xs[g & 1u][8 * q];
     u32x4 xvs[4][NH];
