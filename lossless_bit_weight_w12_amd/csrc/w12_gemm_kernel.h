@@ -34,8 +34,9 @@
 // Split-K (gridDim.y > 1): FP32 partials go to the workspace at device scope and the
 //   split that finishes last in its row-block group sums them in split order
 //   (deterministic; see split_last).
-// RMS launches (p.rms): the output rows are divided by the RMS of their x rows, summed
-//   from the staged x units (harness op of the layer chain, not the W12 method).
+// RMS launches (p.rms; the column-synchronous kernel's EPI_RMS instantiations): the
+//   output rows are divided by the RMS of their x rows, summed from the staged x
+//   (harness op of the layer chain, not the W12 method).
 // The logits epilogue (verification pass 1) sums every tile column from zero before
 //   adding it to the running sum, and keeps per row-block the two largest logits, the
 //   index of the largest and the largest bound of a row's 2-norm; the full FP32 logits
@@ -560,18 +561,8 @@ __global__ __launch_bounds__(NWV * 64) void k_gemm(
   // below the compute to reuse registers: pinning the full one-column-ahead schedule
   // with scheduling barriers (and a single-exit loop) measured slower on these shapes
   // (M1 down -5 %, M16 / M32 gate+up -3 to -4 %), the memory system being saturated by
-  // fewer requests in flight per wave.
-  // RMS launches: per-unit sums of x^2 over the wave's columns, in column order
-  constexpr int kXU = XStage<M>::kUnits;
-  float ssq[kXU];
-#pragma unroll
-  for (int i = 0; i < kXU; ++i) ssq[i] = 0.f;
-  auto xsumsq = [&](bool in_range) {
-    if (EPI == EPI_BF16 && p.rms && in_range) {   // (RMS launches have the BF16 epilogue)
-#pragma unroll
-      for (int i = 0; i < kXU; ++i) ssq[i] += unit_sumsq(xr.v[i]);
-    }
-  };
+  // fewer requests in flight per wave.  (No RMS launch runs here: W12 launches with the
+  // BF16 epilogue are column-synchronous, and the BF16 sources have no RMS form.)
   uint32_t g = ga + (uint32_t)wave;
   if (g < gb) {
     x_load<M>(xr, x, p.k, m_rows, g, gb, lane);
@@ -582,14 +573,12 @@ __global__ __launch_bounds__(NWV * 64) void k_gemm(
 #pragma unroll
       for (int rb = 0; rb < RBW; ++rb) esc_begin(ec[rb], sv[rb].esc_off, sv[rb].esc, bl[rb], ga * 128u);
     }
-    xsumsq(true);
     x_store<M>(xr, xw, lane);
     __builtin_amdgcn_wave_barrier();
     for (;;) {
       x_load<M>(xr, x, p.k, m_rows, g + NWV, gb, lane);
       load_tiles(tB, g + NWV);
       compute(tA, g);
-      xsumsq(g + NWV < gb);
       __builtin_amdgcn_wave_barrier();
       x_store<M>(xr, xw, lane);
       __builtin_amdgcn_wave_barrier();
@@ -598,7 +587,6 @@ __global__ __launch_bounds__(NWV * 64) void k_gemm(
       x_load<M>(xr, x, p.k, m_rows, g + NWV, gb, lane);
       load_tiles(tA, g + NWV);
       compute(tB, g);
-      xsumsq(g + NWV < gb);
       __builtin_amdgcn_wave_barrier();
       x_store<M>(xr, xw, lane);
       __builtin_amdgcn_wave_barrier();
@@ -606,31 +594,7 @@ __global__ __launch_bounds__(NWV * 64) void k_gemm(
       if (g >= gb) break;
     }
   }
-  // RMS launches: each row's sum of x^2 per wave (its 16 unit lanes meet in a fixed
-  // shuffle tree), then over the waves in wave order where it is used
-  __shared__ float s_ssw[NWV][M];
-  if (EPI == EPI_BF16 && p.rms) {
-#pragma unroll
-    for (int i = 0; i < kXU; ++i) {
-      float v = ssq[i];
-#pragma unroll
-      for (int off = 8; off >= 1; off >>= 1) v += __shfl_xor(v, off);
-      const uint32_t u = (uint32_t)lane + 64u * i;
-      if (u < 16u * M && (u & 15u) == 0u) s_ssw[wave][u >> 4] = v;
-    }
-  }
-  auto row_ss = [&](int m) {
-    float t = 0.f;
-#pragma unroll
-    for (int wv = 0; wv < NWV; ++wv) t += s_ssw[wv][m];
-    return t;
-  };
   __syncthreads();   // LDS x no longer read: reuse it for the cross-wave reduction
-  // RMS launches with K split: this split's row sums in the group's slot
-  // ss[group][split][row], at device scope, for the split that completes the group
-  const __amdgpu_buffer_rsrc_t ssrs = make_rsrc(p.ss, gridDim.x * gridDim.y * m_rows * 4u);
-  if (EPI == EPI_BF16 && p.rms && gridDim.y > 1 && tid < M && (uint32_t)tid < m_rows)
-    st_dev(ssrs, ((blockIdx.x * gridDim.y + blockIdx.y) * m_rows + tid) * 4u, row_ss(tid));
 
   // ---- cross-lane / cross-wave reduction into red[] (aliases xs); the row sums of
   // squares, when kept, follow as [wave][rb][row]
@@ -757,19 +721,19 @@ __global__ __launch_bounds__(NWV * 64) void k_gemm(
       bm.gw[og] = wg;
     }
   } else {
-    auto store_y = [&](int rb, int m, int rr, float v, float ss) {
+    auto store_y = [&](int rb, int m, int rr, float v) {
       const bool second = RBW == 2 && rb == 1;     // per-thread: pick the row-block's weight
       uint16_t* yy = second ? sv[RBW - 1].y : sv[0].y;
       const uint32_t nn = second ? sv[RBW - 1].n : sv[0].n;
       const uint32_t bb = second ? bl[RBW - 1] : bl[0];
-      yy[(size_t)m * nn + 16u * bb + rr] = f32_to_bf16_rne(p.rms ? v / rms_of(ss, p.k) : v);
+      yy[(size_t)m * nn + 16u * bb + rr] = f32_to_bf16_rne(v);
     };
     if (gridDim.y == 1) {
       for (int o = tid; o < kOut; o += (NWV * 64)) {
         const int rb = o / (MT * 16), rem = o % (MT * 16), m = rem >> 4, rr = rem & 15;
         const float v = final_value(red, o);
         if (b0 + rb >= p.nb || (uint32_t)m >= m_rows) continue;
-        store_y(rb, m, rr, v, p.rms ? row_ss(m) : 0.f);
+        store_y(rb, m, rr, v);
       }
     } else {
       // K split: this split's partials [split][m][n] at device scope; the split that
@@ -787,18 +751,17 @@ __global__ __launch_bounds__(NWV * 64) void k_gemm(
           const int rb = o / (MT * 16), rem = o % (MT * 16), m = rem >> 4, rr = rem & 15;
           const uint32_t b = b0 + rb;
           if (b >= p.nb || (uint32_t)m >= m_rows) continue;
-          float v[kMaxSplit], ssp[kMaxSplit];
+          float v[kMaxSplit];
 #pragma unroll
           for (uint32_t sp = 0; sp < kMaxSplit; ++sp) {   // every load in flight before the adds
             const uint32_t spl = min(sp, gridDim.y - 1u);
             v[sp] = ld_dev1(prs, ((spl * m_rows + m) * p.n + 16u * b + rr) * 4u);
-            ssp[sp] = p.rms ? ld_dev1(ssrs, ((blockIdx.x * gridDim.y + spl) * m_rows + m) * 4u) : 0.f;
           }
-          float t = 0.f, ss = 0.f;
+          float t = 0.f;
 #pragma unroll
           for (uint32_t sp = 0; sp < kMaxSplit; ++sp)
-            if (sp < gridDim.y) { t += v[sp]; ss += ssp[sp]; }
-          store_y(rb, m, rr, t, ss);
+            if (sp < gridDim.y) t += v[sp];
+          store_y(rb, m, rr, t);
         }
       }
     }
@@ -880,11 +843,27 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_cs(
     else load_tile<SRC>(t, sv.w, p, bl, g, lane, nbw);
   };
   // RMS launches: per-unit sums of x^2 over the K-range, in column order
+  // RMS launches sum each row's x^2 over the K-range.  Up to 32 columns (the EPI_RMS
+  // instantiations) by an MFMA of the x fragments with themselves (waves 0..3 take one of
+  // the column's four 32-column steps each; the diagonal is kept), on matrix cores that
+  // are otherwise 90 % idle: the decode chain's gate/up and o launches at M = 24 49.2 /
+  // 16.4 -> 47.2 / 16.0 us against per-unit VALU sums.  At 64 and 128 columns, where the
+  // MFMA accumulators would spill, the BF16 instantiation sums per unit on the VALU in
+  // column order under the runtime flag (the compiler then keeps a separate copy of the
+  // main loop for plain launches, which measured faster for them than the lone loop of a
+  // compile-time form: gate+up / down M128 83.3 / 65.5 against 91.6 / 69.5 us).
+  constexpr bool kRmsMF = EPI == EPI_RMS;
+  static_assert(!kRmsMF || MT <= 32, "the RMS epilogue is instantiated up to 32 columns");
+  const bool rms_valu = EPI == EPI_BF16 && MT >= 64 && p.rms;
+  const bool rms_on = kRmsMF || rms_valu;
   float ssq[kUnits];
 #pragma unroll
   for (int i = 0; i < kUnits; ++i) ssq[i] = 0.f;
+  f32x4 racc[NH];
+#pragma unroll
+  for (int h = 0; h < NH; ++h) racc[h] = f32x4{0.f, 0.f, 0.f, 0.f};
   auto xsumsq = [&](bool in_range) {
-    if (EPI == EPI_BF16 && p.rms && in_range) {   // (RMS launches have the BF16 epilogue)
+    if (rms_valu && in_range) {
 #pragma unroll
       for (int i = 0; i < kUnits; ++i) ssq[i] += unit_sumsq(xr[i]);
     }
@@ -909,7 +888,7 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_cs(
   // 32-column kernel reached 129-135 VGPRs and lost a workgroup per CU: down M32
   // 28.2 -> 39.2 us), and 64 in the 10-wave workgroups that run one per CU (163 VGPRs;
   // gate+up M48 / M64 58.9 / 58.8 -> 56.6 / 57.8 us).
-  constexpr bool kEarlyX = MT == 16 || (MT == 32 && kUnits == 1 && EPI == EPI_BF16) ||
+  constexpr bool kEarlyX = MT == 16 || (MT == 32 && kUnits == 1 && EPI != EPI_LOGITS) ||
                            (MT == 64 && NW == 10 && EPI == EPI_BF16);
   auto compute = [&](const TileRegs<SRC>& t, uint32_t g) {
     const uint16_t* xrow = &xs[g & 1u][8 * q];
@@ -946,6 +925,21 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_cs(
     if constexpr (kWn) {
 #pragma unroll
       for (int h = 0; h < NH; ++h) acc[h] += col[h];
+    }
+    if constexpr (kRmsMF) {
+      if (wave < 4) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (wave == j) {   // (wave-uniform)
+#pragma unroll
+            for (int h = 0; h < NH; ++h) {
+              const u32x4 xv =
+                  kEarlyX ? xvs[j][h] : *reinterpret_cast<const u32x4*>(xrow + (16 * h + r) * kXs + 32 * j);
+              racc[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, xv),
+                                                                __builtin_bit_cast(bf16x8_t, xv), racc[h], 0, 0, 0);
+            }
+          }
+      }
     }
     if constexpr (kWn) {
 #pragma unroll
@@ -1018,13 +1012,31 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_cs(
     }
   }
 
-  // RMS launches: each row's sum of x^2 over the K-range: the 16 threads of a row's units
-  // (consecutive lanes) meet in a fixed shuffle tree; one value per row in LDS.  With K
-  // split, every workgroup also leaves its split's value in its group's slot
-  // ss[group][split][row] for the split that completes the group (device scope).
+  // RMS launches: each row's sum of x^2 over the K-range, one value per row in LDS: the
+  // four MFMA partials' diagonals (D[c][c] sits in lane c + 16 (c / 4), element c % 4)
+  // added in wave order, or the 16 threads of a row's units meeting in a fixed shuffle
+  // tree.  With K split, every workgroup also leaves its split's value in its group's
+  // slot ss[group][split][row] for the split that completes the group (device scope).
   __shared__ float s_ss[MT];
   const __amdgpu_buffer_rsrc_t ssrs = make_rsrc(p.ss, gridDim.x * gridDim.y * m_rows * 4u);
-  if (EPI == EPI_BF16 && p.rms) {
+  if constexpr (kRmsMF) {
+    __shared__ float s_xs[4][MT];
+    if (wave < 4) {
+#pragma unroll
+      for (int h = 0; h < NH; ++h)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (r == 4 * q + i) s_xs[wave][16 * h + r] = racc[h][i];
+    }
+    __syncthreads();
+    if ((uint32_t)tid < MT) {
+      const float v = (s_xs[0][tid] + s_xs[1][tid]) + (s_xs[2][tid] + s_xs[3][tid]);
+      s_ss[tid] = v;
+      if (gridDim.y > 1 && (uint32_t)tid < m_rows)
+        st_dev(ssrs, ((blockIdx.x * gridDim.y + blockIdx.y) * m_rows + tid) * 4u, v);
+    }
+    __syncthreads();
+  } else if (rms_valu) {
 #pragma unroll
     for (int i = 0; i < kUnits; ++i) {
       float v = ssq[i];
@@ -1132,7 +1144,7 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_cs(
     }
   } else {
     auto store_y = [&](uint32_t m, f32x4 v, float ss) {
-      if (p.rms) {
+      if (rms_on) {
         const float rms = rms_of(ss, p.k);
 #pragma unroll
         for (int i = 0; i < 4; ++i) v[i] = v[i] / rms;
@@ -1145,7 +1157,7 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_cs(
 #pragma unroll
       for (int h = 0; h < NH; ++h) {
         const uint32_t m = 16u * h + (uint32_t)r;
-        if (m < m_rows && bvalid) store_y(m, acc[h], p.rms ? s_ss[m] : 0.f);
+        if (m < m_rows && bvalid) store_y(m, acc[h], rms_on ? s_ss[m] : 0.f);
       }
     } else {
       // K split: this split's partials [split][m][n] (launch numbering) at device scope;
@@ -1167,7 +1179,7 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_cs(
           for (uint32_t sp = 0; sp < kMaxSplit; ++sp) {   // every load in flight before the adds
             const uint32_t spl = min(sp, gridDim.y - 1u);
             v[sp] = ld_dev4(prs, ((spl * m_rows + m) * p.n + n0) * 4u);
-            ssp[sp] = p.rms ? ld_dev1(ssrs, ((blockIdx.x * gridDim.y + spl) * m_rows + m) * 4u) : 0.f;
+            ssp[sp] = rms_on ? ld_dev1(ssrs, ((blockIdx.x * gridDim.y + spl) * m_rows + m) * 4u) : 0.f;
           }
           f32x4 t = {0.f, 0.f, 0.f, 0.f};
           float ss = 0.f;
@@ -1214,8 +1226,8 @@ hipError_t launch_gemm_src(const GemmArgs& a, int epi, const GemmPlan& pl, hipSt
 #define W12_CS(MT_, EPI_)                                                                     \
   do {                                                                                        \
     if (pl.nw == 10) {                                                                        \
-      if constexpr (EPI_ == EPI_BF16 && (MT_ >= 32 || (MT_ == 16 && plain_bf16(SRC))))       \
-        hipLaunchKernelGGL((k_gemm_cs<MT_, 10, SRC, EPI_BF16>), grid, dim3(640), 0, s, a.x, f32, \
+      if constexpr (EPI_ != EPI_LOGITS && (MT_ >= 32 || (MT_ == 16 && plain_bf16(SRC))))       \
+        hipLaunchKernelGGL((k_gemm_cs<MT_, 10, SRC, EPI_>), grid, dim3(640), 0, s, a.x, f32,   \
                            a.sabs, a.bm, p);                                                  \
       else                                                                                    \
         return hipErrorInvalidValue; /* not instantiated: the plan never asks for it */      \
@@ -1226,12 +1238,12 @@ hipError_t launch_gemm_src(const GemmArgs& a, int epi, const GemmPlan& pl, hipSt
       else                                                                                    \
         return hipErrorInvalidValue; /* not instantiated: the plan never asks for it */      \
     } else if (pl.nw == 9 || pl.nw == 7) {                                                    \
-      if constexpr (EPI_ == EPI_BF16 && MT_ <= 32 && !plain_bf16(SRC)) {                      \
+      if constexpr (EPI_ != EPI_LOGITS && MT_ <= 32 && !plain_bf16(SRC)) {                      \
         if (pl.nw == 9)                                                                       \
-          hipLaunchKernelGGL((k_gemm_cs<MT_, 9, SRC, EPI_BF16>), grid, dim3(576), 0, s, a.x, f32, \
+          hipLaunchKernelGGL((k_gemm_cs<MT_, 9, SRC, EPI_>), grid, dim3(576), 0, s, a.x, f32,  \
                              a.sabs, a.bm, p);                                                \
         else                                                                                  \
-          hipLaunchKernelGGL((k_gemm_cs<MT_, 7, SRC, EPI_BF16>), grid, dim3(448), 0, s, a.x, f32, \
+          hipLaunchKernelGGL((k_gemm_cs<MT_, 7, SRC, EPI_>), grid, dim3(448), 0, s, a.x, f32,  \
                              a.sabs, a.bm, p);                                                \
       } else {                                                                                \
         return hipErrorInvalidValue; /* not instantiated: the plan never asks for it */      \
@@ -1243,11 +1255,17 @@ hipError_t launch_gemm_src(const GemmArgs& a, int epi, const GemmPlan& pl, hipSt
       hipLaunchKernelGGL((k_gemm_cs<MT_, 4, SRC, EPI_>), grid, dim3(256), 0, s, a.x, f32,     \
                          a.sabs, a.bm, p);                         \
   } while (0)
+// (the RMS launches, GemmParams.rms with the BF16 epilogue, run their own instantiation
+// up to 32 columns and the BF16 one's runtime path from 64; the BF16 sources have none)
 #define W12_CS_EPI(MT_)                                                     \
   do {                                                                      \
-    if (epi == EPI_BF16) W12_CS(MT_, EPI_BF16);                            \
-    else if constexpr (!plain_bf16(SRC)) W12_CS(MT_, EPI_LOGITS);           \
+    if (epi == EPI_BF16 && (!p.rms || MT_ >= 64)) W12_CS(MT_, EPI_BF16);   \
+    else if constexpr (plain_bf16(SRC)) return hipErrorInvalidValue;        \
+    else if (epi == EPI_LOGITS) W12_CS(MT_, EPI_LOGITS);                    \
+    else if constexpr (MT_ <= 32) W12_CS(MT_, EPI_RMS);                     \
+    else return hipErrorInvalidValue;                                       \
   } while (0)
+  if (pl.kind != KIND_COLUMN_SYNC && p.rms) return hipErrorInvalidValue;   // (never planned)
   if (pl.kind == KIND_COLUMN_SYNC) {
     if (p.m <= 16) W12_CS_EPI(16);
     else if (p.m <= 32) W12_CS_EPI(32);

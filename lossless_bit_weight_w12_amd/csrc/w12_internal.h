@@ -28,6 +28,7 @@ enum Src : int {
 enum Epi : int {
   EPI_BF16 = 0,    // y = bf16(x . W^T)
   EPI_LOGITS = 1,  // per-row-block maxima (+ fp32 logits [m][n] when asked for): verification pass 1
+  EPI_RMS = 2,     // y = bf16((x . W^T) / rms(x)) per row (GemmParams.rms launches, W12 sources)
 };
 
 // One weight of a launch.  A launch multiplies one x by up to kMaxSeg weights that
