@@ -1169,24 +1169,37 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_cs(
         if (m < m_rows && bvalid) st_dev(prs, ((split * m_rows + m) * p.n + n0) * 4u, acc[h]);
       }
       if (split_last(p.tickets, blockIdx.x)) {
+        // two 16-row halves at a time have every split's partials requested before any is
+        // used (one round trip per pair: the halves one after the other cost the decode
+        // chain's split launches a round trip each).  Rows past m read the last row's
+        // partials, a wave past the last row-block reads past them (inside the resource,
+        // or beyond it, which returns zeros without an access); neither is stored.
+        constexpr int kHC = NH < 2 ? NH : 2;
 #pragma unroll
-        for (int h = 0; h < NH; ++h) {
-          const uint32_t m = 16u * h + (uint32_t)r;
-          if (m >= m_rows || !bvalid) continue;
-          f32x4 v[kMaxSplit];
-          float ssp[kMaxSplit];
+        for (int h0 = 0; h0 < NH; h0 += kHC) {
+          f32x4 v[kHC][kMaxSplit];
+          float ssp[kHC][kMaxSplit];
 #pragma unroll
-          for (uint32_t sp = 0; sp < kMaxSplit; ++sp) {   // every load in flight before the adds
-            const uint32_t spl = min(sp, gridDim.y - 1u);
-            v[sp] = ld_dev4(prs, ((spl * m_rows + m) * p.n + n0) * 4u);
-            ssp[sp] = rms_on ? ld_dev1(ssrs, ((blockIdx.x * gridDim.y + spl) * m_rows + m) * 4u) : 0.f;
+          for (int hh = 0; hh < kHC; ++hh) {
+            const uint32_t m = min(16u * (h0 + hh) + (uint32_t)r, m_rows - 1u);
+#pragma unroll
+            for (uint32_t sp = 0; sp < kMaxSplit; ++sp) {
+              const uint32_t spl = min(sp, gridDim.y - 1u);
+              v[hh][sp] = ld_dev4(prs, ((spl * m_rows + m) * p.n + n0) * 4u);
+              ssp[hh][sp] = rms_on ? ld_dev1(ssrs, ((blockIdx.x * gridDim.y + spl) * m_rows + m) * 4u) : 0.f;
+            }
           }
-          f32x4 t = {0.f, 0.f, 0.f, 0.f};
-          float ss = 0.f;
 #pragma unroll
-          for (uint32_t sp = 0; sp < kMaxSplit; ++sp)
-            if (sp < gridDim.y) { t += v[sp]; ss += ssp[sp]; }
-          store_y(m, t, ss);
+          for (int hh = 0; hh < kHC; ++hh) {
+            const uint32_t m = 16u * (h0 + hh) + (uint32_t)r;
+            if (m >= m_rows || !bvalid) continue;
+            f32x4 t = {0.f, 0.f, 0.f, 0.f};
+            float ss = 0.f;
+#pragma unroll
+            for (uint32_t sp = 0; sp < kMaxSplit; ++sp)
+              if (sp < gridDim.y) { t += v[hh][sp]; ss += ssp[hh][sp]; }
+            store_y(m, t, ss);
+          }
         }
       }
     }
