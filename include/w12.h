@@ -200,7 +200,8 @@ w12_status w12_gemm_group(const uint16_t* x, uint32_t m, const w12_desc* const* 
  * y[row] = bf16((x[row] . W^T) / r), r = sqrt(mean_k x[row,k]^2) in FP32, the division
  * applied to the FP32 accumulators (equal to the product of the rescaled row up to
  * rounding; the rescaled row itself is never rounded to BF16).  r comes from the x values
- * each launch streams anyway, summed in a fixed order.  Arguments, workspace
+ * each launch streams anyway (up to 32 rows as matrix-core products of x with itself,
+ * from 33 rows per-unit sums), summed the same way on every call.  Arguments, workspace
  * (W12_OP_GEMM / W12_OP_GEMM_GROUP), errors and determinism as w12_gemm /
  * w12_gemm_group.  Not part of the W12 method itself. */
 w12_status w12_gemm_rms(const uint16_t* x, uint32_t m, const w12_desc* d, uint16_t* y,
