@@ -548,3 +548,71 @@ def screen_logits_reference(x: np.ndarray, q: np.ndarray, s_bits: np.ndarray):
     xf = bf16_to_f64(x)
     what = screen_weights(q, s_bits)
     return xf @ what.T, np.abs(xf) @ np.abs(what).T
+
+
+# ----------------------------------------------------------------------------- FP8 GEMM
+# FP8 GEMM routing ("SpecPilot: an agent doubled speculative decoding speed, and the
+# 10.87x needs context", section "The mechanisms it found": FP8 GEMM routing is one of
+# the batching mechanisms; "StargazerX0/SpecPilot", section "What it is": three of the
+# batching settings run FP8 targets).  The pages give no format.  Reading taken here:
+# the target's own FP8 weights in the usual checkpoint form, and BF16 activations --
+#   codes    q[n][k], one OCP FP8 E4M3 byte per weight: sign bit, 4 exponent bits
+#            (bias 7), 3 mantissa bits; exponent field 0 is subnormal (m/8 * 2^-6);
+#            no infinities; S.1111.111 is NaN (the largest finite is 448)
+#   scales   s[n // 128][k // 128], one FP32 value per 128 x 128 block
+#   weight   W[n][k] = E4M3(q[n][k]) * s[n // 128][k // 128]
+#   product  y = x . W^T, accepted by the same rule as every other GEMM here
+#   tiles    16 rows x 128 columns, 2048 bytes at (g*(N/16) + b)*2048 (column-major
+#            tile order, as W12): the code of element t of lane slot l (the W12 slot
+#            layout) at the W12 sign/mantissa byte position 1024*(t//16) + 16*l + t%16.
+# For such a target this product is the target's own (lossless): no weight is changed.
+F8_TILE_BYTES = 2048
+F8_BLOCK = 128
+
+
+def f8_e4m3_to_f64(b: np.ndarray) -> np.ndarray:
+    """Values of E4M3 bytes (float64; NaN for S.1111.111)."""
+    b = np.asarray(b, dtype=np.uint8).astype(np.int64)
+    sign = np.where(b >> 7, -1.0, 1.0)
+    e = (b >> 3) & 0xF
+    m = b & 0x7
+    mag = np.where(e == 0, np.ldexp(m / 8.0, -6), np.ldexp(1.0 + m / 8.0, e - 7))
+    return np.where((e == 0xF) & (m == 0x7), np.nan, sign * mag)
+
+
+def f8_weights(q: np.ndarray, s: np.ndarray) -> np.ndarray:
+    """W = E4M3(q) * block scale in float64 (exact: a 4-bit significand times an FP32
+    value).  q uint8 [N, K], s float32 [ceil(N/128), K/128]."""
+    n, k = q.shape
+    srow = np.asarray(s, dtype=np.float64)[np.arange(n) // F8_BLOCK]           # [N, K/128]
+    return f8_e4m3_to_f64(q) * np.repeat(srow, F8_BLOCK, axis=1)[:, :k]
+
+
+def f8_pack(q: np.ndarray) -> np.ndarray:
+    """Tile bytes of FP8 codes q uint8 [N, K] (uint8 [(N/16)*(K/128)*2048]), layout above."""
+    n, k = q.shape
+    check_shape(n, k)
+    nb, gk = n // TILE_ROWS, k // TILE_K
+    r, kappa, pos, _, _ = slot_layout()
+    out = np.zeros((gk, nb, F8_TILE_BYTES), dtype=np.uint8)
+    qt = np.asarray(q, dtype=np.uint8).reshape(nb, TILE_ROWS, gk, TILE_K).transpose(2, 0, 1, 3)
+    out[:, :, pos.ravel()] = qt[:, :, r.ravel(), kappa.ravel()]
+    return out.reshape(-1)
+
+
+def gemm_f8_reference(x: np.ndarray, q: np.ndarray, s: np.ndarray, rows_per_chunk: int = 8192):
+    """z = x . W^T and S = |x| . |W|^T in float64 for BF16 bits x [M, K] and the FP8 weight
+    (q, s).  Each product x*W has at most 8 + 4 + 24 significant bits, exact in float64;
+    the float64 sum is within K*2^-53*S of the exact value."""
+    if rows_per_chunk % F8_BLOCK:
+        raise ValueError("rows_per_chunk must be a multiple of 128")
+    xf = bf16_to_f64(x)
+    n = q.shape[0]
+    z = np.empty((x.shape[0], n))
+    sa = np.empty((x.shape[0], n))
+    for n0 in range(0, n, rows_per_chunk):
+        n1 = min(n, n0 + rows_per_chunk)
+        wf = f8_weights(q[n0:n1], s[n0 // F8_BLOCK:(n1 + F8_BLOCK - 1) // F8_BLOCK])
+        z[:, n0:n1] = xf @ wf.T
+        sa[:, n0:n1] = np.abs(xf) @ np.abs(wf).T
+    return z, sa

@@ -582,6 +582,110 @@ def test_screen_bound_holds_and_is_tight():
             assert abs(Fraction(float(z8[0, 0])) - z8x) <= Fraction(k * 2.0 ** -53 * float(s8[0, 0]))
 
 
+# ----------------------------------------------------------------------------- FP8 GEMM
+# Values of the OCP 8-bit floating point specification's E4M3 format (bias 7, no
+# infinities, S.1111.111 NaN): zero, the smallest subnormal 2^-9, the largest subnormal
+# 7 * 2^-9, the smallest normal 2^-6, 1, 1.5, 2, 240, and the largest finite 448.
+F8_SPEC = {0x00: 0.0, 0x01: 2.0 ** -9, 0x07: 7 * 2.0 ** -9, 0x08: 2.0 ** -6, 0x38: 1.0,
+           0x3C: 1.5, 0x40: 2.0, 0x77: 240.0, 0x7E: 448.0, 0xB8: -1.0, 0xFE: -448.0}
+# E4M3 codes of small integers (same specification): value -> code
+F8_INT = {0: 0x00, 1: 0x38, 2: 0x40, 3: 0x44, 4: 0x48, 5: 0x4A, 6: 0x4C, 7: 0x4E, 8: 0x50}
+
+
+def test_f8_decode_matches_torch_float8():
+    """All 256 codes against torch's float8_e4m3fn (a library decoding of the format)."""
+    import torch
+    b = np.arange(256, dtype=np.uint8)
+    mine = o.f8_e4m3_to_f64(b)
+    ref = torch.from_numpy(b.copy()).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert set(np.flatnonzero(np.isnan(mine)).tolist()) == {0x7F, 0xFF}
+    assert np.array_equal(np.isnan(mine), np.isnan(ref))
+    ok = ~np.isnan(mine)
+    assert np.array_equal(mine[ok], ref[ok])
+    assert np.array_equal(np.signbit(mine[ok]), np.signbit(ref[ok]))
+
+
+def test_f8_decode_spec_values():
+    for code, v in F8_SPEC.items():
+        assert o.f8_e4m3_to_f64(np.array([code], dtype=np.uint8))[0] == v, hex(code)
+    for v, code in F8_INT.items():
+        assert o.f8_e4m3_to_f64(np.array([code, code | 0x80], dtype=np.uint8)).tolist() == [v, -v]
+    assert np.signbit(o.f8_e4m3_to_f64(np.array([0x80], dtype=np.uint8))[0])
+    pos = o.f8_e4m3_to_f64(np.arange(0x7F, dtype=np.uint8))
+    assert (np.diff(pos) > 0).all()          # codes 0x00..0x7E strictly increasing
+
+
+def test_f8_values_are_bf16_values():
+    """Every finite E4M3 value is a BF16 value (what an exact conversion to BF16 needs)."""
+    v = o.f8_e4m3_to_f64(np.arange(256, dtype=np.uint8))
+    v = v[~np.isnan(v)]
+    assert np.array_equal(o.bf16_to_f64(o.bf16_round(v)), v)
+
+
+def test_f8_pack_positions():
+    """Hand-placed elements of a 32 x 256 weight (2 row-blocks, 2 tile columns): element
+    (row 16b + r, column 128g + 32j + 8q' + i) of lane slot l = 16q' + r, t = 8j + i, lands
+    at (g*2 + b)*2048 + 1024*(t//16) + 16*l + t%16."""
+    q = np.zeros((32, 256), dtype=np.uint8)
+    cases = {(17, 200): 7440, (15, 127): 2047, (16, 0): 2048, (0, 128): 4096, (0, 0): 0,
+             (1, 8): 16 * 17, (0, 32): 8}
+    for i, (rc, _) in enumerate(cases.items()):
+        q[rc] = i + 1
+    t = o.f8_pack(q)
+    assert t.size == 32 * 256 and np.count_nonzero(t) == len(cases)
+    for i, (_, pos) in enumerate(cases.items()):
+        assert t[pos] == i + 1, pos
+
+
+def test_f8_pack_is_a_per_tile_permutation():
+    g = np.random.default_rng(80)
+    q = g.integers(0, 256, (48, 384)).astype(np.uint8)
+    t = o.f8_pack(q).reshape(3, 3, 2048)                      # [g, b, bytes]
+    for gg in range(3):
+        for b in range(3):
+            blk = q[16 * b:16 * b + 16, 128 * gg:128 * gg + 128].ravel()
+            assert np.array_equal(np.sort(t[gg, b]), np.sort(blk))
+
+
+def test_gemm_f8_integer_closed_form():
+    """Unit scales and small-integer codes: z and S are integer products, exactly."""
+    g = np.random.default_rng(81)
+    a = g.integers(-8, 9, (144, 256))
+    codes = np.vectorize(lambda v: F8_INT[abs(int(v))] | (0x80 if v < 0 else 0))(a).astype(np.uint8)
+    xi = g.integers(-20, 21, (3, 256))
+    x = wi.f32_to_bf16_bits(xi.astype(np.float32))
+    s = np.ones((2, 2), dtype=np.float32)
+    z, sa = o.gemm_f8_reference(x, codes, s)
+    assert np.array_equal(z, (xi @ a.T).astype(np.float64))
+    assert np.array_equal(sa, (np.abs(xi) @ np.abs(a).T).astype(np.float64))
+
+
+def test_gemm_f8_vs_exact_rationals():
+    """Random codes and FP32 scales on a ragged block grid (144 rows: a full and a partial
+    128-row block; 3 column blocks): the oracle against exact rational sums of
+    x * E4M3(q) * s with the codes decoded by torch and s taken from its FP32 value."""
+    import torch
+    g = np.random.default_rng(82)
+    n, k, m = 144, 384, 2
+    q = g.integers(0, 256, (n, k)).astype(np.uint8)
+    q[(q & 0x7F) == 0x7F] = 0x3A                                 # no NaN codes
+    s = (g.uniform(0.5, 2.0, (2, 3)) * 2.0 ** g.integers(-12, 3, (2, 3))).astype(np.float32)
+    x = wi.gaussian_bf16((m, k), 1.0, g)
+    qv = torch.from_numpy(q.copy()).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    z, sa = o.gemm_f8_reference(x, q, s)
+    for row in range(m):
+        xr = [bf16_fraction(v) for v in x[row]]
+        for col in range(n):
+            acc = Fraction(0)
+            mag = Fraction(0)
+            for kk in range(k):
+                w = Fraction(float(qv[col, kk])) * Fraction(float(s[col // 128, kk // 128]))
+                acc += xr[kk] * w
+                mag += abs(xr[kk] * w)
+            assert abs(Fraction(z[row, col]) - acc) <= k * Fraction(2) ** -53 * mag
+            assert abs(Fraction(sa[row, col]) - mag) <= k * Fraction(2) ** -53 * mag
+
+
 # ----------------------------------------------------------------------------- mutations
 def _pins_fail(fn):
     try:
@@ -719,3 +823,35 @@ def test_mutation_screen_residual_halved_is_caught(monkeypatch):
     orig = o.screen_row_sums_exact
     monkeypatch.setattr(o, "screen_row_sums_exact", lambda w, q, s: (orig(w, q, s)[0] // 4, orig(w, q, s)[1]))
     assert _pins_fail(test_screen_bound_holds_and_is_tight)
+
+
+def test_mutation_f8_scale_per_16_rows_is_caught(monkeypatch):
+    def bad(q, s):
+        n, k = q.shape
+        srow = np.asarray(s, dtype=np.float64)[np.minimum(np.arange(n) // 16, s.shape[0] - 1)]
+        return o.f8_e4m3_to_f64(q) * np.repeat(srow, o.F8_BLOCK, axis=1)[:, :k]
+    monkeypatch.setattr(o, "f8_weights", bad)
+    assert _pins_fail(test_gemm_f8_vs_exact_rationals)
+
+
+def test_mutation_f8_subnormal_scale_is_caught(monkeypatch):
+    orig = o.f8_e4m3_to_f64
+
+    def bad(b):
+        v = orig(b)
+        e = (np.asarray(b, dtype=np.uint8) >> 3) & 0xF
+        return np.where(e == 0, 2 * v, v)          # subnormals read at 2^-5 instead of 2^-6
+    monkeypatch.setattr(o, "f8_e4m3_to_f64", bad)
+    assert _pins_fail(test_f8_decode_matches_torch_float8)
+    assert _pins_fail(test_f8_decode_spec_values)
+
+
+def test_mutation_f8_pack_group_halves_swapped_is_caught(monkeypatch):
+    orig = o.slot_layout
+
+    def bad():
+        r, kap, pos, wp, bit = orig()
+        t = np.arange(32)[None, :]
+        return r, kap, 1024 * ((t // 8) % 2) + 16 * np.arange(64)[:, None] + (t % 8) + 8 * (t // 16), wp, bit
+    monkeypatch.setattr(o, "slot_layout", bad)
+    assert _pins_fail(test_f8_pack_positions)

@@ -144,6 +144,47 @@ def device_layer_weight(torch, layer: int, mat: int, n: int, k: int, device="cud
     return w.to(torch.bfloat16)
 
 
+# ----------------------------------------------------------------------------- FP8 weights
+F8_MAX = 448.0     # largest finite OCP FP8 E4M3 value
+F8_BLOCK = 128     # checkpoint block: one scale per 128 x 128 weights
+
+
+def f8_quantize(torch, w):
+    """Checkpoint form of a float32 weight w [n, k] (a torch tensor on any device; k a
+    multiple of 128): one FP32 scale per 128 x 128 block, s = (block max |w|) / 448 (1 for
+    an all-zero block; the last block row covers the rows past the last multiple of 128),
+    and codes q = w / s, clamped to +-448 and cast by torch to float8_e4m3fn (round to
+    nearest even), returned as uint8 bytes.  Returns (q uint8 [n, k], s float32
+    [ceil(n/128), k/128])."""
+    n, k = w.shape
+    nbk = (n + F8_BLOCK - 1) // F8_BLOCK
+    wp = torch.nn.functional.pad(w, (0, 0, 0, nbk * F8_BLOCK - n))
+    amax = wp.abs().reshape(nbk, F8_BLOCK, k // F8_BLOCK, F8_BLOCK).amax(dim=(1, 3))
+    s = torch.where(amax > 0, amax / F8_MAX, torch.ones_like(amax)).to(torch.float32)
+    srow = s.repeat_interleave(F8_BLOCK, 0)[:n].repeat_interleave(F8_BLOCK, 1)
+    v = (w / srow).clamp(-F8_MAX, F8_MAX)
+    return v.to(torch.float8_e4m3fn).view(torch.uint8), s
+
+
+def f8_weight(c: int, t: int, shape, sigma: float = SIGMA_W):
+    """Host FP8 checkpoint weight: the BF16 Gaussian weight(c, t, shape) in float32,
+    quantized by f8_quantize.  Returns numpy (q uint8 [n, k], s float32)."""
+    import torch
+    w = torch.from_numpy(bf16_bits_to_f32(weight(c, t, shape, sigma)))
+    q, s = f8_quantize(torch, w)
+    return q.numpy(), s.numpy()
+
+
+def device_f8_weight(torch, seed: int, n: int, k: int, device="cuda"):
+    """FP8 checkpoint weight drawn on the device: randn(float32) * 0.02 from
+    torch.Generator(device) seeded with `seed`, quantized by f8_quantize."""
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    w = torch.randn((n, k), generator=g, device=device, dtype=torch.float32)
+    w.mul_(SIGMA_W)
+    return f8_quantize(torch, w)
+
+
 # ----------------------------------------------------------------------------- workload 4
 VERIFY_BATCHES = 3        # batch 0 plain, batches 1-2 carry the 32 near-tie rows
 
