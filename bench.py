@@ -25,9 +25,12 @@ Protocol:
   * the streaming-read ceiling for the same byte counts (w12_stream_read, the GEMM's own
     nontemporal loads, best of several grid sizes, rotated over 2 GiB).
 
-Two more workloads are timed in the same run and reported beside the main line:
-the LM-head greedy verification ([151936, 5120], M = 16) and a whole weight-streaming
-decode step (64 layers of q, k, v, o, gate, up, down + LM head, M = 24, RMS-chained).
+More workloads are timed in the same run and reported beside the main line: the same
+matrices at M = 64 and 128 (batched regime); the same shapes in FP8 checkpoint form (E4M3
+codes with FP32 128 x 128 block scales, the GEMMs of FP8 targets) at M = 1..128, their
+sampled outputs checked by the oracle first; the LM-head greedy verification ([151936,
+5120], M = 16, and 24 requests in one pass) and a whole weight-streaming decode step (64
+layers of q, k, v, o, gate, up, down + LM head, M = 24, RMS-chained).
 
 `roofline.traffic` is the HBM traffic of the dominant launch measured by rocprofv3
 counters (FETCH_SIZE and WRITE_SIZE passes over `--profile-only --calibrate-copy`,
@@ -112,6 +115,59 @@ def cpu_baseline(host_w, xs_host, gpu_out, seconds_target: float = 12.0):
                       f"gate+up [{rows}x{K_GU}] and down [{rows}x{K_DN}] matrices, M in {list(MS)}, "
                       f"{reps} passes, {t_total:.1f} s; BLAS threads {blas_threads}"}
     return base, parity
+
+
+def f8_parity(x_host, q_rows, s_rows, y_rows):
+    """Oracle check of sampled FP8 GEMM outputs (cpu_baseline leg): the first 128-row
+    scale block of a matrix (q_rows, s_rows) against the GPU's outputs on those rows."""
+    from oracle import w12_oracle as o
+    z, sa = o.gemm_f8_reference(x_host, q_rows, s_rows)
+    return bool(o.gemm_accept(y_rows, z, sa).all())
+
+
+def f8_bytes(n: int, k: int, m: int) -> int:
+    """Algorithmic bytes of one FP8 GEMM: the codes, the block scales, x and y."""
+    return n * k + 4 * ((n + 127) // 128) * (k // 128) + 2 * m * k + 2 * m * n
+
+
+def fp8_gemms(torch, w12, wi, np, dev, n_copies, per, batched, check):
+    """FP8 GEMM routing: the MLP matrices in FP8 checkpoint form (the Gaussian draw of the
+    device generator quantized to E4M3 with 128 x 128 block scales) at every M of the step
+    and of the batched regime, beside W12 and the tiled BF16 kernel on the same shapes.
+    With `check`, sampled outputs of an untimed pass are checked against the oracle first."""
+    res, parity = {}, {}
+    for name, n, k, seed, tx in (("gate_up", N_GU, K_GU, 2026_0800, wi.T_X),
+                                 ("down", N_DN, K_DN, 2026_0801, wi.T_X2)):
+        q0, s0 = wi.device_f8_weight(torch, seed, n, k, dev)
+        q_rows, s_rows = q0[:128].cpu().numpy(), s0[:1].cpu().numpy()
+        copies = [w12.f8_tile(q0)]
+        del q0
+        while len(copies) < n_copies(n * k):
+            copies.append(copies[0].clone())
+        for m in MS + BATCHED_MS:
+            x_host = wi.activations(3, tx, m, k)
+            x = torch.from_numpy(x_host.view(np.int16)).to(dev)
+            y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+            key = f"M{m}_{name}"
+            if check:
+                w12.gemm_f8(x, copies[0], s0, n, k, out=y)
+                y_rows = y[:, :128].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+                parity[key] = f8_parity(x_host, q_rows, s_rows, y_rows)
+            us, _ = launch_rounds(torch, lambda i: w12.gemm_f8(x, copies[i % len(copies)], s0, n, k,
+                                                               out=y))
+            ref = per.get(key) or batched.get(key)
+            res[key] = {"us_f8": round(us, 2), "gbps_f8": round(f8_bytes(n, k, m) / us / 1e3, 1),
+                        "pct_peak_f8": round(100 * f8_bytes(n, k, m) / us / 1e3 / PEAK_GBPS, 1),
+                        "us_w12": ref["us_w12"], "speedup_vs_w12": round(ref["us_w12"] / us, 3),
+                        "speedup_vs_bf16_tiled": round(ref["us_bf16_tiled"] / us, 3)}
+        del copies
+    res["format"] = "E4M3 codes, FP32 scale per 128x128 block, BF16 x, FP32 accumulation"
+    res["rotated_copies"] = {"gate_up": n_copies(N_GU * K_GU), "down": n_copies(N_DN * K_DN)}
+    if check:
+        res["parity_sampled_vs_oracle"] = parity
+        if not all(parity.values()):
+            raise RuntimeError(f"FP8 GEMM outputs outside the oracle's acceptance rule: {parity}")
+    return res
 
 
 COPY_BYTES = 1 << 30
@@ -514,7 +570,7 @@ def main():
     ap.add_argument("--profile-decode", action="store_true",
                     help="build the 64-layer decode stack, run --steps steps and exit (for rocprofv3)")
     ap.add_argument("--profile-batched", action="store_true",
-                    help="run --steps batched GEMMs (M = 64, 128) and batched verifications and exit")
+                    help="run --steps batched GEMMs (W12 at M = 64, 128; FP8 at M = 1, 16, 32, 64, 128) and batched verifications and exit")
     ap.add_argument("--profile-verify", action="store_true",
                     help="run --steps LM-head verifications (M = 16) and exit (for rocprofv3)")
     args = ap.parse_args()
@@ -546,8 +602,8 @@ def main():
         log("bench: profile-verify run done")
         return
     if args.profile_batched:
-        # batched regime: the MLP matrices at 64 and 128 rows, then the 24-request
-        # verification on the LM head
+        # batched regime: the MLP matrices at 64 and 128 rows (W12, then FP8), then the
+        # 24-request verification on the LM head
         for name, t, k in (("gate_up", (N_GU, K_GU), wi.T_W), ("down", (N_DN, K_DN), wi.T_W2)):
             tt = w12.encode(torch.from_numpy(wi.weight(3, k, t).view(np.int16)).to(dev))
             for m in BATCHED_MS:
@@ -556,6 +612,17 @@ def main():
                 for _ in range(args.steps):
                     w12.gemm(xb, tt, out=yb_)
             del tt
+        # the same shapes in FP8 checkpoint form (M 1, 16, 32, 64, 128)
+        for name, (n, k), seed in (("gate_up", (N_GU, K_GU), 2026_0800), ("down", (N_DN, K_DN), 2026_0801)):
+            q0, s0 = wi.device_f8_weight(torch, seed, n, k, dev)
+            qt = w12.f8_tile(q0)
+            del q0
+            for m in (1, 16, 32) + BATCHED_MS:
+                xb = torch.from_numpy(wi.activations(3, wi.T_X, m, k).view(np.int16)).to(dev)
+                yb_ = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+                for _ in range(args.steps):
+                    w12.gemm_f8(xb, qt, s0, n, k, out=yb_)
+            del qt
         c5 = wi.CONFIG_SHAPES[5]
         head = w12.encode(wi.device_lm_head(torch, c5["vocab"], c5["hidden"]))
         xb = torch.from_numpy(wi.batched_verify_x().view(np.int16)).to(dev)
@@ -765,6 +832,9 @@ def main():
                 "us_w12": round(us_w, 2), "gbps_w12": round(gemm_bytes(tl[0], m) / us_w / 1e3, 1),
                 "us_bf16_tiled": round(us_b, 2), "speedup_vs_bf16_tiled": round(us_b / us_w, 3)}
     log(f"bench: batched GEMMs {batched}")
+    log("bench: FP8 GEMMs ...")
+    fp8 = fp8_gemms(torch, w12, wi, np, dev, n_copies, per, batched, not args.no_cpu_baseline)
+    log(f"bench: FP8 GEMMs {fp8}")
 
     # dominant kernel = the (M, matrix) GEMM with the largest share of the step; its
     # achieved bandwidth from the mean launch time over its timed rounds
@@ -810,6 +880,7 @@ def main():
         "per_gemm": per,
         "read_ceiling": ceiling,
         "batched_gemm": batched,
+        "fp8_gemm": fp8,
         "encode": encode_info,
         "roofline": roofline,
         "cpu_baseline": cpu_base,

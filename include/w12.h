@@ -48,7 +48,8 @@
  *    faults surface at the caller's next synchronisation.
  *  - The workspace `ws` (device, w12_workspace_bytes(op, ...) bytes, 256-byte aligned;
  *    may be NULL when that size is 0) holds intermediate results.  GEMM workspaces
- *    (W12_OP_GEMM, W12_OP_GEMM_BF16, W12_OP_GEMM_GROUP) begin with the split-K tickets
+ *    (W12_OP_GEMM, W12_OP_GEMM_BF16, W12_OP_GEMM_GROUP, W12_OP_GEMM_F8) begin with the
+ *    split-K tickets
  *    (4096 bytes), which must be zero before the first call that uses the workspace
  *    (a zero-filled allocation, or w12_workspace_init); every call leaves them zero, so
  *    one zeroing serves every later call of any shape.  Nothing else in any workspace
@@ -101,6 +102,7 @@ typedef struct w12_desc {
 #define W12_OP_VERIFY    4
 #define W12_OP_GEMM_GROUP 5   /* n = the group's rows added up */
 #define W12_OP_VERIFY2   6   /* two-level verification (w12_lmhead_verify2) */
+#define W12_OP_GEMM_F8   7   /* FP8 GEMM (w12_gemm_f8) */
 
 /* Bytes of the tile array: (n/16)*(k/128)*3072; 0 if the shape is invalid. */
 size_t w12_tiles_bytes(uint64_t n, uint64_t k);
@@ -228,6 +230,31 @@ w12_status w12_bf16_tile(const uint16_t* w, uint64_t n, uint64_t k, void* w_tile
 w12_status w12_gemm_bf16_tiled(const uint16_t* x, uint32_t m, const void* w_tiled, uint64_t n,
                                uint64_t k, uint16_t* y, void* ws, size_t ws_bytes,
                                void* stream);
+
+/* FP8 GEMM routing (review page, "The mechanisms it found": FP8 GEMM routing among the
+ * batching mechanisms; "StargazerX0/SpecPilot", "What it is": batching settings with FP8
+ * targets).  The pages give no format; this library reads it as the target's own FP8
+ * weights in the common checkpoint form: W[n][k] = q[n][k] * s[n/128][k/128], q one OCP
+ * FP8 E4M3 byte per weight (bias 7, no infinities, S.1111.111 NaN), s one FP32 scale per
+ * 128 x 128 block, with BF16 activations.  The product is the W12 GEMM's with those
+ * weights: every x * q is exact in FP32, each 128-column block sum is multiplied by its
+ * scale, the result rounded once to BF16, so it is lossless for such a target to the
+ * same accumulation tolerance as w12_gemm.
+ * w12_f8_tile writes the tiled copy of row-major q [n][k] (device, n*k bytes, 16-byte
+ * aligned) into w_tiled (device, n*k bytes, 16-byte aligned): tile (b, g) at
+ * (g*(n/16) + b)*2048 (column-major), the 8 bytes of lane slot l (r = l%16, q = l/16) in
+ * group j (row 16b + r, columns 128g + 32j + 8q .. +7) at 1024*(j/2) + 16l + 8*(j%2).
+ * w12_gemm_f8: y[row] = bf16(sum_k x[row,k] * q[n,k] * s[n/128][k/128]) for x device
+ * BF16 [m][k] (m in 1..W12_MAX_M, 16-byte aligned), w_tiled as written by w12_f8_tile,
+ * scale device FP32 [ceil(n/128)][k/128] row-major (4-byte aligned; the last block row
+ * covers the rows past the last multiple of 128), y device BF16 [m][n].
+ * ws: w12_workspace_bytes(W12_OP_GEMM_F8, m, n, k) bytes, as for w12_gemm.  Shapes,
+ * errors and determinism as w12_gemm; finite x, q and s keep the result within that
+ * tolerance, a NaN byte makes its rows' outputs NaN. */
+w12_status w12_f8_tile(const uint8_t* w, uint64_t n, uint64_t k, void* w_tiled, void* stream);
+w12_status w12_gemm_f8(const uint16_t* x, uint32_t m, const void* w_tiled, const float* scale,
+                       uint64_t n, uint64_t k, uint16_t* y, void* ws, size_t ws_bytes,
+                       void* stream);
 
 /* Greedy verification over the LM head (review page, "The mechanisms it found":
  * certified exact-argmax LM head; "StargazerX0/SpecPilot", "Results and

@@ -1,12 +1,14 @@
 """W12 on MI355X: lossless 12-bit BF16 weights decoded inside the GEMM, plus greedy
 verification with a certified exact-argmax LM head, in one pass over the W12 head or in
-two levels (an 8-bit screen copy first).  The compute lives in libw12.so (HIP kernels for
+two levels (an 8-bit screen copy first), and the GEMMs of FP8 targets (E4M3 weights with
+128 x 128 block scales) in the same kernel family.  The compute lives in libw12.so (HIP kernels for
 gfx950 behind a C ABI, declared in include/w12.h); this package is its thin Python
 binding."""
 from .w12 import (ENCODE_TOTAL_OFFSET, EXPORTS, MAX_GROUP, MAX_M, NOALLOC_SCRATCH_BYTES,
-                  OP_DECODE, OP_ENCODE, OP_GEMM, OP_GEMM_BF16, OP_GEMM_GROUP, OP_VERIFY,
-                  OP_VERIFY2, Prepared, ScreenCopy, W12Desc, W12Error, W12Tensor, bf16_tile,
-                  decode, encode, gemm, gemm_bf16, gemm_bf16_tiled, gemm_group, gemm_noalloc,
+                  OP_DECODE, OP_ENCODE, OP_GEMM, OP_GEMM_BF16, OP_GEMM_F8, OP_GEMM_GROUP,
+                  OP_VERIFY, OP_VERIFY2, Prepared, ScreenCopy, W12Desc, W12Error, W12Tensor, bf16_tile,
+                  decode, encode, f8_tile, gemm, gemm_bf16, gemm_bf16_tiled, gemm_f8,
+                  gemm_group, gemm_noalloc,
                   lib, lib_path, lmhead_verify, lmhead_verify2, lmhead_verify2_batched,
                   lmhead_verify_batched, logits_f32, prepare_gemm, prepare_gemm_group,
                   prepare_rms, prepare_verify, prepare_verify2, prepare_verify2_batched,
@@ -15,9 +17,11 @@ from .w12 import (ENCODE_TOTAL_OFFSET, EXPORTS, MAX_GROUP, MAX_M, NOALLOC_SCRATC
                   workspace, workspace_bytes)
 
 __all__ = ["ENCODE_TOTAL_OFFSET", "EXPORTS", "MAX_GROUP", "MAX_M", "NOALLOC_SCRATCH_BYTES",
-           "OP_DECODE", "OP_ENCODE", "OP_GEMM", "OP_GEMM_BF16", "OP_GEMM_GROUP", "OP_VERIFY",
+           "OP_DECODE", "OP_ENCODE", "OP_GEMM", "OP_GEMM_BF16", "OP_GEMM_F8", "OP_GEMM_GROUP",
+           "OP_VERIFY",
            "OP_VERIFY2", "Prepared", "ScreenCopy", "W12Desc", "W12Error", "W12Tensor",
-           "bf16_tile", "decode", "encode", "gemm", "gemm_bf16", "gemm_bf16_tiled", "gemm_group",
+           "bf16_tile", "decode", "encode", "f8_tile", "gemm", "gemm_bf16", "gemm_bf16_tiled",
+           "gemm_f8", "gemm_group",
            "gemm_noalloc", "lib", "lib_path", "lmhead_verify", "lmhead_verify2",
            "lmhead_verify2_batched", "lmhead_verify_batched", "logits_f32", "prepare_gemm",
            "prepare_gemm_group", "prepare_rms", "prepare_verify", "prepare_verify2",

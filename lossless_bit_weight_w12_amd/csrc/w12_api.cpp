@@ -622,6 +622,7 @@ size_t w12_workspace_bytes(int op, uint32_t m, uint64_t n, uint64_t k) {
     case W12_OP_DECODE: return 0;
     case W12_OP_GEMM:
     case W12_OP_GEMM_BF16:
+    case W12_OP_GEMM_F8:   // (FP8 tiles are planned as W12 tiles)
       if (m < 1 || m > W12_MAX_M || !mn_ok(m, n)) return 0;
       return gemm_ws_bytes(m, n, k, op == W12_OP_GEMM_BF16);
     case W12_OP_VERIFY:
@@ -782,6 +783,40 @@ w12_status w12_gemm_bf16_tiled(const uint16_t* x, uint32_t m, const void* w_tile
   fill_params(a.p, m, k, n, 1);
   if (!set_split_ws(a, ws, p, m, n)) return W12_ERR_HIP;
   return hip_status(launch_gemm(a, SRC_BF16T, EPI_BF16, p, (hipStream_t)stream));
+}
+
+w12_status w12_f8_tile(const uint8_t* w, uint64_t n, uint64_t k, void* w_tiled, void* stream) {
+  if (!w || !w_tiled) return W12_ERR_NULL;
+  if (!shape_ok(n, k)) return W12_ERR_SHAPE;
+  if (!aligned(w, 16) || !aligned(w_tiled, 16)) return W12_ERR_ALIGN;
+  return hip_status(launch_f8_tile(w, (uint32_t)(n / 16), (uint32_t)(k / 128), (uint8_t*)w_tiled,
+                                   (hipStream_t)stream));
+}
+
+w12_status w12_gemm_f8(const uint16_t* x, uint32_t m, const void* w_tiled, const float* scale,
+                       uint64_t n, uint64_t k, uint16_t* y, void* ws, size_t ws_bytes,
+                       void* stream) {
+  if (!x || !w_tiled || !scale || !y) return W12_ERR_NULL;
+  if (!shape_ok(n, k)) return W12_ERR_SHAPE;
+  if (m < 1 || m > W12_MAX_M) return W12_ERR_RANGE;
+  if (!mn_ok(m, n)) return W12_ERR_SHAPE;
+  const size_t need = gemm_ws_bytes(m, n, k, false);
+  if (ws_bytes < need) return W12_ERR_WORKSPACE;
+  if (need > 0 && !ws) return W12_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(w_tiled, 16) || !aligned(scale, 4) || !aligned(y, 16) ||
+      !aligned(ws, 256))
+    return W12_ERR_ALIGN;
+  const GemmPlan p = make_plan(m, n, k, EPI_BF16, false);
+  GemmArgs a;
+  memset(&a, 0, sizeof(a));
+  a.x = x;
+  a.p.seg[0].w = (const uint8_t*)w_tiled;
+  a.p.seg[0].scale = scale;
+  a.p.seg[0].y = y;
+  a.p.seg[0].n = (uint32_t)n;
+  fill_params(a.p, m, k, n, 1);
+  if (!set_split_ws(a, ws, p, m, n)) return W12_ERR_HIP;
+  return hip_status(launch_gemm(a, SRC_F8, EPI_BF16, p, (hipStream_t)stream));
 }
 
 w12_status w12_lmhead_verify(const uint16_t* x, uint32_t m, const w12_desc* d, const int32_t* draft,

@@ -431,6 +431,35 @@ hipError_t launch_bf16_tile(const uint16_t* w, uint32_t nb, uint32_t g_cols, uin
   return hipGetLastError();
 }
 
+// Row-major FP8 bytes -> 2 KB tiles: tile (b, g) at (g * nb + b) * 2048, the 8 bytes of
+// lane slot l (r = l % 16, q = l / 16) in group j (row 16b + r, columns
+// 128g + 32j + 8q .. +7) at 1024 (j / 2) + 16 l + 8 (j % 2): the byte order of the W12
+// sign/mantissa bytes, so that each wave instruction of the GEMM reads 1 KB of whole
+// lines.  One thread per 8-byte unit.
+__global__ __launch_bounds__(256) void k_f8_tile(const uint8_t* __restrict__ w, uint32_t nb,
+                                                 uint32_t g_cols, uint8_t* __restrict__ out) {
+  const uint64_t units = (uint64_t)nb * g_cols * 256u;
+  const uint64_t k = (uint64_t)g_cols * 128u;
+  for (uint64_t u = (uint64_t)blockIdx.x * 256u + threadIdx.x; u < units;
+       u += (uint64_t)gridDim.x * 256u) {
+    const uint64_t tile = u >> 8;
+    const uint32_t within = (uint32_t)(u & 255u), j = within >> 6, l = within & 63u;
+    const uint64_t b = tile / g_cols, g = tile % g_cols;
+    const uint32_t r = l & 15u, q = l >> 4;
+    const uint2 v = *reinterpret_cast<const uint2*>(w + (16u * b + r) * k + 128u * g + 32u * j + 8u * q);
+    *reinterpret_cast<uint2*>(out + (g * nb + b) * 2048u + 1024u * (j >> 1) + 16u * l + 8u * (j & 1u)) = v;
+  }
+}
+
+hipError_t launch_f8_tile(const uint8_t* w, uint32_t nb, uint32_t g_cols, uint8_t* out,
+                          hipStream_t s) {
+  const uint64_t units = (uint64_t)nb * g_cols * 256u;
+  uint64_t blocks = (units + 255u) / 256u;
+  if (blocks > 65536u) blocks = 65536u;
+  hipLaunchKernelGGL(k_f8_tile, dim3((uint32_t)blocks), dim3(256), 0, s, w, nb, g_cols, out);
+  return hipGetLastError();
+}
+
 hipError_t launch_rms_rescale(const uint16_t* x, uint32_t m, uint32_t k, uint16_t* y,
                               hipStream_t s) {
   hipLaunchKernelGGL(k_rms, dim3(m), dim3(256), 0, s, x, k, y);

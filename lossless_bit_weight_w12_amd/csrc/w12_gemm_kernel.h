@@ -37,6 +37,10 @@
 // RMS launches (p.rms; the column-synchronous kernel's EPI_RMS instantiations): the
 //   output rows are divided by the RMS of their x rows, summed from the staged x
 //   (harness op of the layer chain, not the W12 method).
+// FP8 tiles (SRC_F8: E4M3 weights of an FP8 checkpoint with one FP32 scale per 128 x 128
+//   block) take the column-synchronous path with the BF16 epilogue: each byte pair is
+//   converted exactly to a BF16 pair, each tile column is summed from zero and enters
+//   the running sum times its block scale.
 // The logits epilogue (verification pass 1) sums every tile column from zero before
 //   adding it to the running sum, and keeps per row-block the two largest logits, the
 //   index of the largest and the largest bound of a row's 2-norm; the full FP32 logits
@@ -54,6 +58,13 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 
 // Plain BF16 sources (row-major or tiled): no decode, no escapes.
 constexpr bool plain_bf16(int src) { return src == SRC_BF16 || src == SRC_BF16T; }
+// W12 sources: sign/mantissa bytes, exponent codes and escapes.
+constexpr bool w12_src(int src) { return src == SRC_RUN || src == SRC_LUT; }
+// Bytes of one 16 x 128 tile, and the 16-byte loads per lane that read it.
+constexpr uint32_t tile_bytes(int src) {
+  return src == SRC_BF16T ? 4096u : src == SRC_F8 ? 2048u : 3072u;
+}
+constexpr int tile_loads(int src) { return plain_bf16(src) ? 4 : src == SRC_F8 ? 2 : 3; }
 
 // BF16 per LDS row of an x column: +16 B pad (3.2 bank-conflict cycles per MFMA B read,
 // measured; +32 B has none but is no faster up to 64 columns), +32 B for the 64- and
@@ -72,6 +83,7 @@ struct SegView {
   uint16_t* y;
   uint32_t rb0, n, basepair;
   uint32_t lut[4];
+  const float* scale;
 };
 
 __device__ __forceinline__ SegView seg_view(const GemmParams& p, uint32_t b) {
@@ -83,6 +95,7 @@ __device__ __forceinline__ SegView seg_view(const GemmParams& p, uint32_t b) {
   v.rb0 = p.seg[0].rb0;
   v.n = p.seg[0].n;
   v.basepair = p.seg[0].basepair;
+  v.scale = p.seg[0].scale;
 #pragma unroll
   for (int i = 0; i < 4; ++i) v.lut[i] = p.seg[0].lut[i];
 #pragma unroll
@@ -95,6 +108,7 @@ __device__ __forceinline__ SegView seg_view(const GemmParams& p, uint32_t b) {
     v.rb0 = here ? p.seg[s].rb0 : v.rb0;
     v.n = here ? p.seg[s].n : v.n;
     v.basepair = here ? p.seg[s].basepair : v.basepair;
+    v.scale = here ? p.seg[s].scale : v.scale;
 #pragma unroll
     for (int i = 0; i < 4; ++i) v.lut[i] = here ? p.seg[s].lut[i] : v.lut[i];
   }
@@ -132,7 +146,8 @@ __device__ __forceinline__ uint32_t lut16(uint32_t c, uint32_t t0, uint32_t t1, 
 
 template <int SRC>
 struct TileRegs {
-  u32x4 v[plain_bf16(SRC) ? 4 : 3];
+  u32x4 v[tile_loads(SRC)];
+  float sc;   // SRC_F8: the tile's block scale
 };
 
 // Tile (b, g) of a weight of nbw row-blocks: W12 and 4 KB BF16 tiles are stored column
@@ -215,16 +230,15 @@ __device__ __forceinline__ bool split_last(uint32_t* tickets, uint32_t grp) {
   return s_last != 0u;
 }
 
-// One tile (W12 or 4 KB BF16) through a buffer resource over exactly its bytes, built
-// from a wave-uniform address: advancing a column changes scalar registers only, and the
-// lanes' offsets stay fixed.
+// One tile (W12, FP8 or 4 KB BF16) through a buffer resource over exactly its bytes,
+// built from a wave-uniform address: advancing a column changes scalar registers only,
+// and the lanes' offsets stay fixed.
 template <int SRC>
 __device__ __forceinline__ void load_tile_rs(TileRegs<SRC>& t, const uint8_t* tile, int lane) {
   static_assert(SRC != SRC_BF16, "row-major BF16 rows are not tiles");
-  constexpr uint32_t kTileB = SRC == SRC_BF16T ? 4096u : 3072u;
-  const __amdgpu_buffer_rsrc_t rs = make_rsrc(tile, kTileB);
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(tile, tile_bytes(SRC));
 #pragma unroll
-  for (int s = 0; s < (plain_bf16(SRC) ? 4 : 3); ++s)
+  for (int s = 0; s < tile_loads(SRC); ++s)
     t.v[s] = __builtin_amdgcn_raw_buffer_load_b128(rs, (uint32_t)lane * 16u + 1024u * s, 0, kCpolNT);
 }
 
@@ -237,6 +251,22 @@ __device__ __forceinline__ void unpack_tile(const TileRegs<SRC>& t, const SegVie
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int p = 0; p < 4; ++p) P[4 * j + p] = t.v[j][p];
+  } else if constexpr (SRC == SRC_F8) {
+    // FP8 E4M3 bytes in the W12 sign/mantissa byte order (group j in dwords 2(j&1),
+    // 2(j&1)+1 of load j/2): one v_cvt_scalef32_pk_bf16_fp8 per pair, at scale 1.  Every
+    // E4M3 value (normal 2^-6..448 with 3 mantissa bits, subnormal multiples of 2^-9) is
+    // a BF16 value, so the conversion is exact; the block scale is applied to the FP32
+    // column sums.
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const u32x4& S = t.v[j >> 1];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const uint32_t wd = S[2 * (j & 1) + h];
+        P[4 * j + 2 * h] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wd, 1.0f, false));
+        P[4 * j + 2 * h + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wd, 1.0f, true));
+      }
+    }
   } else {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -422,6 +452,7 @@ __global__ __launch_bounds__(NWV * 64) void k_gemm(
     BlockMax bm,
     GemmParams p) {
   constexpr int NH = MF ? MT / 16 : 1;
+  static_assert(SRC != SRC_F8, "FP8 tiles run column-synchronous only");
   // the logits epilogue (VALU path only: from W12_MFMA_MIN_M rows on it runs in k_gemm_cs)
   // also records per weight row an upper bound of ||w_v||_2 (the scale of its
   // rounding-error bound is ||x||_2 ||w_v||_2, verification pass 2 supplies ||x||_2): the
@@ -480,7 +511,7 @@ __global__ __launch_bounds__(NWV * 64) void k_gemm(
 #pragma unroll
     for (int rb = 0; rb < RBW; ++rb) {
       unpack_tile<SRC>(t[rb], sv[rb], P[rb]);
-      if constexpr (!plain_bf16(SRC)) {
+      if constexpr (w12_src(SRC)) {
         if (b0 + rb < p.nb) esc_apply(ec[rb], sv[rb].esc, g, lane, P[rb]);
       }
     }
@@ -542,7 +573,7 @@ __global__ __launch_bounds__(NWV * 64) void k_gemm(
 #pragma unroll
         for (int m = 0; m < (MF ? 1 : M); ++m) vacc[rb][m] += vcol[rb][m];
     }
-    if constexpr (!plain_bf16(SRC)) {
+    if constexpr (w12_src(SRC)) {
       // refill after the tile's last LDS read: a pending scalar load would otherwise
       // hold up the LDS waits (they share one counter)
       __builtin_amdgcn_sched_barrier(0);
@@ -569,7 +600,7 @@ __global__ __launch_bounds__(NWV * 64) void k_gemm(
     load_tiles(tA, g);
     // escape cursors start after the first tiles are requested: their scalar loads
     // (one or two dependent round trips) overlap the first tile fetch
-    if constexpr (!plain_bf16(SRC)) {
+    if constexpr (w12_src(SRC)) {
 #pragma unroll
       for (int rb = 0; rb < RBW; ++rb) esc_begin(ec[rb], sv[rb].esc_off, sv[rb].esc, bl[rb], ga * 128u);
     }
@@ -813,7 +844,7 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_cs(
   for (int h = 0; h < NH; ++h) acc[h] = f32x4{0.f, 0.f, 0.f, 0.f};
   f32x4 nacc = {0.f, 0.f, 0.f, 0.f};   // kWn: D = W W^T over the K-range, diagonal used
   TileRegs<SRC> tA, tB;
-  u32x4 xr[kUnits];
+  u32x4 xr[2][kUnits];   // x units of the column being staged (two sets up to 32 columns)
   EscCursor ec;
 
   // Loads go through buffer resources (the current tile, x) with fixed lane offsets and
@@ -821,7 +852,7 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_cs(
   // column, the compiler waited for the previous column's loads before issuing the next
   // column's.
   constexpr bool kRs = SRC != SRC_BF16;
-  constexpr uint32_t kTileB = SRC == SRC_BF16T ? 4096u : 3072u;
+  constexpr uint32_t kTileB = tile_bytes(SRC);
   const uint32_t nbw = sv.n / 16u;   // row-blocks of this wave's weight (tile column stride)
   const __amdgpu_buffer_rsrc_t xrs = make_rsrc(x, m_rows * (uint32_t)p.k * 2u);
   uint32_t xoff[kUnits];   // byte offset of the thread's x units in column 0
@@ -833,15 +864,25 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_cs(
     // clamped row / column, used unzeroed (see x_load)
     xoff[i] = (min(m, m_rows - 1u) * (uint32_t)p.k + 8u * cu) * 2u;
   }
-  auto xload = [&](uint32_t g) {
+  auto xload = [&](int set, uint32_t g) {
     const uint32_t gl = min(g, gb - 1u);
 #pragma unroll
-    for (int i = 0; i < kUnits; ++i) xr[i] = __builtin_amdgcn_raw_buffer_load_b128(xrs, xoff[i], 256u * gl, 0);
+    for (int i = 0; i < kUnits; ++i)
+      xr[set][i] = __builtin_amdgcn_raw_buffer_load_b128(xrs, xoff[i], 256u * gl, 0);
   };
+  // FP8: the block scale of the wave's tile, one uniform load beside the tile's (the
+  // 16 rows of a row-block lie in one 128-row scale block)
+  constexpr bool kF8 = SRC == SRC_F8;
+  const __amdgpu_buffer_rsrc_t scrs =
+      make_rsrc(kF8 ? sv.scale : nullptr, kF8 ? ((nbw + 7u) / 8u) * p.g_cols * 4u : 0u);
+  const uint32_t scrow = (bl / 8u) * p.g_cols * 4u;
   auto tload = [&](TileRegs<SRC>& t, uint32_t g) {
     if constexpr (kRs) load_tile_rs<SRC>(t, sv.w + ((size_t)g * nbw + bl) * kTileB, lane);
     else load_tile<SRC>(t, sv.w, p, bl, g, lane, nbw);
+    if constexpr (kF8)
+      t.sc = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(scrs, 0u, scrow + 4u * g, 0));
   };
+
   // RMS launches: per-unit sums of x^2 over the K-range, in column order
   // RMS launches sum each row's x^2 over the K-range.  Up to 32 columns (the EPI_RMS
   // instantiations) by an MFMA of the x fragments with themselves (waves 0..3 take one of
@@ -865,17 +906,17 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_cs(
   auto xsumsq = [&](bool in_range) {
     if (rms_valu && in_range) {
 #pragma unroll
-      for (int i = 0; i < kUnits; ++i) ssq[i] += unit_sumsq(xr[i]);
+      for (int i = 0; i < kUnits; ++i) ssq[i] += unit_sumsq(xr[0][i]);
     }
   };
-  auto xstore = [&](uint32_t slot) {
+  auto xstore = [&](int set, uint32_t slot) {
 #pragma unroll
     for (int i = 0; i < kUnits; ++i) {
       const uint32_t u = (uint32_t)tid + NT * i;
       // (a compile-time true test when the units divide evenly: no exec-masked branch)
       if (kUnits * NT == 16 * MT || u < 16u * MT) {
         const uint32_t m = u >> 4, cu = u & 15u;
-        *reinterpret_cast<u32x4*>(&xs[slot][m * kXs + 8u * cu]) = xr[i];
+        *reinterpret_cast<u32x4*>(&xs[slot][m * kXs + 8u * cu]) = xr[set][i];
       }
     }
   };
@@ -903,23 +944,45 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_cs(
     }
     uint32_t P[16];
     unpack_tile<SRC>(t, sv, P);
-    if constexpr (!plain_bf16(SRC)) {
+    if constexpr (w12_src(SRC)) {
       if (bvalid) esc_apply(ec, sv.esc, g, lane, P);
     }
     // logits: the column's 4 MFMAs chain from zero and the column sum is added to the
     // running sum, so a product meets at most 4 MFMA accumulations (whatever their
     // internal order) and one addition per later column: the certified bound's depth
     f32x4 col[NH];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const u32x4 av = {P[4 * j], P[4 * j + 1], P[4 * j + 2], P[4 * j + 3]};
+    if constexpr (kF8) {
+      // FP8: each x column block's chain over the tile column (one 128-column scale
+      // block) starts from zero and enters the running sum times the block scale (one
+      // FMA); blocks one after the other, so one chain's sum is live at a time (with
+      // every block's sum live, 128 columns took 168 VGPRs and spilled)
 #pragma unroll
       for (int h = 0; h < NH; ++h) {
-        const u32x4 xv =
-            kEarlyX ? xvs[j][h] : *reinterpret_cast<const u32x4*>(xrow + (16 * h + r) * kXs + 32 * j);
-        f32x4& c = kWn ? col[h] : acc[h];
-        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av), __builtin_bit_cast(bf16x8_t, xv),
-                                                    (kWn && j == 0) ? f32x4{0.f, 0.f, 0.f, 0.f} : c, 0, 0, 0);
+        f32x4 c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const u32x4 av = {P[4 * j], P[4 * j + 1], P[4 * j + 2], P[4 * j + 3]};
+          const u32x4 xv =
+              kEarlyX ? xvs[j][h] : *reinterpret_cast<const u32x4*>(xrow + (16 * h + r) * kXs + 32 * j);
+          c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av),
+                                                      __builtin_bit_cast(bf16x8_t, xv), c, 0, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[h][i] = __builtin_fmaf(t.sc, c[i], acc[h][i]);
+        if (MT >= 64 && (h & 1) == 1) __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const u32x4 av = {P[4 * j], P[4 * j + 1], P[4 * j + 2], P[4 * j + 3]};
+#pragma unroll
+        for (int h = 0; h < NH; ++h) {
+          const u32x4 xv =
+              kEarlyX ? xvs[j][h] : *reinterpret_cast<const u32x4*>(xrow + (16 * h + r) * kXs + 32 * j);
+          f32x4& c = kWn ? col[h] : acc[h];
+          c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av), __builtin_bit_cast(bf16x8_t, xv),
+                                                      (kWn && j == 0) ? f32x4{0.f, 0.f, 0.f, 0.f} : c, 0, 0, 0);
+        }
       }
     }
     if constexpr (kWn) {
@@ -949,7 +1012,7 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_cs(
                                                        __builtin_bit_cast(bf16x8_t, av), nacc, 0, 0, 0);
       }
     }
-    if constexpr (!plain_bf16(SRC)) {
+    if constexpr (w12_src(SRC)) {
       __builtin_amdgcn_sched_barrier(0);
       if (ec.stale) esc_refill(ec, sv.esc);
     }
@@ -963,29 +1026,37 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_cs(
   // launches 0.2-0.6 us faster).
   // As in k_gemm, the compiler's schedule (which may wait for tile g before issuing
   // tile g+1) measured faster than a pinned deeper prefetch.
+  // x two columns ahead (staged into LDS one column ahead) up to 32 columns for the
+  // plain and FP8 sources: all workgroups read the same x column at about the same time,
+  // so its loads miss together, and waiting for them one column ahead put a memory
+  // latency on every column (FP8 gate+up M1 / M32 38.2 / 40.6 -> 27.1 / 30.2 us).  The
+  // W12 launches, bound by their larger tile stream, measured no gain (the 4-8 more
+  // registers cost them 0.1-0.6 us) and keep x one column ahead.
+  constexpr bool kXAhead = MT <= 32 && !w12_src(SRC);
   uint32_t g = ga;
-  xload(g);
+  xload(0, g);
   tload(tA, g);
-  if constexpr (!plain_bf16(SRC)) esc_begin(ec, sv.esc_off, sv.esc, bl, ga * 128u);
+  if constexpr (kXAhead) xload(1, g + 1);
+  if constexpr (w12_src(SRC)) esc_begin(ec, sv.esc_off, sv.esc, bl, ga * 128u);
   xsumsq(true);
-  xstore(g & 1u);
+  xstore(0, g & 1u);
   __syncthreads();
   if constexpr (MT <= 32) {
+    // (no RMS sums here: up to 32 columns they come from the MFMA path)
+    constexpr int kA = kXAhead ? 1 : 0;   // register set of the x column staged next
     for (;;) {
       if (g + 1 >= gb) { compute(tA, g); break; }
-      xload(g + 1);
+      xload(0, kXAhead ? g + 2 : g + 1);
       tload(tB, g + 1);
       compute(tA, g);
-      xsumsq(true);
-      xstore((g + 1) & 1u);
+      xstore(kA, (g + 1) & 1u);
       __syncthreads();
       ++g;
       if (g + 1 >= gb) { compute(tB, g); break; }
-      xload(g + 1);
+      xload(kA, kXAhead ? g + 2 : g + 1);
       tload(tA, g + 1);
       compute(tB, g);
-      xsumsq(true);
-      xstore((g + 1) & 1u);
+      xstore(0, (g + 1) & 1u);
       __syncthreads();
       ++g;
     }
@@ -994,19 +1065,21 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_cs(
     // 64 and 128 columns: the peeled column's second copy of the compute raised these
     // instantiations' registers past an occupancy step (the tiled BF16 kernel at 64 rows:
     // 94 -> 130 VGPRs, down 41 -> 54 us), so the loop keeps a clamped dead prefetch
+    // (x two columns ahead here as well measured slower: 64-column W12 and 128-column
+    // FP8 launches lost occupancy or spilled)
     for (;;) {
-      xload(g + 1);
+      xload(0, g + 1);
       tload(tB, min(g + 1, gb - 1u));
       compute(tA, g);
       xsumsq(g + 1 < gb);
-      xstore((g + 1) & 1u);
+      xstore(0, (g + 1) & 1u);
       __syncthreads();
       if (++g >= gb) break;
-      xload(g + 1);
+      xload(0, g + 1);
       tload(tA, min(g + 1, gb - 1u));
       compute(tB, g);
       xsumsq(g + 1 < gb);
-      xstore((g + 1) & 1u);
+      xstore(0, (g + 1) & 1u);
       __syncthreads();
       if (++g >= gb) break;
     }
@@ -1226,7 +1299,9 @@ hipError_t launch_gemm_src(const GemmArgs& a, int epi, const GemmPlan& pl, hipSt
 // instantiated here)
 #define W12_EPI(M_, MT_, MF_)                                                 \
   do {                                                                        \
-    if constexpr (plain_bf16(SRC)) {                                          \
+    if constexpr (SRC == SRC_F8) {                                            \
+      return hipErrorInvalidValue; /* FP8 runs column-synchronous only */     \
+    } else if constexpr (plain_bf16(SRC)) {                                   \
       if (epi != EPI_BF16) return hipErrorInvalidValue;                       \
       W12_RBW(M_, MT_, MF_, EPI_BF16);                                        \
     } else if constexpr (!MF_) {                                              \
@@ -1269,11 +1344,12 @@ hipError_t launch_gemm_src(const GemmArgs& a, int epi, const GemmPlan& pl, hipSt
                          a.sabs, a.bm, p);                         \
   } while (0)
 // (the RMS launches, GemmParams.rms with the BF16 epilogue, run their own instantiation
-// up to 32 columns and the BF16 one's runtime path from 64; the BF16 sources have none)
+// up to 32 columns and the BF16 one's runtime path from 64; the BF16 and FP8 sources
+// have neither RMS nor logits launches)
 #define W12_CS_EPI(MT_)                                                     \
   do {                                                                      \
     if (epi == EPI_BF16 && (!p.rms || MT_ >= 64)) W12_CS(MT_, EPI_BF16);   \
-    else if constexpr (plain_bf16(SRC)) return hipErrorInvalidValue;        \
+    else if constexpr (!w12_src(SRC)) return hipErrorInvalidValue;         \
     else if (epi == EPI_LOGITS) W12_CS(MT_, EPI_LOGITS);                    \
     else if constexpr (MT_ <= 32) W12_CS(MT_, EPI_RMS);                     \
     else return hipErrorInvalidValue;                                       \

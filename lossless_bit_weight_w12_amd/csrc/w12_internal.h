@@ -22,6 +22,7 @@ enum Src : int {
   SRC_LUT = 1,   // W12 tiles, arbitrary ascending codebook (16-entry byte LUT)
   SRC_BF16 = 2,  // plain BF16 rows [n][k]
   SRC_BF16T = 3, // plain BF16 in 4 KB tiles (the layout of w12_bf16_tile)
+  SRC_F8 = 4,    // FP8 E4M3 in 2 KB tiles with one FP32 scale per 128 x 128 block (w12_f8_tile)
 };
 
 // Epilogue of the GEMM kernel family.
@@ -48,6 +49,7 @@ struct Seg {
   uint32_t n;               // rows of this weight
   uint32_t basepair;        // SRC_RUN: C[0] | C[0] << 16
   uint32_t lut[4];          // SRC_LUT: codebook bytes C[0..15]
+  const float* scale;       // SRC_F8: block scales [ceil(n/128)][k/128]
 };
 
 // Scalar parameters of one launch (a kernel argument).
@@ -182,11 +184,13 @@ hipError_t launch_gemm_run(const GemmArgs& a, int epi, const GemmPlan& p, hipStr
 hipError_t launch_gemm_lut(const GemmArgs& a, int epi, const GemmPlan& p, hipStream_t s);
 hipError_t launch_gemm_bf16_src(const GemmArgs& a, int epi, const GemmPlan& p, hipStream_t s);
 hipError_t launch_gemm_bf16t_src(const GemmArgs& a, int epi, const GemmPlan& p, hipStream_t s);
+hipError_t launch_gemm_f8_src(const GemmArgs& a, int epi, const GemmPlan& p, hipStream_t s);
 inline hipError_t launch_gemm(const GemmArgs& a, int src, int epi, const GemmPlan& p,
                               hipStream_t s) {
   if (src == SRC_RUN) return launch_gemm_run(a, epi, p, s);
   if (src == SRC_LUT) return launch_gemm_lut(a, epi, p, s);
   if (src == SRC_BF16T) return launch_gemm_bf16t_src(a, epi, p, s);
+  if (src == SRC_F8) return launch_gemm_f8_src(a, epi, p, s);
   return launch_gemm_bf16_src(a, epi, p, s);
 }
 
@@ -213,6 +217,8 @@ hipError_t launch_encode_pack(const uint16_t* w, uint32_t nb, uint32_t g_cols,
                               hipStream_t s);
 hipError_t launch_bf16_tile(const uint16_t* w, uint32_t nb, uint32_t g_cols, uint8_t* out,
                             hipStream_t s);
+hipError_t launch_f8_tile(const uint8_t* w, uint32_t nb, uint32_t g_cols, uint8_t* out,
+                          hipStream_t s);
 hipError_t launch_decode(const uint8_t* tiles, const uint32_t* esc_off, const uint32_t* esc,
                          uint32_t nb, uint32_t g_cols, const Codebook16& cb,
                          uint16_t* w_out, hipStream_t s);

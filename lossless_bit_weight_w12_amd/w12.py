@@ -14,7 +14,8 @@ from dataclasses import dataclass
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libw12.so")
 _LIB = None
 
-OP_ENCODE, OP_DECODE, OP_GEMM, OP_GEMM_BF16, OP_VERIFY, OP_GEMM_GROUP, OP_VERIFY2 = 0, 1, 2, 3, 4, 5, 6
+OP_ENCODE, OP_DECODE, OP_GEMM, OP_GEMM_BF16, OP_VERIFY, OP_GEMM_GROUP, OP_VERIFY2, OP_GEMM_F8 = \
+    0, 1, 2, 3, 4, 5, 6, 7
 MAX_M = 128
 MAX_GROUP = 4
 STATUS = {0: "W12_OK", -1: "W12_ERR_NULL", -2: "W12_ERR_SHAPE", -3: "W12_ERR_RANGE",
@@ -26,7 +27,7 @@ EXPORTS = ("w12_tiles_bytes", "w12_workspace_bytes", "w12_workspace_init", "w12_
            "w12_logits_f32",
            "w12_rms_rescale", "w12_status_str", "w12_version", "w12_gemm_noalloc", "w12_stream_read",
            "w12_screen_bytes", "w12_screen_encode", "w12_lmhead_verify2", "w12_lmhead_verify2_batched",
-           "w12_screen_logits_f32")
+           "w12_screen_logits_f32", "w12_f8_tile", "w12_gemm_f8")
 NOALLOC_SCRATCH_BYTES = 32 << 20   # W12_NOALLOC_SCRATCH_BYTES
 ENCODE_TOTAL_OFFSET = 2112   # W12_ENCODE_TOTAL_OFFSET: true escape count in an encode workspace
 
@@ -95,6 +96,11 @@ def lib():
         L.w12_gemm_bf16_tiled.restype = c_int32
         L.w12_gemm_bf16_tiled.argtypes = [c_void_p, c_uint32, c_void_p, c_uint64, c_uint64,
                                           c_void_p, c_void_p, c_size_t, c_void_p]
+        L.w12_f8_tile.restype = c_int32
+        L.w12_f8_tile.argtypes = [c_void_p, c_uint64, c_uint64, c_void_p, c_void_p]
+        L.w12_gemm_f8.restype = c_int32
+        L.w12_gemm_f8.argtypes = [c_void_p, c_uint32, c_void_p, c_void_p, c_uint64, c_uint64,
+                                  c_void_p, c_void_p, c_size_t, c_void_p]
         L.w12_lmhead_verify.restype = c_int32
         L.w12_lmhead_verify.argtypes = [c_void_p, c_uint32, ctypes.POINTER(W12Desc), c_void_p,
                                         c_uint32, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]
@@ -366,6 +372,38 @@ def gemm_bf16_tiled(x, w_tiled, n: int, k: int, out=None):
     ws = workspace(max(workspace_bytes(OP_GEMM_BF16, m, n, k), 256), x.device)
     _check("w12_gemm_bf16_tiled", lib().w12_gemm_bf16_tiled(
         _ptr(x), m, _ptr(w_tiled), n, k, _ptr(_as_bits(out)), _ptr(ws), ws.numel(), _stream(x.device)))
+    return out
+
+
+def f8_tile(q):
+    """2 KB-tiled copy of FP8 E4M3 codes q [n, k] (uint8 storage) for gemm_f8."""
+    torch = _torch()
+    if not q.is_cuda or q.dtype != torch.uint8 or not q.is_contiguous() or q.dim() != 2:
+        raise ValueError("f8_tile: q must be a contiguous uint8 CUDA tensor [n, k]")
+    n, k = q.shape
+    out = torch.empty(n * k, dtype=torch.uint8, device=q.device)
+    _check("w12_f8_tile", lib().w12_f8_tile(_ptr(q), n, k, _ptr(out), _stream(q.device)))
+    return out
+
+
+def gemm_f8(x, q_tiled, scale, n: int, k: int, out=None):
+    """y = x . W^T for the FP8 weight W = E4M3(q) * block scale: q_tiled from f8_tile,
+    scale float32 [ceil(n/128), k/128]."""
+    torch = _torch()
+    x = _as_bits(x)
+    m = x.shape[0]
+    if x.shape[1] != k or q_tiled.numel() * q_tiled.element_size() != n * k:
+        raise ValueError("gemm_f8: x must be [m, k] and q_tiled n*k bytes")
+    if (not scale.is_cuda or scale.dtype != torch.float32 or not scale.is_contiguous()
+            or scale.numel() != ((n + 127) // 128) * (k // 128)):
+        raise ValueError("gemm_f8: scale must be a contiguous float32 CUDA tensor "
+                         "[ceil(n/128), k/128]")
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.bfloat16, device=x.device)
+    ws = workspace(max(workspace_bytes(OP_GEMM_F8, m, n, k), 256), x.device)
+    _check("w12_gemm_f8", lib().w12_gemm_f8(
+        _ptr(x), m, _ptr(q_tiled), _ptr(scale), n, k, _ptr(_as_bits(out)), _ptr(ws), ws.numel(),
+        _stream(x.device)))
     return out
 
 

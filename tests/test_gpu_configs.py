@@ -8,6 +8,8 @@
 4  LM head [151936, 5120], three M = 16 batches (batch 0 plain, batches 1-2 the 32 rows
    with planted near-ties): codebook, escape count and decode of the whole head, bytes of
    sampled row-block bands, argmax and accepted length of every row against the oracle.
+   The same matrices in FP8 checkpoint form (E4M3, 128 x 128 block scales) at M = 16,
+   64 and 128: every output of the FP8 GEMM.
 5  Decode step: 64 layers of q, k, v, o, gate, up, down + LM head drawn on the device,
    M = 24, RMS-chained (the rescales folded into the consuming GEMMs); at layers 0, 21,
    42, 63 every GEMM output is checked against the oracle on the captured inputs
@@ -141,6 +143,25 @@ def test_config3_mlp_block_batched(env, name):
         xt = to_dev(x, torch)
         _check_gemm(w12.gemm(xt, t), x, w)
         _check_gemm(w12.gemm_bf16_tiled(xt, wt, n, k), x, w)
+
+
+@pytest.mark.parametrize("name", ["gate_up", "down"])
+def test_config3_mlp_block_f8(env, name):
+    """The MLP matrices in FP8 checkpoint form (the same Gaussian weights quantized to
+    E4M3 with 128 x 128 block scales) at the batched sizes the bench times, every output
+    against the oracle."""
+    torch, w12 = env
+    q, s = wi.f8_weight(3, wi.T_W if name == "gate_up" else wi.T_W2, wi.CONFIG_SHAPES[3][name])
+    n, k = q.shape
+    qt = w12.f8_tile(torch.from_numpy(q).to("cuda:0"))
+    st = torch.from_numpy(s).to("cuda:0")
+    for m in (16, 64, 128):
+        say("config 3 f8", name, "m", m)
+        x = wi.activations(3, wi.T_X if name == "gate_up" else wi.T_X2, m, k)
+        y = w12.gemm_f8(to_dev(x, torch), qt, st, n, k)
+        z, sa = o.gemm_f8_reference(x, q, s)
+        ok = o.gemm_accept(to_host(y), z, sa)
+        assert ok.all(), f"{int((~ok).sum())} outputs outside tolerance"
 
 
 @pytest.fixture(scope="module")

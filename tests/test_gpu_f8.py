@@ -1,0 +1,149 @@
+"""GPU parity of the FP8 GEMM (E4M3 codes with FP32 128 x 128 block scales, BF16
+activations) against the CPU oracle, element by element, through the C ABI: the tile
+bytes exactly, every output by oracle.gemm_accept.  Shapes span several tiles, ragged
+128-row scale blocks, odd row-block counts and K splits; m covers the 16-, 32-, 64- and
+128-column x tiles and their ragged edges."""
+import numpy as np
+import pytest
+
+from oracle import w12_oracle as o
+import w12_inputs as wi
+from gpu_util import say, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+# (n, k): one tile; a partial last scale-block row (144 = 128 + 16); odd row-block counts
+# and tile columns; many row-blocks; a long K on few rows (split)
+SHAPES = [(16, 128), (144, 640), (272, 1280), (2080, 512), (64, 4096)]
+MS = [1, 2, 3, 5, 8, 16, 17, 24, 32, 33, 48, 64, 65, 96, 128]
+
+
+@pytest.fixture(scope="module")
+def env():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a visible MI355X"
+    import lossless_bit_weight_w12_amd as w12
+    w12.lib()
+    return torch, w12
+
+
+def random_codes(shape, g):
+    """Uniform E4M3 codes without the NaN pattern: every finite value, subnormals included."""
+    q = g.integers(0, 256, shape).astype(np.uint8)
+    q[(q & 0x7F) == 0x7F] = 0x7E
+    return q
+
+
+def random_scales(n, k, g):
+    return (g.uniform(0.5, 2.0, ((n + 127) // 128, k // 128))
+            * 2.0 ** g.integers(-14, 2, ((n + 127) // 128, k // 128))).astype(np.float32)
+
+
+def run(torch, w12, x, q, s):
+    n, k = q.shape
+    qt = w12.f8_tile(torch.from_numpy(q).to("cuda:0"))
+    y = w12.gemm_f8(to_dev(x, torch), qt, torch.from_numpy(s).to("cuda:0"), n, k)
+    torch.cuda.synchronize()
+    return qt, y
+
+
+def check(y_dev, x, q, s):
+    z, sa = o.gemm_f8_reference(x, q, s)
+    ok = o.gemm_accept(to_host(y_dev), z, sa)
+    bad = np.argwhere(~ok)
+    assert ok.all(), f"{bad.shape[0]} outputs outside tolerance, first {bad[:4].tolist()}"
+
+
+@pytest.mark.parametrize("n,k", SHAPES)
+def test_f8_tile_bytes(env, n, k):
+    torch, w12 = env
+    g = np.random.default_rng(8100 + n + k)
+    q = random_codes((n, k), g)
+    say("f8 tile", n, k)
+    qt = w12.f8_tile(torch.from_numpy(q).to("cuda:0"))
+    torch.cuda.synchronize()
+    assert np.array_equal(qt.cpu().numpy(), o.f8_pack(q))
+
+
+@pytest.mark.parametrize("m", MS)
+def test_gemm_f8_checkpoint_weights(env, m):
+    """Gaussian weights in checkpoint form (block max mapped to 448), x ~ N(0, 1)."""
+    torch, w12 = env
+    for i, (n, k) in enumerate(SHAPES):
+        say("gemm f8 checkpoint", m, n, k)
+        q, s = wi.f8_weight(0, 40 + i, (n, k))
+        x = wi.gaussian_bf16((m, k), 1.0, np.random.default_rng(8200 + 16 * m + i))
+        _, y = run(torch, w12, x, q, s)
+        check(y, x, q, s)
+
+
+@pytest.mark.parametrize("m", [1, 4, 16, 32, 64, 128])
+def test_gemm_f8_random_codes_and_scales(env, m):
+    """Every finite code (subnormals included) under block scales spread over 2^-15..2^2."""
+    torch, w12 = env
+    g = np.random.default_rng(8300 + m)
+    for n, k in SHAPES:
+        say("gemm f8 random codes", m, n, k)
+        q = random_codes((n, k), g)
+        s = random_scales(n, k, g)
+        x = wi.gaussian_bf16((m, k), 1.0, g)
+        _, y = run(torch, w12, x, q, s)
+        check(y, x, q, s)
+
+
+def test_gemm_f8_zero_and_negative_scales(env):
+    """A zero block contributes nothing; negative scales are applied with their sign."""
+    torch, w12 = env
+    g = np.random.default_rng(8400)
+    n, k = 272, 1280
+    q = random_codes((n, k), g)
+    s = random_scales(n, k, g)
+    s[0, 3] = 0.0
+    s[1, :] *= -1.0
+    for m in (3, 32, 100):
+        say("gemm f8 zero/negative scales", m)
+        x = wi.gaussian_bf16((m, k), 1.0, g)
+        _, y = run(torch, w12, x, q, s)
+        check(y, x, q, s)
+
+
+def test_gemm_f8_nan_code_poisons_its_row(env):
+    torch, w12 = env
+    g = np.random.default_rng(8500)
+    n, k = 144, 640
+    q = random_codes((n, k), g)
+    q[5, 300] = 0x7F
+    q[130, 7] = 0xFF
+    s = random_scales(n, k, g)
+    for m in (2, 40):
+        say("gemm f8 NaN code", m)
+        x = wi.gaussian_bf16((m, k), 1.0, g)
+        _, y = run(torch, w12, x, q, s)
+        yf = y.float().cpu().numpy()
+        assert np.isnan(yf[:, [5, 130]]).all()
+        keep = np.setdiff1d(np.arange(n), [5, 130])
+        q2 = q.copy()
+        q2[5, 300] = 0
+        q2[130, 7] = 0
+        z, sa = o.gemm_f8_reference(x, q2, s)
+        assert o.gemm_accept(to_host(y)[:, keep], z[:, keep], sa[:, keep]).all()
+
+
+def test_gemm_f8_deterministic_and_overwrites(env):
+    """Repeated calls (K split and whole) give identical bits and overwrite y entirely."""
+    torch, w12 = env
+    g = np.random.default_rng(8600)
+    for m, (n, k) in [(1, (64, 4096)), (24, (272, 1280)), (128, (2080, 512))]:
+        say("gemm f8 determinism", m, n, k)
+        q = random_codes((n, k), g)
+        s = random_scales(n, k, g)
+        x = wi.gaussian_bf16((m, k), 1.0, g)
+        qt, y0 = run(torch, w12, x, q, s)
+        st = torch.from_numpy(s).to("cuda:0")
+        xt = to_dev(x, torch)
+        out = torch.full((m, n), float("nan"), dtype=torch.bfloat16, device="cuda:0")
+        for _ in range(3):
+            y = w12.gemm_f8(xt, qt, st, n, k, out=out)
+            torch.cuda.synchronize()
+            assert torch.equal(y.view(torch.int16), y0.view(torch.int16))
+        check(y0, x, q, s)

@@ -174,6 +174,24 @@ def test_bf16_tiled_validation(L):
     assert f(FAKE, 1, FAKE + 4, 1024, 1024, FAKE, FAKE, 1 << 30, None) == -7
 
 
+def test_f8_validation(L):
+    assert L.w12_f8_tile(None, 1024, 1024, FAKE, None) == -1
+    assert L.w12_f8_tile(FAKE, 1000, 1024, FAKE, None) == -2
+    assert L.w12_f8_tile(FAKE, 1024, 1024, FAKE + 8, None) == -7
+    f = L.w12_gemm_f8
+    assert f(FAKE, 1, FAKE, None, 1024, 1024, FAKE, FAKE, 1 << 30, None) == -1     # no scales
+    assert f(FAKE, 1, None, FAKE, 1024, 1024, FAKE, FAKE, 1 << 30, None) == -1
+    assert f(FAKE, 1, FAKE, FAKE, 1024, 100, FAKE, FAKE, 1 << 30, None) == -2
+    assert f(FAKE, 0, FAKE, FAKE, 1024, 1024, FAKE, FAKE, 1 << 30, None) == -3
+    assert f(FAKE, 129, FAKE, FAKE, 1024, 1024, FAKE, FAKE, 1 << 30, None) == -3
+    assert f(FAKE, 1, FAKE + 4, FAKE, 1024, 1024, FAKE, FAKE, 1 << 30, None) == -7
+    assert f(FAKE, 1, FAKE, FAKE + 2, 1024, 1024, FAKE, FAKE, 1 << 30, None) == -7
+    need = w12.workspace_bytes(w12.OP_GEMM_F8, 1, 1024, 4096)
+    assert need == w12.workspace_bytes(w12.OP_GEMM, 1, 1024, 4096) and need > 0   # (K split)
+    assert f(FAKE, 1, FAKE, FAKE, 1024, 4096, FAKE, FAKE, need - 1, None) == -5
+    assert f(FAKE, 1, FAKE, FAKE, 1024, 4096, FAKE, None, need, None) == -1
+
+
 def test_verify_validation(L):
     f = L.w12_lmhead_verify
     d = desc(n=2048, k=512)
@@ -286,7 +304,8 @@ def test_header_constants_match_binding():
     assert define("W12_MAX_M") == b.MAX_M
     for name, val in [("W12_OP_ENCODE", b.OP_ENCODE), ("W12_OP_DECODE", b.OP_DECODE),
                       ("W12_OP_GEMM", b.OP_GEMM), ("W12_OP_GEMM_BF16", b.OP_GEMM_BF16),
-                      ("W12_OP_VERIFY", b.OP_VERIFY), ("W12_OP_GEMM_GROUP", b.OP_GEMM_GROUP)]:
+                      ("W12_OP_VERIFY", b.OP_VERIFY), ("W12_OP_GEMM_GROUP", b.OP_GEMM_GROUP),
+                      ("W12_OP_VERIFY2", b.OP_VERIFY2), ("W12_OP_GEMM_F8", b.OP_GEMM_F8)]:
         assert define(name) == val, name
 
 
