@@ -903,10 +903,10 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_cs(
   f32x4 racc[NH];
 #pragma unroll
   for (int h = 0; h < NH; ++h) racc[h] = f32x4{0.f, 0.f, 0.f, 0.f};
-  auto xsumsq = [&](bool in_range) {
+  auto xsumsq = [&](int set, bool in_range) {
     if (rms_valu && in_range) {
 #pragma unroll
-      for (int i = 0; i < kUnits; ++i) ssq[i] += unit_sumsq(xr[0][i]);
+      for (int i = 0; i < kUnits; ++i) ssq[i] += unit_sumsq(xr[set][i]);
     }
   };
   auto xstore = [&](int set, uint32_t slot) {
@@ -1026,24 +1026,26 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_cs(
   // launches 0.2-0.6 us faster).
   // As in k_gemm, the compiler's schedule (which may wait for tile g before issuing
   // tile g+1) measured faster than a pinned deeper prefetch.
-  // x two columns ahead (staged into LDS one column ahead) up to 32 columns for the
-  // plain and FP8 sources: all workgroups read the same x column at about the same time,
+  // x two columns ahead (staged into LDS one column ahead) for the plain sources, and for
+  // FP8 up to 32 columns: all workgroups read the same x column at about the same time,
   // so its loads miss together, and waiting for them one column ahead put a memory
-  // latency on every column (FP8 gate+up M1 / M32 38.2 / 40.6 -> 27.1 / 30.2 us).  The
+  // latency on every column (FP8 gate+up M1 / M32 38.2 / 40.6 -> 27.1 / 30.2 us; tiled
+  // BF16 gate+up M32 / M64 / M128 74.6 / 87.4 / 132.4 -> 66.4 / 81.9 / 121.9 us).  The
   // W12 launches, bound by their larger tile stream, measured no gain (the 4-8 more
-  // registers cost them 0.1-0.6 us) and keep x one column ahead.
-  constexpr bool kXAhead = MT <= 32 && !w12_src(SRC);
+  // registers cost them 0.1-0.6 us), and FP8 from 64 columns lost more to the registers
+  // (gate+up M128 70.6 -> 106.7 us, spilling): both keep x one column ahead.
+  constexpr bool kXAhead = !w12_src(SRC) && (MT <= 32 || SRC != SRC_F8);
   uint32_t g = ga;
   xload(0, g);
   tload(tA, g);
   if constexpr (kXAhead) xload(1, g + 1);
   if constexpr (w12_src(SRC)) esc_begin(ec, sv.esc_off, sv.esc, bl, ga * 128u);
-  xsumsq(true);
+  xsumsq(0, true);
   xstore(0, g & 1u);
   __syncthreads();
+  constexpr int kA = kXAhead ? 1 : 0;   // register set of the x column staged next
   if constexpr (MT <= 32) {
     // (no RMS sums here: up to 32 columns they come from the MFMA path)
-    constexpr int kA = kXAhead ? 1 : 0;   // register set of the x column staged next
     for (;;) {
       if (g + 1 >= gb) { compute(tA, g); break; }
       xload(0, kXAhead ? g + 2 : g + 1);
@@ -1065,20 +1067,18 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_cs(
     // 64 and 128 columns: the peeled column's second copy of the compute raised these
     // instantiations' registers past an occupancy step (the tiled BF16 kernel at 64 rows:
     // 94 -> 130 VGPRs, down 41 -> 54 us), so the loop keeps a clamped dead prefetch
-    // (x two columns ahead here as well measured slower: 64-column W12 and 128-column
-    // FP8 launches lost occupancy or spilled)
     for (;;) {
-      xload(0, g + 1);
+      xload(0, kXAhead ? g + 2 : g + 1);
       tload(tB, min(g + 1, gb - 1u));
       compute(tA, g);
-      xsumsq(g + 1 < gb);
-      xstore(0, (g + 1) & 1u);
+      xsumsq(kA, g + 1 < gb);
+      xstore(kA, (g + 1) & 1u);
       __syncthreads();
       if (++g >= gb) break;
-      xload(0, g + 1);
+      xload(kA, kXAhead ? g + 2 : g + 1);
       tload(tA, min(g + 1, gb - 1u));
       compute(tB, g);
-      xsumsq(g + 1 < gb);
+      xsumsq(0, g + 1 < gb);
       xstore(0, (g + 1) & 1u);
       __syncthreads();
       if (++g >= gb) break;
