@@ -954,8 +954,9 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_cs(
     if constexpr (kF8) {
       // FP8: each x column block's chain over the tile column (one 128-column scale
       // block) starts from zero and enters the running sum times the block scale (one
-      // FMA); blocks one after the other, so one chain's sum is live at a time (with
-      // every block's sum live, 128 columns took 168 VGPRs and spilled)
+      // FMA); written block by block, and from 64 columns scheduled two blocks at a time
+      // (with every block's chain interleaved the 128-column kernel spilled 72 bytes per
+      // lane; scheduled freely, 8 bytes but gate+up M128 71.0 -> 77.0 us; in pairs, 16)
 #pragma unroll
       for (int h = 0; h < NH; ++h) {
         f32x4 c = {0.f, 0.f, 0.f, 0.f};
@@ -1029,12 +1030,13 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_cs(
   // x two columns ahead (staged into LDS one column ahead) for the plain sources, and for
   // FP8 up to 32 columns: all workgroups read the same x column at about the same time,
   // so its loads miss together, and waiting for them one column ahead put a memory
-  // latency on every column (FP8 gate+up M1 / M32 38.2 / 40.6 -> 27.1 / 30.2 us; tiled
-  // BF16 gate+up M32 / M64 / M128 74.6 / 87.4 / 132.4 -> 66.4 / 81.9 / 121.9 us).  The
-  // W12 launches, bound by their larger tile stream, measured no gain (the 4-8 more
-  // registers cost them 0.1-0.6 us), and FP8 from 64 columns lost more to the registers
-  // (gate+up M128 70.6 -> 106.7 us, spilling): both keep x one column ahead.
-  constexpr bool kXAhead = !w12_src(SRC) && (MT <= 32 || SRC != SRC_F8);
+  // latency on every column (FP8 gate+up M1 / M32 / M64 38.2 / 40.6 / 46.7 -> 27.1 / 30.2 /
+  // 42.7 us; tiled BF16 gate+up M32 / M64 / M128 74.6 / 87.4 / 132.4 -> 66.4 / 81.9 /
+  // 121.9 us).  The W12 launches, bound by their larger tile stream, measured no gain (the
+  // 4-8 more registers cost them 0.1-0.6 us), and FP8 in the 5-wave 64-column and in the
+  // 128-column kernels lost more to the registers (down M64 32.7 -> 41.2 us, gate+up M128
+  // 70.6 -> 106.7 us, spilling): they keep x one column ahead.
+  constexpr bool kXAhead = !w12_src(SRC) && (MT <= 32 || SRC != SRC_F8 || (MT == 64 && NW == 10));
   uint32_t g = ga;
   xload(0, g);
   tload(tA, g);

@@ -13,8 +13,9 @@ from gpu_util import say, to_dev, to_host
 pytestmark = pytest.mark.gpu
 
 # (n, k): one tile; a partial last scale-block row (144 = 128 + 16); odd row-block counts
-# and tile columns; many row-blocks; a long K on few rows (split)
-SHAPES = [(16, 128), (144, 640), (272, 1280), (2080, 512), (64, 4096)]
+# and tile columns; many row-blocks; a long K on few rows (split); 2049 row-blocks (the
+# 10-wave workgroups from 17 rows on, a partial last scale block)
+SHAPES = [(16, 128), (144, 640), (272, 1280), (2080, 512), (64, 4096), (32784, 256)]
 MS = [1, 2, 3, 5, 8, 16, 17, 24, 32, 33, 48, 64, 65, 96, 128]
 
 
