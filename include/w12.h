@@ -79,7 +79,7 @@ typedef int32_t w12_status;
 /* Rows of one call: decode-sized batches (1..32) and the batched regime of several
  * requests verified together (16 to 24 requests of a few draft tokens each). */
 #define W12_MAX_M 128
-#define W12_MAX_GROUP 4   /* weights of one w12_gemm_group call, at most */
+#define W12_MAX_GROUP 4   /* weights of one w12_gemm_group or w12_gemm_f8_group call, at most */
 
 /* Host-side descriptor of one W12 tensor (device buffers + host metadata). */
 typedef struct w12_desc {
@@ -255,6 +255,17 @@ w12_status w12_f8_tile(const uint8_t* w, uint64_t n, uint64_t k, void* w_tiled, 
 w12_status w12_gemm_f8(const uint16_t* x, uint32_t m, const void* w_tiled, const float* scale,
                        uint64_t n, uint64_t k, uint16_t* y, void* ws, size_t ws_bytes,
                        void* stream);
+
+/* Up to W12_MAX_GROUP FP8 weights that read one x (q, k and v of a layer, or gate and up)
+ * in one launch: y_i = bf16(x . W_i^T) for weight i given by w_tiled[i] (from w12_f8_tile),
+ * scales[i] (FP32 [ceil(ns[i]/128)][k/128]) and ns[i] rows, all with the same k; ys[i]
+ * device BF16 [m][ns[i]].  The arrays of pointers and ns are host memory.
+ * ws: w12_workspace_bytes(W12_OP_GEMM_GROUP, m, sum of ns[i], k) bytes.  Errors as
+ * w12_gemm_f8; W12_ERR_RANGE for n_w outside 1..W12_MAX_GROUP. */
+w12_status w12_gemm_f8_group(const uint16_t* x, uint32_t m, const void* const* w_tiled,
+                             const float* const* scales, const uint64_t* ns, uint32_t n_w,
+                             uint64_t k, uint16_t* const* ys, void* ws, size_t ws_bytes,
+                             void* stream);
 
 /* Greedy verification over the LM head (review page, "The mechanisms it found":
  * certified exact-argmax LM head; "StargazerX0/SpecPilot", "Results and

@@ -7,7 +7,7 @@ binding."""
 from .w12 import (ENCODE_TOTAL_OFFSET, EXPORTS, MAX_GROUP, MAX_M, NOALLOC_SCRATCH_BYTES,
                   OP_DECODE, OP_ENCODE, OP_GEMM, OP_GEMM_BF16, OP_GEMM_F8, OP_GEMM_GROUP,
                   OP_VERIFY, OP_VERIFY2, Prepared, ScreenCopy, W12Desc, W12Error, W12Tensor, bf16_tile,
-                  decode, encode, f8_tile, gemm, gemm_bf16, gemm_bf16_tiled, gemm_f8,
+                  decode, encode, f8_tile, gemm, gemm_bf16, gemm_bf16_tiled, gemm_f8, gemm_f8_group,
                   gemm_group, gemm_noalloc,
                   lib, lib_path, lmhead_verify, lmhead_verify2, lmhead_verify2_batched,
                   lmhead_verify_batched, logits_f32, prepare_gemm, prepare_gemm_group,
@@ -21,7 +21,7 @@ __all__ = ["ENCODE_TOTAL_OFFSET", "EXPORTS", "MAX_GROUP", "MAX_M", "NOALLOC_SCRA
            "OP_VERIFY",
            "OP_VERIFY2", "Prepared", "ScreenCopy", "W12Desc", "W12Error", "W12Tensor",
            "bf16_tile", "decode", "encode", "f8_tile", "gemm", "gemm_bf16", "gemm_bf16_tiled",
-           "gemm_f8", "gemm_group",
+           "gemm_f8", "gemm_f8_group", "gemm_group",
            "gemm_noalloc", "lib", "lib_path", "lmhead_verify", "lmhead_verify2",
            "lmhead_verify2_batched", "lmhead_verify_batched", "logits_f32", "prepare_gemm",
            "prepare_gemm_group", "prepare_rms", "prepare_verify", "prepare_verify2",

@@ -819,6 +819,43 @@ w12_status w12_gemm_f8(const uint16_t* x, uint32_t m, const void* w_tiled, const
   return hip_status(launch_gemm(a, SRC_F8, EPI_BF16, p, (hipStream_t)stream));
 }
 
+w12_status w12_gemm_f8_group(const uint16_t* x, uint32_t m, const void* const* w_tiled,
+                             const float* const* scales, const uint64_t* ns, uint32_t n_w,
+                             uint64_t k, uint16_t* const* ys, void* ws, size_t ws_bytes,
+                             void* stream) {
+  if (!x || !w_tiled || !scales || !ns || !ys) return W12_ERR_NULL;
+  if (n_w < 1 || n_w > W12_MAX_GROUP || m < 1 || m > W12_MAX_M) return W12_ERR_RANGE;
+  uint64_t n_total = 0;
+  for (uint32_t i = 0; i < n_w; ++i) {
+    if (!w_tiled[i] || !scales[i] || !ys[i]) return W12_ERR_NULL;
+    if (!shape_ok(ns[i], k)) return W12_ERR_SHAPE;
+    if (!aligned(w_tiled[i], 16) || !aligned(scales[i], 4) || !aligned(ys[i], 16))
+      return W12_ERR_ALIGN;
+    n_total += ns[i];
+  }
+  if (n_total >= kMaxN || !mn_ok(m, n_total)) return W12_ERR_SHAPE;
+  const size_t need = group_ws_bytes(m, n_total, k);
+  if (ws_bytes < need) return W12_ERR_WORKSPACE;
+  if (need > 0 && !ws) return W12_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(ws, 256)) return W12_ERR_ALIGN;
+  GemmArgs a;
+  memset(&a, 0, sizeof(a));
+  a.x = x;
+  n_total = 0;
+  for (uint32_t i = 0; i < n_w; ++i) {
+    a.p.seg[i].w = (const uint8_t*)w_tiled[i];
+    a.p.seg[i].scale = scales[i];
+    a.p.seg[i].y = ys[i];
+    a.p.seg[i].n = (uint32_t)ns[i];
+    a.p.seg[i].rb0 = (uint32_t)(n_total / 16);
+    n_total += ns[i];
+  }
+  fill_params(a.p, m, k, n_total, n_w);
+  const GemmPlan p = make_plan(m, n_total, k, EPI_BF16, false);
+  if (!set_split_ws(a, ws, p, m, n_total)) return W12_ERR_HIP;
+  return hip_status(launch_gemm(a, SRC_F8, EPI_BF16, p, (hipStream_t)stream));
+}
+
 w12_status w12_lmhead_verify(const uint16_t* x, uint32_t m, const w12_desc* d, const int32_t* draft,
                              uint32_t n_draft, int32_t* argmax_out, int32_t* accepted_out,
                              void* ws, size_t ws_bytes, void* stream) {

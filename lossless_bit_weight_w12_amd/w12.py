@@ -27,7 +27,7 @@ EXPORTS = ("w12_tiles_bytes", "w12_workspace_bytes", "w12_workspace_init", "w12_
            "w12_logits_f32",
            "w12_rms_rescale", "w12_status_str", "w12_version", "w12_gemm_noalloc", "w12_stream_read",
            "w12_screen_bytes", "w12_screen_encode", "w12_lmhead_verify2", "w12_lmhead_verify2_batched",
-           "w12_screen_logits_f32", "w12_f8_tile", "w12_gemm_f8")
+           "w12_screen_logits_f32", "w12_f8_tile", "w12_gemm_f8", "w12_gemm_f8_group")
 NOALLOC_SCRATCH_BYTES = 32 << 20   # W12_NOALLOC_SCRATCH_BYTES
 ENCODE_TOTAL_OFFSET = 2112   # W12_ENCODE_TOTAL_OFFSET: true escape count in an encode workspace
 
@@ -101,6 +101,9 @@ def lib():
         L.w12_gemm_f8.restype = c_int32
         L.w12_gemm_f8.argtypes = [c_void_p, c_uint32, c_void_p, c_void_p, c_uint64, c_uint64,
                                   c_void_p, c_void_p, c_size_t, c_void_p]
+        L.w12_gemm_f8_group.restype = c_int32
+        L.w12_gemm_f8_group.argtypes = [c_void_p, c_uint32, c_void_p, c_void_p, c_void_p, c_uint32,
+                                        c_uint64, c_void_p, c_void_p, c_size_t, c_void_p]
         L.w12_lmhead_verify.restype = c_int32
         L.w12_lmhead_verify.argtypes = [c_void_p, c_uint32, ctypes.POINTER(W12Desc), c_void_p,
                                         c_uint32, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]
@@ -405,6 +408,33 @@ def gemm_f8(x, q_tiled, scale, n: int, k: int, out=None):
         _ptr(x), m, _ptr(q_tiled), _ptr(scale), n, k, _ptr(_as_bits(out)), _ptr(ws), ws.numel(),
         _stream(x.device)))
     return out
+
+
+def gemm_f8_group(x, weights, k: int, outs=None):
+    """One launch over up to MAX_GROUP FP8 weights that read x: weights is a list of
+    (q_tiled, scale, n) as gemm_f8 takes them; returns the outputs [m, n_i]."""
+    torch = _torch()
+    x = _as_bits(x)
+    m = x.shape[0]
+    if x.shape[1] != k or not 1 <= len(weights) <= MAX_GROUP:
+        raise ValueError("gemm_f8_group: x must be [m, k] and 1..MAX_GROUP weights given")
+    for qt, sc, n in weights:
+        if qt.numel() * qt.element_size() != n * k or sc.dtype != torch.float32 or \
+                not sc.is_contiguous() or sc.numel() != ((n + 127) // 128) * (k // 128):
+            raise ValueError("gemm_f8_group: each weight is (q_tiled of n*k bytes, float32 "
+                             "scale [ceil(n/128), k/128], n)")
+    if outs is None:
+        outs = [torch.empty((m, n), dtype=torch.bfloat16, device=x.device) for _, _, n in weights]
+    nw = len(weights)
+    ptrs = (c_void_p * nw)(*[qt.data_ptr() for qt, _, _ in weights])
+    scs = (c_void_p * nw)(*[sc.data_ptr() for _, sc, _ in weights])
+    ns = (ctypes.c_uint64 * nw)(*[n for _, _, n in weights])
+    ys = (c_void_p * nw)(*[_as_bits(o).data_ptr() for o in outs])
+    n_total = sum(n for _, _, n in weights)
+    ws = workspace(max(workspace_bytes(OP_GEMM_GROUP, m, n_total, k), 256), x.device)
+    _check("w12_gemm_f8_group", lib().w12_gemm_f8_group(
+        _ptr(x), m, ptrs, scs, ns, nw, k, ys, _ptr(ws), ws.numel(), _stream(x.device)))
+    return outs
 
 
 def lmhead_verify(x, t: W12Tensor, draft, argmax_out=None, accepted_out=None):

@@ -148,3 +148,22 @@ def test_gemm_f8_deterministic_and_overwrites(env):
             torch.cuda.synchronize()
             assert torch.equal(y.view(torch.int16), y0.view(torch.int16))
         check(y0, x, q, s)
+
+
+@pytest.mark.parametrize("m", [1, 5, 16, 24, 33, 64, 128])
+def test_gemm_f8_group(env, m):
+    """q, k, v-like and gate, up-like groups in one launch: every output of every weight
+    against the oracle (segments with partial last scale blocks and odd row-block counts)."""
+    torch, w12 = env
+    g = np.random.default_rng(8700 + m)
+    for ns, k in (((272, 144, 144), 640), ((2080, 2080), 512), ((64, 48, 16, 32), 4096)):
+        say("gemm f8 group", m, ns, k)
+        qs = [random_codes((n, k), g) for n in ns]
+        ss = [random_scales(n, k, g) for n in ns]
+        x = wi.gaussian_bf16((m, k), 1.0, g)
+        weights = [(w12.f8_tile(torch.from_numpy(q).to("cuda:0")), torch.from_numpy(s).to("cuda:0"), q.shape[0])
+                   for q, s in zip(qs, ss)]
+        ys = w12.gemm_f8_group(to_dev(x, torch), weights, k)
+        torch.cuda.synchronize()
+        for y, q, s in zip(ys, qs, ss):
+            check(y, x, q, s)

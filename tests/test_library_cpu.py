@@ -192,6 +192,29 @@ def test_f8_validation(L):
     assert f(FAKE, 1, FAKE, FAKE, 1024, 4096, FAKE, None, need, None) == -1
 
 
+def test_f8_group_validation(L):
+    P = lambda *v: (ctypes.c_void_p * len(v))(*v)
+    N = lambda *v: (ctypes.c_uint64 * len(v))(*v)
+    f = L.w12_gemm_f8_group
+    ok = dict(x=FAKE, m=1, w=P(FAKE, FAKE), s=P(FAKE, FAKE), n=N(1024, 512), nw=2, k=1024,
+              y=P(FAKE, FAKE), ws=FAKE, wsb=1 << 30)
+
+    def call(**kw):
+        a = {**ok, **kw}
+        return f(a["x"], a["m"], a["w"], a["s"], a["n"], a["nw"], a["k"], a["y"], a["ws"], a["wsb"], None)
+    assert call(x=None) == -1
+    assert call(s=P(FAKE, None)) == -1
+    assert call(y=P(None, FAKE)) == -1
+    assert call(nw=0) == -3 and call(nw=5) == -3 and call(m=0) == -3 and call(m=129) == -3
+    assert call(n=N(1024, 1000)) == -2
+    assert call(k=100) == -2
+    assert call(w=P(FAKE, FAKE + 8)) == -7
+    assert call(s=P(FAKE + 2, FAKE)) == -7
+    assert call(x=FAKE + 8) == -7
+    need = w12.workspace_bytes(w12.OP_GEMM_GROUP, 1, 1536, 1024)
+    assert need > 0 and call(wsb=need - 1) == -5 and call(ws=None, wsb=need) == -1
+
+
 def test_verify_validation(L):
     f = L.w12_lmhead_verify
     d = desc(n=2048, k=512)
