@@ -883,7 +883,6 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_cs(
       t.sc = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(scrs, 0u, scrow + 4u * g, 0));
   };
 
-  // RMS launches: per-unit sums of x^2 over the K-range, in column order
   // RMS launches sum each row's x^2 over the K-range.  Up to 32 columns (the EPI_RMS
   // instantiations) by an MFMA of the x fragments with themselves (waves 0..3 take one of
   // the column's four 32-column steps each; the diagonal is kept), on matrix cores that
@@ -1028,7 +1027,7 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_cs(
   // As in k_gemm, the compiler's schedule (which may wait for tile g before issuing
   // tile g+1) measured faster than a pinned deeper prefetch.
   // x two columns ahead (staged into LDS one column ahead) for the plain sources, and for
-  // FP8 up to 32 columns: all workgroups read the same x column at about the same time,
+  // FP8 up to 32 columns and in the 10-wave 64-column kernel: all workgroups read the same x column at about the same time,
   // so its loads miss together, and waiting for them one column ahead put a memory
   // latency on every column (FP8 gate+up M1 / M32 / M64 38.2 / 40.6 / 46.7 -> 27.1 / 30.2 /
   // 42.7 us; tiled BF16 gate+up M32 / M64 / M128 74.6 / 87.4 / 132.4 -> 66.4 / 81.9 /
