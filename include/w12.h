@@ -2,8 +2,9 @@
  * w12.h -- C ABI of libw12.so: the W12 lossless 12-bit weight format on MI355X
  * (gfx950): encode, bit-exact decode, the memory-bound decode/verification GEMM
  * (M = 1..32 rows of BF16 x against W12 weights, FP32 accumulate, BF16 out; up to 128
- * rows for several requests verified together) and the greedy verification epilogue
- * (exact-logit argmax per row, accepted-prefix length per request).
+ * rows for several requests verified together), the greedy verification epilogue
+ * (exact-logit argmax per row, accepted-prefix length per request), and the same GEMM
+ * for the FP8 weights of FP8 targets (E4M3 codes with 128 x 128 block scales).
  *
  * Sources (pages cited by title and section):
  *  - "StargazerX0/SpecPilot" (hotrepo.ai), "What it is": W12 is a 12-bit weight
@@ -16,7 +17,9 @@
  *    context", "The mechanisms it found": about 12.01-12.02 bits per weight, decoded
  *    in GEMM registers, a quarter less weight traffic than BF16 in memory-bound
  *    decode, and a certified exact-argmax LM head; "The caveats the README states":
- *    reduction order can flip near-ties (hence argmax on exact logits).
+ *    reduction order can flip near-ties (hence argmax on exact logits); FP8 GEMM
+ *    routing among the batching mechanisms, with the "What it is" section of the digest
+ *    placing three batching settings on FP8 targets.
  *
  * W12 v1 layout (the pages fix only its properties; this is the layout defined here):
  *  - W is [n out][k in] BF16, row-major; n % 16 == 0, k % 128 == 0, 0 < k < 2^20.
