@@ -170,6 +170,71 @@ def fp8_gemms(torch, w12, wi, np, dev, n_copies, per, batched, check):
     return res
 
 
+FP8_LAYER_MS = (24, 64, 128)
+
+
+def fp8_layers(torch, w12, wi, np, dev, rotate_bytes):
+    """One decoder layer's GEMMs at the decode-step shapes (q/k/v in one launch, o, gate/up
+    in one launch, down; plain products, no RMS), FP8 checkpoint weights against W12
+    weights, at M = 24, 64 and 128: microseconds per layer over rotated layer copies."""
+    shapes = {name: (n, k) for name, n, k in wi.LAYER_MATS}
+    names = [name for name, _, _ in wi.LAYER_MATS]
+    f8_bytes_layer = sum(n * k for n, k in shapes.values())
+    copies = max(2, -(-int(rotate_bytes) // f8_bytes_layer))
+    f8l, w12l = [], []
+    for c in range(copies):
+        F, W = {}, {}
+        for mi, name in enumerate(names):
+            n, k = shapes[name]
+            q, sc = wi.device_f8_weight(torch, 2026_0900 + 8 * c + mi, n, k, dev)
+            F[name] = (w12.f8_tile(q), sc, n)
+            del q
+            W[name] = w12.encode(wi.device_layer_weight(torch, c, mi, n, k))
+        f8l.append(F)
+        w12l.append(W)
+    torch.cuda.synchronize()
+    w12_bytes_layer = sum(t.nbytes() for t in w12l[0].values())
+    hid, mlp = shapes["q"][1], shapes["down"][1]
+    res = {}
+    for m in FP8_LAYER_MS:
+        x = torch.from_numpy(wi.activations(5, wi.T_X, m, hid).view(np.int16)).to(dev)
+        xd = torch.from_numpy(wi.activations(5, wi.T_X2, m, mlp).view(np.int16)).to(dev)
+        ys = {name: torch.empty((m, shapes[name][0]), dtype=torch.bfloat16, device=dev) for name in names}
+        io = 2 * m * (3 * hid + mlp) + 2 * m * sum(n for n, _ in shapes.values())
+
+        def calls_f8(F):
+            return [w12.prepare_gemm_f8_group(x, [F["q"], F["k"], F["v"]], hid, [ys["q"], ys["k"], ys["v"]]),
+                    w12.prepare_gemm_f8(x, F["o"][0], F["o"][1], F["o"][2], hid, ys["o"]),
+                    w12.prepare_gemm_f8_group(x, [F["gate"], F["up"]], hid, [ys["gate"], ys["up"]]),
+                    w12.prepare_gemm_f8(xd, F["down"][0], F["down"][1], F["down"][2], mlp, ys["down"])]
+
+        def calls_w12(W):
+            return [w12.prepare_gemm_group(x, [W["q"], W["k"], W["v"]], [ys["q"], ys["k"], ys["v"]]),
+                    w12.prepare_gemm(x, W["o"], ys["o"]),
+                    w12.prepare_gemm_group(x, [W["gate"], W["up"]], [ys["gate"], ys["up"]]),
+                    w12.prepare_gemm(xd, W["down"], ys["down"])]
+        pf = [calls_f8(F) for F in f8l]
+        pw = [calls_w12(W) for W in w12l]
+
+        def run(prep):
+            def fn(i):
+                for c in prep[i % len(prep)]:
+                    c()
+            return fn
+        us_f8, _ = launch_rounds(torch, run(pf))
+        us_w12, _ = launch_rounds(torch, run(pw))
+        res[f"M{m}"] = {"us_f8": round(us_f8, 2), "gbps_f8": round((f8_bytes_layer + io) / us_f8 / 1e3, 1),
+                        "us_w12": round(us_w12, 2),
+                        "gbps_w12": round((w12_bytes_layer + io) / us_w12 / 1e3, 1),
+                        "speedup_vs_w12": round(us_w12 / us_f8, 3)}
+    res["workload"] = ("one decoder layer: q/k/v [5120+1024+1024, 5120] in one launch, o [5120, "
+                       "5120], gate/up [2x17408, 5120] in one launch, down [5120, 17408]; FP8 "
+                       "checkpoint weights vs W12, no RMS")
+    res["rotated_layers"] = copies
+    del f8l, w12l
+    return res
+
+
 COPY_BYTES = 1 << 30
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "w12_gemm_traffic.json")
 
@@ -835,6 +900,8 @@ def main():
     log("bench: FP8 GEMMs ...")
     fp8 = fp8_gemms(torch, w12, wi, np, dev, n_copies, per, batched, not args.no_cpu_baseline)
     log(f"bench: FP8 GEMMs {fp8}")
+    fp8["layer"] = fp8_layers(torch, w12, wi, np, dev, args.rotate_bytes)
+    log(f"bench: FP8 / W12 layers {fp8['layer']}")
 
     # dominant kernel = the (M, matrix) GEMM with the largest share of the step; its
     # achieved bandwidth from the mean launch time over its timed rounds

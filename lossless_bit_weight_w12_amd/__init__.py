@@ -10,7 +10,8 @@ from .w12 import (ENCODE_TOTAL_OFFSET, EXPORTS, MAX_GROUP, MAX_M, NOALLOC_SCRATC
                   decode, encode, f8_tile, gemm, gemm_bf16, gemm_bf16_tiled, gemm_f8, gemm_f8_group,
                   gemm_group, gemm_noalloc,
                   lib, lib_path, lmhead_verify, lmhead_verify2, lmhead_verify2_batched,
-                  lmhead_verify_batched, logits_f32, prepare_gemm, prepare_gemm_group,
+                  lmhead_verify_batched, logits_f32, prepare_gemm, prepare_gemm_f8,
+                  prepare_gemm_f8_group, prepare_gemm_group,
                   prepare_rms, prepare_verify, prepare_verify2, prepare_verify2_batched,
                   prepare_verify_batched, rms_rescale, screen_encode, screen_logits_f32,
                   status_str, stream_read, tiles_bytes, verify2_candidates, verify_candidates,
@@ -23,7 +24,7 @@ __all__ = ["ENCODE_TOTAL_OFFSET", "EXPORTS", "MAX_GROUP", "MAX_M", "NOALLOC_SCRA
            "bf16_tile", "decode", "encode", "f8_tile", "gemm", "gemm_bf16", "gemm_bf16_tiled",
            "gemm_f8", "gemm_f8_group", "gemm_group",
            "gemm_noalloc", "lib", "lib_path", "lmhead_verify", "lmhead_verify2",
-           "lmhead_verify2_batched", "lmhead_verify_batched", "logits_f32", "prepare_gemm",
+           "lmhead_verify2_batched", "lmhead_verify_batched", "logits_f32", "prepare_gemm", "prepare_gemm_f8", "prepare_gemm_f8_group",
            "prepare_gemm_group", "prepare_rms", "prepare_verify", "prepare_verify2",
            "prepare_verify2_batched", "prepare_verify_batched", "rms_rescale", "screen_encode",
            "screen_logits_f32", "status_str", "stream_read", "tiles_bytes", "verify2_candidates",

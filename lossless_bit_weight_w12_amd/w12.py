@@ -410,9 +410,7 @@ def gemm_f8(x, q_tiled, scale, n: int, k: int, out=None):
     return out
 
 
-def gemm_f8_group(x, weights, k: int, outs=None):
-    """One launch over up to MAX_GROUP FP8 weights that read x: weights is a list of
-    (q_tiled, scale, n) as gemm_f8 takes them; returns the outputs [m, n_i]."""
+def _f8_group_args(x, weights, k: int, outs):
     torch = _torch()
     x = _as_bits(x)
     m = x.shape[0]
@@ -428,12 +426,21 @@ def gemm_f8_group(x, weights, k: int, outs=None):
     nw = len(weights)
     ptrs = (c_void_p * nw)(*[qt.data_ptr() for qt, _, _ in weights])
     scs = (c_void_p * nw)(*[sc.data_ptr() for _, sc, _ in weights])
-    ns = (ctypes.c_uint64 * nw)(*[n for _, _, n in weights])
+    ns = (c_uint64 * nw)(*[n for _, _, n in weights])
     ys = (c_void_p * nw)(*[_as_bits(o).data_ptr() for o in outs])
     n_total = sum(n for _, _, n in weights)
     ws = workspace(max(workspace_bytes(OP_GEMM_GROUP, m, n_total, k), 256), x.device)
-    _check("w12_gemm_f8_group", lib().w12_gemm_f8_group(
-        _ptr(x), m, ptrs, scs, ns, nw, k, ys, _ptr(ws), ws.numel(), _stream(x.device)))
+    args = (_ptr(x), m, ctypes.cast(ptrs, c_void_p), ctypes.cast(scs, c_void_p),
+            ctypes.cast(ns, c_void_p), nw, k, ctypes.cast(ys, c_void_p), _ptr(ws), ws.numel(),
+            _stream(x.device))
+    return args, outs, (x, weights, outs, ws, ptrs, scs, ns, ys)
+
+
+def gemm_f8_group(x, weights, k: int, outs=None):
+    """One launch over up to MAX_GROUP FP8 weights that read x: weights is a list of
+    (q_tiled, scale, n) as gemm_f8 takes them; returns the outputs [m, n_i]."""
+    args, outs, _keep = _f8_group_args(x, weights, k, outs)
+    _check("w12_gemm_f8_group", lib().w12_gemm_f8_group(*args))
     return outs
 
 
@@ -664,6 +671,22 @@ def prepare_gemm_group(x, ts, outs, rms: bool = False) -> Prepared:
     args, outs, keep = _group_args(x, ts, outs)
     fn = "w12_gemm_group_rms" if rms else "w12_gemm_group"
     return Prepared(fn, getattr(lib(), fn), args, keep)
+
+
+def prepare_gemm_f8(x, q_tiled, scale, n: int, k: int, out) -> Prepared:
+    x, out = _as_bits(x), _as_bits(out)
+    m = x.shape[0]
+    if x.shape[1] != k or tuple(out.shape) != (m, n) or q_tiled.numel() * q_tiled.element_size() != n * k:
+        raise ValueError("prepare_gemm_f8: x must be [m, k], out [m, n], q_tiled n*k bytes")
+    ws = workspace(max(workspace_bytes(OP_GEMM_F8, m, n, k), 256), x.device)
+    args = (_ptr(x), m, _ptr(q_tiled), _ptr(scale), n, k, _ptr(out), _ptr(ws), ws.numel(),
+            _stream(x.device))
+    return Prepared("w12_gemm_f8", lib().w12_gemm_f8, args, (x, q_tiled, scale, out, ws))
+
+
+def prepare_gemm_f8_group(x, weights, k: int, outs) -> Prepared:
+    args, outs, keep = _f8_group_args(x, weights, k, outs)
+    return Prepared("w12_gemm_f8_group", lib().w12_gemm_f8_group, args, keep)
 
 
 def prepare_rms(x, out) -> Prepared:

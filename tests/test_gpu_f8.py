@@ -167,3 +167,29 @@ def test_gemm_f8_group(env, m):
         torch.cuda.synchronize()
         for y, q, s in zip(ys, qs, ss):
             check(y, x, q, s)
+
+
+def test_prepared_f8_calls_match_direct_calls(env):
+    """The prepared FP8 calls (marshalled once, re-issued by the layer timing) give the
+    direct calls' bits, also when re-issued after the inputs change in place."""
+    torch, w12 = env
+    g = np.random.default_rng(8800)
+    k = 640
+    qs = [random_codes((n, k), g) for n in (272, 144)]
+    ss = [random_scales(n, k, g) for n in (272, 144)]
+    weights = [(w12.f8_tile(torch.from_numpy(q).to("cuda:0")), torch.from_numpy(s).to("cuda:0"), q.shape[0])
+               for q, s in zip(qs, ss)]
+    x = to_dev(wi.gaussian_bf16((24, k), 1.0, g), torch)
+    y1 = torch.empty((24, 272), dtype=torch.bfloat16, device="cuda:0")
+    outs = [torch.empty((24, n), dtype=torch.bfloat16, device="cuda:0") for _, _, n in weights]
+    p1 = w12.prepare_gemm_f8(x, weights[0][0], weights[0][1], 272, k, y1)
+    pg = w12.prepare_gemm_f8_group(x, weights, k, outs)
+    for trial in range(2):
+        say("prepared f8 calls", trial)
+        p1()
+        pg()
+        torch.cuda.synchronize()
+        assert torch.equal(y1.view(torch.int16), w12.gemm_f8(x, weights[0][0], weights[0][1], 272, k).view(torch.int16))
+        for o, ref in zip(outs, w12.gemm_f8_group(x, weights, k)):
+            assert torch.equal(o.view(torch.int16), ref.view(torch.int16))
+        x.copy_(to_dev(wi.gaussian_bf16((24, k), 1.0, g), torch))
