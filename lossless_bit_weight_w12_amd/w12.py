@@ -266,10 +266,38 @@ def decode(t: W12Tensor, out=None):
     return out
 
 
-def gemm(x, t: W12Tensor, out=None, rms: bool = False):
-    """y = x . W^T, x BF16 [m, k] (m <= 32), y BF16 [m, n].  rms: each output row divided
-    by the RMS of its x row (w12_gemm_rms)."""
+@dataclass
+class F8Tensor:
+    """An FP8 weight [n, k] of an FP8 target resident on the GPU: E4M3 codes in the GEMM's
+    2 KB tiles (w12_f8_tile) and FP32 scales per 128 x 128 block [ceil(n/128), k/128]."""
+    n: int
+    k: int
+    tiles: object      # torch.uint8 [n*k]
+    scale: object      # torch.float32 [ceil(n/128), k/128]
+
+    def nbytes(self) -> int:
+        return self.tiles.numel() + 4 * self.scale.numel()
+
+
+def f8_encode(q, scale) -> F8Tensor:
+    """F8Tensor of row-major E4M3 codes q [n, k] (uint8, CUDA) and their block scales."""
     torch = _torch()
+    n, k = q.shape
+    if scale.dtype != torch.float32 or tuple(scale.shape) != ((n + 127) // 128, k // 128):
+        raise ValueError("f8_encode: scale must be float32 [ceil(n/128), k/128]")
+    return F8Tensor(n, k, f8_tile(q), scale.contiguous())
+
+
+def gemm(x, t, out=None, rms: bool = False):
+    """y = x . W^T, x BF16 [m, k] (m <= MAX_M), y BF16 [m, n].  rms: each output row divided
+    by the RMS of its x row (w12_gemm_rms).  A GEMM is routed by its weight's format: a
+    W12Tensor to w12_gemm, an F8Tensor (the weight of an FP8 target) to w12_gemm_f8 (FP8 GEMM
+    routing, review page "The mechanisms it found"; no RMS form)."""
+    torch = _torch()
+    if isinstance(t, F8Tensor):
+        if rms:
+            raise ValueError("gemm: the FP8 GEMM has no RMS form")
+        return gemm_f8(x, t.tiles, t.scale, t.n, t.k, out)
     x = _as_bits(x)
     m = x.shape[0]
     if x.shape[1] != t.k:
@@ -331,7 +359,13 @@ def _group_args(x, ts, outs):
 
 def gemm_group(x, ts, outs=None, rms: bool = False):
     """y_i = x . W_i^T for the weights ts (1..4, same k) in one launch per codebook kind;
-    rms as for gemm (w12_gemm_group_rms)."""
+    rms as for gemm (w12_gemm_group_rms).  A group of F8Tensors goes to w12_gemm_f8_group."""
+    if ts and all(isinstance(t, F8Tensor) for t in ts):
+        if rms:
+            raise ValueError("gemm_group: the FP8 GEMM has no RMS form")
+        return gemm_f8_group(x, [(t.tiles, t.scale, t.n) for t in ts], ts[0].k, outs)
+    if any(isinstance(t, F8Tensor) for t in ts):
+        raise ValueError("gemm_group: a group holds W12 weights or FP8 weights, not both")
     args, outs, keep = _group_args(x, ts, outs)
     fn = "w12_gemm_group_rms" if rms else "w12_gemm_group"
     _check(fn, getattr(lib(), fn)(*args))

@@ -193,3 +193,35 @@ def test_prepared_f8_calls_match_direct_calls(env):
         for o, ref in zip(outs, w12.gemm_f8_group(x, weights, k)):
             assert torch.equal(o.view(torch.int16), ref.view(torch.int16))
         x.copy_(to_dev(wi.gaussian_bf16((24, k), 1.0, g), torch))
+
+
+def test_gemm_routes_by_weight_format(env):
+    """gemm / gemm_group take an F8Tensor to the FP8 kernels (same bits as the direct
+    calls) and a W12Tensor to the W12 ones; a mixed group and an FP8 RMS call are refused."""
+    torch, w12 = env
+    g = np.random.default_rng(8900)
+    k = 512
+    q = random_codes((272, k), g)
+    s = random_scales(272, k, g)
+    t8 = w12.f8_encode(torch.from_numpy(q).to("cuda:0"), torch.from_numpy(s).to("cuda:0"))
+    assert (t8.n, t8.k) == (272, k) and t8.nbytes() == 272 * k + 4 * s.size
+    w = wi.gaussian_bf16((144, k), 0.02, g)
+    t12 = w12.encode(to_dev(w, torch))
+    x = wi.gaussian_bf16((5, k), 1.0, g)
+    xt = to_dev(x, torch)
+    say("gemm routing by weight format")
+    y8 = w12.gemm(xt, t8)
+    y12 = w12.gemm(xt, t12)
+    yg = w12.gemm_group(xt, [t8, t8])
+    torch.cuda.synchronize()
+    ref8 = w12.gemm_f8(xt, t8.tiles, t8.scale, 272, k)
+    assert torch.equal(y8.view(torch.int16), ref8.view(torch.int16))
+    check(y8, x, q, s)
+    z, sa = o.gemm_reference(x, w)
+    assert o.gemm_accept(to_host(y12), z, sa).all()
+    for yy in yg:
+        check(yy, x, q, s)
+    with pytest.raises(ValueError):
+        w12.gemm_group(xt, [t8, t12])
+    with pytest.raises(ValueError):
+        w12.gemm(xt, t8, rms=True)
