@@ -785,6 +785,19 @@ def main():
         for i in range(args.steps):
             w12_step(i)
             bf16_step(i)
+        # the same GEMMs in FP8 checkpoint form (the FP8 rows of the counter record)
+        f8w = {}
+        for name, n, k, seed in (("gate_up", N_GU, K_GU, 2026_0800), ("down", N_DN, K_DN, 2026_0801)):
+            q0, s0 = wi.device_f8_weight(torch, seed, n, k, dev)
+            f8w[name] = (w12.f8_tile(q0), s0, n, k)
+            del q0
+        yf = {m: (torch.empty((m, N_GU), dtype=torch.bfloat16, device=dev),
+                  torch.empty((m, N_DN), dtype=torch.bfloat16, device=dev)) for m in MS}
+        for i in range(args.steps):
+            for m in MS:
+                for j, name in ((0, "gate_up"), (1, "down")):
+                    qt, sc, n, k = f8w[name]
+                    w12.gemm_f8(xs[m][j], qt, sc, n, k, out=yf[m][j])
         if args.calibrate_copy:
             # known-size kernels for the counters: 1 GiB streamed with the GEMM's
             # nontemporal loads, a 1 GiB fill, and a 1 GiB device copy

@@ -12,8 +12,9 @@ from the known-size kernels at the end of the run: w12_stream_read over 1 GiB - 
 (read with the nontemporal 16-byte buffer loads the GEMM issues for W12 tiles) for
 FETCH_SIZE, and the 1 GiB fill before it (writes 1 GiB) for WRITE_SIZE; the 1 GiB
 device-to-device copy after it is reported as a cross-check of the read scale.  A
-`w12_gemm` launch is one GEMM kernel (K-split launches complete inside it).  Writes
-profiles/w12_gemm_traffic.json and profiles/w12_gemm_mlp_block_traffic.md.
+`w12_gemm` launch is one GEMM kernel (K-split launches complete inside it).  The FP8
+launches of the same shapes (`w12_gemm_f8`, after the profiled W12 / BF16 steps) get their
+own rows.  Writes profiles/w12_gemm_traffic.json and profiles/w12_gemm_mlp_block_traffic.md.
 
 With --stats it summarises a `rocprofv3 --kernel-trace --stats` run instead: the stats
 table and the average duration of every (kernel, grid) launch shape, as markdown; with
@@ -52,11 +53,20 @@ def is_gemm(name: str) -> bool:
     return "w12::k_gemm" in name
 
 
-def launches(rows):
-    """The GEMM-family dispatches, one per w12_gemm / w12_gemm_bf16 launch."""
+def is_f8(name: str) -> bool:
+    """An FP8 instantiation: weight source 4, the third template argument of k_gemm_cs."""
+    if "w12::k_gemm_cs<" not in name:
+        return False
+    args = name.split("k_gemm_cs<", 1)[1].split(">", 1)[0].split(",")
+    return len(args) == 4 and args[2].strip() == "4"
+
+
+def launches(rows, f8: bool = False):
+    """The GEMM-family dispatches, one per w12_gemm / w12_gemm_bf16 launch (f8: one per
+    w12_gemm_f8 launch)."""
     out = []
     for _, name, grid, val in rows:
-        if not is_gemm(name):
+        if not is_gemm(name) or is_f8(name) != f8:
             continue
         short = name.split("(")[0].replace("void ", "")
         out.append({"kernels": [short], "grid": grid, "value": val})
@@ -98,7 +108,7 @@ def main():
                            "copy_fetch_scale": copy_scale,
                            "fill_kernel": fill_w[1][:80], "fill_write_kib": fill_w[3],
                            "bytes": bench.COPY_BYTES},
-           "launches": {}, "bf16_launches": {}}
+           "launches": {}, "bf16_launches": {}, "f8_launches": {}}
     steps = len(lf) // 20
     for i, key in enumerate(keys):
         for kind, off in (("launches", 0), ("bf16_launches", 10)):
@@ -113,6 +123,20 @@ def main():
                               "hbm_bytes": int(round(f_kib * 1024 * fetch_scale
                                                      + w_kib * 1024 * write_scale)),
                               "alg_bytes": wb + 2 * m * k + 2 * m * n}
+    # the FP8 GEMMs of the same shapes, 10 launches per profiled step after the W12 / BF16 steps
+    ff, fw = launches(fr, f8=True), launches(wr, f8=True)
+    assert len(ff) == len(fw) == 10 * PROFILED_STEPS, (len(ff), len(fw))
+    for i, key in enumerate(keys):
+        idx = [10 * s + i for s in range(PROFILED_STEPS)]
+        f_kib = sum(ff[j]["value"] for j in idx) / PROFILED_STEPS
+        w_kib = sum(fw[j]["value"] for j in idx) / PROFILED_STEPS
+        m = int(key.split("_")[0][1:])
+        n, k = shapes[key.split("_", 1)[1]]
+        rec["f8_launches"][key] = {"kernels": ff[idx[0]]["kernels"], "grid": ff[idx[0]]["grid"],
+                                   "fetch_kib": round(f_kib, 3), "write_kib": round(w_kib, 3),
+                                   "hbm_bytes": int(round(f_kib * 1024 * fetch_scale
+                                                          + w_kib * 1024 * write_scale)),
+                                   "alg_bytes": bench.f8_bytes(n, k, m)}
     with open(os.path.join(ROOT, "profiles", "w12_gemm_traffic.json"), "w") as f:
         json.dump(rec, f, indent=1)
     lines = ["# HBM traffic per launch: MLP block GEMMs (rocprofv3 counters)", "",
@@ -133,6 +157,13 @@ def main():
         lines.append(f"| {key} | `{' + '.join(a['kernels'])}` | {a['hbm_bytes']:,} | {a['alg_bytes']:,} | "
                      f"{a['hbm_bytes'] / a['alg_bytes']:.3f} | {b['hbm_bytes']:,} | {b['alg_bytes']:,} | "
                      f"{b['hbm_bytes'] / b['alg_bytes']:.3f} |")
+    lines += ["", "The same shapes in FP8 checkpoint form (`w12_gemm_f8`: E4M3 codes + FP32 block "
+              "scales; algorithmic bytes = codes + scales + x + y):", "",
+              "| launch | kernels | FP8: HBM bytes | algorithmic | ratio |", "|---|---|---|---|---|"]
+    for key in keys:
+        c = rec["f8_launches"][key]
+        lines.append(f"| {key} | `{' + '.join(c['kernels'])}` | {c['hbm_bytes']:,} | {c['alg_bytes']:,} | "
+                     f"{c['hbm_bytes'] / c['alg_bytes']:.3f} |")
     with open(os.path.join(ROOT, "profiles", "w12_gemm_mlp_block_traffic.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
     print(json.dumps({k: v["hbm_bytes"] for k, v in rec["launches"].items()}))
