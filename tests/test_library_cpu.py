@@ -422,3 +422,17 @@ def test_verify2_batched_and_logits_validation(L):
     assert g(FAKE, 0, ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, big, None) == -3
     assert g(FAKE, 4, ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, 100, None) == -5
     assert g(FAKE, 4, ctypes.byref(d), FAKE, FAKE + 8, FAKE, FAKE, big, None) == -7
+
+
+def test_gemm_routing_refusals_need_no_device():
+    """The binding's routing by weight format refuses a mixed W12 / FP8 group and an FP8
+    RMS call before touching any tensor."""
+    t8 = B.F8Tensor(n=16, k=128, tiles=None, scale=None)
+    t12 = B.W12Tensor(n=16, k=128, n_esc=0, codebook=tuple(range(16)), e_max=0, tiles=None,
+                      esc_off=None, esc=None)
+    with pytest.raises(ValueError):
+        w12.gemm_group(None, [t8, t12])
+    with pytest.raises(ValueError):
+        w12.gemm_group(None, [t8], rms=True)
+    with pytest.raises(ValueError):
+        w12.gemm(None, t8, rms=True)
