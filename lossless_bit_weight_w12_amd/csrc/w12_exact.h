@@ -160,7 +160,7 @@ __device__ int32_t exact_best(ExactShared& ex, const ExactRow& c, uint32_t ns, G
       ex.vid[wave] = (int32_t)get(ci);
     }
     __syncthreads();
-    if (tid == 0) {   // this round's candidates against the best so far
+    if (tid == 0) {   // this batch of candidates (one per wave) against the best so far
       for (uint32_t w = 0; w < kExactWaves && c0i + w < ns; ++w) {
         bool better;
         if (ex.best_v < 0) {
