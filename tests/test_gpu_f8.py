@@ -225,3 +225,23 @@ def test_gemm_routes_by_weight_format(env):
         w12.gemm_group(xt, [t8, t12])
     with pytest.raises(ValueError):
         w12.gemm(xt, t8, rms=True)
+
+
+def test_f8_worked_example_golden(env):
+    """The hand-worked FP8 GEMM: tile bytes and output bits exactly (its few products and
+    their sums are exact in FP32, so the kernel's result is the rounding of the exact z)."""
+    torch, w12 = env
+    g, q, s, x = __import__("test_oracle").golden_f8()
+    say("f8 worked example")
+    qt = w12.f8_tile(torch.from_numpy(q).to("cuda:0"))
+    y = w12.gemm_f8(to_dev(x, torch), qt, torch.from_numpy(s).to("cuda:0"), g["n"], g["k"])
+    torch.cuda.synchronize()
+    tiles = qt.cpu().numpy()
+    listed = {off: int(b, 16) for off, b in g["tile_bytes"]}
+    assert all(int(tiles[off]) == b for off, b in listed.items())
+    assert np.count_nonzero(tiles) == len(listed)
+    yb = to_host(y)
+    want = np.zeros_like(yb)
+    for r, c, b in g["y_bf16"]:
+        want[r, c] = int(b, 16)
+    assert np.array_equal(yb, want)

@@ -686,6 +686,35 @@ def test_gemm_f8_vs_exact_rationals():
             assert abs(Fraction(sa[row, col]) - mag) <= k * Fraction(2) ** -53 * mag
 
 
+def golden_f8():
+    """The hand-worked FP8 GEMM (tests/golden/fp8_gemm_worked_example.json) as arrays."""
+    with open(os.path.join(GOLDEN, "fp8_gemm_worked_example.json")) as f:
+        g = json.load(f)
+    q = np.zeros((g["n"], g["k"]), dtype=np.uint8)
+    for r, c, b in g["codes"]:
+        q[r, c] = int(b, 16)
+    x = np.zeros((2, g["k"]), dtype=np.float32)
+    for r, c, v in g["x"]:
+        x[r, c] = v
+    return g, q, np.array(g["scales"], dtype=np.float32), wi.f32_to_bf16_bits(x)
+
+
+def test_f8_worked_example_golden():
+    g, q, s, x = golden_f8()
+    tiles = o.f8_pack(q)
+    listed = {off: int(b, 16) for off, b in g["tile_bytes"]}
+    assert all(int(tiles[off]) == b for off, b in listed.items())
+    assert np.count_nonzero(tiles) == len(listed)
+    z, _ = o.gemm_f8_reference(x, q, s)
+    want = np.zeros_like(z)
+    for r, c, v in g["z"]:
+        want[r, c] = v
+    assert np.array_equal(z, want)
+    y = o.bf16_round(z)
+    for r, c, b in g["y_bf16"]:
+        assert int(y[r, c]) == int(b, 16), (r, c)
+
+
 # ----------------------------------------------------------------------------- mutations
 def _pins_fail(fn):
     try:
