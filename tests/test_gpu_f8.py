@@ -245,3 +245,18 @@ def test_f8_worked_example_golden(env):
     for r, c, b in g["y_bf16"]:
         want[r, c] = int(b, 16)
     assert np.array_equal(yb, want)
+
+
+@pytest.mark.parametrize("m", [1, 33, 128])
+def test_gemm_f8_max_k(env, m):
+    """The longest K the shape rules allow (2^20 - 128, 8191 tile and scale columns): the
+    largest tile, x and scale offsets, K split over the few row-blocks."""
+    torch, w12 = env
+    g = np.random.default_rng(8950 + m)
+    n, k = 32, (1 << 20) - 128
+    q = random_codes((n, k), g)
+    s = random_scales(n, k, g)
+    x = wi.gaussian_bf16((m, k), 1.0, g)
+    say("gemm f8 max k", m, n, k)
+    _, y = run(torch, w12, x, q, s)
+    check(y, x, q, s)
