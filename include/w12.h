@@ -270,6 +270,19 @@ w12_status w12_gemm_f8_group(const uint16_t* x, uint32_t m, const void* const* w
                              uint64_t k, uint16_t* const* ys, void* ws, size_t ws_bytes,
                              void* stream);
 
+/* The same products of the row-wise RMS-normalised input, as w12_gemm_rms for W12
+ * weights (harness op of a layer chain, not part of the FP8 routing itself):
+ * y[row] = bf16((x[row] . W^T) / r), r = sqrt(mean_k x[row,k]^2) in FP32, the division
+ * applied to the FP32 sums.  Arguments, workspace, errors and determinism as
+ * w12_gemm_f8 / w12_gemm_f8_group. */
+w12_status w12_gemm_f8_rms(const uint16_t* x, uint32_t m, const void* w_tiled, const float* scale,
+                           uint64_t n, uint64_t k, uint16_t* y, void* ws, size_t ws_bytes,
+                           void* stream);
+w12_status w12_gemm_f8_group_rms(const uint16_t* x, uint32_t m, const void* const* w_tiled,
+                                 const float* const* scales, const uint64_t* ns, uint32_t n_w,
+                                 uint64_t k, uint16_t* const* ys, void* ws, size_t ws_bytes,
+                                 void* stream);
+
 /* Greedy verification over the LM head (review page, "The mechanisms it found":
  * certified exact-argmax LM head; "StargazerX0/SpecPilot", "Results and
  * verification": committed tokens are the target's own choice).

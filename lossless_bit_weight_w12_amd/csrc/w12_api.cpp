@@ -793,9 +793,13 @@ w12_status w12_f8_tile(const uint8_t* w, uint64_t n, uint64_t k, void* w_tiled, 
                                    (hipStream_t)stream));
 }
 
-w12_status w12_gemm_f8(const uint16_t* x, uint32_t m, const void* w_tiled, const float* scale,
-                       uint64_t n, uint64_t k, uint16_t* y, void* ws, size_t ws_bytes,
-                       void* stream) {
+}  // extern "C"
+
+namespace {
+
+w12_status gemm_f8_impl(const uint16_t* x, uint32_t m, const void* w_tiled, const float* scale,
+                        uint64_t n, uint64_t k, uint16_t* y, void* ws, size_t ws_bytes,
+                        void* stream, bool rms) {
   if (!x || !w_tiled || !scale || !y) return W12_ERR_NULL;
   if (!shape_ok(n, k)) return W12_ERR_SHAPE;
   if (m < 1 || m > W12_MAX_M) return W12_ERR_RANGE;
@@ -815,14 +819,15 @@ w12_status w12_gemm_f8(const uint16_t* x, uint32_t m, const void* w_tiled, const
   a.p.seg[0].y = y;
   a.p.seg[0].n = (uint32_t)n;
   fill_params(a.p, m, k, n, 1);
+  a.p.rms = rms ? 1u : 0u;
   if (!set_split_ws(a, ws, p, m, n)) return W12_ERR_HIP;
   return hip_status(launch_gemm(a, SRC_F8, EPI_BF16, p, (hipStream_t)stream));
 }
 
-w12_status w12_gemm_f8_group(const uint16_t* x, uint32_t m, const void* const* w_tiled,
-                             const float* const* scales, const uint64_t* ns, uint32_t n_w,
-                             uint64_t k, uint16_t* const* ys, void* ws, size_t ws_bytes,
-                             void* stream) {
+w12_status gemm_f8_group_impl(const uint16_t* x, uint32_t m, const void* const* w_tiled,
+                              const float* const* scales, const uint64_t* ns, uint32_t n_w,
+                              uint64_t k, uint16_t* const* ys, void* ws, size_t ws_bytes,
+                              void* stream, bool rms) {
   if (!x || !w_tiled || !scales || !ns || !ys) return W12_ERR_NULL;
   if (n_w < 1 || n_w > W12_MAX_GROUP || m < 1 || m > W12_MAX_M) return W12_ERR_RANGE;
   uint64_t n_total = 0;
@@ -851,9 +856,40 @@ w12_status w12_gemm_f8_group(const uint16_t* x, uint32_t m, const void* const* w
     n_total += ns[i];
   }
   fill_params(a.p, m, k, n_total, n_w);
+  a.p.rms = rms ? 1u : 0u;
   const GemmPlan p = make_plan(m, n_total, k, EPI_BF16, false);
   if (!set_split_ws(a, ws, p, m, n_total)) return W12_ERR_HIP;
   return hip_status(launch_gemm(a, SRC_F8, EPI_BF16, p, (hipStream_t)stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+w12_status w12_gemm_f8(const uint16_t* x, uint32_t m, const void* w_tiled, const float* scale,
+                       uint64_t n, uint64_t k, uint16_t* y, void* ws, size_t ws_bytes,
+                       void* stream) {
+  return gemm_f8_impl(x, m, w_tiled, scale, n, k, y, ws, ws_bytes, stream, false);
+}
+
+w12_status w12_gemm_f8_rms(const uint16_t* x, uint32_t m, const void* w_tiled, const float* scale,
+                           uint64_t n, uint64_t k, uint16_t* y, void* ws, size_t ws_bytes,
+                           void* stream) {
+  return gemm_f8_impl(x, m, w_tiled, scale, n, k, y, ws, ws_bytes, stream, true);
+}
+
+w12_status w12_gemm_f8_group(const uint16_t* x, uint32_t m, const void* const* w_tiled,
+                             const float* const* scales, const uint64_t* ns, uint32_t n_w,
+                             uint64_t k, uint16_t* const* ys, void* ws, size_t ws_bytes,
+                             void* stream) {
+  return gemm_f8_group_impl(x, m, w_tiled, scales, ns, n_w, k, ys, ws, ws_bytes, stream, false);
+}
+
+w12_status w12_gemm_f8_group_rms(const uint16_t* x, uint32_t m, const void* const* w_tiled,
+                                 const float* const* scales, const uint64_t* ns, uint32_t n_w,
+                                 uint64_t k, uint16_t* const* ys, void* ws, size_t ws_bytes,
+                                 void* stream) {
+  return gemm_f8_group_impl(x, m, w_tiled, scales, ns, n_w, k, ys, ws, ws_bytes, stream, true);
 }
 
 w12_status w12_lmhead_verify(const uint16_t* x, uint32_t m, const w12_desc* d, const int32_t* draft,

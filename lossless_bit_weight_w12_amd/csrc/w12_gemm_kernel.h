@@ -38,9 +38,9 @@
 //   output rows are divided by the RMS of their x rows, summed from the staged x
 //   (harness op of the layer chain, not the W12 method).
 // FP8 tiles (SRC_F8: E4M3 weights of an FP8 checkpoint with one FP32 scale per 128 x 128
-//   block) take the column-synchronous path with the BF16 epilogue: each byte pair is
-//   converted exactly to a BF16 pair, each tile column is summed from zero and enters
-//   the running sum times its block scale.
+//   block) take the column-synchronous path with the BF16 and RMS epilogues: each byte
+//   pair is converted exactly to a BF16 pair, each tile column is summed from zero and
+//   enters the running sum times its block scale.
 // The logits epilogue (verification pass 1) sums every tile column from zero before
 //   adding it to the running sum, and keeps per row-block the two largest logits, the
 //   index of the largest and the largest bound of a row's 2-norm; the full FP32 logits
@@ -1345,12 +1345,17 @@ hipError_t launch_gemm_src(const GemmArgs& a, int epi, const GemmPlan& pl, hipSt
                          a.sabs, a.bm, p);                         \
   } while (0)
 // (the RMS launches, GemmParams.rms with the BF16 epilogue, run their own instantiation
-// up to 32 columns and the BF16 one's runtime path from 64; the BF16 and FP8 sources
-// have neither RMS nor logits launches)
+// up to 32 columns and the BF16 one's runtime path from 64; the BF16 sources have neither
+// RMS nor logits launches, FP8 no logits launches)
 #define W12_CS_EPI(MT_)                                                     \
   do {                                                                      \
     if (epi == EPI_BF16 && (!p.rms || MT_ >= 64)) W12_CS(MT_, EPI_BF16);   \
-    else if constexpr (!w12_src(SRC)) return hipErrorInvalidValue;         \
+    else if constexpr (plain_bf16(SRC)) return hipErrorInvalidValue;       \
+    else if constexpr (SRC == SRC_F8) {                                     \
+      if (epi == EPI_LOGITS) return hipErrorInvalidValue;                   \
+      if constexpr (MT_ <= 32) W12_CS(MT_, EPI_RMS);                        \
+      else return hipErrorInvalidValue;                                     \
+    }                                                                       \
     else if (epi == EPI_LOGITS) W12_CS(MT_, EPI_LOGITS);                    \
     else if constexpr (MT_ <= 32) W12_CS(MT_, EPI_RMS);                     \
     else return hipErrorInvalidValue;                                       \

@@ -27,7 +27,8 @@ EXPORTS = ("w12_tiles_bytes", "w12_workspace_bytes", "w12_workspace_init", "w12_
            "w12_logits_f32",
            "w12_rms_rescale", "w12_status_str", "w12_version", "w12_gemm_noalloc", "w12_stream_read",
            "w12_screen_bytes", "w12_screen_encode", "w12_lmhead_verify2", "w12_lmhead_verify2_batched",
-           "w12_screen_logits_f32", "w12_f8_tile", "w12_gemm_f8", "w12_gemm_f8_group")
+           "w12_screen_logits_f32", "w12_f8_tile", "w12_gemm_f8", "w12_gemm_f8_group",
+           "w12_gemm_f8_rms", "w12_gemm_f8_group_rms")
 NOALLOC_SCRATCH_BYTES = 32 << 20   # W12_NOALLOC_SCRATCH_BYTES
 ENCODE_TOTAL_OFFSET = 2112   # W12_ENCODE_TOTAL_OFFSET: true escape count in an encode workspace
 
@@ -104,6 +105,10 @@ def lib():
         L.w12_gemm_f8_group.restype = c_int32
         L.w12_gemm_f8_group.argtypes = [c_void_p, c_uint32, c_void_p, c_void_p, c_void_p, c_uint32,
                                         c_uint64, c_void_p, c_void_p, c_size_t, c_void_p]
+        L.w12_gemm_f8_rms.restype = c_int32
+        L.w12_gemm_f8_rms.argtypes = L.w12_gemm_f8.argtypes
+        L.w12_gemm_f8_group_rms.restype = c_int32
+        L.w12_gemm_f8_group_rms.argtypes = L.w12_gemm_f8_group.argtypes
         L.w12_lmhead_verify.restype = c_int32
         L.w12_lmhead_verify.argtypes = [c_void_p, c_uint32, ctypes.POINTER(W12Desc), c_void_p,
                                         c_uint32, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]
@@ -292,12 +297,10 @@ def gemm(x, t, out=None, rms: bool = False):
     """y = x . W^T, x BF16 [m, k] (m <= MAX_M), y BF16 [m, n].  rms: each output row divided
     by the RMS of its x row (w12_gemm_rms).  A GEMM is routed by its weight's format: a
     W12Tensor to w12_gemm, an F8Tensor (the weight of an FP8 target) to w12_gemm_f8 (FP8 GEMM
-    routing, review page "The mechanisms it found"; no RMS form)."""
+    routing, review page "The mechanisms it found")."""
     torch = _torch()
     if isinstance(t, F8Tensor):
-        if rms:
-            raise ValueError("gemm: the FP8 GEMM has no RMS form")
-        return gemm_f8(x, t.tiles, t.scale, t.n, t.k, out)
+        return gemm_f8(x, t.tiles, t.scale, t.n, t.k, out, rms=rms)
     x = _as_bits(x)
     m = x.shape[0]
     if x.shape[1] != t.k:
@@ -361,9 +364,7 @@ def gemm_group(x, ts, outs=None, rms: bool = False):
     """y_i = x . W_i^T for the weights ts (1..4, same k) in one launch per codebook kind;
     rms as for gemm (w12_gemm_group_rms).  A group of F8Tensors goes to w12_gemm_f8_group."""
     if ts and all(isinstance(t, F8Tensor) for t in ts):
-        if rms:
-            raise ValueError("gemm_group: the FP8 GEMM has no RMS form")
-        return gemm_f8_group(x, [(t.tiles, t.scale, t.n) for t in ts], ts[0].k, outs)
+        return gemm_f8_group(x, [(t.tiles, t.scale, t.n) for t in ts], ts[0].k, outs, rms=rms)
     if any(isinstance(t, F8Tensor) for t in ts):
         raise ValueError("gemm_group: a group holds W12 weights or FP8 weights, not both")
     args, outs, keep = _group_args(x, ts, outs)
@@ -423,9 +424,10 @@ def f8_tile(q):
     return out
 
 
-def gemm_f8(x, q_tiled, scale, n: int, k: int, out=None):
+def gemm_f8(x, q_tiled, scale, n: int, k: int, out=None, rms: bool = False):
     """y = x . W^T for the FP8 weight W = E4M3(q) * block scale: q_tiled from f8_tile,
-    scale float32 [ceil(n/128), k/128]."""
+    scale float32 [ceil(n/128), k/128].  rms: each output row divided by the RMS of its x
+    row (w12_gemm_f8_rms)."""
     torch = _torch()
     x = _as_bits(x)
     m = x.shape[0]
@@ -438,7 +440,8 @@ def gemm_f8(x, q_tiled, scale, n: int, k: int, out=None):
     if out is None:
         out = torch.empty((m, n), dtype=torch.bfloat16, device=x.device)
     ws = workspace(max(workspace_bytes(OP_GEMM_F8, m, n, k), 256), x.device)
-    _check("w12_gemm_f8", lib().w12_gemm_f8(
+    fn = "w12_gemm_f8_rms" if rms else "w12_gemm_f8"
+    _check(fn, getattr(lib(), fn)(
         _ptr(x), m, _ptr(q_tiled), _ptr(scale), n, k, _ptr(_as_bits(out)), _ptr(ws), ws.numel(),
         _stream(x.device)))
     return out
@@ -470,11 +473,13 @@ def _f8_group_args(x, weights, k: int, outs):
     return args, outs, (x, weights, outs, ws, ptrs, scs, ns, ys)
 
 
-def gemm_f8_group(x, weights, k: int, outs=None):
+def gemm_f8_group(x, weights, k: int, outs=None, rms: bool = False):
     """One launch over up to MAX_GROUP FP8 weights that read x: weights is a list of
-    (q_tiled, scale, n) as gemm_f8 takes them; returns the outputs [m, n_i]."""
+    (q_tiled, scale, n) as gemm_f8 takes them; returns the outputs [m, n_i].  rms as for
+    gemm_f8 (w12_gemm_f8_group_rms)."""
     args, outs, _keep = _f8_group_args(x, weights, k, outs)
-    _check("w12_gemm_f8_group", lib().w12_gemm_f8_group(*args))
+    fn = "w12_gemm_f8_group_rms" if rms else "w12_gemm_f8_group"
+    _check(fn, getattr(lib(), fn)(*args))
     return outs
 
 
@@ -707,7 +712,7 @@ def prepare_gemm_group(x, ts, outs, rms: bool = False) -> Prepared:
     return Prepared(fn, getattr(lib(), fn), args, keep)
 
 
-def prepare_gemm_f8(x, q_tiled, scale, n: int, k: int, out) -> Prepared:
+def prepare_gemm_f8(x, q_tiled, scale, n: int, k: int, out, rms: bool = False) -> Prepared:
     x, out = _as_bits(x), _as_bits(out)
     m = x.shape[0]
     if x.shape[1] != k or tuple(out.shape) != (m, n) or q_tiled.numel() * q_tiled.element_size() != n * k:
@@ -715,12 +720,14 @@ def prepare_gemm_f8(x, q_tiled, scale, n: int, k: int, out) -> Prepared:
     ws = workspace(max(workspace_bytes(OP_GEMM_F8, m, n, k), 256), x.device)
     args = (_ptr(x), m, _ptr(q_tiled), _ptr(scale), n, k, _ptr(out), _ptr(ws), ws.numel(),
             _stream(x.device))
-    return Prepared("w12_gemm_f8", lib().w12_gemm_f8, args, (x, q_tiled, scale, out, ws))
+    fn = "w12_gemm_f8_rms" if rms else "w12_gemm_f8"
+    return Prepared(fn, getattr(lib(), fn), args, (x, q_tiled, scale, out, ws))
 
 
-def prepare_gemm_f8_group(x, weights, k: int, outs) -> Prepared:
+def prepare_gemm_f8_group(x, weights, k: int, outs, rms: bool = False) -> Prepared:
     args, outs, keep = _f8_group_args(x, weights, k, outs)
-    return Prepared("w12_gemm_f8_group", lib().w12_gemm_f8_group, args, keep)
+    fn = "w12_gemm_f8_group_rms" if rms else "w12_gemm_f8_group"
+    return Prepared(fn, getattr(lib(), fn), args, keep)
 
 
 def prepare_rms(x, out) -> Prepared:

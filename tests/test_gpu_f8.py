@@ -223,8 +223,10 @@ def test_gemm_routes_by_weight_format(env):
         check(yy, x, q, s)
     with pytest.raises(ValueError):
         w12.gemm_group(xt, [t8, t12])
-    with pytest.raises(ValueError):
-        w12.gemm(xt, t8, rms=True)
+    yr = w12.gemm(xt, t8, rms=True)
+    torch.cuda.synchronize()
+    refr = w12.gemm_f8(xt, t8.tiles, t8.scale, 272, k, rms=True)
+    assert torch.equal(yr.view(torch.int16), refr.view(torch.int16))
 
 
 def test_f8_worked_example_golden(env):
@@ -260,3 +262,36 @@ def test_gemm_f8_max_k(env, m):
     say("gemm f8 max k", m, n, k)
     _, y = run(torch, w12, x, q, s)
     check(y, x, q, s)
+
+
+def rms_f8_reference(x, q, s):
+    """Reference of the FP8 RMS GEMM (harness op of a layer chain): the oracle's product
+    divided by the row's RMS, sqrt(mean_k x^2) in FP64 from the BF16 values, with the
+    magnitude scale divided the same way (for oracle.gemm_accept)."""
+    z, sa = o.gemm_f8_reference(x, q, s)
+    xf = wi.bf16_bits_to_f32(x).astype(np.float64)
+    r = np.sqrt((xf * xf).mean(axis=1))[:, None]
+    return z / r, sa / r
+
+
+@pytest.mark.parametrize("m", [1, 5, 16, 24, 32, 33, 64, 100, 128])
+def test_gemm_f8_rms(env, m):
+    """The RMS form (single and grouped launches, K whole and split) against the oracle's
+    product divided by each x row's RMS."""
+    torch, w12 = env
+    g = np.random.default_rng(9100 + m)
+    for ns, k in (((272,), 1280), ((64,), 4096), ((272, 144, 144), 640), ((2080,), 512)):
+        say("gemm f8 rms", m, ns, k)
+        qs = [random_codes((n, k), g) for n in ns]
+        ss = [random_scales(n, k, g) for n in ns]
+        x = wi.gaussian_bf16((m, k), 1.0, g)
+        weights = [(w12.f8_tile(torch.from_numpy(q).to("cuda:0")), torch.from_numpy(sc).to("cuda:0"), q.shape[0])
+                   for q, sc in zip(qs, ss)]
+        xt = to_dev(x, torch)
+        ys = (w12.gemm_f8_group(xt, weights, k, rms=True) if len(ns) > 1
+              else [w12.gemm_f8(xt, weights[0][0], weights[0][1], ns[0], k, rms=True)])
+        torch.cuda.synchronize()
+        for y, q, sc in zip(ys, qs, ss):
+            z, sa = rms_f8_reference(x, q, sc)
+            ok = o.gemm_accept(to_host(y), z, sa)
+            assert ok.all(), f"{int((~ok).sum())} outputs outside tolerance"

@@ -425,14 +425,24 @@ def test_verify2_batched_and_logits_validation(L):
 
 
 def test_gemm_routing_refusals_need_no_device():
-    """The binding's routing by weight format refuses a mixed W12 / FP8 group and an FP8
-    RMS call before touching any tensor."""
+    """The binding's routing by weight format refuses a mixed W12 / FP8 group before
+    touching any tensor."""
     t8 = B.F8Tensor(n=16, k=128, tiles=None, scale=None)
     t12 = B.W12Tensor(n=16, k=128, n_esc=0, codebook=tuple(range(16)), e_max=0, tiles=None,
                       esc_off=None, esc=None)
     with pytest.raises(ValueError):
         w12.gemm_group(None, [t8, t12])
     with pytest.raises(ValueError):
-        w12.gemm_group(None, [t8], rms=True)
-    with pytest.raises(ValueError):
-        w12.gemm(None, t8, rms=True)
+        w12.gemm_group(None, [t12, t8], rms=True)
+
+
+def test_f8_rms_validation(L):
+    f = L.w12_gemm_f8_rms
+    assert f(FAKE, 1, FAKE, None, 1024, 1024, FAKE, FAKE, 1 << 30, None) == -1
+    assert f(FAKE, 0, FAKE, FAKE, 1024, 1024, FAKE, FAKE, 1 << 30, None) == -3
+    assert f(FAKE, 1, FAKE, FAKE, 1000, 1024, FAKE, FAKE, 1 << 30, None) == -2
+    P = lambda *v: (ctypes.c_void_p * len(v))(*v)
+    N = lambda *v: (ctypes.c_uint64 * len(v))(*v)
+    g = L.w12_gemm_f8_group_rms
+    assert g(FAKE, 1, P(FAKE), P(None), N(1024), 1, 1024, P(FAKE), FAKE, 1 << 30, None) == -1
+    assert g(FAKE, 1, P(FAKE), P(FAKE), N(1024), 5, 1024, P(FAKE), FAKE, 1 << 30, None) == -3
