@@ -1,8 +1,10 @@
 """GPU parity of the FP8 GEMM (E4M3 codes with FP32 128 x 128 block scales, BF16
 activations) against the CPU oracle, element by element, through the C ABI: the tile
-bytes exactly, every output by oracle.gemm_accept.  Shapes span several tiles, ragged
-128-row scale blocks, odd row-block counts and K splits; m covers the 16-, 32-, 64- and
-128-column x tiles and their ragged edges."""
+bytes exactly, every output by oracle.gemm_accept (a hand-worked example bit for bit).
+Shapes span several tiles, ragged 128-row scale blocks, odd row-block counts, K splits and
+the longest K; m covers the 16-, 32-, 64- and 128-column x tiles and their ragged edges.
+Also the grouped launches, the RMS forms, the prepared calls and the binding's routing
+by weight format."""
 import numpy as np
 import pytest
 
